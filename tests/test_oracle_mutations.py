@@ -1,0 +1,65 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case copies the oracle and its pin tests into a temporary directory,
+plants one mistake in the copied oracle (a dropped term, a wrong index or
+sign, a wrong rounding), runs the pins there, and requires them to fail.
+Nothing under the repository is modified.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTATIONS = {
+    "tie_to_higher_start": ("order = np.lexsort((starts, -scores))", "order = np.lexsort((-starts, -scores))"),
+    "samples_past_length": ("valid = t < length", "valid = t >= 0"),
+    "head_group_mapping": ("Q[h // G] += q8[h].astype(np.int64)", "Q[h % num_kv_heads] += q8[h].astype(np.int64)"),
+    "reciprocal_multiply": ("code = np.rint(x / np.float32(scale))", "code = np.rint(x * (np.float32(1) / np.float32(scale)))"),
+    "truncating_round": ("code = np.rint(x / np.float32(scale))", "code = np.trunc(x / np.float32(scale))"),
+    "half_away_from_zero": ("code = np.rint(x / np.float32(scale))", "code = np.sign(x) * np.floor(np.abs(x / np.float32(scale)) + 0.5)"),
+    "no_window": ("mask[max(0, length - window):] = True", "pass"),
+    "sink_off_by_one": ("mask[:min(sink, length)] = True", "mask[1:min(sink, length)] = True"),
+    "no_softmax_scale": ("z = scale * (k_f64 @ q_f64)", "z = (k_f64 @ q_f64)"),
+    "children_step": ("x = (kept[:, None] + chunk * np.arange(parent_chunk // chunk", "x = (kept[:, None] + 1 * np.arange(parent_chunk // chunk"),
+    "absmax_over_padding": ("vals = np.abs(bf16_to_f32(k_bits[:length]))", "vals = np.abs(bf16_to_f32(k_bits))"),
+    "ignore_stride": ("t = starts[:, None] + stride * np.arange(n_samp", "t = starts[:, None] + 1 * np.arange(n_samp"),
+    "keep_one_more": ("return np.sort(starts[order[:keep]])", "return np.sort(starts[order[:keep + 1]])"),
+    "sum_not_max": ("return S.max(axis=1)", "return np.where(S == np.iinfo(np.int64).min, 0, S).sum(axis=1)"),
+    "lru_evicts_newest": ("if self.last.get(blk) == last:", "if self.last.get(blk) == last and False:"),
+}
+
+
+@pytest.fixture(scope="module")
+def sandbox(tmp_path_factory):
+    d = tmp_path_factory.mktemp("oracle_copy")
+    shutil.copytree(os.path.join(ROOT, "oracle"), d / "oracle",
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    os.makedirs(d / "tests")
+    for f in ("conftest.py", "test_oracle_pins.py"):
+        shutil.copy(os.path.join(ROOT, "tests", f), d / "tests" / f)
+    shutil.copytree(os.path.join(ROOT, "tests", "golden"), d / "tests" / "golden")
+    os.makedirs(d / "sparse_attention_kv_int8_amd")
+    shutil.copy(os.path.join(ROOT, "sparse_attention_kv_int8_amd", "inputs.py"),
+                d / "sparse_attention_kv_int8_amd" / "inputs.py")
+    (d / "sparse_attention_kv_int8_amd" / "__init__.py").write_text("")
+    return d
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(sandbox, name):
+    src_path = sandbox / "oracle" / "sparse_decode.py"
+    original = src_path.read_text()
+    old, new = MUTATIONS[name]
+    assert old in original, name
+    try:
+        src_path.write_text(original.replace(old, new))
+        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                            "tests/test_oracle_pins.py"], cwd=sandbox, capture_output=True, text=True,
+                           timeout=600)
+    finally:
+        src_path.write_text(original)
+    assert r.returncode != 0, f"mutation {name} was not caught:\n{r.stdout[-2000:]}"

@@ -1,0 +1,367 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test names the oracle function it pins and what fixes the expected
+value: exact rational arithmetic, a brute-force definition, a closed form,
+a hand-worked fixture under tests/golden/, or the independent loop
+implementation in oracle/loop_ref.py.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st, HealthCheck
+
+from oracle import sparse_decode as O
+from oracle import loop_ref as LR
+from sparse_attention_kv_int8_amd.inputs import f32_to_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def bf16_from_f32(x):
+    return f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def exact_code(k_bits, a_bits):
+    """Exact rational round-half-even of 127 k / a (Python's round() on a
+    Fraction rounds half to even)."""
+    k = Fraction(float(O.bf16_to_f32(np.uint16(k_bits))))
+    a = Fraction(float(O.bf16_to_f32(np.uint16(a_bits))))
+    return round(Fraction(127) * k / a)
+
+
+# ---------------------------------------------------------------- O1-O3 ---
+def test_quantize_random_pairs_match_exact_rounding():
+    """quantize_symmetric vs exact rational RNE on random bf16 pairs |k| <= a."""
+    rng = np.random.default_rng(7)
+    n = 20000
+    a = bf16_from_f32(np.exp(rng.uniform(-20, 20, n)).astype(np.float32))
+    af = O.bf16_to_f32(a)
+    k = bf16_from_f32((af * rng.uniform(-1, 1, n)).astype(np.float32))
+    # keep |k| <= a after bf16 rounding of k
+    ok = np.abs(O.bf16_to_f32(k)) <= af
+    a, k = a[ok], k[ok]
+    got = np.array([O.quantize_symmetric(k[i:i + 1], O.bf16_to_f32(a[i]))[0] for i in range(len(a))])
+    want = np.array([exact_code(k[i], a[i]) for i in range(len(a))])
+    assert np.array_equal(got, want)
+
+
+def test_quantize_exact_ties_round_to_even():
+    """a = 127 * 2^e makes 127 k / a = k / 2^e: every half-integer k / 2^e is a
+    tie, and the code must be the even neighbour."""
+    for e in (-10, -3, 0, 2, 7):
+        a = np.float32(127.0 * 2.0 ** e)
+        a_bits = bf16_from_f32(a)
+        assert O.bf16_to_f32(a_bits) == a          # 127 fits in 8 significant bits
+        for n in range(0, 127):
+            x = np.float32((n + 0.5) * 2.0 ** e)
+            kb = bf16_from_f32(x)
+            if O.bf16_to_f32(kb) != x:
+                continue                           # not representable in bf16
+            for sgn in (1, -1):
+                kbs = kb if sgn > 0 else np.uint16(kb | 0x8000)
+                got = int(O.quantize_symmetric(np.array([kbs]), a)[0])
+                want = sgn * (n if n % 2 == 0 else n + 1)
+                assert got == want, (e, n, sgn, got)
+
+
+def test_quantize_ties_other_mantissas():
+    """Ties with a not of the form 127 * 2^e: k = (2n+1) a / 254 exactly."""
+    count = 0
+    for a_bits in range(0x3F80, 0x4000):        # every bf16 in [1, 2)
+        a = Fraction(float(O.bf16_to_f32(np.uint16(a_bits))))
+        for n in range(127):
+            k = Fraction(2 * n + 1) * a / 254
+            kf = np.float32(float(k))
+            if Fraction(float(kf)) != k:
+                continue
+            kb = bf16_from_f32(kf)
+            if Fraction(float(O.bf16_to_f32(kb))) != k:
+                continue
+            got = int(O.quantize_symmetric(np.array([kb]), O.bf16_to_f32(np.uint16(a_bits)))[0])
+            assert got == exact_code(kb, a_bits)
+            count += 1
+    assert count > 50
+
+
+def test_quantize_special_cases():
+    a = np.float32(3.0)
+    kb = bf16_from_f32(np.array([3.0, -3.0, 0.0, -0.0], np.float32))
+    assert list(O.quantize_symmetric(kb, a)) == [127, -127, 0, 0]
+    assert not O.quantize_symmetric(kb, np.float32(0.0)).any()
+
+
+def test_key_quant_range_and_absmax_excludes_padding():
+    rng = np.random.default_rng(3)
+    k = bf16_from_f32(rng.standard_normal((50, 128)).astype(np.float32))
+    k[40:] = bf16_from_f32(np.float32(1000.0))        # padding rows
+    k8, a = O.quantize_keys(k, 40)
+    assert a == np.abs(O.bf16_to_f32(k[:40])).max()
+    assert k8.shape == (40, 128)
+    assert np.abs(k8.astype(int)).max() == 127
+    assert np.abs(k8.astype(int)).max() <= 127
+
+
+def test_query_codes_use_one_scale_per_head():
+    """Scaling one query head by a power of two leaves every code unchanged
+    (per-head scale); a shared scale across heads would change them."""
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((4, 128)).astype(np.float32)
+    q8 = O.quantize_query(bf16_from_f32(q))
+    q2 = q.copy()
+    q2[1] *= 8.0
+    q82 = O.quantize_query(bf16_from_f32(q2))
+    assert np.array_equal(q8, q82)
+    for h in range(4):
+        assert np.abs(q8[h].astype(int)).max() == 127
+
+
+# ---------------------------------------------------------------- O4-O5 ---
+def test_group_sum_identity_and_head_mapping():
+    rng = np.random.default_rng(11)
+    q8 = rng.integers(-127, 128, size=(32, 128)).astype(np.int8)
+    k8 = rng.integers(-127, 128, size=(100, 128)).astype(np.int8)
+    Q = O.group_query(q8, 8)
+    for j in range(8):
+        direct = sum(k8.astype(np.int64) @ q8[h].astype(np.int64) for h in range(4 * j, 4 * j + 4))
+        assert np.array_equal(O.token_scores(Q[j], k8), direct)
+    # contiguous grouping: only head 13 nonzero -> only KV head 3 sees it
+    one = np.zeros((32, 128), np.int8)
+    one[13, 5] = 1
+    Qo = O.group_query(one, 8)
+    assert Qo[3, 5] == 1 and Qo.sum() == 1
+    # the int32 bound the kernels rely on
+    Qmax = O.group_query(np.full((4, 128), 127, np.int8), 1)
+    assert O.token_scores(Qmax[0], np.full((1, 128), 127, np.int8))[0] == 8258048 < 2 ** 31
+
+
+# ---------------------------------------------------------------- O6-O9 ---
+def _S_from_list(S):
+    S = np.asarray(S, dtype=np.int64)
+    return lambda t: S[t]
+
+
+def test_prune_hand_worked_fixture():
+    g = json.load(open(os.path.join(GOLDEN, "select_hand.json")))
+    stages = [O.StageSpec(*s) for s in g["stages"]]
+    kept = O.prune(_S_from_list(g["S"]), g["length"], stages)
+    assert [list(map(int, k)) for k in kept] == g["expected_kept"]
+    T = O.attended_tokens(kept[-1], stages[-1].chunk, g["length"], g["sink"], g["window"])
+    assert list(map(int, T)) == g["expected_T"]
+    tc = g["tie_case"]
+    kept = O.prune(_S_from_list(g["S"]), g["length"], [O.StageSpec(*s) for s in tc["stages"]])
+    assert [list(map(int, k)) for k in kept] == tc["expected_kept"]
+
+
+@pytest.mark.parametrize("L,c,K", [(1000, 16, 5), (1024, 32, 40), (777, 8, 1), (50, 64, 3)])
+def test_single_stage_stride1_equals_brute_force(L, c, K):
+    """One stage with stride 1: kept = top-K chunks by (full chunk max desc,
+    start asc), computed with Python's sorted over explicit maxima."""
+    rng = np.random.default_rng(L + c + K)
+    S = rng.integers(-50, 50, size=L)          # small range -> many ties
+    kept = O.prune(_S_from_list(S), L, [O.StageSpec(c, 1, K)])[0]
+    chunks = [(max(S[x:min(x + c, L)]), x) for x in range(0, L, c)]
+    want = sorted(x for _, x in sorted(chunks, key=lambda p: (-p[0], p[1]))[:K])
+    assert list(kept) == want
+
+
+def test_selection_is_nested_in_keep():
+    rng = np.random.default_rng(2)
+    S = rng.integers(-20, 20, size=4096)
+    prev = set()
+    for K in range(1, 60):
+        kept = set(O.prune(_S_from_list(S), 4096, [O.StageSpec(64, 8, K)])[0].tolist())
+        assert prev <= kept and len(kept) == K
+        prev = kept
+
+
+def test_multistage_structure():
+    rng = np.random.default_rng(4)
+    L = 5000
+    S = rng.integers(-1000, 1000, size=L)
+    stages = [O.StageSpec(256, 8, 6), O.StageSpec(32, 2, 12), O.StageSpec(8, 1, 20)]
+    kept = O.prune(_S_from_list(S), L, stages)
+    for s in range(1, 3):
+        parents = kept[s - 1]
+        for x in kept[s]:
+            assert any(p <= x < p + stages[s - 1].chunk for p in parents)
+        n_cand = len(O.children(parents, stages[s - 1].chunk, stages[s].chunk, L))
+        assert len(kept[s]) == min(stages[s].keep, n_cand)
+    assert len(kept[0]) == min(6, math.ceil(L / 256))
+
+
+def test_full_budgets_cover_everything():
+    L = 1000
+    S = np.random.default_rng(0).integers(-5, 5, size=L)
+    stages = [O.StageSpec(64, 8, 100), O.StageSpec(16, 2, 400), O.StageSpec(8, 1, 1000)]
+    kept = O.prune(_S_from_list(S), L, stages)
+    T = O.attended_tokens(kept[-1], 8, L, 0, 0)
+    assert np.array_equal(T, np.arange(L))
+
+
+# ---------------------------------------------------------------- O10 -----
+def test_attended_set_bounds():
+    rng = np.random.default_rng(9)
+    for L in (1, 7, 63, 64, 65, 600, 1100, 4000):
+        S = rng.integers(-100, 100, size=L)
+        stages = [O.StageSpec(256, 8, 4), O.StageSpec(32, 2, 8), O.StageSpec(8, 1, 16)]
+        kept = O.prune(_S_from_list(S), L, stages)
+        T = O.attended_tokens(kept[-1], 8, L, 64, 512)
+        Ts = set(T.tolist())
+        assert set(range(min(64, L))) <= Ts
+        assert set(range(max(0, L - 512), L)) <= Ts
+        assert len(T) <= 16 * 8 + 64 + 512
+        assert np.all(np.diff(T) > 0) and T.min() >= 0 and T.max() < L
+
+
+# ---------------------------------------------------------------- O11 -----
+def test_attend_closed_forms():
+    rng = np.random.default_rng(1)
+    d = 128
+    q = rng.standard_normal(d)
+    k = rng.standard_normal((2, d))
+    v = rng.standard_normal((2, d))
+    s = 1 / np.sqrt(d)
+    o, p = O.attend(q, k, v, s)
+    z0, z1 = s * k[0] @ q, s * k[1] @ q
+    p0 = 1.0 / (1.0 + math.exp(z1 - z0))         # two-token softmax closed form
+    assert abs(p[0] - p0) < 1e-14 and abs(p.sum() - 1) < 1e-14
+    assert np.allclose(o, p0 * v[0] + (1 - p0) * v[1], atol=1e-14, rtol=0)
+    o1, p1 = O.attend(q, k[:1], v[:1], s)          # one token: output is its value
+    assert np.array_equal(o1, v[0]) and p1[0] == 1.0
+    # permutation invariance
+    k5, v5 = rng.standard_normal((50, d)), rng.standard_normal((50, d))
+    perm = rng.permutation(50)
+    oa, _ = O.attend(q, k5, v5, s)
+    ob, _ = O.attend(q, k5[perm], v5[perm], s)
+    assert np.allclose(oa, ob, atol=1e-13, rtol=0)
+
+
+def _tiny_inputs(L, Hkv=1, G=4, d=128, seed=0, planted=()):
+    rng = np.random.default_rng(seed)
+    q = bf16_from_f32(rng.standard_normal((Hkv * G, d)).astype(np.float32))
+    k = bf16_from_f32(rng.standard_normal((Hkv, L, d)).astype(np.float32))
+    v = bf16_from_f32(rng.standard_normal((Hkv, L, d)).astype(np.float32))
+    for j in range(Hkv):
+        mq = O.bf16_to_f32(q[j * G:(j + 1) * G]).mean(axis=0)
+        for t in planted:
+            k[j, t] = bf16_from_f32(2 * mq + 0.5 * rng.standard_normal(d).astype(np.float32))
+    return q, k, v
+
+
+def _run_oracle(q, k, v, L, stages, sink, window):
+    Hkv = k.shape[0]
+    k8 = np.zeros(k.shape, np.int8)
+    for j in range(Hkv):
+        k8[j, :L] = O.quantize_keys(k[j], L)[0]
+    cfg = O.StepConfig(tuple(O.StageSpec(*s) for s in stages), sink, window, 1 / np.sqrt(k.shape[2]))
+    return O.decode_step(q[None], k[None], k8[None], v[None], [L], cfg), k8
+
+
+def test_full_budgets_equal_dense_attention():
+    """Budgets that keep every chunk: the sparse output equals the dense
+    softmax(q K^T / sqrt(d)) V over all L tokens, and weights sum to 1."""
+    L = 700
+    q, k, v = _tiny_inputs(L, Hkv=2, G=4, seed=12)
+    res, _ = _run_oracle(q, k, v, L, [(64, 8, 11), (16, 2, 44), (8, 1, 88)], 0, 0)
+    for j in range(2):
+        assert np.array_equal(res.attended[0][j], np.arange(L))
+        for h in range(4 * j, 4 * j + 4):
+            dense = O.dense_attention(O.bf16_to_f64(q[h]), O.bf16_to_f64(k[j, :L]),
+                                      O.bf16_to_f64(v[j, :L]), 1 / np.sqrt(128))
+            assert np.max(np.abs(res.out[0, h] - dense)) < 1e-12
+    assert np.max(np.abs(res.psum - 1)) < 1e-12
+
+
+def test_length_one_returns_the_value():
+    q, k, v = _tiny_inputs(1, seed=3)
+    res, _ = _run_oracle(q, k, v, 1, [(256, 8, 16), (32, 2, 32), (8, 1, 64)], 64, 512)
+    for h in range(4):
+        assert np.array_equal(res.out[0, h], O.bf16_to_f64(v[0, 0]))
+
+
+def test_planted_tokens_are_recalled():
+    """Planted heavy keys at positions that every stage samples (multiples of
+    8), in distinct final chunks, fewer than every keep budget: once their
+    scores beat every other token's, all of them must be attended."""
+    L = 16384
+    planted = [8 * p for p in (100, 333, 700, 901, 1200, 1500, 1777, 1999)]
+    q, k, v = _tiny_inputs(L, seed=21, planted=planted)
+    res, k8 = _run_oracle(q, k, v, L, [(256, 8, 16), (32, 2, 32), (8, 1, 64)], 64, 512)
+    S = O.token_scores(res.Q[0, 0], k8[0, :L])
+    others = np.delete(S, planted)
+    assert S[planted].min() > others.max()          # precondition
+    assert set(planted) <= set(res.attended[0][0].tolist())
+
+
+# --------------------------------------------------- loop cross-check -----
+@settings(max_examples=25, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(L=st.integers(1, 160), seed=st.integers(0, 10 ** 6), G=st.sampled_from([1, 2, 4]),
+       dup=st.booleans(), budgets=st.sampled_from([
+           [(16, 4, 3), (4, 2, 4), (2, 1, 4)],
+           [(32, 8, 2), (8, 2, 3), (4, 1, 5)],
+           [(16, 1, 100)],
+           [(8, 2, 1), (4, 1, 1)]]),
+       sink=st.integers(0, 6), window=st.integers(0, 9))
+def test_vectorised_oracle_matches_loop_oracle(L, seed, G, dup, budgets, sink, window):
+    d = 16
+    rng = np.random.default_rng(seed)
+    q = bf16_from_f32(rng.standard_normal((2 * G, d)).astype(np.float32))
+    k = bf16_from_f32(rng.standard_normal((2, L + 3, d)).astype(np.float32))
+    v = bf16_from_f32(rng.standard_normal((2, L + 3, d)).astype(np.float32))
+    k[:, L:] = bf16_from_f32(np.float32(100.0))          # padding must be ignored
+    if dup and L > 4:                                     # forced score ties
+        for t in range(2, L, 5):
+            k[:, t] = k[:, 0]
+    ref = LR.step(q.tolist(), k.tolist(), v.tolist(), L, G, budgets, sink, window, 1 / math.sqrt(d))
+    k8 = np.zeros(k.shape, np.int8)
+    for j in range(2):
+        k8[j, :L] = O.quantize_keys(k[j], L)[0]
+    cfg = O.StepConfig(tuple(O.StageSpec(*s) for s in budgets), sink, window, 1 / math.sqrt(d))
+    res = O.decode_step(q[None], k[None], k8[None], v[None], [L], cfg)
+    assert np.array_equal(res.q8[0], np.array(ref["q8"]))
+    for j in range(2):
+        assert np.array_equal(k8[j, :L], np.array(ref["k8"][j]).reshape(L, d))
+        off = 0
+        for s, (_, _, keep) in enumerate(budgets):
+            got = res.kept_idx[0, j, off:off + keep]
+            want = ref["kept"][j][s]
+            assert list(got[:len(want)]) == want and np.all(got[len(want):] == -1)
+            off += keep
+        assert res.attended[0][j].tolist() == ref["T"][j]
+    assert np.max(np.abs(res.out[0] - np.array(ref["out"]))) < 1e-12
+
+
+# ---------------------------------------------------------------- O12 -----
+def test_lru_hand_traces():
+    g = json.load(open(os.path.join(GOLDEN, "lru_hand.json")))
+    for tr in g["traces"]:
+        lru = O.LRU(tr["capacity"])
+        got = [list(lru.step(b, t)) for t, b in enumerate(tr["steps"])]
+        assert got == tr["expected"]
+
+
+def test_lru_matches_brute_force_definition():
+    """Heap-based LRU vs a direct min-scan over the resident set."""
+    rng = np.random.default_rng(8)
+    cap = 13
+    lru = O.LRU(cap)
+    last = {}
+    for t in range(200):
+        need = sorted(set(rng.integers(0, 40, size=rng.integers(1, cap + 1)).tolist()))
+        h = sum(1 for x in need if x in last)
+        for x in need:
+            if x in last:
+                last[x] = t
+        for x in need:
+            if x not in last:
+                if len(last) == cap:
+                    victim = min(last, key=lambda b: (last[b], b))
+                    del last[victim]
+                last[x] = t
+        assert lru.step(need, t) == (h, len(need) - h)
+        assert lru.last == last
