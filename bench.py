@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of one sparse decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line.  A step is the whole per-step path: query codes,
+three pruning stages with their top-K selects, the attended set, the sparse
+flash decode and its log-sum-exp merge.  Inputs sit in HBM before the timed
+region starts.  Successive steps rotate over several copies of the KV cache
+at different addresses so that no step finds its bytes in the 256 MB
+Infinity Cache or the L2 (a cold-cache measurement; the copies hold the same
+data).  The int8 key quantisation runs once per cache and is reported
+separately.
+
+value  = algorithmic HBM bytes of a step / wall time per step (GB/s), where
+         the algorithmic bytes are the unique int8 key rows any stage samples
+         (128 B each), bf16 K and V of every attended token (512 B each), and
+         the query read and output written.
+roofline = the dominant kernel's algorithmic bytes per launch / its average
+         launch duration, timed with HIP events on the launch stream during
+         the timed region, against 8 TB/s.
+cpu_baseline = the CPU oracle (numpy, one core) on one full step of the same
+         workload.
+"""
+from __future__ import annotations
+
+import os
+
+import argparse
+import json
+import math
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from sparse_attention_kv_int8_amd.inputs import WORKLOADS, make_inputs  # noqa: E402
+
+METRIC = "sparse decode-attention µs/step + achieved HBM GB/s at 128K and 1M ctx (GQA 32/8)"
+HBM_PEAK_GBS = 8000.0
+KIND_NAMES = ["stage0", "stage1", "stage2", "stage3", "value_cache", "attend", "quantize"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- bytes ---
+def algorithmic_bytes(w, kept: np.ndarray, lengths: np.ndarray) -> dict:
+    """Bytes the method must move once, per kernel kind, from the step's kept
+    sets: int8 rows first sampled by each stage, K+V of the attended tokens,
+    the query and the output."""
+    per = {f"stage{s}": 0 for s in range(len(w.stages))}
+    per["attend"] = 0
+    rows_total = 0
+    tokens_total = 0
+    koff = np.cumsum([0] + [s.keep for s in w.stages])
+    for b in range(w.batch):
+        L = int(lengths[b])
+        for j in range(w.num_kv_heads):
+            seen = np.zeros(L, dtype=bool)
+            cand = np.arange(0, L, w.stages[0].chunk, dtype=np.int64)
+            for s, st in enumerate(w.stages):
+                t = (cand[:, None] + st.stride * np.arange(st.chunk // st.stride)[None, :]).ravel()
+                t = t[t < L]
+                new = np.unique(t[~seen[t]])
+                seen[new] = True
+                per[f"stage{s}"] += 128 * len(new)
+                rows_total += len(new)
+                kept_s = kept[b, j, koff[s]:koff[s + 1]]
+                kept_s = kept_s[kept_s >= 0].astype(np.int64)
+                if s + 1 < len(w.stages):
+                    c_n = w.stages[s + 1].chunk
+                    cand = (kept_s[:, None] + c_n * np.arange(st.chunk // c_n)[None, :]).ravel()
+                    cand = cand[cand < L]
+            T = np.zeros(L, dtype=bool)
+            for x in kept_s:
+                T[x:x + w.stages[-1].chunk] = True
+            T[:w.sink] = True
+            T[max(0, L - w.window):] = True
+            n = int(T.sum())
+            tokens_total += n
+            per["attend"] += 512 * n
+    qbytes = 2 * w.batch * w.num_q_heads * w.head_dim
+    per["stage0"] += qbytes
+    per["attend"] += 2 * qbytes            # query in, output out
+    return dict(per_kernel=per, total=sum(per.values()), int8_rows=rows_total, attended_tokens=tokens_total)
+
+
+# ---------------------------------------------------------------- GPU -----
+class Bench:
+    def __init__(self, w, copies: int):
+        import torch
+        from sparse_attention_kv_int8_amd import binding as B
+        self.torch, self.B, self.w = torch, B, w
+        t = time.perf_counter()
+        inp = make_inputs(w)
+        log(f"[bench] {w.name}: inputs generated in {time.perf_counter() - t:.1f}s")
+        self.inp = inp
+        dev = "cuda"
+        to_bf16 = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        self.dec = B.SparseDecoder.for_workload(w)
+        q = inp.q_step0
+        self.q = to_bf16(np.ascontiguousarray(q))
+        self.lengths = torch.from_numpy(inp.lengths.astype(np.int32)).to(dev)
+        k0 = to_bf16(inp.k)
+        v0 = to_bf16(inp.v)
+        k80 = torch.empty(inp.k.shape, dtype=torch.int8, device=dev)
+        # one-time key quantisation, timed with events
+        self.dec.sd_profile_start(1 << B.SD_PROF_QUANTIZE, 4)
+        self.dec.sd_quantize_keys(k0, self.lengths, k80)
+        prof = self.dec.sd_profile_stop()
+        self.quantize_us = prof["quantize"][0] * 1e3
+        self.ks, self.vs, self.k8s = [k0], [v0], [k80]
+        for _ in range(copies - 1):
+            self.ks.append(k0.clone())
+            self.vs.append(v0.clone())
+            self.k8s.append(k80.clone())
+        self.out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+        self.kept = torch.empty((w.batch, w.num_kv_heads, w.keep_total), dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        self.stream = torch.cuda.current_stream().cuda_stream
+        # raw pointers so that the timed loop is one ctypes call per step
+        self.args = [(self.q.data_ptr(), self.ks[i].data_ptr(), self.k8s[i].data_ptr(), self.vs[i].data_ptr(),
+                      self.lengths.data_ptr(), self.out.data_ptr(), self.kept.data_ptr())
+                     for i in range(copies)]
+
+    def run(self, n: int) -> None:
+        lib, h, s = self.B.lib, self.dec.handle, self.stream
+        nc = len(self.args)
+        for i in range(n):
+            a = self.args[i % nc]
+            st = lib.sd_decode_step(h, *a, s)
+            if st:
+                self.B.check(st, "sd_decode_step")
+
+    def profile(self, n: int, mask: int) -> dict:
+        self.dec.sd_profile_start(mask, 8 * n + 8)
+        self.run(n)
+        return self.dec.sd_profile_stop()
+
+
+def oracle_baseline(w, inp, kept_gpu_bytes: float) -> dict:
+    """The CPU oracle on one full step of the same inputs (one core)."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:          # pragma: no cover
+        threadpool_limits = None
+    from oracle import sparse_decode as O
+    import contextlib
+    ctx = threadpool_limits(1) if threadpool_limits else contextlib.nullcontext()
+    with ctx:
+        t = time.perf_counter()
+        k8 = np.zeros(inp.k.shape, np.int8)
+        for b in range(w.batch):
+            L = int(inp.lengths[b])
+            for j in range(w.num_kv_heads):
+                k8[b, j, :L] = O.quantize_keys(inp.k[b, j], L)[0]
+        tq = time.perf_counter() - t
+        cfg = O.StepConfig(tuple(O.StageSpec(s.chunk, s.stride, s.keep) for s in w.stages), w.sink, w.window,
+                           1.0 / math.sqrt(w.head_dim))
+        times = []
+        for _ in range(3):
+            t = time.perf_counter()
+            O.decode_step(inp.q_step0, inp.k, k8, inp.v, inp.lengths, cfg)
+            times.append(time.perf_counter() - t)
+            if sum(times) > 20:
+                break
+    ts = statistics.median(times)
+    return {"value": round(kept_gpu_bytes / ts / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"one full decode step of {w.name} (median of {len(times)} runs, {ts:.2f} s/step); "
+                      f"key quantisation {tq:.2f} s once",
+            "s_per_step": round(ts, 4), "quantize_s": round(tq, 3)}
+
+
+def measure(w, steps: int, warmup: int, copies: int) -> tuple:
+    b = Bench(w, copies)
+    torch = b.torch
+    b.run(warmup)
+    torch.cuda.synchronize()
+    # calibration: all kernels timed, to pick the dominant one
+    cal = b.profile(max(20, warmup), 0x7F)
+    avg_us = {k: v[0] * 1e3 / v[1] for k, v in cal.items()}
+    dominant = max((k for k in avg_us if k != "quantize"), key=lambda k: avg_us[k])
+    dom_kind = KIND_NAMES.index(dominant)
+    # timed region: K steps, events bracket the dominant kernel only
+    b.dec.sd_profile_start(1 << dom_kind, steps + 8)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    b.run(steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    live = b.dec.sd_profile_stop()
+    us_per_step = (t1 - t0) / steps * 1e6
+    dom_us = live[dominant][0] * 1e3 / live[dominant][1]
+    kept = b.kept.cpu().numpy()
+    ab = algorithmic_bytes(w, kept, b.inp.lengths)
+    return b, dict(us_per_step=us_per_step, avg_us=avg_us, dominant=dominant, dominant_us=dom_us, bytes=ab)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama8b_128k", choices=sorted(WORKLOADS))
+    ap.add_argument("--copies", type=int, default=0, help="KV-cache copies rotated over (0 = enough to "
+                    "defeat the 256 MB Infinity Cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--secondary", default="ctx_1m", help="second workload reported inside the line ('' = none)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        log("bench.py: one GPU only (the per-(request, KV head) path shards trivially, but no "
+            "multi-GPU run is part of this build)")
+        return 2
+    w = WORKLOADS[args.workload]
+    if w.values_on_host:
+        log("bench.py: the host-value workload is measured by tests/test_gpu_hostv.py")
+        return 2
+
+    def auto_copies(wl):
+        if args.copies:
+            return args.copies
+        est = 38e6 if wl.max_context <= 131072 else 160e6
+        est *= wl.batch if wl.batch > 1 else 1
+        return max(2, min(16, math.ceil(600e6 / est) + 1))
+
+    b, r = measure(w, args.steps, args.warmup, auto_copies(w))
+    total = r["bytes"]["total"]
+    dom_bytes = r["bytes"]["per_kernel"][r["dominant"]]
+    achieved = dom_bytes / (r["dominant_us"] * 1e-6) / 1e9
+    sum_kernel_us = sum(v for k, v in r["avg_us"].items() if k != "quantize")
+    line = {
+        "metric": METRIC,
+        "value": round(total / (r["us_per_step"] * 1e-6) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["us_per_step"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+fp32",
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": w.name, "batch": w.batch, "context": w.max_context, "gqa": f"{w.num_q_heads}/{w.num_kv_heads}",
+                   "stages": [[s.chunk, s.stride, s.keep] for s in w.stages], "sink": w.sink, "window": w.window,
+                   "cache": f"cold: {len(b.args)} rotating copies"},
+        "us_per_step": round(r["us_per_step"], 3),
+        "tokens_per_s": round(w.batch / (r["us_per_step"] * 1e-6), 1),
+        "algorithmic_bytes": total,
+        "roofline": {"bound": "hbm", "kernel": r["dominant"], "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": dom_bytes,
+                     "avg_launch_us": round(r["dominant_us"], 3)},
+        "step_kernels_us": {k: round(v, 3) for k, v in r["avg_us"].items()},
+        "step_roofline": {"achieved": round(total / (sum_kernel_us * 1e-6) / 1e9, 2), "unit": "GB/s",
+                          "frac": round(total / (sum_kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                          "note": "all per-step bytes / sum of per-step kernel durations"},
+        "quantize_keys_us": round(b.quantize_us, 2),
+    }
+    inp, kb = b.inp, total
+    del b
+    b_torch = __import__("torch")
+    b_torch.cuda.empty_cache()
+    if args.secondary and args.secondary != w.name:
+        w2 = WORKLOADS[args.secondary]
+        b2, r2 = measure(w2, max(20, args.steps // 2), args.warmup, auto_copies(w2))
+        t2 = r2["bytes"]["total"]
+        line["secondary"] = {"workload": w2.name, "us_per_step": round(r2["us_per_step"], 3),
+                             "value_GBs": round(t2 / (r2["us_per_step"] * 1e-6) / 1e9, 2),
+                             "algorithmic_bytes": t2, "step_kernels_us": {k: round(v, 3) for k, v in r2["avg_us"].items()},
+                             "dominant": r2["dominant"],
+                             "dominant_frac": round(r2["bytes"]["per_kernel"][r2["dominant"]] /
+                                                    (r2["dominant_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                             "quantize_keys_us": round(b2.quantize_us, 2)}
+        del b2
+        b_torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on one step ...")
+        line["cpu_baseline"] = oracle_baseline(w, inp, kb)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

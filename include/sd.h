@@ -1,0 +1,207 @@
+/*
+ * sd.h -- C ABI of the sparse decode-attention library (libsd.so).
+ *
+ * One decode step of attention over a long KV cache, in three parts:
+ *
+ *  1. Keys are quantised once to symmetric int8 with one absmax scale per
+ *     (request, KV head).  Sources: summary page of "HCAttention: Extreme KV
+ *     cache compression via heterogeneous attention computing for LLMs",
+ *     sections 摘要 and 引言 (quantised keys stay on the GPU and drive a
+ *     global approximate scoring); page "KV Cache 与长上下文推理", section
+ *     "KV Cache 压缩技术" (INT8 key cache).
+ *  2. Stacked pruning stages rank fixed-length chunks by one representative
+ *     score each and keep the top K chunks, refining chunk length stage by
+ *     stage.  Source: news article on InfiniteHiP ("韩国通过卸载键值缓存节约
+ *     英伟达GPU内存，实现18.95倍解码加速"), section "实现 7.24 倍的端到端解码加速".
+ *     A chunk's score is the maximum, over tokens sampled at the stage's
+ *     stride from the chunk start, of the exact integer dot product between
+ *     the int8 key and the sum of the group's int8 query vectors; ties go
+ *     to the lower chunk start.
+ *  3. Exact GQA attention (bf16 q and K, fp32 accumulation, bf16 output)
+ *     over the kept chunks plus the first `sink` and last `window` tokens.
+ *     Sources: page "KV Cache 与长上下文推理", section "KV Cache 回顾" (decode
+ *     attention equation) and section "KV Cache 压缩技术" (GQA table;
+ *     StreamingLLM sink + sliding window).
+ *
+ * Optionally values live in pinned host memory behind an LRU cache of
+ * 8-token value blocks in device memory (news article on InfiniteHiP, same
+ * section: LRU-based offload; HCAttention summary, section 引言: values in
+ * CPU memory, fetched late for the final aggregation).
+ *
+ * Conventions for every call:
+ *  - bf16 tensors are passed as uint16_t bit patterns.
+ *  - "device" pointers are device memory of the context's GPU; "host"
+ *    pointers are ordinary host memory.  The caller owns every buffer it
+ *    passes; the context owns its workspace (allocated in sd_create only).
+ *  - Work is enqueued on the caller's HIP stream (`stream`, a hipStream_t;
+ *    NULL = the null stream) and the call returns without waiting, except
+ *    where a call says it synchronises.
+ *  - Calls return a status and never abort.  Argument and configuration
+ *    errors are reported synchronously.  Bad values found on the device
+ *    (a length outside [1, max_context]) set a flag reported by sd_check.
+ *  - A context is used from one host thread and one stream at a time.
+ */
+#ifndef SD_H_
+#define SD_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sd_ctx sd_ctx;
+
+typedef enum sd_status {
+    SD_OK = 0,
+    SD_ERR_INVALID_ARG = 1,     /* null pointer, bad size or inconsistent config */
+    SD_ERR_UNSUPPORTED = 2,     /* valid but outside what the kernels implement */
+    SD_ERR_OUT_OF_MEMORY = 3,   /* workspace allocation failed in sd_create */
+    SD_ERR_HIP = 4,             /* a HIP runtime call failed */
+    SD_ERR_DEVICE_FLAG = 5      /* a kernel flagged bad input (see sd_check) */
+} sd_status;
+
+#define SD_MAX_STAGES 4
+
+/* One pruning stage: chunks of `chunk` tokens, representative sampled every
+ * `stride` tokens from the chunk start, the `keep` best chunks survive.
+ * Stage 1 chunks start at 0, chunk, 2*chunk, ...; the chunks of stage s+1
+ * are the sub-chunks of the survivors of stage s. */
+typedef struct sd_stage {
+    int32_t chunk;
+    int32_t stride;
+    int32_t keep;
+} sd_stage;
+
+typedef struct sd_config {
+    int32_t batch;              /* B >= 1 */
+    int32_t num_q_heads;        /* Hq */
+    int32_t num_kv_heads;       /* Hkv; Hq = G * Hkv with G in {1, 2, 4} */
+    int32_t head_dim;           /* d; must be 128 */
+    int64_t max_context;        /* Lmax: token stride of every [B][Hkv][Lmax][d] buffer */
+    int32_t num_stages;         /* S in [1, SD_MAX_STAGES] */
+    sd_stage stage[SD_MAX_STAGES];
+    /* Requirements: stride divides chunk; chunk[s+1] divides chunk[s];
+     * the last stage's chunk is a multiple of 8; keep >= 1;
+     * chunk / stride <= 64 at every stage; for every stage the number of
+     * candidates n_s (n_0 = ceil(Lmax / chunk[0]), n_s = keep[s-1] *
+     * chunk[s-1] / chunk[s]) plus keep[s] is at most 15872. */
+    int32_t sink;               /* first `sink` tokens always attended (>= 0) */
+    int32_t window;             /* last `window` tokens always attended (>= 0) */
+    float softmax_scale;        /* 0 selects 1 / sqrt(head_dim) */
+    int32_t values_on_host;     /* 0: v is device memory; 1: v is pinned host memory */
+    int64_t value_cache_tokens; /* values_on_host: device cache size in tokens per
+                                   (request, KV head); a multiple of 8 that holds at
+                                   least one step's attended blocks */
+} sd_config;
+
+/* Counters of the host-value path (values_on_host = 1), over all steps
+ * since creation or the last sd_reset_value_cache, and for the last step. */
+typedef struct sd_stats {
+    int64_t steps;
+    int64_t blocks_needed;      /* sum over steps and (request, KV head) of |blocks of T| */
+    int64_t hits;
+    int64_t misses;
+    int64_t h2d_bytes;          /* misses * 8 tokens * d * 2 bytes */
+    int64_t last_needed;
+    int64_t last_hits;
+    int64_t last_misses;
+} sd_stats;
+
+/* Creates a context on the current HIP device, validating `cfg` and
+ * allocating all device workspace (no later call allocates).  On success
+ * *out receives the context; on failure *out is set to NULL. */
+sd_status sd_create(const sd_config* cfg, sd_ctx** out);
+
+/* Releases the context and its workspace after the device is idle.
+ * NULL is a no-op. */
+void sd_destroy(sd_ctx* ctx);
+
+/* Static text for a status code. */
+const char* sd_status_string(sd_status status);
+
+/* Quantises the key cache (part 1).
+ *  k_bf16   device [B][Hkv][Lmax][d] bf16 keys.
+ *  lengths  device [B] int32 request lengths L_b in [1, Lmax].
+ *  k_int8   device [B][Hkv][Lmax][d] int8 output: for t < L_b the code
+ *           rint(127 * k / a_bj) (round half to even, correctly rounded
+ *           fp32 division), a_bj = max |k| over t < L_b and all channels
+ *           (codes are 0 when a_bj = 0).  Rows t >= L_b are not written.
+ *  k_absmax device [B][Hkv] fp32 output a_bj, or NULL. */
+sd_status sd_quantize_keys(sd_ctx* ctx, const uint16_t* k_bf16, const int32_t* lengths,
+                           int8_t* k_int8, float* k_absmax, void* stream);
+
+/* One decode step (parts 2 and 3).
+ *  q        device [B][Hq][d] bf16 query of the step.
+ *  k_bf16   device [B][Hkv][Lmax][d] bf16 keys (exact attention).
+ *  k_int8   device [B][Hkv][Lmax][d] int8 keys from sd_quantize_keys.
+ *  v        [B][Hkv][Lmax][d] bf16 values: device memory, or pinned host
+ *           memory (allocated with hipHostMalloc) when values_on_host = 1.
+ *  lengths  device [B] int32, each in [1, Lmax].
+ *  out      device [B][Hq][d] bf16 attention output.
+ *  kept_idx device [B][Hkv][sum_s keep_s] int32: stage s occupies offset
+ *           sum_{u<s} keep_u and holds its kept chunk starts (token
+ *           positions) ascending, padded with -1.
+ * Query head h uses KV head h / G.  A request with a length outside
+ * [1, Lmax] gets zero output and -1 indices, and raises the device flag. */
+sd_status sd_decode_step(sd_ctx* ctx, const uint16_t* q, const uint16_t* k_bf16,
+                         const int8_t* k_int8, const uint16_t* v, const int32_t* lengths,
+                         uint16_t* out, int32_t* kept_idx, void* stream);
+
+/* The step's query codes, for inspection: q8 device [B][Hq][d] int8 with one
+ * absmax scale per query head (same rounding as the keys), and q_group
+ * device [B][Hkv][d] int32, the sum of q8 over each KV head's group.  Either
+ * output may be NULL.  Uses the same device code as sd_decode_step. */
+sd_status sd_quantize_query(sd_ctx* ctx, const uint16_t* q, int8_t* q8, int32_t* q_group,
+                            void* stream);
+
+/* Copies the chunk scores stage `stage` (0-based) computed by the last
+ * sd_decode_step into device memory `dst`, laid out [B][Hkv][n_stage] int32
+ * (n_0 = ceil(Lmax / chunk_0), n_s = keep_{s-1} * chunk_{s-1} / chunk_s);
+ * entries of chunks that do not exist hold INT32_MIN.  For inspection. */
+sd_status sd_stage_scores(sd_ctx* ctx, int32_t stage, int32_t* dst, int64_t dst_len,
+                          void* stream);
+
+/* Number of int32 entries per (request, KV head) of sd_stage_scores. */
+int64_t sd_stage_candidates(const sd_ctx* ctx, int32_t stage);
+
+/* Synchronises `stream`, then reports SD_ERR_DEVICE_FLAG (and clears the
+ * flag) if a kernel flagged bad input since the last check, else SD_OK. */
+sd_status sd_check(sd_ctx* ctx, void* stream);
+
+/* Synchronises `stream` and fills *stats (host-value path counters; all
+ * zero when values_on_host = 0). */
+sd_status sd_get_stats(sd_ctx* ctx, sd_stats* stats, void* stream);
+
+/* Empties the value cache and zeroes the counters (enqueued on `stream`). */
+sd_status sd_reset_value_cache(sd_ctx* ctx, void* stream);
+
+/* Kernel kinds timed by the profiler. */
+enum {
+    SD_PROF_STAGE0 = 0,         /* pruning stage s is SD_PROF_STAGE0 + s */
+    SD_PROF_VALUE_CACHE = 4,    /* LRU update of the host-value path */
+    SD_PROF_ATTEND = 5,         /* sparse flash decode + log-sum-exp merge */
+    SD_PROF_QUANTIZE = 6,       /* the three kernels of sd_quantize_keys, as one interval */
+    SD_PROF_KINDS = 7
+};
+
+typedef struct sd_profile {
+    float ms[SD_PROF_KINDS];        /* summed device time between the bracketing events */
+    int32_t launches[SD_PROF_KINDS];
+} sd_profile;
+
+/* Starts timing: while active, every launch of a kind whose bit is set in
+ * `kind_mask` is bracketed by two HIP events recorded on the caller's
+ * stream, for at most `max_launches` launches.  Allocates the events (host
+ * call; not to be used where allocation is forbidden). */
+sd_status sd_profile_start(sd_ctx* ctx, uint32_t kind_mask, int32_t max_launches);
+
+/* Stops timing: synchronises the device, sums the elapsed times per kind
+ * into *out (may be NULL) and frees the events. */
+sd_status sd_profile_stop(sd_ctx* ctx, sd_profile* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SD_H_ */

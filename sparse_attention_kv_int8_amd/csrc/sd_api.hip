@@ -1,0 +1,361 @@
+// Host side of the C ABI declared in include/sd.h: validation, launch
+// geometry, the one workspace allocation, and the entry points.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "sd_device.h"
+#include "sd_internal.h"
+
+namespace {
+
+constexpr int kMaxCandidates = 15872;   // per-stage candidates (+ keep) held in LDS by the select
+constexpr int kMaxSamples = 64;         // chunk / stride
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+sd_status from_hip(hipError_t e) {
+    if (e == hipSuccess) return SD_OK;
+    if (e == hipErrorOutOfMemory) return SD_ERR_OUT_OF_MEMORY;
+    return SD_ERR_HIP;
+}
+
+// Validates the configuration and fills the geometry of `c` (no HIP calls).
+sd_status plan(const sd_config& cfg, sd_ctx* c) {
+    if (cfg.batch < 1 || cfg.num_kv_heads < 1 || cfg.num_q_heads < 1) return SD_ERR_INVALID_ARG;
+    if (cfg.num_q_heads % cfg.num_kv_heads != 0) return SD_ERR_INVALID_ARG;
+    const int G = cfg.num_q_heads / cfg.num_kv_heads;
+    if (G != 1 && G != 2 && G != 4) return SD_ERR_UNSUPPORTED;
+    if (cfg.head_dim != sd::kHeadDim) return SD_ERR_UNSUPPORTED;
+    if (cfg.max_context < 1 || cfg.max_context > (int64_t(1) << 31) - 8) return SD_ERR_INVALID_ARG;
+    if (cfg.num_stages < 1 || cfg.num_stages > SD_MAX_STAGES) return SD_ERR_INVALID_ARG;
+    if (cfg.sink < 0 || cfg.window < 0) return SD_ERR_INVALID_ARG;
+    if (!(cfg.softmax_scale >= 0.0f) || !std::isfinite(cfg.softmax_scale)) return SD_ERR_INVALID_ARG;
+    if (cfg.values_on_host != 0 && cfg.values_on_host != 1) return SD_ERR_INVALID_ARG;
+    if (int64_t(cfg.batch) * cfg.num_kv_heads > 65535) return SD_ERR_UNSUPPORTED;
+
+    c->cfg = cfg;
+    c->G = G;
+    c->S = cfg.num_stages;
+    c->Lmax = cfg.max_context;
+    int koff = 0;
+    for (int s = 0; s < cfg.num_stages; ++s) {
+        const sd_stage& in = cfg.stage[s];
+        if (in.chunk < 1 || in.stride < 1 || in.keep < 1) return SD_ERR_INVALID_ARG;
+        if (in.chunk % in.stride != 0) return SD_ERR_INVALID_ARG;
+        if (s > 0 && cfg.stage[s - 1].chunk % in.chunk != 0) return SD_ERR_INVALID_ARG;
+        sd::StageGeom& g = c->st[s];
+        g.chunk = in.chunk;
+        g.stride = in.stride;
+        g.keep = in.keep;
+        g.nsamp = in.chunk / in.stride;
+        if (g.nsamp > kMaxSamples) return SD_ERR_UNSUPPORTED;
+        const int64_t nc = s == 0 ? (cfg.max_context + in.chunk - 1) / in.chunk
+                                  : int64_t(cfg.stage[s - 1].keep) * (cfg.stage[s - 1].chunk / in.chunk);
+        if (nc + in.keep > kMaxCandidates) return SD_ERR_UNSUPPORTED;
+        g.ncand = int(nc);
+        g.koff = koff;
+        koff += in.keep;
+        // candidates per workgroup: 4 waves x (one or two batches of 8 row loads)
+        const int ns8 = (g.nsamp + 7) / 8;
+        const int ns8p = ns8 == 1 ? 1 : ns8 == 2 ? 2 : ns8 <= 4 ? 4 : 8;
+        const int cb = ns8p >= 8 ? 1 : 8 / ns8p;
+        const int cpw = s == 0 ? 2 * cb : cb;
+        g.per_wg = 4 * cpw;
+        g.nwg = (g.ncand + g.per_wg - 1) / g.per_wg;
+    }
+    if (cfg.stage[cfg.num_stages - 1].chunk % 8 != 0) return SD_ERR_UNSUPPORTED;
+    if (koff > 65535) return SD_ERR_UNSUPPORTED;
+    c->keep_total = koff;
+    const sd_stage& last = cfg.stage[cfg.num_stages - 1];
+    const int64_t mb = int64_t(last.keep) * (last.chunk / 8) + (cfg.sink + 7) / 8 + (cfg.window + 7) / 8 + 1;
+    if (mb > (int64_t(1) << 20)) return SD_ERR_UNSUPPORTED;
+    c->max_blocks = int(mb);
+    const int BH = cfg.batch * cfg.num_kv_heads;
+    int ns = (512 + BH - 1) / BH;
+    ns = ns < 1 ? 1 : ns > 64 ? 64 : ns;
+    const int cap = (c->max_blocks + 3) / 4;
+    c->nsplit = ns > cap ? cap : ns;
+    const float scale = cfg.softmax_scale > 0.0f ? cfg.softmax_scale : 1.0f / std::sqrt(float(cfg.head_dim));
+    c->scale_log2 = scale * 1.4426950408889634f;
+
+    if (cfg.values_on_host) {
+        if (cfg.value_cache_tokens < 8 || cfg.value_cache_tokens % 8 != 0) return SD_ERR_INVALID_ARG;
+        if (cfg.value_cache_tokens / 8 < c->max_blocks) return SD_ERR_INVALID_ARG;
+        if (cfg.value_cache_tokens / 8 > (int64_t(1) << 24)) return SD_ERR_UNSUPPORTED;
+    }
+    return SD_OK;
+}
+
+// Brackets one launch with profiling events when its kind is being timed.
+template <class F>
+hipError_t timed(sd_ctx* c, int kind, hipStream_t s, F&& launch) {
+    const bool on = c->prof_ev && ((c->prof_mask >> kind) & 1u) && c->prof_n < c->prof_max;
+    hipError_t e = hipSuccess;
+    if (on) e = hipEventRecord(c->prof_ev[2 * c->prof_n], s);
+    if (e == hipSuccess) e = launch();
+    if (on && e == hipSuccess) {
+        e = hipEventRecord(c->prof_ev[2 * c->prof_n + 1], s);
+        c->prof_kind[c->prof_n] = int8_t(kind);
+        ++c->prof_n;
+    }
+    return e;
+}
+
+void free_profiler(sd_ctx* c) {
+    if (c->prof_ev) {
+        for (int i = 0; i < 2 * c->prof_max; ++i)
+            if (c->prof_ev[i]) (void)hipEventDestroy(c->prof_ev[i]);
+        delete[] c->prof_ev;
+        delete[] c->prof_kind;
+    }
+    c->prof_ev = nullptr;
+    c->prof_kind = nullptr;
+    c->prof_max = c->prof_n = 0;
+    c->prof_mask = 0;
+}
+
+struct Carver {
+    size_t off = 0;
+    template <class T>
+    size_t take(size_t count) {
+        size_t o = off;
+        off = round_up(off + count * sizeof(T), 256);
+        return o;
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* sd_status_string(sd_status s) {
+    switch (s) {
+        case SD_OK: return "ok";
+        case SD_ERR_INVALID_ARG: return "invalid argument";
+        case SD_ERR_UNSUPPORTED: return "unsupported configuration";
+        case SD_ERR_OUT_OF_MEMORY: return "out of device memory";
+        case SD_ERR_HIP: return "HIP runtime error";
+        case SD_ERR_DEVICE_FLAG: return "device flagged bad input (length outside [1, max_context])";
+    }
+    return "unknown status";
+}
+
+sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
+    if (!out) return SD_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (!cfg) return SD_ERR_INVALID_ARG;
+    sd_ctx* c = new (std::nothrow) sd_ctx();
+    if (!c) return SD_ERR_OUT_OF_MEMORY;
+    sd_status st = plan(*cfg, c);
+    if (st != SD_OK) { delete c; return st; }
+    if (hipGetDevice(&c->device) != hipSuccess) { delete c; return SD_ERR_HIP; }
+
+    const size_t B = size_t(cfg->batch), H = size_t(cfg->num_kv_heads), BH = B * H;
+    Carver cv;
+    size_t o_scores[SD_MAX_STAGES];
+    for (int s = 0; s < c->S; ++s) o_scores[s] = cv.take<int32_t>(BH * c->st[s].ncand);
+    const size_t o_qg = cv.take<int32_t>(BH * sd::kHeadDim);
+    const size_t o_blocks = cv.take<uint32_t>(BH * c->max_blocks);
+    const size_t o_nblocks = cv.take<int32_t>(BH);
+    const size_t o_part = cv.take<float>(BH * c->nsplit * c->G * (2 + sd::kHeadDim));
+    const size_t o_cnt = cv.take<unsigned>((SD_MAX_STAGES + 1) * BH);
+    const size_t o_abs = cv.take<unsigned>(BH);
+    const size_t o_flag = cv.take<int32_t>(1);
+    size_t o_vc[10] = {0};
+    if (cfg->values_on_host) {
+        c->vc.slots = int32_t(cfg->value_cache_tokens / 8);
+        c->vc.nblk_max = int32_t((c->Lmax + 7) / 8);
+        o_vc[0] = cv.take<uint16_t>(BH * size_t(c->vc.slots) * 8 * sd::kHeadDim);
+        o_vc[1] = cv.take<int32_t>(BH * size_t(c->vc.nblk_max));
+        o_vc[2] = cv.take<int32_t>(BH * size_t(c->vc.slots));
+        o_vc[3] = cv.take<int32_t>(BH * size_t(c->vc.slots));
+        o_vc[4] = cv.take<int32_t>(BH);
+        o_vc[5] = cv.take<int32_t>(2 * BH * size_t(c->vc.slots));
+        o_vc[6] = cv.take<int32_t>(BH * size_t(c->max_blocks));
+        o_vc[7] = cv.take<int32_t>(BH * size_t(c->max_blocks));
+        o_vc[8] = cv.take<int64_t>(sd::kVcCounters);
+    }
+    c->ws_bytes = cv.off;
+    hipError_t e = hipMalloc(&c->ws, c->ws_bytes);
+    if (e != hipSuccess) { (void)hipGetLastError(); delete c; return from_hip(e); }
+    char* base = static_cast<char*>(c->ws);
+    for (int s = 0; s < c->S; ++s) c->scores[s] = reinterpret_cast<int32_t*>(base + o_scores[s]);
+    c->qgroup = reinterpret_cast<int32_t*>(base + o_qg);
+    c->blocks = reinterpret_cast<uint32_t*>(base + o_blocks);
+    c->nblocks = reinterpret_cast<int32_t*>(base + o_nblocks);
+    c->part = reinterpret_cast<float*>(base + o_part);
+    c->counters = reinterpret_cast<unsigned*>(base + o_cnt);
+    c->absmax_bits = reinterpret_cast<unsigned*>(base + o_abs);
+    c->flag = reinterpret_cast<int32_t*>(base + o_flag);
+    if (cfg->values_on_host) {
+        c->vc.pool = reinterpret_cast<uint16_t*>(base + o_vc[0]);
+        c->vc.page = reinterpret_cast<int32_t*>(base + o_vc[1]);
+        c->vc.slot_block = reinterpret_cast<int32_t*>(base + o_vc[2]);
+        c->vc.slot_last = reinterpret_cast<int32_t*>(base + o_vc[3]);
+        c->vc.used = reinterpret_cast<int32_t*>(base + o_vc[4]);
+        c->vc.order = reinterpret_cast<int32_t*>(base + o_vc[5]);
+        c->vc.evicted = reinterpret_cast<int32_t*>(base + o_vc[6]);
+        c->vc.blk_slot = reinterpret_cast<int32_t*>(base + o_vc[7]);
+        c->vc.counters = reinterpret_cast<int64_t*>(base + o_vc[8]);
+    }
+    // Counters, flag and score buffers start defined; this is setup, outside any step.
+    e = hipMemset(c->ws, 0, c->ws_bytes);
+    if (e == hipSuccess && cfg->values_on_host) e = sd::launch_value_cache_reset(c, nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) { (void)hipFree(c->ws); delete c; return from_hip(e); }
+    *out = c;
+    return SD_OK;
+}
+
+void sd_destroy(sd_ctx* c) {
+    if (!c) return;
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != c->device) (void)hipSetDevice(c->device);
+    (void)hipDeviceSynchronize();
+    free_profiler(c);
+    (void)hipFree(c->ws);
+    if (cur != c->device && cur >= 0) (void)hipSetDevice(cur);
+    delete c;
+}
+
+sd_status sd_quantize_keys(sd_ctx* c, const uint16_t* k, const int32_t* lengths, int8_t* k8, float* absmax,
+                           void* stream) {
+    if (!c || !k || !lengths || !k8) return SD_ERR_INVALID_ARG;
+    if (!aligned16(k) || !aligned16(k8)) return SD_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return from_hip(timed(c, SD_PROF_QUANTIZE, s, [&] { return sd::launch_quantize_keys(c, k, lengths, k8, absmax, s); }));
+}
+
+sd_status sd_quantize_query(sd_ctx* c, const uint16_t* q, int8_t* q8, int32_t* qg, void* stream) {
+    if (!c || !q) return SD_ERR_INVALID_ARG;
+    if (!aligned16(q)) return SD_ERR_INVALID_ARG;
+    return from_hip(sd::launch_quantize_query(c, q, q8, qg, static_cast<hipStream_t>(stream)));
+}
+
+sd_status sd_decode_step(sd_ctx* c, const uint16_t* q, const uint16_t* k, const int8_t* k8, const uint16_t* v,
+                         const int32_t* lengths, uint16_t* out, int32_t* kept, void* stream) {
+    if (!c || !q || !k || !k8 || !v || !lengths || !out || !kept) return SD_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(k8) || !aligned16(v) || !aligned16(out))
+        return SD_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t* vk = v;
+    if (c->cfg.values_on_host) {
+        // v is pinned host memory: the kernels read it through its device alias
+        if (v != c->vhost_key) {
+            void* dev = nullptr;
+            if (hipHostGetDevicePointer(&dev, const_cast<uint16_t*>(v), 0) != hipSuccess || !dev) {
+                (void)hipGetLastError();
+                return SD_ERR_INVALID_ARG;
+            }
+            c->vhost_key = v;
+            c->vhost_dev = static_cast<const uint16_t*>(dev);
+        }
+        vk = c->vhost_dev;
+    }
+    hipError_t e = hipSuccess;
+    for (int st = 0; st < c->S && e == hipSuccess; ++st)
+        e = timed(c, SD_PROF_STAGE0 + st, s, [&] { return sd::launch_prune_stage(c, st, q, k8, lengths, kept, s); });
+    if (e == hipSuccess && c->cfg.values_on_host)
+        e = timed(c, SD_PROF_VALUE_CACHE, s, [&] { return sd::launch_value_cache_update(c, s); });
+    if (e == hipSuccess)
+        e = timed(c, SD_PROF_ATTEND, s, [&] { return sd::launch_attend(c, q, k, vk, lengths, out, s); });
+    return from_hip(e);
+}
+
+int64_t sd_stage_candidates(const sd_ctx* c, int32_t stage) {
+    if (!c || stage < 0 || stage >= c->S) return -1;
+    return c->st[stage].ncand;
+}
+
+sd_status sd_stage_scores(sd_ctx* c, int32_t stage, int32_t* dst, int64_t dst_len, void* stream) {
+    if (!c || !dst || stage < 0 || stage >= c->S) return SD_ERR_INVALID_ARG;
+    const int64_t n = int64_t(c->cfg.batch) * c->cfg.num_kv_heads * c->st[stage].ncand;
+    if (dst_len < n) return SD_ERR_INVALID_ARG;
+    return from_hip(hipMemcpyAsync(dst, c->scores[stage], size_t(n) * 4, hipMemcpyDeviceToDevice,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+sd_status sd_check(sd_ctx* c, void* stream) {
+    if (!c) return SD_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return from_hip(e);
+    int32_t flag = 0;
+    e = hipMemcpy(&flag, c->flag, sizeof(flag), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return from_hip(e);
+    if (flag) {
+        e = hipMemset(c->flag, 0, sizeof(int32_t));
+        if (e != hipSuccess) return from_hip(e);
+        return SD_ERR_DEVICE_FLAG;
+    }
+    return SD_OK;
+}
+
+sd_status sd_get_stats(sd_ctx* c, sd_stats* out, void* stream) {
+    if (!c || !out) return SD_ERR_INVALID_ARG;
+    std::memset(out, 0, sizeof(*out));
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return from_hip(e);
+    if (!c->cfg.values_on_host) return SD_OK;
+    int64_t h[sd::kVcCounters];
+    e = hipMemcpy(h, c->vc.counters, sizeof(h), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return from_hip(e);
+    out->steps = h[0];
+    out->blocks_needed = h[1];
+    out->hits = h[2];
+    out->misses = h[3];
+    out->h2d_bytes = h[3] * 8 * sd::kHeadDim * 2;
+    if (h[0] > 0) {
+        const int par = int((h[0] - 1) & 1);
+        out->last_needed = h[4 + 4 * par];
+        out->last_hits = h[5 + 4 * par];
+        out->last_misses = h[6 + 4 * par];
+    }
+    return SD_OK;
+}
+
+sd_status sd_reset_value_cache(sd_ctx* c, void* stream) {
+    if (!c) return SD_ERR_INVALID_ARG;
+    if (!c->cfg.values_on_host) return SD_OK;
+    return from_hip(sd::launch_value_cache_reset(c, static_cast<hipStream_t>(stream)));
+}
+
+sd_status sd_profile_start(sd_ctx* c, uint32_t kind_mask, int32_t max_launches) {
+    if (!c || max_launches < 1 || max_launches > (1 << 20)) return SD_ERR_INVALID_ARG;
+    free_profiler(c);
+    c->prof_ev = new (std::nothrow) hipEvent_t[2 * size_t(max_launches)]();
+    c->prof_kind = new (std::nothrow) int8_t[size_t(max_launches)]();
+    if (!c->prof_ev || !c->prof_kind) { free_profiler(c); return SD_ERR_OUT_OF_MEMORY; }
+    c->prof_max = max_launches;
+    for (int i = 0; i < 2 * max_launches; ++i) {
+        if (hipEventCreate(&c->prof_ev[i]) != hipSuccess) { free_profiler(c); return SD_ERR_HIP; }
+    }
+    c->prof_mask = kind_mask;
+    c->prof_n = 0;
+    return SD_OK;
+}
+
+sd_status sd_profile_stop(sd_ctx* c, sd_profile* out) {
+    if (!c) return SD_ERR_INVALID_ARG;
+    sd_profile r;
+    std::memset(&r, 0, sizeof(r));
+    hipError_t e = c->prof_ev ? hipDeviceSynchronize() : hipSuccess;
+    for (int i = 0; e == hipSuccess && i < c->prof_n; ++i) {
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, c->prof_ev[2 * i], c->prof_ev[2 * i + 1]);
+        r.ms[c->prof_kind[i]] += ms;
+        r.launches[c->prof_kind[i]] += 1;
+    }
+    free_profiler(c);
+    if (out) *out = r;
+    return from_hip(e);
+}
+
+}  // extern "C"

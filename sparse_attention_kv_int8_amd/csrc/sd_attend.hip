@@ -1,0 +1,253 @@
+// Exact GQA attention of the step's query over the attended token set T.
+//
+// Source: page "KV Cache 与长上下文推理", section "KV Cache 回顾": the decode
+// attention softmax(q K^T / sqrt(d_k)) V, here restricted to T (kept chunks
+// plus sink and window); the GQA table of section "KV Cache 压缩技术" maps
+// query head h to KV head h / G.  The score matrix is never written to
+// memory: each split keeps a running max, a running sum and an fp32
+// accumulator (the tiling idea the InfiniteHiP article credits to
+// FlashAttention, section "从赫赫有名的注意力机制说起"), and the last split
+// of each (request, KV head) merges all splits by log-sum-exp.
+//
+// Workgroup (split, KV head, request) = 4 waves; waves take the split's
+// blocks round-robin.  For one 8-token block a wave computes the G scores of
+// every token (lane = token * 8 + 16-dim slice; bf16 pair dot products,
+// DPP sum over the 8 slice lanes), takes the block max per head (uniform
+// over the wave), then accumulates P V with lane l owning output dims 2l and
+// 2l+1, reading each value row with one coalesced dword per lane.
+#include "sd_device.h"
+#include "sd_internal.h"
+
+namespace sd {
+
+constexpr int kAttnThreads = 256;
+constexpr int kAttnWaves = kAttnThreads / kWave;
+constexpr int kPartStride = 2 + kHeadDim;     // m, l, acc[128] per (split, head)
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+struct AttendParams {
+    const uint16_t* q;        // [B][Hq][d]
+    const uint16_t* k;        // [B][Hkv][Lmax][d]
+    const uint16_t* v;        // [B][Hkv][Lmax][d] values (device, or the device alias of pinned host memory)
+    uint16_t* vpool;          // [B][Hkv][slots][8][d] (host-value path)
+    const int32_t* blk_slot;  // [B][Hkv][max_blocks]   (host-value path)
+    int vslots;
+    const int32_t* lengths;
+    const uint32_t* blocks;   // [B][Hkv][max_blocks]
+    const int32_t* nblocks;   // [B][Hkv]
+    int max_blocks;
+    float* part;              // [B][Hkv][nsplit][G][2 + d]
+    unsigned* counter;        // [B][Hkv]
+    int nsplit;
+    int64_t Lmax;
+    int Hq, Hkv;
+    float scale_log2;
+    uint16_t* out;            // [B][Hq][d]
+};
+
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// exp2(a - m) with exp2(-inf - m) = 0 and no NaN when both are -inf.
+__device__ __forceinline__ float rescale(float a, float m) {
+    return a == -INFINITY ? 0.0f : fast_exp2(a - m);
+}
+
+template <int G, bool HOSTV>
+__global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendParams p) {
+    __shared__ float wm[kAttnWaves][G];
+    __shared__ float wl[kAttnWaves][G];
+    __shared__ float wacc[kAttnWaves][G][kHeadDim];
+    __shared__ unsigned last_flag;
+
+    const int sp = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    const int bj = b * p.Hkv + j;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tok = lane >> 3, sl = lane & 7;
+    const int nb = p.nblocks[bj];
+    const int per = (nb + p.nsplit - 1) / p.nsplit;
+    const int r0 = sp * per, r1 = min(nb, r0 + per);
+
+    // this lane's 16 query dims of every head of the group (bf16 pairs)
+    uint32_t qv[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const u32x4* qp = reinterpret_cast<const u32x4*>(p.q + (int64_t(b) * p.Hq + j * G + h) * kHeadDim + sl * 16);
+        const u32x4 a = qp[0], c = qp[1];
+        qv[h][0] = a.x; qv[h][1] = a.y; qv[h][2] = a.z; qv[h][3] = a.w;
+        qv[h][4] = c.x; qv[h][5] = c.y; qv[h][6] = c.z; qv[h][7] = c.w;
+    }
+    float m[G], lsum[G], acc0[G], acc1[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) { m[h] = -INFINITY; lsum[h] = 0.f; acc0[h] = 0.f; acc1[h] = 0.f; }
+
+    const uint16_t* kbase = p.k + int64_t(bj) * p.Lmax * kHeadDim;
+    const uint16_t* vbase = p.v + int64_t(bj) * p.Lmax * kHeadDim;
+    const int64_t L = p.lengths[b];
+    const uint32_t* blist = p.blocks + int64_t(bj) * p.max_blocks;
+
+    for (int r = r0 + wave; r < r1; r += kAttnWaves) {
+        const uint32_t e = blist[r];
+        const int64_t t0 = int64_t(e >> 8) * 8;
+        const uint32_t mask = e & 0xffu;
+        const bool in = (mask >> tok) & 1u;
+        // keys: 32 bytes of token t0 + tok
+        u32x4 k0 = {0, 0, 0, 0}, k1 = {0, 0, 0, 0};
+        if (in) {
+            const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + (t0 + tok) * kHeadDim + sl * 16);
+            k0 = __builtin_nontemporal_load(kp);
+            k1 = __builtin_nontemporal_load(kp + 1);
+        }
+        // values: dims 2*lane, 2*lane+1 of the 8 rows
+        uint32_t vv[8];
+        if (HOSTV) {
+            const int32_t se = p.blk_slot[int64_t(bj) * p.max_blocks + r];
+            uint32_t* prow = reinterpret_cast<uint32_t*>(p.vpool + (int64_t(bj) * p.vslots + (se & ~kVcMissBit)) * 8 * kHeadDim);
+            if (se & kVcMissBit) {
+                // miss: the whole block (rows t < L) comes from host memory and fills its slot
+                const uint32_t* hrow = reinterpret_cast<const uint32_t*>(p.v + (int64_t(bj) * p.Lmax + t0) * kHeadDim);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    vv[u] = (t0 + u < L) ? hrow[u * (kHeadDim / 2) + lane] : 0u;
+                    if (t0 + u < L) prow[u * (kHeadDim / 2) + lane] = vv[u];
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) vv[u] = ((mask >> u) & 1u) ? prow[u * (kHeadDim / 2) + lane] : 0u;
+            }
+        } else {
+            const uint32_t* vrow = reinterpret_cast<const uint32_t*>(vbase + t0 * kHeadDim);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                vv[u] = ((mask >> u) & 1u) ? __builtin_nontemporal_load(vrow + u * (kHeadDim / 2) + lane) : 0u;
+        }
+
+        float z[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float s = dot2bf(qv[h][0], k0.x, 0.f);
+            s = dot2bf(qv[h][1], k0.y, s);
+            s = dot2bf(qv[h][2], k0.z, s);
+            s = dot2bf(qv[h][3], k0.w, s);
+            s = dot2bf(qv[h][4], k1.x, s);
+            s = dot2bf(qv[h][5], k1.y, s);
+            s = dot2bf(qv[h][6], k1.z, s);
+            s = dot2bf(qv[h][7], k1.w, s);
+            s = sum8_f(s);
+            z[h] = in ? s * p.scale_log2 : -INFINITY;
+        }
+        float pw[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float bm = max_groups_f(z[h]);
+            const float mn = fmaxf(m[h], bm);
+            const float alpha = rescale(m[h], mn);
+            pw[h] = in ? fast_exp2(z[h] - mn) : 0.f;
+            lsum[h] = lsum[h] * alpha + pw[h];
+            acc0[h] *= alpha;
+            acc1[h] *= alpha;
+            m[h] = mn;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if ((mask >> u) & 1u) {
+                const float v0 = bf16_lo(vv[u]), v1 = bf16_hi(vv[u]);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float pu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw[h]), u * 8));
+                    acc0[h] = fmaf(pu, v0, acc0[h]);
+                    acc1[h] = fmaf(pu, v1, acc1[h]);
+                }
+            }
+        }
+    }
+
+    // wave totals: lsum is per token group (identical in its 8 lanes)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float lt = sum_groups_f(lsum[h]);
+        if (lane == 0) { wm[wave][h] = m[h]; wl[wave][h] = lt; }
+        wacc[wave][h][2 * lane] = acc0[h];
+        wacc[wave][h][2 * lane + 1] = acc1[h];
+    }
+    __syncthreads();
+    float* part = p.part + (int64_t(bj) * p.nsplit + sp) * G * kPartStride;
+    for (int o = threadIdx.x; o < G * kHeadDim; o += kAttnThreads) {
+        const int h = o / kHeadDim, dd = o % kHeadDim;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, wm[w][h]);
+        float a = 0.f, l = 0.f;
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w) {
+            const float f = rescale(wm[w][h], M);
+            a = fmaf(wacc[w][h][dd], f, a);
+            l = fmaf(wl[w][h], f, l);
+        }
+        part[h * kPartStride + 2 + dd] = a;
+        if (dd == 0) { part[h * kPartStride] = M; part[h * kPartStride + 1] = l; }
+    }
+
+    if (!arrive_last(p.counter + bj, unsigned(p.nsplit), &last_flag)) return;
+
+    // ---- last split of this (request, KV head): log-sum-exp merge ----
+    const float* pb = p.part + int64_t(bj) * p.nsplit * G * kPartStride;
+    for (int o = threadIdx.x; o < G * kHeadDim; o += kAttnThreads) {
+        const int h = o / kHeadDim, dd = o % kHeadDim;
+        float M = -INFINITY;
+        for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, pb[(s * G + h) * kPartStride]);
+        float a = 0.f, l = 0.f;
+        for (int s = 0; s < p.nsplit; ++s) {
+            const float* ps = pb + (s * G + h) * kPartStride;
+            const float f = rescale(ps[0], M);
+            a = fmaf(ps[2 + dd], f, a);
+            l = fmaf(ps[1], f, l);
+        }
+        const float o_val = l > 0.f ? a / l : 0.f;
+        p.out[(int64_t(b) * p.Hq + j * G + h) * kHeadDim + dd] = f32_to_bf16_rne(o_val);
+    }
+}
+
+template <int G>
+static void launch_g(const AttendParams& p, dim3 grid, bool hostv, hipStream_t s) {
+    if (hostv) sd_flash_decode_kernel<G, true><<<grid, kAttnThreads, 0, s>>>(p);
+    else sd_flash_decode_kernel<G, false><<<grid, kAttnThreads, 0, s>>>(p);
+}
+
+hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const int32_t* lengths, uint16_t* out, hipStream_t s) {
+    AttendParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.vpool = c->vc.pool;
+    p.blk_slot = c->vc.blk_slot;
+    p.vslots = c->vc.slots;
+    p.lengths = lengths;
+    p.blocks = c->blocks;
+    p.nblocks = c->nblocks;
+    p.max_blocks = c->max_blocks;
+    p.part = c->part;
+    p.counter = c->counters + size_t(SD_MAX_STAGES) * c->cfg.batch * c->cfg.num_kv_heads;
+    p.nsplit = c->nsplit;
+    p.Lmax = c->Lmax;
+    p.Hq = c->cfg.num_q_heads;
+    p.Hkv = c->cfg.num_kv_heads;
+    p.scale_log2 = c->scale_log2;
+    p.out = out;
+    dim3 grid(c->nsplit, c->cfg.num_kv_heads, c->cfg.batch);
+    const bool hostv = c->cfg.values_on_host != 0;
+    switch (c->G) {
+        case 1: launch_g<1>(p, grid, hostv, s); break;
+        case 2: launch_g<2>(p, grid, hostv, s); break;
+        default: launch_g<4>(p, grid, hostv, s); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sd

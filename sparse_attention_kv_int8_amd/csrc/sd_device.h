@@ -1,0 +1,192 @@
+// Device helpers shared by the sparse decode kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sd {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kHeadDim = 128;
+
+// ---------------------------------------------------------------- bf16 ----
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+
+// Symmetric int8 code of one bf16 value: rint((127 * x) / scale).
+// 127 * x is exact in fp32 (bf16 carries 8 significant bits) and the
+// division is correctly rounded (the library is built with
+// -fhip-fp32-correctly-rounded-divide-sqrt), so the code equals the exact
+// rational round-half-even.  scale == 0 gives 0.
+__device__ __forceinline__ int code_of(float x, float scale) {
+    if (scale == 0.0f) return 0;
+    return int(__builtin_rintf((127.0f * x) / scale));
+}
+
+// ----------------------------------------------------------- DPP moves ----
+// quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
+// row_half_mirror (lane i <-> 7 - i inside each group of 8),
+// row_ror:8 (lane ^ 8 inside each row of 16).
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppRor8 = 0x128;
+
+// Sum over the 8 consecutive lanes 8g..8g+7; every lane of the group gets it.
+__device__ __forceinline__ int sum8_i(int v) {
+    v += dpp_i<kDppXor1>(v);
+    v += dpp_i<kDppXor2>(v);
+    v += dpp_i<kDppHalfMirror>(v);
+    return v;
+}
+__device__ __forceinline__ float sum8_f(float v) {
+    v += dpp_f<kDppXor1>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    return v;
+}
+
+// Max / sum across the 8 lane groups of a wave (lanes differing in bits 3..5).
+__device__ __forceinline__ int max_groups_i(int v) {
+    v = max(v, dpp_i<kDppRor8>(v));
+    v = max(v, __shfl_xor(v, 16));
+    v = max(v, __shfl_xor(v, 32));
+    return v;
+}
+__device__ __forceinline__ float max_groups_f(float v) {
+    v = fmaxf(v, dpp_f<kDppRor8>(v));
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+__device__ __forceinline__ float sum_groups_f(float v) {
+    v += dpp_f<kDppRor8>(v);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ unsigned wave_max_u(unsigned v) {
+    for (int o = 32; o > 0; o >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, o));
+    return v;
+}
+__device__ __forceinline__ unsigned wave_min_u(unsigned v) {
+    for (int o = 32; o > 0; o >>= 1) v = min(v, (unsigned)__shfl_xor((int)v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ unsigned wave_incl_scan(unsigned v) {
+    const int lane = threadIdx.x & 63;
+    for (int o = 1; o < 64; o <<= 1) {
+        unsigned t = (unsigned)__shfl_up((int)v, o);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over the block (NT threads, NT % 64 == 0).
+// `tmp` holds NT/64 + 1 words of LDS; returns the block total in *total.
+template <int NT>
+__device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* tmp, unsigned* total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    constexpr int NW = NT / 64;
+    unsigned incl = wave_incl_scan(v);
+    if (lane == 63) tmp[wid] = incl;
+    __syncthreads();
+    if (wid == 0) {
+        unsigned w = lane < NW ? tmp[lane] : 0u;
+        unsigned wi = wave_incl_scan(w);
+        if (lane < NW) tmp[lane] = wi - w;
+        if (lane == NW - 1) tmp[NW] = wi;
+    }
+    __syncthreads();
+    unsigned r = tmp[wid] + incl - v;
+    *total = tmp[NW];
+    __syncthreads();
+    return r;
+}
+
+// "Last workgroup done" hand-off.  Every thread has written its results;
+// all of them are made visible at device scope, then one atomic per
+// workgroup counts arrivals.  Returns true in every thread of the last
+// arriving workgroup, which also re-arms the counter for the next launch
+// and acquires the other workgroups' results.
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected, unsigned* lds_flag) {
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned old = atomicAdd(counter, 1u);
+        bool last = old == expected - 1;
+        if (last) atomicExch(counter, 0u);
+        *lds_flag = last ? 1u : 0u;
+    }
+    __syncthreads();
+    bool last = *lds_flag != 0;
+    if (last) __threadfence();
+    return last;
+}
+
+// |x| of the two bf16 values of a dword, as bit patterns; max of the two.
+__device__ __forceinline__ unsigned abs_bits2(uint32_t w) {
+    return max(w & 0x7fffu, (w >> 16) & 0x7fffu);
+}
+
+// ---------------------------------------------------------------------------
+// Query: one absmax scale per query head, codes with the same rounding as the
+// keys, and the group sum Q_j over the G query heads of KV head j (GQA
+// table of "KV Cache 与长上下文推理", section "KV Cache 压缩技术").
+// Wave w < G handles query head j*G + w; lane l handles dims 2l and 2l+1.
+// Qlds must hold 128 ints; the caller's block has at least G waves.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void group_query_codes(const uint16_t* __restrict__ q_b, int j, int G, int* Qlds,
+                                  int8_t* __restrict__ q8_b) {
+    if (threadIdx.x < kHeadDim) Qlds[threadIdx.x] = 0;
+    __syncthreads();
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (w < G) {
+        const int h = j * G + w;
+        const uint32_t pr = reinterpret_cast<const uint32_t*>(q_b + h * kHeadDim)[lane];
+        const unsigned ab = wave_max_u(abs_bits2(pr));
+        const float amax = bf16_to_f32(uint16_t(ab));
+        const int c0 = code_of(bf16_lo(pr), amax), c1 = code_of(bf16_hi(pr), amax);
+        atomicAdd(Qlds + 2 * lane, c0);
+        atomicAdd(Qlds + 2 * lane + 1, c1);
+        if (q8_b) {
+            uint16_t two = uint16_t((uint32_t(c0) & 0xffu) | ((uint32_t(c1) & 0xffu) << 8));
+            reinterpret_cast<uint16_t*>(q8_b + h * kHeadDim)[lane] = two;
+        }
+    }
+    __syncthreads();
+}
+
+}  // namespace sd

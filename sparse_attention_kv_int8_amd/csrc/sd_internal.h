@@ -1,0 +1,89 @@
+// Library-internal context and kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sd.h"
+
+namespace sd {
+
+// Per-stage launch geometry.
+struct StageGeom {
+    int chunk, stride, keep;
+    int nsamp;          // samples per chunk = chunk / stride
+    int ncand;          // candidates per (request, KV head)
+    int koff;           // offset of this stage in kept_idx
+    int per_wg;         // candidates scored per workgroup
+    int nwg;            // workgroups per (request, KV head)
+};
+
+constexpr int kVcCounters = 16;
+constexpr int32_t kVcMissBit = int32_t(0x40000000);
+
+// Device-side state of the host-value path (values_on_host = 1).
+struct ValueCache {
+    int32_t slots;          // slots (8-token blocks) per (request, KV head)
+    int32_t nblk_max;       // ceil(Lmax / 8): page-table entries per (b, j)
+    uint16_t* pool;         // [B][Hkv][slots][8][d] bf16 value blocks
+    int32_t* page;          // [B][Hkv][nblk_max] slot of a block or -1
+    int32_t* slot_block;    // [B][Hkv][slots] block held by a slot or -1
+    int32_t* slot_last;     // [B][Hkv][slots] last step the slot was used
+    int32_t* used;          // [B][Hkv] slots filled so far
+    int32_t* order;         // [2][B][Hkv][slots] recency order (oldest first), double buffered
+    int32_t* evicted;       // [B][Hkv][max_blocks] slots evicted this step, oldest first
+    int32_t* blk_slot;      // [B][Hkv][max_blocks] slot of each attended block (| kVcMissBit on a miss)
+    int64_t* counters;      // [16]: steps, needed, hits, misses, then per step parity p:
+                            //       [4+4p] needed, [5+4p] hits, [6+4p] misses
+};
+
+}  // namespace sd
+
+struct sd_ctx {
+    sd_config cfg;
+    int device;
+    int G;                  // query heads per KV head
+    int S;                  // stages
+    int64_t Lmax;
+    int keep_total;
+    int max_blocks;         // attended 8-token blocks per (request, KV head)
+    int nsplit;             // flash-decode splits per (request, KV head)
+    float scale_log2;       // softmax_scale * log2(e)
+    sd::StageGeom st[SD_MAX_STAGES];
+    size_t select_lds;      // dynamic LDS bytes of the stage kernels
+
+    // device workspace (one allocation)
+    void* ws;
+    size_t ws_bytes;
+    int32_t* scores[SD_MAX_STAGES];   // [B][Hkv][ncand]
+    int32_t* qgroup;                  // [B][Hkv][d] group query sums
+    uint32_t* blocks;                 // [B][Hkv][max_blocks] (block << 8) | token mask
+    int32_t* nblocks;                 // [B][Hkv]
+    float* part;                      // [B][Hkv][nsplit][G][2 + d]
+    unsigned* counters;               // [SD_MAX_STAGES + 1][B][Hkv]
+    unsigned* absmax_bits;            // [B][Hkv]
+    int32_t* flag;                    // device error flag
+    sd::ValueCache vc;
+    int64_t vc_step;                  // steps applied to the value cache since its reset
+    const void* vhost_key;            // last host value pointer seen, and its device alias
+    const uint16_t* vhost_dev;
+    // profiling (sd_profile_start / sd_profile_stop)
+    uint32_t prof_mask;
+    int32_t prof_max, prof_n;
+    hipEvent_t* prof_ev;              // [2 * prof_max]
+    int8_t* prof_kind;                // [prof_max]
+};
+
+namespace sd {
+
+hipError_t launch_quantize_keys(sd_ctx* c, const uint16_t* k, const int32_t* lengths, int8_t* k8,
+                                float* absmax, hipStream_t s);
+hipError_t launch_quantize_query(sd_ctx* c, const uint16_t* q, int8_t* q8, int32_t* qg, hipStream_t s);
+hipError_t launch_prune_stage(sd_ctx* c, int stage, const uint16_t* q, const int8_t* k8,
+                              const int32_t* lengths, int32_t* kept, hipStream_t s);
+hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const int32_t* lengths, uint16_t* out, hipStream_t s);
+hipError_t launch_value_cache_update(sd_ctx* c, hipStream_t s);
+hipError_t launch_value_cache_reset(sd_ctx* c, hipStream_t s);
+
+}  // namespace sd

@@ -1,0 +1,140 @@
+// Symmetric int8 quantisation of the key cache and of the step's query.
+//
+// Keys: one absmax scale per (request, KV head) over its valid rows; codes
+// rint(127 k / a).  Sources: summary page of "HCAttention: Extreme KV cache
+// compression via heterogeneous attention computing for LLMs", section 引言
+// (keys quantised and kept on the GPU for scoring); page "KV Cache 与长上下文
+// 推理", section "KV Cache 压缩技术" (INT8 key cache).
+//
+// Both passes stream the bf16 cache with 16-byte loads, 16 lanes per
+// 256-byte row.  The absmax pass works on bf16 bit patterns (|x| ordering is
+// the ordering of the low 15 bits for finite values).
+#include "sd_device.h"
+#include "sd_internal.h"
+
+namespace sd {
+
+namespace {
+
+constexpr int kQuantThreads = 256;
+constexpr int kQuantRowsPerWg = 1024;     // 256 KiB of bf16 keys per workgroup
+
+__global__ void sd_absmax_init_kernel(unsigned* absmax_bits, int n) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) absmax_bits[i] = 0u;
+}
+
+__global__ __launch_bounds__(kQuantThreads) void sd_absmax_kernel(
+    const uint16_t* __restrict__ k, const int32_t* __restrict__ lengths, int64_t Lmax, int Hkv,
+    unsigned* __restrict__ absmax_bits, int32_t* __restrict__ flag) {
+    const int bj = blockIdx.y, b = bj / Hkv;
+    const int64_t L = lengths[b];
+    if (L < 1 || L > Lmax) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(flag, 1);
+        return;
+    }
+    const int64_t r0 = int64_t(blockIdx.x) * kQuantRowsPerWg;
+    const int64_t r1 = min(r0 + kQuantRowsPerWg, L);
+    if (r0 >= r1) return;
+    const u32x4* base = reinterpret_cast<const u32x4*>(k + int64_t(bj) * Lmax * kHeadDim);
+    const int64_t e0 = r0 * 16, e1 = r1 * 16;   // 16 u32x4 per row
+    unsigned m = 0;
+    int64_t e = e0 + threadIdx.x;
+    for (; e + 3 * kQuantThreads < e1; e += 4 * kQuantThreads) {
+        u32x4 w0 = __builtin_nontemporal_load(base + e);
+        u32x4 w1 = __builtin_nontemporal_load(base + e + kQuantThreads);
+        u32x4 w2 = __builtin_nontemporal_load(base + e + 2 * kQuantThreads);
+        u32x4 w3 = __builtin_nontemporal_load(base + e + 3 * kQuantThreads);
+        m = max(m, max(max(abs_bits2(w0.x), abs_bits2(w0.y)), max(abs_bits2(w0.z), abs_bits2(w0.w))));
+        m = max(m, max(max(abs_bits2(w1.x), abs_bits2(w1.y)), max(abs_bits2(w1.z), abs_bits2(w1.w))));
+        m = max(m, max(max(abs_bits2(w2.x), abs_bits2(w2.y)), max(abs_bits2(w2.z), abs_bits2(w2.w))));
+        m = max(m, max(max(abs_bits2(w3.x), abs_bits2(w3.y)), max(abs_bits2(w3.z), abs_bits2(w3.w))));
+    }
+    for (; e < e1; e += kQuantThreads) {
+        u32x4 w = base[e];
+        m = max(m, max(max(abs_bits2(w.x), abs_bits2(w.y)), max(abs_bits2(w.z), abs_bits2(w.w))));
+    }
+    m = wave_max_u(m);
+    __shared__ unsigned red[kQuantThreads / kWave];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned r = red[0];
+        for (int i = 1; i < kQuantThreads / kWave; ++i) r = max(r, red[i]);
+        atomicMax(absmax_bits + bj, r);
+    }
+}
+
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+    return (uint32_t(a) & 0xffu) | ((uint32_t(b) & 0xffu) << 8) | ((uint32_t(c) & 0xffu) << 16) |
+           (uint32_t(d) << 24);
+}
+
+__device__ __forceinline__ uint2 codes8(u32x4 w, float a) {
+    uint2 r;
+    r.x = pack4(code_of(bf16_lo(w.x), a), code_of(bf16_hi(w.x), a), code_of(bf16_lo(w.y), a),
+                code_of(bf16_hi(w.y), a));
+    r.y = pack4(code_of(bf16_lo(w.z), a), code_of(bf16_hi(w.z), a), code_of(bf16_lo(w.w), a),
+                code_of(bf16_hi(w.w), a));
+    return r;
+}
+
+__global__ __launch_bounds__(kQuantThreads) void sd_quantize_kernel(
+    const uint16_t* __restrict__ k, const int32_t* __restrict__ lengths, int64_t Lmax, int Hkv,
+    const unsigned* __restrict__ absmax_bits, int8_t* __restrict__ k8, float* __restrict__ absmax_out) {
+    const int bj = blockIdx.y, b = bj / Hkv;
+    const int64_t L = lengths[b];
+    if (L < 1 || L > Lmax) return;
+    const float a = bf16_to_f32(uint16_t(absmax_bits[bj]));
+    if (absmax_out && blockIdx.x == 0 && threadIdx.x == 0) absmax_out[bj] = a;
+    const int64_t r0 = int64_t(blockIdx.x) * kQuantRowsPerWg;
+    const int64_t r1 = min(r0 + kQuantRowsPerWg, L);
+    if (r0 >= r1) return;
+    const u32x4* src = reinterpret_cast<const u32x4*>(k + int64_t(bj) * Lmax * kHeadDim);
+    uint2* dst = reinterpret_cast<uint2*>(k8 + int64_t(bj) * Lmax * kHeadDim);
+    const int64_t e0 = r0 * 16, e1 = r1 * 16;
+    int64_t e = e0 + threadIdx.x;
+    for (; e + kQuantThreads < e1; e += 2 * kQuantThreads) {
+        u32x4 w0 = __builtin_nontemporal_load(src + e);
+        u32x4 w1 = __builtin_nontemporal_load(src + e + kQuantThreads);
+        dst[e] = codes8(w0, a);
+        dst[e + kQuantThreads] = codes8(w1, a);
+    }
+    for (; e < e1; e += kQuantThreads) dst[e] = codes8(src[e], a);
+}
+
+}  // namespace
+
+namespace {
+
+__global__ __launch_bounds__(256) void sd_quantize_query_kernel(const uint16_t* __restrict__ q, int Hq,
+                                                                int Hkv, int G, int8_t* __restrict__ q8,
+                                                                int32_t* __restrict__ qg) {
+    __shared__ int Qlds[kHeadDim];
+    const int j = blockIdx.x, b = blockIdx.y;
+    group_query_codes(q + int64_t(b) * Hq * kHeadDim, j, G, Qlds, q8 ? q8 + int64_t(b) * Hq * kHeadDim : nullptr);
+    if (qg && threadIdx.x < kHeadDim) qg[(int64_t(b) * Hkv + j) * kHeadDim + threadIdx.x] = Qlds[threadIdx.x];
+}
+
+}  // namespace
+
+hipError_t launch_quantize_keys(sd_ctx* c, const uint16_t* k, const int32_t* lengths, int8_t* k8,
+                                float* absmax, hipStream_t s) {
+    const int BH = c->cfg.batch * c->cfg.num_kv_heads;
+    sd_absmax_init_kernel<<<(BH + 255) / 256, 256, 0, s>>>(c->absmax_bits, BH);
+    const int nwg = int((c->Lmax + kQuantRowsPerWg - 1) / kQuantRowsPerWg);
+    dim3 grid(nwg, BH);
+    sd_absmax_kernel<<<grid, kQuantThreads, 0, s>>>(k, lengths, c->Lmax, c->cfg.num_kv_heads,
+                                                   c->absmax_bits, c->flag);
+    sd_quantize_kernel<<<grid, kQuantThreads, 0, s>>>(k, lengths, c->Lmax, c->cfg.num_kv_heads,
+                                                     c->absmax_bits, k8, absmax);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_query(sd_ctx* c, const uint16_t* q, int8_t* q8, int32_t* qg, hipStream_t s) {
+    dim3 grid(c->cfg.num_kv_heads, c->cfg.batch);
+    sd_quantize_query_kernel<<<grid, 256, 0, s>>>(q, c->cfg.num_q_heads, c->cfg.num_kv_heads, c->G, q8, qg);
+    return hipGetLastError();
+}
+
+}  // namespace sd

@@ -1,0 +1,146 @@
+// LRU cache of 8-token value blocks in device memory, for values that live
+// in pinned host memory.
+//
+// Sources: news article on InfiniteHiP ("韩国通过卸载键值缓存节约英伟达GPU内存，
+// 实现18.95倍解码加速"), section "实现 7.24 倍的端到端解码加速" (offloaded KV
+// behind an LRU-based cache) and section "解决长上下文推理问题，能通过键值缓存卸载
+// 节约 GPU 内存" (the attention kernel reads CPU memory while it runs);
+// HCAttention summary page, section 引言 (values held in CPU memory and
+// fetched late, for the final aggregation only).
+//
+// Policy, per (request, KV head): every attended block of a step is touched;
+// a block that is not resident takes a free slot (lowest first) or evicts
+// the resident block with the smallest (last step used, block id).  The
+// recency order is kept explicitly: an array of slots, oldest first, that
+// each step rebuilds as [untouched survivors in order] ++ [this step's blocks
+// by ascending id], so evicting "the oldest untouched entries" is exactly
+// the (last step, block id) rule.  One workgroup per (request, KV head)
+// applies a step; the decode kernel then reads hits from the slot pool and
+// misses straight from host memory, writing each missed block into its slot.
+#include "sd_device.h"
+#include "sd_internal.h"
+
+namespace sd {
+
+constexpr int kLruThreads = 256;
+
+__global__ void sd_vcache_reset_kernel(ValueCache vc, int64_t BH) {
+    const int64_t n_page = BH * vc.nblk_max, n_slot = BH * vc.slots;
+    const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+    const int64_t t0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    for (int64_t i = t0; i < n_page; i += stride) vc.page[i] = -1;
+    for (int64_t i = t0; i < n_slot; i += stride) {
+        vc.slot_block[i] = -1;
+        vc.slot_last[i] = -1;
+    }
+    for (int64_t i = t0; i < BH; i += stride) vc.used[i] = 0;
+    if (t0 < kVcCounters) vc.counters[t0] = 0;
+}
+
+__global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(ValueCache vc, const uint32_t* blocks,
+                                                                      const int32_t* nblocks, int max_blocks,
+                                                                      int Hkv, int32_t step) {
+    __shared__ unsigned tmp[16];
+    const int j = blockIdx.x, b = blockIdx.y, bj = b * Hkv + j;
+    const int64_t BH = int64_t(gridDim.x) * gridDim.y;
+    const int tid = threadIdx.x;
+    const int nb = nblocks[bj];
+    const uint32_t* bl = blocks + int64_t(bj) * max_blocks;
+    int32_t* page = vc.page + int64_t(bj) * vc.nblk_max;
+    int32_t* sblk = vc.slot_block + int64_t(bj) * vc.slots;
+    int32_t* slast = vc.slot_last + int64_t(bj) * vc.slots;
+    int32_t* bslot = vc.blk_slot + int64_t(bj) * max_blocks;
+    int32_t* evicted = vc.evicted + int64_t(bj) * max_blocks;
+    const int32_t* order_old = vc.order + (int64_t(step & 1) * BH + bj) * vc.slots;
+    int32_t* order_new = vc.order + (int64_t((step + 1) & 1) * BH + bj) * vc.slots;
+    const int used = vc.used[bj];
+
+    // 1. hits touch their slot; misses are ranked in block order (ascending id)
+    const int per = (nb + kLruThreads - 1) / kLruThreads;
+    const int r0 = min(nb, tid * per), r1 = min(nb, r0 + per);
+    unsigned nm = 0;
+    for (int r = r0; r < r1; ++r) {
+        const int32_t s = page[bl[r] >> 8];
+        if (s >= 0) {
+            slast[s] = step;
+            bslot[r] = s;
+        } else {
+            bslot[r] = -1;
+            ++nm;
+        }
+    }
+    unsigned nmiss;
+    unsigned mrank = block_excl_scan<kLruThreads>(nm, tmp, &nmiss);   // barrier inside
+    const int nfree = vc.slots - used;
+    const int nevict = int(nmiss) > nfree ? int(nmiss) - nfree : 0;
+
+    // 2. untouched entries keep their order; the oldest `nevict` of them leave
+    const int per2 = (used + kLruThreads - 1) / kLruThreads;
+    const int i0 = min(used, tid * per2), i1 = min(used, i0 + per2);
+    unsigned nk = 0;
+    for (int i = i0; i < i1; ++i) nk += slast[order_old[i]] != step;
+    unsigned nuntouched;
+    unsigned krank = block_excl_scan<kLruThreads>(nk, tmp, &nuntouched);
+    for (int i = i0; i < i1; ++i) {
+        const int32_t s = order_old[i];
+        if (slast[s] == step) continue;
+        if (int(krank) < nevict) {
+            page[sblk[s]] = -1;
+            evicted[krank] = s;
+        } else {
+            order_new[krank - nevict] = s;
+        }
+        ++krank;
+    }
+    __syncthreads();
+    const int nsurv = int(nuntouched) - nevict;
+
+    // 3. misses take free slots first (ascending), then the evicted slots
+    //    (oldest first); the decode kernel fills them from host memory
+    for (int r = r0; r < r1; ++r) {
+        if (bslot[r] >= 0) continue;
+        const int32_t blk = int32_t(bl[r] >> 8);
+        const int m = int(mrank++);
+        const int32_t s = m < nfree ? used + m : evicted[m - nfree];
+        page[blk] = s;
+        sblk[s] = blk;
+        slast[s] = step;
+        bslot[r] = s | kVcMissBit;
+    }
+    // 4. this step's blocks become the newest entries, ascending by id
+    for (int r = r0; r < r1; ++r) order_new[nsurv + r] = bslot[r] & ~kVcMissBit;
+    if (tid == 0) {
+        vc.used[bj] = used + (int(nmiss) < nfree ? int(nmiss) : nfree);
+        const int par = step & 1;
+        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 1), (unsigned long long)nb);
+        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 2), (unsigned long long)(nb - int(nmiss)));
+        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 3), (unsigned long long)nmiss);
+        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 4 + 4 * par), (unsigned long long)nb);
+        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 5 + 4 * par), (unsigned long long)(nb - int(nmiss)));
+        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 6 + 4 * par), (unsigned long long)nmiss);
+        if (bj == 0) {
+            vc.counters[0] = step + 1;
+            const int nxt = (step + 1) & 1;
+            vc.counters[4 + 4 * nxt] = 0;
+            vc.counters[5 + 4 * nxt] = 0;
+            vc.counters[6 + 4 * nxt] = 0;
+        }
+    }
+}
+
+hipError_t launch_value_cache_reset(sd_ctx* c, hipStream_t s) {
+    const int64_t BH = int64_t(c->cfg.batch) * c->cfg.num_kv_heads;
+    sd_vcache_reset_kernel<<<1024, 256, 0, s>>>(c->vc, BH);
+    c->vc_step = 0;
+    return hipGetLastError();
+}
+
+hipError_t launch_value_cache_update(sd_ctx* c, hipStream_t s) {
+    dim3 grid(c->cfg.num_kv_heads, c->cfg.batch);
+    sd_vcache_step_kernel<<<grid, kLruThreads, 0, s>>>(c->vc, c->blocks, c->nblocks, c->max_blocks,
+                                                        c->cfg.num_kv_heads, int32_t(c->vc_step));
+    ++c->vc_step;
+    return hipGetLastError();
+}
+
+}  // namespace sd

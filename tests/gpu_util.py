@@ -1,0 +1,110 @@
+"""Helpers shared by the GPU tests: upload seeded inputs, run the library
+through the C ABI, run the oracle on the same inputs, compare."""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import sparse_decode as O
+from sparse_attention_kv_int8_amd.inputs import Inputs, Workload
+
+OUT_TOL = 8e-3          # max |bf16 output - fp64 oracle| allowed
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def to_dev_bf16(a: np.ndarray, device="cuda"):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def bf16_dev_to_bits(t) -> np.ndarray:
+    torch = torch_mod()
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def oracle_config(w: Workload) -> O.StepConfig:
+    return O.StepConfig(tuple(O.StageSpec(s.chunk, s.stride, s.keep) for s in w.stages),
+                        w.sink, w.window, 1.0 / np.sqrt(w.head_dim))
+
+
+def oracle_keys(inp: Inputs):
+    """Oracle int8 codes and scales for every (request, KV head)."""
+    w = inp.workload
+    k8 = np.zeros(inp.k.shape, np.int8)
+    a = np.zeros((w.batch, w.num_kv_heads), np.float32)
+    for b in range(w.batch):
+        L = int(inp.lengths[b])
+        for j in range(w.num_kv_heads):
+            k8[b, j, :L], a[b, j] = O.quantize_keys(inp.k[b, j], L)
+    return k8, a
+
+
+class GpuRun:
+    """Uploads one workload's inputs and runs quantize + decode step."""
+
+    def __init__(self, inp: Inputs, decoder=None, stream=None):
+        from sparse_attention_kv_int8_amd.binding import SparseDecoder
+        torch = torch_mod()
+        self.torch = torch
+        self.inp = inp
+        w = inp.workload
+        self.w = w
+        self.dec = decoder or SparseDecoder.for_workload(w)
+        self.k = to_dev_bf16(inp.k)
+        if w.values_on_host:
+            self.v = torch.empty(inp.v.shape, dtype=torch.bfloat16, pin_memory=True)
+            self.v.view(torch.int16).numpy()[...] = inp.v.view(np.int16)
+        else:
+            self.v = to_dev_bf16(inp.v)
+        self.lengths = torch.from_numpy(inp.lengths.astype(np.int32)).cuda()
+        self.k8 = torch.zeros(inp.k.shape, dtype=torch.int8, device="cuda")
+        self.absmax = torch.zeros((w.batch, w.num_kv_heads), dtype=torch.float32, device="cuda")
+        self.out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+        self.kept = torch.empty((w.batch, w.num_kv_heads, w.keep_total), dtype=torch.int32, device="cuda")
+        self.stream = stream
+
+    def quantize(self):
+        self.dec.sd_quantize_keys(self.k, self.lengths, self.k8, self.absmax, stream=self.stream)
+
+    def step(self, q_bits: np.ndarray):
+        q = to_dev_bf16(q_bits)
+        self.dec.sd_decode_step(q, self.k, self.k8, self.v, self.lengths, self.out, self.kept,
+                                stream=self.stream)
+        self.torch.cuda.synchronize()
+        return bf16_dev_to_bits(self.out), self.kept.cpu().numpy()
+
+    def query_codes(self, q_bits: np.ndarray):
+        torch = self.torch
+        w = self.w
+        q = to_dev_bf16(q_bits)
+        q8 = torch.zeros((w.batch, w.num_q_heads, w.head_dim), dtype=torch.int8, device="cuda")
+        qg = torch.zeros((w.batch, w.num_kv_heads, w.head_dim), dtype=torch.int32, device="cuda")
+        self.dec.sd_quantize_query(q, q8, qg, stream=self.stream)
+        torch.cuda.synchronize()
+        return q8.cpu().numpy(), qg.cpu().numpy()
+
+    def stage_scores(self, stage: int) -> np.ndarray:
+        torch = self.torch
+        n = self.dec.sd_stage_candidates(stage)
+        dst = torch.empty((self.w.batch, self.w.num_kv_heads, n), dtype=torch.int32, device="cuda")
+        self.dec.sd_stage_scores(stage, dst, stream=self.stream)
+        torch.cuda.synchronize()
+        return dst.cpu().numpy()
+
+
+def compare_step(inp: Inputs, q_bits: np.ndarray, k8_ref: np.ndarray, out_bits: np.ndarray,
+                 kept: np.ndarray, ref=None):
+    """Kept indices bit-exact, outputs within OUT_TOL of the fp64 oracle.
+    Returns (oracle result, max abs error, max |o|)."""
+    w = inp.workload
+    if ref is None:
+        ref = O.decode_step(q_bits, inp.k, k8_ref, inp.v, inp.lengths, oracle_config(w))
+    bad = np.argwhere(kept != ref.kept_idx)
+    assert bad.size == 0, f"kept_idx differs at {bad[:5].tolist()} (of {len(bad)})"
+    got = O.bf16_to_f64(out_bits)
+    err = np.abs(got - ref.out).max()
+    assert err <= OUT_TOL, f"max |err| = {err}"
+    return ref, float(err), float(np.abs(ref.out).max())
