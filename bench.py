@@ -43,7 +43,7 @@ from sparse_attention_kv_int8_amd.inputs import WORKLOADS, make_inputs  # noqa: 
 
 METRIC = "sparse decode-attention µs/step + achieved HBM GB/s at 128K and 1M ctx (GQA 32/8)"
 HBM_PEAK_GBS = 8000.0
-KIND_NAMES = ["stage0", "stage1", "stage2", "stage3", "value_cache", "attend", "quantize"]
+KIND_NAMES = ["stage0", "stage1", "stage2", "stage3", "value_cache", "attend", "quantize", "combine"]
 
 
 def log(*a):
@@ -184,7 +184,7 @@ def measure(w, steps: int, warmup: int, copies: int) -> tuple:
     b.run(warmup)
     torch.cuda.synchronize()
     # calibration: all kernels timed, to pick the dominant one
-    cal = b.profile(max(20, warmup), 0x7F)
+    cal = b.profile(max(20, warmup), 0xFF)
     avg_us = {k: v[0] * 1e3 / v[1] for k, v in cal.items()}
     dominant = max((k for k in avg_us if k != "quantize"), key=lambda k: avg_us[k])
     dom_kind = KIND_NAMES.index(dominant)

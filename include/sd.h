@@ -120,6 +120,10 @@ void sd_destroy(sd_ctx* ctx);
 /* Static text for a status code. */
 const char* sd_status_string(sd_status status);
 
+/* Text of the last HIP failure seen by this thread ("" if none): the HIP
+ * call and its error string.  Valid until the thread's next library call. */
+const char* sd_last_error(void);
+
 /* Quantises the key cache (part 1).
  *  k_bf16   device [B][Hkv][Lmax][d] bf16 keys.
  *  lengths  device [B] int32 request lengths L_b in [1, Lmax].
@@ -180,9 +184,10 @@ sd_status sd_reset_value_cache(sd_ctx* ctx, void* stream);
 enum {
     SD_PROF_STAGE0 = 0,         /* pruning stage s is SD_PROF_STAGE0 + s */
     SD_PROF_VALUE_CACHE = 4,    /* LRU update of the host-value path */
-    SD_PROF_ATTEND = 5,         /* sparse flash decode + log-sum-exp merge */
+    SD_PROF_ATTEND = 5,         /* last select + attended set + sparse flash decode (partials) */
     SD_PROF_QUANTIZE = 6,       /* the three kernels of sd_quantize_keys, as one interval */
-    SD_PROF_KINDS = 7
+    SD_PROF_COMBINE = 7,        /* log-sum-exp merge of the splits into the bf16 output */
+    SD_PROF_KINDS = 8
 };
 
 typedef struct sd_profile {

@@ -40,9 +40,9 @@ class sd_config(C.Structure):
     ]
 
 
-SD_PROF_KINDS = 7
-SD_PROF_STAGE0, SD_PROF_VALUE_CACHE, SD_PROF_ATTEND, SD_PROF_QUANTIZE = 0, 4, 5, 6
-PROF_NAMES = ["stage0", "stage1", "stage2", "stage3", "value_cache", "attend", "quantize"]
+SD_PROF_KINDS = 8
+SD_PROF_STAGE0, SD_PROF_VALUE_CACHE, SD_PROF_ATTEND, SD_PROF_QUANTIZE, SD_PROF_COMBINE = 0, 4, 5, 6, 7
+PROF_NAMES = ["stage0", "stage1", "stage2", "stage3", "value_cache", "attend", "quantize", "combine"]
 
 
 class sd_profile(C.Structure):
@@ -57,6 +57,10 @@ class sd_stats(C.Structure):
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_attention_kv_int8_amd.build` "
                       "(there is no fallback implementation)")
+# torch provides device memory and streams and brings its own HIP runtime.
+# It must be loaded first: libsd.so then binds to that already-loaded runtime
+# (same SONAME) instead of loading a second HIP runtime into the process.
+import torch  # noqa: E402,F401
 lib = C.CDLL(LIB_PATH)
 
 _p = C.c_void_p
@@ -64,6 +68,7 @@ _SIGS = {
     "sd_create": (C.c_int, [C.POINTER(sd_config), C.POINTER(_p)]),
     "sd_destroy": (None, [_p]),
     "sd_status_string": (C.c_char_p, [C.c_int]),
+    "sd_last_error": (C.c_char_p, []),
     "sd_quantize_keys": (C.c_int, [_p, _p, _p, _p, _p, _p]),
     "sd_decode_step": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "sd_quantize_query": (C.c_int, [_p, _p, _p, _p, _p]),
@@ -85,7 +90,9 @@ EXPORTED = tuple(_SIGS)
 class SDError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
-        super().__init__(f"{what}: {lib.sd_status_string(status).decode()} (status {status})")
+        detail = lib.sd_last_error().decode(errors="replace") if status == SD_ERR_HIP else ""
+        super().__init__(f"{what}: {lib.sd_status_string(status).decode()} (status {status})"
+                         + (f" [{detail}]" if detail else ""))
 
 
 def check(status: int, what: str) -> None:

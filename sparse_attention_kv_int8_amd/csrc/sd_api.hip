@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
 #include <new>
 
@@ -19,8 +20,11 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-sd_status from_hip(hipError_t e) {
+thread_local char g_last_error[256];
+
+sd_status from_hip(hipError_t e, const char* where = "HIP call") {
     if (e == hipSuccess) return SD_OK;
+    std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(e), int(e));
     if (e == hipErrorOutOfMemory) return SD_ERR_OUT_OF_MEMORY;
     return SD_ERR_HIP;
 }
@@ -134,6 +138,8 @@ struct Carver {
 
 extern "C" {
 
+const char* sd_last_error(void) { return g_last_error; }
+
 const char* sd_status_string(sd_status s) {
     switch (s) {
         case SD_OK: return "ok";
@@ -154,7 +160,10 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
     if (!c) return SD_ERR_OUT_OF_MEMORY;
     sd_status st = plan(*cfg, c);
     if (st != SD_OK) { delete c; return st; }
-    if (hipGetDevice(&c->device) != hipSuccess) { delete c; return SD_ERR_HIP; }
+    {
+        hipError_t e0 = hipGetDevice(&c->device);
+        if (e0 != hipSuccess) { delete c; return from_hip(e0, "hipGetDevice"); }
+    }
 
     const size_t B = size_t(cfg->batch), H = size_t(cfg->num_kv_heads), BH = B * H;
     Carver cv;
@@ -164,7 +173,6 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
     const size_t o_blocks = cv.take<uint32_t>(BH * c->max_blocks);
     const size_t o_nblocks = cv.take<int32_t>(BH);
     const size_t o_part = cv.take<float>(BH * c->nsplit * c->G * (2 + sd::kHeadDim));
-    const size_t o_cnt = cv.take<unsigned>((SD_MAX_STAGES + 1) * BH);
     const size_t o_abs = cv.take<unsigned>(BH);
     const size_t o_flag = cv.take<int32_t>(1);
     size_t o_vc[10] = {0};
@@ -183,14 +191,13 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
     }
     c->ws_bytes = cv.off;
     hipError_t e = hipMalloc(&c->ws, c->ws_bytes);
-    if (e != hipSuccess) { (void)hipGetLastError(); delete c; return from_hip(e); }
+    if (e != hipSuccess) { (void)hipGetLastError(); delete c; return from_hip(e, "hipMalloc(workspace)"); }
     char* base = static_cast<char*>(c->ws);
     for (int s = 0; s < c->S; ++s) c->scores[s] = reinterpret_cast<int32_t*>(base + o_scores[s]);
     c->qgroup = reinterpret_cast<int32_t*>(base + o_qg);
     c->blocks = reinterpret_cast<uint32_t*>(base + o_blocks);
     c->nblocks = reinterpret_cast<int32_t*>(base + o_nblocks);
     c->part = reinterpret_cast<float*>(base + o_part);
-    c->counters = reinterpret_cast<unsigned*>(base + o_cnt);
     c->absmax_bits = reinterpret_cast<unsigned*>(base + o_abs);
     c->flag = reinterpret_cast<int32_t*>(base + o_flag);
     if (cfg->values_on_host) {
@@ -204,11 +211,11 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
         c->vc.blk_slot = reinterpret_cast<int32_t*>(base + o_vc[7]);
         c->vc.counters = reinterpret_cast<int64_t*>(base + o_vc[8]);
     }
-    // Counters, flag and score buffers start defined; this is setup, outside any step.
+    // Flag and score buffers start defined; this is setup, outside any step.
     e = hipMemset(c->ws, 0, c->ws_bytes);
     if (e == hipSuccess && cfg->values_on_host) e = sd::launch_value_cache_reset(c, nullptr);
     if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e != hipSuccess) { (void)hipFree(c->ws); delete c; return from_hip(e); }
+    if (e != hipSuccess) { (void)hipFree(c->ws); delete c; return from_hip(e, "workspace initialisation"); }
     *out = c;
     return SD_OK;
 }
@@ -263,9 +270,10 @@ sd_status sd_decode_step(sd_ctx* c, const uint16_t* q, const uint16_t* k, const 
     for (int st = 0; st < c->S && e == hipSuccess; ++st)
         e = timed(c, SD_PROF_STAGE0 + st, s, [&] { return sd::launch_prune_stage(c, st, q, k8, lengths, kept, s); });
     if (e == hipSuccess && c->cfg.values_on_host)
-        e = timed(c, SD_PROF_VALUE_CACHE, s, [&] { return sd::launch_value_cache_update(c, s); });
+        e = timed(c, SD_PROF_VALUE_CACHE, s, [&] { return sd::launch_value_cache_update(c, lengths, kept, s); });
     if (e == hipSuccess)
-        e = timed(c, SD_PROF_ATTEND, s, [&] { return sd::launch_attend(c, q, k, vk, lengths, out, s); });
+        e = timed(c, SD_PROF_ATTEND, s, [&] { return sd::launch_attend(c, q, k, vk, lengths, kept, out, s); });
+    if (e == hipSuccess) e = timed(c, SD_PROF_COMBINE, s, [&] { return sd::launch_combine(c, out, s); });
     return from_hip(e);
 }
 

@@ -9,14 +9,18 @@
 // FlashAttention, section "从赫赫有名的注意力机制说起"), and the last split
 // of each (request, KV head) merges all splits by log-sum-exp.
 //
-// Workgroup (split, KV head, request) = 4 waves; waves take the split's
-// blocks round-robin.  For one 8-token block a wave computes the G scores of
+// Every workgroup first recomputes the last stage's kept set from its scores
+// and builds the attended block list in LDS (with values in host memory the
+// value-cache kernel has built it already); workgroup 0 publishes the kept
+// set.  Workgroup (split, KV head, request) = 4 waves; waves take the
+// split's blocks round-robin.  For one 8-token block a wave computes the G scores of
 // every token (lane = token * 8 + 16-dim slice; bf16 pair dot products,
 // DPP sum over the 8 slice lanes), takes the block max per head (uniform
 // over the wave), then accumulates P V with lane l owning output dims 2l and
 // 2l+1, reading each value row with one coalesced dword per lane.
 #include "sd_device.h"
 #include "sd_internal.h"
+#include "sd_select.h"
 
 namespace sd {
 
@@ -34,11 +38,18 @@ struct AttendParams {
     const int32_t* blk_slot;  // [B][Hkv][max_blocks]   (host-value path)
     int vslots;
     const int32_t* lengths;
-    const uint32_t* blocks;   // [B][Hkv][max_blocks]
-    const int32_t* nblocks;   // [B][Hkv]
+    const uint32_t* blocks;   // [B][Hkv][max_blocks] (host-value path: built by the value-cache kernel)
+    const int32_t* nblocks;   // [B][Hkv]           (host-value path)
     int max_blocks;
+    // last-stage select (device-value path)
+    StageDev last;
+    int first_stage;          // the last stage is also the first
+    int pp_koff;              // kept_idx offset of the stage before the last
+    const int32_t* last_scores;   // [B][Hkv][last.ncand]
+    int32_t* kept;            // [B][Hkv][keep_total]
+    int keep_total;
+    int sink, window;
     float* part;              // [B][Hkv][nsplit][G][2 + d]
-    unsigned* counter;        // [B][Hkv]
     int nsplit;
     int64_t Lmax;
     int Hq, Hkv;
@@ -60,16 +71,37 @@ __device__ __forceinline__ float rescale(float a, float m) {
 
 template <int G, bool HOSTV>
 __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendParams p) {
+    extern __shared__ uint32_t dyn[];   // device values: keys [last.ncand], sel [last.keep], blocks [max_blocks]
     __shared__ float wm[kAttnWaves][G];
     __shared__ float wl[kAttnWaves][G];
     __shared__ float wacc[kAttnWaves][G][kHeadDim];
-    __shared__ unsigned last_flag;
+    __shared__ unsigned hist[256];
+    __shared__ unsigned tmp[32];
 
     const int sp = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int bj = b * p.Hkv + j;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int tok = lane >> 3, sl = lane & 7;
-    const int nb = p.nblocks[bj];
+    int64_t L = p.lengths[b];
+    if (L < 1 || L > p.Lmax) L = 0;
+
+    const uint32_t* blist;
+    int nb;
+    if (HOSTV) {
+        blist = p.blocks + int64_t(bj) * p.max_blocks;
+        nb = p.nblocks[bj];
+    } else {
+        uint32_t* keys = dyn;
+        int* sel = reinterpret_cast<int*>(dyn + p.last.ncand);
+        uint32_t* bl = dyn + p.last.ncand + p.last.keep;
+        int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
+        const int nk = kept_of_stage<kAttnThreads>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
+                                                   p.first_stage ? nullptr : kept_bj + p.pp_koff, L, keys, sel, hist, tmp);
+        if (sp == 0)
+            for (int i = threadIdx.x; i < p.last.keep; i += kAttnThreads) kept_bj[p.last.koff + i] = i < nk ? sel[i] : -1;
+        nb = build_attended<kAttnThreads>(sel, nk, p.last.chunk, L, p.sink, p.window, bl, tmp);
+        blist = bl;
+    }
     const int per = (nb + p.nsplit - 1) / p.nsplit;
     const int r0 = sp * per, r1 = min(nb, r0 + per);
 
@@ -88,8 +120,6 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
 
     const uint16_t* kbase = p.k + int64_t(bj) * p.Lmax * kHeadDim;
     const uint16_t* vbase = p.v + int64_t(bj) * p.Lmax * kHeadDim;
-    const int64_t L = p.lengths[b];
-    const uint32_t* blist = p.blocks + int64_t(bj) * p.max_blocks;
 
     for (int r = r0 + wave; r < r1; r += kAttnWaves) {
         const uint32_t e = blist[r];
@@ -193,34 +223,40 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         if (dd == 0) { part[h * kPartStride] = M; part[h * kPartStride + 1] = l; }
     }
 
-    if (!arrive_last(p.counter + bj, unsigned(p.nsplit), &last_flag)) return;
+}
 
-    // ---- last split of this (request, KV head): log-sum-exp merge ----
-    const float* pb = p.part + int64_t(bj) * p.nsplit * G * kPartStride;
+// Log-sum-exp merge of the splits of one (request, KV head), rounding to bf16.
+template <int G>
+__global__ __launch_bounds__(kAttnThreads) void sd_combine_kernel(const float* __restrict__ part, int nsplit, int Hq,
+                                                                 int Hkv, uint16_t* __restrict__ out) {
+    const int j = blockIdx.x, b = blockIdx.y, bj = b * Hkv + j;
+    const float* pb = part + int64_t(bj) * nsplit * G * kPartStride;
     for (int o = threadIdx.x; o < G * kHeadDim; o += kAttnThreads) {
         const int h = o / kHeadDim, dd = o % kHeadDim;
         float M = -INFINITY;
-        for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, pb[(s * G + h) * kPartStride]);
+#pragma unroll 8
+        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pb[(s * G + h) * kPartStride]);
         float a = 0.f, l = 0.f;
-        for (int s = 0; s < p.nsplit; ++s) {
+#pragma unroll 8
+        for (int s = 0; s < nsplit; ++s) {
             const float* ps = pb + (s * G + h) * kPartStride;
             const float f = rescale(ps[0], M);
             a = fmaf(ps[2 + dd], f, a);
             l = fmaf(ps[1], f, l);
         }
         const float o_val = l > 0.f ? a / l : 0.f;
-        p.out[(int64_t(b) * p.Hq + j * G + h) * kHeadDim + dd] = f32_to_bf16_rne(o_val);
+        out[(int64_t(b) * Hq + j * G + h) * kHeadDim + dd] = f32_to_bf16_rne(o_val);
     }
 }
 
 template <int G>
-static void launch_g(const AttendParams& p, dim3 grid, bool hostv, hipStream_t s) {
+static void launch_g(const AttendParams& p, dim3 grid, bool hostv, size_t lds, hipStream_t s) {
     if (hostv) sd_flash_decode_kernel<G, true><<<grid, kAttnThreads, 0, s>>>(p);
-    else sd_flash_decode_kernel<G, false><<<grid, kAttnThreads, 0, s>>>(p);
+    else sd_flash_decode_kernel<G, false><<<grid, kAttnThreads, lds, s>>>(p);
 }
 
 hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                         const int32_t* lengths, uint16_t* out, hipStream_t s) {
+                         const int32_t* lengths, int32_t* kept, uint16_t* out, hipStream_t s) {
     AttendParams p{};
     p.q = q;
     p.k = k;
@@ -233,8 +269,17 @@ hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const 
     p.nblocks = c->nblocks;
     p.max_blocks = c->max_blocks;
     p.part = c->part;
-    p.counter = c->counters + size_t(SD_MAX_STAGES) * c->cfg.batch * c->cfg.num_kv_heads;
     p.nsplit = c->nsplit;
+    const int S = c->S;
+    p.last = stage_dev(c, S - 1);
+    p.first_stage = S == 1;
+    p.pp_koff = S >= 2 ? c->st[S - 2].koff : 0;
+    p.last_scores = c->scores[S - 1];
+    p.kept = kept;
+    p.keep_total = c->keep_total;
+    p.sink = c->cfg.sink;
+    p.window = c->cfg.window;
+    const size_t lds = (size_t(p.last.ncand) + size_t(p.last.keep) + size_t(c->max_blocks)) * 4;
     p.Lmax = c->Lmax;
     p.Hq = c->cfg.num_q_heads;
     p.Hkv = c->cfg.num_kv_heads;
@@ -243,9 +288,24 @@ hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const 
     dim3 grid(c->nsplit, c->cfg.num_kv_heads, c->cfg.batch);
     const bool hostv = c->cfg.values_on_host != 0;
     switch (c->G) {
-        case 1: launch_g<1>(p, grid, hostv, s); break;
-        case 2: launch_g<2>(p, grid, hostv, s); break;
-        default: launch_g<4>(p, grid, hostv, s); break;
+        case 1: launch_g<1>(p, grid, hostv, lds, s); break;
+        case 2: launch_g<2>(p, grid, hostv, lds, s); break;
+        default: launch_g<4>(p, grid, hostv, lds, s); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sd
+
+namespace sd {
+
+hipError_t launch_combine(sd_ctx* c, uint16_t* out, hipStream_t s) {
+    dim3 grid(c->cfg.num_kv_heads, c->cfg.batch);
+    const int Hq = c->cfg.num_q_heads, Hkv = c->cfg.num_kv_heads;
+    switch (c->G) {
+        case 1: sd_combine_kernel<1><<<grid, kAttnThreads, 0, s>>>(c->part, c->nsplit, Hq, Hkv, out); break;
+        case 2: sd_combine_kernel<2><<<grid, kAttnThreads, 0, s>>>(c->part, c->nsplit, Hq, Hkv, out); break;
+        default: sd_combine_kernel<4><<<grid, kAttnThreads, 0, s>>>(c->part, c->nsplit, Hq, Hkv, out); break;
     }
     return hipGetLastError();
 }

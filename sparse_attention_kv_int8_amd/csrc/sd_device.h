@@ -136,26 +136,6 @@ __device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* tmp, u
     return r;
 }
 
-// "Last workgroup done" hand-off.  Every thread has written its results;
-// all of them are made visible at device scope, then one atomic per
-// workgroup counts arrivals.  Returns true in every thread of the last
-// arriving workgroup, which also re-arms the counter for the next launch
-// and acquires the other workgroups' results.
-__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected, unsigned* lds_flag) {
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned old = atomicAdd(counter, 1u);
-        bool last = old == expected - 1;
-        if (last) atomicExch(counter, 0u);
-        *lds_flag = last ? 1u : 0u;
-    }
-    __syncthreads();
-    bool last = *lds_flag != 0;
-    if (last) __threadfence();
-    return last;
-}
-
 // |x| of the two bf16 values of a dword, as bit patterns; max of the two.
 __device__ __forceinline__ unsigned abs_bits2(uint32_t w) {
     return max(w & 0x7fffu, (w >> 16) & 0x7fffu);

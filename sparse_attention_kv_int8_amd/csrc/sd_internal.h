@@ -18,6 +18,12 @@ struct StageGeom {
     int nwg;            // workgroups per (request, KV head)
 };
 
+// Geometry of one stage as the kernels see it.
+struct StageDev {
+    int chunk, stride, keep, nsamp, ncand, koff;
+    int ratio;      // children per parent chunk (chunk of stage s-1 / chunk of stage s); 1 for stage 0
+};
+
 constexpr int kVcCounters = 16;
 constexpr int32_t kVcMissBit = int32_t(0x40000000);
 
@@ -60,7 +66,6 @@ struct sd_ctx {
     uint32_t* blocks;                 // [B][Hkv][max_blocks] (block << 8) | token mask
     int32_t* nblocks;                 // [B][Hkv]
     float* part;                      // [B][Hkv][nsplit][G][2 + d]
-    unsigned* counters;               // [SD_MAX_STAGES + 1][B][Hkv]
     unsigned* absmax_bits;            // [B][Hkv]
     int32_t* flag;                    // device error flag
     sd::ValueCache vc;
@@ -82,8 +87,10 @@ hipError_t launch_quantize_query(sd_ctx* c, const uint16_t* q, int8_t* q8, int32
 hipError_t launch_prune_stage(sd_ctx* c, int stage, const uint16_t* q, const int8_t* k8,
                               const int32_t* lengths, int32_t* kept, hipStream_t s);
 hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                         const int32_t* lengths, uint16_t* out, hipStream_t s);
-hipError_t launch_value_cache_update(sd_ctx* c, hipStream_t s);
+                         const int32_t* lengths, int32_t* kept, uint16_t* out, hipStream_t s);
+hipError_t launch_combine(sd_ctx* c, uint16_t* out, hipStream_t s);
+hipError_t launch_value_cache_update(sd_ctx* c, const int32_t* lengths, int32_t* kept, hipStream_t s);
 hipError_t launch_value_cache_reset(sd_ctx* c, hipStream_t s);
+StageDev stage_dev(const sd_ctx* c, int st);
 
 }  // namespace sd

@@ -15,10 +15,13 @@
 // each step rebuilds as [untouched survivors in order] ++ [this step's blocks
 // by ascending id], so evicting "the oldest untouched entries" is exactly
 // the (last step, block id) rule.  One workgroup per (request, KV head)
-// applies a step; the decode kernel then reads hits from the slot pool and
-// misses straight from host memory, writing each missed block into its slot.
+// applies a step (after selecting the last stage's kept set and building the
+// attended block list, which it publishes for the decode kernel); the decode
+// kernel then reads hits from the slot pool and misses straight from host
+// memory, writing each missed block into its slot.
 #include "sd_device.h"
 #include "sd_internal.h"
+#include "sd_select.h"
 
 namespace sd {
 
@@ -37,15 +40,47 @@ __global__ void sd_vcache_reset_kernel(ValueCache vc, int64_t BH) {
     if (t0 < kVcCounters) vc.counters[t0] = 0;
 }
 
-__global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(ValueCache vc, const uint32_t* blocks,
-                                                                      const int32_t* nblocks, int max_blocks,
-                                                                      int Hkv, int32_t step) {
-    __shared__ unsigned tmp[16];
-    const int j = blockIdx.x, b = blockIdx.y, bj = b * Hkv + j;
+struct VcStepParams {
+    ValueCache vc;
+    StageDev last;
+    int first_stage;
+    int pp_koff;
+    const int32_t* last_scores;   // [B][Hkv][last.ncand]
+    int32_t* kept;                // [B][Hkv][keep_total]
+    int keep_total;
+    int sink, window;
+    const int32_t* lengths;
+    int64_t Lmax;
+    uint32_t* blocks;             // [B][Hkv][max_blocks]
+    int32_t* nblocks;             // [B][Hkv]
+    int max_blocks;
+    int Hkv;
+    int32_t step;
+};
+
+__global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParams p) {
+    extern __shared__ uint32_t dyn[];    // keys [last.ncand], sel [last.keep]
+    __shared__ unsigned hist[256];
+    __shared__ unsigned tmp[32];
+    const ValueCache& vc = p.vc;
+    const int max_blocks = p.max_blocks;
+    const int32_t step = p.step;
+    const int j = blockIdx.x, b = blockIdx.y, bj = b * p.Hkv + j;
     const int64_t BH = int64_t(gridDim.x) * gridDim.y;
     const int tid = threadIdx.x;
-    const int nb = nblocks[bj];
-    const uint32_t* bl = blocks + int64_t(bj) * max_blocks;
+    int64_t L = p.lengths[b];
+    if (L < 1 || L > p.Lmax) L = 0;
+
+    // last stage's kept set and the attended blocks
+    int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
+    int* sel = reinterpret_cast<int*>(dyn + p.last.ncand);
+    const int nk = kept_of_stage<kLruThreads>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
+                                              p.first_stage ? nullptr : kept_bj + p.pp_koff, L, dyn, sel, hist, tmp);
+    for (int i = tid; i < p.last.keep; i += kLruThreads) kept_bj[p.last.koff + i] = i < nk ? sel[i] : -1;
+    uint32_t* blocks_bj = p.blocks + int64_t(bj) * max_blocks;
+    const int nb = build_attended<kLruThreads>(sel, nk, p.last.chunk, L, p.sink, p.window, blocks_bj, tmp);
+    if (tid == 0) p.nblocks[bj] = nb;
+    const uint32_t* bl = blocks_bj;
     int32_t* page = vc.page + int64_t(bj) * vc.nblk_max;
     int32_t* sblk = vc.slot_block + int64_t(bj) * vc.slots;
     int32_t* slast = vc.slot_last + int64_t(bj) * vc.slots;
@@ -70,17 +105,17 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(ValueCache 
         }
     }
     unsigned nmiss;
-    unsigned mrank = block_excl_scan<kLruThreads>(nm, tmp, &nmiss);   // barrier inside
+    unsigned mrank = block_excl_scan<kLruThreads>(nm, tmp, &nmiss);   // barriers inside
     const int nfree = vc.slots - used;
     const int nevict = int(nmiss) > nfree ? int(nmiss) - nfree : 0;
 
     // 2. untouched entries keep their order; the oldest `nevict` of them leave
     const int per2 = (used + kLruThreads - 1) / kLruThreads;
     const int i0 = min(used, tid * per2), i1 = min(used, i0 + per2);
-    unsigned nk = 0;
-    for (int i = i0; i < i1; ++i) nk += slast[order_old[i]] != step;
+    unsigned nu = 0;
+    for (int i = i0; i < i1; ++i) nu += slast[order_old[i]] != step;
     unsigned nuntouched;
-    unsigned krank = block_excl_scan<kLruThreads>(nk, tmp, &nuntouched);
+    unsigned krank = block_excl_scan<kLruThreads>(nu, tmp, &nuntouched);
     for (int i = i0; i < i1; ++i) {
         const int32_t s = order_old[i];
         if (slast[s] == step) continue;
@@ -135,10 +170,28 @@ hipError_t launch_value_cache_reset(sd_ctx* c, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_value_cache_update(sd_ctx* c, hipStream_t s) {
+hipError_t launch_value_cache_update(sd_ctx* c, const int32_t* lengths, int32_t* kept, hipStream_t s) {
+    VcStepParams p{};
+    p.vc = c->vc;
+    const int S = c->S;
+    p.last = stage_dev(c, S - 1);
+    p.first_stage = S == 1;
+    p.pp_koff = S >= 2 ? c->st[S - 2].koff : 0;
+    p.last_scores = c->scores[S - 1];
+    p.kept = kept;
+    p.keep_total = c->keep_total;
+    p.sink = c->cfg.sink;
+    p.window = c->cfg.window;
+    p.lengths = lengths;
+    p.Lmax = c->Lmax;
+    p.blocks = c->blocks;
+    p.nblocks = c->nblocks;
+    p.max_blocks = c->max_blocks;
+    p.Hkv = c->cfg.num_kv_heads;
+    p.step = int32_t(c->vc_step);
+    const size_t lds = (size_t(p.last.ncand) + size_t(p.last.keep)) * 4;
     dim3 grid(c->cfg.num_kv_heads, c->cfg.batch);
-    sd_vcache_step_kernel<<<grid, kLruThreads, 0, s>>>(c->vc, c->blocks, c->nblocks, c->max_blocks,
-                                                        c->cfg.num_kv_heads, int32_t(c->vc_step));
+    sd_vcache_step_kernel<<<grid, kLruThreads, lds, s>>>(p);
     ++c->vc_step;
     return hipGetLastError();
 }

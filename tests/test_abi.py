@@ -81,3 +81,11 @@ def test_null_arguments():
     assert B.lib.sd_quantize_keys(None, None, None, None, None, None) == B.SD_ERR_INVALID_ARG
     assert B.lib.sd_check(None, None) == B.SD_ERR_INVALID_ARG
     assert B.lib.sd_stage_candidates(None, 0) == -1
+
+
+def test_single_hip_runtime_in_process():
+    """The binding loads torch first, so libsd.so binds to torch's HIP runtime
+    instead of mapping a second one."""
+    maps = open("/proc/self/maps").read()
+    hip = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(hip) == 1, hip
