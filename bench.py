@@ -198,9 +198,16 @@ def measure(w, steps: int, warmup: int, copies: int) -> tuple:
     live = b.dec.sd_profile_stop()
     us_per_step = (t1 - t0) / steps * 1e6
     dom_us = live[dominant][0] * 1e3 / live[dominant][1]
+    # the same steps again with no profiling at all, to expose its overhead
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    b.run(steps)
+    torch.cuda.synchronize()
+    us_plain = (time.perf_counter() - t0) / steps * 1e6
     kept = b.kept.cpu().numpy()
     ab = algorithmic_bytes(w, kept, b.inp.lengths)
-    return b, dict(us_per_step=us_per_step, avg_us=avg_us, dominant=dominant, dominant_us=dom_us, bytes=ab)
+    return b, dict(us_per_step=us_per_step, us_plain=us_plain, avg_us=avg_us, dominant=dominant, dominant_us=dom_us,
+                   bytes=ab)
 
 
 def main() -> int:
@@ -253,6 +260,7 @@ def main() -> int:
                    "stages": [[s.chunk, s.stride, s.keep] for s in w.stages], "sink": w.sink, "window": w.window,
                    "cache": f"cold: {len(b.args)} rotating copies"},
         "us_per_step": round(r["us_per_step"], 3),
+        "us_per_step_unprofiled": round(r["us_plain"], 3),
         "tokens_per_s": round(w.batch / (r["us_per_step"] * 1e-6), 1),
         "algorithmic_bytes": total,
         "roofline": {"bound": "hbm", "kernel": r["dominant"], "achieved": round(achieved, 2),

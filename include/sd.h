@@ -196,9 +196,10 @@ typedef struct sd_profile {
 } sd_profile;
 
 /* Starts timing: while active, every launch of a kind whose bit is set in
- * `kind_mask` is bracketed by two HIP events recorded on the caller's
- * stream, for at most `max_launches` launches.  Allocates the events (host
- * call; not to be used where allocation is forbidden). */
+ * `kind_mask` carries a start and a stop HIP event in its own dispatch on
+ * the caller's stream (no separate marker packets), for at most
+ * `max_launches` launches.  Allocates the events (host call; not to be used
+ * where allocation is forbidden). */
 sd_status sd_profile_start(sd_ctx* ctx, uint32_t kind_mask, int32_t max_launches);
 
 /* Stops timing: synchronises the device, sums the elapsed times per kind

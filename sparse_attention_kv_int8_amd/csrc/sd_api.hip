@@ -82,7 +82,7 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
     c->max_blocks = int(mb);
     const int BH = cfg.batch * cfg.num_kv_heads;
     int ns = (512 + BH - 1) / BH;
-    ns = ns < 1 ? 1 : ns > 64 ? 64 : ns;
+    ns = ns < 1 ? 1 : ns > 64 ? 64 : ns;      // at most 64 splits (one per lane in the merge)
     const int cap = (c->max_blocks + 3) / 4;
     c->nsplit = ns > cap ? cap : ns;
     const float scale = cfg.softmax_scale > 0.0f ? cfg.softmax_scale : 1.0f / std::sqrt(float(cfg.head_dim));
@@ -96,15 +96,16 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
     return SD_OK;
 }
 
-// Brackets one launch with profiling events when its kind is being timed.
+// Runs one launch, handing it a pair of profiling events (carried by the
+// dispatch itself) when its kind is being timed.
 template <class F>
-hipError_t timed(sd_ctx* c, int kind, hipStream_t s, F&& launch) {
+hipError_t timed(sd_ctx* c, int kind, hipStream_t s, F&& launch_fn) {
+    (void)s;
     const bool on = c->prof_ev && ((c->prof_mask >> kind) & 1u) && c->prof_n < c->prof_max;
-    hipError_t e = hipSuccess;
-    if (on) e = hipEventRecord(c->prof_ev[2 * c->prof_n], s);
-    if (e == hipSuccess) e = launch();
-    if (on && e == hipSuccess) {
-        e = hipEventRecord(c->prof_ev[2 * c->prof_n + 1], s);
+    if (!on) return launch_fn(sd::Timing{});
+    sd::Timing t{c->prof_ev[2 * c->prof_n], c->prof_ev[2 * c->prof_n + 1]};
+    const hipError_t e = launch_fn(t);
+    if (e == hipSuccess) {
         c->prof_kind[c->prof_n] = int8_t(kind);
         ++c->prof_n;
     }
@@ -237,7 +238,8 @@ sd_status sd_quantize_keys(sd_ctx* c, const uint16_t* k, const int32_t* lengths,
     if (!c || !k || !lengths || !k8) return SD_ERR_INVALID_ARG;
     if (!aligned16(k) || !aligned16(k8)) return SD_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return from_hip(timed(c, SD_PROF_QUANTIZE, s, [&] { return sd::launch_quantize_keys(c, k, lengths, k8, absmax, s); }));
+    return from_hip(timed(c, SD_PROF_QUANTIZE, s,
+                          [&](sd::Timing t) { return sd::launch_quantize_keys(c, k, lengths, k8, absmax, s, t); }));
 }
 
 sd_status sd_quantize_query(sd_ctx* c, const uint16_t* q, int8_t* q8, int32_t* qg, void* stream) {
@@ -268,12 +270,16 @@ sd_status sd_decode_step(sd_ctx* c, const uint16_t* q, const uint16_t* k, const 
     }
     hipError_t e = hipSuccess;
     for (int st = 0; st < c->S && e == hipSuccess; ++st)
-        e = timed(c, SD_PROF_STAGE0 + st, s, [&] { return sd::launch_prune_stage(c, st, q, k8, lengths, kept, s); });
+        e = timed(c, SD_PROF_STAGE0 + st, s,
+                  [&](sd::Timing t) { return sd::launch_prune_stage(c, st, q, k8, lengths, kept, s, t); });
     if (e == hipSuccess && c->cfg.values_on_host)
-        e = timed(c, SD_PROF_VALUE_CACHE, s, [&] { return sd::launch_value_cache_update(c, lengths, kept, s); });
+        e = timed(c, SD_PROF_VALUE_CACHE, s,
+                  [&](sd::Timing t) { return sd::launch_value_cache_update(c, lengths, kept, s, t); });
     if (e == hipSuccess)
-        e = timed(c, SD_PROF_ATTEND, s, [&] { return sd::launch_attend(c, q, k, vk, lengths, kept, out, s); });
-    if (e == hipSuccess) e = timed(c, SD_PROF_COMBINE, s, [&] { return sd::launch_combine(c, out, s); });
+        e = timed(c, SD_PROF_ATTEND, s,
+                  [&](sd::Timing t) { return sd::launch_attend(c, q, k, vk, lengths, kept, out, s, t); });
+    if (e == hipSuccess)
+        e = timed(c, SD_PROF_COMBINE, s, [&](sd::Timing t) { return sd::launch_combine(c, out, s, t); });
     return from_hip(e);
 }
 

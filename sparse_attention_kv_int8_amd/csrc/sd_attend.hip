@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
     __shared__ float wm[kAttnWaves][G];
     __shared__ float wl[kAttnWaves][G];
     __shared__ float wacc[kAttnWaves][G][kHeadDim];
-    __shared__ unsigned hist[256];
+    __shared__ unsigned hist[4 * 256];
     __shared__ unsigned tmp[32];
 
     const int sp = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
@@ -226,37 +226,50 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
 }
 
 // Log-sum-exp merge of the splits of one (request, KV head), rounding to bf16.
+// Wave h computes head h's split weights exp2(m_s - M) / sum_s l_s exp2(m_s - M)
+// (one split per lane); then every output is one weighted sum over splits.
+constexpr int kMaxSplit = 64;
+
 template <int G>
 __global__ __launch_bounds__(kAttnThreads) void sd_combine_kernel(const float* __restrict__ part, int nsplit, int Hq,
                                                                  int Hkv, uint16_t* __restrict__ out) {
+    __shared__ float wgt[kMaxSplit][G];
     const int j = blockIdx.x, b = blockIdx.y, bj = b * Hkv + j;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const float* pb = part + int64_t(bj) * nsplit * G * kPartStride;
+    if (wid < G) {
+        const float m = lane < nsplit ? pb[(lane * G + wid) * kPartStride] : -INFINITY;
+        const float l = lane < nsplit ? pb[(lane * G + wid) * kPartStride + 1] : 0.f;
+        const float M = wave_max_f(m);
+        const float f = rescale(m, M);
+        const float Lt = wave_sum_f(l * f);
+        if (lane < nsplit) wgt[lane][wid] = Lt > 0.f ? f / Lt : 0.f;
+    }
+    __syncthreads();
     for (int o = threadIdx.x; o < G * kHeadDim; o += kAttnThreads) {
         const int h = o / kHeadDim, dd = o % kHeadDim;
-        float M = -INFINITY;
-#pragma unroll 8
-        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pb[(s * G + h) * kPartStride]);
-        float a = 0.f, l = 0.f;
-#pragma unroll 8
-        for (int s = 0; s < nsplit; ++s) {
-            const float* ps = pb + (s * G + h) * kPartStride;
-            const float f = rescale(ps[0], M);
-            a = fmaf(ps[2 + dd], f, a);
-            l = fmaf(ps[1], f, l);
+        const float* pa = pb + h * kPartStride + 2 + dd;
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+        int s = 0;
+        for (; s + 3 < nsplit; s += 4) {
+            a0 = fmaf(pa[(s + 0) * G * kPartStride], wgt[s + 0][h], a0);
+            a1 = fmaf(pa[(s + 1) * G * kPartStride], wgt[s + 1][h], a1);
+            a2 = fmaf(pa[(s + 2) * G * kPartStride], wgt[s + 2][h], a2);
+            a3 = fmaf(pa[(s + 3) * G * kPartStride], wgt[s + 3][h], a3);
         }
-        const float o_val = l > 0.f ? a / l : 0.f;
-        out[(int64_t(b) * Hq + j * G + h) * kHeadDim + dd] = f32_to_bf16_rne(o_val);
+        for (; s < nsplit; ++s) a0 = fmaf(pa[s * G * kPartStride], wgt[s][h], a0);
+        out[(int64_t(b) * Hq + j * G + h) * kHeadDim + dd] = f32_to_bf16_rne((a0 + a1) + (a2 + a3));
     }
 }
 
 template <int G>
-static void launch_g(const AttendParams& p, dim3 grid, bool hostv, size_t lds, hipStream_t s) {
-    if (hostv) sd_flash_decode_kernel<G, true><<<grid, kAttnThreads, 0, s>>>(p);
-    else sd_flash_decode_kernel<G, false><<<grid, kAttnThreads, lds, s>>>(p);
+static void launch_g(const AttendParams& p, dim3 grid, bool hostv, size_t lds, hipStream_t s, Timing t) {
+    if (hostv) launch(sd_flash_decode_kernel<G, true>, grid, dim3(kAttnThreads), 0, s, t, p);
+    else launch(sd_flash_decode_kernel<G, false>, grid, dim3(kAttnThreads), lds, s, t, p);
 }
 
 hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                         const int32_t* lengths, int32_t* kept, uint16_t* out, hipStream_t s) {
+                         const int32_t* lengths, int32_t* kept, uint16_t* out, hipStream_t s, Timing t) {
     AttendParams p{};
     p.q = q;
     p.k = k;
@@ -288,9 +301,9 @@ hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const 
     dim3 grid(c->nsplit, c->cfg.num_kv_heads, c->cfg.batch);
     const bool hostv = c->cfg.values_on_host != 0;
     switch (c->G) {
-        case 1: launch_g<1>(p, grid, hostv, lds, s); break;
-        case 2: launch_g<2>(p, grid, hostv, lds, s); break;
-        default: launch_g<4>(p, grid, hostv, lds, s); break;
+        case 1: launch_g<1>(p, grid, hostv, lds, s, t); break;
+        case 2: launch_g<2>(p, grid, hostv, lds, s, t); break;
+        default: launch_g<4>(p, grid, hostv, lds, s, t); break;
     }
     return hipGetLastError();
 }
@@ -299,13 +312,14 @@ hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const 
 
 namespace sd {
 
-hipError_t launch_combine(sd_ctx* c, uint16_t* out, hipStream_t s) {
-    dim3 grid(c->cfg.num_kv_heads, c->cfg.batch);
+hipError_t launch_combine(sd_ctx* c, uint16_t* out, hipStream_t s, Timing t) {
+    dim3 grid(c->cfg.num_kv_heads, c->cfg.batch), block(kAttnThreads);
     const int Hq = c->cfg.num_q_heads, Hkv = c->cfg.num_kv_heads;
+    const float* part = c->part;
     switch (c->G) {
-        case 1: sd_combine_kernel<1><<<grid, kAttnThreads, 0, s>>>(c->part, c->nsplit, Hq, Hkv, out); break;
-        case 2: sd_combine_kernel<2><<<grid, kAttnThreads, 0, s>>>(c->part, c->nsplit, Hq, Hkv, out); break;
-        default: sd_combine_kernel<4><<<grid, kAttnThreads, 0, s>>>(c->part, c->nsplit, Hq, Hkv, out); break;
+        case 1: launch(sd_combine_kernel<1>, grid, block, 0, s, t, part, c->nsplit, Hq, Hkv, out); break;
+        case 2: launch(sd_combine_kernel<2>, grid, block, 0, s, t, part, c->nsplit, Hq, Hkv, out); break;
+        default: launch(sd_combine_kernel<4>, grid, block, 0, s, t, part, c->nsplit, Hq, Hkv, out); break;
     }
     return hipGetLastError();
 }

@@ -67,73 +67,94 @@ __device__ __forceinline__ float sum8_f(float v) {
     return v;
 }
 
-// Max / sum across the 8 lane groups of a wave (lanes differing in bits 3..5).
+// Max / sum across the 8 lane groups of a wave (lanes differing in bits
+// 3..5), for values that are equal inside each group of 8: row_ror:8 pairs
+// the two groups of a row, readlane combines the four rows.  The result is
+// wave-uniform.
 __device__ __forceinline__ int max_groups_i(int v) {
     v = max(v, dpp_i<kDppRor8>(v));
-    v = max(v, __shfl_xor(v, 16));
-    v = max(v, __shfl_xor(v, 32));
-    return v;
+    return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ float rl_f(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 __device__ __forceinline__ float max_groups_f(float v) {
     v = fmaxf(v, dpp_f<kDppRor8>(v));
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    return fmaxf(fmaxf(rl_f(v, 0), rl_f(v, 16)), fmaxf(rl_f(v, 32), rl_f(v, 48)));
 }
 __device__ __forceinline__ float sum_groups_f(float v) {
     v += dpp_f<kDppRor8>(v);
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
+    return (rl_f(v, 0) + rl_f(v, 16)) + (rl_f(v, 32) + rl_f(v, 48));
 }
 
-__device__ __forceinline__ int wave_max_i(int v) {
-    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-    return v;
+// ------------------------------------------------ wave-wide (DPP) ops ----
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele inside each row of
+// 16 lanes (row_shr 1, 2, 4, 8), then row_bcast:15 and row_bcast:31 carry
+// the row totals forward.
+__device__ __forceinline__ unsigned wave_incl_scan(unsigned v) {
+    int x = int(v);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
+    return unsigned(x);
+}
+__device__ __forceinline__ unsigned wave_sum_u(unsigned v) {
+    return unsigned(__builtin_amdgcn_readlane(int(wave_incl_scan(v)), 63));
+}
+// Butterfly inside rows of 16 lanes, then the four row results.
+template <class Op>
+__device__ __forceinline__ unsigned wave_reduce_u(unsigned v, Op op) {
+    v = op(v, unsigned(dpp_i<kDppXor1>(int(v))));
+    v = op(v, unsigned(dpp_i<kDppXor2>(int(v))));
+    v = op(v, unsigned(dpp_i<kDppHalfMirror>(int(v))));
+    v = op(v, unsigned(dpp_i<0x140>(int(v))));          // row_mirror
+    const unsigned r0 = unsigned(__builtin_amdgcn_readlane(int(v), 0));
+    const unsigned r1 = unsigned(__builtin_amdgcn_readlane(int(v), 16));
+    const unsigned r2 = unsigned(__builtin_amdgcn_readlane(int(v), 32));
+    const unsigned r3 = unsigned(__builtin_amdgcn_readlane(int(v), 48));
+    return op(op(r0, r1), op(r2, r3));
 }
 __device__ __forceinline__ unsigned wave_max_u(unsigned v) {
-    for (int o = 32; o > 0; o >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, o));
-    return v;
+    return wave_reduce_u(v, [](unsigned a, unsigned b) { return a > b ? a : b; });
 }
 __device__ __forceinline__ unsigned wave_min_u(unsigned v) {
-    for (int o = 32; o > 0; o >>= 1) v = min(v, (unsigned)__shfl_xor((int)v, o));
-    return v;
+    return wave_reduce_u(v, [](unsigned a, unsigned b) { return a < b ? a : b; });
 }
+
 __device__ __forceinline__ float wave_max_f(float v) {
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    return __uint_as_float(wave_reduce_u(__float_as_uint(v), [](unsigned a, unsigned b) {
+        return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+    }));
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+    return __uint_as_float(wave_reduce_u(__float_as_uint(v), [](unsigned a, unsigned b) {
+        return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+    }));
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ unsigned wave_incl_scan(unsigned v) {
-    const int lane = threadIdx.x & 63;
-    for (int o = 1; o < 64; o <<= 1) {
-        unsigned t = (unsigned)__shfl_up((int)v, o);
-        if (lane >= o) v += t;
-    }
-    return v;
-}
-
-// Exclusive prefix sum over the block (NT threads, NT % 64 == 0).
-// `tmp` holds NT/64 + 1 words of LDS; returns the block total in *total.
+// Exclusive prefix sum over the block (NT threads, NT % 64 == 0, NT <= 1024).
+// `tmp` holds NT/64 words of LDS; returns the block total in *total.
 template <int NT>
 __device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* tmp, unsigned* total) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     constexpr int NW = NT / 64;
-    unsigned incl = wave_incl_scan(v);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const unsigned incl = wave_incl_scan(v);
     if (lane == 63) tmp[wid] = incl;
     __syncthreads();
-    if (wid == 0) {
-        unsigned w = lane < NW ? tmp[lane] : 0u;
-        unsigned wi = wave_incl_scan(w);
-        if (lane < NW) tmp[lane] = wi - w;
-        if (lane == NW - 1) tmp[NW] = wi;
+    unsigned before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const unsigned t = tmp[w];
+        before += w < wid ? t : 0u;
+        all += t;
     }
+    *total = all;
     __syncthreads();
-    unsigned r = tmp[wid] + incl - v;
-    *total = tmp[NW];
-    __syncthreads();
-    return r;
+    return before + incl - v;
 }
 
 // |x| of the two bf16 values of a dword, as bit patterns; max of the two.

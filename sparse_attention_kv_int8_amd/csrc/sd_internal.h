@@ -1,8 +1,11 @@
 // Library-internal context and kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <utility>
 
 #include "../../include/sd.h"
 
@@ -81,15 +84,33 @@ struct sd_ctx {
 
 namespace sd {
 
+// Optional profiling timestamps carried by a kernel dispatch itself
+// (hipExtLaunchKernelGGL), so that timing adds no marker packets between
+// kernels.  start/stop may each be null.
+struct Timing {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
+template <typename... KArgs, typename... Args>
+inline void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t s, Timing t,
+                   Args&&... args) {
+    if (t.start || t.stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, uint32_t(lds), s, t.start, t.stop, 0u, std::forward<Args>(args)...);
+    else
+        kernel<<<grid, block, lds, s>>>(std::forward<Args>(args)...);
+}
+
 hipError_t launch_quantize_keys(sd_ctx* c, const uint16_t* k, const int32_t* lengths, int8_t* k8,
-                                float* absmax, hipStream_t s);
+                                float* absmax, hipStream_t s, Timing t = {});
 hipError_t launch_quantize_query(sd_ctx* c, const uint16_t* q, int8_t* q8, int32_t* qg, hipStream_t s);
 hipError_t launch_prune_stage(sd_ctx* c, int stage, const uint16_t* q, const int8_t* k8,
-                              const int32_t* lengths, int32_t* kept, hipStream_t s);
+                              const int32_t* lengths, int32_t* kept, hipStream_t s, Timing t = {});
 hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                         const int32_t* lengths, int32_t* kept, uint16_t* out, hipStream_t s);
-hipError_t launch_combine(sd_ctx* c, uint16_t* out, hipStream_t s);
-hipError_t launch_value_cache_update(sd_ctx* c, const int32_t* lengths, int32_t* kept, hipStream_t s);
+                         const int32_t* lengths, int32_t* kept, uint16_t* out, hipStream_t s, Timing t = {});
+hipError_t launch_combine(sd_ctx* c, uint16_t* out, hipStream_t s, Timing t = {});
+hipError_t launch_value_cache_update(sd_ctx* c, const int32_t* lengths, int32_t* kept, hipStream_t s,
+                                     Timing t = {});
 hipError_t launch_value_cache_reset(sd_ctx* c, hipStream_t s);
 StageDev stage_dev(const sd_ctx* c, int st);
 

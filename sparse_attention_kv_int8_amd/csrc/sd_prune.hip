@@ -117,7 +117,7 @@ __device__ __forceinline__ void split_query(const int* Qlds, int sl, u32x4& qh, 
 __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PruneParams p) {
     extern __shared__ uint32_t dyn[];                // keys [prev.ncand] then sel [prev.keep]
     __shared__ int Qlds[kHeadDim];
-    __shared__ unsigned hist[256];
+    __shared__ unsigned hist[4 * 256];
     __shared__ unsigned tmp[32];
 
     const int j = blockIdx.y, b = blockIdx.z;
@@ -177,7 +177,7 @@ StageDev stage_dev(const sd_ctx* c, int st) {
 }
 
 hipError_t launch_prune_stage(sd_ctx* c, int st, const uint16_t* q, const int8_t* k8, const int32_t* lengths,
-                              int32_t* kept, hipStream_t s) {
+                              int32_t* kept, hipStream_t s, Timing t) {
     PruneParams p{};
     p.q = q;
     p.k8 = k8;
@@ -202,7 +202,7 @@ hipError_t launch_prune_stage(sd_ctx* c, int st, const uint16_t* q, const int8_t
         lds = (size_t(p.prev.ncand) + size_t(p.prev.keep)) * 4;
     }
     dim3 grid(c->st[st].nwg, c->cfg.num_kv_heads, c->cfg.batch);
-    sd_prune_stage_kernel<<<grid, kPruneThreads, lds, s>>>(p);
+    launch(sd_prune_stage_kernel, grid, dim3(kPruneThreads), lds, s, t, p);
     return hipGetLastError();
 }
 

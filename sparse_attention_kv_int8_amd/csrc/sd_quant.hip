@@ -119,15 +119,16 @@ __global__ __launch_bounds__(256) void sd_quantize_query_kernel(const uint16_t* 
 }  // namespace
 
 hipError_t launch_quantize_keys(sd_ctx* c, const uint16_t* k, const int32_t* lengths, int8_t* k8,
-                                float* absmax, hipStream_t s) {
+                                float* absmax, hipStream_t s, Timing t) {
     const int BH = c->cfg.batch * c->cfg.num_kv_heads;
-    sd_absmax_init_kernel<<<(BH + 255) / 256, 256, 0, s>>>(c->absmax_bits, BH);
+    launch(sd_absmax_init_kernel, dim3((BH + 255) / 256), dim3(256), 0, s, Timing{t.start, nullptr},
+           c->absmax_bits, BH);
     const int nwg = int((c->Lmax + kQuantRowsPerWg - 1) / kQuantRowsPerWg);
     dim3 grid(nwg, BH);
-    sd_absmax_kernel<<<grid, kQuantThreads, 0, s>>>(k, lengths, c->Lmax, c->cfg.num_kv_heads,
-                                                   c->absmax_bits, c->flag);
-    sd_quantize_kernel<<<grid, kQuantThreads, 0, s>>>(k, lengths, c->Lmax, c->cfg.num_kv_heads,
-                                                     c->absmax_bits, k8, absmax);
+    launch(sd_absmax_kernel, grid, dim3(kQuantThreads), 0, s, Timing{}, k, lengths, c->Lmax,
+           c->cfg.num_kv_heads, c->absmax_bits, c->flag);
+    launch(sd_quantize_kernel, grid, dim3(kQuantThreads), 0, s, Timing{nullptr, t.stop}, k, lengths, c->Lmax,
+           c->cfg.num_kv_heads, (const unsigned*)c->absmax_bits, k8, absmax);
     return hipGetLastError();
 }
 

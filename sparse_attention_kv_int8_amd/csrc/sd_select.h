@@ -39,7 +39,13 @@ __device__ __forceinline__ int64_t cand_start(const StageDev& st, bool first_sta
 // Exact top-K of n keys (0 = no candidate; otherwise larger is better, ties
 // to the lower index).  keys: LDS [n].  Writes the kept indices ascending to
 // sel[0..kept) and returns kept = min(K, #valid).  All NT threads call it.
-// hist: 256 words of LDS; tmp: 32 words of LDS.
+// hist: NT/64 * 256 words of LDS (one histogram per wave); tmp: 32 words.
+//
+// Radix select over the bits in which the valid keys differ, 8 bits per
+// pass from the top: each pass histograms the keys that share the prefix
+// found so far and picks the digit at which the count of larger keys
+// reaches K.  The threshold key T and the number of keys equal to T to keep
+// (lowest indices first) then drive one ordered compaction.
 template <int NT>
 __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, unsigned* hist, unsigned* tmp) {
     constexpr int NW = NT / kWave;
@@ -50,7 +56,7 @@ __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, unsigned
         const unsigned k = keys[i];
         if (k) { ++cnt; kmn = min(kmn, k); kmx = max(kmx, k); }
     }
-    for (int o = 32; o > 0; o >>= 1) cnt += (unsigned)__shfl_xor((int)cnt, o);
+    cnt = wave_sum_u(cnt);
     kmn = wave_min_u(kmn);
     kmx = wave_max_u(kmx);
     if (lane == 0) { tmp[wid] = cnt; tmp[NW + wid] = kmn; tmp[2 * NW + wid] = kmx; }
@@ -58,6 +64,7 @@ __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, unsigned
     unsigned nvalid = 0;
     kmn = 0xffffffffu;
     kmx = 0;
+#pragma unroll
     for (int w = 0; w < NW; ++w) { nvalid += tmp[w]; kmn = min(kmn, tmp[NW + w]); kmx = max(kmx, tmp[2 * NW + w]); }
     __syncthreads();
 
@@ -68,24 +75,34 @@ __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, unsigned
         int bits = diff ? 32 - __clz(diff) : 0;      // low bits in which keys differ
         unsigned prefix = bits >= 32 ? 0u : (kmx >> bits) << bits;
         int remaining = K;
+        unsigned* my_hist = hist + wid * 256;
         while (bits > 0) {
             const int w = bits < 8 ? bits : 8;
             const int shift = bits - w;
-            for (int i = tid; i < 256; i += NT) hist[i] = 0;
+            for (int i = tid; i < NW * 256; i += NT) hist[i] = 0;
             __syncthreads();
             const unsigned hi_mask = bits >= 32 ? 0u : ~((1u << bits) - 1u);
+            const unsigned want = prefix & hi_mask, dmask = (1u << w) - 1u;
             for (int i = tid; i < n; i += NT) {
                 const unsigned k = keys[i];
-                if (k && (k & hi_mask) == (prefix & hi_mask)) atomicAdd(hist + ((k >> shift) & ((1u << w) - 1u)), 1u);
+                if (k && (k & hi_mask) == want) atomicAdd(my_hist + ((k >> shift) & dmask), 1u);
             }
             __syncthreads();
             if (wid == 0) {
                 // lane l owns bins 255-4l .. 252-4l (descending digit order)
-                unsigned h[4], s = 0;
-                for (int u = 0; u < 4; ++u) { h[u] = hist[255 - 4 * lane - u]; s += h[u]; }
-                const unsigned incl = wave_incl_scan(s), excl = incl - s;
+                unsigned h[4], s4 = 0;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    unsigned c = 0;
+#pragma unroll
+                    for (int v = 0; v < NW; ++v) c += hist[v * 256 + 255 - 4 * lane - u];
+                    h[u] = c;
+                    s4 += c;
+                }
+                const unsigned incl = wave_incl_scan(s4), excl = incl - s4;
                 if (excl < unsigned(remaining) && unsigned(remaining) <= incl) {
                     unsigned c = excl;
+#pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         if (c + h[u] >= unsigned(remaining)) {
                             tmp[28] = unsigned(255 - 4 * lane - u);
@@ -101,7 +118,6 @@ __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, unsigned
             remaining -= int(above);
             prefix |= dd << shift;
             bits = shift;
-            __syncthreads();
         }
         T = prefix;
         need_eq = remaining;

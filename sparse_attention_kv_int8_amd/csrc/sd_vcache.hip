@@ -60,7 +60,7 @@ struct VcStepParams {
 
 __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParams p) {
     extern __shared__ uint32_t dyn[];    // keys [last.ncand], sel [last.keep]
-    __shared__ unsigned hist[256];
+    __shared__ unsigned hist[4 * 256];
     __shared__ unsigned tmp[32];
     const ValueCache& vc = p.vc;
     const int max_blocks = p.max_blocks;
@@ -170,7 +170,7 @@ hipError_t launch_value_cache_reset(sd_ctx* c, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_value_cache_update(sd_ctx* c, const int32_t* lengths, int32_t* kept, hipStream_t s) {
+hipError_t launch_value_cache_update(sd_ctx* c, const int32_t* lengths, int32_t* kept, hipStream_t s, Timing t) {
     VcStepParams p{};
     p.vc = c->vc;
     const int S = c->S;
@@ -191,7 +191,7 @@ hipError_t launch_value_cache_update(sd_ctx* c, const int32_t* lengths, int32_t*
     p.step = int32_t(c->vc_step);
     const size_t lds = (size_t(p.last.ncand) + size_t(p.last.keep)) * 4;
     dim3 grid(c->cfg.num_kv_heads, c->cfg.batch);
-    sd_vcache_step_kernel<<<grid, kLruThreads, lds, s>>>(p);
+    launch(sd_vcache_step_kernel, grid, dim3(kLruThreads), lds, s, t, p);
     ++c->vc_step;
     return hipGetLastError();
 }

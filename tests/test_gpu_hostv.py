@@ -79,5 +79,6 @@ def test_hostv_reset_starts_cold():
     assert st.steps == 1 and st.last_hits == 0 and st.last_misses == st.last_needed
 
 
+@pytest.mark.timeout(900)
 def test_hostv_full_3m_workload():
     run_sequence(WORKLOADS["ctx_3m_hostv"], check_every=4)
