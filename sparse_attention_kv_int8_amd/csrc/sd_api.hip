@@ -62,6 +62,10 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
         const int64_t nc = s == 0 ? (cfg.max_context + in.chunk - 1) / in.chunk
                                   : int64_t(cfg.stage[s - 1].keep) * (cfg.stage[s - 1].chunk / in.chunk);
         if (nc + in.keep > kMaxCandidates) return SD_ERR_UNSUPPORTED;
+        // the select reduces groups of 1024 candidates to their top `keep`
+        // and then picks from at most 1024 survivors
+        const int64_t groups = (nc + 1023) / 1024;
+        if (in.keep < nc && groups > 1 && groups * in.keep > 1024) return SD_ERR_UNSUPPORTED;
         g.ncand = int(nc);
         g.koff = koff;
         koff += in.keep;
@@ -164,6 +168,16 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
     {
         hipError_t e0 = hipGetDevice(&c->device);
         if (e0 != hipSuccess) { delete c; return from_hip(e0, "hipGetDevice"); }
+        int lds_max = 0;
+        e0 = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device);
+        if (e0 != hipSuccess) { delete c; return from_hip(e0, "hipDeviceGetAttribute"); }
+        // dynamic LDS of the largest kernel (the decode kernel: last-stage select
+        // and block list) plus its static LDS (partials of 4 waves)
+        const sd::StageGeom& g = c->st[c->S - 1];
+        const int64_t groups = (g.ncand + 1023) / 1024;
+        const int64_t words = g.ncand + g.keep + (groups > 1 ? groups * g.keep + groups : 0) + c->max_blocks;
+        const int64_t static_bytes = 4 * (4 * (2 + sd::kHeadDim) * c->G + 64);
+        if (words * 4 + static_bytes > lds_max) { delete c; return SD_ERR_UNSUPPORTED; }
     }
 
     const size_t B = size_t(cfg->batch), H = size_t(cfg->num_kv_heads), BH = B * H;

@@ -71,11 +71,11 @@ __device__ __forceinline__ float rescale(float a, float m) {
 
 template <int G, bool HOSTV>
 __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendParams p) {
-    extern __shared__ uint32_t dyn[];   // device values: keys [last.ncand], sel [last.keep], blocks [max_blocks]
+    extern __shared__ uint32_t dyn[];   // device values: keys [last.ncand], sel [last.keep], select scratch,
+                                        // blocks [max_blocks]
     __shared__ float wm[kAttnWaves][G];
     __shared__ float wl[kAttnWaves][G];
     __shared__ float wacc[kAttnWaves][G][kHeadDim];
-    __shared__ unsigned hist[4 * 256];
     __shared__ unsigned tmp[32];
 
     const int sp = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
@@ -93,10 +93,11 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
     } else {
         uint32_t* keys = dyn;
         int* sel = reinterpret_cast<int*>(dyn + p.last.ncand);
-        uint32_t* bl = dyn + p.last.ncand + p.last.keep;
+        int* cand = sel + p.last.keep;
+        uint32_t* bl = dyn + p.last.ncand + p.last.keep + select_cand_words(p.last.ncand, p.last.keep);
         int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
         const int nk = kept_of_stage<kAttnThreads>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
-                                                   p.first_stage ? nullptr : kept_bj + p.pp_koff, L, keys, sel, hist, tmp);
+                                                   p.first_stage ? nullptr : kept_bj + p.pp_koff, L, keys, sel, cand, tmp);
         if (sp == 0)
             for (int i = threadIdx.x; i < p.last.keep; i += kAttnThreads) kept_bj[p.last.koff + i] = i < nk ? sel[i] : -1;
         nb = build_attended<kAttnThreads>(sel, nk, p.last.chunk, L, p.sink, p.window, bl, tmp);
@@ -292,7 +293,8 @@ hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const 
     p.keep_total = c->keep_total;
     p.sink = c->cfg.sink;
     p.window = c->cfg.window;
-    const size_t lds = (size_t(p.last.ncand) + size_t(p.last.keep) + size_t(c->max_blocks)) * 4;
+    const size_t lds = (size_t(p.last.ncand) + size_t(p.last.keep) +
+                        size_t(select_cand_words(p.last.ncand, p.last.keep)) + size_t(c->max_blocks)) * 4;
     p.Lmax = c->Lmax;
     p.Hq = c->cfg.num_q_heads;
     p.Hkv = c->cfg.num_kv_heads;

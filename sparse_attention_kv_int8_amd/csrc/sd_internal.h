@@ -7,7 +7,7 @@
 
 #include <utility>
 
-#include "../../include/sd.h"
+#include "sd.h"
 
 namespace sd {
 

@@ -19,6 +19,12 @@
 
 namespace sd {
 
+// LDS words the select needs besides keys and sel.
+__host__ __device__ inline int select_cand_words(int n, int K) {
+    const int groups = (n + 1023) / 1024;
+    return groups > 1 ? groups * K + groups : 0;
+}
+
 // Start of candidate i of a stage (token position), or -1 if it does not
 // exist.  Stage 0 candidates are i * chunk; later ones are children of the
 // previous stage's kept starts `parents` (ascending, -1 padded).
@@ -36,133 +42,157 @@ __device__ __forceinline__ int64_t cand_start(const StageDev& st, bool first_sta
     return x < L ? x : -1;
 }
 
-// Exact top-K of n keys (0 = no candidate; otherwise larger is better, ties
-// to the lower index).  keys: LDS [n].  Writes the kept indices ascending to
-// sel[0..kept) and returns kept = min(K, #valid).  All NT threads call it.
-// hist: NT/64 * 256 words of LDS (one histogram per wave); tmp: 32 words.
+// ------------------------------------------------------------------------
+// Exact top-K select.
 //
-// Radix select over the bits in which the valid keys differ, 8 bits per
-// pass from the top: each pass histograms the keys that share the prefix
-// found so far and picks the digit at which the count of larger keys
-// reaches K.  The threshold key T and the number of keys equal to T to keep
-// (lowest indices first) then drive one ordered compaction.
-template <int NT>
-__device__ int select_top(const uint32_t* keys, int n, int K, int* sel, unsigned* hist, unsigned* tmp) {
-    constexpr int NW = NT / kWave;
-    static_assert(3 * NW <= 28, "tmp layout: 3 words per wave below the digit slots 28/29");
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    unsigned cnt = 0, kmn = 0xffffffffu, kmx = 0;
-    for (int i = tid; i < n; i += NT) {
-        const unsigned k = keys[i];
-        if (k) { ++cnt; kmn = min(kmn, k); kmx = max(kmx, k); }
-    }
-    cnt = wave_sum_u(cnt);
-    kmn = wave_min_u(kmn);
-    kmx = wave_max_u(kmx);
-    if (lane == 0) { tmp[wid] = cnt; tmp[NW + wid] = kmn; tmp[2 * NW + wid] = kmx; }
-    __syncthreads();
-    unsigned nvalid = 0;
-    kmn = 0xffffffffu;
-    kmx = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) { nvalid += tmp[w]; kmn = min(kmn, tmp[NW + w]); kmx = max(kmx, tmp[2 * NW + w]); }
-    __syncthreads();
+// Keys are uint32 with 0 meaning "no candidate"; a larger key is better and
+// equal keys go to the lower index.  The threshold T (the K-th largest key)
+// is built bit by bit from the top: T keeps a bit when at least K keys are
+// >= (prefix | bit).  Counting uses one ballot + popcount per register-held
+// key, inside a single wave, so the search needs no barrier and no LDS
+// atomics.  Keys > T are kept, and of the keys equal to T the lowest
+// indices, K - #(keys > T) of them.
+// ------------------------------------------------------------------------
+constexpr int kSelGroup = 1024;              // keys one wave selects from (16 per lane)
 
-    unsigned T = 0;          // threshold key
-    int need_eq = 0;         // keys equal to T that are kept (lowest indices first)
-    if (int(nvalid) > K) {
+__device__ __forceinline__ int wave_count_ge(const uint32_t (&kk)[16], int E, uint32_t c) {
+    int n = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+        if (u < E) n += __popcll(__ballot(kk[u] >= c));
+    return n;
+}
+
+// One wave: top-K of m keys key(i) = keys[idx ? idx[i] : i] (m <= 1024).
+// Lane l owns the contiguous positions [l*E, l*E + E).  Writes the kept
+// positions i (ascending) to out[0..kept); returns kept = min(K, #valid).
+__device__ __forceinline__ int wave_select(const uint32_t* keys, const int* idx, int m, int K, int* out) {
+    const int lane = threadIdx.x & 63;
+    const int E = (m + 63) >> 6;
+    uint32_t kk[16];
+    unsigned kmn = 0xffffffffu, kmx = 0, nv = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int i = lane * E + u;
+        kk[u] = (u < E && i < m) ? keys[idx ? idx[i] : i] : 0u;
+        if (kk[u]) { ++nv; kmn = min(kmn, kk[u]); kmx = max(kmx, kk[u]); }
+    }
+    const int nvalid = int(wave_sum_u(nv));
+    uint32_t T = 0;
+    int need_eq = 0;
+    if (nvalid > K) {
+        kmn = wave_min_u(kmn);
+        kmx = wave_max_u(kmx);
         const unsigned diff = kmx ^ kmn;
-        int bits = diff ? 32 - __clz(diff) : 0;      // low bits in which keys differ
-        unsigned prefix = bits >= 32 ? 0u : (kmx >> bits) << bits;
-        int remaining = K;
-        unsigned* my_hist = hist + wid * 256;
-        while (bits > 0) {
-            const int w = bits < 8 ? bits : 8;
-            const int shift = bits - w;
-            for (int i = tid; i < NW * 256; i += NT) hist[i] = 0;
-            __syncthreads();
-            const unsigned hi_mask = bits >= 32 ? 0u : ~((1u << bits) - 1u);
-            const unsigned want = prefix & hi_mask, dmask = (1u << w) - 1u;
-            for (int i = tid; i < n; i += NT) {
-                const unsigned k = keys[i];
-                if (k && (k & hi_mask) == want) atomicAdd(my_hist + ((k >> shift) & dmask), 1u);
-            }
-            __syncthreads();
-            if (wid == 0) {
-                // lane l owns bins 255-4l .. 252-4l (descending digit order)
-                unsigned h[4], s4 = 0;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    unsigned c = 0;
-#pragma unroll
-                    for (int v = 0; v < NW; ++v) c += hist[v * 256 + 255 - 4 * lane - u];
-                    h[u] = c;
-                    s4 += c;
-                }
-                const unsigned incl = wave_incl_scan(s4), excl = incl - s4;
-                if (excl < unsigned(remaining) && unsigned(remaining) <= incl) {
-                    unsigned c = excl;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        if (c + h[u] >= unsigned(remaining)) {
-                            tmp[28] = unsigned(255 - 4 * lane - u);
-                            tmp[29] = c;
-                            break;
-                        }
-                        c += h[u];
-                    }
-                }
-            }
-            __syncthreads();
-            const unsigned dd = tmp[28], above = tmp[29];
-            remaining -= int(above);
-            prefix |= dd << shift;
-            bits = shift;
+        const int hb = diff ? 32 - __clz(diff) : 0;
+        uint32_t prefix = hb >= 32 ? 0u : (kmx >> hb) << hb;
+        for (int b = hb - 1; b >= 0; --b) {
+            const uint32_t c = prefix | (1u << b);
+            if (wave_count_ge(kk, E, c) >= K) prefix = c;
         }
         T = prefix;
-        need_eq = remaining;
+        need_eq = K - wave_count_ge(kk, E, T + 1u);
     }
-    // Compaction in index order: thread t owns the contiguous range [i0, i1).
-    const int per = (n + NT - 1) / NT;
-    const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
+    // ordered compaction: (count of keys > T, count of keys == T) per lane, scanned
     unsigned g = 0, e = 0;
-    for (int i = i0; i < i1; ++i) {
-        const unsigned k = keys[i];
-        g += k > T;
-        e += (k == T) && k;
-    }
-    unsigned total;
-    const unsigned ex = block_excl_scan<NT>((g << 16) | e, tmp, &total);
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+        if (u < E) { g += kk[u] > T; e += (kk[u] == T) && kk[u]; }
+    const unsigned packed = (g << 16) | e;
+    const unsigned ex = wave_incl_scan(packed) - packed;
     g = ex >> 16;
     e = ex & 0xffffu;
-    for (int i = i0; i < i1; ++i) {
-        const unsigned k = keys[i];
-        if (k > T) {
-            sel[g + min(e, unsigned(need_eq))] = i;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        if (u >= E) break;
+        const int i = lane * E + u;
+        if (kk[u] > T) {
+            out[g + min(e, unsigned(need_eq))] = i;
             ++g;
-        } else if (k == T && k) {
-            if (e < unsigned(need_eq)) sel[g + e] = i;
+        } else if (kk[u] == T && kk[u]) {
+            if (e < unsigned(need_eq)) out[g + e] = i;
             ++e;
         }
     }
-    __syncthreads();
-    return min(K, int(nvalid));
+    return min(K, nvalid);
+}
+
+// Block-level: top-K of n keys in LDS (n <= 16 * kSelGroup).  Groups of
+// kSelGroup keys are reduced to their own top-K by the waves in parallel
+// (exact: a key among the global top K is among its group's top K under the
+// same order); one wave then selects from the groups' survivors.  sel
+// receives the kept indices ascending.  cand: LDS, ngroups * K + 16 ints.
+template <int NT>
+__device__ int select_top(const uint32_t* keys, int n, int K, int* sel, int* cand, unsigned* tmp) {
+    constexpr int NW = NT / kWave;
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int ngroups = (n + kSelGroup - 1) / kSelGroup;
+    int kept;
+    if (K >= n) {
+        // every valid key is kept: ordered compaction
+        const int per = (n + NT - 1) / NT;
+        const int i0 = min(n, int(threadIdx.x) * per), i1 = min(n, i0 + per);
+        unsigned c = 0;
+        for (int i = i0; i < i1; ++i) c += keys[i] != 0u;
+        unsigned total;
+        unsigned pos = block_excl_scan<NT>(c, tmp, &total);
+        for (int i = i0; i < i1; ++i)
+            if (keys[i]) sel[pos++] = i;
+        __syncthreads();
+        kept = int(total);
+    } else if (ngroups <= 1) {
+        if (wid == 0) {
+            const int r = wave_select(keys, nullptr, n, K, sel);
+            if (lane == 0) tmp[0] = unsigned(r);
+        }
+        __syncthreads();
+        kept = int(tmp[0]);
+    } else {
+        int* counts = cand + ngroups * K;           // [ngroups]
+        for (int g = wid; g < ngroups; g += NW) {
+            const int base = g * kSelGroup;
+            const int m = min(kSelGroup, n - base);
+            int* out = cand + g * K;
+            const int r = wave_select(keys + base, nullptr, m, K, out);
+            for (int i = lane; i < r; i += kWave) out[i] += base;
+            if (lane == 0) counts[g] = r;
+        }
+        __syncthreads();
+        if (wid == 0) {
+            // compact the survivors in group order (ascending index) in place
+            int off = 0;
+            for (int g = 0; g < ngroups; ++g) {
+                const int r = counts[g];
+                for (int i = lane; i < r; i += kWave) cand[off + i] = cand[g * K + i];
+                off += r;
+                __builtin_amdgcn_wave_barrier();
+            }
+            const int r = wave_select(keys, cand, off, K, sel);
+            // positions -> indices
+            for (int i = lane; i < r; i += kWave) sel[i] = cand[sel[i]];
+            if (lane == 0) tmp[0] = unsigned(r);
+        }
+        __syncthreads();
+        kept = int(tmp[0]);
+    }
+    return kept;
 }
 
 // Kept set of stage `st` for one (request, KV head), from that stage's
 // scores (global, INT32_MIN = no candidate): sel[0..nk) receives the kept
 // chunk starts, ascending.  `parents` are the kept starts of the stage
-// before (global or LDS; unused for the first stage).  keys: LDS [ncand].
+// before (global or LDS; unused for the first stage).  keys: LDS [ncand];
+// cand: LDS [select_cand_words(ncand, keep)].
 template <int NT>
 __device__ int kept_of_stage(const StageDev& st, bool first_stage, const int32_t* scores_bj,
-                             const int32_t* parents, int64_t L, uint32_t* keys, int* sel, unsigned* hist,
+                             const int32_t* parents, int64_t L, uint32_t* keys, int* sel, int* cand,
                              unsigned* tmp) {
     for (int i = threadIdx.x; i < st.ncand; i += NT) {
         const int s = scores_bj[i];
         keys[i] = s == INT32_MIN ? 0u : (uint32_t(s) ^ 0x80000000u);
     }
     __syncthreads();
-    const int nk = select_top<NT>(keys, st.ncand, st.keep, sel, hist, tmp);
+    const int nk = select_top<NT>(keys, st.ncand, st.keep, sel, cand, tmp);
     for (int i = threadIdx.x; i < nk; i += NT) sel[i] = int(cand_start(st, first_stage, parents, sel[i], L));
     __syncthreads();
     return nk;
@@ -171,10 +201,18 @@ __device__ int kept_of_stage(const StageDev& st, bool first_stage, const int32_t
 // Attended 8-token blocks of one (request, KV head): the kept last-stage
 // chunks (starts kept_s[0..nk), ascending, chunk a multiple of 8), the sink
 // [0, sink) and the window [L - window, L), each token once, as ascending
-// (block << 8 | token mask) words.  Returns the count; all NT threads call.
+// (block << 8 | token mask) words.  Returns the count (the same in every
+// thread); the list is complete after the closing barrier.
+//
+// Layout of the output: sink-range blocks, then the kept blocks strictly
+// between the two ranges, then the window-range blocks (one merged range
+// when sink and window touch).  The kept blocks form a sorted list (index
+// q -> block kept_s[q / bpc] / 8 + q % bpc), so the middle ones are the
+// contiguous slice between two binary searches.
 template <int NT>
 __device__ int build_attended(const int32_t* kept_s, int nk, int chunk, int64_t L, int sink, int window,
                               uint32_t* blocks, unsigned* tmp) {
+    (void)tmp;
     const int tid = threadIdx.x;
     const int64_t s_end = min<int64_t>(sink, L);
     const int64_t w0 = window > 0 ? max<int64_t>(0, L - window) : L;
@@ -184,39 +222,46 @@ __device__ int build_attended(const int32_t* kept_s, int nk, int chunk, int64_t 
     const int64_t nr1 = merged ? wb1 : sb1;
     const int64_t nr2 = merged ? 0 : wb1 - wb0;
     const int bpc = chunk >> 3;
-    const int nmc = nk * bpc;
-
-    auto kept_block = [&](int64_t blk) -> bool {
-        int lo = 0, hi = nk - 1, pos = -1;
-        while (lo <= hi) {
+    const int nq = nk * bpc;
+    auto blk_at = [&](int q) -> int64_t { return (int64_t(kept_s[q / bpc]) >> 3) + (q % bpc); };
+    auto lower = [&](int64_t v) -> int {     // first q with blk_at(q) >= v
+        int lo = 0, hi = nq;
+        while (lo < hi) {
             const int mid = (lo + hi) >> 1;
-            if (int64_t(kept_s[mid]) <= blk * 8) { pos = mid; lo = mid + 1; } else { hi = mid - 1; }
+            if (blk_at(mid) < v) lo = mid + 1; else hi = mid;
         }
-        return pos >= 0 && blk * 8 < int64_t(kept_s[pos]) + chunk;
+        return lo;
     };
-    auto mask_of = [&](int64_t blk) -> uint32_t {
-        const bool kb = kept_block(blk);
+    auto kept_block = [&](int64_t blk) -> bool {
+        const int q = lower(blk);
+        return q < nq && blk_at(q) == blk;
+    };
+    auto valid_mask = [&](int64_t blk) -> uint32_t {
+        const int64_t over = blk * 8 + 8 - L;
+        return over <= 0 ? 0xffu : (over >= 8 ? 0u : (0xffu >> over));
+    };
+    auto range_mask = [&](int64_t blk) -> uint32_t {
         uint32_t m = 0;
         for (int u = 0; u < 8; ++u) {
             const int64_t t = blk * 8 + u;
-            if (t < L && (t < s_end || t >= w0 || kb)) m |= 1u << u;
+            if (t < s_end || t >= w0) m |= 1u << u;
         }
+        m &= valid_mask(blk);
+        if (m != valid_mask(blk) && kept_block(blk)) m = valid_mask(blk);
         return m;
     };
-    auto is_mid = [&](int64_t blk) { return !merged && blk >= sb1 && blk < wb0 && blk * 8 < L; };
-
-    const int per = (nmc + NT - 1) / NT;
-    const int i0 = min(nmc, tid * per), i1 = min(nmc, i0 + per);
-    unsigned cnt = 0;
-    for (int i = i0; i < i1; ++i) cnt += is_mid((int64_t(kept_s[i / bpc]) >> 3) + (i % bpc));
-    unsigned nmid;
-    unsigned pos = block_excl_scan<NT>(cnt, tmp, &nmid);
-    for (int i = i0; i < i1; ++i) {
-        const int64_t blk = (int64_t(kept_s[i / bpc]) >> 3) + (i % bpc);
-        if (is_mid(blk)) blocks[nr1 + pos++] = uint32_t(blk << 8) | mask_of(blk);
+    int q0 = 0, q1 = 0;
+    if (!merged) {
+        q0 = lower(sb1);
+        q1 = lower(wb0);
     }
-    for (int64_t r = tid; r < nr1; r += NT) blocks[r] = uint32_t(r << 8) | mask_of(r);
-    for (int64_t r = tid; r < nr2; r += NT) blocks[nr1 + nmid + r] = uint32_t((wb0 + r) << 8) | mask_of(wb0 + r);
+    const int64_t nmid = q1 - q0;
+    for (int q = q0 + tid; q < q1; q += NT) {
+        const int64_t blk = blk_at(q);
+        blocks[nr1 + (q - q0)] = uint32_t(blk << 8) | valid_mask(blk);
+    }
+    for (int64_t r = tid; r < nr1; r += NT) blocks[r] = uint32_t(r << 8) | range_mask(r);
+    for (int64_t r = tid; r < nr2; r += NT) blocks[nr1 + nmid + r] = uint32_t((wb0 + r) << 8) | range_mask(wb0 + r);
     __syncthreads();
     return int(nr1 + nmid + nr2);
 }

@@ -105,9 +105,25 @@ def test_small_shapes(name):
 
 def test_full_budgets_equal_dense():
     w = tiny_workload(name="dense", max_context=2048,
-                      stages=(Stage(256, 8, 100), Stage(32, 2, 1000), Stage(8, 1, 5000)), sink=0, window=0)
+                      stages=(Stage(256, 8, 8), Stage(32, 2, 64), Stage(8, 1, 256)), sink=0, window=0)
     g, inp, ref = run_case(w)
     assert all(len(T) == 2048 for T in ref.attended[0])
+
+
+def test_many_candidate_groups_with_ties():
+    """4,688 stage-1 candidates (five groups of 1,024 in the select) with
+    many equal scores, and a later stage that keeps every candidate."""
+    w = tiny_workload(name="groups", batch=1, num_q_heads=8, num_kv_heads=2, max_context=300000,
+                      stages=(Stage(64, 8, 40), Stage(16, 2, 160)), sink=16, window=64, planted=0)
+
+    def dup(inp):
+        rng = np.random.default_rng(11)
+        for j in range(2):
+            rows = inp.k[0, j, rng.integers(0, 300000, size=6)]
+            for t in range(0, 300000, 8 * 3):          # every third sampled row is one of six rows
+                inp.k[0, j, t] = rows[(t // 24) % 6]
+
+    run_case(w, modify=dup, check_scores=True)
 
 
 def test_forced_ties():
