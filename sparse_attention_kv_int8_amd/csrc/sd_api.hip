@@ -62,10 +62,11 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
         const int64_t nc = s == 0 ? (cfg.max_context + in.chunk - 1) / in.chunk
                                   : int64_t(cfg.stage[s - 1].keep) * (cfg.stage[s - 1].chunk / in.chunk);
         if (nc + in.keep > kMaxCandidates) return SD_ERR_UNSUPPORTED;
-        // the select reduces groups of 1024 candidates to their top `keep`
-        // and then picks from at most 1024 survivors
-        const int64_t groups = (nc + 1023) / 1024;
-        if (in.keep < nc && groups > 1 && groups * in.keep > 1024) return SD_ERR_UNSUPPORTED;
+        // the select reduces groups of 1023 candidates to their top `keep`
+        // and then picks from at most 1023 survivors
+        const int64_t groups = (nc + 1022) / 1023;
+        if (in.keep < nc && groups > 1 && groups * in.keep > 1023) return SD_ERR_UNSUPPORTED;
+        if (in.keep > kMaxCandidates) return SD_ERR_UNSUPPORTED;
         g.ncand = int(nc);
         g.koff = koff;
         koff += in.keep;
@@ -73,7 +74,7 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
         const int ns8 = (g.nsamp + 7) / 8;
         const int ns8p = ns8 == 1 ? 1 : ns8 == 2 ? 2 : ns8 <= 4 ? 4 : 8;
         const int cb = ns8p >= 8 ? 1 : 8 / ns8p;
-        const int cpw = s == 0 ? 2 * cb : cb;
+        const int cpw = cb;
         g.per_wg = 4 * cpw;
         g.nwg = (g.ncand + g.per_wg - 1) / g.per_wg;
     }
@@ -89,6 +90,18 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
     ns = ns < 1 ? 1 : ns > 64 ? 64 : ns;      // at most 64 splits (one per lane in the merge)
     const int cap = (c->max_blocks + 3) / 4;
     c->nsplit = ns > cap ? cap : ns;
+    // device values: split the splits between sink/window blocks and kept blocks
+    // in proportion to their largest sizes
+    const int64_t ra = (cfg.sink > 0 || cfg.window > 0) ? (cfg.sink + 7) / 8 + (cfg.window + 7) / 8 + 1 : 0;
+    const int64_t rk = int64_t(last.keep) * (last.chunk / 8);
+    if (cfg.values_on_host || ra == 0) {
+        c->nsplit_a = 0;
+    } else {
+        if (c->nsplit < 2) c->nsplit = 2;
+        int na = int((int64_t(c->nsplit) * ra + (ra + rk) / 2) / (ra + rk));
+        na = na < 1 ? 1 : na > c->nsplit - 1 ? c->nsplit - 1 : na;
+        c->nsplit_a = na;
+    }
     const float scale = cfg.softmax_scale > 0.0f ? cfg.softmax_scale : 1.0f / std::sqrt(float(cfg.head_dim));
     c->scale_log2 = scale * 1.4426950408889634f;
 
@@ -174,8 +187,8 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
         // dynamic LDS of the largest kernel (the decode kernel: last-stage select
         // and block list) plus its static LDS (partials of 4 waves)
         const sd::StageGeom& g = c->st[c->S - 1];
-        const int64_t groups = (g.ncand + 1023) / 1024;
-        const int64_t words = g.ncand + g.keep + (groups > 1 ? groups * g.keep + groups : 0) + c->max_blocks;
+        const int64_t groups = (g.ncand + 1022) / 1023;
+        const int64_t words = g.ncand + g.keep + 1 + (groups > 1 ? groups * (g.keep + 1) + groups : 0);
         const int64_t static_bytes = 4 * (4 * (2 + sd::kHeadDim) * c->G + 64);
         if (words * 4 + static_bytes > lds_max) { delete c; return SD_ERR_UNSUPPORTED; }
     }

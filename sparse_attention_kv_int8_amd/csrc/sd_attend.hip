@@ -26,7 +26,6 @@ namespace sd {
 
 constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = kAttnThreads / kWave;
-constexpr int kPartStride = 2 + kHeadDim;     // m, l, acc[128] per (split, head)
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -49,8 +48,10 @@ struct AttendParams {
     int32_t* kept;            // [B][Hkv][keep_total]
     int keep_total;
     int sink, window;
-    float* part;              // [B][Hkv][nsplit][G][2 + d]
-    int nsplit;
+    float* part;              // acc [B*Hkv][G][d][nsplit], then (m, l) [B*Hkv][G][nsplit][2]
+    int nsplit;               // splits per (request, KV head)
+    int nsplit_a;             // of which sink/window splits (device values)
+    int Bh;                   // B * Hkv
     int64_t Lmax;
     int Hq, Hkv;
     float scale_log2;
@@ -69,10 +70,139 @@ __device__ __forceinline__ float rescale(float a, float m) {
     return a == -INFINITY ? 0.0f : fast_exp2(a - m);
 }
 
+// Tokens of block blk that are in the sink [0, s_end) or the window [w0, L).
+__device__ __forceinline__ uint32_t valid_mask8(int64_t blk, int64_t L) {
+    const int64_t over = blk * 8 + 8 - L;
+    return over <= 0 ? 0xffu : over >= 8 ? 0u : (0xffu >> over);
+}
+__device__ __forceinline__ uint32_t sinkwin_mask8(int64_t blk, int64_t L, int64_t s_end, int64_t w0) {
+    const int64_t lo = min<int64_t>(max<int64_t>(s_end - blk * 8, 0), 8);   // tokens below s_end
+    const int64_t hi = min<int64_t>(max<int64_t>(w0 - blk * 8, 0), 8);      // first token at or after w0
+    const uint32_t m = ((1u << lo) - 1u) | (0xffu & (0xffu << hi));
+    return m & valid_mask8(blk, L);
+}
+
+// Where a workgroup's blocks come from.
+//  kList:   the block list built by the value-cache kernel (host values)
+//  kRanges: the sink and window ranges, masked to sink/window tokens
+//  kKept:   the kept last-stage chunks' blocks, masked to the tokens the
+//           ranges do not cover (the two masks are disjoint; their union is T)
+enum { kList = 0, kRanges = 1, kKept = 2 };
+
+struct BlockSrc {
+    int type;
+    const uint32_t* list;
+    const int* kept;            // LDS, ascending kept starts
+    int bpc;
+    int64_t L, s_end, w0, nr1, wb0;
+};
+
+__device__ __forceinline__ void block_at(const BlockSrc& s, int r, int64_t& blk, uint32_t& mask) {
+    if (s.type == kList) {
+        const uint32_t e = s.list[r];
+        blk = e >> 8;
+        mask = e & 0xffu;
+    } else if (s.type == kRanges) {
+        blk = r < s.nr1 ? int64_t(r) : s.wb0 + (r - s.nr1);
+        mask = sinkwin_mask8(blk, s.L, s.s_end, s.w0);
+    } else {
+        blk = (int64_t(s.kept[r / s.bpc]) >> 3) + (r % s.bpc);
+        mask = valid_mask8(blk, s.L) & ~sinkwin_mask8(blk, s.L, s.s_end, s.w0);
+    }
+}
+
+struct BlockData {
+    u32x4 k0, k1;
+    uint32_t vv[8];
+    uint32_t mask;
+};
+
+template <bool HOSTV>
+__device__ __forceinline__ void load_block(const AttendParams& p, const BlockSrc& src, int r, int bj, int64_t L,
+                                           const uint16_t* kbase, const uint16_t* vbase, BlockData& d) {
+    const int lane = threadIdx.x & 63, tok = lane >> 3, sl = lane & 7;
+    int64_t blk;
+    block_at(src, r, blk, d.mask);
+    const int64_t t0 = blk * 8;
+    d.k0 = u32x4{0, 0, 0, 0};
+    d.k1 = u32x4{0, 0, 0, 0};
+    if ((d.mask >> tok) & 1u) {
+        const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + (t0 + tok) * kHeadDim + sl * 16);
+        d.k0 = __builtin_nontemporal_load(kp);
+        d.k1 = __builtin_nontemporal_load(kp + 1);
+    }
+    if (HOSTV) {
+        const int32_t se = p.blk_slot[int64_t(bj) * p.max_blocks + r];
+        uint32_t* prow = reinterpret_cast<uint32_t*>(p.vpool + (int64_t(bj) * p.vslots + (se & ~kVcMissBit)) * 8 * kHeadDim);
+        if (se & kVcMissBit) {
+            // miss: the whole block (rows t < L) comes from host memory and fills its slot
+            const uint32_t* hrow = reinterpret_cast<const uint32_t*>(vbase + t0 * kHeadDim);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                d.vv[u] = (t0 + u < L) ? hrow[u * (kHeadDim / 2) + lane] : 0u;
+                if (t0 + u < L) prow[u * (kHeadDim / 2) + lane] = d.vv[u];
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) d.vv[u] = ((d.mask >> u) & 1u) ? prow[u * (kHeadDim / 2) + lane] : 0u;
+        }
+    } else {
+        const uint32_t* vrow = reinterpret_cast<const uint32_t*>(vbase + t0 * kHeadDim);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            d.vv[u] = ((d.mask >> u) & 1u) ? __builtin_nontemporal_load(vrow + u * (kHeadDim / 2) + lane) : 0u;
+    }
+}
+
+// Online-softmax update of one wave's state with one block.
+template <int G>
+__device__ __forceinline__ void attend_block(const BlockData& d, const uint32_t (&qv)[G][8], float scale_log2,
+                                             float (&m)[G], float (&lsum)[G], float (&acc0)[G], float (&acc1)[G]) {
+    const int lane = threadIdx.x & 63, tok = lane >> 3;
+    const bool in = (d.mask >> tok) & 1u;
+    float z[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float s = dot2bf(qv[h][0], d.k0.x, 0.f);
+        s = dot2bf(qv[h][1], d.k0.y, s);
+        s = dot2bf(qv[h][2], d.k0.z, s);
+        s = dot2bf(qv[h][3], d.k0.w, s);
+        s = dot2bf(qv[h][4], d.k1.x, s);
+        s = dot2bf(qv[h][5], d.k1.y, s);
+        s = dot2bf(qv[h][6], d.k1.z, s);
+        s = dot2bf(qv[h][7], d.k1.w, s);
+        s = sum8_f(s);
+        z[h] = in ? s * scale_log2 : -INFINITY;
+    }
+    float pw[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float bm = max_groups_f(z[h]);
+        const float mn = fmaxf(m[h], bm);
+        const float alpha = rescale(m[h], mn);
+        pw[h] = in ? fast_exp2(z[h] - mn) : 0.f;
+        lsum[h] = lsum[h] * alpha + pw[h];
+        acc0[h] *= alpha;
+        acc1[h] *= alpha;
+        m[h] = mn;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        if ((d.mask >> u) & 1u) {
+            const float v0 = bf16_lo(d.vv[u]), v1 = bf16_hi(d.vv[u]);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float pu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw[h]), u * 8));
+                acc0[h] = fmaf(pu, v0, acc0[h]);
+                acc1[h] = fmaf(pu, v1, acc1[h]);
+            }
+        }
+    }
+}
+
 template <int G, bool HOSTV>
 __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendParams p) {
-    extern __shared__ uint32_t dyn[];   // device values: keys [last.ncand], sel [last.keep], select scratch,
-                                        // blocks [max_blocks]
+    extern __shared__ uint32_t dyn[];   // device values: keys [last.ncand], sel [last.keep + 1], select scratch
     __shared__ float wm[kAttnWaves][G];
     __shared__ float wl[kAttnWaves][G];
     __shared__ float wacc[kAttnWaves][G][kHeadDim];
@@ -81,30 +211,9 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
     const int sp = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int bj = b * p.Hkv + j;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int tok = lane >> 3, sl = lane & 7;
+    const int sl = lane & 7;
     int64_t L = p.lengths[b];
     if (L < 1 || L > p.Lmax) L = 0;
-
-    const uint32_t* blist;
-    int nb;
-    if (HOSTV) {
-        blist = p.blocks + int64_t(bj) * p.max_blocks;
-        nb = p.nblocks[bj];
-    } else {
-        uint32_t* keys = dyn;
-        int* sel = reinterpret_cast<int*>(dyn + p.last.ncand);
-        int* cand = sel + p.last.keep;
-        uint32_t* bl = dyn + p.last.ncand + p.last.keep + select_cand_words(p.last.ncand, p.last.keep);
-        int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
-        const int nk = kept_of_stage<kAttnThreads>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
-                                                   p.first_stage ? nullptr : kept_bj + p.pp_koff, L, keys, sel, cand, tmp);
-        if (sp == 0)
-            for (int i = threadIdx.x; i < p.last.keep; i += kAttnThreads) kept_bj[p.last.koff + i] = i < nk ? sel[i] : -1;
-        nb = build_attended<kAttnThreads>(sel, nk, p.last.chunk, L, p.sink, p.window, bl, tmp);
-        blist = bl;
-    }
-    const int per = (nb + p.nsplit - 1) / p.nsplit;
-    const int r0 = sp * per, r1 = min(nb, r0 + per);
 
     // this lane's 16 query dims of every head of the group (bf16 pairs)
     uint32_t qv[G][8];
@@ -115,6 +224,51 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         qv[h][0] = a.x; qv[h][1] = a.y; qv[h][2] = a.z; qv[h][3] = a.w;
         qv[h][4] = c.x; qv[h][5] = c.y; qv[h][6] = c.z; qv[h][7] = c.w;
     }
+
+    BlockSrc src{};
+    src.L = L;
+    src.s_end = min<int64_t>(p.sink, L);
+    src.w0 = p.window > 0 ? max<int64_t>(0, L - p.window) : L;
+    int r0, r1;
+    if (HOSTV) {
+        src.type = kList;
+        src.list = p.blocks + int64_t(bj) * p.max_blocks;
+        const int nb = p.nblocks[bj];
+        const int per = (nb + p.nsplit - 1) / p.nsplit;
+        r0 = min(nb, sp * per);
+        r1 = min(nb, r0 + per);
+    } else if (sp < p.nsplit_a) {
+        // sink / window blocks: known without any selection
+        src.type = kRanges;
+        const int64_t sb1 = (src.s_end + 7) >> 3, wb1 = (L + 7) >> 3;
+        const int64_t wb0 = p.window > 0 ? (src.w0 >> 3) : wb1;
+        const bool merged = wb0 <= sb1;
+        src.nr1 = merged ? wb1 : sb1;
+        src.wb0 = wb0;
+        const int nb = int(src.nr1 + (merged ? 0 : wb1 - wb0));
+        const int per = (nb + p.nsplit_a - 1) / p.nsplit_a;
+        r0 = min(nb, sp * per);
+        r1 = min(nb, r0 + per);
+    } else {
+        // kept chunks of the last stage, recomputed from its scores
+        src.type = kKept;
+        uint32_t* keys = dyn;
+        int* sel = reinterpret_cast<int*>(dyn + p.last.ncand);
+        int* cand = sel + p.last.keep + 1;
+        int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
+        const int nk = kept_of_stage<kAttnThreads>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
+                                                   p.first_stage ? nullptr : kept_bj + p.pp_koff, L, keys, sel, cand, tmp);
+        const int spb = sp - p.nsplit_a, nsb = p.nsplit - p.nsplit_a;
+        if (spb == 0)
+            for (int i = threadIdx.x; i < p.last.keep; i += kAttnThreads) kept_bj[p.last.koff + i] = i < nk ? sel[i] : -1;
+        src.kept = sel;
+        src.bpc = p.last.chunk >> 3;
+        const int nb = nk * src.bpc;
+        const int per = (nb + nsb - 1) / nsb;
+        r0 = min(nb, spb * per);
+        r1 = min(nb, r0 + per);
+    }
+
     float m[G], lsum[G], acc0[G], acc1[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) { m[h] = -INFINITY; lsum[h] = 0.f; acc0[h] = 0.f; acc1[h] = 0.f; }
@@ -122,80 +276,14 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
     const uint16_t* kbase = p.k + int64_t(bj) * p.Lmax * kHeadDim;
     const uint16_t* vbase = p.v + int64_t(bj) * p.Lmax * kHeadDim;
 
-    for (int r = r0 + wave; r < r1; r += kAttnWaves) {
-        const uint32_t e = blist[r];
-        const int64_t t0 = int64_t(e >> 8) * 8;
-        const uint32_t mask = e & 0xffu;
-        const bool in = (mask >> tok) & 1u;
-        // keys: 32 bytes of token t0 + tok
-        u32x4 k0 = {0, 0, 0, 0}, k1 = {0, 0, 0, 0};
-        if (in) {
-            const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + (t0 + tok) * kHeadDim + sl * 16);
-            k0 = __builtin_nontemporal_load(kp);
-            k1 = __builtin_nontemporal_load(kp + 1);
-        }
-        // values: dims 2*lane, 2*lane+1 of the 8 rows
-        uint32_t vv[8];
-        if (HOSTV) {
-            const int32_t se = p.blk_slot[int64_t(bj) * p.max_blocks + r];
-            uint32_t* prow = reinterpret_cast<uint32_t*>(p.vpool + (int64_t(bj) * p.vslots + (se & ~kVcMissBit)) * 8 * kHeadDim);
-            if (se & kVcMissBit) {
-                // miss: the whole block (rows t < L) comes from host memory and fills its slot
-                const uint32_t* hrow = reinterpret_cast<const uint32_t*>(p.v + (int64_t(bj) * p.Lmax + t0) * kHeadDim);
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    vv[u] = (t0 + u < L) ? hrow[u * (kHeadDim / 2) + lane] : 0u;
-                    if (t0 + u < L) prow[u * (kHeadDim / 2) + lane] = vv[u];
-                }
-            } else {
-#pragma unroll
-                for (int u = 0; u < 8; ++u) vv[u] = ((mask >> u) & 1u) ? prow[u * (kHeadDim / 2) + lane] : 0u;
-            }
-        } else {
-            const uint32_t* vrow = reinterpret_cast<const uint32_t*>(vbase + t0 * kHeadDim);
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                vv[u] = ((mask >> u) & 1u) ? __builtin_nontemporal_load(vrow + u * (kHeadDim / 2) + lane) : 0u;
-        }
-
-        float z[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float s = dot2bf(qv[h][0], k0.x, 0.f);
-            s = dot2bf(qv[h][1], k0.y, s);
-            s = dot2bf(qv[h][2], k0.z, s);
-            s = dot2bf(qv[h][3], k0.w, s);
-            s = dot2bf(qv[h][4], k1.x, s);
-            s = dot2bf(qv[h][5], k1.y, s);
-            s = dot2bf(qv[h][6], k1.z, s);
-            s = dot2bf(qv[h][7], k1.w, s);
-            s = sum8_f(s);
-            z[h] = in ? s * p.scale_log2 : -INFINITY;
-        }
-        float pw[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float bm = max_groups_f(z[h]);
-            const float mn = fmaxf(m[h], bm);
-            const float alpha = rescale(m[h], mn);
-            pw[h] = in ? fast_exp2(z[h] - mn) : 0.f;
-            lsum[h] = lsum[h] * alpha + pw[h];
-            acc0[h] *= alpha;
-            acc1[h] *= alpha;
-            m[h] = mn;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if ((mask >> u) & 1u) {
-                const float v0 = bf16_lo(vv[u]), v1 = bf16_hi(vv[u]);
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float pu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw[h]), u * 8));
-                    acc0[h] = fmaf(pu, v0, acc0[h]);
-                    acc1[h] = fmaf(pu, v1, acc1[h]);
-                }
-            }
-        }
+    // two blocks in flight per wave
+    for (int r = r0 + wave; r < r1; r += 2 * kAttnWaves) {
+        BlockData d0, d1;
+        const bool two = r + kAttnWaves < r1;
+        load_block<HOSTV>(p, src, r, bj, L, kbase, vbase, d0);
+        if (two) load_block<HOSTV>(p, src, r + kAttnWaves, bj, L, kbase, vbase, d1);
+        attend_block<G>(d0, qv, p.scale_log2, m, lsum, acc0, acc1);
+        if (two) attend_block<G>(d1, qv, p.scale_log2, m, lsum, acc0, acc1);
     }
 
     // wave totals: lsum is per token group (identical in its 8 lanes)
@@ -207,7 +295,10 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         wacc[wave][h][2 * lane + 1] = acc1[h];
     }
     __syncthreads();
-    float* part = p.part + (int64_t(bj) * p.nsplit + sp) * G * kPartStride;
+    // partials: acc at [bj][h][dd][split] (a split's values of one output are
+    // adjacent for the merge), (m, l) at [bj][h][split][2] after all acc
+    float* pacc = p.part + int64_t(bj) * G * kHeadDim * p.nsplit;
+    float* pml = p.part + int64_t(p.Bh) * G * kHeadDim * p.nsplit + int64_t(bj) * G * p.nsplit * 2;
     for (int o = threadIdx.x; o < G * kHeadDim; o += kAttnThreads) {
         const int h = o / kHeadDim, dd = o % kHeadDim;
         float M = -INFINITY;
@@ -220,10 +311,12 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
             a = fmaf(wacc[w][h][dd], f, a);
             l = fmaf(wl[w][h], f, l);
         }
-        part[h * kPartStride + 2 + dd] = a;
-        if (dd == 0) { part[h * kPartStride] = M; part[h * kPartStride + 1] = l; }
+        pacc[(h * kHeadDim + dd) * p.nsplit + sp] = a;
+        if (dd == 0) {
+            pml[(h * p.nsplit + sp) * 2] = M;
+            pml[(h * p.nsplit + sp) * 2 + 1] = l;
+        }
     }
-
 }
 
 // Log-sum-exp merge of the splits of one (request, KV head), rounding to bf16.
@@ -232,34 +325,40 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
 constexpr int kMaxSplit = 64;
 
 template <int G>
-__global__ __launch_bounds__(kAttnThreads) void sd_combine_kernel(const float* __restrict__ part, int nsplit, int Hq,
-                                                                 int Hkv, uint16_t* __restrict__ out) {
-    __shared__ float wgt[kMaxSplit][G];
+__global__ __launch_bounds__(kAttnThreads) void sd_combine_kernel(const float* __restrict__ part, int nsplit, int Bh,
+                                                                 int Hq, int Hkv, uint16_t* __restrict__ out) {
+    __shared__ float wgt[G][kMaxSplit];
     const int j = blockIdx.x, b = blockIdx.y, bj = b * Hkv + j;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const float* pb = part + int64_t(bj) * nsplit * G * kPartStride;
+    const float* pacc = part + int64_t(bj) * G * kHeadDim * nsplit;
+    const float* pml = part + int64_t(Bh) * G * kHeadDim * nsplit + int64_t(bj) * G * nsplit * 2;
     if (wid < G) {
-        const float m = lane < nsplit ? pb[(lane * G + wid) * kPartStride] : -INFINITY;
-        const float l = lane < nsplit ? pb[(lane * G + wid) * kPartStride + 1] : 0.f;
+        const float m = lane < nsplit ? pml[(wid * nsplit + lane) * 2] : -INFINITY;
+        const float l = lane < nsplit ? pml[(wid * nsplit + lane) * 2 + 1] : 0.f;
         const float M = wave_max_f(m);
         const float f = rescale(m, M);
         const float Lt = wave_sum_f(l * f);
-        if (lane < nsplit) wgt[lane][wid] = Lt > 0.f ? f / Lt : 0.f;
+        if (lane < nsplit) wgt[wid][lane] = Lt > 0.f ? f / Lt : 0.f;
     }
     __syncthreads();
     for (int o = threadIdx.x; o < G * kHeadDim; o += kAttnThreads) {
-        const int h = o / kHeadDim, dd = o % kHeadDim;
-        const float* pa = pb + h * kPartStride + 2 + dd;
+        const int h = o / kHeadDim;
+        const float* pa = pacc + int64_t(o) * nsplit;
+        const float* w = wgt[h];
         float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
         int s = 0;
-        for (; s + 3 < nsplit; s += 4) {
-            a0 = fmaf(pa[(s + 0) * G * kPartStride], wgt[s + 0][h], a0);
-            a1 = fmaf(pa[(s + 1) * G * kPartStride], wgt[s + 1][h], a1);
-            a2 = fmaf(pa[(s + 2) * G * kPartStride], wgt[s + 2][h], a2);
-            a3 = fmaf(pa[(s + 3) * G * kPartStride], wgt[s + 3][h], a3);
+        if ((nsplit & 3) == 0) {
+#pragma unroll 16
+            for (; s < nsplit; s += 4) {
+                const float4 v = *reinterpret_cast<const float4*>(pa + s);
+                a0 = fmaf(v.x, w[s], a0);
+                a1 = fmaf(v.y, w[s + 1], a1);
+                a2 = fmaf(v.z, w[s + 2], a2);
+                a3 = fmaf(v.w, w[s + 3], a3);
+            }
         }
-        for (; s < nsplit; ++s) a0 = fmaf(pa[s * G * kPartStride], wgt[s][h], a0);
-        out[(int64_t(b) * Hq + j * G + h) * kHeadDim + dd] = f32_to_bf16_rne((a0 + a1) + (a2 + a3));
+        for (; s < nsplit; ++s) a0 = fmaf(pa[s], w[s], a0);
+        out[(int64_t(b) * Hq + j * G + (o / kHeadDim)) * kHeadDim + (o % kHeadDim)] = f32_to_bf16_rne((a0 + a1) + (a2 + a3));
     }
 }
 
@@ -284,6 +383,8 @@ hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const 
     p.max_blocks = c->max_blocks;
     p.part = c->part;
     p.nsplit = c->nsplit;
+    p.nsplit_a = c->nsplit_a;
+    p.Bh = c->cfg.batch * c->cfg.num_kv_heads;
     const int S = c->S;
     p.last = stage_dev(c, S - 1);
     p.first_stage = S == 1;
@@ -293,8 +394,8 @@ hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const 
     p.keep_total = c->keep_total;
     p.sink = c->cfg.sink;
     p.window = c->cfg.window;
-    const size_t lds = (size_t(p.last.ncand) + size_t(p.last.keep) +
-                        size_t(select_cand_words(p.last.ncand, p.last.keep)) + size_t(c->max_blocks)) * 4;
+    const size_t lds = (size_t(p.last.ncand) + size_t(p.last.keep) + 1 +
+                        size_t(select_cand_words(p.last.ncand, p.last.keep))) * 4;
     p.Lmax = c->Lmax;
     p.Hq = c->cfg.num_q_heads;
     p.Hkv = c->cfg.num_kv_heads;
@@ -318,10 +419,11 @@ hipError_t launch_combine(sd_ctx* c, uint16_t* out, hipStream_t s, Timing t) {
     dim3 grid(c->cfg.num_kv_heads, c->cfg.batch), block(kAttnThreads);
     const int Hq = c->cfg.num_q_heads, Hkv = c->cfg.num_kv_heads;
     const float* part = c->part;
+    const int Bh = c->cfg.batch * c->cfg.num_kv_heads;
     switch (c->G) {
-        case 1: launch(sd_combine_kernel<1>, grid, block, 0, s, t, part, c->nsplit, Hq, Hkv, out); break;
-        case 2: launch(sd_combine_kernel<2>, grid, block, 0, s, t, part, c->nsplit, Hq, Hkv, out); break;
-        default: launch(sd_combine_kernel<4>, grid, block, 0, s, t, part, c->nsplit, Hq, Hkv, out); break;
+        case 1: launch(sd_combine_kernel<1>, grid, block, 0, s, t, part, c->nsplit, Bh, Hq, Hkv, out); break;
+        case 2: launch(sd_combine_kernel<2>, grid, block, 0, s, t, part, c->nsplit, Bh, Hq, Hkv, out); break;
+        default: launch(sd_combine_kernel<4>, grid, block, 0, s, t, part, c->nsplit, Bh, Hq, Hkv, out); break;
     }
     return hipGetLastError();
 }

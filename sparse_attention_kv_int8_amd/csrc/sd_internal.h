@@ -57,6 +57,7 @@ struct sd_ctx {
     int keep_total;
     int max_blocks;         // attended 8-token blocks per (request, KV head)
     int nsplit;             // flash-decode splits per (request, KV head)
+    int nsplit_a;           // of which cover the sink/window blocks (device values only)
     float scale_log2;       // softmax_scale * log2(e)
     sd::StageGeom st[SD_MAX_STAGES];
     size_t select_lds;      // dynamic LDS bytes of the stage kernels
@@ -68,7 +69,7 @@ struct sd_ctx {
     int32_t* qgroup;                  // [B][Hkv][d] group query sums
     uint32_t* blocks;                 // [B][Hkv][max_blocks] (block << 8) | token mask
     int32_t* nblocks;                 // [B][Hkv]
-    float* part;                      // [B][Hkv][nsplit][G][2 + d]
+    float* part;                      // acc [B*Hkv][G][d][nsplit], then (m, l) [B*Hkv][G][nsplit][2]
     unsigned* absmax_bits;            // [B][Hkv]
     int32_t* flag;                    // device error flag
     sd::ValueCache vc;

@@ -19,10 +19,10 @@
 
 namespace sd {
 
-// LDS words the select needs besides keys and sel.
+// LDS words the select needs besides keys [n] and sel [K + 1].
 __host__ __device__ inline int select_cand_words(int n, int K) {
-    const int groups = (n + 1023) / 1024;
-    return groups > 1 ? groups * K + groups : 0;
+    const int groups = (n + 1022) / 1023;
+    return groups > 1 ? groups * (K + 1) + groups : 0;
 }
 
 // Start of candidate i of a stage (token position), or -1 if it does not
@@ -45,83 +45,104 @@ __device__ __forceinline__ int64_t cand_start(const StageDev& st, bool first_sta
 // ------------------------------------------------------------------------
 // Exact top-K select.
 //
-// Keys are uint32 with 0 meaning "no candidate"; a larger key is better and
-// equal keys go to the lower index.  The threshold T (the K-th largest key)
-// is built bit by bit from the top: T keeps a bit when at least K keys are
-// >= (prefix | bit).  Counting uses one ballot + popcount per register-held
-// key, inside a single wave, so the search needs no barrier and no LDS
-// atomics.  Keys > T are kept, and of the keys equal to T the lowest
-// indices, K - #(keys > T) of them.
+// Keys are score + 2^23 (a chunk score satisfies |S| <= 4 * 127 * 127 * 128
+// < 2^23, so a key lies in [1, 2^24)), with 0 meaning "no candidate"; a
+// larger key is better and equal keys go to the lower index.  The
+// threshold T (the K-th largest key) is built two bits per round from the
+// top: three candidate thresholds are counted per lane in VALU, the counts
+// packed into 16-bit fields and summed across the wave with DPP, and the
+// largest threshold whose count reaches K is kept.  Keys > T are kept, and
+// of the keys equal to T the lowest indices, K - #(keys > T) of them.  One
+// wave does the whole search: no barrier and no LDS atomics (both are slow
+// on this chip compared with DPP).
 // ------------------------------------------------------------------------
-constexpr int kSelGroup = 1024;              // keys one wave selects from (16 per lane)
+constexpr int kSelGroup = 1023;              // keys one wave selects from (<= 16 per lane)
+constexpr int kKeyBits = 24;
 
-__device__ __forceinline__ int wave_count_ge(const uint32_t (&kk)[16], int E, uint32_t c) {
-    int n = 0;
-#pragma unroll
-    for (int u = 0; u < 16; ++u)
-        if (u < E) n += __popcll(__ballot(kk[u] >= c));
-    return n;
+__device__ __forceinline__ uint32_t score_key(int s) {
+    return s == INT32_MIN ? 0u : uint32_t(s + (1 << 23));
 }
 
-// One wave: top-K of m keys key(i) = keys[idx ? idx[i] : i] (m <= 1024).
+// Wave-wide sum of a value whose 16-bit fields stay below 2^16.
+__device__ __forceinline__ unsigned wave_sum_packed(unsigned v) { return wave_sum_u(v); }
+
+// One wave: top-K of m keys key(i) = keys[idx ? idx[i] : i], m <= min(64 E, 1023).
 // Lane l owns the contiguous positions [l*E, l*E + E).  Writes the kept
-// positions i (ascending) to out[0..kept); returns kept = min(K, #valid).
-__device__ __forceinline__ int wave_select(const uint32_t* keys, const int* idx, int m, int K, int* out) {
+// positions i (ascending) to out[0..kept) (out has K + 1 slots; slot K is
+// scratch); returns kept = min(K, #valid).
+template <int E>
+__device__ __forceinline__ int wave_select_e(const uint32_t* keys, const int* idx, int m, int K, int* out) {
     const int lane = threadIdx.x & 63;
-    const int E = (m + 63) >> 6;
-    uint32_t kk[16];
-    unsigned kmn = 0xffffffffu, kmx = 0, nv = 0;
+    uint32_t kk[E];
+    unsigned nv = 0;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < E; ++u) {
         const int i = lane * E + u;
-        kk[u] = (u < E && i < m) ? keys[idx ? idx[i] : i] : 0u;
-        if (kk[u]) { ++nv; kmn = min(kmn, kk[u]); kmx = max(kmx, kk[u]); }
+        kk[u] = i < m ? keys[idx ? idx[i] : i] : 0u;
+        nv += kk[u] != 0u;
     }
     const int nvalid = int(wave_sum_u(nv));
     uint32_t T = 0;
     int need_eq = 0;
     if (nvalid > K) {
-        kmn = wave_min_u(kmn);
-        kmx = wave_max_u(kmx);
-        const unsigned diff = kmx ^ kmn;
-        const int hb = diff ? 32 - __clz(diff) : 0;
-        uint32_t prefix = hb >= 32 ? 0u : (kmx >> hb) << hb;
-        for (int b = hb - 1; b >= 0; --b) {
-            const uint32_t c = prefix | (1u << b);
-            if (wave_count_ge(kk, E, c) >= K) prefix = c;
+        // Round: thresholds prefix + {1,2,3} << b.  For a key, d = number of
+        // them it reaches = clamp((key - prefix) >> b, 0, 3); its packed
+        // contribution 0x100401 >> (30 - 10 d) adds 1 to each of the d lowest
+        // 10-bit fields (fields: reaches c1, c2, c3).  Wave sums of a field
+        // stay below 2^10 because m <= 1023.
+        uint32_t prefix = 0;
+        for (int b = kKeyBits - 2; b >= 0; b -= 2) {
+            unsigned acc = 0;
+#pragma unroll
+            for (int u = 0; u < E; ++u) {
+                const int d = min(max((int(kk[u]) - int(prefix)) >> b, 0), 3);
+                acc += 0x100401u >> (30 - 10 * d);
+            }
+            acc = wave_sum_u(acc);
+            const int n1 = int(acc & 0x3ffu), n2 = int((acc >> 10) & 0x3ffu), n3 = int(acc >> 20);
+            prefix += n3 >= K ? (3u << b) : n2 >= K ? (2u << b) : n1 >= K ? (1u << b) : 0u;
         }
         T = prefix;
-        need_eq = K - wave_count_ge(kk, E, T + 1u);
+        unsigned gl = 0;
+#pragma unroll
+        for (int u = 0; u < E; ++u) gl += kk[u] > T ? 1u : 0u;
+        need_eq = K - int(wave_sum_u(gl));
     }
     // ordered compaction: (count of keys > T, count of keys == T) per lane, scanned
     unsigned g = 0, e = 0;
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-        if (u < E) { g += kk[u] > T; e += (kk[u] == T) && kk[u]; }
+    for (int u = 0; u < E; ++u) { g += kk[u] > T; e += (kk[u] == T) && kk[u]; }
     const unsigned packed = (g << 16) | e;
     const unsigned ex = wave_incl_scan(packed) - packed;
     g = ex >> 16;
     e = ex & 0xffffu;
+    const unsigned neq = unsigned(need_eq);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-        if (u >= E) break;
-        const int i = lane * E + u;
-        if (kk[u] > T) {
-            out[g + min(e, unsigned(need_eq))] = i;
-            ++g;
-        } else if (kk[u] == T && kk[u]) {
-            if (e < unsigned(need_eq)) out[g + e] = i;
-            ++e;
-        }
+    for (int u = 0; u < E; ++u) {
+        const bool gt = kk[u] > T;
+        const bool eq = (kk[u] == T) && kk[u];
+        const unsigned pos = gt ? g + min(e, neq) : (eq && e < neq) ? g + e : unsigned(K);
+        out[pos] = lane * E + u;          // non-kept keys land in the scratch slot K
+        g += gt;
+        e += eq;
     }
     return min(K, nvalid);
+}
+
+__device__ __forceinline__ int wave_select(const uint32_t* keys, const int* idx, int m, int K, int* out) {
+    if (m <= 64) return wave_select_e<1>(keys, idx, m, K, out);
+    if (m <= 128) return wave_select_e<2>(keys, idx, m, K, out);
+    if (m <= 256) return wave_select_e<4>(keys, idx, m, K, out);
+    if (m <= 512) return wave_select_e<8>(keys, idx, m, K, out);
+    return wave_select_e<16>(keys, idx, m, K, out);      // m <= 1023
 }
 
 // Block-level: top-K of n keys in LDS (n <= 16 * kSelGroup).  Groups of
 // kSelGroup keys are reduced to their own top-K by the waves in parallel
 // (exact: a key among the global top K is among its group's top K under the
 // same order); one wave then selects from the groups' survivors.  sel
-// receives the kept indices ascending.  cand: LDS, ngroups * K + 16 ints.
+// (K + 1 ints) receives the kept indices ascending.  cand: LDS,
+// select_cand_words(n, K) ints.
 template <int NT>
 __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, int* cand, unsigned* tmp) {
     constexpr int NW = NT / kWave;
@@ -148,11 +169,11 @@ __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, int* can
         __syncthreads();
         kept = int(tmp[0]);
     } else {
-        int* counts = cand + ngroups * K;           // [ngroups]
+        int* counts = cand + ngroups * (K + 1);     // [ngroups]
         for (int g = wid; g < ngroups; g += NW) {
             const int base = g * kSelGroup;
             const int m = min(kSelGroup, n - base);
-            int* out = cand + g * K;
+            int* out = cand + g * (K + 1);
             const int r = wave_select(keys + base, nullptr, m, K, out);
             for (int i = lane; i < r; i += kWave) out[i] += base;
             if (lane == 0) counts[g] = r;
@@ -163,7 +184,7 @@ __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, int* can
             int off = 0;
             for (int g = 0; g < ngroups; ++g) {
                 const int r = counts[g];
-                for (int i = lane; i < r; i += kWave) cand[off + i] = cand[g * K + i];
+                for (int i = lane; i < r; i += kWave) cand[off + i] = cand[g * (K + 1) + i];
                 off += r;
                 __builtin_amdgcn_wave_barrier();
             }
@@ -182,14 +203,13 @@ __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, int* can
 // scores (global, INT32_MIN = no candidate): sel[0..nk) receives the kept
 // chunk starts, ascending.  `parents` are the kept starts of the stage
 // before (global or LDS; unused for the first stage).  keys: LDS [ncand];
-// cand: LDS [select_cand_words(ncand, keep)].
+// sel: LDS [keep + 1]; cand: LDS [select_cand_words(ncand, keep)].
 template <int NT>
 __device__ int kept_of_stage(const StageDev& st, bool first_stage, const int32_t* scores_bj,
                              const int32_t* parents, int64_t L, uint32_t* keys, int* sel, int* cand,
                              unsigned* tmp) {
     for (int i = threadIdx.x; i < st.ncand; i += NT) {
-        const int s = scores_bj[i];
-        keys[i] = s == INT32_MIN ? 0u : (uint32_t(s) ^ 0x80000000u);
+        keys[i] = score_key(scores_bj[i]);
     }
     __syncthreads();
     const int nk = select_top<NT>(keys, st.ncand, st.keep, sel, cand, tmp);

@@ -200,3 +200,32 @@ def test_non_default_stream():
 @pytest.mark.parametrize("name", ["llama8b_128k", "ragged_b16", "ctx_1m"])
 def test_full_workload(name):
     run_case(WORKLOADS[name])
+
+
+def test_graph_capture_replays_match_eager():
+    """A decode step captured into a HIP graph (no allocation, memset or host
+    sync inside) replays to the eager result, with eager steps and
+    synchronisations between the replays."""
+    import torch
+    w = WORKLOADS["llama8b_128k"].replace(max_context=32768, planted=16)
+    inp = make_inputs(w)
+    g = GpuRun(inp)
+    g.quantize()
+    out_e, kept_e = g.step(inp.q)
+    q_dev = g.torch.from_numpy(np.ascontiguousarray(inp.q).view(np.int16)).view(torch.bfloat16).cuda()
+    out_g = torch.empty_like(g.out)
+    kept_g = torch.empty_like(g.kept)
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        g.dec.sd_decode_step(q_dev, g.k, g.k8, g.v, g.lengths, out_g, kept_g)
+    for rep in range(3):
+        out_g.zero_()
+        kept_g.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out_g.view(torch.int16).cpu().numpy().view(np.uint16), out_e), rep
+        assert np.array_equal(kept_g.cpu().numpy(), kept_e), rep
+        g.step(inp.q)                         # eager work between replays
+        torch.cuda.synchronize()
