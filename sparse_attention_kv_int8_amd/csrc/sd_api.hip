@@ -2,6 +2,7 @@
 // geometry, the one workspace allocation, and the entry points.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -10,6 +11,7 @@
 
 #include "sd_device.h"
 #include "sd_internal.h"
+#include "sd_select.h"
 
 namespace {
 
@@ -62,10 +64,10 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
         const int64_t nc = s == 0 ? (cfg.max_context + in.chunk - 1) / in.chunk
                                   : int64_t(cfg.stage[s - 1].keep) * (cfg.stage[s - 1].chunk / in.chunk);
         if (nc + in.keep > kMaxCandidates) return SD_ERR_UNSUPPORTED;
-        // the select reduces groups of 1023 candidates to their top `keep`
-        // and then picks from at most 1023 survivors
-        const int64_t groups = (nc + 1022) / 1023;
-        if (in.keep < nc && groups > 1 && groups * in.keep > 1023) return SD_ERR_UNSUPPORTED;
+        // the select reduces groups of 1024 candidates to their top `keep`
+        // and then picks from at most 1024 survivors
+        const int64_t groups = (nc + 1023) / 1024;
+        if (in.keep < nc && groups > 1 && groups * in.keep > 1024) return SD_ERR_UNSUPPORTED;
         if (in.keep > kMaxCandidates) return SD_ERR_UNSUPPORTED;
         g.ncand = int(nc);
         g.koff = koff;
@@ -184,11 +186,12 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
         int lds_max = 0;
         e0 = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device);
         if (e0 != hipSuccess) { delete c; return from_hip(e0, "hipDeviceGetAttribute"); }
-        // dynamic LDS of the largest kernel (the decode kernel: last-stage select
-        // and block list) plus its static LDS (partials of 4 waves)
-        const sd::StageGeom& g = c->st[c->S - 1];
-        const int64_t groups = (g.ncand + 1022) / 1023;
-        const int64_t words = g.ncand + g.keep + 1 + (groups > 1 ? groups * (g.keep + 1) + groups : 0);
+        // every stage's select runs in some kernel (stage s - 1's in the
+        // pruning kernel of stage s, the last one's in the decode kernel);
+        // the decode kernel's static LDS (partials of 4 waves) is the largest
+        int64_t words = 0;
+        for (int s = 0; s < c->S; ++s)
+            words = std::max<int64_t>(words, sd::kept_lds_words(sd::stage_dev(c, s), s == 0));
         const int64_t static_bytes = 4 * (4 * (2 + sd::kHeadDim) * c->G + 64);
         if (words * 4 + static_bytes > lds_max) { delete c; return SD_ERR_UNSUPPORTED; }
     }

@@ -252,12 +252,10 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
     } else {
         // kept chunks of the last stage, recomputed from its scores
         src.type = kKept;
-        uint32_t* keys = dyn;
         int* sel = reinterpret_cast<int*>(dyn + p.last.ncand);
-        int* cand = sel + p.last.keep + 1;
         int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
         const int nk = kept_of_stage<kAttnThreads>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
-                                                   p.first_stage ? nullptr : kept_bj + p.pp_koff, L, keys, sel, cand, tmp);
+                                                   p.first_stage ? nullptr : kept_bj + p.pp_koff, L, dyn, tmp);
         const int spb = sp - p.nsplit_a, nsb = p.nsplit - p.nsplit_a;
         if (spb == 0)
             for (int i = threadIdx.x; i < p.last.keep; i += kAttnThreads) kept_bj[p.last.koff + i] = i < nk ? sel[i] : -1;
@@ -319,47 +317,66 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
     }
 }
 
-// Log-sum-exp merge of the splits of one (request, KV head), rounding to bf16.
-// Wave h computes head h's split weights exp2(m_s - M) / sum_s l_s exp2(m_s - M)
-// (one split per lane); then every output is one weighted sum over splits.
+// Log-sum-exp merge of the splits, rounding to bf16.  A workgroup merges 64
+// outputs of one head (4 lanes per output, a quarter of the splits each, so
+// the partials are read by many workgroups at once and with few dependent
+// loads per lane): the partial loads are issued first, wave 0 meanwhile
+// computes the head's split weights exp2(m_s - M) / sum_s l_s exp2(m_s - M),
+// and each output is a weighted sum over splits finished across its 4 lanes.
 constexpr int kMaxSplit = 64;
+constexpr int kCombOut = 64;                 // outputs per combine workgroup
 
-template <int G>
 __global__ __launch_bounds__(kAttnThreads) void sd_combine_kernel(const float* __restrict__ part, int nsplit, int Bh,
-                                                                 int Hq, int Hkv, uint16_t* __restrict__ out) {
-    __shared__ float wgt[G][kMaxSplit];
-    const int j = blockIdx.x, b = blockIdx.y, bj = b * Hkv + j;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const float* pacc = part + int64_t(bj) * G * kHeadDim * nsplit;
-    const float* pml = part + int64_t(Bh) * G * kHeadDim * nsplit + int64_t(bj) * G * nsplit * 2;
-    if (wid < G) {
-        const float m = lane < nsplit ? pml[(wid * nsplit + lane) * 2] : -INFINITY;
-        const float l = lane < nsplit ? pml[(wid * nsplit + lane) * 2 + 1] : 0.f;
+                                                                 int G, int Hq, int Hkv, uint16_t* __restrict__ out) {
+    __shared__ float wgt[kMaxSplit];
+    const int j = blockIdx.y, b = blockIdx.z, bj = b * Hkv + j;
+    const int o = blockIdx.x * kCombOut + (threadIdx.x >> 2);        // output of this lane, in [0, G*128)
+    const int h = (blockIdx.x * kCombOut) / kHeadDim;
+    const int qq = threadIdx.x & 3;
+    const float* pa = part + (int64_t(bj) * G * kHeadDim + o) * nsplit;
+    const float* pml = part + int64_t(Bh) * G * kHeadDim * nsplit + (int64_t(bj) * G + h) * nsplit * 2;
+    // lane qq owns splits {4 qq + 16 i + u}
+    float4 v[kMaxSplit / 16];
+    const bool vec = (nsplit & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < kMaxSplit / 16; ++i) {
+        const int s0 = 4 * qq + 16 * i;
+        v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (vec) {
+            if (s0 < nsplit) v[i] = *reinterpret_cast<const float4*>(pa + s0);
+        } else {
+            if (s0 < nsplit) v[i].x = pa[s0];
+            if (s0 + 1 < nsplit) v[i].y = pa[s0 + 1];
+            if (s0 + 2 < nsplit) v[i].z = pa[s0 + 2];
+            if (s0 + 3 < nsplit) v[i].w = pa[s0 + 3];
+        }
+    }
+    if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        const float m = lane < nsplit ? pml[lane * 2] : -INFINITY;
+        const float l = lane < nsplit ? pml[lane * 2 + 1] : 0.f;
         const float M = wave_max_f(m);
         const float f = rescale(m, M);
         const float Lt = wave_sum_f(l * f);
-        if (lane < nsplit) wgt[wid][lane] = Lt > 0.f ? f / Lt : 0.f;
+        wgt[lane] = (lane < nsplit && Lt > 0.f) ? f / Lt : 0.f;
     }
     __syncthreads();
-    for (int o = threadIdx.x; o < G * kHeadDim; o += kAttnThreads) {
-        const int h = o / kHeadDim;
-        const float* pa = pacc + int64_t(o) * nsplit;
-        const float* w = wgt[h];
-        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-        int s = 0;
-        if ((nsplit & 3) == 0) {
-#pragma unroll 16
-            for (; s < nsplit; s += 4) {
-                const float4 v = *reinterpret_cast<const float4*>(pa + s);
-                a0 = fmaf(v.x, w[s], a0);
-                a1 = fmaf(v.y, w[s + 1], a1);
-                a2 = fmaf(v.z, w[s + 2], a2);
-                a3 = fmaf(v.w, w[s + 3], a3);
-            }
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxSplit / 16; ++i) {
+        const int s0 = 4 * qq + 16 * i;
+        if (s0 < nsplit) {
+            a0 = fmaf(v[i].x, wgt[s0], a0);
+            a1 = fmaf(v[i].y, wgt[s0 + 1], a1);
+            a0 = fmaf(v[i].z, wgt[s0 + 2], a0);
+            a1 = fmaf(v[i].w, wgt[s0 + 3], a1);
         }
-        for (; s < nsplit; ++s) a0 = fmaf(pa[s], w[s], a0);
-        out[(int64_t(b) * Hq + j * G + (o / kHeadDim)) * kHeadDim + (o % kHeadDim)] = f32_to_bf16_rne((a0 + a1) + (a2 + a3));
     }
+    float a = a0 + a1;
+    a += dpp_f<kDppXor1>(a);
+    a += dpp_f<kDppXor2>(a);
+    if (qq == 0)
+        out[(int64_t(b) * Hq + j * G + h) * kHeadDim + (o % kHeadDim)] = f32_to_bf16_rne(a);
 }
 
 template <int G>
@@ -394,8 +411,7 @@ hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const 
     p.keep_total = c->keep_total;
     p.sink = c->cfg.sink;
     p.window = c->cfg.window;
-    const size_t lds = (size_t(p.last.ncand) + size_t(p.last.keep) + 1 +
-                        size_t(select_cand_words(p.last.ncand, p.last.keep))) * 4;
+    const size_t lds = size_t(kept_lds_words(p.last, p.first_stage != 0)) * 4;
     p.Lmax = c->Lmax;
     p.Hq = c->cfg.num_q_heads;
     p.Hkv = c->cfg.num_kv_heads;
@@ -416,15 +432,12 @@ hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const 
 namespace sd {
 
 hipError_t launch_combine(sd_ctx* c, uint16_t* out, hipStream_t s, Timing t) {
-    dim3 grid(c->cfg.num_kv_heads, c->cfg.batch), block(kAttnThreads);
-    const int Hq = c->cfg.num_q_heads, Hkv = c->cfg.num_kv_heads;
-    const float* part = c->part;
-    const int Bh = c->cfg.batch * c->cfg.num_kv_heads;
-    switch (c->G) {
-        case 1: launch(sd_combine_kernel<1>, grid, block, 0, s, t, part, c->nsplit, Bh, Hq, Hkv, out); break;
-        case 2: launch(sd_combine_kernel<2>, grid, block, 0, s, t, part, c->nsplit, Bh, Hq, Hkv, out); break;
-        default: launch(sd_combine_kernel<4>, grid, block, 0, s, t, part, c->nsplit, Bh, Hq, Hkv, out); break;
-    }
+    const int G = c->G;
+    dim3 grid(G * kHeadDim / kCombOut, c->cfg.num_kv_heads, c->cfg.batch), block(kAttnThreads);
+    static_assert(kAttnThreads == 4 * kCombOut, "4 lanes per output");
+    static_assert(kHeadDim % kCombOut == 0, "a combine workgroup stays within one head");
+    launch(sd_combine_kernel, grid, block, 0, s, t, static_cast<const float*>(c->part), c->nsplit,
+           c->cfg.batch * c->cfg.num_kv_heads, G, c->cfg.num_q_heads, c->cfg.num_kv_heads, out);
     return hipGetLastError();
 }
 

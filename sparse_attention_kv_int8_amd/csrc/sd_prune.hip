@@ -115,7 +115,7 @@ __device__ __forceinline__ void split_query(const int* Qlds, int sl, u32x4& qh, 
 }
 
 __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PruneParams p) {
-    extern __shared__ uint32_t dyn[];      // keys [prev.ncand], sel [prev.keep], select scratch
+    extern __shared__ uint32_t dyn[];      // the previous stage's select (kept_lds_words)
     __shared__ int Qlds[kHeadDim];
     __shared__ unsigned tmp[32];
 
@@ -137,12 +137,10 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
         // the group query load is issued together with the previous scores' loads
         const int qval = threadIdx.x < kHeadDim ? p.qgroup[int64_t(bj) * kHeadDim + threadIdx.x] : 0;
         // kept set of the previous stage (its own parents are in kept_idx already)
-        uint32_t* keys = dyn;
         int* sel = reinterpret_cast<int*>(dyn + p.prev.ncand);
-        int* cand = sel + p.prev.keep + 1;
         const int32_t* pp = p.stage >= 2 ? kept_bj + p.pp_koff : nullptr;
         const int nk = kept_of_stage<kPruneThreads>(p.prev, p.stage == 1, p.prev_scores + int64_t(bj) * p.prev.ncand,
-                                                    pp, L, keys, sel, cand, tmp);
+                                                    pp, L, dyn, tmp);
         if (blockIdx.x == 0)
             for (int i = threadIdx.x; i < p.prev.keep; i += kPruneThreads) kept_bj[p.prev.koff + i] = i < nk ? sel[i] : -1;
         for (int i = nk + threadIdx.x; i < p.prev.keep; i += kPruneThreads) sel[i] = -1;
@@ -201,7 +199,7 @@ hipError_t launch_prune_stage(sd_ctx* c, int st, const uint16_t* q, const int8_t
         p.prev = stage_dev(c, st - 1);
         p.prev_scores = c->scores[st - 1];
         p.pp_koff = st >= 2 ? c->st[st - 2].koff : 0;
-        lds = (size_t(p.prev.ncand) + size_t(p.prev.keep) + 1 + size_t(select_cand_words(p.prev.ncand, p.prev.keep))) * 4;
+        lds = size_t(kept_lds_words(p.prev, st == 1)) * 4;
     }
     dim3 grid(c->st[st].nwg, c->cfg.num_kv_heads, c->cfg.batch);
     launch(sd_prune_stage_kernel, grid, dim3(kPruneThreads), lds, s, t, p);

@@ -21,7 +21,7 @@ namespace sd {
 
 // LDS words the select needs besides keys [n] and sel [K + 1].
 __host__ __device__ inline int select_cand_words(int n, int K) {
-    const int groups = (n + 1022) / 1023;
+    const int groups = (n + 1023) / 1024;
     return groups > 1 ? groups * (K + 1) + groups : 0;
 }
 
@@ -50,65 +50,144 @@ __device__ __forceinline__ int64_t cand_start(const StageDev& st, bool first_sta
 // larger key is better and equal keys go to the lower index.  The
 // threshold T (the K-th largest key) is built two bits per round from the
 // top: three candidate thresholds are counted per lane in VALU, the counts
-// packed into 16-bit fields and summed across the wave with DPP, and the
+// packed into bit fields and summed across the wave with DPP, and the
 // largest threshold whose count reaches K is kept.  Keys > T are kept, and
 // of the keys equal to T the lowest indices, K - #(keys > T) of them.  One
 // wave does the whole search: no barrier and no LDS atomics (both are slow
 // on this chip compared with DPP).
 // ------------------------------------------------------------------------
-constexpr int kSelGroup = 1023;              // keys one wave selects from (<= 16 per lane)
+constexpr int kSelGroup = 1024;              // keys one wave selects from (<= 16 per lane)
 constexpr int kKeyBits = 24;
 
 __device__ __forceinline__ uint32_t score_key(int s) {
     return s == INT32_MIN ? 0u : uint32_t(s + (1 << 23));
 }
 
-// Wave-wide sum of a value whose 16-bit fields stay below 2^16.
-__device__ __forceinline__ unsigned wave_sum_packed(unsigned v) { return wave_sum_u(v); }
+// Single instructions the compiler would otherwise rewrite into
+// compare/select chains through VCC (or a 64-bit multiply).  Kept as
+// separate statements so that the keys' independent chains interleave.
+__device__ __forceinline__ int med3_03(int t) {
+    int d;
+    asm("v_med3_i32 %0, %1, 0, 3" : "=v"(d) : "v"(t));
+    return d;
+}
+__device__ __forceinline__ unsigned shift_of(int d) {      // 30 - 10 d
+    unsigned r;
+    asm("v_mad_i32_i24 %0, %1, -10, 30" : "=v"(r) : "v"(d));
+    return r;
+}
+__device__ __forceinline__ unsigned lshr(unsigned x, unsigned s) {
+    unsigned r;
+    asm("v_lshrrev_b32 %0, %1, %2" : "=v"(r) : "v"(s), "v"(x));
+    return r;
+}
 
-// One wave: top-K of m keys key(i) = keys[idx ? idx[i] : i], m <= min(64 E, 1023).
+// Sign bit of a wave-uniform value as 0/1 in a scalar register (written out
+// because the compiler turns the equivalent comparison into a round trip
+// through a vector register).
+__device__ __forceinline__ int sign_bit_s(int v) {
+    int r;
+    asm("s_lshr_b32 %0, %1, 31" : "=s"(r) : "s"(__builtin_amdgcn_readfirstlane(v)));
+    return r;
+}
+
+// One wave: top-K of m keys key(i) = keys[idx ? idx[i] : i], m <= 64 E <= 1024.
 // Lane l owns the contiguous positions [l*E, l*E + E).  Writes the kept
-// positions i (ascending) to out[0..kept) (out has K + 1 slots; slot K is
-// scratch); returns kept = min(K, #valid).
+// positions i (ascending) to out[0..kept) (out has K + 1 slots); returns
+// kept = min(K, #valid).
 template <int E>
 __device__ __forceinline__ int wave_select_e(const uint32_t* keys, const int* idx, int m, int K, int* out) {
     const int lane = threadIdx.x & 63;
     uint32_t kk[E];
-    unsigned nv = 0;
+    unsigned nv = 0, kmin = 0xffffffffu, kmax = 0;
 #pragma unroll
     for (int u = 0; u < E; ++u) {
         const int i = lane * E + u;
         kk[u] = i < m ? keys[idx ? idx[i] : i] : 0u;
         nv += kk[u] != 0u;
+        kmin = min(kmin, kk[u] ? kk[u] : 0xffffffffu);
+        kmax = max(kmax, kk[u]);
     }
     const int nvalid = int(wave_sum_u(nv));
     uint32_t T = 0;
     int need_eq = 0;
     if (nvalid > K) {
-        // Round: thresholds prefix + {1,2,3} << b.  For a key, d = number of
-        // them it reaches = clamp((key - prefix) >> b, 0, 3); its packed
-        // contribution 0x100401 >> (30 - 10 d) adds 1 to each of the d lowest
-        // 10-bit fields (fields: reaches c1, c2, c3).  Wave sums of a field
-        // stay below 2^10 because m <= 1023.
+        // Rebase valid keys to key - min + 1 (order and validity kept) so the
+        // search starts at the highest bit in which they can differ.
+        kmin = wave_min_u(kmin);
+        kmax = wave_max_u(kmax);
+#pragma unroll
+        for (int u = 0; u < E; ++u) kk[u] = kk[u] ? kk[u] - kmin + 1u : 0u;
+        const uint32_t range = kmax - kmin + 1u;              // largest rebased key
+        const int bits = 32 - __builtin_clz(range);           // range < 2^bits
+        int b = bits > 2 ? ((bits - 1) & ~1) : 0;             // even, 4 << b > range
+        // Round b: thresholds prefix + {1,2,3} << b.  A key reaches
+        // d = clamp((key - prefix) >> b, 0, 3) of them (prefix is a multiple
+        // of 4 << b); 0x100401 >> (30 - 10 d) adds 1 to each of the d lowest
+        // 10-bit fields, so one wave sum gives the three counts.  A count can
+        // reach 1024 only with 16 keys per lane: there the key at position
+        // 1023 is counted in scalar registers instead, keeping the fields
+        // below 1024.
+        uint32_t kc[E];
+#pragma unroll
+        for (int u = 0; u < E; ++u) kc[u] = kk[u];
+        uint32_t kx = 0;
+        if (E == 16) {
+            kx = __builtin_amdgcn_readlane(kk[E - 1], 63);
+            if (lane == 63) kc[E - 1] = 0u;
+        }
+        const unsigned ones = 0x100401u;
         uint32_t prefix = 0;
-        for (int b = kKeyBits - 2; b >= 0; b -= 2) {
+        int cnt = nvalid;                      // valid keys >= prefix
+        bool exact = false;
+        for (; b >= 0; b -= 2) {
+            int t[E];
+            unsigned f[E];
+#pragma unroll
+            for (int u = 0; u < E; ++u) t[u] = (int(kc[u]) - int(prefix)) >> b;
+#pragma unroll
+            for (int u = 0; u < E; ++u) t[u] = med3_03(t[u]);
+#pragma unroll
+            for (int u = 0; u < E; ++u) f[u] = shift_of(t[u]);
+#pragma unroll
+            for (int u = 0; u < E; ++u) f[u] = lshr(ones, f[u]);
             unsigned acc = 0;
 #pragma unroll
-            for (int u = 0; u < E; ++u) {
-                const int d = min(max((int(kk[u]) - int(prefix)) >> b, 0), 3);
-                acc += 0x100401u >> (30 - 10 * d);
-            }
+            for (int u = 0; u < E; ++u) acc += f[u];
             acc = wave_sum_u(acc);
-            const int n1 = int(acc & 0x3ffu), n2 = int((acc >> 10) & 0x3ffu), n3 = int(acc >> 20);
-            prefix += n3 >= K ? (3u << b) : n2 >= K ? (2u << b) : n1 >= K ? (1u << b) : 0u;
+            int n1 = int(acc & 0x3ffu), n2 = int((acc >> 10) & 0x3ffu), n3 = int(acc >> 20);
+            if (E == 16) {
+                const int dx = min(max((int(kx) - int(prefix)) >> b, 0), 3);
+                n1 += dx >= 1;
+                n2 += dx >= 2;
+                n3 += dx >= 3;
+            }
+            // n1 >= n2 >= n3: the largest threshold still reaching K is the
+            // number of counts >= K
+            // (sign bits: n >= K  <=>  K - 1 - n < 0, kept in scalar ALU)
+            const int c = sign_bit_s(K - 1 - n1) + sign_bit_s(K - 1 - n2) + sign_bit_s(K - 1 - n3);
+            prefix += uint32_t(c) << b;
+            const int nc = c >= 3 ? n3 : c >= 2 ? n2 : n1;
+            cnt = c > 0 ? nc : cnt;
+            if (cnt == K) {                    // exactly K keys >= prefix: they are the top K
+                exact = true;
+                break;
+            }
         }
-        T = prefix;
-        unsigned gl = 0;
+        if (exact) {
+            T = prefix - 1u;                   // keys > T are kept, no tie to break
+            need_eq = 0;
+        } else {
+            T = prefix;                        // the K-th largest (rebased) key
+            unsigned gl = 0;
 #pragma unroll
-        for (int u = 0; u < E; ++u) gl += kk[u] > T ? 1u : 0u;
-        need_eq = K - int(wave_sum_u(gl));
+            for (int u = 0; u < E; ++u) gl += kk[u] > T ? 1u : 0u;
+            need_eq = K - int(wave_sum_u(gl));
+        }
     }
-    // ordered compaction: (count of keys > T, count of keys == T) per lane, scanned
+    // ordered compaction: (count of keys > T, count of keys == T) per lane,
+    // scanned; a kept key goes to (#greater before it) + min(#equal before it,
+    // need_eq).  Stores are masked (distinct addresses, no LDS conflicts).
     unsigned g = 0, e = 0;
 #pragma unroll
     for (int u = 0; u < E; ++u) { g += kk[u] > T; e += (kk[u] == T) && kk[u]; }
@@ -121,8 +200,7 @@ __device__ __forceinline__ int wave_select_e(const uint32_t* keys, const int* id
     for (int u = 0; u < E; ++u) {
         const bool gt = kk[u] > T;
         const bool eq = (kk[u] == T) && kk[u];
-        const unsigned pos = gt ? g + min(e, neq) : (eq && e < neq) ? g + e : unsigned(K);
-        out[pos] = lane * E + u;          // non-kept keys land in the scratch slot K
+        if (gt || (eq && e < neq)) out[g + min(e, neq)] = lane * E + u;
         g += gt;
         e += eq;
     }
@@ -134,7 +212,7 @@ __device__ __forceinline__ int wave_select(const uint32_t* keys, const int* idx,
     if (m <= 128) return wave_select_e<2>(keys, idx, m, K, out);
     if (m <= 256) return wave_select_e<4>(keys, idx, m, K, out);
     if (m <= 512) return wave_select_e<8>(keys, idx, m, K, out);
-    return wave_select_e<16>(keys, idx, m, K, out);      // m <= 1023
+    return wave_select_e<16>(keys, idx, m, K, out);      // m <= 1024
 }
 
 // Block-level: top-K of n keys in LDS (n <= 16 * kSelGroup).  Groups of
@@ -199,21 +277,32 @@ __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, int* can
     return kept;
 }
 
+// LDS words kept_of_stage uses: keys [ncand], sel [keep + 1], select
+// scratch, and (after the first stage) the parents [ncand / ratio].
+__host__ __device__ inline int kept_lds_words(const StageDev& st, bool first_stage) {
+    return st.ncand + st.keep + 1 + select_cand_words(st.ncand, st.keep) + (first_stage ? 0 : st.ncand / st.ratio);
+}
+
 // Kept set of stage `st` for one (request, KV head), from that stage's
-// scores (global, INT32_MIN = no candidate): sel[0..nk) receives the kept
-// chunk starts, ascending.  `parents` are the kept starts of the stage
-// before (global or LDS; unused for the first stage).  keys: LDS [ncand];
-// sel: LDS [keep + 1]; cand: LDS [select_cand_words(ncand, keep)].
+// scores (global, INT32_MIN = no candidate).  Returns nk; the kept chunk
+// starts, ascending, are sel[0..nk) with sel = (int*)(lds + st.ncand).
+// `parents` are the kept starts of the stage before (global, -1 padded;
+// unused for the first stage): they are staged in LDS together with the
+// scores, so turning selected indices into starts costs no memory latency
+// after the select.  lds: kept_lds_words(st, first_stage) words.
 template <int NT>
 __device__ int kept_of_stage(const StageDev& st, bool first_stage, const int32_t* scores_bj,
-                             const int32_t* parents, int64_t L, uint32_t* keys, int* sel, int* cand,
-                             unsigned* tmp) {
-    for (int i = threadIdx.x; i < st.ncand; i += NT) {
-        keys[i] = score_key(scores_bj[i]);
-    }
+                             const int32_t* parents, int64_t L, uint32_t* lds, unsigned* tmp) {
+    uint32_t* keys = lds;
+    int* sel = reinterpret_cast<int*>(lds + st.ncand);
+    int* cand = sel + st.keep + 1;
+    int* par = cand + select_cand_words(st.ncand, st.keep);
+    for (int i = threadIdx.x; i < st.ncand; i += NT) keys[i] = score_key(scores_bj[i]);
+    if (!first_stage)
+        for (int i = threadIdx.x; i < st.ncand / st.ratio; i += NT) par[i] = parents[i];
     __syncthreads();
     const int nk = select_top<NT>(keys, st.ncand, st.keep, sel, cand, tmp);
-    for (int i = threadIdx.x; i < nk; i += NT) sel[i] = int(cand_start(st, first_stage, parents, sel[i], L));
+    for (int i = threadIdx.x; i < nk; i += NT) sel[i] = int(cand_start(st, first_stage, par, sel[i], L));
     __syncthreads();
     return nk;
 }

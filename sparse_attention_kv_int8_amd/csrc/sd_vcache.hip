@@ -59,7 +59,7 @@ struct VcStepParams {
 };
 
 __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParams p) {
-    extern __shared__ uint32_t dyn[];    // keys [last.ncand], sel [last.keep], select scratch
+    extern __shared__ uint32_t dyn[];    // the last stage's select (kept_lds_words)
     __shared__ unsigned tmp[32];
     const ValueCache& vc = p.vc;
     const int max_blocks = p.max_blocks;
@@ -73,9 +73,8 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
     // last stage's kept set and the attended blocks
     int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
     int* sel = reinterpret_cast<int*>(dyn + p.last.ncand);
-    int* cand = sel + p.last.keep + 1;
     const int nk = kept_of_stage<kLruThreads>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
-                                              p.first_stage ? nullptr : kept_bj + p.pp_koff, L, dyn, sel, cand, tmp);
+                                              p.first_stage ? nullptr : kept_bj + p.pp_koff, L, dyn, tmp);
     for (int i = tid; i < p.last.keep; i += kLruThreads) kept_bj[p.last.koff + i] = i < nk ? sel[i] : -1;
     uint32_t* blocks_bj = p.blocks + int64_t(bj) * max_blocks;
     const int nb = build_attended<kLruThreads>(sel, nk, p.last.chunk, L, p.sink, p.window, blocks_bj, tmp);
@@ -189,8 +188,7 @@ hipError_t launch_value_cache_update(sd_ctx* c, const int32_t* lengths, int32_t*
     p.max_blocks = c->max_blocks;
     p.Hkv = c->cfg.num_kv_heads;
     p.step = int32_t(c->vc_step);
-    const size_t lds = (size_t(p.last.ncand) + size_t(p.last.keep) + 1 +
-                        size_t(select_cand_words(p.last.ncand, p.last.keep))) * 4;
+    const size_t lds = size_t(kept_lds_words(p.last, p.first_stage != 0)) * 4;
     dim3 grid(c->cfg.num_kv_heads, c->cfg.batch);
     launch(sd_vcache_step_kernel, grid, dim3(kLruThreads), lds, s, t, p);
     ++c->vc_step;

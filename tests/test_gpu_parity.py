@@ -126,6 +126,22 @@ def test_many_candidate_groups_with_ties():
     run_case(w, modify=dup, check_scores=True)
 
 
+@pytest.mark.parametrize("max_context", [65536, 131072 - 40])
+def test_all_scores_equal_in_full_groups(max_context):
+    """Every key row identical, so every chunk score of a stage is equal: the
+    lowest starts must win.  65,536 tokens give exactly 1,024 stage-0
+    candidates (one full group of the select); the ragged second size gives
+    two groups, the last one partial."""
+    w = tiny_workload(name="equal", batch=1, num_q_heads=4, num_kv_heads=1, max_context=max_context,
+                      stages=(Stage(64, 8, 40), Stage(8, 1, 64)), sink=0, window=0, planted=0)
+
+    def same(inp):
+        inp.k[0, 0, :] = inp.k[0, 0, 0]
+
+    g, inp, ref = run_case(w, modify=same, check_scores=True)
+    assert list(ref.kept_idx[0, 0, :40]) == [64 * i for i in range(40)]
+
+
 def test_forced_ties():
     """Many identical key rows: chunk scores tie, the lower start must win."""
     w = tiny_workload(name="ties", max_context=8192, planted=0)
