@@ -18,7 +18,10 @@ value  = algorithmic HBM bytes of a step / wall time per step (GB/s), where
          the query read and output written.
 roofline = the dominant kernel's algorithmic bytes per launch / its average
          launch duration, timed with HIP events on the launch stream during
-         the timed region, against 8 TB/s.
+         the timed region, against 8 TB/s.  `traffic` is that kernel's HBM
+         bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE counters
+         (scaled by a plain copy of known size; see profiles/), or null when
+         no record exists or the kernel sources changed since it was taken.
 cpu_baseline = the CPU oracle (numpy, one core) on one full step of the same
          workload.
 """
@@ -242,6 +245,9 @@ def main() -> int:
                     "defeat the 256 MB Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary", default="ctx_1m", help="second workload reported inside the line ('' = none)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain elementwise copy (torch.neg) of MIB MiB three times: the "
+                         "reference that scales hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -260,11 +266,23 @@ def main() -> int:
         est *= wl.batch if wl.batch > 1 else 1
         return max(2, min(16, math.ceil(600e6 / est) + 1))
 
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
     b, r = measure(w, args.steps, args.warmup, auto_copies(w))
     total = r["bytes"]["total"]
     dom_bytes = r["bytes"]["per_kernel"][r["dominant"]]
     achieved = dom_bytes / (r["dominant_us"] * 1e-6) / 1e9
     sum_kernel_us = sum(v for k, v in r["avg_us"].items() if k != "quantize")
+    from sparse_attention_kv_int8_amd.profiling import load_traffic
+    tr = load_traffic(w.name, r["dominant"])
     line = {
         "metric": METRIC,
         "value": round(total / (r["us_per_step"] * 1e-6) / 1e9, 2),
@@ -287,7 +305,7 @@ def main() -> int:
         "algorithmic_bytes": total,
         "roofline": {"bound": "hbm", "kernel": r["dominant"], "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": dom_bytes,
+                     "traffic": tr["traffic_bytes"] if tr else None, "bytes_per_launch": dom_bytes,
                      "avg_launch_us": round(r["dominant_us"], 3)},
         "step_kernels_us": {k: round(v, 3) for k, v in r["avg_us"].items()},
         "step_roofline": {"achieved": round(total / (sum_kernel_us * 1e-6) / 1e9, 2), "unit": "GB/s",

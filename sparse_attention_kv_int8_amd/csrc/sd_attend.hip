@@ -293,10 +293,10 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         wacc[wave][h][2 * lane + 1] = acc1[h];
     }
     __syncthreads();
-    // partials: acc at [bj][h][dd][split] (a split's values of one output are
-    // adjacent for the merge), (m, l) at [bj][h][split][2] after all acc
-    float* pacc = p.part + int64_t(bj) * G * kHeadDim * p.nsplit;
-    float* pml = p.part + int64_t(p.Bh) * G * kHeadDim * p.nsplit + int64_t(bj) * G * p.nsplit * 2;
+    // partials: acc at [bj][split][h][dd] (each workgroup writes one
+    // contiguous G x 128 slab), (m, l) at [bj][split][h][2] after all acc
+    float* pacc = p.part + (int64_t(bj) * p.nsplit + sp) * G * kHeadDim;
+    float* pml = p.part + int64_t(p.Bh) * G * kHeadDim * p.nsplit + (int64_t(bj) * p.nsplit + sp) * G * 2;
     for (int o = threadIdx.x; o < G * kHeadDim; o += kAttnThreads) {
         const int h = o / kHeadDim, dd = o % kHeadDim;
         float M = -INFINITY;
@@ -309,74 +309,80 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
             a = fmaf(wacc[w][h][dd], f, a);
             l = fmaf(wl[w][h], f, l);
         }
-        pacc[(h * kHeadDim + dd) * p.nsplit + sp] = a;
+        pacc[o] = a;
         if (dd == 0) {
-            pml[(h * p.nsplit + sp) * 2] = M;
-            pml[(h * p.nsplit + sp) * 2 + 1] = l;
+            pml[h * 2] = M;
+            pml[h * 2 + 1] = l;
         }
     }
 }
 
 // Log-sum-exp merge of the splits, rounding to bf16.  A workgroup merges 64
-// outputs of one head (4 lanes per output, a quarter of the splits each, so
-// the partials are read by many workgroups at once and with few dependent
-// loads per lane): the partial loads are issued first, wave 0 meanwhile
-// computes the head's split weights exp2(m_s - M) / sum_s l_s exp2(m_s - M),
-// and each output is a weighted sum over splits finished across its 4 lanes.
+// outputs of one head: thread t reads float4 q = t % 16 of those outputs from
+// splits t / 16, t / 16 + 16, ... (each split's 64 values are one contiguous
+// 256 B row, so the reads coalesce).  The partial loads are issued first;
+// wave 0 meanwhile computes the head's split weights
+// exp2(m_s - M) / sum_s l_s exp2(m_s - M); each thread sums its splits
+// weighted, and the 16 split groups are added through LDS.
 constexpr int kMaxSplit = 64;
 constexpr int kCombOut = 64;                 // outputs per combine workgroup
+constexpr int kCombGroups = kAttnThreads / (kCombOut / 4);   // 16 split groups
 
 __global__ __launch_bounds__(kAttnThreads) void sd_combine_kernel(const float* __restrict__ part, int nsplit, int Bh,
                                                                  int G, int Hq, int Hkv, uint16_t* __restrict__ out) {
     __shared__ float wgt[kMaxSplit];
+    __shared__ float4 red[kCombGroups][kCombOut / 4];
     const int j = blockIdx.y, b = blockIdx.z, bj = b * Hkv + j;
-    const int o = blockIdx.x * kCombOut + (threadIdx.x >> 2);        // output of this lane, in [0, G*128)
-    const int h = (blockIdx.x * kCombOut) / kHeadDim;
-    const int qq = threadIdx.x & 3;
-    const float* pa = part + (int64_t(bj) * G * kHeadDim + o) * nsplit;
-    const float* pml = part + int64_t(Bh) * G * kHeadDim * nsplit + (int64_t(bj) * G + h) * nsplit * 2;
-    // lane qq owns splits {4 qq + 16 i + u}
-    float4 v[kMaxSplit / 16];
-    const bool vec = (nsplit & 3) == 0;
+    const int o0 = blockIdx.x * kCombOut;                  // first output, in [0, G*128)
+    const int h = o0 / kHeadDim;
+    const int q = threadIdx.x % (kCombOut / 4), sg = threadIdx.x / (kCombOut / 4);
+    const int64_t row = int64_t(G) * kHeadDim;             // floats per split
+    const float* pa = part + int64_t(bj) * nsplit * row + o0 + 4 * q;
+    const float* pml = part + int64_t(Bh) * G * kHeadDim * nsplit + int64_t(bj) * nsplit * G * 2 + h * 2;
+    float4 v[kMaxSplit / kCombGroups];
 #pragma unroll
-    for (int i = 0; i < kMaxSplit / 16; ++i) {
-        const int s0 = 4 * qq + 16 * i;
-        v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (vec) {
-            if (s0 < nsplit) v[i] = *reinterpret_cast<const float4*>(pa + s0);
-        } else {
-            if (s0 < nsplit) v[i].x = pa[s0];
-            if (s0 + 1 < nsplit) v[i].y = pa[s0 + 1];
-            if (s0 + 2 < nsplit) v[i].z = pa[s0 + 2];
-            if (s0 + 3 < nsplit) v[i].w = pa[s0 + 3];
-        }
+    for (int i = 0; i < kMaxSplit / kCombGroups; ++i) {
+        const int s = sg + kCombGroups * i;
+        v[i] = s < nsplit ? *reinterpret_cast<const float4*>(pa + s * row) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if (threadIdx.x < kWave) {
         const int lane = threadIdx.x;
-        const float m = lane < nsplit ? pml[lane * 2] : -INFINITY;
-        const float l = lane < nsplit ? pml[lane * 2 + 1] : 0.f;
+        const float m = lane < nsplit ? pml[lane * G * 2] : -INFINITY;
+        const float l = lane < nsplit ? pml[lane * G * 2 + 1] : 0.f;
         const float M = wave_max_f(m);
         const float f = rescale(m, M);
         const float Lt = wave_sum_f(l * f);
         wgt[lane] = (lane < nsplit && Lt > 0.f) ? f / Lt : 0.f;
     }
     __syncthreads();
-    float a0 = 0.f, a1 = 0.f;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int i = 0; i < kMaxSplit / 16; ++i) {
-        const int s0 = 4 * qq + 16 * i;
-        if (s0 < nsplit) {
-            a0 = fmaf(v[i].x, wgt[s0], a0);
-            a1 = fmaf(v[i].y, wgt[s0 + 1], a1);
-            a0 = fmaf(v[i].z, wgt[s0 + 2], a0);
-            a1 = fmaf(v[i].w, wgt[s0 + 3], a1);
-        }
+    for (int i = 0; i < kMaxSplit / kCombGroups; ++i) {
+        const int s = sg + kCombGroups * i;
+        const float w = s < nsplit ? wgt[s] : 0.f;
+        a.x = fmaf(v[i].x, w, a.x);
+        a.y = fmaf(v[i].y, w, a.y);
+        a.z = fmaf(v[i].z, w, a.z);
+        a.w = fmaf(v[i].w, w, a.w);
     }
-    float a = a0 + a1;
-    a += dpp_f<kDppXor1>(a);
-    a += dpp_f<kDppXor2>(a);
-    if (qq == 0)
-        out[(int64_t(b) * Hq + j * G + h) * kHeadDim + (o % kHeadDim)] = f32_to_bf16_rne(a);
+    red[sg][q] = a;
+    __syncthreads();
+    if (threadIdx.x < kCombOut / 4) {
+        float4 t = red[0][threadIdx.x];
+#pragma unroll
+        for (int g = 1; g < kCombGroups; ++g) {
+            const float4 u = red[g][threadIdx.x];
+            t.x += u.x;
+            t.y += u.y;
+            t.z += u.z;
+            t.w += u.w;
+        }
+        const int dd = (o0 % kHeadDim) + 4 * threadIdx.x;
+        uint16_t* o = out + (int64_t(b) * Hq + j * G + h) * kHeadDim + dd;
+        const uint32_t lo = uint32_t(f32_to_bf16_rne(t.x)) | (uint32_t(f32_to_bf16_rne(t.y)) << 16);
+        const uint32_t hi = uint32_t(f32_to_bf16_rne(t.z)) | (uint32_t(f32_to_bf16_rne(t.w)) << 16);
+        *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+    }
 }
 
 template <int G>
@@ -434,7 +440,7 @@ namespace sd {
 hipError_t launch_combine(sd_ctx* c, uint16_t* out, hipStream_t s, Timing t) {
     const int G = c->G;
     dim3 grid(G * kHeadDim / kCombOut, c->cfg.num_kv_heads, c->cfg.batch), block(kAttnThreads);
-    static_assert(kAttnThreads == 4 * kCombOut, "4 lanes per output");
+    static_assert(kAttnThreads % (kCombOut / 4) == 0 && kMaxSplit % kCombGroups == 0, "combine thread layout");
     static_assert(kHeadDim % kCombOut == 0, "a combine workgroup stays within one head");
     launch(sd_combine_kernel, grid, block, 0, s, t, static_cast<const float*>(c->part), c->nsplit,
            c->cfg.batch * c->cfg.num_kv_heads, G, c->cfg.num_q_heads, c->cfg.num_kv_heads, out);
