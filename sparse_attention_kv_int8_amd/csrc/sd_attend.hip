@@ -200,7 +200,9 @@ __device__ __forceinline__ void attend_block(const BlockData& d, const uint32_t 
     }
 }
 
-template <int G, bool HOSTV>
+// One instantiation per (group size, values on host, select width of the
+// last stage; unused with host values).
+template <int G, bool HOSTV, int SEL>
 __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendParams p) {
     extern __shared__ uint32_t dyn[];   // device values: keys [last.ncand], sel [last.keep + 1], select scratch
     __shared__ float wm[kAttnWaves][G];
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         src.type = kKept;
         int* sel = reinterpret_cast<int*>(dyn + p.last.ncand);
         int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
-        const int nk = kept_of_stage<kAttnThreads>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
+        const int nk = kept_of_stage<kAttnThreads, SEL>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
                                                    p.first_stage ? nullptr : kept_bj + p.pp_koff, L, dyn, tmp);
         const int spb = sp - p.nsplit_a, nsb = p.nsplit - p.nsplit_a;
         if (spb == 0)
@@ -387,8 +389,9 @@ __global__ __launch_bounds__(kAttnThreads) void sd_combine_kernel(const float* _
 
 template <int G>
 static void launch_g(const AttendParams& p, dim3 grid, bool hostv, size_t lds, hipStream_t s, Timing t) {
-    if (hostv) launch(sd_flash_decode_kernel<G, true>, grid, dim3(kAttnThreads), 0, s, t, p);
-    else launch(sd_flash_decode_kernel<G, false>, grid, dim3(kAttnThreads), lds, s, t, p);
+    if (hostv) launch(sd_flash_decode_kernel<G, true, 8>, grid, dim3(kAttnThreads), 0, s, t, p);
+    else if (select_width(p.last.ncand) == 8) launch(sd_flash_decode_kernel<G, false, 8>, grid, dim3(kAttnThreads), lds, s, t, p);
+    else launch(sd_flash_decode_kernel<G, false, 16>, grid, dim3(kAttnThreads), lds, s, t, p);
 }
 
 hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -114,6 +114,10 @@ __device__ __forceinline__ void split_query(const int* Qlds, int sl, u32x4& qh, 
     ql = u32x4{l4[0], l4[1], l4[2], l4[3]};
 }
 
+// One instantiation per (rows per candidate / 8, select width of the
+// previous stage; 0 = stage 0): each launch carries only its own path, which
+// keeps code size and scalar-register pressure down.
+template <int NS8, int SEL>
 __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PruneParams p) {
     extern __shared__ uint32_t dyn[];      // the previous stage's select (kept_lds_words)
     __shared__ int Qlds[kHeadDim];
@@ -121,15 +125,14 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
 
     const int j = blockIdx.y, b = blockIdx.z;
     const int bj = b * p.Hkv + j;
-    int64_t L = p.lengths[b];
-    if (L < 1 || L > p.Lmax) {
-        if (p.stage == 0 && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(p.flag, 1);
-        L = 0;
-    }
+    const int64_t Lraw = p.lengths[b];
+    const bool bad = Lraw < 1 || Lraw > p.Lmax;
+    const int64_t L = bad ? 0 : Lraw;          // an invalid request has no candidates
     int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
 
     const int32_t* parents = nullptr;
-    if (p.stage == 0) {
+    if constexpr (SEL == 0) {
+        if (bad && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(p.flag, 1);
         group_query_codes(p.q + int64_t(b) * p.Hq * kHeadDim, j, p.G, Qlds, nullptr);
         if (blockIdx.x == 0 && threadIdx.x < kHeadDim)
             p.qgroup[int64_t(bj) * kHeadDim + threadIdx.x] = Qlds[threadIdx.x];
@@ -139,8 +142,8 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
         // kept set of the previous stage (its own parents are in kept_idx already)
         int* sel = reinterpret_cast<int*>(dyn + p.prev.ncand);
         const int32_t* pp = p.stage >= 2 ? kept_bj + p.pp_koff : nullptr;
-        const int nk = kept_of_stage<kPruneThreads>(p.prev, p.stage == 1, p.prev_scores + int64_t(bj) * p.prev.ncand,
-                                                    pp, L, dyn, tmp);
+        const int nk = kept_of_stage<kPruneThreads, SEL>(p.prev, p.stage == 1, p.prev_scores + int64_t(bj) * p.prev.ncand,
+                                                         pp, L, dyn, tmp);
         if (blockIdx.x == 0)
             for (int i = threadIdx.x; i < p.prev.keep; i += kPruneThreads) kept_bj[p.prev.koff + i] = i < nk ? sel[i] : -1;
         for (int i = nk + threadIdx.x; i < p.prev.keep; i += kPruneThreads) sel[i] = -1;
@@ -156,11 +159,7 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
     int32_t* scores_bj = p.scores + int64_t(bj) * p.cur.ncand;
     const int wave = threadIdx.x >> 6;
     const int first = (blockIdx.x * kPruneWaves + wave) * p.cpw;
-    const int ns8 = (p.cur.nsamp + 7) >> 3;
-    if (ns8 == 1) score_slice<1>(p, parents, L, k8_bj, qh, ql, first, scores_bj);
-    else if (ns8 == 2) score_slice<2>(p, parents, L, k8_bj, qh, ql, first, scores_bj);
-    else if (ns8 <= 4) score_slice<4>(p, parents, L, k8_bj, qh, ql, first, scores_bj);
-    else score_slice<8>(p, parents, L, k8_bj, qh, ql, first, scores_bj);
+    score_slice<NS8>(p, parents, L, k8_bj, qh, ql, first, scores_bj);
 }
 
 StageDev stage_dev(const sd_ctx* c, int st) {
@@ -202,7 +201,19 @@ hipError_t launch_prune_stage(sd_ctx* c, int st, const uint16_t* q, const int8_t
         lds = size_t(kept_lds_words(p.prev, st == 1)) * 4;
     }
     dim3 grid(c->st[st].nwg, c->cfg.num_kv_heads, c->cfg.batch);
-    launch(sd_prune_stage_kernel, grid, dim3(kPruneThreads), lds, s, t, p);
+    const int ns8 = (p.cur.nsamp + 7) >> 3;
+    const int sel = st == 0 ? 0 : select_width(p.prev.ncand);
+#define SD_PRUNE(N, S) launch(sd_prune_stage_kernel<N, S>, grid, dim3(kPruneThreads), lds, s, t, p)
+#define SD_PRUNE_NS(S)                    \
+    if (ns8 == 1) SD_PRUNE(1, S);         \
+    else if (ns8 == 2) SD_PRUNE(2, S);    \
+    else if (ns8 <= 4) SD_PRUNE(4, S);    \
+    else SD_PRUNE(8, S)
+    if (sel == 0) { SD_PRUNE_NS(0); }
+    else if (sel == 8) { SD_PRUNE_NS(8); }
+    else { SD_PRUNE_NS(16); }
+#undef SD_PRUNE_NS
+#undef SD_PRUNE
     return hipGetLastError();
 }
 

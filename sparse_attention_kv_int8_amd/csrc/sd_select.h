@@ -47,14 +47,11 @@ __device__ __forceinline__ int64_t cand_start(const StageDev& st, bool first_sta
 //
 // Keys are score + 2^23 (a chunk score satisfies |S| <= 4 * 127 * 127 * 128
 // < 2^23, so a key lies in [1, 2^24)), with 0 meaning "no candidate"; a
-// larger key is better and equal keys go to the lower index.  The
-// threshold T (the K-th largest key) is built two bits per round from the
-// top: three candidate thresholds are counted per lane in VALU, the counts
-// packed into bit fields and summed across the wave with DPP, and the
-// largest threshold whose count reaches K is kept.  Keys > T are kept, and
-// of the keys equal to T the lowest indices, K - #(keys > T) of them.  One
-// wave does the whole search: no barrier and no LDS atomics (both are slow
-// on this chip compared with DPP).
+// larger key is better and equal keys go to the lower index.  One wave
+// finds the threshold T (the K-th largest key) two bits per round, counting
+// with compares into scalar masks and scalar popcounts, then compacts the
+// kept positions in order: no barrier, no LDS atomics and no cross-lane
+// reduction chain inside the search.
 // ------------------------------------------------------------------------
 constexpr int kSelGroup = 1024;              // keys one wave selects from (<= 16 per lane)
 constexpr int kKeyBits = 24;
@@ -63,23 +60,36 @@ __device__ __forceinline__ uint32_t score_key(int s) {
     return s == INT32_MIN ? 0u : uint32_t(s + (1 << 23));
 }
 
-// Single instructions the compiler would otherwise rewrite into
-// compare/select chains through VCC (or a 64-bit multiply).  Kept as
-// separate statements so that the keys' independent chains interleave.
-__device__ __forceinline__ int med3_03(int t) {
-    int d;
-    asm("v_med3_i32 %0, %1, 0, 3" : "=v"(d) : "v"(t));
-    return d;
+// Compares of 4 keys against wave-uniform thresholds, each into its own
+// scalar register pair (the lanes that pass), issued back to back: a
+// compare's mask is ready for its scalar popcount only some 30 cycles
+// later, so the compares of a block overlap that latency.
+#define SD_CMP(op, d, v, t) "v_cmp_" op "_u32_e64 %" #d ", %" #v ", %" #t "\n\t"
+__device__ __forceinline__ void cmp4x3_ge(const uint32_t* k, uint32_t t1, uint32_t t2, uint32_t t3, uint64_t* m) {
+    asm(SD_CMP("ge", 0, 12, 16) SD_CMP("ge", 1, 12, 17) SD_CMP("ge", 2, 12, 18)
+        SD_CMP("ge", 3, 13, 16) SD_CMP("ge", 4, 13, 17) SD_CMP("ge", 5, 13, 18)
+        SD_CMP("ge", 6, 14, 16) SD_CMP("ge", 7, 14, 17) SD_CMP("ge", 8, 14, 18)
+        SD_CMP("ge", 9, 15, 16) SD_CMP("ge", 10, 15, 17) SD_CMP("ge", 11, 15, 18)
+        : "=&s"(m[0]), "=&s"(m[1]), "=&s"(m[2]), "=&s"(m[3]), "=&s"(m[4]), "=&s"(m[5]),
+          "=&s"(m[6]), "=&s"(m[7]), "=&s"(m[8]), "=&s"(m[9]), "=&s"(m[10]), "=&s"(m[11])
+        : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "s"(__builtin_amdgcn_readfirstlane(t1)),
+          "s"(__builtin_amdgcn_readfirstlane(t2)), "s"(__builtin_amdgcn_readfirstlane(t3)));
 }
-__device__ __forceinline__ unsigned shift_of(int d) {      // 30 - 10 d
-    unsigned r;
-    asm("v_mad_i32_i24 %0, %1, -10, 30" : "=v"(r) : "v"(d));
-    return r;
+__device__ __forceinline__ void cmp4_ge(const uint32_t* k, uint32_t t, uint64_t* m) {
+    asm(SD_CMP("ge", 0, 4, 8) SD_CMP("ge", 1, 5, 8) SD_CMP("ge", 2, 6, 8) SD_CMP("ge", 3, 7, 8)
+        : "=&s"(m[0]), "=&s"(m[1]), "=&s"(m[2]), "=&s"(m[3])
+        : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "s"(__builtin_amdgcn_readfirstlane(t)));
 }
-__device__ __forceinline__ unsigned lshr(unsigned x, unsigned s) {
-    unsigned r;
-    asm("v_lshrrev_b32 %0, %1, %2" : "=v"(r) : "v"(s), "v"(x));
-    return r;
+__device__ __forceinline__ void cmp4_gt(const uint32_t* k, uint32_t t, uint64_t* m) {
+    asm(SD_CMP("gt", 0, 4, 8) SD_CMP("gt", 1, 5, 8) SD_CMP("gt", 2, 6, 8) SD_CMP("gt", 3, 7, 8)
+        : "=&s"(m[0]), "=&s"(m[1]), "=&s"(m[2]), "=&s"(m[3])
+        : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "s"(__builtin_amdgcn_readfirstlane(t)));
+}
+#undef SD_CMP
+__device__ __forceinline__ int popc(uint64_t m) { return __builtin_popcountll(m); }
+// Set bits of m in lanes below this one.
+__device__ __forceinline__ unsigned below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi(unsigned(m >> 32), __builtin_amdgcn_mbcnt_lo(unsigned(m), 0u));
 }
 
 // Sign bit of a wave-uniform value as 0/1 in a scalar register (written out
@@ -91,80 +101,69 @@ __device__ __forceinline__ int sign_bit_s(int v) {
     return r;
 }
 
-// One wave: top-K of m keys key(i) = keys[idx ? idx[i] : i], m <= 64 E <= 1024.
-// Lane l owns the contiguous positions [l*E, l*E + E).  Writes the kept
-// positions i (ascending) to out[0..kept) (out has K + 1 slots); returns
-// kept = min(K, #valid).
+// One full wave: top-K of m keys key(i) = keys[idx ? idx[i] : i], m <= 64 E
+// <= 1024.  Slot u of lane l holds position i = 64 u + l (conflict-free LDS
+// reads; ascending i is slot-major).  Writes the kept positions i, ascending,
+// to out[0..kept) (out has K + 1 slots); returns kept = min(K, #valid).
+//
+// The threshold T (the K-th largest key) is built two bits per round from
+// the top: the counts of keys >= prefix + {1,2,3} << b come from compares
+// into scalar masks and scalar popcounts, and the largest threshold whose
+// count reaches K extends the prefix.  The search stops early once exactly K
+// keys lie at or above the prefix (then those are the top K and no tie needs
+// breaking).  Keys > T are kept, and of the keys equal to T the lowest
+// positions, K - #(keys > T) of them.
 template <int E>
 __device__ __forceinline__ int wave_select_e(const uint32_t* keys, const int* idx, int m, int K, int* out) {
+    constexpr int EP = E < 4 ? 4 : E;          // slots, padded with empty keys to blocks of 4
     const int lane = threadIdx.x & 63;
-    uint32_t kk[E];
-    unsigned nv = 0, kmin = 0xffffffffu, kmax = 0;
+    uint32_t kk[EP];
 #pragma unroll
-    for (int u = 0; u < E; ++u) {
-        const int i = lane * E + u;
-        kk[u] = i < m ? keys[idx ? idx[i] : i] : 0u;
-        nv += kk[u] != 0u;
-        kmin = min(kmin, kk[u] ? kk[u] : 0xffffffffu);
-        kmax = max(kmax, kk[u]);
+    for (int u = 0; u < EP; ++u) {
+        const int i = 64 * u + lane;
+        kk[u] = (u < E && i < m) ? keys[idx ? idx[i] : i] : 0u;
     }
-    const int nvalid = int(wave_sum_u(nv));
+    int nvalid = 0;
+#pragma unroll
+    for (int u = 0; u < EP; u += 4) {
+        uint64_t mk[4];
+        cmp4_ge(kk + u, 1u, mk);
+        nvalid += popc(mk[0]) + popc(mk[1]) + popc(mk[2]) + popc(mk[3]);
+    }
     uint32_t T = 0;
     int need_eq = 0;
     if (nvalid > K) {
         // Rebase valid keys to key - min + 1 (order and validity kept) so the
         // search starts at the highest bit in which they can differ.
+        uint32_t kmin = 0xffffffffu, kmax = 0;
+#pragma unroll
+        for (int u = 0; u < E; ++u) {
+            kmin = min(kmin, kk[u] ? kk[u] : 0xffffffffu);
+            kmax = max(kmax, kk[u]);
+        }
         kmin = wave_min_u(kmin);
         kmax = wave_max_u(kmax);
 #pragma unroll
         for (int u = 0; u < E; ++u) kk[u] = kk[u] ? kk[u] - kmin + 1u : 0u;
         const uint32_t range = kmax - kmin + 1u;              // largest rebased key
         const int bits = 32 - __builtin_clz(range);           // range < 2^bits
-        int b = bits > 2 ? ((bits - 1) & ~1) : 0;             // even, 4 << b > range
-        // Round b: thresholds prefix + {1,2,3} << b.  A key reaches
-        // d = clamp((key - prefix) >> b, 0, 3) of them (prefix is a multiple
-        // of 4 << b); 0x100401 >> (30 - 10 d) adds 1 to each of the d lowest
-        // 10-bit fields, so one wave sum gives the three counts.  A count can
-        // reach 1024 only with 16 keys per lane: there the key at position
-        // 1023 is counted in scalar registers instead, keeping the fields
-        // below 1024.
-        uint32_t kc[E];
-#pragma unroll
-        for (int u = 0; u < E; ++u) kc[u] = kk[u];
-        uint32_t kx = 0;
-        if (E == 16) {
-            kx = __builtin_amdgcn_readlane(kk[E - 1], 63);
-            if (lane == 63) kc[E - 1] = 0u;
-        }
-        const unsigned ones = 0x100401u;
         uint32_t prefix = 0;
         int cnt = nvalid;                      // valid keys >= prefix
         bool exact = false;
-        for (; b >= 0; b -= 2) {
-            int t[E];
-            unsigned f[E];
+        // b even with 4 << b > range
+        for (int b = bits > 2 ? ((bits - 1) & ~1) : 0; b >= 0; b -= 2) {
+            const uint32_t t1 = prefix + (1u << b), t2 = prefix + (2u << b), t3 = prefix + (3u << b);
+            int n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
-            for (int u = 0; u < E; ++u) t[u] = (int(kc[u]) - int(prefix)) >> b;
-#pragma unroll
-            for (int u = 0; u < E; ++u) t[u] = med3_03(t[u]);
-#pragma unroll
-            for (int u = 0; u < E; ++u) f[u] = shift_of(t[u]);
-#pragma unroll
-            for (int u = 0; u < E; ++u) f[u] = lshr(ones, f[u]);
-            unsigned acc = 0;
-#pragma unroll
-            for (int u = 0; u < E; ++u) acc += f[u];
-            acc = wave_sum_u(acc);
-            int n1 = int(acc & 0x3ffu), n2 = int((acc >> 10) & 0x3ffu), n3 = int(acc >> 20);
-            if (E == 16) {
-                const int dx = min(max((int(kx) - int(prefix)) >> b, 0), 3);
-                n1 += dx >= 1;
-                n2 += dx >= 2;
-                n3 += dx >= 3;
+            for (int u = 0; u < EP; u += 4) {
+                uint64_t c[12];
+                cmp4x3_ge(kk + u, t1, t2, t3, c);
+                n1 += popc(c[0]) + popc(c[3]) + popc(c[6]) + popc(c[9]);
+                n2 += popc(c[1]) + popc(c[4]) + popc(c[7]) + popc(c[10]);
+                n3 += popc(c[2]) + popc(c[5]) + popc(c[8]) + popc(c[11]);
             }
             // n1 >= n2 >= n3: the largest threshold still reaching K is the
-            // number of counts >= K
-            // (sign bits: n >= K  <=>  K - 1 - n < 0, kept in scalar ALU)
+            // number of counts >= K (sign bits: n >= K  <=>  K - 1 - n < 0)
             const int c = sign_bit_s(K - 1 - n1) + sign_bit_s(K - 1 - n2) + sign_bit_s(K - 1 - n3);
             prefix += uint32_t(c) << b;
             const int nc = c >= 3 ? n3 : c >= 2 ? n2 : n1;
@@ -176,53 +175,65 @@ __device__ __forceinline__ int wave_select_e(const uint32_t* keys, const int* id
         }
         if (exact) {
             T = prefix - 1u;                   // keys > T are kept, no tie to break
-            need_eq = 0;
         } else {
             T = prefix;                        // the K-th largest (rebased) key
-            unsigned gl = 0;
+            int ngt = 0;
 #pragma unroll
-            for (int u = 0; u < E; ++u) gl += kk[u] > T ? 1u : 0u;
-            need_eq = K - int(wave_sum_u(gl));
+            for (int u = 0; u < EP; u += 4) {
+                uint64_t mk[4];
+                cmp4_gt(kk + u, T, mk);
+                ngt += popc(mk[0]) + popc(mk[1]) + popc(mk[2]) + popc(mk[3]);
+            }
+            need_eq = K - ngt;
         }
     }
-    // ordered compaction: (count of keys > T, count of keys == T) per lane,
-    // scanned; a kept key goes to (#greater before it) + min(#equal before it,
-    // need_eq).  Stores are masked (distinct addresses, no LDS conflicts).
-    unsigned g = 0, e = 0;
+    // ordered compaction: a kept key goes to #(greater keys before it) +
+    // min(#(equal keys before it), need_eq); "before" = smaller position.
+    // Masks are taken four slots at a time (few scalar registers live).
+    int gsum = 0, esum = 0;
 #pragma unroll
-    for (int u = 0; u < E; ++u) { g += kk[u] > T; e += (kk[u] == T) && kk[u]; }
-    const unsigned packed = (g << 16) | e;
-    const unsigned ex = wave_incl_scan(packed) - packed;
-    g = ex >> 16;
-    e = ex & 0xffffu;
-    const unsigned neq = unsigned(need_eq);
+    for (int u0 = 0; u0 < EP; u0 += 4) {
+        uint64_t G[4];
+        cmp4_gt(kk + u0, T, G);
+        if (need_eq == 0) {
 #pragma unroll
-    for (int u = 0; u < E; ++u) {
-        const bool gt = kk[u] > T;
-        const bool eq = (kk[u] == T) && kk[u];
-        if (gt || (eq && e < neq)) out[g + min(e, neq)] = lane * E + u;
-        g += gt;
-        e += eq;
+            for (int v = 0; v < 4; ++v) {
+                const int u = u0 + v;
+                if (u < E && kk[u] > T) out[gsum + int(below(G[v]))] = 64 * u + lane;
+                gsum += popc(G[v]);
+            }
+        } else {
+            // equal keys: >= T and not > T (T >= 1 here, so they are valid keys)
+            uint64_t Q[4];
+            cmp4_ge(kk + u0, T, Q);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int u = u0 + v;
+                Q[v] &= ~G[v];
+                const int er = esum + int(below(Q[v]));
+                const bool gt = kk[u] > T, eq = kk[u] == T;
+                if (u < E && (gt || (eq && er < need_eq))) out[gsum + int(below(G[v])) + min(er, need_eq)] = 64 * u + lane;
+                gsum += popc(G[v]);
+                esum += popc(Q[v]);
+            }
+        }
     }
     return min(K, nvalid);
 }
 
-__device__ __forceinline__ int wave_select(const uint32_t* keys, const int* idx, int m, int K, int* out) {
-    if (m <= 64) return wave_select_e<1>(keys, idx, m, K, out);
-    if (m <= 128) return wave_select_e<2>(keys, idx, m, K, out);
-    if (m <= 256) return wave_select_e<4>(keys, idx, m, K, out);
-    if (m <= 512) return wave_select_e<8>(keys, idx, m, K, out);
-    return wave_select_e<16>(keys, idx, m, K, out);      // m <= 1024
-}
+// Select width for n candidates: 8 keys per lane up to 512, else 16 (groups
+// of 1024 and the final select over their survivors).
+__host__ __device__ constexpr int select_width(int n) { return n <= 512 ? 8 : 16; }
 
-// Block-level: top-K of n keys in LDS (n <= 16 * kSelGroup).  Groups of
-// kSelGroup keys are reduced to their own top-K by the waves in parallel
-// (exact: a key among the global top K is among its group's top K under the
-// same order); one wave then selects from the groups' survivors.  sel
-// (K + 1 ints) receives the kept indices ascending.  cand: LDS,
-// select_cand_words(n, K) ints.
-template <int NT>
+// Block-level: top-K of n keys in LDS (n <= 16 * kSelGroup), with
+// E = select_width(n).  Groups of kSelGroup keys are reduced to their own
+// top-K by the waves in parallel (exact: a key among the global top K is
+// among its group's top K under the same order); one wave then selects from
+// the groups' survivors.  sel (K + 1 ints) receives the kept indices
+// ascending.  cand: LDS, select_cand_words(n, K) ints.
+template <int NT, int E>
 __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, int* cand, unsigned* tmp) {
+    static_assert(E == 8 || E == 16, "select width");
     constexpr int NW = NT / kWave;
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int ngroups = (n + kSelGroup - 1) / kSelGroup;
@@ -241,7 +252,7 @@ __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, int* can
         kept = int(total);
     } else if (ngroups <= 1) {
         if (wid == 0) {
-            const int r = wave_select(keys, nullptr, n, K, sel);
+            const int r = wave_select_e<E>(keys, nullptr, n, K, sel);
             if (lane == 0) tmp[0] = unsigned(r);
         }
         __syncthreads();
@@ -252,7 +263,7 @@ __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, int* can
             const int base = g * kSelGroup;
             const int m = min(kSelGroup, n - base);
             int* out = cand + g * (K + 1);
-            const int r = wave_select(keys + base, nullptr, m, K, out);
+            const int r = wave_select_e<16>(keys + base, nullptr, m, K, out);
             for (int i = lane; i < r; i += kWave) out[i] += base;
             if (lane == 0) counts[g] = r;
         }
@@ -266,7 +277,7 @@ __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, int* can
                 off += r;
                 __builtin_amdgcn_wave_barrier();
             }
-            const int r = wave_select(keys, cand, off, K, sel);
+            const int r = wave_select_e<16>(keys, cand, off, K, sel);
             // positions -> indices
             for (int i = lane; i < r; i += kWave) sel[i] = cand[sel[i]];
             if (lane == 0) tmp[0] = unsigned(r);
@@ -290,7 +301,7 @@ __host__ __device__ inline int kept_lds_words(const StageDev& st, bool first_sta
 // unused for the first stage): they are staged in LDS together with the
 // scores, so turning selected indices into starts costs no memory latency
 // after the select.  lds: kept_lds_words(st, first_stage) words.
-template <int NT>
+template <int NT, int E>
 __device__ int kept_of_stage(const StageDev& st, bool first_stage, const int32_t* scores_bj,
                              const int32_t* parents, int64_t L, uint32_t* lds, unsigned* tmp) {
     uint32_t* keys = lds;
@@ -301,7 +312,7 @@ __device__ int kept_of_stage(const StageDev& st, bool first_stage, const int32_t
     if (!first_stage)
         for (int i = threadIdx.x; i < st.ncand / st.ratio; i += NT) par[i] = parents[i];
     __syncthreads();
-    const int nk = select_top<NT>(keys, st.ncand, st.keep, sel, cand, tmp);
+    const int nk = select_top<NT, E>(keys, st.ncand, st.keep, sel, cand, tmp);
     for (int i = threadIdx.x; i < nk; i += NT) sel[i] = int(cand_start(st, first_stage, par, sel[i], L));
     __syncthreads();
     return nk;

@@ -58,6 +58,7 @@ struct VcStepParams {
     int32_t step;
 };
 
+template <int SEL>
 __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParams p) {
     extern __shared__ uint32_t dyn[];    // the last stage's select (kept_lds_words)
     __shared__ unsigned tmp[32];
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
     // last stage's kept set and the attended blocks
     int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
     int* sel = reinterpret_cast<int*>(dyn + p.last.ncand);
-    const int nk = kept_of_stage<kLruThreads>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
+    const int nk = kept_of_stage<kLruThreads, SEL>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
                                               p.first_stage ? nullptr : kept_bj + p.pp_koff, L, dyn, tmp);
     for (int i = tid; i < p.last.keep; i += kLruThreads) kept_bj[p.last.koff + i] = i < nk ? sel[i] : -1;
     uint32_t* blocks_bj = p.blocks + int64_t(bj) * max_blocks;
@@ -190,7 +191,8 @@ hipError_t launch_value_cache_update(sd_ctx* c, const int32_t* lengths, int32_t*
     p.step = int32_t(c->vc_step);
     const size_t lds = size_t(kept_lds_words(p.last, p.first_stage != 0)) * 4;
     dim3 grid(c->cfg.num_kv_heads, c->cfg.batch);
-    launch(sd_vcache_step_kernel, grid, dim3(kLruThreads), lds, s, t, p);
+    if (select_width(p.last.ncand) == 8) launch(sd_vcache_step_kernel<8>, grid, dim3(kLruThreads), lds, s, t, p);
+    else launch(sd_vcache_step_kernel<16>, grid, dim3(kLruThreads), lds, s, t, p);
     ++c->vc_step;
     return hipGetLastError();
 }
