@@ -70,46 +70,52 @@ __device__ __forceinline__ float rescale(float a, float m) {
     return a == -INFINITY ? 0.0f : fast_exp2(a - m);
 }
 
-// Tokens of block blk that are in the sink [0, s_end) or the window [w0, L).
-__device__ __forceinline__ uint32_t valid_mask8(int64_t blk, int64_t L) {
-    const int64_t over = blk * 8 + 8 - L;
+// Token positions fit 32 bits (max_context < 2^31 - 8 is checked at
+// creation), so block and mask arithmetic is 32-bit.
+//
+// Tokens of block blk below L.
+__device__ __forceinline__ uint32_t valid_mask8(int blk, int L) {
+    const int over = blk * 8 + 8 - L;
     return over <= 0 ? 0xffu : over >= 8 ? 0u : (0xffu >> over);
 }
-__device__ __forceinline__ uint32_t sinkwin_mask8(int64_t blk, int64_t L, int64_t s_end, int64_t w0) {
-    const int64_t lo = min<int64_t>(max<int64_t>(s_end - blk * 8, 0), 8);   // tokens below s_end
-    const int64_t hi = min<int64_t>(max<int64_t>(w0 - blk * 8, 0), 8);      // first token at or after w0
+// Tokens of block blk in the sink [0, s_end) or the window [w0, L).
+__device__ __forceinline__ uint32_t sinkwin_mask8(int blk, int L, int s_end, int w0) {
+    const int lo = min(max(s_end - blk * 8, 0), 8);   // tokens below s_end
+    const int hi = min(max(w0 - blk * 8, 0), 8);      // first token at or after w0
     const uint32_t m = ((1u << lo) - 1u) | (0xffu & (0xffu << hi));
     return m & valid_mask8(blk, L);
 }
 
-// Where a workgroup's blocks come from.
-//  kList:   the block list built by the value-cache kernel (host values)
-//  kRanges: the sink and window ranges, masked to sink/window tokens
-//  kKept:   the kept last-stage chunks' blocks, masked to the tokens the
-//           ranges do not cover (the two masks are disjoint; their union is T)
-enum { kList = 0, kRanges = 1, kKept = 2 };
-
-struct BlockSrc {
-    int type;
+// Where a workgroup's blocks come from (one kind per workgroup, so each
+// kind gets its own copy of the block loop).
+//  ListSrc:  the block list built by the value-cache kernel (host values)
+//  RangeSrc: the sink and window ranges, masked to sink/window tokens
+//  KeptSrc:  the kept last-stage chunks' blocks, masked to the tokens the
+//            ranges do not cover (the two masks are disjoint; their union is T)
+struct ListSrc {
     const uint32_t* list;
-    const int* kept;            // LDS, ascending kept starts
-    int bpc;
-    int64_t L, s_end, w0, nr1, wb0;
-};
-
-__device__ __forceinline__ void block_at(const BlockSrc& s, int r, int64_t& blk, uint32_t& mask) {
-    if (s.type == kList) {
-        const uint32_t e = s.list[r];
-        blk = e >> 8;
+    __device__ void at(int r, int& blk, uint32_t& mask) const {
+        const uint32_t e = list[r];
+        blk = int(e >> 8);
         mask = e & 0xffu;
-    } else if (s.type == kRanges) {
-        blk = r < s.nr1 ? int64_t(r) : s.wb0 + (r - s.nr1);
-        mask = sinkwin_mask8(blk, s.L, s.s_end, s.w0);
-    } else {
-        blk = (int64_t(s.kept[r / s.bpc]) >> 3) + (r % s.bpc);
-        mask = valid_mask8(blk, s.L) & ~sinkwin_mask8(blk, s.L, s.s_end, s.w0);
     }
-}
+};
+struct RangeSrc {
+    int nr1, wb0, s_end, w0, L;
+    __device__ void at(int r, int& blk, uint32_t& mask) const {
+        blk = r < nr1 ? r : wb0 + (r - nr1);
+        mask = sinkwin_mask8(blk, L, s_end, w0);
+    }
+};
+struct KeptSrc {
+    const int* kept;            // LDS, ascending kept starts
+    int bpc, s_end, w0, L;
+    __device__ void at(int r, int& blk, uint32_t& mask) const {
+        const int q = r / bpc;
+        blk = (kept[q] >> 3) + (r - q * bpc);
+        mask = valid_mask8(blk, L) & ~sinkwin_mask8(blk, L, s_end, w0);
+    }
+};
 
 struct BlockData {
     u32x4 k0, k1;
@@ -117,26 +123,24 @@ struct BlockData {
     uint32_t mask;
 };
 
+// Loads of one block (t0 = first token, mask = tokens that count).  Device
+// values: every load is issued unconditionally, from rows clamped below L
+// (always inside the cache), and rows outside the mask are zeroed by a
+// select, so the issue is branch-free.  Host values: hits come from the slot
+// pool, misses from host memory (rows t < L), written into their slot.
 template <bool HOSTV>
-__device__ __forceinline__ void load_block(const AttendParams& p, const BlockSrc& src, int r, int bj, int64_t L,
+__device__ __forceinline__ void load_block(const AttendParams& p, int r, int t0, uint32_t mask, int bj, int L,
                                            const uint16_t* kbase, const uint16_t* vbase, BlockData& d) {
     const int lane = threadIdx.x & 63, tok = lane >> 3, sl = lane & 7;
-    int64_t blk;
-    block_at(src, r, blk, d.mask);
-    const int64_t t0 = blk * 8;
-    d.k0 = u32x4{0, 0, 0, 0};
-    d.k1 = u32x4{0, 0, 0, 0};
-    if ((d.mask >> tok) & 1u) {
-        const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + (t0 + tok) * kHeadDim + sl * 16);
-        d.k0 = __builtin_nontemporal_load(kp);
-        d.k1 = __builtin_nontemporal_load(kp + 1);
-    }
+    d.mask = mask;
+    const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + int64_t(min(t0 + tok, L - 1)) * kHeadDim + sl * 16);
+    d.k0 = __builtin_nontemporal_load(kp);
+    d.k1 = __builtin_nontemporal_load(kp + 1);
     if (HOSTV) {
         const int32_t se = p.blk_slot[int64_t(bj) * p.max_blocks + r];
         uint32_t* prow = reinterpret_cast<uint32_t*>(p.vpool + (int64_t(bj) * p.vslots + (se & ~kVcMissBit)) * 8 * kHeadDim);
         if (se & kVcMissBit) {
-            // miss: the whole block (rows t < L) comes from host memory and fills its slot
-            const uint32_t* hrow = reinterpret_cast<const uint32_t*>(vbase + t0 * kHeadDim);
+            const uint32_t* hrow = reinterpret_cast<const uint32_t*>(vbase + int64_t(t0) * kHeadDim);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 d.vv[u] = (t0 + u < L) ? hrow[u * (kHeadDim / 2) + lane] : 0u;
@@ -144,13 +148,18 @@ __device__ __forceinline__ void load_block(const AttendParams& p, const BlockSrc
             }
         } else {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) d.vv[u] = ((d.mask >> u) & 1u) ? prow[u * (kHeadDim / 2) + lane] : 0u;
+            for (int u = 0; u < 8; ++u) d.vv[u] = ((mask >> u) & 1u) ? prow[u * (kHeadDim / 2) + lane] : 0u;
         }
-    } else {
-        const uint32_t* vrow = reinterpret_cast<const uint32_t*>(vbase + t0 * kHeadDim);
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            d.vv[u] = ((d.mask >> u) & 1u) ? __builtin_nontemporal_load(vrow + u * (kHeadDim / 2) + lane) : 0u;
+        for (int u = 0; u < 8; ++u) d.vv[u] = ((mask >> u) & 1u) ? d.vv[u] : 0u;
+    } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t* vrow = reinterpret_cast<const uint32_t*>(vbase + int64_t(min(t0 + u, L - 1)) * kHeadDim);
+            d.vv[u] = __builtin_nontemporal_load(vrow + lane);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) d.vv[u] = ((mask >> u) & 1u) ? d.vv[u] : 0u;
     }
 }
 
@@ -186,17 +195,52 @@ __device__ __forceinline__ void attend_block(const BlockData& d, const uint32_t 
         acc1[h] *= alpha;
         m[h] = mn;
     }
+    // tokens outside the mask have p = 0 and zeroed values: no branch
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-        if ((d.mask >> u) & 1u) {
-            const float v0 = bf16_lo(d.vv[u]), v1 = bf16_hi(d.vv[u]);
+        const float v0 = bf16_lo(d.vv[u]), v1 = bf16_hi(d.vv[u]);
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float pu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw[h]), u * 8));
-                acc0[h] = fmaf(pu, v0, acc0[h]);
-                acc1[h] = fmaf(pu, v1, acc1[h]);
-            }
+        for (int h = 0; h < G; ++h) {
+            const float pu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw[h]), u * 8));
+            acc0[h] = fmaf(pu, v0, acc0[h]);
+            acc1[h] = fmaf(pu, v1, acc1[h]);
         }
+    }
+}
+
+// The block loop of one workgroup over blocks [r0, r1) of its source.  The
+// (block, mask) entries are computed once per tile of kBlkTile blocks, one
+// per thread, into LDS; each wave then takes every kAttnWaves-th block of
+// the tile, two blocks in flight.
+constexpr int kBlkTile = kAttnThreads;
+
+template <int G, bool HOSTV, class Src>
+__device__ __forceinline__ void decode_blocks(const AttendParams& p, const Src& src, int r0, int r1, int bj, int L,
+                                              const uint16_t* kbase, const uint16_t* vbase,
+                                              const uint32_t (&qv)[G][8], float (&m)[G], float (&lsum)[G],
+                                              float (&acc0)[G], float (&acc1)[G], int* tblk, uint32_t* tmask) {
+    const int wave = threadIdx.x >> 6;
+    if (L <= 0) return;                    // no blocks (and no row to clamp to)
+    for (int tb = r0; tb < r1; tb += kBlkTile) {
+        const int n = min(kBlkTile, r1 - tb);
+        if (int(threadIdx.x) < n) {
+            int blk;
+            uint32_t mask;
+            src.at(tb + threadIdx.x, blk, mask);
+            tblk[threadIdx.x] = blk * 8;
+            tmask[threadIdx.x] = mask;
+        }
+        __syncthreads();
+        for (int i = wave; i < n; i += 2 * kAttnWaves) {
+            BlockData d0, d1;
+            const bool two = i + kAttnWaves < n;
+            load_block<HOSTV>(p, tb + i, tblk[i], tmask[i], bj, L, kbase, vbase, d0);
+            if (two) load_block<HOSTV>(p, tb + i + kAttnWaves, tblk[i + kAttnWaves], tmask[i + kAttnWaves], bj, L, kbase,
+                                       vbase, d1);
+            attend_block<G>(d0, qv, p.scale_log2, m, lsum, acc0, acc1);
+            if (two) attend_block<G>(d1, qv, p.scale_log2, m, lsum, acc0, acc1);
+        }
+        __syncthreads();
     }
 }
 
@@ -209,13 +253,15 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
     __shared__ float wl[kAttnWaves][G];
     __shared__ float wacc[kAttnWaves][G][kHeadDim];
     __shared__ unsigned tmp[32];
+    __shared__ int tblk[kBlkTile];          // first token of each block of the current tile
+    __shared__ uint32_t tmask[kBlkTile];    // its token mask
 
     const int sp = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int bj = b * p.Hkv + j;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sl = lane & 7;
-    int64_t L = p.lengths[b];
-    if (L < 1 || L > p.Lmax) L = 0;
+    const int64_t Lraw = p.lengths[b];
+    const int L = (Lraw < 1 || Lraw > p.Lmax) ? 0 : int(Lraw);
 
     // this lane's 16 query dims of every head of the group (bf16 pairs)
     uint32_t qv[G][8];
@@ -227,47 +273,8 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         qv[h][4] = c.x; qv[h][5] = c.y; qv[h][6] = c.z; qv[h][7] = c.w;
     }
 
-    BlockSrc src{};
-    src.L = L;
-    src.s_end = min<int64_t>(p.sink, L);
-    src.w0 = p.window > 0 ? max<int64_t>(0, L - p.window) : L;
-    int r0, r1;
-    if (HOSTV) {
-        src.type = kList;
-        src.list = p.blocks + int64_t(bj) * p.max_blocks;
-        const int nb = p.nblocks[bj];
-        const int per = (nb + p.nsplit - 1) / p.nsplit;
-        r0 = min(nb, sp * per);
-        r1 = min(nb, r0 + per);
-    } else if (sp < p.nsplit_a) {
-        // sink / window blocks: known without any selection
-        src.type = kRanges;
-        const int64_t sb1 = (src.s_end + 7) >> 3, wb1 = (L + 7) >> 3;
-        const int64_t wb0 = p.window > 0 ? (src.w0 >> 3) : wb1;
-        const bool merged = wb0 <= sb1;
-        src.nr1 = merged ? wb1 : sb1;
-        src.wb0 = wb0;
-        const int nb = int(src.nr1 + (merged ? 0 : wb1 - wb0));
-        const int per = (nb + p.nsplit_a - 1) / p.nsplit_a;
-        r0 = min(nb, sp * per);
-        r1 = min(nb, r0 + per);
-    } else {
-        // kept chunks of the last stage, recomputed from its scores
-        src.type = kKept;
-        int* sel = reinterpret_cast<int*>(dyn + p.last.ncand);
-        int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
-        const int nk = kept_of_stage<kAttnThreads, SEL>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
-                                                   p.first_stage ? nullptr : kept_bj + p.pp_koff, L, dyn, tmp);
-        const int spb = sp - p.nsplit_a, nsb = p.nsplit - p.nsplit_a;
-        if (spb == 0)
-            for (int i = threadIdx.x; i < p.last.keep; i += kAttnThreads) kept_bj[p.last.koff + i] = i < nk ? sel[i] : -1;
-        src.kept = sel;
-        src.bpc = p.last.chunk >> 3;
-        const int nb = nk * src.bpc;
-        const int per = (nb + nsb - 1) / nsb;
-        r0 = min(nb, spb * per);
-        r1 = min(nb, r0 + per);
-    }
+    const int s_end = min(p.sink, L);
+    const int w0 = p.window > 0 ? max(0, L - p.window) : L;
 
     float m[G], lsum[G], acc0[G], acc1[G];
 #pragma unroll
@@ -276,14 +283,38 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
     const uint16_t* kbase = p.k + int64_t(bj) * p.Lmax * kHeadDim;
     const uint16_t* vbase = p.v + int64_t(bj) * p.Lmax * kHeadDim;
 
-    // two blocks in flight per wave
-    for (int r = r0 + wave; r < r1; r += 2 * kAttnWaves) {
-        BlockData d0, d1;
-        const bool two = r + kAttnWaves < r1;
-        load_block<HOSTV>(p, src, r, bj, L, kbase, vbase, d0);
-        if (two) load_block<HOSTV>(p, src, r + kAttnWaves, bj, L, kbase, vbase, d1);
-        attend_block<G>(d0, qv, p.scale_log2, m, lsum, acc0, acc1);
-        if (two) attend_block<G>(d1, qv, p.scale_log2, m, lsum, acc0, acc1);
+    if (HOSTV) {
+        const int nb = p.nblocks[bj];
+        const int per = (nb + p.nsplit - 1) / p.nsplit;
+        const int r0 = min(nb, sp * per), r1 = min(nb, r0 + per);
+        decode_blocks<G, HOSTV>(p, ListSrc{p.blocks + int64_t(bj) * p.max_blocks}, r0, r1, bj, L, kbase, vbase,
+                                qv, m, lsum, acc0, acc1, tblk, tmask);
+    } else if (sp < p.nsplit_a) {
+        // sink / window blocks: known without any selection
+        const int sb1 = (s_end + 7) >> 3, wb1 = (L + 7) >> 3;
+        const int wb0 = p.window > 0 ? (w0 >> 3) : wb1;
+        const bool merged = wb0 <= sb1;
+        const int nr1 = merged ? wb1 : sb1;
+        const int nb = nr1 + (merged ? 0 : wb1 - wb0);
+        const int per = (nb + p.nsplit_a - 1) / p.nsplit_a;
+        const int r0 = min(nb, sp * per), r1 = min(nb, r0 + per);
+        decode_blocks<G, HOSTV>(p, RangeSrc{nr1, wb0, s_end, w0, L}, r0, r1, bj, L, kbase, vbase, qv, m, lsum,
+                                acc0, acc1, tblk, tmask);
+    } else {
+        // kept chunks of the last stage, recomputed from its scores
+        int* sel = reinterpret_cast<int*>(dyn + p.last.ncand);
+        int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
+        const int nk = kept_of_stage<kAttnThreads, SEL>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
+                                                        p.first_stage ? nullptr : kept_bj + p.pp_koff, L, dyn, tmp);
+        const int spb = sp - p.nsplit_a, nsb = p.nsplit - p.nsplit_a;
+        if (spb == 0)
+            for (int i = threadIdx.x; i < p.last.keep; i += kAttnThreads) kept_bj[p.last.koff + i] = i < nk ? sel[i] : -1;
+        const int bpc = p.last.chunk >> 3;
+        const int nb = nk * bpc;
+        const int per = (nb + nsb - 1) / nsb;
+        const int r0 = min(nb, spb * per), r1 = min(nb, r0 + per);
+        decode_blocks<G, HOSTV>(p, KeptSrc{sel, bpc, s_end, w0, L}, r0, r1, bj, L, kbase, vbase, qv, m, lsum,
+                                acc0, acc1, tblk, tmask);
     }
 
     // wave totals: lsum is per token group (identical in its 8 lanes)

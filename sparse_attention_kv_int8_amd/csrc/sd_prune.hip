@@ -23,6 +23,7 @@ namespace sd {
 
 constexpr int kPruneThreads = 256;
 constexpr int kPruneWaves = kPruneThreads / kWave;
+constexpr int kMaxCandPerWave = 8;          // candidates per wave (one batch of 8 row loads)
 
 struct PruneParams {
     const uint16_t* q;        // [B][Hq][d]
@@ -44,19 +45,19 @@ struct PruneParams {
 
 // Score `cpw` candidates per wave.  NS8 = rows per candidate / 8 (rounded up);
 // each load slot covers 8 rows (8 lanes x 16 bytes per 128-byte row).
+// cstart: LDS, the starts of this wave's candidates (-1 = none).
 template <int NS8>
-__device__ __forceinline__ void score_slice(const PruneParams& p, const int32_t* parents, int64_t L,
+__device__ __forceinline__ void score_slice(const PruneParams& p, const int* cstart, int64_t L,
                                             const int8_t* __restrict__ k8_bj, const u32x4& qh,
                                             const u32x4& ql, int first, int32_t* __restrict__ out) {
     const StageDev& st = p.cur;
-    const bool first_stage = p.stage == 0;
     constexpr int CB = NS8 >= 8 ? 1 : 8 / NS8;     // candidates per batch
     constexpr int NL = CB * NS8;                   // loads per batch
     const int lane = threadIdx.x & 63, row8 = lane >> 3, sl = lane & 7;
     for (int c0 = 0; c0 < p.cpw; c0 += CB) {
         int64_t xs[CB];
 #pragma unroll
-        for (int c = 0; c < CB; ++c) xs[c] = (c0 + c < p.cpw) ? cand_start(st, first_stage, parents, first + c0 + c, L) : -1;
+        for (int c = 0; c < CB; ++c) xs[c] = (c0 + c < p.cpw) ? cstart[c0 + c] : -1;
         u32x4 v[NL];
         bool ok[NL];
 #pragma unroll
@@ -122,6 +123,7 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
     extern __shared__ uint32_t dyn[];      // the previous stage's select (kept_lds_words)
     __shared__ int Qlds[kHeadDim];
     __shared__ unsigned tmp[32];
+    __shared__ int cstart[kPruneWaves * kMaxCandPerWave];
 
     const int j = blockIdx.y, b = blockIdx.z;
     const int bj = b * p.Hkv + j;
@@ -151,15 +153,20 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
         __syncthreads();
         parents = sel;
     }
+    // the starts of this workgroup's candidates, one thread each
+    const int wg_first = blockIdx.x * kPruneWaves * p.cpw;
+    if (int(threadIdx.x) < kPruneWaves * p.cpw)
+        cstart[threadIdx.x] = int(cand_start(p.cur, SEL == 0, parents, wg_first + threadIdx.x, L));
     const int sl = threadIdx.x & 7;
     u32x4 qh, ql;
     split_query(Qlds, sl, qh, ql);
+    __syncthreads();
 
     const int8_t* k8_bj = p.k8 + int64_t(bj) * p.Lmax * kHeadDim;
     int32_t* scores_bj = p.scores + int64_t(bj) * p.cur.ncand;
     const int wave = threadIdx.x >> 6;
-    const int first = (blockIdx.x * kPruneWaves + wave) * p.cpw;
-    score_slice<NS8>(p, parents, L, k8_bj, qh, ql, first, scores_bj);
+    const int first = wg_first + wave * p.cpw;
+    score_slice<NS8>(p, cstart + wave * p.cpw, L, k8_bj, qh, ql, first, scores_bj);
 }
 
 StageDev stage_dev(const sd_ctx* c, int st) {

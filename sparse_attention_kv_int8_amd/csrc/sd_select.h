@@ -250,7 +250,7 @@ __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, int* can
             if (keys[i]) sel[pos++] = i;
         __syncthreads();
         kept = int(total);
-    } else if (ngroups <= 1) {
+    } else if (E == 8 || ngroups <= 1) {     // width 8 means n <= 512: one group
         if (wid == 0) {
             const int r = wave_select_e<E>(keys, nullptr, n, K, sel);
             if (lane == 0) tmp[0] = unsigned(r);
