@@ -283,6 +283,7 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
     const uint16_t* kbase = p.k + int64_t(bj) * p.Lmax * kHeadDim;
     const uint16_t* vbase = p.v + int64_t(bj) * p.Lmax * kHeadDim;
 
+    int kept_n = -1;
     if (HOSTV) {
         const int nb = p.nblocks[bj];
         const int per = (nb + p.nsplit - 1) / p.nsplit;
@@ -307,8 +308,7 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         const int nk = kept_of_stage<kAttnThreads, SEL>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
                                                         p.first_stage ? nullptr : kept_bj + p.pp_koff, L, dyn, tmp);
         const int spb = sp - p.nsplit_a, nsb = p.nsplit - p.nsplit_a;
-        if (spb == 0)
-            for (int i = threadIdx.x; i < p.last.keep; i += kAttnThreads) kept_bj[p.last.koff + i] = i < nk ? sel[i] : -1;
+        kept_n = spb == 0 ? nk : -1;        // the first of these workgroups publishes the kept set
         const int bpc = p.last.chunk >> 3;
         const int nb = nk * bpc;
         const int per = (nb + nsb - 1) / nsb;
@@ -347,6 +347,13 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
             pml[h * 2] = M;
             pml[h * 2 + 1] = l;
         }
+    }
+    if (!HOSTV && kept_n >= 0) {
+        // the last stage's kept set (ascending, -1 padded), stored last so
+        // that no barrier waits on these stores
+        const int* sel = reinterpret_cast<const int*>(dyn + p.last.ncand);
+        int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
+        for (int i = threadIdx.x; i < p.last.keep; i += kAttnThreads) kept_bj[p.last.koff + i] = i < kept_n ? sel[i] : -1;
     }
 }
 

@@ -146,8 +146,6 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
         const int32_t* pp = p.stage >= 2 ? kept_bj + p.pp_koff : nullptr;
         const int nk = kept_of_stage<kPruneThreads, SEL>(p.prev, p.stage == 1, p.prev_scores + int64_t(bj) * p.prev.ncand,
                                                          pp, L, dyn, tmp);
-        if (blockIdx.x == 0)
-            for (int i = threadIdx.x; i < p.prev.keep; i += kPruneThreads) kept_bj[p.prev.koff + i] = i < nk ? sel[i] : -1;
         for (int i = nk + threadIdx.x; i < p.prev.keep; i += kPruneThreads) sel[i] = -1;
         if (threadIdx.x < kHeadDim) Qlds[threadIdx.x] = qval;
         __syncthreads();
@@ -167,6 +165,12 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
     const int wave = threadIdx.x >> 6;
     const int first = wg_first + wave * p.cpw;
     score_slice<NS8>(p, cstart + wave * p.cpw, L, k8_bj, qh, ql, first, scores_bj);
+    if constexpr (SEL != 0) {
+        // workgroup 0 publishes the previous stage's kept set (ascending,
+        // -1 padded); stored last, so no barrier waits on these stores
+        if (blockIdx.x == 0)
+            for (int i = threadIdx.x; i < p.prev.keep; i += kPruneThreads) kept_bj[p.prev.koff + i] = parents[i];
+    }
 }
 
 StageDev stage_dev(const sd_ctx* c, int st) {
