@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 
@@ -79,6 +80,8 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
         const int cpw = cb;
         g.per_wg = 4 * cpw;
         g.nwg = (g.ncand + g.per_wg - 1) / g.per_wg;
+        g.nrows = g.nsamp;
+        g.rstride = g.stride;
     }
     if (cfg.stage[cfg.num_stages - 1].chunk % 8 != 0) return SD_ERR_UNSUPPORTED;
     if (koff > 65535) return SD_ERR_UNSUPPORTED;
@@ -103,6 +106,37 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
         int na = int((int64_t(c->nsplit) * ra + (ra + rk) / 2) / (ra + rk));
         na = na < 1 ? 1 : na > c->nsplit - 1 ? c->nsplit - 1 : na;
         c->nsplit_a = na;
+    }
+    // Optionally (environment SD_FUSE_LAST_STAGE=1) fuse the last stage Q
+    // into the kernel of the stage P before it.  Possible when Q's chunks are
+    // exactly 8 sampled rows (one load slot), Q's stride divides P's (so P's
+    // samples are among the rows read), P reads at most 4x its own samples,
+    // all children's scores fit in LDS, and Q's select is the 8-wide one; not
+    // with host values (their value-cache kernel selects the last stage by
+    // itself).  It trades one kernel and one scoring pass for a second select
+    // in the decode kernel and more rows read by P; on the measured
+    // configurations the two are about even, so it is off by default.
+    c->fuse = 0;
+    c->fuse_rq = 0;
+    c->fuse_m = 0;
+    const char* fenv = std::getenv("SD_FUSE_LAST_STAGE");
+    const bool want_fuse = fenv && fenv[0] == '1';
+    if (want_fuse && cfg.num_stages >= 2 && !cfg.values_on_host) {
+        sd::StageGeom& P = c->st[cfg.num_stages - 2];
+        const sd::StageGeom& Q = c->st[cfg.num_stages - 1];
+        const int rq = P.chunk / Q.chunk;
+        if (Q.chunk / Q.stride == 8 && P.stride % Q.stride == 0 && P.stride / Q.stride <= 4 &&
+            P.chunk / Q.stride <= kMaxSamples && int64_t(P.ncand) * rq <= 8192 && Q.ncand <= 512) {
+            c->fuse = 1;
+            c->fuse_rq = rq;
+            c->fuse_m = P.stride / Q.stride;
+            P.nrows = P.chunk / Q.stride;
+            P.rstride = Q.stride;
+            const int ns8 = (P.nrows + 7) / 8;
+            const int ns8p = ns8 == 1 ? 1 : ns8 == 2 ? 2 : ns8 <= 4 ? 4 : 8;
+            P.per_wg = 4 * (ns8p >= 8 ? 1 : 8 / ns8p);
+            P.nwg = (P.ncand + P.per_wg - 1) / P.per_wg;
+        }
     }
     const float scale = cfg.softmax_scale > 0.0f ? cfg.softmax_scale : 1.0f / std::sqrt(float(cfg.head_dim));
     c->scale_log2 = scale * 1.4426950408889634f;
@@ -192,6 +226,9 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
         int64_t words = 0;
         for (int s = 0; s < c->S; ++s)
             words = std::max<int64_t>(words, sd::kept_lds_words(sd::stage_dev(c, s), s == 0));
+        if (c->fuse)
+            words = std::max<int64_t>(words, sd::fused_lds_words(sd::stage_dev(c, c->S - 2), c->S == 2,
+                                                                 sd::stage_dev(c, c->S - 1), c->fuse_rq));
         const int64_t static_bytes = 4 * (4 * (2 + sd::kHeadDim) * c->G + 64);
         if (words * 4 + static_bytes > lds_max) { delete c; return SD_ERR_UNSUPPORTED; }
     }
@@ -206,6 +243,7 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
     const size_t o_part = cv.take<float>(BH * c->nsplit * c->G * (2 + sd::kHeadDim));
     const size_t o_abs = cv.take<unsigned>(BH);
     const size_t o_flag = cv.take<int32_t>(1);
+    const size_t o_pre = c->fuse ? cv.take<int32_t>(BH * size_t(c->st[c->S - 2].ncand) * c->fuse_rq) : 0;
     size_t o_vc[10] = {0};
     if (cfg->values_on_host) {
         c->vc.slots = int32_t(cfg->value_cache_tokens / 8);
@@ -231,6 +269,7 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
     c->part = reinterpret_cast<float*>(base + o_part);
     c->absmax_bits = reinterpret_cast<unsigned*>(base + o_abs);
     c->flag = reinterpret_cast<int32_t*>(base + o_flag);
+    c->pre = c->fuse ? reinterpret_cast<int32_t*>(base + o_pre) : nullptr;
     if (cfg->values_on_host) {
         c->vc.pool = reinterpret_cast<uint16_t*>(base + o_vc[0]);
         c->vc.page = reinterpret_cast<int32_t*>(base + o_vc[1]);
@@ -299,7 +338,8 @@ sd_status sd_decode_step(sd_ctx* c, const uint16_t* q, const uint16_t* k, const 
         vk = c->vhost_dev;
     }
     hipError_t e = hipSuccess;
-    for (int st = 0; st < c->S && e == hipSuccess; ++st)
+    const int nprune = c->fuse ? c->S - 1 : c->S;     // a fused last stage has no kernel of its own
+    for (int st = 0; st < nprune && e == hipSuccess; ++st)
         e = timed(c, SD_PROF_STAGE0 + st, s,
                   [&](sd::Timing t) { return sd::launch_prune_stage(c, st, q, k8, lengths, kept, s, t); });
     if (e == hipSuccess && c->cfg.values_on_host)

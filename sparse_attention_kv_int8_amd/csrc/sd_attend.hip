@@ -44,11 +44,18 @@ struct AttendParams {
     StageDev last;
     int first_stage;          // the last stage is also the first
     int pp_koff;              // kept_idx offset of the stage before the last
-    const int32_t* last_scores;   // [B][Hkv][last.ncand]
+    int32_t* last_scores;     // [B][Hkv][last.ncand] (fused: written here, for inspection)
+    // fused last two stages: P = the stage before the last
+    StageDev P;
+    int p_first;              // P is the first stage
+    int pp_koff_p;            // kept_idx offset of the stage before P
+    const int32_t* p_scores;  // [B][Hkv][P.ncand]
+    const int32_t* pre;       // [B][Hkv][P.ncand * fuse_rq] every child's last-stage score
+    int fuse_rq;
     int32_t* kept;            // [B][Hkv][keep_total]
     int keep_total;
     int sink, window;
-    float* part;              // acc [B*Hkv][G][d][nsplit], then (m, l) [B*Hkv][G][nsplit][2]
+    float* part;              // acc [B*Hkv][nsplit][G][d], then (m, l) [B*Hkv][nsplit][G][2]
     int nsplit;               // splits per (request, KV head)
     int nsplit_a;             // of which sink/window splits (device values)
     int Bh;                   // B * Hkv
@@ -245,8 +252,9 @@ __device__ __forceinline__ void decode_blocks(const AttendParams& p, const Src& 
 }
 
 // One instantiation per (group size, values on host, select width of the
-// last stage; unused with host values).
-template <int G, bool HOSTV, int SEL>
+// last stage (unused with host values), select width of the stage before
+// it when the last two stages are fused here (0 = not fused)).
+template <int G, bool HOSTV, int SEL, int SELP>
 __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendParams p) {
     extern __shared__ uint32_t dyn[];   // device values: keys [last.ncand], sel [last.keep + 1], select scratch
     __shared__ float wm[kAttnWaves][G];
@@ -284,6 +292,7 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
     const uint16_t* vbase = p.v + int64_t(bj) * p.Lmax * kHeadDim;
 
     int kept_n = -1;
+    FusedOut fused{};
     if (HOSTV) {
         const int nb = p.nblocks[bj];
         const int per = (nb + p.nsplit - 1) / p.nsplit;
@@ -302,18 +311,30 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         decode_blocks<G, HOSTV>(p, RangeSrc{nr1, wb0, s_end, w0, L}, r0, r1, bj, L, kbase, vbase, qv, m, lsum,
                                 acc0, acc1, tblk, tmask);
     } else {
-        // kept chunks of the last stage, recomputed from its scores
-        int* sel = reinterpret_cast<int*>(dyn + p.last.ncand);
+        // kept chunks of the last stage, recomputed from its scores (fused:
+        // from the previous stage's scores and every child's precomputed score)
         int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
-        const int nk = kept_of_stage<kAttnThreads, SEL>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
-                                                        p.first_stage ? nullptr : kept_bj + p.pp_koff, L, dyn, tmp);
+        int nk;
+        const int* kstarts;
+        if constexpr (SELP != 0) {
+            const FusedOut fo = kept_two_stages<kAttnThreads, SELP, SEL>(
+                p.P, p.p_first != 0, p.p_scores + int64_t(bj) * p.P.ncand, p.p_first ? nullptr : kept_bj + p.pp_koff_p,
+                p.pre + int64_t(bj) * p.P.ncand * p.fuse_rq, p.fuse_rq, p.last, L, dyn, tmp);
+            nk = fo.nq;
+            kstarts = fo.q_starts;
+            fused = fo;
+        } else {
+            nk = kept_of_stage<kAttnThreads, SEL>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
+                                                  p.first_stage ? nullptr : kept_bj + p.pp_koff, L, dyn, tmp);
+            kstarts = reinterpret_cast<const int*>(dyn + p.last.ncand);
+        }
         const int spb = sp - p.nsplit_a, nsb = p.nsplit - p.nsplit_a;
         kept_n = spb == 0 ? nk : -1;        // the first of these workgroups publishes the kept set
         const int bpc = p.last.chunk >> 3;
         const int nb = nk * bpc;
         const int per = (nb + nsb - 1) / nsb;
         const int r0 = min(nb, spb * per), r1 = min(nb, r0 + per);
-        decode_blocks<G, HOSTV>(p, KeptSrc{sel, bpc, s_end, w0, L}, r0, r1, bj, L, kbase, vbase, qv, m, lsum,
+        decode_blocks<G, HOSTV>(p, KeptSrc{kstarts, bpc, s_end, w0, L}, r0, r1, bj, L, kbase, vbase, qv, m, lsum,
                                 acc0, acc1, tblk, tmask);
     }
 
@@ -350,10 +371,19 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
     }
     if (!HOSTV && kept_n >= 0) {
         // the last stage's kept set (ascending, -1 padded), stored last so
-        // that no barrier waits on these stores
-        const int* sel = reinterpret_cast<const int*>(dyn + p.last.ncand);
+        // that no barrier waits on these stores; fused: also the previous
+        // stage's kept set and the last stage's candidate scores
         int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
+        const int* sel = SELP != 0 ? fused.q_starts : reinterpret_cast<const int*>(dyn + p.last.ncand);
         for (int i = threadIdx.x; i < p.last.keep; i += kAttnThreads) kept_bj[p.last.koff + i] = i < kept_n ? sel[i] : -1;
+        if (SELP != 0) {
+            for (int i = threadIdx.x; i < p.P.keep; i += kAttnThreads) kept_bj[p.P.koff + i] = fused.p_starts[i];
+            int32_t* sc = p.last_scores + int64_t(bj) * p.last.ncand;
+            for (int i = threadIdx.x; i < p.last.ncand; i += kAttnThreads) {
+                const uint32_t key = fused.q_keys[i];
+                sc[i] = key ? int32_t(key) - (1 << 23) : INT32_MIN;
+            }
+        }
     }
 }
 
@@ -426,10 +456,13 @@ __global__ __launch_bounds__(kAttnThreads) void sd_combine_kernel(const float* _
 }
 
 template <int G>
-static void launch_g(const AttendParams& p, dim3 grid, bool hostv, size_t lds, hipStream_t s, Timing t) {
-    if (hostv) launch(sd_flash_decode_kernel<G, true, 8>, grid, dim3(kAttnThreads), 0, s, t, p);
-    else if (select_width(p.last.ncand) == 8) launch(sd_flash_decode_kernel<G, false, 8>, grid, dim3(kAttnThreads), lds, s, t, p);
-    else launch(sd_flash_decode_kernel<G, false, 16>, grid, dim3(kAttnThreads), lds, s, t, p);
+static void launch_g(const AttendParams& p, dim3 grid, bool hostv, bool fuse, size_t lds, hipStream_t s, Timing t) {
+    const dim3 block(kAttnThreads);
+    if (hostv) launch(sd_flash_decode_kernel<G, true, 8, 0>, grid, block, 0, s, t, p);
+    else if (fuse && select_width(p.P.ncand) == 8) launch(sd_flash_decode_kernel<G, false, 8, 8>, grid, block, lds, s, t, p);
+    else if (fuse) launch(sd_flash_decode_kernel<G, false, 8, 16>, grid, block, lds, s, t, p);
+    else if (select_width(p.last.ncand) == 8) launch(sd_flash_decode_kernel<G, false, 8, 0>, grid, block, lds, s, t, p);
+    else launch(sd_flash_decode_kernel<G, false, 16, 0>, grid, block, lds, s, t, p);
 }
 
 hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -458,7 +491,17 @@ hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const 
     p.keep_total = c->keep_total;
     p.sink = c->cfg.sink;
     p.window = c->cfg.window;
-    const size_t lds = size_t(kept_lds_words(p.last, p.first_stage != 0)) * 4;
+    const bool fuse = c->fuse != 0;
+    if (fuse) {
+        p.P = stage_dev(c, S - 2);
+        p.p_first = S == 2;
+        p.pp_koff_p = S >= 3 ? c->st[S - 3].koff : 0;
+        p.p_scores = c->scores[S - 2];
+        p.pre = c->pre;
+        p.fuse_rq = c->fuse_rq;
+    }
+    const size_t lds = size_t(fuse ? fused_lds_words(p.P, p.p_first != 0, p.last, p.fuse_rq)
+                                   : kept_lds_words(p.last, p.first_stage != 0)) * 4;
     p.Lmax = c->Lmax;
     p.Hq = c->cfg.num_q_heads;
     p.Hkv = c->cfg.num_kv_heads;
@@ -467,9 +510,9 @@ hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const 
     dim3 grid(c->nsplit, c->cfg.num_kv_heads, c->cfg.batch);
     const bool hostv = c->cfg.values_on_host != 0;
     switch (c->G) {
-        case 1: launch_g<1>(p, grid, hostv, lds, s, t); break;
-        case 2: launch_g<2>(p, grid, hostv, lds, s, t); break;
-        default: launch_g<4>(p, grid, hostv, lds, s, t); break;
+        case 1: launch_g<1>(p, grid, hostv, fuse, lds, s, t); break;
+        case 2: launch_g<2>(p, grid, hostv, fuse, lds, s, t); break;
+        default: launch_g<4>(p, grid, hostv, fuse, lds, s, t); break;
     }
     return hipGetLastError();
 }

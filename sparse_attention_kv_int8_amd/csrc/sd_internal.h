@@ -19,6 +19,8 @@ struct StageGeom {
     int koff;           // offset of this stage in kept_idx
     int per_wg;         // candidates scored per workgroup
     int nwg;            // workgroups per (request, KV head)
+    int nrows;          // key rows read per candidate (nsamp, or more when the next stage is fused in)
+    int rstride;        // their token stride
 };
 
 // Geometry of one stage as the kernels see it.
@@ -69,7 +71,15 @@ struct sd_ctx {
     int32_t* qgroup;                  // [B][Hkv][d] group query sums
     uint32_t* blocks;                 // [B][Hkv][max_blocks] (block << 8) | token mask
     int32_t* nblocks;                 // [B][Hkv]
-    float* part;                      // acc [B*Hkv][G][d][nsplit], then (m, l) [B*Hkv][G][nsplit][2]
+    float* part;                      // acc [B*Hkv][nsplit][G][d], then (m, l) [B*Hkv][nsplit][G][2]
+    // fused last stage: the kernel of stage S-2 also scores every child chunk
+    // of every stage S-2 candidate for stage S-1 (reading all rows stage S-1
+    // samples), and the decode kernel selects stage S-2, gathers the kept
+    // children's scores and selects stage S-1; no kernel runs for stage S-1
+    int fuse;
+    int fuse_rq;                      // children per stage S-2 chunk
+    int fuse_m;                       // stage S-2 stride / stage S-1 stride
+    int32_t* pre;                     // [B][Hkv][st[S-2].ncand * fuse_rq] children's stage S-1 scores
     unsigned* absmax_bits;            // [B][Hkv]
     int32_t* flag;                    // device error flag
     sd::ValueCache vc;

@@ -41,19 +41,31 @@ struct PruneParams {
     const int32_t* prev_scores;   // [B][Hkv][prev.ncand]
     int pp_koff;                  // kept_idx offset of stage - 2 (the previous stage's parents)
     int32_t* scores;              // [B][Hkv][cur.ncand]
+    int nrows, rstride;           // key rows read per candidate, and their token stride
+    int fuse_rq, fuse_m;          // fused next stage: children per chunk, stride ratio
+    int32_t* pre;                 // fused next stage: [B][Hkv][cur.ncand * fuse_rq] children's scores
 };
 
 // Score `cpw` candidates per wave.  NS8 = rows per candidate / 8 (rounded up);
 // each load slot covers 8 rows (8 lanes x 16 bytes per 128-byte row).
-// cstart: LDS, the starts of this wave's candidates (-1 = none).
-template <int NS8>
+// cstart: LDS, the starts of this wave's candidates (-1 = none).  Rows
+// t = x + i * rstride, i < nrows, are read (8 lanes per row, 8 rows per load
+// slot).  Without FUSE they are this stage's samples.  With FUSE they are
+// the next stage's samples (rstride = its stride, one 8-row slot per child
+// chunk): this stage's score is the max over rows i % fuse_m == 0 (its own
+// samples), and each slot's max is written as that child's score.
+template <int NS8, bool FUSE>
 __device__ __forceinline__ void score_slice(const PruneParams& p, const int* cstart, int64_t L,
                                             const int8_t* __restrict__ k8_bj, const u32x4& qh,
-                                            const u32x4& ql, int first, int32_t* __restrict__ out) {
+                                            const u32x4& ql, int first, int32_t* __restrict__ out,
+                                            int32_t* __restrict__ pre_bj) {
     const StageDev& st = p.cur;
     constexpr int CB = NS8 >= 8 ? 1 : 8 / NS8;     // candidates per batch
     constexpr int NL = CB * NS8;                   // loads per batch
     const int lane = threadIdx.x & 63, row8 = lane >> 3, sl = lane & 7;
+    bool own[NS8];                                 // row of slot it is one of this stage's samples
+#pragma unroll
+    for (int it = 0; it < NS8; ++it) own[it] = !FUSE || ((it * 8 + row8) % p.fuse_m) == 0;
     for (int c0 = 0; c0 < p.cpw; c0 += CB) {
         int64_t xs[CB];
 #pragma unroll
@@ -64,8 +76,8 @@ __device__ __forceinline__ void score_slice(const PruneParams& p, const int* cst
         for (int u = 0; u < NL; ++u) {
             const int c = u / NS8, it = u % NS8;
             const int i = it * 8 + row8;
-            const int64_t t = xs[c] + int64_t(i) * st.stride;
-            ok[u] = xs[c] >= 0 && i < st.nsamp && t < L;
+            const int64_t t = xs[c] + int64_t(i) * p.rstride;
+            ok[u] = xs[c] >= 0 && i < p.nrows && t < L;
             v[u] = ok[u] ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k8_bj + t * kHeadDim) + sl)
                          : u32x4{0, 0, 0, 0};
         }
@@ -83,7 +95,13 @@ __device__ __forceinline__ void score_slice(const PruneParams& p, const int* cst
             al = __builtin_amdgcn_sdot4((int)ql.z, (int)v[u].z, al, false);
             al = __builtin_amdgcn_sdot4((int)ql.w, (int)v[u].w, al, false);
             const int s = sum8_i(ah * 64 + al);
-            if (ok[u]) best[u / NS8] = max(best[u / NS8], s);
+            if (ok[u] && own[u % NS8]) best[u / NS8] = max(best[u / NS8], s);
+            if (FUSE) {
+                const int c = u / NS8, it = u % NS8;
+                const int sub = max_groups_i(ok[u] ? s : INT32_MIN);
+                if (lane == 0 && it < p.fuse_rq && c0 + c < p.cpw && first + c0 + c < st.ncand)
+                    pre_bj[int64_t(first + c0 + c) * p.fuse_rq + it] = sub;
+            }
         }
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
@@ -116,9 +134,9 @@ __device__ __forceinline__ void split_query(const int* Qlds, int sl, u32x4& qh, 
 }
 
 // One instantiation per (rows per candidate / 8, select width of the
-// previous stage; 0 = stage 0): each launch carries only its own path, which
-// keeps code size and scalar-register pressure down.
-template <int NS8, int SEL>
+// previous stage (0 = stage 0), fused next stage): each launch carries only
+// its own path, which keeps code size and scalar-register pressure down.
+template <int NS8, int SEL, bool FUSE>
 __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PruneParams p) {
     extern __shared__ uint32_t dyn[];      // the previous stage's select (kept_lds_words)
     __shared__ int Qlds[kHeadDim];
@@ -164,7 +182,8 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
     int32_t* scores_bj = p.scores + int64_t(bj) * p.cur.ncand;
     const int wave = threadIdx.x >> 6;
     const int first = wg_first + wave * p.cpw;
-    score_slice<NS8>(p, cstart + wave * p.cpw, L, k8_bj, qh, ql, first, scores_bj);
+    score_slice<NS8, FUSE>(p, cstart + wave * p.cpw, L, k8_bj, qh, ql, first, scores_bj,
+                           FUSE ? p.pre + int64_t(bj) * p.cur.ncand * p.fuse_rq : nullptr);
     if constexpr (SEL != 0) {
         // workgroup 0 publishes the previous stage's kept set (ascending,
         // -1 padded); stored last, so no barrier waits on these stores
@@ -204,6 +223,12 @@ hipError_t launch_prune_stage(sd_ctx* c, int st, const uint16_t* q, const int8_t
     p.cur = stage_dev(c, st);
     p.cpw = c->st[st].per_wg / kPruneWaves;
     p.scores = c->scores[st];
+    p.nrows = c->st[st].nrows;
+    p.rstride = c->st[st].rstride;
+    const bool fuse = c->fuse && st == c->S - 2;
+    p.fuse_rq = fuse ? c->fuse_rq : 0;
+    p.fuse_m = fuse ? c->fuse_m : 1;
+    p.pre = fuse ? c->pre : nullptr;
     size_t lds = 0;
     if (st > 0) {
         p.prev = stage_dev(c, st - 1);
@@ -212,14 +237,18 @@ hipError_t launch_prune_stage(sd_ctx* c, int st, const uint16_t* q, const int8_t
         lds = size_t(kept_lds_words(p.prev, st == 1)) * 4;
     }
     dim3 grid(c->st[st].nwg, c->cfg.num_kv_heads, c->cfg.batch);
-    const int ns8 = (p.cur.nsamp + 7) >> 3;
+    const int ns8 = (p.nrows + 7) >> 3;
     const int sel = st == 0 ? 0 : select_width(p.prev.ncand);
-#define SD_PRUNE(N, S) launch(sd_prune_stage_kernel<N, S>, grid, dim3(kPruneThreads), lds, s, t, p)
-#define SD_PRUNE_NS(S)                    \
-    if (ns8 == 1) SD_PRUNE(1, S);         \
-    else if (ns8 == 2) SD_PRUNE(2, S);    \
-    else if (ns8 <= 4) SD_PRUNE(4, S);    \
-    else SD_PRUNE(8, S)
+#define SD_PRUNE(N, S, F) launch(sd_prune_stage_kernel<N, S, F>, grid, dim3(kPruneThreads), lds, s, t, p)
+#define SD_PRUNE_NS(S)                                          \
+    if (fuse) {                                                 \
+        if (ns8 <= 2) SD_PRUNE(2, S, true);                     \
+        else if (ns8 <= 4) SD_PRUNE(4, S, true);                \
+        else SD_PRUNE(8, S, true);                              \
+    } else if (ns8 == 1) SD_PRUNE(1, S, false);                 \
+    else if (ns8 == 2) SD_PRUNE(2, S, false);                   \
+    else if (ns8 <= 4) SD_PRUNE(4, S, false);                   \
+    else SD_PRUNE(8, S, false)
     if (sel == 0) { SD_PRUNE_NS(0); }
     else if (sel == 8) { SD_PRUNE_NS(8); }
     else { SD_PRUNE_NS(16); }

@@ -318,6 +318,62 @@ __device__ int kept_of_stage(const StageDev& st, bool first_stage, const int32_t
     return nk;
 }
 
+// Fused last two stages P (= S-2) and Q (= S-1), for one (request, KV head):
+// select P from its scores, gather the precomputed Q scores of the kept P
+// chunks' children, select Q.  LDS words:
+//   P select [kept_lds_words(P)] | all children's Q scores [P.ncand * rq] |
+//   Q keys [Q.ncand] | Q sel [Q.keep + 1] | Q select scratch | P starts [P.keep]
+__host__ __device__ inline int fused_lds_words(const StageDev& P, bool p_first, const StageDev& Q, int rq) {
+    return kept_lds_words(P, p_first) + P.ncand * rq + Q.ncand + Q.keep + 1 + select_cand_words(Q.ncand, Q.keep) +
+           P.keep;
+}
+
+struct FusedOut {
+    int* p_starts;      // LDS [P.keep]: P's kept starts, ascending, -1 padded
+    int np;             // kept P chunks
+    int* q_starts;      // LDS [Q.keep + 1]: Q's kept starts, ascending
+    int nq;             // kept Q chunks
+    const uint32_t* q_keys;   // LDS [Q.ncand]: Q's candidate keys
+};
+
+template <int NT, int EP, int EQ>
+__device__ FusedOut kept_two_stages(const StageDev& P, bool p_first, const int32_t* scoresP_bj,
+                                    const int32_t* parentsP, const int32_t* pre_bj, int rq, const StageDev& Q,
+                                    int64_t L, uint32_t* lds, unsigned* tmp) {
+    uint32_t* keysP = lds;
+    int* selP = reinterpret_cast<int*>(lds + P.ncand);
+    int* candP = selP + P.keep + 1;
+    int* parP = candP + select_cand_words(P.ncand, P.keep);
+    int* preL = parP + (p_first ? 0 : P.ncand / P.ratio);
+    uint32_t* keysQ = reinterpret_cast<uint32_t*>(preL + P.ncand * rq);
+    int* selQ = reinterpret_cast<int*>(keysQ + Q.ncand);
+    int* candQ = selQ + Q.keep + 1;
+    int* startsP = candQ + select_cand_words(Q.ncand, Q.keep);
+
+    // every load is issued up front: P's scores, P's parents, all children's Q scores
+    for (int i = threadIdx.x; i < P.ncand; i += NT) keysP[i] = score_key(scoresP_bj[i]);
+    if (!p_first)
+        for (int i = threadIdx.x; i < P.ncand / P.ratio; i += NT) parP[i] = parentsP[i];
+    for (int i = threadIdx.x; i < P.ncand * rq; i += NT) preL[i] = pre_bj[i];
+    __syncthreads();
+    const int np = select_top<NT, EP>(keysP, P.ncand, P.keep, selP, candP, tmp);
+    // P starts; Q candidate i is child i % rq of kept P chunk i / rq
+    for (int i = threadIdx.x; i < P.keep; i += NT)
+        startsP[i] = i < np ? int(cand_start(P, p_first, parP, selP[i], L)) : -1;
+    for (int i = threadIdx.x; i < Q.ncand; i += NT) {
+        const int q = i / rq;
+        keysQ[i] = q < np ? score_key(preL[selP[q] * rq + (i - q * rq)]) : 0u;
+    }
+    __syncthreads();
+    const int nq = select_top<NT, EQ>(keysQ, Q.ncand, Q.keep, selQ, candQ, tmp);
+    for (int i = threadIdx.x; i < nq; i += NT) {
+        const int c = selQ[i], q = c / rq;
+        selQ[i] = startsP[q] + (c - q * rq) * Q.chunk;
+    }
+    __syncthreads();
+    return FusedOut{startsP, np, selQ, nq, keysQ};
+}
+
 // Attended 8-token blocks of one (request, KV head): the kept last-stage
 // chunks (starts kept_s[0..nk), ascending, chunk a multiple of 8), the sink
 // [0, sink) and the window [L - window, L), each token once, as ascending
