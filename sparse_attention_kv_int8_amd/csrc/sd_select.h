@@ -221,6 +221,181 @@ __device__ __forceinline__ int wave_select_e(const uint32_t* keys, const int* id
     return min(K, nvalid);
 }
 
+// All NW waves of the workgroup together: top-K of n <= NW * 64 * EW keys
+// in LDS.  Wave w holds positions [w * 64 EW, (w + 1) * 64 EW) (slot-major,
+// so ascending position is wave-major), counts its own keys against each
+// round's thresholds, and the per-wave counts are added through LDS (xch:
+// 2 x NW x 4 words, double buffered, so one barrier per round).  Every wave
+// takes the same decisions from the same totals.  Writes the kept positions,
+// ascending, to sel; ends with a barrier; returns min(K, #valid).
+template <int NT, int EW>
+__device__ int coop_select(const uint32_t* keys, int n, int K, int* sel, unsigned* xch) {
+    constexpr int NW = NT / kWave;
+    static_assert(EW % 4 == 0 && 2 * NW * 4 <= 32, "coop_select layout");
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int base = wid * 64 * EW;
+    uint32_t kk[EW];
+#pragma unroll
+    for (int u = 0; u < EW; ++u) {
+        const int i = base + 64 * u + lane;
+        kk[u] = i < n ? keys[i] : 0u;
+    }
+    int nv = 0;
+    uint32_t kmin = 0xffffffffu, kmax = 0;
+#pragma unroll
+    for (int u = 0; u < EW; u += 4) {
+        uint64_t mk[4];
+        cmp4_ge(kk + u, 1u, mk);
+        nv += popc(mk[0]) + popc(mk[1]) + popc(mk[2]) + popc(mk[3]);
+    }
+#pragma unroll
+    for (int u = 0; u < EW; ++u) {
+        kmin = min(kmin, kk[u] ? kk[u] : 0xffffffffu);
+        kmax = max(kmax, kk[u]);
+    }
+    kmin = wave_min_u(kmin);
+    kmax = wave_max_u(kmax);
+    int buf = 0;
+    auto exchange3 = [&](unsigned a, unsigned b, unsigned c, unsigned (&tot)[3], unsigned* before) {
+        unsigned* x = xch + buf * (NW * 4);
+        if (lane == 0) {
+            x[wid * 4] = a;
+            x[wid * 4 + 1] = b;
+            x[wid * 4 + 2] = c;
+        }
+        __syncthreads();
+        tot[0] = tot[1] = tot[2] = 0;
+        if (before) before[0] = before[1] = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const unsigned xa = x[w * 4], xb = x[w * 4 + 1], xc = x[w * 4 + 2];
+            if (before && w < wid) { before[0] += xa; before[1] += xb; }
+            tot[0] += xa;
+            tot[1] += xb;
+            tot[2] += xc;
+        }
+        buf ^= 1;
+    };
+    // valid count; min and max travel as a sum-free pair (min of mins via
+    // ~max of complements)
+    unsigned t0[3];
+    {
+        unsigned* x = xch + buf * (NW * 4);
+        if (lane == 0) {
+            x[wid * 4] = unsigned(nv);
+            x[wid * 4 + 1] = kmin;
+            x[wid * 4 + 2] = kmax;
+        }
+        __syncthreads();
+        t0[0] = 0;
+        t0[1] = 0xffffffffu;
+        t0[2] = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            t0[0] += x[w * 4];
+            t0[1] = min(t0[1], x[w * 4 + 1]);
+            t0[2] = max(t0[2], x[w * 4 + 2]);
+        }
+        buf ^= 1;
+    }
+    const int nvalid = int(t0[0]);
+    uint32_t T = 0;
+    int need_eq = 0;
+    if (nvalid > K) {
+        const uint32_t gmin = t0[1], gmax = t0[2];
+#pragma unroll
+        for (int u = 0; u < EW; ++u) kk[u] = kk[u] ? kk[u] - gmin + 1u : 0u;
+        const uint32_t range = gmax - gmin + 1u;
+        const int bits = 32 - __builtin_clz(range);
+        uint32_t prefix = 0;
+        int cnt = nvalid;
+        bool exact = false;
+        for (int b = bits > 2 ? ((bits - 1) & ~1) : 0; b >= 0; b -= 2) {
+            const uint32_t t1 = prefix + (1u << b), t2 = prefix + (2u << b), t3 = prefix + (3u << b);
+            unsigned n1 = 0, n2 = 0, n3 = 0;
+#pragma unroll
+            for (int u = 0; u < EW; u += 4) {
+                uint64_t c[12];
+                cmp4x3_ge(kk + u, t1, t2, t3, c);
+                n1 += popc(c[0]) + popc(c[3]) + popc(c[6]) + popc(c[9]);
+                n2 += popc(c[1]) + popc(c[4]) + popc(c[7]) + popc(c[10]);
+                n3 += popc(c[2]) + popc(c[5]) + popc(c[8]) + popc(c[11]);
+            }
+            unsigned tot[3];
+            exchange3(n1, n2, n3, tot, nullptr);
+            const int N1 = int(tot[0]), N2 = int(tot[1]), N3 = int(tot[2]);
+            const int c = sign_bit_s(K - 1 - N1) + sign_bit_s(K - 1 - N2) + sign_bit_s(K - 1 - N3);
+            prefix += uint32_t(c) << b;
+            const int nc = c >= 3 ? N3 : c >= 2 ? N2 : N1;
+            cnt = c > 0 ? nc : cnt;
+            if (cnt == K) {
+                exact = true;
+                break;
+            }
+        }
+        if (exact) {
+            T = prefix - 1u;
+        } else {
+            T = prefix;
+            unsigned ng = 0;
+#pragma unroll
+            for (int u = 0; u < EW; u += 4) {
+                uint64_t mk[4];
+                cmp4_gt(kk + u, T, mk);
+                ng += popc(mk[0]) + popc(mk[1]) + popc(mk[2]) + popc(mk[3]);
+            }
+            unsigned tot[3];
+            exchange3(ng, 0u, 0u, tot, nullptr);
+            need_eq = K - int(tot[0]);
+        }
+    }
+    // ordered compaction: this wave's (greater, equal) counts, then the
+    // counts of the waves before it
+    unsigned g = 0, e = 0;
+#pragma unroll
+    for (int u = 0; u < EW; u += 4) {
+        uint64_t G[4], Q[4];
+        cmp4_gt(kk + u, T, G);
+        cmp4_ge(kk + u, T ? T : 1u, Q);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            g += popc(G[v]);
+            e += popc(Q[v] & ~G[v]);
+        }
+    }
+    unsigned tot[3], before[2];
+    exchange3(g, e, 0u, tot, before);
+    int gsum = int(before[0]), esum = int(before[1]);
+#pragma unroll
+    for (int u0 = 0; u0 < EW; u0 += 4) {
+        uint64_t G[4];
+        cmp4_gt(kk + u0, T, G);
+        if (need_eq == 0) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int u = u0 + v;
+                if (kk[u] > T) sel[gsum + int(below(G[v]))] = base + 64 * u + lane;
+                gsum += popc(G[v]);
+            }
+        } else {
+            uint64_t Q[4];
+            cmp4_ge(kk + u0, T, Q);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int u = u0 + v;
+                Q[v] &= ~G[v];
+                const int er = esum + int(below(Q[v]));
+                const bool gt = kk[u] > T, eq = kk[u] == T;
+                if (gt || (eq && er < need_eq)) sel[gsum + int(below(G[v])) + min(er, need_eq)] = base + 64 * u + lane;
+                gsum += popc(G[v]);
+                esum += popc(Q[v]);
+            }
+        }
+    }
+    __syncthreads();
+    return min(K, nvalid);
+}
+
 // Select width for n candidates: 8 keys per lane up to 512, else 16 (groups
 // of 1024 and the final select over their survivors).
 __host__ __device__ constexpr int select_width(int n) { return n <= 512 ? 8 : 16; }
@@ -250,6 +425,10 @@ __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, int* can
             if (keys[i]) sel[pos++] = i;
         __syncthreads();
         kept = int(total);
+    } else if (E == 16 && n <= NW * 64 * 4) {
+        kept = coop_select<NT, 4>(keys, n, K, sel, tmp);
+    } else if (E == 16 && n <= NW * 64 * 16) {
+        kept = coop_select<NT, 16>(keys, n, K, sel, tmp);
     } else if (E == 8 || ngroups <= 1) {     // width 8 means n <= 512: one group
         if (wid == 0) {
             const int r = wave_select_e<E>(keys, nullptr, n, K, sel);
