@@ -85,8 +85,7 @@ typedef struct sd_config {
      * the last stage's chunk is a multiple of 8; keep >= 1;
      * chunk / stride <= 64 at every stage; for every stage the number of
      * candidates n_s (n_0 = ceil(Lmax / chunk[0]), n_s = keep[s-1] *
-     * chunk[s-1] / chunk[s]) plus keep[s] is at most 15872; and when
-     * n_s > 1024 and keep[s] < n_s, ceil(n_s / 1024) * keep[s] <= 1024. */
+     * chunk[s-1] / chunk[s]) plus keep[s] is at most 15872. */
     int32_t sink;               /* first `sink` tokens always attended (>= 0) */
     int32_t window;             /* last `window` tokens always attended (>= 0) */
     float softmax_scale;        /* 0 selects 1 / sqrt(head_dim) */

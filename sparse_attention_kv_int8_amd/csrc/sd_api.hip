@@ -65,10 +65,6 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
         const int64_t nc = s == 0 ? (cfg.max_context + in.chunk - 1) / in.chunk
                                   : int64_t(cfg.stage[s - 1].keep) * (cfg.stage[s - 1].chunk / in.chunk);
         if (nc + in.keep > kMaxCandidates) return SD_ERR_UNSUPPORTED;
-        // the select reduces groups of 1024 candidates to their top `keep`
-        // and then picks from at most 1024 survivors
-        const int64_t groups = (nc + 1023) / 1024;
-        if (in.keep < nc && groups > 1 && groups * in.keep > 1024) return SD_ERR_UNSUPPORTED;
         if (in.keep > kMaxCandidates) return SD_ERR_UNSUPPORTED;
         g.ncand = int(nc);
         g.koff = koff;

@@ -19,10 +19,17 @@
 
 namespace sd {
 
-// LDS words the select needs besides keys [n] and sel [K + 1].
+// Keys the cooperative select of a 256-thread workgroup holds in registers
+// (16 per lane); more stay in LDS (coop_select_lds).
+constexpr int kSelRegMax = 4096;
+// Undecided keys coop_select_lds moves from LDS to registers (4 per lane).
+constexpr int kSelList = 1024;
+
+// LDS words the select needs besides keys [n] and sel [K + 1] (the
+// cooperative selects exchange their counts through the workgroup's 32-word
+// scratch): the list of undecided keys of coop_select_lds.
 __host__ __device__ inline int select_cand_words(int n, int K) {
-    const int groups = (n + 1023) / 1024;
-    return groups > 1 ? groups * (K + 1) + groups : 0;
+    return n > kSelRegMax && K < n ? kSelList : 0;
 }
 
 // Start of candidate i of a stage (token position), or -1 if it does not
@@ -53,7 +60,6 @@ __device__ __forceinline__ int64_t cand_start(const StageDev& st, bool first_sta
 // kept positions in order: no barrier, no LDS atomics and no cross-lane
 // reduction chain inside the search.
 // ------------------------------------------------------------------------
-constexpr int kSelGroup = 1024;              // keys one wave selects from (<= 16 per lane)
 constexpr int kKeyBits = 24;
 
 __device__ __forceinline__ uint32_t score_key(int s) {
@@ -396,22 +402,242 @@ __device__ int coop_select(const uint32_t* keys, int n, int K, int* sel, unsigne
     return min(K, nvalid);
 }
 
-// Select width for n candidates: 8 keys per lane up to 512, else 16 (groups
-// of 1024 and the final select over their survivors).
+// coop_select for more keys than the waves hold in registers: the keys stay
+// in LDS, and each wave reads its share in blocks of 4 slots per pass (the
+// loop over blocks is not unrolled, which bounds register use).  The 2-bit
+// rounds leave undecided only the keys whose bits above the current digit
+// equal the prefix found so far; once those are at most kSelList, they are
+// copied to `lst` (LDS) and the remaining rounds count them from registers,
+// 4 per lane, adding the count above that bucket.  The final compaction
+// reads every key again.  Full passes: min/max, the rounds before the copy
+// (one or two on spread-out scores), the copy, and two for the compaction.
+
+template <int NT>
+__device__ int coop_select_lds(const uint32_t* keys, int n, int K, int* sel, unsigned* xch, uint32_t* lst) {
+    constexpr int NW = NT / kWave;
+    static_assert(NW * kWave * 4 == kSelList, "the list is held 4 keys per lane");
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int per_wave = (n + NW - 1) / NW;
+    const int nblk = ((per_wave + 63) / 64 + 3) / 4;        // blocks of 4 slots per wave
+    const int base = wid * nblk * 4 * 64;
+    auto key_at = [&](int u) -> uint32_t {
+        const int i = base + 64 * u + lane;
+        return i < n ? keys[i] : 0u;
+    };
+    int buf = 0;
+    // totals over the waves of (a, b, c) (or min of b and max of c), and
+    // the sums of a and b over the waves before this one
+    auto exchange = [&](unsigned a, unsigned b, unsigned c, unsigned (&tot)[3], unsigned* before, bool minmax) {
+        unsigned* x = xch + buf * (NW * 4);
+        if (lane == 0) {
+            x[wid * 4] = a;
+            x[wid * 4 + 1] = b;
+            x[wid * 4 + 2] = c;
+        }
+        __syncthreads();
+        tot[0] = 0;
+        tot[1] = minmax ? 0xffffffffu : 0u;
+        tot[2] = 0;
+        if (before) before[0] = before[1] = 0;
+        for (int w = 0; w < NW; ++w) {
+            const unsigned xa = x[w * 4], xb = x[w * 4 + 1], xc = x[w * 4 + 2];
+            if (before && w < wid) {
+                before[0] += xa;
+                before[1] += xb;
+            }
+            tot[0] += xa;
+            tot[1] = minmax ? min(tot[1], xb) : tot[1] + xb;
+            tot[2] = minmax ? max(tot[2], xc) : tot[2] + xc;
+        }
+        buf ^= 1;
+    };
+    unsigned nv = 0, kmin = 0xffffffffu, kmax = 0;
+#pragma unroll 1
+    for (int u0 = 0; u0 < nblk * 4; u0 += 4) {
+        uint32_t k4[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            k4[v] = key_at(u0 + v);
+            kmin = min(kmin, k4[v] ? k4[v] : 0xffffffffu);
+            kmax = max(kmax, k4[v]);
+        }
+        uint64_t mk[4];
+        cmp4_ge(k4, 1u, mk);
+        nv += popc(mk[0]) + popc(mk[1]) + popc(mk[2]) + popc(mk[3]);
+    }
+    kmin = wave_min_u(kmin);
+    kmax = wave_max_u(kmax);
+    unsigned t0[3];
+    exchange(nv, kmin, kmax, t0, nullptr, true);
+    const int nvalid = int(t0[0]);
+    const uint32_t gmin = t0[1];
+    auto rk = [&](uint32_t k) -> uint32_t { return k ? k - gmin + 1u : 0u; };   // rebased, order and validity kept
+    uint32_t T = 0;
+    int need_eq = 0;
+    if (nvalid > K) {
+        const uint32_t range = t0[2] - gmin + 1u;
+        const int bits = 32 - __builtin_clz(range);
+        uint32_t prefix = 0;
+        int cnt = nvalid;        // valid keys >= prefix
+        int above = 0;           // keys >= prefix + (1 << b) after a round at b
+        int cnt_w = int(nv), above_w = 0;                    // the same, this wave's keys (before the copy)
+        bool listed = false;
+        int above0 = 0;          // keys above the copied bucket
+        uint32_t lk[4] = {0u, 0u, 0u, 0u};
+        bool exact = false;
+        for (int b = bits > 2 ? ((bits - 1) & ~1) : 0; b >= 0; b -= 2) {
+            const uint32_t t1 = prefix + (1u << b), t2 = prefix + (2u << b), t3 = prefix + (3u << b);
+            unsigned n1 = 0, n2 = 0, n3 = 0;
+            if (listed) {
+                uint64_t c[12];
+                cmp4x3_ge(lk, t1, t2, t3, c);
+                n1 = popc(c[0]) + popc(c[3]) + popc(c[6]) + popc(c[9]);
+                n2 = popc(c[1]) + popc(c[4]) + popc(c[7]) + popc(c[10]);
+                n3 = popc(c[2]) + popc(c[5]) + popc(c[8]) + popc(c[11]);
+            } else {
+#pragma unroll 1
+                for (int u0 = 0; u0 < nblk * 4; u0 += 4) {
+                    uint32_t k4[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) k4[v] = rk(key_at(u0 + v));
+                    uint64_t c[12];
+                    cmp4x3_ge(k4, t1, t2, t3, c);
+                    n1 += popc(c[0]) + popc(c[3]) + popc(c[6]) + popc(c[9]);
+                    n2 += popc(c[1]) + popc(c[4]) + popc(c[7]) + popc(c[10]);
+                    n3 += popc(c[2]) + popc(c[5]) + popc(c[8]) + popc(c[11]);
+                }
+            }
+            unsigned tot[3];
+            exchange(n1, n2, n3, tot, nullptr, false);
+            const int N1 = int(tot[0]) + above0, N2 = int(tot[1]) + above0, N3 = int(tot[2]) + above0;
+            const int c = sign_bit_s(K - 1 - N1) + sign_bit_s(K - 1 - N2) + sign_bit_s(K - 1 - N3);
+            prefix += uint32_t(c) << b;
+            if (c > 0) {
+                cnt = c >= 3 ? N3 : c >= 2 ? N2 : N1;
+                cnt_w = int(c >= 3 ? n3 : c >= 2 ? n2 : n1);
+            }
+            if (c < 3) {
+                above = c >= 2 ? N3 : c >= 1 ? N2 : N1;
+                above_w = int(c >= 2 ? n3 : c >= 1 ? n2 : n1);
+            }
+            if (cnt == K) {
+                exact = true;
+                break;
+            }
+            if (!listed && b >= 2 && cnt - above <= kSelList) {
+                // copy the undecided bucket [max(prefix, 1), prefix + (1 << b)) to lst
+                unsigned tw[3], bw[2];
+                exchange(unsigned(cnt_w - above_w), 0u, 0u, tw, bw, false);
+                const uint32_t lo = prefix ? prefix : 1u, hi = prefix + (1u << b);
+                int pos = int(bw[0]);
+#pragma unroll 1
+                for (int u0 = 0; u0 < nblk * 4; u0 += 4) {
+                    uint32_t k4[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) k4[v] = rk(key_at(u0 + v));
+                    uint64_t A[4], B[4];
+                    cmp4_ge(k4, lo, A);
+                    cmp4_ge(k4, hi, B);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const uint64_t in = A[v] & ~B[v];
+                        if (k4[v] >= lo && k4[v] < hi) lst[pos + int(below(in))] = k4[v];
+                        pos += popc(in);
+                    }
+                }
+                __syncthreads();
+                const int U = int(tw[0]);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int i = wid * 256 + 64 * v + lane;
+                    lk[v] = i < U ? lst[i] : 0u;
+                }
+                above0 = above;
+                listed = true;
+            }
+        }
+        if (exact) {
+            T = prefix - 1u;
+        } else {
+            T = prefix;
+            unsigned ng = 0;
+            if (listed) {
+                uint64_t mk[4];
+                cmp4_gt(lk, T, mk);
+                ng = popc(mk[0]) + popc(mk[1]) + popc(mk[2]) + popc(mk[3]);
+            } else {
+#pragma unroll 1
+                for (int u0 = 0; u0 < nblk * 4; u0 += 4) {
+                    uint32_t k4[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) k4[v] = rk(key_at(u0 + v));
+                    uint64_t mk[4];
+                    cmp4_gt(k4, T, mk);
+                    ng += popc(mk[0]) + popc(mk[1]) + popc(mk[2]) + popc(mk[3]);
+                }
+            }
+            unsigned tot[3];
+            exchange(ng, 0u, 0u, tot, nullptr, false);
+            need_eq = K - (int(tot[0]) + above0);
+        }
+    }
+    // ordered compaction (positions are wave-major, then slot-major)
+    unsigned g = 0, e = 0;
+#pragma unroll 1
+    for (int u0 = 0; u0 < nblk * 4; u0 += 4) {
+        uint32_t k4[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) k4[v] = rk(key_at(u0 + v));
+        uint64_t G[4], Q[4];
+        cmp4_gt(k4, T, G);
+        cmp4_ge(k4, T ? T : 1u, Q);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            g += popc(G[v]);
+            e += popc(Q[v] & ~G[v]);
+        }
+    }
+    unsigned tot[3], before[2];
+    exchange(g, e, 0u, tot, before, false);
+    int gsum = int(before[0]), esum = int(before[1]);
+#pragma unroll 1
+    for (int u0 = 0; u0 < nblk * 4; u0 += 4) {
+        uint32_t k4[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) k4[v] = rk(key_at(u0 + v));
+        uint64_t G[4], Q[4];
+        cmp4_gt(k4, T, G);
+        cmp4_ge(k4, T ? T : 1u, Q);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            Q[v] &= ~G[v];
+            const int er = esum + int(below(Q[v]));
+            const bool gt = k4[v] > T, eq = k4[v] == T && k4[v] != 0u;
+            if (gt || (eq && er < need_eq)) sel[gsum + int(below(G[v])) + min(er, need_eq)] = base + 64 * (u0 + v) + lane;
+            gsum += popc(G[v]);
+            esum += popc(Q[v]);
+        }
+    }
+    __syncthreads();
+    return min(K, nvalid);
+}
+
+// Select width for n candidates: 8 keys per lane of one wave up to 512, else
+// 16 (the cooperative selects of select_top).
 __host__ __device__ constexpr int select_width(int n) { return n <= 512 ? 8 : 16; }
 
-// Block-level: top-K of n keys in LDS (n <= 16 * kSelGroup), with
-// E = select_width(n).  Groups of kSelGroup keys are reduced to their own
-// top-K by the waves in parallel (exact: a key among the global top K is
-// among its group's top K under the same order); one wave then selects from
-// the groups' survivors.  sel (K + 1 ints) receives the kept indices
-// ascending.  cand: LDS, select_cand_words(n, K) ints.
+// Block-level: top-K of n keys in LDS, with E = select_width(n): up to 512
+// keys one wave selects alone (8 per lane); more are split between the
+// waves, which search the threshold together, holding 4 or 16 keys per lane
+// in registers (coop_select) or, past NW * 1024 keys, reading them from LDS
+// in every pass (coop_select_lds).  sel (K + 1 ints) receives the kept indices ascending.
+// cand: select_cand_words(n, K) words of LDS.  tmp: 32 words of LDS.
 template <int NT, int E>
 __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, int* cand, unsigned* tmp) {
     static_assert(E == 8 || E == 16, "select width");
+    static_assert(E == 8 || NT * 16 == kSelRegMax, "the cooperative select is laid out for 256 threads");
     constexpr int NW = NT / kWave;
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int ngroups = (n + kSelGroup - 1) / kSelGroup;
     int kept;
     if (K >= n) {
         // every valid key is kept: ordered compaction
@@ -429,36 +655,11 @@ __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, int* can
         kept = coop_select<NT, 4>(keys, n, K, sel, tmp);
     } else if (E == 16 && n <= NW * 64 * 16) {
         kept = coop_select<NT, 16>(keys, n, K, sel, tmp);
-    } else if (E == 8 || ngroups <= 1) {     // width 8 means n <= 512: one group
+    } else if (E == 16) {
+        kept = coop_select_lds<NT>(keys, n, K, sel, tmp, reinterpret_cast<uint32_t*>(cand));
+    } else {                                                  // width 8: n <= 512, one wave
         if (wid == 0) {
             const int r = wave_select_e<E>(keys, nullptr, n, K, sel);
-            if (lane == 0) tmp[0] = unsigned(r);
-        }
-        __syncthreads();
-        kept = int(tmp[0]);
-    } else {
-        int* counts = cand + ngroups * (K + 1);     // [ngroups]
-        for (int g = wid; g < ngroups; g += NW) {
-            const int base = g * kSelGroup;
-            const int m = min(kSelGroup, n - base);
-            int* out = cand + g * (K + 1);
-            const int r = wave_select_e<16>(keys + base, nullptr, m, K, out);
-            for (int i = lane; i < r; i += kWave) out[i] += base;
-            if (lane == 0) counts[g] = r;
-        }
-        __syncthreads();
-        if (wid == 0) {
-            // compact the survivors in group order (ascending index) in place
-            int off = 0;
-            for (int g = 0; g < ngroups; ++g) {
-                const int r = counts[g];
-                for (int i = lane; i < r; i += kWave) cand[off + i] = cand[g * (K + 1) + i];
-                off += r;
-                __builtin_amdgcn_wave_barrier();
-            }
-            const int r = wave_select_e<16>(keys, cand, off, K, sel);
-            // positions -> indices
-            for (int i = lane; i < r; i += kWave) sel[i] = cand[sel[i]];
             if (lane == 0) tmp[0] = unsigned(r);
         }
         __syncthreads();

@@ -138,8 +138,9 @@ def test_full_budgets_equal_dense(fusion):
 
 
 def test_many_candidate_groups_with_ties():
-    """4,688 stage-1 candidates (five groups of 1,024 in the select) with
-    many equal scores, and a later stage that keeps every candidate."""
+    """4,688 stage-0 candidates (more than the cooperative select holds in
+    registers, so it reads them from LDS in every pass) with many equal
+    scores, and a later stage that keeps every candidate."""
     w = tiny_workload(name="groups", batch=1, num_q_heads=8, num_kv_heads=2, max_context=300000,
                       stages=(Stage(64, 8, 40), Stage(16, 2, 160)), sink=16, window=64, planted=0)
 
@@ -153,12 +154,13 @@ def test_many_candidate_groups_with_ties():
     run_case(w, modify=dup, check_scores=True)
 
 
-@pytest.mark.parametrize("max_context", [65536, 131072 - 40])
+@pytest.mark.parametrize("max_context", [65536, 131072 - 40, 300000 - 8])
 def test_all_scores_equal_in_full_groups(max_context):
     """Every key row identical, so every chunk score of a stage is equal: the
-    lowest starts must win.  65,536 tokens give exactly 1,024 stage-0
-    candidates (one full group of the select); the ragged second size gives
-    two groups, the last one partial."""
+    lowest starts must win.  The sizes give 1,024 stage-0 candidates (four
+    keys per lane of the cooperative select, all slots full), 2,048 with a
+    ragged last chunk (sixteen per lane), and 4,688 (read from LDS in every
+    pass, last block partial)."""
     w = tiny_workload(name="equal", batch=1, num_q_heads=4, num_kv_heads=1, max_context=max_context,
                       stages=(Stage(64, 8, 40), Stage(8, 1, 64)), sink=0, window=0, planted=0)
 
