@@ -24,6 +24,10 @@ roofline = the dominant kernel's algorithmic bytes per launch / its average
          no record exists or the kernel sources changed since it was taken.
 cpu_baseline = the CPU oracle (numpy, one core) on one full step of the same
          workload.
+reuse  = steps that reuse the first r pruning stages' kept sets from an
+         earlier step (sd_decode_step_reuse): us per step for each r, and,
+         over a drifting query sequence, how much of the fully recomputed
+         last-stage kept set such a step still finds.
 """
 from __future__ import annotations
 
@@ -42,7 +46,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-from sparse_attention_kv_int8_amd.inputs import WORKLOADS, make_inputs  # noqa: E402
+from sparse_attention_kv_int8_amd.inputs import WORKLOADS, make_inputs, make_queries  # noqa: E402
 
 METRIC = "sparse decode-attention µs/step + achieved HBM GB/s at 128K and 1M ctx (GQA 32/8)"
 HBM_PEAK_GBS = 8000.0
@@ -167,6 +171,68 @@ class Bench:
         return self.dec.sd_profile_stop()
 
 
+def reuse_study(b, steps: int, seq: int = 8) -> dict:
+    """Pruning stages reused from an earlier step (sd_decode_step_reuse).
+
+    time: us per step when the first r stages are reused, r = 1..S, timed
+    like the main figure (HIP graph replay over the rotating cache copies,
+    kept_idx holding the last full step's kept sets).  recall: over the
+    workload's drifting query sequence (q_t = 0.9 q_(t-1) + 0.44 N(0, 1)),
+    steps t = 1..seq-1 reuse the first r stages of step 0; the share of the
+    last stage's fully recomputed kept chunks that the reusing step also
+    keeps (mean over steps, requests and KV heads), and the largest
+    |output difference| to the fully recomputed step."""
+    torch, lib, h, w = b.torch, b.B.lib, b.dec.handle, b.w
+    S = len(w.stages)
+    res = {"us_per_step": {}, "recall_last_stage": {}, "max_abs_out_diff": {}, "sequence_steps": seq}
+    b.run(1)                                     # kept_idx: a full step's kept sets
+    torch.cuda.synchronize()
+    for r in range(1, S + 1):
+        graphs = []
+        for a in b.args:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                st = lib.sd_decode_step_reuse(h, *a, r, torch.cuda.current_stream().cuda_stream)
+                if st:
+                    b.B.check(st, "sd_decode_step_reuse (capture)")
+            graphs.append(g)
+        for i in range(20):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        res["us_per_step"][str(r)] = round((time.perf_counter() - t0) / steps * 1e6, 3)
+        del graphs
+    # quality over the drifting sequence (outside any timed region)
+    qs = make_queries(w, seq)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    kept0 = torch.empty_like(b.kept)
+    kept_f, kept_r = torch.empty_like(b.kept), torch.empty_like(b.kept)
+    out_f, out_r = torch.empty_like(b.out), torch.empty_like(b.out)
+    b.dec.sd_decode_step(to_dev(qs[0]), b.ks[0], b.k8s[0], b.vs[0], b.lengths, b.out, kept0)
+    off = sum(st.keep for st in w.stages[:-1])
+    for r in range(1, S + 1):
+        rec, diff = [], 0.0
+        for t in range(1, seq):
+            q = to_dev(qs[t])
+            b.dec.sd_decode_step(q, b.ks[0], b.k8s[0], b.vs[0], b.lengths, out_f, kept_f)
+            kept_r.copy_(kept0)
+            b.dec.sd_decode_step_reuse(q, b.ks[0], b.k8s[0], b.vs[0], b.lengths, out_r, kept_r, r)
+            torch.cuda.synchronize()
+            kf, kr = kept_f.cpu().numpy()[..., off:], kept_r.cpu().numpy()[..., off:]
+            for bb in range(w.batch):
+                for j in range(w.num_kv_heads):
+                    f = set(kf[bb, j][kf[bb, j] >= 0].tolist())
+                    if f:
+                        rec.append(len(f & set(kr[bb, j].tolist())) / len(f))
+            diff = max(diff, float((out_f.float() - out_r.float()).abs().max()))
+        res["recall_last_stage"][str(r)] = round(statistics.fmean(rec), 4)
+        res["max_abs_out_diff"][str(r)] = round(diff, 4)
+    return res
+
+
 def oracle_baseline(w, inp, kept_gpu_bytes: float) -> dict:
     """The CPU oracle on one full step of the same inputs (one core)."""
     try:
@@ -231,8 +297,9 @@ def measure(w, steps: int, warmup: int, copies: int) -> tuple:
     dom_us = live[dominant][0] * 1e3 / live[dominant][1]
     kept = b.kept.cpu().numpy()
     ab = algorithmic_bytes(w, kept, b.inp.lengths)
+    reuse = reuse_study(b, steps) if w.steps == 1 else None
     return b, dict(us_per_step=us_per_step, us_eager=us_eager, avg_us=avg_us, dominant=dominant, dominant_us=dom_us,
-                   bytes=ab)
+                   bytes=ab, reuse=reuse)
 
 
 def measure_hostv(w, repeats: int = 3) -> dict:
@@ -394,6 +461,7 @@ def main() -> int:
                           "frac": round(total / (sum_kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                           "note": "all per-step bytes / sum of per-step kernel durations"},
         "quantize_keys_us": round(b.quantize_us, 2),
+        "reuse": r["reuse"],
     }
     inp, kb = b.inp, total
     del b
@@ -409,7 +477,7 @@ def main() -> int:
                              "dominant": r2["dominant"],
                              "dominant_frac": round(r2["bytes"]["per_kernel"][r2["dominant"]] /
                                                     (r2["dominant_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                             "quantize_keys_us": round(b2.quantize_us, 2)}
+                             "quantize_keys_us": round(b2.quantize_us, 2), "reuse": r2["reuse"]}
         del b2
         b_torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -152,6 +152,32 @@ sd_status sd_decode_step(sd_ctx* ctx, const uint16_t* q, const uint16_t* k_bf16,
                          const int8_t* k_int8, const uint16_t* v, const int32_t* lengths,
                          uint16_t* out, int32_t* kept_idx, void* stream);
 
+/* sd_decode_step with the first `reuse_stages` pruning stages reused from an
+ * earlier step: news article on InfiniteHiP ("韩国通过卸载键值缓存节约英伟达GPU
+ * 内存，实现18.95倍解码加速"), section "实现 7.24 倍的端到端解码加速": the modular
+ * design allows fine-grained control over caching the pruning stages, for
+ * faster decoding.  Stages s < reuse_stages are not run: their kept sets are
+ * the ones kept_idx holds (as an earlier step on the same kept_idx left
+ * them), and stage reuse_stages takes its candidates from the children of
+ * stage reuse_stages - 1's kept chunks that start before the current
+ * length.  Later stages, the attended set and the attention run as in
+ * sd_decode_step, with this step's query.  reuse_stages = 0 is
+ * sd_decode_step; reuse_stages = num_stages reuses every stage and runs
+ * only the attention.
+ *  reuse_stages  in [0, num_stages], else SD_ERR_INVALID_ARG.
+ * kept_idx is read as well as written: the entries of reused stages are
+ * left as they are; entries outside [0, length) are ignored.  kept sets not
+ * written by a step of this context (unsorted, repeated, or not multiples
+ * of the chunk) give unspecified results but no out-of-range access.
+ * Chunk scores of reused stages (sd_stage_scores) stay those of the step
+ * that computed them.  A context created with the last stage fused
+ * (environment SD_FUSE_LAST_STAGE=1) returns SD_ERR_UNSUPPORTED for
+ * reuse_stages > 0. */
+sd_status sd_decode_step_reuse(sd_ctx* ctx, const uint16_t* q, const uint16_t* k_bf16,
+                               const int8_t* k_int8, const uint16_t* v, const int32_t* lengths,
+                               uint16_t* out, int32_t* kept_idx, int32_t reuse_stages,
+                               void* stream);
+
 /* The step's query codes, for inspection: q8 device [B][Hq][d] int8 with one
  * absmax scale per query head (same rounding as the keys), and q_group
  * device [B][Hkv][d] int32, the sum of q8 over each KV head's group.  Either

@@ -173,11 +173,24 @@ def children(kept: np.ndarray, parent_chunk: int, chunk: int, length: int) -> np
     return x[x < length]
 
 
-def prune(S_of_rows, length: int, stages: Sequence[StageSpec]) -> List[np.ndarray]:
-    """Runs every stage; returns the kept chunk starts P_1..P_S (ascending)."""
-    kept_all = []
-    cand = np.arange(0, length, stages[0].chunk, dtype=np.int64)
-    for s, st in enumerate(stages):
+def prune(S_of_rows, length: int, stages: Sequence[StageSpec],
+          given: Sequence[np.ndarray] = ()) -> List[np.ndarray]:
+    """Runs the stages; returns the kept chunk starts P_1..P_S (ascending).
+
+    ``given`` holds kept sets of the first len(given) stages, reused from an
+    earlier step ([HiP] same section: the modular design lets the pruning
+    stages' results be cached, for faster decoding): those stages are not
+    run, and the first stage that runs takes the children of the last given
+    set.  Only entries in [0, length) of a given set count."""
+    r = len(given)
+    kept_all = [np.asarray(g, dtype=np.int64) for g in given]
+    kept_all = [g[(g >= 0) & (g < length)] for g in kept_all]
+    if r == 0:
+        cand = np.arange(0, length, stages[0].chunk, dtype=np.int64)
+    elif r < len(stages):
+        cand = children(kept_all[r - 1], stages[r - 1].chunk, stages[r].chunk, length)
+    for s in range(r, len(stages)):
+        st = stages[s]
         sc = chunk_scores(S_of_rows, cand, st.chunk, st.stride, length)
         kept = select_top(cand, sc, st.keep)
         kept_all.append(kept)
@@ -246,11 +259,17 @@ class StepResult:
 
 
 def decode_step(q_bits: np.ndarray, k_bits: np.ndarray, k8: np.ndarray, v_bits: np.ndarray,
-                lengths: Sequence[int], cfg: StepConfig) -> StepResult:
+                lengths: Sequence[int], cfg: StepConfig, reuse: int = 0,
+                kept_prev: Optional[np.ndarray] = None) -> StepResult:
     """One decode step for a batch.
 
     q_bits [B][Hq][d] bf16 bits; k_bits, v_bits [B][Hkv][Lmax][d] bf16 bits;
-    k8 [B][Hkv][Lmax][d] int8 codes (only rows t < L_b are read)."""
+    k8 [B][Hkv][Lmax][d] int8 codes (only rows t < L_b are read).  With
+    reuse > 0 the first ``reuse`` stages are not run: their kept sets are
+    taken from kept_prev [B][Hkv][sum keep] (an earlier step's kept_idx),
+    whose rows for those stages are also returned unchanged."""
+    if reuse:
+        assert kept_prev is not None and 0 < reuse <= len(cfg.stages)
     B, Hq, d = q_bits.shape
     Hkv = k_bits.shape[1]
     G = Hq // Hkv
@@ -267,11 +286,14 @@ def decode_step(q_bits: np.ndarray, k_bits: np.ndarray, k8: np.ndarray, v_bits: 
             Qj = Qs[b, j]
             k8_bj = k8[b, j]
             S_of_rows = lambda t, k8_bj=k8_bj, Qj=Qj: token_scores(Qj, k8_bj[t.reshape(-1)]).reshape(t.shape)
-            kept = prune(S_of_rows, L, cfg.stages)
-            off = 0
-            for st, P in zip(cfg.stages, kept):
-                kept_idx[b, j, off:off + len(P)] = P
-                off += st.keep
+            offs = np.cumsum([0] + [st.keep for st in cfg.stages])
+            given = [kept_prev[b, j, offs[s]:offs[s + 1]] for s in range(reuse)]
+            kept = prune(S_of_rows, L, cfg.stages, given)
+            for s, (st, P) in enumerate(zip(cfg.stages, kept)):
+                if s < reuse:
+                    kept_idx[b, j, offs[s]:offs[s + 1]] = given[s]
+                else:
+                    kept_idx[b, j, offs[s]:offs[s] + len(P)] = P
             T = attended_tokens(kept[-1], cfg.stages[-1].chunk, L, cfg.sink, cfg.window)
             row.append(T)
             kf = bf16_to_f64(k_bits[b, j, T])

@@ -71,6 +71,7 @@ _SIGS = {
     "sd_last_error": (C.c_char_p, []),
     "sd_quantize_keys": (C.c_int, [_p, _p, _p, _p, _p, _p]),
     "sd_decode_step": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "sd_decode_step_reuse": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, C.c_int32, _p]),
     "sd_quantize_query": (C.c_int, [_p, _p, _p, _p, _p]),
     "sd_stage_scores": (C.c_int, [_p, C.c_int32, _p, C.c_int64, _p]),
     "sd_stage_candidates": (C.c_int64, [_p, C.c_int32]),
@@ -176,6 +177,12 @@ class SparseDecoder:
     def sd_decode_step(self, q, k, k_int8, v, lengths, out, kept_idx, stream=None) -> None:
         check(lib.sd_decode_step(self.handle, _ptr(q), _ptr(k), _ptr(k_int8), _ptr(v), _ptr(lengths),
                                  _ptr(out), _ptr(kept_idx), _stream(stream)), "sd_decode_step")
+
+    def sd_decode_step_reuse(self, q, k, k_int8, v, lengths, out, kept_idx, reuse_stages: int,
+                             stream=None) -> None:
+        check(lib.sd_decode_step_reuse(self.handle, _ptr(q), _ptr(k), _ptr(k_int8), _ptr(v), _ptr(lengths),
+                                       _ptr(out), _ptr(kept_idx), int(reuse_stages), _stream(stream)),
+              "sd_decode_step_reuse")
 
     def sd_quantize_query(self, q, q8=None, q_group=None, stream=None) -> None:
         check(lib.sd_quantize_query(self.handle, _ptr(q), _ptr(q8), _ptr(q_group), _stream(stream)),

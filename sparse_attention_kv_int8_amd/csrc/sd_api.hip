@@ -313,11 +313,13 @@ sd_status sd_quantize_query(sd_ctx* c, const uint16_t* q, int8_t* q8, int32_t* q
     return from_hip(sd::launch_quantize_query(c, q, q8, qg, static_cast<hipStream_t>(stream)));
 }
 
-sd_status sd_decode_step(sd_ctx* c, const uint16_t* q, const uint16_t* k, const int8_t* k8, const uint16_t* v,
-                         const int32_t* lengths, uint16_t* out, int32_t* kept, void* stream) {
+sd_status sd_decode_step_reuse(sd_ctx* c, const uint16_t* q, const uint16_t* k, const int8_t* k8, const uint16_t* v,
+                               const int32_t* lengths, uint16_t* out, int32_t* kept, int32_t reuse, void* stream) {
     if (!c || !q || !k || !k8 || !v || !lengths || !out || !kept) return SD_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(k8) || !aligned16(v) || !aligned16(out))
         return SD_ERR_INVALID_ARG;
+    if (reuse < 0 || reuse > c->S) return SD_ERR_INVALID_ARG;
+    if (reuse > 0 && c->fuse) return SD_ERR_UNSUPPORTED;     // the fused plan reads other rows at stage S-2
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint16_t* vk = v;
     if (c->cfg.values_on_host) {
@@ -334,19 +336,30 @@ sd_status sd_decode_step(sd_ctx* c, const uint16_t* q, const uint16_t* k, const 
         vk = c->vhost_dev;
     }
     hipError_t e = hipSuccess;
+    // stages [0, reuse) keep the kept sets that kept_idx holds; the first
+    // stage run reads its parents from there
     const int nprune = c->fuse ? c->S - 1 : c->S;     // a fused last stage has no kernel of its own
-    for (int st = 0; st < nprune && e == hipSuccess; ++st)
-        e = timed(c, SD_PROF_STAGE0 + st, s,
-                  [&](sd::Timing t) { return sd::launch_prune_stage(c, st, q, k8, lengths, kept, s, t); });
+    for (int st = reuse; st < nprune && e == hipSuccess; ++st)
+        e = timed(c, SD_PROF_STAGE0 + st, s, [&](sd::Timing t) {
+            return sd::launch_prune_stage(c, st, st == reuse && st > 0, q, k8, lengths, kept, s, t);
+        });
+    const bool last_given = reuse == c->S;
     if (e == hipSuccess && c->cfg.values_on_host)
-        e = timed(c, SD_PROF_VALUE_CACHE, s,
-                  [&](sd::Timing t) { return sd::launch_value_cache_update(c, lengths, kept, s, t); });
+        e = timed(c, SD_PROF_VALUE_CACHE, s, [&](sd::Timing t) {
+            return sd::launch_value_cache_update(c, last_given, lengths, kept, s, t);
+        });
     if (e == hipSuccess)
-        e = timed(c, SD_PROF_ATTEND, s,
-                  [&](sd::Timing t) { return sd::launch_attend(c, q, k, vk, lengths, kept, out, s, t); });
+        e = timed(c, SD_PROF_ATTEND, s, [&](sd::Timing t) {
+            return sd::launch_attend(c, last_given, q, k, vk, lengths, kept, out, s, t);
+        });
     if (e == hipSuccess)
         e = timed(c, SD_PROF_COMBINE, s, [&](sd::Timing t) { return sd::launch_combine(c, out, s, t); });
     return from_hip(e);
+}
+
+sd_status sd_decode_step(sd_ctx* c, const uint16_t* q, const uint16_t* k, const int8_t* k8, const uint16_t* v,
+                         const int32_t* lengths, uint16_t* out, int32_t* kept, void* stream) {
+    return sd_decode_step_reuse(c, q, k, k8, v, lengths, out, kept, 0, stream);
 }
 
 int64_t sd_stage_candidates(const sd_ctx* c, int32_t stage) {

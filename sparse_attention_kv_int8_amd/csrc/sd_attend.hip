@@ -54,6 +54,7 @@ struct AttendParams {
     int fuse_rq;
     int32_t* kept;            // [B][Hkv][keep_total]
     int keep_total;
+    int32_t* flag;            // set when the last stage is given (no pruning kernel ran)
     int sink, window;
     float* part;              // acc [B*Hkv][nsplit][G][d], then (m, l) [B*Hkv][nsplit][G][2]
     int nsplit;               // splits per (request, KV head)
@@ -252,7 +253,8 @@ __device__ __forceinline__ void decode_blocks(const AttendParams& p, const Src& 
 }
 
 // One instantiation per (group size, values on host, select width of the
-// last stage (unused with host values), select width of the stage before
+// last stage (kGiven: reused, read from kept_idx; unused with host values),
+// select width of the stage before
 // it when the last two stages are fused here (0 = not fused)).
 template <int G, bool HOSTV, int SEL, int SELP>
 __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendParams p) {
@@ -316,7 +318,13 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
         int nk;
         const int* kstarts;
-        if constexpr (SELP != 0) {
+        if constexpr (SEL == kGiven) {
+            // the last stage is reused: its kept set is read from kept_idx
+            if (L == 0 && sp == p.nsplit_a && threadIdx.x == 0) atomicOr(p.flag, 1);
+            int* sel = reinterpret_cast<int*>(dyn + p.last.ncand);
+            nk = given_kept<kAttnThreads>(p.last, kept_bj + p.last.koff, L, sel, tmp);
+            kstarts = sel;
+        } else if constexpr (SELP != 0) {
             const FusedOut fo = kept_two_stages<kAttnThreads, SELP, SEL>(
                 p.P, p.p_first != 0, p.p_scores + int64_t(bj) * p.P.ncand, p.p_first ? nullptr : kept_bj + p.pp_koff_p,
                 p.pre + int64_t(bj) * p.P.ncand * p.fuse_rq, p.fuse_rq, p.last, L, dyn, tmp);
@@ -329,7 +337,7 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
             kstarts = reinterpret_cast<const int*>(dyn + p.last.ncand);
         }
         const int spb = sp - p.nsplit_a, nsb = p.nsplit - p.nsplit_a;
-        kept_n = spb == 0 ? nk : -1;        // the first of these workgroups publishes the kept set
+        kept_n = spb == 0 && SEL != kGiven ? nk : -1;   // the first of these workgroups publishes the kept set
         const int bpc = p.last.chunk >> 3;
         const int nb = nk * bpc;
         const int per = (nb + nsb - 1) / nsb;
@@ -456,16 +464,18 @@ __global__ __launch_bounds__(kAttnThreads) void sd_combine_kernel(const float* _
 }
 
 template <int G>
-static void launch_g(const AttendParams& p, dim3 grid, bool hostv, bool fuse, size_t lds, hipStream_t s, Timing t) {
+static void launch_g(const AttendParams& p, dim3 grid, bool hostv, bool fuse, bool given, size_t lds, hipStream_t s,
+                     Timing t) {
     const dim3 block(kAttnThreads);
     if (hostv) launch(sd_flash_decode_kernel<G, true, 8, 0>, grid, block, 0, s, t, p);
+    else if (given) launch(sd_flash_decode_kernel<G, false, kGiven, 0>, grid, block, lds, s, t, p);
     else if (fuse && select_width(p.P.ncand) == 8) launch(sd_flash_decode_kernel<G, false, 8, 8>, grid, block, lds, s, t, p);
     else if (fuse) launch(sd_flash_decode_kernel<G, false, 8, 16>, grid, block, lds, s, t, p);
     else if (select_width(p.last.ncand) == 8) launch(sd_flash_decode_kernel<G, false, 8, 0>, grid, block, lds, s, t, p);
     else launch(sd_flash_decode_kernel<G, false, 16, 0>, grid, block, lds, s, t, p);
 }
 
-hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+hipError_t launch_attend(sd_ctx* c, bool given, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const int32_t* lengths, int32_t* kept, uint16_t* out, hipStream_t s, Timing t) {
     AttendParams p{};
     p.q = q;
@@ -489,9 +499,10 @@ hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const 
     p.last_scores = c->scores[S - 1];
     p.kept = kept;
     p.keep_total = c->keep_total;
+    p.flag = c->flag;
     p.sink = c->cfg.sink;
     p.window = c->cfg.window;
-    const bool fuse = c->fuse != 0;
+    const bool fuse = c->fuse != 0 && !given;
     if (fuse) {
         p.P = stage_dev(c, S - 2);
         p.p_first = S == 2;
@@ -510,9 +521,9 @@ hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const 
     dim3 grid(c->nsplit, c->cfg.num_kv_heads, c->cfg.batch);
     const bool hostv = c->cfg.values_on_host != 0;
     switch (c->G) {
-        case 1: launch_g<1>(p, grid, hostv, fuse, lds, s, t); break;
-        case 2: launch_g<2>(p, grid, hostv, fuse, lds, s, t); break;
-        default: launch_g<4>(p, grid, hostv, fuse, lds, s, t); break;
+        case 1: launch_g<1>(p, grid, hostv, fuse, given, lds, s, t); break;
+        case 2: launch_g<2>(p, grid, hostv, fuse, given, lds, s, t); break;
+        default: launch_g<4>(p, grid, hostv, fuse, given, lds, s, t); break;
     }
     return hipGetLastError();
 }

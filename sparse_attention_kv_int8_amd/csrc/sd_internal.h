@@ -115,12 +115,15 @@ inline void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, 
 hipError_t launch_quantize_keys(sd_ctx* c, const uint16_t* k, const int32_t* lengths, int8_t* k8,
                                 float* absmax, hipStream_t s, Timing t = {});
 hipError_t launch_quantize_query(sd_ctx* c, const uint16_t* q, int8_t* q8, int32_t* qg, hipStream_t s);
-hipError_t launch_prune_stage(sd_ctx* c, int stage, const uint16_t* q, const int8_t* k8,
+// given: the kept set that the launch would select (stage - 1's for a
+// pruning stage, the last stage's for the decode and value-cache kernels)
+// is read from kept_idx instead, where an earlier step left it.
+hipError_t launch_prune_stage(sd_ctx* c, int stage, bool given, const uint16_t* q, const int8_t* k8,
                               const int32_t* lengths, int32_t* kept, hipStream_t s, Timing t = {});
-hipError_t launch_attend(sd_ctx* c, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+hipError_t launch_attend(sd_ctx* c, bool given, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const int32_t* lengths, int32_t* kept, uint16_t* out, hipStream_t s, Timing t = {});
 hipError_t launch_combine(sd_ctx* c, uint16_t* out, hipStream_t s, Timing t = {});
-hipError_t launch_value_cache_update(sd_ctx* c, const int32_t* lengths, int32_t* kept, hipStream_t s,
+hipError_t launch_value_cache_update(sd_ctx* c, bool given, const int32_t* lengths, int32_t* kept, hipStream_t s,
                                      Timing t = {});
 hipError_t launch_value_cache_reset(sd_ctx* c, hipStream_t s);
 StageDev stage_dev(const sd_ctx* c, int st);

@@ -12,7 +12,10 @@
 //
 // One kernel per stage.  The kernel of stage s > 0 first recomputes, in
 // every workgroup, the kept set of stage s-1 from its scores (sd_select.h);
-// workgroup 0 publishes it in kept_idx.  Then each workgroup scores its
+// workgroup 0 publishes it in kept_idx.  When stage s-1 is reused from an
+// earlier step (the same article, same section: the modular design gives
+// fine-grained control over caching the pruning stages), that kept set is
+// read from kept_idx instead.  Then each workgroup scores its
 // slice of stage s's candidates (the children of that kept set).  The kept
 // set of the last stage is selected by the attention kernel.
 #include "sd_device.h"
@@ -134,7 +137,8 @@ __device__ __forceinline__ void split_query(const int* Qlds, int sl, u32x4& qh, 
 }
 
 // One instantiation per (rows per candidate / 8, select width of the
-// previous stage (0 = stage 0), fused next stage): each launch carries only
+// previous stage (0 = stage 0, kGiven = the previous stage reused), fused
+// next stage): each launch carries only
 // its own path, which keeps code size and scalar-register pressure down.
 template <int NS8, int SEL, bool FUSE>
 __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PruneParams p) {
@@ -151,12 +155,20 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
     int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
 
     const int32_t* parents = nullptr;
-    if constexpr (SEL == 0) {
+    if constexpr (SEL == 0 || SEL == kGiven) {
+        // the first stage this step runs: flags a bad length and forms the
+        // group query codes, which the later stages read
         if (bad && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(p.flag, 1);
         group_query_codes(p.q + int64_t(b) * p.Hq * kHeadDim, j, p.G, Qlds, nullptr);
         if (blockIdx.x == 0 && threadIdx.x < kHeadDim)
             p.qgroup[int64_t(bj) * kHeadDim + threadIdx.x] = Qlds[threadIdx.x];
-    } else {
+    }
+    if constexpr (SEL == kGiven) {
+        // the previous stage is reused: its kept set is read from kept_idx
+        int* sel = reinterpret_cast<int*>(dyn + p.prev.ncand);
+        given_kept<kPruneThreads>(p.prev, kept_bj + p.prev.koff, L, sel, tmp);
+        parents = sel;
+    } else if constexpr (SEL != 0) {
         // the group query load is issued together with the previous scores' loads
         const int qval = threadIdx.x < kHeadDim ? p.qgroup[int64_t(bj) * kHeadDim + threadIdx.x] : 0;
         // kept set of the previous stage (its own parents are in kept_idx already)
@@ -184,7 +196,7 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
     const int first = wg_first + wave * p.cpw;
     score_slice<NS8, FUSE>(p, cstart + wave * p.cpw, L, k8_bj, qh, ql, first, scores_bj,
                            FUSE ? p.pre + int64_t(bj) * p.cur.ncand * p.fuse_rq : nullptr);
-    if constexpr (SEL != 0) {
+    if constexpr (SEL != 0 && SEL != kGiven) {
         // workgroup 0 publishes the previous stage's kept set (ascending,
         // -1 padded); stored last, so no barrier waits on these stores
         if (blockIdx.x == 0)
@@ -205,8 +217,8 @@ StageDev stage_dev(const sd_ctx* c, int st) {
     return d;
 }
 
-hipError_t launch_prune_stage(sd_ctx* c, int st, const uint16_t* q, const int8_t* k8, const int32_t* lengths,
-                              int32_t* kept, hipStream_t s, Timing t) {
+hipError_t launch_prune_stage(sd_ctx* c, int st, bool given, const uint16_t* q, const int8_t* k8,
+                              const int32_t* lengths, int32_t* kept, hipStream_t s, Timing t) {
     PruneParams p{};
     p.q = q;
     p.k8 = k8;
@@ -238,21 +250,27 @@ hipError_t launch_prune_stage(sd_ctx* c, int st, const uint16_t* q, const int8_t
     }
     dim3 grid(c->st[st].nwg, c->cfg.num_kv_heads, c->cfg.batch);
     const int ns8 = (p.nrows + 7) >> 3;
-    const int sel = st == 0 ? 0 : select_width(p.prev.ncand);
+    const int sel = st == 0 ? 0 : given ? kGiven : select_width(p.prev.ncand);
 #define SD_PRUNE(N, S, F) launch(sd_prune_stage_kernel<N, S, F>, grid, dim3(kPruneThreads), lds, s, t, p)
+#define SD_PRUNE_UNFUSED(S)                                     \
+    if (ns8 == 1) SD_PRUNE(1, S, false);                        \
+    else if (ns8 == 2) SD_PRUNE(2, S, false);                   \
+    else if (ns8 <= 4) SD_PRUNE(4, S, false);                   \
+    else SD_PRUNE(8, S, false)
 #define SD_PRUNE_NS(S)                                          \
     if (fuse) {                                                 \
         if (ns8 <= 2) SD_PRUNE(2, S, true);                     \
         else if (ns8 <= 4) SD_PRUNE(4, S, true);                \
         else SD_PRUNE(8, S, true);                              \
-    } else if (ns8 == 1) SD_PRUNE(1, S, false);                 \
-    else if (ns8 == 2) SD_PRUNE(2, S, false);                   \
-    else if (ns8 <= 4) SD_PRUNE(4, S, false);                   \
-    else SD_PRUNE(8, S, false)
+    } else {                                                    \
+        SD_PRUNE_UNFUSED(S);                                    \
+    }
     if (sel == 0) { SD_PRUNE_NS(0); }
+    else if (sel == kGiven) { SD_PRUNE_UNFUSED(kGiven); }   // reuse is not combined with fusion
     else if (sel == 8) { SD_PRUNE_NS(8); }
     else { SD_PRUNE_NS(16); }
 #undef SD_PRUNE_NS
+#undef SD_PRUNE_UNFUSED
 #undef SD_PRUNE
     return hipGetLastError();
 }

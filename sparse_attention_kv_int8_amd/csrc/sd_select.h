@@ -668,6 +668,33 @@ __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, int* can
     return kept;
 }
 
+// Select-width code of a kernel whose kept set is not selected but read
+// from kept_idx, where an earlier step left it (a reused pruning stage).
+constexpr int kGiven = 1;
+
+// Kept set of stage `st` as kept_idx holds it (ascending token starts,
+// -1 padded, as a step wrote it): the entries in [0, L), in their order, to
+// sel[0..nk), then -1 up to st.keep.  Returns nk; ends with a barrier.
+template <int NT>
+__device__ int given_kept(const StageDev& st, const int32_t* kept_st, int64_t L, int* sel, unsigned* tmp) {
+    const int per = (st.keep + NT - 1) / NT;
+    const int i0 = min(st.keep, int(threadIdx.x) * per), i1 = min(st.keep, i0 + per);
+    unsigned c = 0;
+    for (int i = i0; i < i1; ++i) {
+        const int32_t x = kept_st[i];
+        c += x >= 0 && x < L;
+    }
+    unsigned total;
+    unsigned pos = block_excl_scan<NT>(c, tmp, &total);
+    for (int i = i0; i < i1; ++i) {
+        const int32_t x = kept_st[i];
+        if (x >= 0 && x < L) sel[pos++] = x;
+    }
+    for (int i = int(total) + threadIdx.x; i < st.keep; i += NT) sel[i] = -1;
+    __syncthreads();
+    return int(total);
+}
+
 // LDS words kept_of_stage uses: keys [ncand], sel [keep + 1], select
 // scratch, and (after the first stage) the parents [ncand / ratio].
 __host__ __device__ inline int kept_lds_words(const StageDev& st, bool first_stage) {

@@ -48,6 +48,7 @@ struct VcStepParams {
     const int32_t* last_scores;   // [B][Hkv][last.ncand]
     int32_t* kept;                // [B][Hkv][keep_total]
     int keep_total;
+    int32_t* flag;                // bad-length flag (set here when the last stage is given)
     int sink, window;
     const int32_t* lengths;
     int64_t Lmax;
@@ -58,6 +59,8 @@ struct VcStepParams {
     int32_t step;
 };
 
+// SEL: select width of the last stage, or kGiven when it is reused (read
+// from kept_idx).
 template <int SEL>
 __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParams p) {
     extern __shared__ uint32_t dyn[];    // the last stage's select (kept_lds_words)
@@ -74,9 +77,17 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
     // last stage's kept set and the attended blocks
     int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
     int* sel = reinterpret_cast<int*>(dyn + p.last.ncand);
-    const int nk = kept_of_stage<kLruThreads, SEL>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
-                                              p.first_stage ? nullptr : kept_bj + p.pp_koff, L, dyn, tmp);
-    for (int i = tid; i < p.last.keep; i += kLruThreads) kept_bj[p.last.koff + i] = i < nk ? sel[i] : -1;
+    int nk;
+    if constexpr (SEL == kGiven) {
+        // the last stage is reused: its kept set is read from kept_idx (and
+        // no pruning kernel ran this step to flag a bad length)
+        if (L == 0 && tid == 0) atomicOr(p.flag, 1);
+        nk = given_kept<kLruThreads>(p.last, kept_bj + p.last.koff, L, sel, tmp);
+    } else {
+        nk = kept_of_stage<kLruThreads, SEL>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
+                                             p.first_stage ? nullptr : kept_bj + p.pp_koff, L, dyn, tmp);
+        for (int i = tid; i < p.last.keep; i += kLruThreads) kept_bj[p.last.koff + i] = i < nk ? sel[i] : -1;
+    }
     uint32_t* blocks_bj = p.blocks + int64_t(bj) * max_blocks;
     const int nb = build_attended<kLruThreads>(sel, nk, p.last.chunk, L, p.sink, p.window, blocks_bj, tmp);
     if (tid == 0) p.nblocks[bj] = nb;
@@ -170,7 +181,8 @@ hipError_t launch_value_cache_reset(sd_ctx* c, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_value_cache_update(sd_ctx* c, const int32_t* lengths, int32_t* kept, hipStream_t s, Timing t) {
+hipError_t launch_value_cache_update(sd_ctx* c, bool given, const int32_t* lengths, int32_t* kept, hipStream_t s,
+                                     Timing t) {
     VcStepParams p{};
     p.vc = c->vc;
     const int S = c->S;
@@ -180,6 +192,7 @@ hipError_t launch_value_cache_update(sd_ctx* c, const int32_t* lengths, int32_t*
     p.last_scores = c->scores[S - 1];
     p.kept = kept;
     p.keep_total = c->keep_total;
+    p.flag = c->flag;
     p.sink = c->cfg.sink;
     p.window = c->cfg.window;
     p.lengths = lengths;
@@ -191,7 +204,8 @@ hipError_t launch_value_cache_update(sd_ctx* c, const int32_t* lengths, int32_t*
     p.step = int32_t(c->vc_step);
     const size_t lds = size_t(kept_lds_words(p.last, p.first_stage != 0)) * 4;
     dim3 grid(c->cfg.num_kv_heads, c->cfg.batch);
-    if (select_width(p.last.ncand) == 8) launch(sd_vcache_step_kernel<8>, grid, dim3(kLruThreads), lds, s, t, p);
+    if (given) launch(sd_vcache_step_kernel<kGiven>, grid, dim3(kLruThreads), lds, s, t, p);
+    else if (select_width(p.last.ncand) == 8) launch(sd_vcache_step_kernel<8>, grid, dim3(kLruThreads), lds, s, t, p);
     else launch(sd_vcache_step_kernel<16>, grid, dim3(kLruThreads), lds, s, t, p);
     ++c->vc_step;
     return hipGetLastError();

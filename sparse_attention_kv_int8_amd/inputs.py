@@ -190,6 +190,32 @@ def _fill_blocks(dst: np.ndarray, ss: np.random.SeedSequence, L: int,
         dst[L:] = PAD_BF16
 
 
+def _queries(w: Workload, streams, steps: int) -> np.ndarray:
+    """[B][Hq][d] bf16 bits for one step; for more, [steps][B][Hq][d] with
+    q_0 ~ N(0, 1) and q_t = 0.9 q_{t-1} + 0.44 N(0, 1) (fp32, then bf16)."""
+    B, Hq, d = w.batch, w.num_q_heads, w.head_dim
+    q = np.empty((steps, B, Hq, d) if steps > 1 else (B, Hq, d), np.uint16)
+    for b, st in enumerate(streams):
+        rq = np.random.Generator(np.random.PCG64(st["q"]))
+        if steps > 1:
+            cur = rq.standard_normal((Hq, d), dtype=np.float32)
+            q[0, b] = f32_to_bf16_bits(cur)
+            for s in range(1, steps):
+                cur = np.float32(0.9) * cur + np.float32(0.44) * rq.standard_normal((Hq, d), dtype=np.float32)
+                q[s, b] = f32_to_bf16_bits(cur)
+        else:
+            q[b] = f32_to_bf16_bits(rq.standard_normal((Hq, d), dtype=np.float32))
+    return q
+
+
+def make_queries(w: Workload, steps: int, seed: Optional[int] = None) -> np.ndarray:
+    """The drifting query sequence [steps][B][Hq][d] that make_inputs draws
+    for a workload of `steps` steps (its first step is the query of the
+    one-step workload), without generating the cache."""
+    seed = w.seed if seed is None else seed
+    return _queries(w, _request_streams(w, seed), max(2, steps))[:steps]
+
+
 def make_inputs(w: Workload, seed: Optional[int] = None,
                 k_out: Optional[np.ndarray] = None,
                 v_out: Optional[np.ndarray] = None,
@@ -213,22 +239,9 @@ def make_inputs(w: Workload, seed: Optional[int] = None,
     v = np.empty(shape, np.uint16) if v_out is None else v_out
     assert k.shape == shape and v.shape == shape and k.dtype == np.uint16 and v.dtype == np.uint16
 
-    # queries
-    if w.steps > 1:
-        q = np.empty((w.steps, B, Hq, d), np.uint16)
-    else:
-        q = np.empty((B, Hq, d), np.uint16)
+    q = _queries(w, streams, w.steps)
     scales = np.ones((B, Hkv, d), np.float32) if w.channel_scale else None
     for b, st in enumerate(streams):
-        rq = np.random.Generator(np.random.PCG64(st["q"]))
-        if w.steps > 1:
-            cur = rq.standard_normal((Hq, d), dtype=np.float32)
-            q[0, b] = f32_to_bf16_bits(cur)
-            for s in range(1, w.steps):
-                cur = np.float32(0.9) * cur + np.float32(0.44) * rq.standard_normal((Hq, d), dtype=np.float32)
-                q[s, b] = f32_to_bf16_bits(cur)
-        else:
-            q[b] = f32_to_bf16_bits(rq.standard_normal((Hq, d), dtype=np.float32))
         if scales is not None:
             rs = np.random.Generator(np.random.PCG64(st["scale"]))
             scales[b] = np.exp(rs.uniform(np.log(0.25), np.log(4.0), size=(Hkv, d))).astype(np.float32)

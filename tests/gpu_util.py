@@ -76,6 +76,19 @@ class GpuRun:
         self.torch.cuda.synchronize()
         return bf16_dev_to_bits(self.out), self.kept.cpu().numpy()
 
+    def set_lengths(self, lengths):
+        self.lengths.copy_(self.torch.as_tensor(np.asarray(lengths, np.int32)))
+
+    def step_reuse(self, q_bits: np.ndarray, reuse: int, kept_prev: np.ndarray = None):
+        """sd_decode_step_reuse; kept_idx holds kept_prev (if given) on entry."""
+        if kept_prev is not None:
+            self.kept.copy_(self.torch.from_numpy(np.ascontiguousarray(kept_prev, np.int32)))
+        q = to_dev_bf16(q_bits)
+        self.dec.sd_decode_step_reuse(q, self.k, self.k8, self.v, self.lengths, self.out, self.kept, reuse,
+                                      stream=self.stream)
+        self.torch.cuda.synchronize()
+        return bf16_dev_to_bits(self.out), self.kept.cpu().numpy()
+
     def query_codes(self, q_bits: np.ndarray):
         torch = self.torch
         w = self.w

@@ -17,7 +17,9 @@ from tests.gpu_util import GpuRun, compare_step, oracle_config, oracle_keys
 pytestmark = pytest.mark.gpu
 
 
-def run_sequence(w, check_every=1):
+def run_sequence(w, check_every=1, reuse_at=None):
+    """reuse_at(t): how many pruning stages step t reuses from step t - 1
+    (default none)."""
     print(f"host-value case {w.name} L={w.max_context} cache={w.value_cache_tokens} steps={w.steps}", flush=True)
     inp = make_inputs(w)
     g = GpuRun(inp)
@@ -30,10 +32,16 @@ def run_sequence(w, check_every=1):
     lrus = [[O.LRU(cap) for _ in range(w.num_kv_heads)] for _ in range(w.batch)]
     cfg = oracle_config(w)
     tot_h = tot_m = 0
+    ref = None
     for t in range(w.steps):
         q = inp.q[t]
-        out, kept = g.step(q)
-        ref = O.decode_step(q, inp.k, k8_ref, inp.v, inp.lengths, cfg)
+        r = reuse_at(t) if reuse_at and t > 0 else 0
+        if r:
+            out, kept = g.step_reuse(q, r)
+            ref = O.decode_step(q, inp.k, k8_ref, inp.v, inp.lengths, cfg, reuse=r, kept_prev=ref.kept_idx)
+        else:
+            out, kept = g.step(q)
+            ref = O.decode_step(q, inp.k, k8_ref, inp.v, inp.lengths, cfg)
         hits = misses = 0
         for b in range(w.batch):
             for j in range(w.num_kv_heads):
@@ -46,7 +54,7 @@ def run_sequence(w, check_every=1):
         tot_m += misses
         if t % check_every == 0 or t == w.steps - 1:
             compare_step(inp, q, k8_ref, out, kept, ref=ref)
-        print(f"  step {t}: hits {hits} misses {misses}", flush=True)
+        print(f"  step {t} (reuse {r}): hits {hits} misses {misses}", flush=True)
     st = g.dec.sd_get_stats()
     assert (st.steps, st.hits, st.misses) == (w.steps, tot_h, tot_m)
     assert st.h2d_bytes == tot_m * 8 * 128 * 2
@@ -61,6 +69,14 @@ def test_hostv_small_with_evictions():
     h, m = run_sequence(w)
     assert m > 2048 * 8        # more misses than slots: evictions took place
     assert h > 0
+
+
+def test_hostv_with_reused_stages():
+    """Host values with pruning stages reused between refreshes: every
+    fourth step runs all stages, the others reuse one, two or all three."""
+    w = WORKLOADS["ctx_3m_hostv"].replace(name="hostv_reuse", max_context=65536, value_cache_tokens=16384,
+                                          planted=32, steps=12)
+    run_sequence(w, reuse_at=lambda t: t % 4)
 
 
 def test_hostv_reset_starts_cold():

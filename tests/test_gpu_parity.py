@@ -33,14 +33,17 @@ def _check_keys(g, inp, k8_ref, a_ref):
     assert np.array_equal(g.absmax.cpu().numpy(), a_ref)
 
 
-def check_stage_scores(g, inp, ref, k8_ref):
+def check_stage_scores(g, inp, ref, k8_ref, first=0):
     """Every stage's candidate scores equal the oracle's: stage 0 scores
     every chunk, stage s > 0 the children of the oracle's stage s - 1 kept
     starts (candidate i = child i % ratio of kept chunk i // ratio); a
-    missing candidate reads INT32_MIN."""
+    missing candidate reads INT32_MIN.  Stages before `first` (reused, not
+    run) are skipped."""
     w = inp.workload
     koff = np.concatenate([[0], np.cumsum([st.keep for st in w.stages])])
     for s, st in enumerate(w.stages):
+        if s < first:
+            continue
         sc = g.stage_scores(s)
         n = sc.shape[2]
         for b in range(w.batch):
@@ -239,6 +242,84 @@ def test_non_default_stream():
         out, kept = g.step(inp.q)
     k8_ref, _ = oracle_keys(inp)
     compare_step(inp, inp.q, k8_ref, out, kept)
+
+
+# ------------------------------------------------- reused pruning stages ---
+def reuse_sequence(w, L1, L2, reuses, check_scores=True):
+    """Step 0 at lengths L1 runs every stage; then, at lengths L2 with the
+    next (drifting) query, steps that reuse the first r stages' kept sets
+    of step 0, for each r in `reuses`: kept sets bit-exact, outputs within
+    tolerance and the scores of the stages that ran equal to the oracle
+    given the same reused sets."""
+    print(f"reuse case {w.name} B={w.batch} L1={L1} L2={L2} reuses={reuses}", flush=True)
+    inp = make_inputs(w, lengths=L2)
+    g = GpuRun(inp)
+    g.quantize()
+    k8_ref, _ = oracle_keys(inp)
+    cfg = oracle_config(w)
+    g.set_lengths(L1)
+    out0, kept0 = g.step(inp.q[0])
+    ref0 = O.decode_step(inp.q[0], inp.k, k8_ref, inp.v, L1, cfg)
+    assert np.array_equal(kept0, ref0.kept_idx)
+    g.set_lengths(L2)
+    for r in reuses:
+        out, kept = g.step_reuse(inp.q[1], r, kept_prev=kept0)
+        ref = O.decode_step(inp.q[1], inp.k, k8_ref, inp.v, L2, cfg, reuse=r, kept_prev=ref0.kept_idx)
+        bad = np.argwhere(kept != ref.kept_idx)
+        assert bad.size == 0, f"reuse {r}: kept_idx differs at {bad[:5].tolist()}"
+        err = np.abs(O.bf16_to_f64(out) - ref.out).max()
+        assert err <= 8e-3, f"reuse {r}: max |err| = {err}"
+        if check_scores:
+            check_stage_scores(g, inp, ref, k8_ref, first=r)
+        assert g.dec.sd_check() == 0
+        print(f"  reuse {r} ok: max|err|={err:.2e}", flush=True)
+    return g, inp
+
+
+def test_reused_stages_small():
+    """Two ragged requests that grew since the reused step (new chunks and a
+    longer window), every reuse level, on a shape with padded kept sets."""
+    w = tiny_workload(name="reuse", batch=2, num_q_heads=8, num_kv_heads=2, max_context=20000, steps=2,
+                      stages=(Stage(256, 8, 12), Stage(32, 2, 40), Stage(8, 1, 100)), sink=13, window=300)
+    reuse_sequence(w, L1=[19000, 2900], L2=[20000, 3011], reuses=[0, 1, 2, 3])
+
+
+def test_reused_stages_llama8b_128k():
+    """The benchmark's 128K shape (launch configuration included), one
+    decode step later (length + 1, next drifting query)."""
+    w = WORKLOADS["llama8b_128k"].replace(steps=2)
+    reuse_sequence(w, L1=[131071], L2=[131072], reuses=[1, 2, 3], check_scores=False)
+
+
+def test_reuse_all_stages_with_bad_length_flags_it():
+    w = tiny_workload(name="reuse_bad", batch=2, max_context=8192, steps=2)
+    inp = make_inputs(w, lengths=[8192, 5000])
+    g = GpuRun(inp)
+    g.quantize()
+    _, kept0 = g.step(inp.q[0])
+    g.lengths[0] = 0
+    out, kept = g.step_reuse(inp.q[1], len(w.stages), kept_prev=kept0)
+    assert g.dec.sd_check() != 0
+    assert np.array_equal(kept, kept0)           # reused rows are left as they are
+    assert np.all(out[0] == 0)
+
+
+def test_reuse_argument_errors(fusion):
+    from sparse_attention_kv_int8_amd.binding import SDError, SD_ERR_INVALID_ARG, SD_ERR_UNSUPPORTED
+    w = tiny_workload(name="reuse_args", max_context=4096, steps=2)
+    inp = make_inputs(w)
+    g = GpuRun(inp)
+    g.quantize()
+    for bad in (-1, len(w.stages) + 1):
+        with pytest.raises(SDError) as e:
+            g.step_reuse(inp.q[0], bad)
+        assert e.value.status == SD_ERR_INVALID_ARG
+    if fusion == "fused":
+        with pytest.raises(SDError) as e:
+            g.step_reuse(inp.q[0], 1)
+        assert e.value.status == SD_ERR_UNSUPPORTED
+    else:
+        g.step_reuse(inp.q[0], 0)
 
 
 # ------------------------------------------------------------ full size ---

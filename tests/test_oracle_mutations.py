@@ -30,6 +30,9 @@ MUTATIONS = {
     "keep_one_more": ("return np.sort(starts[order[:keep]])", "return np.sort(starts[order[:keep + 1]])"),
     "sum_not_max": ("return S.max(axis=1)", "return np.where(S == np.iinfo(np.int64).min, 0, S).sum(axis=1)"),
     "lru_evicts_newest": ("if self.last.get(blk) == last:", "if self.last.get(blk) == last and False:"),
+    "reuse_ignores_given_parents": ("cand = children(kept_all[r - 1], stages[r - 1].chunk, stages[r].chunk, length)",
+                                    "cand = np.arange(0, length, stages[r].chunk, dtype=np.int64)"),
+    "reuse_keeps_padding": ("kept_all = [g[(g >= 0) & (g < length)] for g in kept_all]", "kept_all = list(kept_all)"),
 }
 
 

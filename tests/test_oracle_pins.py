@@ -203,6 +203,77 @@ def test_full_budgets_cover_everything():
     assert np.array_equal(T, np.arange(L))
 
 
+# ------------------------------------------------- reused pruning stages ---
+def _brute_stages_after(S, L, stages, r, given_last):
+    """Stages r.. written as plain loops over every chunk of stage r's length
+    whose enclosing stage r-1 chunk start is a given kept start (no use of
+    the oracle's children / chunk_scores / select_top)."""
+    parents = {int(x) for x in given_last if 0 <= x < L}
+    out = []
+    for s in range(r, len(stages)):
+        c, stride, K = stages[s]
+        pc = stages[s - 1][0]
+        cands = [x for x in range(0, L, c) if (x // pc) * pc in parents]
+        scored = []
+        for x in cands:
+            samples = [S[t] for t in range(x, min(x + c, L), stride)]
+            scored.append((-max(samples), x))
+        kept = sorted(x for _, x in sorted(scored)[:K])
+        out.append(kept)
+        parents = set(kept)
+    return out
+
+
+@pytest.mark.parametrize("r", [1, 2])
+def test_reused_stages_then_brute_force(r):
+    """Stages before r given (from a shorter context, with -1 padding and an
+    entry past the length); the stages that run match plain loops over
+    every chunk under a given parent."""
+    rng = np.random.default_rng(40 + r)
+    L = 3000
+    S = rng.integers(-30, 30, size=L)                 # small range: many ties
+    stages = [(256, 8, 6), (32, 2, 12), (8, 1, 20)]
+    specs = [O.StageSpec(*x) for x in stages]
+    first = O.prune(_S_from_list(S[:2100]), 2100, specs)      # an earlier, shorter step
+    given = [np.asarray(k) for k in first[:r]]
+    c = stages[r - 1][0]
+    # one kept entry dropped, one start past L and two -1 pads added
+    given[r - 1] = np.concatenate([given[r - 1][:-1], [(L // c + 1) * c], [-1, -1]])
+    kept = O.prune(_S_from_list(S), L, specs, given)
+    for s in range(r):
+        assert sorted(kept[s].tolist()) == sorted(int(x) for x in given[s] if 0 <= x < L)
+    want = _brute_stages_after(S, L, stages, r, given[r - 1])
+    assert [list(map(int, k)) for k in kept[r:]] == want
+
+
+def test_all_stages_reused_attend_the_given_chunks():
+    """Every stage reused: the attended set is the given last-stage chunks
+    (cut at L) plus sink and window, whatever the scores; entries < 0 or
+    >= L contribute nothing."""
+    L = 1000
+    stages = [O.StageSpec(64, 8, 3), O.StageSpec(16, 2, 4), O.StageSpec(8, 1, 5)]
+    given = [np.array([0, 128, 960]), np.array([128, 144, 960, 976]), np.array([136, 968, 992, 1000, -1])]
+    S = np.zeros(L, np.int64)
+    kept = O.prune(_S_from_list(S), L, stages, given)
+    T = O.attended_tokens(kept[-1], 8, L, 4, 3)
+    want = set(range(136, 144)) | set(range(968, 976)) | set(range(992, 1000)) | set(range(4)) | set(range(997, 1000))
+    assert T.tolist() == sorted(want)
+
+
+@pytest.mark.parametrize("reuse", [1, 2, 3])
+def test_reusing_a_steps_own_kept_sets_changes_nothing(reuse):
+    """Kept sets that the same query and length produce, given back as
+    reused stages, reproduce the step exactly (the kept rows included)."""
+    L = 2500
+    q, k, v = _tiny_inputs(L, Hkv=2, G=2, seed=33)
+    stages = [(256, 8, 5), (32, 2, 9), (8, 1, 14)]
+    res, k8 = _run_oracle(q, k, v, L, stages, 16, 100)
+    cfg = O.StepConfig(tuple(O.StageSpec(*s) for s in stages), 16, 100, 1 / np.sqrt(128))
+    again = O.decode_step(q[None], k[None], k8[None], v[None], [L], cfg, reuse=reuse, kept_prev=res.kept_idx)
+    assert np.array_equal(again.kept_idx, res.kept_idx)
+    assert np.array_equal(again.out, res.out)
+
+
 # ---------------------------------------------------------------- O10 -----
 def test_attended_set_bounds():
     rng = np.random.default_rng(9)
