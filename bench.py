@@ -180,8 +180,10 @@ def reuse_study(b, steps: int, seq: int = 8) -> dict:
     workload's drifting query sequence (q_t = 0.9 q_(t-1) + 0.44 N(0, 1)),
     steps t = 1..seq-1 reuse the first r stages of step 0; the share of the
     last stage's fully recomputed kept chunks that the reusing step also
-    keeps (mean over steps, requests and KV heads), and the largest
-    |output difference| to the fully recomputed step."""
+    keeps (mean over steps, requests and KV heads; also per step), the
+    largest |output difference| to the fully recomputed step, and the share
+    of the planted heavy tokens (the stand-in for a needle the query looks
+    for) that the attended set holds, for reused and full steps."""
     torch, lib, h, w = b.torch, b.B.lib, b.dec.handle, b.w
     S = len(w.stages)
     res = {"us_per_step": {}, "recall_last_stage": {}, "max_abs_out_diff": {}, "sequence_steps": seq}
@@ -213,8 +215,23 @@ def reuse_study(b, steps: int, seq: int = 8) -> dict:
     out_f, out_r = torch.empty_like(b.out), torch.empty_like(b.out)
     b.dec.sd_decode_step(to_dev(qs[0]), b.ks[0], b.k8s[0], b.vs[0], b.lengths, b.out, kept0)
     off = sum(st.keep for st in w.stages[:-1])
+    c_last = w.stages[-1].chunk
+    lengths = b.inp.lengths
+
+    def planted_hit(kept_last, bb, j):
+        """planted heavy tokens of (bb, j) inside the attended set"""
+        L = int(lengths[bb])
+        pos = np.asarray(b.inp.planted[bb][j])
+        ks = kept_last[kept_last >= 0]
+        inside = ((pos[:, None] >= ks[None, :]) & (pos[:, None] < ks[None, :] + c_last)).any(axis=1)
+        inside |= (pos < w.sink) | (pos >= L - w.window)
+        return int(inside.sum()), len(pos)
+
+    res["recall_by_step"] = {}
+    res["planted_recall"] = {}
+    full_hit = full_n = 0
     for r in range(1, S + 1):
-        rec, diff = [], 0.0
+        rec_t, diff, hit, n = [], 0.0, 0, 0
         for t in range(1, seq):
             q = to_dev(qs[t])
             b.dec.sd_decode_step(q, b.ks[0], b.k8s[0], b.vs[0], b.lengths, out_f, kept_f)
@@ -222,14 +239,24 @@ def reuse_study(b, steps: int, seq: int = 8) -> dict:
             b.dec.sd_decode_step_reuse(q, b.ks[0], b.k8s[0], b.vs[0], b.lengths, out_r, kept_r, r)
             torch.cuda.synchronize()
             kf, kr = kept_f.cpu().numpy()[..., off:], kept_r.cpu().numpy()[..., off:]
+            rec = []
             for bb in range(w.batch):
                 for j in range(w.num_kv_heads):
                     f = set(kf[bb, j][kf[bb, j] >= 0].tolist())
                     if f:
                         rec.append(len(f & set(kr[bb, j].tolist())) / len(f))
+                    h1, n1 = planted_hit(kr[bb, j], bb, j)
+                    hit, n = hit + h1, n + n1
+                    if r == 1:
+                        h0, n0 = planted_hit(kf[bb, j], bb, j)
+                        full_hit, full_n = full_hit + h0, full_n + n0
+            rec_t.append(round(statistics.fmean(rec), 4))
             diff = max(diff, float((out_f.float() - out_r.float()).abs().max()))
-        res["recall_last_stage"][str(r)] = round(statistics.fmean(rec), 4)
+        res["recall_last_stage"][str(r)] = round(statistics.fmean(rec_t), 4)
+        res["recall_by_step"][str(r)] = rec_t
         res["max_abs_out_diff"][str(r)] = round(diff, 4)
+        res["planted_recall"][str(r)] = round(hit / max(1, n), 4)
+    res["planted_recall"]["full"] = round(full_hit / max(1, full_n), 4)
     return res
 
 
@@ -266,7 +293,7 @@ def oracle_baseline(w, inp, kept_gpu_bytes: float) -> dict:
             "s_per_step": round(ts, 4), "quantize_s": round(tq, 3)}
 
 
-def measure(w, steps: int, warmup: int, copies: int) -> tuple:
+def measure(w, steps: int, warmup: int, copies: int, reuse: bool = True) -> tuple:
     b = Bench(w, copies)
     torch = b.torch
     b.run(warmup)
@@ -297,7 +324,7 @@ def measure(w, steps: int, warmup: int, copies: int) -> tuple:
     dom_us = live[dominant][0] * 1e3 / live[dominant][1]
     kept = b.kept.cpu().numpy()
     ab = algorithmic_bytes(w, kept, b.inp.lengths)
-    reuse = reuse_study(b, steps) if w.steps == 1 else None
+    reuse = reuse_study(b, steps) if reuse and w.steps == 1 else None
     return b, dict(us_per_step=us_per_step, us_eager=us_eager, avg_us=avg_us, dominant=dominant, dominant_us=dom_us,
                    bytes=ab, reuse=reuse)
 
@@ -369,6 +396,8 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=0, help="KV-cache copies rotated over (0 = enough to "
                     "defeat the 256 MB Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-reuse", action="store_true", help="skip the stage-reuse study (profiling runs: its "
+                    "warm-cache steps would mix into the per-kernel averages)")
     ap.add_argument("--secondary", default="ctx_1m", help="second workload reported inside the line ('' = none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain elementwise copy (torch.neg) of MIB MiB three times: the "
@@ -425,7 +454,7 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
-    b, r = measure(w, args.steps, args.warmup, auto_copies(w))
+    b, r = measure(w, args.steps, args.warmup, auto_copies(w), not args.no_reuse)
     total = r["bytes"]["total"]
     dom_bytes = r["bytes"]["per_kernel"][r["dominant"]]
     achieved = dom_bytes / (r["dominant_us"] * 1e-6) / 1e9
@@ -469,7 +498,7 @@ def main() -> int:
     b_torch.cuda.empty_cache()
     if args.secondary and args.secondary != w.name:
         w2 = WORKLOADS[args.secondary]
-        b2, r2 = measure(w2, max(20, args.steps // 2), args.warmup, auto_copies(w2))
+        b2, r2 = measure(w2, max(20, args.steps // 2), args.warmup, auto_copies(w2), not args.no_reuse)
         t2 = r2["bytes"]["total"]
         line["secondary"] = {"workload": w2.name, "us_per_step": round(r2["us_per_step"], 3),
                              "value_GBs": round(t2 / (r2["us_per_step"] * 1e-6) / 1e9, 2),

@@ -252,9 +252,9 @@ __device__ __forceinline__ void decode_blocks(const AttendParams& p, const Src& 
     }
 }
 
-// One instantiation per (group size, values on host, select width of the
+// One instantiation per (group size, values on host, select code of the
 // last stage (kGiven: reused, read from kept_idx; unused with host values),
-// select width of the stage before
+// select code of the stage before
 // it when the last two stages are fused here (0 = not fused)).
 template <int G, bool HOSTV, int SEL, int SELP>
 __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendParams p) {
@@ -467,12 +467,16 @@ template <int G>
 static void launch_g(const AttendParams& p, dim3 grid, bool hostv, bool fuse, bool given, size_t lds, hipStream_t s,
                      Timing t) {
     const dim3 block(kAttnThreads);
-    if (hostv) launch(sd_flash_decode_kernel<G, true, 8, 0>, grid, block, 0, s, t, p);
+    // a fused Q select is the 4-wide one (Q.ncand <= 512 when fused)
+    const int sq = select_width(p.last.ncand), sp = fuse ? select_width(p.P.ncand) : 0;
+    if (hostv) launch(sd_flash_decode_kernel<G, true, 4, 0>, grid, block, 0, s, t, p);
     else if (given) launch(sd_flash_decode_kernel<G, false, kGiven, 0>, grid, block, lds, s, t, p);
-    else if (fuse && select_width(p.P.ncand) == 8) launch(sd_flash_decode_kernel<G, false, 8, 8>, grid, block, lds, s, t, p);
-    else if (fuse) launch(sd_flash_decode_kernel<G, false, 8, 16>, grid, block, lds, s, t, p);
-    else if (select_width(p.last.ncand) == 8) launch(sd_flash_decode_kernel<G, false, 8, 0>, grid, block, lds, s, t, p);
-    else launch(sd_flash_decode_kernel<G, false, 16, 0>, grid, block, lds, s, t, p);
+    else if (fuse && sp == 4) launch(sd_flash_decode_kernel<G, false, 4, 4>, grid, block, lds, s, t, p);
+    else if (fuse && sp == 16) launch(sd_flash_decode_kernel<G, false, 4, 16>, grid, block, lds, s, t, p);
+    else if (fuse) launch(sd_flash_decode_kernel<G, false, 4, kSelLds>, grid, block, lds, s, t, p);
+    else if (sq == 4) launch(sd_flash_decode_kernel<G, false, 4, 0>, grid, block, lds, s, t, p);
+    else if (sq == 16) launch(sd_flash_decode_kernel<G, false, 16, 0>, grid, block, lds, s, t, p);
+    else launch(sd_flash_decode_kernel<G, false, kSelLds, 0>, grid, block, lds, s, t, p);
 }
 
 hipError_t launch_attend(sd_ctx* c, bool given, const uint16_t* q, const uint16_t* k, const uint16_t* v,

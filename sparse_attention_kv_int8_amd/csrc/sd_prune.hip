@@ -136,7 +136,7 @@ __device__ __forceinline__ void split_query(const int* Qlds, int sl, u32x4& qh, 
     ql = u32x4{l4[0], l4[1], l4[2], l4[3]};
 }
 
-// One instantiation per (rows per candidate / 8, select width of the
+// One instantiation per (rows per candidate / 8, select code of the
 // previous stage (0 = stage 0, kGiven = the previous stage reused), fused
 // next stage): each launch carries only
 // its own path, which keeps code size and scalar-register pressure down.
@@ -267,8 +267,9 @@ hipError_t launch_prune_stage(sd_ctx* c, int st, bool given, const uint16_t* q, 
     }
     if (sel == 0) { SD_PRUNE_NS(0); }
     else if (sel == kGiven) { SD_PRUNE_UNFUSED(kGiven); }   // reuse is not combined with fusion
-    else if (sel == 8) { SD_PRUNE_NS(8); }
-    else { SD_PRUNE_NS(16); }
+    else if (sel == 4) { SD_PRUNE_NS(4); }
+    else if (sel == 16) { SD_PRUNE_NS(16); }
+    else { SD_PRUNE_NS(kSelLds); }
 #undef SD_PRUNE_NS
 #undef SD_PRUNE_UNFUSED
 #undef SD_PRUNE

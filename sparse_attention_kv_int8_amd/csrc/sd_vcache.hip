@@ -59,7 +59,7 @@ struct VcStepParams {
     int32_t step;
 };
 
-// SEL: select width of the last stage, or kGiven when it is reused (read
+// SEL: select code of the last stage, or kGiven when it is reused (read
 // from kept_idx).
 template <int SEL>
 __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParams p) {
@@ -204,9 +204,11 @@ hipError_t launch_value_cache_update(sd_ctx* c, bool given, const int32_t* lengt
     p.step = int32_t(c->vc_step);
     const size_t lds = size_t(kept_lds_words(p.last, p.first_stage != 0)) * 4;
     dim3 grid(c->cfg.num_kv_heads, c->cfg.batch);
+    const int sw = select_width(p.last.ncand);
     if (given) launch(sd_vcache_step_kernel<kGiven>, grid, dim3(kLruThreads), lds, s, t, p);
-    else if (select_width(p.last.ncand) == 8) launch(sd_vcache_step_kernel<8>, grid, dim3(kLruThreads), lds, s, t, p);
-    else launch(sd_vcache_step_kernel<16>, grid, dim3(kLruThreads), lds, s, t, p);
+    else if (sw == 4) launch(sd_vcache_step_kernel<4>, grid, dim3(kLruThreads), lds, s, t, p);
+    else if (sw == 16) launch(sd_vcache_step_kernel<16>, grid, dim3(kLruThreads), lds, s, t, p);
+    else launch(sd_vcache_step_kernel<kSelLds>, grid, dim3(kLruThreads), lds, s, t, p);
     ++c->vc_step;
     return hipGetLastError();
 }
