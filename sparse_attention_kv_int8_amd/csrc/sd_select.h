@@ -118,21 +118,57 @@ __device__ __forceinline__ KeyStats block_key_stats(unsigned nv, uint32_t kmin, 
 }
 
 // Loads n chunk scores into LDS as select keys, clears the histogram of the
-// select scratch `cand` (kRadixWords words), and returns the KeyStats.
-// xch: 16 words.  Ends with a barrier.
+// select scratch `cand` (kRadixWords words), and returns the KeyStats; also
+// stages npar ints `parents` into `par` (LDS).  The parents' loads and the
+// first kLoadBatch scores of every thread are issued before any of them is
+// waited for, so the staging costs one memory round trip (the loads of a
+// wave complete in issue order: a load-wait-store loop would pay one round
+// trip per iteration).  xch: 16 words.  Ends with a barrier.
+constexpr int kLoadBatch = 8;
+constexpr int kParBatch = 2;
+
 template <int NT>
-__device__ KeyStats load_keys(const int32_t* scores, int n, uint32_t* keys, uint32_t* cand, unsigned* xch) {
+__device__ KeyStats load_keys(const int32_t* scores, int n, uint32_t* keys, uint32_t* cand, unsigned* xch,
+                              const int32_t* parents = nullptr, int npar = 0, int* par = nullptr) {
     static_assert(NT >= 256, "one thread per histogram bin");
     const int tid = threadIdx.x;
     if (tid < 256) cand[tid] = 0u;
     unsigned nv = 0, kmin = 0xffffffffu, kmax = 0;
-    for (int i = tid; i < n; i += NT) {
-        const uint32_t k = score_key(scores[i]);
+    auto put = [&](int i, int32_t sc) {
+        const uint32_t k = score_key(sc);
         keys[i] = k;
         nv += k != 0u;
         kmin = min(kmin, k ? k : 0xffffffffu);
         kmax = max(kmax, k);
+    };
+    int32_t pv[kParBatch];
+#pragma unroll
+    for (int u = 0; u < kParBatch; ++u) {
+        const int i = tid + u * NT;
+        pv[u] = i < npar ? parents[i] : -1;
     }
+    for (int i0 = tid; i0 < n; i0 += kLoadBatch * NT) {
+        int32_t sv[kLoadBatch];
+#pragma unroll
+        for (int u = 0; u < kLoadBatch; ++u) {
+            const int i = i0 + u * NT;
+            sv[u] = i < n ? scores[i] : INT32_MIN;
+        }
+        if (i0 == tid) {
+#pragma unroll
+            for (int u = 0; u < kParBatch; ++u)
+                if (tid + u * NT < npar) par[tid + u * NT] = pv[u];
+        }
+#pragma unroll
+        for (int u = 0; u < kLoadBatch; ++u)
+            if (i0 + u * NT < n) put(i0 + u * NT, sv[u]);
+    }
+    if (n <= tid) {                              // no score of this thread: its parents still go in
+#pragma unroll
+        for (int u = 0; u < kParBatch; ++u)
+            if (tid + u * NT < npar) par[tid + u * NT] = pv[u];
+    }
+    for (int i = tid + kParBatch * NT; i < npar; i += NT) par[i] = parents[i];
     return block_key_stats<NT>(nv, kmin, kmax, xch);
 }
 
@@ -379,9 +415,8 @@ __device__ int kept_of_stage(const StageDev& st, bool first_stage, const int32_t
     int* sel = reinterpret_cast<int*>(lds + st.ncand);
     int* cand = sel + st.keep + 1;
     int* par = cand + select_cand_words(st.ncand, st.keep);
-    if (!first_stage)
-        for (int i = threadIdx.x; i < st.ncand / st.ratio; i += NT) par[i] = parents[i];
-    const KeyStats ks = load_keys<NT>(scores_bj, st.ncand, keys, reinterpret_cast<uint32_t*>(cand), tmp);
+    const KeyStats ks = load_keys<NT>(scores_bj, st.ncand, keys, reinterpret_cast<uint32_t*>(cand), tmp, parents,
+                                      first_stage ? 0 : st.ncand / st.ratio, par);
     const int nk = select_top<NT, E>(keys, st.ncand, st.keep, sel, cand, tmp, ks);
     for (int i = threadIdx.x; i < nk; i += NT) sel[i] = int(cand_start(st, first_stage, par, sel[i], L));
     __syncthreads();
@@ -420,11 +455,21 @@ __device__ FusedOut kept_two_stages(const StageDev& P, bool p_first, const int32
     int* candQ = selQ + Q.keep + 1;
     int* startsP = candQ + select_cand_words(Q.ncand, Q.keep);
 
-    // every load is issued up front: P's parents, all children's Q scores, P's scores
-    if (!p_first)
-        for (int i = threadIdx.x; i < P.ncand / P.ratio; i += NT) parP[i] = parentsP[i];
-    for (int i = threadIdx.x; i < P.ncand * rq; i += NT) preL[i] = pre_bj[i];
-    const KeyStats ksP = load_keys<NT>(scoresP_bj, P.ncand, keysP, reinterpret_cast<uint32_t*>(candP), tmp);
+    // the children's Q scores are issued first (in batches, no wait between
+    // the loads of a batch), then P's parents and scores
+    for (int i0 = threadIdx.x; i0 < P.ncand * rq; i0 += kLoadBatch * NT) {
+        int32_t v[kLoadBatch];
+#pragma unroll
+        for (int u = 0; u < kLoadBatch; ++u) {
+            const int i = i0 + u * NT;
+            v[u] = i < P.ncand * rq ? pre_bj[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kLoadBatch; ++u)
+            if (i0 + u * NT < P.ncand * rq) preL[i0 + u * NT] = v[u];
+    }
+    const KeyStats ksP = load_keys<NT>(scoresP_bj, P.ncand, keysP, reinterpret_cast<uint32_t*>(candP), tmp, parentsP,
+                                       p_first ? 0 : P.ncand / P.ratio, parP);
     const int np = select_top<NT, EP>(keysP, P.ncand, P.keep, selP, candP, tmp, ksP);
     // P starts; Q candidate i is child i % rq of kept P chunk i / rq
     for (int i = threadIdx.x; i < P.keep; i += NT)
