@@ -24,6 +24,11 @@ roofline = the dominant kernel's algorithmic bytes per launch / its average
          no record exists or the kernel sources changed since it was taken.
 cpu_baseline = the CPU oracle (numpy, one core) on one full step of the same
          workload.
+us_per_step_spread = p10 / p50 / p90 of single replayed steps, each
+         between HIP events (outside the timed region).
+stream_ceiling = a plain streaming copy (torch.neg, 1 GiB read + 1 GiB
+         written) on the same GPU: the practically reachable HBM rate, for
+         context.
 reuse  = steps that reuse the first r pruning stages' kept sets from an
          earlier step (sd_decode_step_reuse): us per step for each r, and,
          over a drifting query sequence, how much of the fully recomputed
@@ -260,6 +265,30 @@ def reuse_study(b, steps: int, seq: int = 8) -> dict:
     return res
 
 
+def stream_ceiling(mib: int = 1024) -> dict:
+    """A plain streaming kernel on the same GPU, for context: torch's
+    elementwise negation of a bf16 tensor of `mib` MiB into another (the
+    bytes read plus the bytes written), median of 5 event-timed runs after a
+    warm-up."""
+    import torch
+    x = torch.ones(mib * (1 << 20) // 2, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    torch.neg(x, out=y)
+    times = []
+    for _ in range(5):
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.neg(x, out=y)
+        e.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(e) * 1e-3)
+    del x, y
+    torch.cuda.empty_cache()
+    t = statistics.median(times)
+    return {"GBs": round(2 * mib * (1 << 20) / t / 1e9, 1), "kernel": "torch.neg, bf16 copy (read + write)",
+            "bytes": 2 * mib * (1 << 20)}
+
+
 def oracle_baseline(w, inp, kept_gpu_bytes: float) -> dict:
     """The CPU oracle on one full step of the same inputs (one core)."""
     try:
@@ -312,6 +341,17 @@ def measure(w, steps: int, warmup: int, copies: int, reuse: bool = True) -> tupl
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     us_per_step = (t1 - t0) / steps * 1e6
+    # spread: the same replays one at a time between HIP events on the
+    # replay stream (outside the timed region; each step's own time)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, e) in enumerate(evs):
+        a.record()
+        b.graphs[i % len(b.graphs)].replay()
+        e.record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(e) * 1e3 for a, e in evs)
+    spread = {"p10": round(per[len(per) // 10], 3), "p50": round(per[len(per) // 2], 3),
+              "p90": round(per[(9 * len(per)) // 10], 3)}
     # the same K steps launched eagerly, the dominant kernel's dispatches
     # carrying HIP events on the launch stream: its live average duration
     b.dec.sd_profile_start(1 << dom_kind, steps + 8)
@@ -326,7 +366,7 @@ def measure(w, steps: int, warmup: int, copies: int, reuse: bool = True) -> tupl
     ab = algorithmic_bytes(w, kept, b.inp.lengths)
     reuse = reuse_study(b, steps) if reuse and w.steps == 1 else None
     return b, dict(us_per_step=us_per_step, us_eager=us_eager, avg_us=avg_us, dominant=dominant, dominant_us=dom_us,
-                   bytes=ab, reuse=reuse)
+                   bytes=ab, reuse=reuse, spread=spread)
 
 
 def measure_hostv(w, repeats: int = 3) -> dict:
@@ -478,6 +518,7 @@ def main() -> int:
                    "stages": [[s.chunk, s.stride, s.keep] for s in w.stages], "sink": w.sink, "window": w.window,
                    "cache": f"cold: {len(b.args)} rotating copies", "launch": "HIP graph replay, one step per graph"},
         "us_per_step": round(r["us_per_step"], 3),
+        "us_per_step_spread": r["spread"],
         "us_per_step_eager": round(r["us_eager"], 3),
         "tokens_per_s": round(w.batch / (r["us_per_step"] * 1e-6), 1),
         "algorithmic_bytes": total,
@@ -509,6 +550,7 @@ def main() -> int:
                              "quantize_keys_us": round(b2.quantize_us, 2), "reuse": r2["reuse"]}
         del b2
         b_torch.cuda.empty_cache()
+    line["stream_ceiling"] = stream_ceiling()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on one step ...")
         line["cpu_baseline"] = oracle_baseline(w, inp, kb)

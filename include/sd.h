@@ -170,9 +170,7 @@ sd_status sd_decode_step(sd_ctx* ctx, const uint16_t* q, const uint16_t* k_bf16,
  * written by a step of this context (unsorted, repeated, or not multiples
  * of the chunk) give unspecified results but no out-of-range access.
  * Chunk scores of reused stages (sd_stage_scores) stay those of the step
- * that computed them.  A context created with the last stage fused
- * (environment SD_FUSE_LAST_STAGE=1) returns SD_ERR_UNSUPPORTED for
- * reuse_stages > 0. */
+ * that computed them. */
 sd_status sd_decode_step_reuse(sd_ctx* ctx, const uint16_t* q, const uint16_t* k_bf16,
                                const int8_t* k_int8, const uint16_t* v, const int32_t* lengths,
                                uint16_t* out, int32_t* kept_idx, int32_t reuse_stages,

@@ -103,20 +103,21 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
         na = na < 1 ? 1 : na > c->nsplit - 1 ? c->nsplit - 1 : na;
         c->nsplit_a = na;
     }
-    // Optionally (environment SD_FUSE_LAST_STAGE=1) fuse the last stage Q
-    // into the kernel of the stage P before it.  Possible when Q's chunks are
-    // exactly 8 sampled rows (one load slot), Q's stride divides P's (so P's
-    // samples are among the rows read), P reads at most 4x its own samples,
-    // all children's scores fit in LDS, and Q's select is the 8-wide one; not
-    // with host values (their value-cache kernel selects the last stage by
-    // itself).  It trades one kernel and one scoring pass for a second select
-    // in the decode kernel and more rows read by P; on the measured
-    // configurations the two are about even, so it is off by default.
+    // Fuse the last stage Q into the kernel of the stage P before it (unless
+    // the environment sets SD_FUSE_LAST_STAGE=0).  Possible when Q's chunks
+    // are exactly 8 sampled rows (one load slot), Q's stride divides P's (so
+    // P's samples are among the rows read), P reads at most 4x its own
+    // samples, all children's scores fit in LDS, and Q's select keeps its
+    // keys in registers (at most 512 candidates); not with host values
+    // (their value-cache kernel selects the last stage by itself).  It
+    // trades one kernel boundary and one scoring pass for a second select
+    // in the decode kernel and more rows read by P: about 1.5 us less per
+    // step at 128K and at 1M.
     c->fuse = 0;
     c->fuse_rq = 0;
     c->fuse_m = 0;
     const char* fenv = std::getenv("SD_FUSE_LAST_STAGE");
-    const bool want_fuse = fenv && fenv[0] == '1';
+    const bool want_fuse = !(fenv && fenv[0] == '0');
     if (want_fuse && cfg.num_stages >= 2 && !cfg.values_on_host) {
         sd::StageGeom& P = c->st[cfg.num_stages - 2];
         const sd::StageGeom& Q = c->st[cfg.num_stages - 1];
@@ -319,7 +320,6 @@ sd_status sd_decode_step_reuse(sd_ctx* c, const uint16_t* q, const uint16_t* k, 
     if (!aligned16(q) || !aligned16(k) || !aligned16(k8) || !aligned16(v) || !aligned16(out))
         return SD_ERR_INVALID_ARG;
     if (reuse < 0 || reuse > c->S) return SD_ERR_INVALID_ARG;
-    if (reuse > 0 && c->fuse) return SD_ERR_UNSUPPORTED;     // the fused plan reads other rows at stage S-2
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint16_t* vk = v;
     if (c->cfg.values_on_host) {
@@ -336,12 +336,16 @@ sd_status sd_decode_step_reuse(sd_ctx* c, const uint16_t* q, const uint16_t* k, 
         vk = c->vhost_dev;
     }
     hipError_t e = hipSuccess;
-    // stages [0, reuse) keep the kept sets that kept_idx holds; the first
-    // stage run reads its parents from there
-    const int nprune = c->fuse ? c->S - 1 : c->S;     // a fused last stage has no kernel of its own
+    // Stages [0, reuse) keep the kept sets that kept_idx holds; the first
+    // stage run reads its parents from there.  The fused plan (the last
+    // stage scored inside the kernel of the one before, both selected by
+    // the decode kernel) serves while that stage before the last runs;
+    // when it is reused, the last stage runs in a kernel of its own.
+    const bool fused = c->fuse && reuse <= c->S - 2;
+    const int nprune = fused ? c->S - 1 : c->S;
     for (int st = reuse; st < nprune && e == hipSuccess; ++st)
         e = timed(c, SD_PROF_STAGE0 + st, s, [&](sd::Timing t) {
-            return sd::launch_prune_stage(c, st, st == reuse && st > 0, q, k8, lengths, kept, s, t);
+            return sd::launch_prune_stage(c, st, st == reuse && st > 0, fused, q, k8, lengths, kept, s, t);
         });
     const bool last_given = reuse == c->S;
     if (e == hipSuccess && c->cfg.values_on_host)
@@ -350,7 +354,7 @@ sd_status sd_decode_step_reuse(sd_ctx* c, const uint16_t* q, const uint16_t* k, 
         });
     if (e == hipSuccess)
         e = timed(c, SD_PROF_ATTEND, s, [&](sd::Timing t) {
-            return sd::launch_attend(c, last_given, q, k, vk, lengths, kept, out, s, t);
+            return sd::launch_attend(c, last_given, fused, q, k, vk, lengths, kept, out, s, t);
         });
     if (e == hipSuccess)
         e = timed(c, SD_PROF_COMBINE, s, [&](sd::Timing t) { return sd::launch_combine(c, out, s, t); });

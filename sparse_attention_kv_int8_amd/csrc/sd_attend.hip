@@ -479,7 +479,7 @@ static void launch_g(const AttendParams& p, dim3 grid, bool hostv, bool fuse, bo
     else launch(sd_flash_decode_kernel<G, false, kSelLds, 0>, grid, block, lds, s, t, p);
 }
 
-hipError_t launch_attend(sd_ctx* c, bool given, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+hipError_t launch_attend(sd_ctx* c, bool given, bool fused, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const int32_t* lengths, int32_t* kept, uint16_t* out, hipStream_t s, Timing t) {
     AttendParams p{};
     p.q = q;
@@ -506,7 +506,7 @@ hipError_t launch_attend(sd_ctx* c, bool given, const uint16_t* q, const uint16_
     p.flag = c->flag;
     p.sink = c->cfg.sink;
     p.window = c->cfg.window;
-    const bool fuse = c->fuse != 0 && !given;
+    const bool fuse = fused && !given;
     if (fuse) {
         p.P = stage_dev(c, S - 2);
         p.p_first = S == 2;

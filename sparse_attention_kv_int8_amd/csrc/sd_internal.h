@@ -118,9 +118,11 @@ hipError_t launch_quantize_query(sd_ctx* c, const uint16_t* q, int8_t* q8, int32
 // given: the kept set that the launch would select (stage - 1's for a
 // pruning stage, the last stage's for the decode and value-cache kernels)
 // is read from kept_idx instead, where an earlier step left it.
-hipError_t launch_prune_stage(sd_ctx* c, int stage, bool given, const uint16_t* q, const int8_t* k8,
+// fused: this step runs the fused plan (the stage before the last also
+// scores the last stage's candidates, and the decode kernel selects both).
+hipError_t launch_prune_stage(sd_ctx* c, int stage, bool given, bool fused, const uint16_t* q, const int8_t* k8,
                               const int32_t* lengths, int32_t* kept, hipStream_t s, Timing t = {});
-hipError_t launch_attend(sd_ctx* c, bool given, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+hipError_t launch_attend(sd_ctx* c, bool given, bool fused, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const int32_t* lengths, int32_t* kept, uint16_t* out, hipStream_t s, Timing t = {});
 hipError_t launch_combine(sd_ctx* c, uint16_t* out, hipStream_t s, Timing t = {});
 hipError_t launch_value_cache_update(sd_ctx* c, bool given, const int32_t* lengths, int32_t* kept, hipStream_t s,

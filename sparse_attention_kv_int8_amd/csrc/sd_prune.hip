@@ -217,7 +217,7 @@ StageDev stage_dev(const sd_ctx* c, int st) {
     return d;
 }
 
-hipError_t launch_prune_stage(sd_ctx* c, int st, bool given, const uint16_t* q, const int8_t* k8,
+hipError_t launch_prune_stage(sd_ctx* c, int st, bool given, bool fused, const uint16_t* q, const int8_t* k8,
                               const int32_t* lengths, int32_t* kept, hipStream_t s, Timing t) {
     PruneParams p{};
     p.q = q;
@@ -237,7 +237,7 @@ hipError_t launch_prune_stage(sd_ctx* c, int st, bool given, const uint16_t* q, 
     p.scores = c->scores[st];
     p.nrows = c->st[st].nrows;
     p.rstride = c->st[st].rstride;
-    const bool fuse = c->fuse && st == c->S - 2;
+    const bool fuse = fused && st == c->S - 2;
     p.fuse_rq = fuse ? c->fuse_rq : 0;
     p.fuse_m = fuse ? c->fuse_m : 1;
     p.pre = fuse ? c->pre : nullptr;
@@ -266,7 +266,7 @@ hipError_t launch_prune_stage(sd_ctx* c, int st, bool given, const uint16_t* q, 
         SD_PRUNE_UNFUSED(S);                                    \
     }
     if (sel == 0) { SD_PRUNE_NS(0); }
-    else if (sel == kGiven) { SD_PRUNE_UNFUSED(kGiven); }   // reuse is not combined with fusion
+    else if (sel == kGiven) { SD_PRUNE_NS(kGiven); }
     else if (sel == 4) { SD_PRUNE_NS(4); }
     else if (sel == 16) { SD_PRUNE_NS(16); }
     else { SD_PRUNE_NS(kSelLds); }
