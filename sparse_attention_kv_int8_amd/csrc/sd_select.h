@@ -121,7 +121,7 @@ __device__ __forceinline__ KeyStats block_key_stats(unsigned nv, uint32_t kmin, 
 // select scratch `cand` (kRadixWords words), and returns the KeyStats; also
 // stages npar ints `parents` into `par` (LDS).  The parents' loads and the
 // first kLoadBatch scores of every thread are issued before any of them is
-// waited for, so the staging costs one memory round trip (the loads of a
+// waited for, so up to 2048 candidates cost one memory round trip (the loads of a
 // wave complete in issue order: a load-wait-store loop would pay one round
 // trip per iteration).  xch: 16 words.  Ends with a barrier.
 constexpr int kLoadBatch = 8;

@@ -40,6 +40,8 @@ __global__ void sd_vcache_reset_kernel(ValueCache vc, int64_t BH) {
     if (t0 < kVcCounters) vc.counters[t0] = 0;
 }
 
+constexpr int kVcBatch = 8;     // LRU entries per batch of loads (per thread)
+
 struct VcStepParams {
     ValueCache vc;
     StageDev last;
@@ -104,15 +106,28 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
     // 1. hits touch their slot; misses are ranked in block order (ascending id)
     const int per = (nb + kLruThreads - 1) / kLruThreads;
     const int r0 = min(nb, tid * per), r1 = min(nb, r0 + per);
+    // (the loops below take kVcBatch entries at a time: their independent
+    // loads, then the loads that depend on them, then the updates, so that
+    // a batch costs two memory round trips instead of two per entry)
     unsigned nm = 0;
-    for (int r = r0; r < r1; ++r) {
-        const int32_t s = page[bl[r] >> 8];
-        if (s >= 0) {
-            slast[s] = step;
-            bslot[r] = s;
-        } else {
-            bslot[r] = -1;
-            ++nm;
+    for (int b0 = r0; b0 < r1; b0 += kVcBatch) {
+        uint32_t e[kVcBatch];
+        int32_t sv[kVcBatch];
+#pragma unroll
+        for (int u = 0; u < kVcBatch; ++u) e[u] = bl[min(b0 + u, r1 - 1)];    // clamped: no branch
+#pragma unroll
+        for (int u = 0; u < kVcBatch; ++u) sv[u] = page[e[u] >> 8];
+#pragma unroll
+        for (int u = 0; u < kVcBatch; ++u) {
+            const int r = b0 + u;
+            if (r >= r1) break;
+            if (sv[u] >= 0) {
+                slast[sv[u]] = step;
+                bslot[r] = sv[u];
+            } else {
+                bslot[r] = -1;
+                ++nm;
+            }
         }
     }
     unsigned nmiss;
@@ -124,19 +139,37 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
     const int per2 = (used + kLruThreads - 1) / kLruThreads;
     const int i0 = min(used, tid * per2), i1 = min(used, i0 + per2);
     unsigned nu = 0;
-    for (int i = i0; i < i1; ++i) nu += slast[order_old[i]] != step;
+    for (int b0 = i0; b0 < i1; b0 += kVcBatch) {
+        int32_t sv[kVcBatch], lv[kVcBatch];
+#pragma unroll
+        for (int u = 0; u < kVcBatch; ++u) sv[u] = order_old[min(b0 + u, i1 - 1)];
+#pragma unroll
+        for (int u = 0; u < kVcBatch; ++u) lv[u] = slast[sv[u]];
+#pragma unroll
+        for (int u = 0; u < kVcBatch; ++u) nu += b0 + u < i1 && lv[u] != step;
+    }
     unsigned nuntouched;
     unsigned krank = block_excl_scan<kLruThreads>(nu, tmp, &nuntouched);
-    for (int i = i0; i < i1; ++i) {
-        const int32_t s = order_old[i];
-        if (slast[s] == step) continue;
-        if (int(krank) < nevict) {
-            page[sblk[s]] = -1;
-            evicted[krank] = s;
-        } else {
-            order_new[krank - nevict] = s;
+    for (int b0 = i0; b0 < i1; b0 += kVcBatch) {
+        int32_t sv[kVcBatch], lv[kVcBatch], bv[kVcBatch];
+#pragma unroll
+        for (int u = 0; u < kVcBatch; ++u) sv[u] = order_old[min(b0 + u, i1 - 1)];
+#pragma unroll
+        for (int u = 0; u < kVcBatch; ++u) {
+            lv[u] = slast[sv[u]];
+            bv[u] = sblk[sv[u]];
         }
-        ++krank;
+#pragma unroll
+        for (int u = 0; u < kVcBatch; ++u) {
+            if (b0 + u >= i1 || lv[u] == step) continue;     // past the range, or touched this step
+            if (int(krank) < nevict) {
+                page[bv[u]] = -1;
+                evicted[krank] = sv[u];
+            } else {
+                order_new[krank - nevict] = sv[u];
+            }
+            ++krank;
+        }
     }
     __syncthreads();
     const int nsurv = int(nuntouched) - nevict;
