@@ -550,7 +550,8 @@ def main() -> int:
                              "quantize_keys_us": round(b2.quantize_us, 2), "reuse": r2["reuse"]}
         del b2
         b_torch.cuda.empty_cache()
-    line["stream_ceiling"] = stream_ceiling()
+    if not args.copy_calibration:            # its copies would mix with the calibration copies
+        line["stream_ceiling"] = stream_ceiling()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on one step ...")
         line["cpu_baseline"] = oracle_baseline(w, inp, kb)
