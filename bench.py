@@ -29,6 +29,9 @@ us_per_step_spread = p10 / p50 / p90 of single replayed steps, each
 stream_ceiling = a plain streaming copy (torch.neg, 1 GiB read + 1 GiB
          written) on the same GPU: the practically reachable HBM rate, for
          context.
+dense  = dense decode attention over every cached token (sd_dense_decode),
+         timed the same way: us per step, its kernel's bandwidth against
+         8 TB/s, and the sparse step's speedup over it.
 reuse  = steps that reuse the first r pruning stages' kept sets from an
          earlier step (sd_decode_step_reuse): us per step for each r, and,
          over a drifting query sequence, how much of the fully recomputed
@@ -55,7 +58,7 @@ from sparse_attention_kv_int8_amd.inputs import WORKLOADS, make_inputs, make_que
 
 METRIC = "sparse decode-attention µs/step + achieved HBM GB/s at 128K and 1M ctx (GQA 32/8)"
 HBM_PEAK_GBS = 8000.0
-KIND_NAMES = ["stage0", "stage1", "stage2", "stage3", "value_cache", "attend", "quantize", "combine"]
+KIND_NAMES = ["stage0", "stage1", "stage2", "stage3", "value_cache", "attend", "quantize", "combine", "dense"]
 
 
 def log(*a):
@@ -265,6 +268,54 @@ def reuse_study(b, steps: int, seq: int = 8) -> dict:
     return res
 
 
+def dense_study(b, steps: int, warmup: int, sparse_us: float) -> dict:
+    """Dense decode attention over every cached token (sd_dense_decode), the
+    comparison the sparse step is made to beat: timed like the main figure
+    (one HIP graph per cache copy, replayed), then the same steps launched
+    eagerly with the dense kernel's and its merge's dispatches carrying HIP
+    events on the launch stream.  bytes = bf16 K and V of every token t < L_b
+    of every (request, KV head), plus the query and the output."""
+    torch, lib, h, w, B = b.torch, b.B.lib, b.dec.handle, b.w, b.B
+    out = torch.empty_like(b.out)
+    args = [(b.q.data_ptr(), b.ks[i].data_ptr(), b.vs[i].data_ptr(), b.lengths.data_ptr(), out.data_ptr())
+            for i in range(len(b.ks))]
+    graphs = []
+    torch.cuda.synchronize()
+    for a in args:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st = lib.sd_dense_decode(h, *a, torch.cuda.current_stream().cuda_stream)
+            if st:
+                B.check(st, "sd_dense_decode (capture)")
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / steps * 1e6
+    del graphs
+    b.dec.sd_profile_start((1 << B.SD_PROF_DENSE) | (1 << B.SD_PROF_COMBINE), 2 * steps + 8)
+    for i in range(steps):
+        st = lib.sd_dense_decode(h, *args[i % len(args)], b.stream)
+        if st:
+            B.check(st, "sd_dense_decode")
+    prof = b.dec.sd_profile_stop()
+    k_us = prof["dense"][0] * 1e3 / prof["dense"][1]
+    c_us = prof["combine"][0] * 1e3 / prof["combine"][1]
+    nbytes = int(512 * w.num_kv_heads * int(np.sum(b.inp.lengths.astype(np.int64)))
+                 + 4 * w.batch * w.num_q_heads * w.head_dim)
+    return {"us_per_step": round(us, 3), "value_GBs": round(nbytes / (us * 1e-6) / 1e9, 2),
+            "bytes": nbytes, "kernel_us": round(k_us, 3), "combine_us": round(c_us, 3),
+            "kernel_roofline": {"bound": "hbm", "achieved": round(nbytes / (k_us * 1e-6) / 1e9, 2),
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(nbytes / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+            "sparse_speedup": round(us / sparse_us, 2),
+            "note": "sd_dense_decode over every token, same rotating cold copies, HIP graph replay"}
+
+
 def stream_ceiling(mib: int = 1024) -> dict:
     """A plain streaming kernel on the same GPU, for context: torch's
     elementwise negation of a bf16 tensor of `mib` MiB into another (the
@@ -322,13 +373,13 @@ def oracle_baseline(w, inp, kept_gpu_bytes: float) -> dict:
             "s_per_step": round(ts, 4), "quantize_s": round(tq, 3)}
 
 
-def measure(w, steps: int, warmup: int, copies: int, reuse: bool = True) -> tuple:
+def measure(w, steps: int, warmup: int, copies: int, reuse: bool = True, dense: bool = True) -> tuple:
     b = Bench(w, copies)
     torch = b.torch
     b.run(warmup)
     torch.cuda.synchronize()
     # calibration: all kernels timed, to pick the dominant one
-    cal = b.profile(max(20, warmup), 0xFF)
+    cal = b.profile(max(20, warmup), 0xFF)          # the step's kinds (not the dense comparison)
     avg_us = {k: v[0] * 1e3 / v[1] for k, v in cal.items()}
     dominant = max((k for k in avg_us if k != "quantize"), key=lambda k: avg_us[k])
     dom_kind = KIND_NAMES.index(dominant)
@@ -365,8 +416,9 @@ def measure(w, steps: int, warmup: int, copies: int, reuse: bool = True) -> tupl
     kept = b.kept.cpu().numpy()
     ab = algorithmic_bytes(w, kept, b.inp.lengths)
     reuse = reuse_study(b, steps) if reuse and w.steps == 1 else None
+    dense = dense_study(b, steps, warmup, us_per_step) if dense else None
     return b, dict(us_per_step=us_per_step, us_eager=us_eager, avg_us=avg_us, dominant=dominant, dominant_us=dom_us,
-                   bytes=ab, reuse=reuse, spread=spread)
+                   bytes=ab, reuse=reuse, spread=spread, dense=dense)
 
 
 def measure_hostv(w, repeats: int = 3) -> dict:
@@ -438,6 +490,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reuse", action="store_true", help="skip the stage-reuse study (profiling runs: its "
                     "warm-cache steps would mix into the per-kernel averages)")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-decode comparison (sd_dense_decode)")
     ap.add_argument("--secondary", default="ctx_1m", help="second workload reported inside the line ('' = none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain elementwise copy (torch.neg) of MIB MiB three times: the "
@@ -494,7 +547,7 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
-    b, r = measure(w, args.steps, args.warmup, auto_copies(w), not args.no_reuse)
+    b, r = measure(w, args.steps, args.warmup, auto_copies(w), not args.no_reuse, not args.no_dense)
     total = r["bytes"]["total"]
     dom_bytes = r["bytes"]["per_kernel"][r["dominant"]]
     achieved = dom_bytes / (r["dominant_us"] * 1e-6) / 1e9
@@ -532,6 +585,7 @@ def main() -> int:
                           "note": "all per-step bytes / sum of per-step kernel durations"},
         "quantize_keys_us": round(b.quantize_us, 2),
         "reuse": r["reuse"],
+        "dense": r["dense"],
     }
     inp, kb = b.inp, total
     del b
@@ -539,7 +593,8 @@ def main() -> int:
     b_torch.cuda.empty_cache()
     if args.secondary and args.secondary != w.name:
         w2 = WORKLOADS[args.secondary]
-        b2, r2 = measure(w2, max(20, args.steps // 2), args.warmup, auto_copies(w2), not args.no_reuse)
+        b2, r2 = measure(w2, max(20, args.steps // 2), args.warmup, auto_copies(w2), not args.no_reuse,
+                         not args.no_dense)
         t2 = r2["bytes"]["total"]
         line["secondary"] = {"workload": w2.name, "us_per_step": round(r2["us_per_step"], 3),
                              "value_GBs": round(t2 / (r2["us_per_step"] * 1e-6) / 1e9, 2),
@@ -547,7 +602,8 @@ def main() -> int:
                              "dominant": r2["dominant"],
                              "dominant_frac": round(r2["bytes"]["per_kernel"][r2["dominant"]] /
                                                     (r2["dominant_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                             "quantize_keys_us": round(b2.quantize_us, 2), "reuse": r2["reuse"]}
+                             "quantize_keys_us": round(b2.quantize_us, 2), "reuse": r2["reuse"],
+                             "dense": r2["dense"]}
         del b2
         b_torch.cuda.empty_cache()
     if not args.copy_calibration:            # its copies would mix with the calibration copies

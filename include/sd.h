@@ -176,6 +176,28 @@ sd_status sd_decode_step_reuse(sd_ctx* ctx, const uint16_t* q, const uint16_t* k
                                uint16_t* out, int32_t* kept_idx, int32_t reuse_stages,
                                void* stream);
 
+/* Dense decode attention over every cached token, for comparison with the
+ * sparse step: for each query head h, softmax(softmax_scale * q_h K^T) V
+ * over all tokens t < L_b of KV head h / G, with the same arithmetic as the
+ * sparse step's attention (bf16 q and K, fp32 scores, online softmax and
+ * accumulation, log-sum-exp merge of the splits, bf16 output rounded to
+ * nearest even).  Sources: page "KV Cache 与长上下文推理", section "KV Cache
+ * 回顾" (the decode attention equation over the whole cache); the news
+ * article on InfiniteHiP, opening section, compares its sparse decoding
+ * against exactly this dense attention at long context.
+ *  q        device [B][Hq][d] bf16.
+ *  k_bf16   device [B][Hkv][Lmax][d] bf16 keys.
+ *  v        device [B][Hkv][Lmax][d] bf16 values.
+ *  lengths  device [B] int32, each in [1, Lmax].
+ *  out      device [B][Hq][d] bf16 output.
+ * Needs values_on_host = 0 (else SD_ERR_UNSUPPORTED).  Uses the context's
+ * workspace for its split partials, so it must not overlap a decode step of
+ * the same context.  A request with a length outside [1, Lmax] gets zero
+ * output and raises the device flag (see sd_check).  Allocates nothing. */
+sd_status sd_dense_decode(sd_ctx* ctx, const uint16_t* q, const uint16_t* k_bf16,
+                          const uint16_t* v, const int32_t* lengths, uint16_t* out,
+                          void* stream);
+
 /* The step's query codes, for inspection: q8 device [B][Hq][d] int8 with one
  * absmax scale per query head (same rounding as the keys), and q_group
  * device [B][Hkv][d] int32, the sum of q8 over each KV head's group.  Either
@@ -211,7 +233,8 @@ enum {
     SD_PROF_ATTEND = 5,         /* last select + attended set + sparse flash decode (partials) */
     SD_PROF_QUANTIZE = 6,       /* the three kernels of sd_quantize_keys, as one interval */
     SD_PROF_COMBINE = 7,        /* log-sum-exp merge of the splits into the bf16 output */
-    SD_PROF_KINDS = 8
+    SD_PROF_DENSE = 8,          /* dense flash decode of sd_dense_decode (partials; its merge is COMBINE) */
+    SD_PROF_KINDS = 9
 };
 
 typedef struct sd_profile {

@@ -40,9 +40,9 @@ class sd_config(C.Structure):
     ]
 
 
-SD_PROF_KINDS = 8
-SD_PROF_STAGE0, SD_PROF_VALUE_CACHE, SD_PROF_ATTEND, SD_PROF_QUANTIZE, SD_PROF_COMBINE = 0, 4, 5, 6, 7
-PROF_NAMES = ["stage0", "stage1", "stage2", "stage3", "value_cache", "attend", "quantize", "combine"]
+SD_PROF_KINDS = 9
+SD_PROF_STAGE0, SD_PROF_VALUE_CACHE, SD_PROF_ATTEND, SD_PROF_QUANTIZE, SD_PROF_COMBINE, SD_PROF_DENSE = 0, 4, 5, 6, 7, 8
+PROF_NAMES = ["stage0", "stage1", "stage2", "stage3", "value_cache", "attend", "quantize", "combine", "dense"]
 
 
 class sd_profile(C.Structure):
@@ -72,6 +72,7 @@ _SIGS = {
     "sd_quantize_keys": (C.c_int, [_p, _p, _p, _p, _p, _p]),
     "sd_decode_step": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "sd_decode_step_reuse": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, C.c_int32, _p]),
+    "sd_dense_decode": (C.c_int, [_p, _p, _p, _p, _p, _p, _p]),
     "sd_quantize_query": (C.c_int, [_p, _p, _p, _p, _p]),
     "sd_stage_scores": (C.c_int, [_p, C.c_int32, _p, C.c_int64, _p]),
     "sd_stage_candidates": (C.c_int64, [_p, C.c_int32]),
@@ -183,6 +184,10 @@ class SparseDecoder:
         check(lib.sd_decode_step_reuse(self.handle, _ptr(q), _ptr(k), _ptr(k_int8), _ptr(v), _ptr(lengths),
                                        _ptr(out), _ptr(kept_idx), int(reuse_stages), _stream(stream)),
               "sd_decode_step_reuse")
+
+    def sd_dense_decode(self, q, k, v, lengths, out, stream=None) -> None:
+        check(lib.sd_dense_decode(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(lengths), _ptr(out),
+                                  _stream(stream)), "sd_dense_decode")
 
     def sd_quantize_query(self, q, q8=None, q_group=None, stream=None) -> None:
         check(lib.sd_quantize_query(self.handle, _ptr(q), _ptr(q8), _ptr(q_group), _stream(stream)),

@@ -103,6 +103,16 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
         na = na < 1 ? 1 : na > c->nsplit - 1 ? c->nsplit - 1 : na;
         c->nsplit_a = na;
     }
+    // Dense decode (sd_dense_decode): about 2048 workgroups in all (eight per
+    // compute unit), at most 512 splits per (request, KV head) (the merge's
+    // limit), and at least 32 blocks of the longest request per split.
+    {
+        const int64_t nbmax = (cfg.max_context + 7) / 8;
+        int64_t nd = (2048 + BH - 1) / BH;
+        nd = std::min<int64_t>(nd, 512);
+        nd = std::min<int64_t>(nd, std::max<int64_t>(1, (nbmax + 31) / 32));
+        c->nsplit_d = int(std::max<int64_t>(nd, 1));
+    }
     // Fuse the last stage Q into the kernel of the stage P before it (unless
     // the environment sets SD_FUSE_LAST_STAGE=0).  Possible when Q's chunks
     // are exactly 8 sampled rows (one load slot), Q's stride divides P's (so
@@ -237,7 +247,7 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
     const size_t o_qg = cv.take<int32_t>(BH * sd::kHeadDim);
     const size_t o_blocks = cv.take<uint32_t>(BH * c->max_blocks);
     const size_t o_nblocks = cv.take<int32_t>(BH);
-    const size_t o_part = cv.take<float>(BH * c->nsplit * c->G * (2 + sd::kHeadDim));
+    const size_t o_part = cv.take<float>(BH * size_t(std::max(c->nsplit, c->nsplit_d)) * c->G * (2 + sd::kHeadDim));
     const size_t o_abs = cv.take<unsigned>(BH);
     const size_t o_flag = cv.take<int32_t>(1);
     const size_t o_pre = c->fuse ? cv.take<int32_t>(BH * size_t(c->st[c->S - 2].ncand) * c->fuse_rq) : 0;
@@ -357,7 +367,21 @@ sd_status sd_decode_step_reuse(sd_ctx* c, const uint16_t* q, const uint16_t* k, 
             return sd::launch_attend(c, last_given, fused, q, k, vk, lengths, kept, out, s, t);
         });
     if (e == hipSuccess)
-        e = timed(c, SD_PROF_COMBINE, s, [&](sd::Timing t) { return sd::launch_combine(c, out, s, t); });
+        e = timed(c, SD_PROF_COMBINE, s, [&](sd::Timing t) { return sd::launch_combine(c, c->nsplit, out, s, t); });
+    return from_hip(e);
+}
+
+sd_status sd_dense_decode(sd_ctx* c, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* lengths,
+                          uint16_t* out, void* stream) {
+    if (!c || !q || !k || !v || !lengths || !out) return SD_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SD_ERR_INVALID_ARG;
+    if (c->cfg.values_on_host) return SD_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed(c, SD_PROF_DENSE, s,
+                         [&](sd::Timing t) { return sd::launch_dense(c, q, k, v, lengths, s, t); });
+    if (e == hipSuccess)
+        e = timed(c, SD_PROF_COMBINE, s,
+                  [&](sd::Timing t) { return sd::launch_combine(c, c->nsplit_d, out, s, t); });
     return from_hip(e);
 }
 

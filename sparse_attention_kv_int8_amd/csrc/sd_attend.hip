@@ -252,6 +252,47 @@ __device__ __forceinline__ void decode_blocks(const AttendParams& p, const Src& 
     }
 }
 
+// Merges the four waves' online-softmax states of one workgroup and stores
+// them as split `sp` of (request, KV head) bj: acc at [bj][sp][h][dd] (one
+// contiguous G x 128 slab per workgroup), (m, l) at [bj][sp][h][2] after
+// all acc (nsplit splits per (request, KV head)).
+template <int G>
+__device__ __forceinline__ void write_partials(float* part, int Bh, int nsplit, int bj, int sp, const float (&m)[G],
+                                               const float (&lsum)[G], const float (&acc0)[G], const float (&acc1)[G],
+                                               float (&wm)[kAttnWaves][G], float (&wl)[kAttnWaves][G],
+                                               float (&wacc)[kAttnWaves][G][kHeadDim]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // wave totals: lsum is per token group (identical in its 8 lanes)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float lt = sum_groups_f(lsum[h]);
+        if (lane == 0) { wm[wave][h] = m[h]; wl[wave][h] = lt; }
+        wacc[wave][h][2 * lane] = acc0[h];
+        wacc[wave][h][2 * lane + 1] = acc1[h];
+    }
+    __syncthreads();
+    float* pacc = part + (int64_t(bj) * nsplit + sp) * G * kHeadDim;
+    float* pml = part + int64_t(Bh) * G * kHeadDim * nsplit + (int64_t(bj) * nsplit + sp) * G * 2;
+    for (int o = threadIdx.x; o < G * kHeadDim; o += kAttnThreads) {
+        const int h = o / kHeadDim, dd = o % kHeadDim;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, wm[w][h]);
+        float a = 0.f, l = 0.f;
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w) {
+            const float f = rescale(wm[w][h], M);
+            a = fmaf(wacc[w][h][dd], f, a);
+            l = fmaf(wl[w][h], f, l);
+        }
+        pacc[o] = a;
+        if (dd == 0) {
+            pml[h * 2] = M;
+            pml[h * 2 + 1] = l;
+        }
+    }
+}
+
 // One instantiation per (group size, values on host, select code of the
 // last stage (kGiven: reused, read from kept_idx; unused with host values),
 // select code of the stage before
@@ -346,37 +387,7 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
                                 acc0, acc1, tblk, tmask);
     }
 
-    // wave totals: lsum is per token group (identical in its 8 lanes)
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const float lt = sum_groups_f(lsum[h]);
-        if (lane == 0) { wm[wave][h] = m[h]; wl[wave][h] = lt; }
-        wacc[wave][h][2 * lane] = acc0[h];
-        wacc[wave][h][2 * lane + 1] = acc1[h];
-    }
-    __syncthreads();
-    // partials: acc at [bj][split][h][dd] (each workgroup writes one
-    // contiguous G x 128 slab), (m, l) at [bj][split][h][2] after all acc
-    float* pacc = p.part + (int64_t(bj) * p.nsplit + sp) * G * kHeadDim;
-    float* pml = p.part + int64_t(p.Bh) * G * kHeadDim * p.nsplit + (int64_t(bj) * p.nsplit + sp) * G * 2;
-    for (int o = threadIdx.x; o < G * kHeadDim; o += kAttnThreads) {
-        const int h = o / kHeadDim, dd = o % kHeadDim;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, wm[w][h]);
-        float a = 0.f, l = 0.f;
-#pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w) {
-            const float f = rescale(wm[w][h], M);
-            a = fmaf(wacc[w][h][dd], f, a);
-            l = fmaf(wl[w][h], f, l);
-        }
-        pacc[o] = a;
-        if (dd == 0) {
-            pml[h * 2] = M;
-            pml[h * 2 + 1] = l;
-        }
-    }
+    write_partials<G>(p.part, p.Bh, p.nsplit, bj, sp, m, lsum, acc0, acc1, wm, wl, wacc);
     if (!HOSTV && kept_n >= 0) {
         // the last stage's kept set (ascending, -1 padded), stored last so
         // that no barrier waits on these stores; fused: also the previous
@@ -395,6 +406,76 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
     }
 }
 
+// Dense decode over every token t < L, the comparison path of
+// sd_dense_decode.  Workgroup (split, KV head, request) takes a contiguous
+// run of 8-token blocks; wave w takes blocks w, w + 4, w + 8, ... of the run
+// and keeps four blocks in flight: it issues the loads of the next pair
+// before it attends the current pair, so the block loop never waits on a
+// load issued in the same iteration.  Loads, scores and the online softmax
+// are the sparse decode's (load_block, attend_block); only the block source
+// differs (every block, masked to t < L).
+template <int G>
+__global__ __launch_bounds__(kAttnThreads) void sd_dense_decode_kernel(AttendParams p) {
+    __shared__ float wm[kAttnWaves][G];
+    __shared__ float wl[kAttnWaves][G];
+    __shared__ float wacc[kAttnWaves][G][kHeadDim];
+
+    const int sp = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    const int bj = b * p.Hkv + j;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sl = lane & 7;
+    const int64_t Lraw = p.lengths[b];
+    const bool bad = Lraw < 1 || Lraw > p.Lmax;
+    const int L = bad ? 0 : int(Lraw);
+    if (bad && sp == 0 && j == 0 && threadIdx.x == 0) atomicOr(p.flag, 1);
+
+    uint32_t qv[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const u32x4* qp = reinterpret_cast<const u32x4*>(p.q + (int64_t(b) * p.Hq + j * G + h) * kHeadDim + sl * 16);
+        const u32x4 a = qp[0], c = qp[1];
+        qv[h][0] = a.x; qv[h][1] = a.y; qv[h][2] = a.z; qv[h][3] = a.w;
+        qv[h][4] = c.x; qv[h][5] = c.y; qv[h][6] = c.z; qv[h][7] = c.w;
+    }
+    float m[G], lsum[G], acc0[G], acc1[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) { m[h] = -INFINITY; lsum[h] = 0.f; acc0[h] = 0.f; acc1[h] = 0.f; }
+
+    const uint16_t* kbase = p.k + int64_t(bj) * p.Lmax * kHeadDim;
+    const uint16_t* vbase = p.v + int64_t(bj) * p.Lmax * kHeadDim;
+    const int nb = (L + 7) >> 3;
+    // whole groups of 2 x 4 blocks per split, so every wave gets pairs
+    constexpr int kGrp = 2 * kAttnWaves;
+    const int per = ((nb + p.nsplit - 1) / p.nsplit + kGrp - 1) / kGrp * kGrp;
+    const int r0 = min(nb, sp * per), r1 = min(nb, r0 + per);
+
+    // wave-uniform block indices; a block at or past r1 is neither loaded nor attended
+    int r = r0 + wave;
+    BlockData a0, a1, b0, b1;
+    if (r < r1) load_block<false>(p, r, r * 8, valid_mask8(r, L), bj, L, kbase, vbase, a0);
+    if (r + kAttnWaves < r1)
+        load_block<false>(p, r + kAttnWaves, (r + kAttnWaves) * 8, valid_mask8(r + kAttnWaves, L), bj, L, kbase,
+                          vbase, a1);
+    for (; r < r1; r += 2 * kGrp) {
+        const int rb = r + kGrp;
+        if (rb < r1) load_block<false>(p, rb, rb * 8, valid_mask8(rb, L), bj, L, kbase, vbase, b0);
+        if (rb + kAttnWaves < r1)
+            load_block<false>(p, rb + kAttnWaves, (rb + kAttnWaves) * 8, valid_mask8(rb + kAttnWaves, L), bj, L,
+                              kbase, vbase, b1);
+        attend_block<G>(a0, qv, p.scale_log2, m, lsum, acc0, acc1);
+        if (r + kAttnWaves < r1) attend_block<G>(a1, qv, p.scale_log2, m, lsum, acc0, acc1);
+        if (rb >= r1) break;
+        const int ra = rb + kGrp;
+        if (ra < r1) load_block<false>(p, ra, ra * 8, valid_mask8(ra, L), bj, L, kbase, vbase, a0);
+        if (ra + kAttnWaves < r1)
+            load_block<false>(p, ra + kAttnWaves, (ra + kAttnWaves) * 8, valid_mask8(ra + kAttnWaves, L), bj, L,
+                              kbase, vbase, a1);
+        attend_block<G>(b0, qv, p.scale_log2, m, lsum, acc0, acc1);
+        if (rb + kAttnWaves < r1) attend_block<G>(b1, qv, p.scale_log2, m, lsum, acc0, acc1);
+    }
+    write_partials<G>(p.part, p.Bh, p.nsplit, bj, sp, m, lsum, acc0, acc1, wm, wl, wacc);
+}
+
 // Log-sum-exp merge of the splits, rounding to bf16.  A workgroup merges 64
 // outputs of one head: thread t reads float4 q = t % 16 of those outputs from
 // splits t / 16, t / 16 + 16, ... (each split's 64 values are one contiguous
@@ -402,12 +483,19 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
 // wave 0 meanwhile computes the head's split weights
 // exp2(m_s - M) / sum_s l_s exp2(m_s - M); each thread sums its splits
 // weighted, and the 16 split groups are added through LDS.
+// MAXS is the largest split count an instantiation merges: 64 for the
+// sparse decode (one split per lane of the weight pass), up to 512 for the
+// dense decode (the weight pass loops over 64 splits at a time).
 constexpr int kMaxSplit = 64;
+constexpr int kMaxSplitDense = 512;
 constexpr int kCombOut = 64;                 // outputs per combine workgroup
 constexpr int kCombGroups = kAttnThreads / (kCombOut / 4);   // 16 split groups
 
+template <int MAXS>
 __global__ __launch_bounds__(kAttnThreads) void sd_combine_kernel(const float* __restrict__ part, int nsplit, int Bh,
                                                                  int G, int Hq, int Hkv, uint16_t* __restrict__ out) {
+    static_assert(MAXS % kWave == 0 && MAXS % kCombGroups == 0, "combine split layout");
+    constexpr int kMaxSplit = MAXS;
     __shared__ float wgt[kMaxSplit];
     __shared__ float4 red[kCombGroups][kCombOut / 4];
     const int j = blockIdx.y, b = blockIdx.z, bj = b * Hkv + j;
@@ -425,12 +513,29 @@ __global__ __launch_bounds__(kAttnThreads) void sd_combine_kernel(const float* _
     }
     if (threadIdx.x < kWave) {
         const int lane = threadIdx.x;
-        const float m = lane < nsplit ? pml[lane * G * 2] : -INFINITY;
-        const float l = lane < nsplit ? pml[lane * G * 2 + 1] : 0.f;
-        const float M = wave_max_f(m);
-        const float f = rescale(m, M);
-        const float Lt = wave_sum_f(l * f);
-        wgt[lane] = (lane < nsplit && Lt > 0.f) ? f / Lt : 0.f;
+        constexpr int kW = kMaxSplit / kWave;    // splits per lane
+        float m[kW], l[kW];
+        float M = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kW; ++i) {
+            const int s = lane + kWave * i;
+            m[i] = s < nsplit ? pml[s * G * 2] : -INFINITY;
+            l[i] = s < nsplit ? pml[s * G * 2 + 1] : 0.f;
+            M = fmaxf(M, m[i]);
+        }
+        M = wave_max_f(M);
+        float f[kW], Lp = 0.f;
+#pragma unroll
+        for (int i = 0; i < kW; ++i) {
+            f[i] = rescale(m[i], M);
+            Lp = fmaf(l[i], f[i], Lp);
+        }
+        const float Lt = wave_sum_f(Lp);
+#pragma unroll
+        for (int i = 0; i < kW; ++i) {
+            const int s = lane + kWave * i;
+            wgt[s] = (s < nsplit && Lt > 0.f) ? f[i] / Lt : 0.f;
+        }
     }
     __syncthreads();
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -536,13 +641,43 @@ hipError_t launch_attend(sd_ctx* c, bool given, bool fused, const uint16_t* q, c
 
 namespace sd {
 
-hipError_t launch_combine(sd_ctx* c, uint16_t* out, hipStream_t s, Timing t) {
+hipError_t launch_combine(sd_ctx* c, int nsplit, uint16_t* out, hipStream_t s, Timing t) {
     const int G = c->G;
     dim3 grid(G * kHeadDim / kCombOut, c->cfg.num_kv_heads, c->cfg.batch), block(kAttnThreads);
-    static_assert(kAttnThreads % (kCombOut / 4) == 0 && kMaxSplit % kCombGroups == 0, "combine thread layout");
+    static_assert(kAttnThreads % (kCombOut / 4) == 0 && kMaxSplitDense % kCombGroups == 0, "combine thread layout");
     static_assert(kHeadDim % kCombOut == 0, "a combine workgroup stays within one head");
-    launch(sd_combine_kernel, grid, block, 0, s, t, static_cast<const float*>(c->part), c->nsplit,
-           c->cfg.batch * c->cfg.num_kv_heads, G, c->cfg.num_q_heads, c->cfg.num_kv_heads, out);
+    const int Bh = c->cfg.batch * c->cfg.num_kv_heads;
+    const float* part = c->part;
+    if (nsplit <= kMaxSplit)
+        launch(sd_combine_kernel<kMaxSplit>, grid, block, 0, s, t, part, nsplit, Bh, G, c->cfg.num_q_heads,
+               c->cfg.num_kv_heads, out);
+    else
+        launch(sd_combine_kernel<kMaxSplitDense>, grid, block, 0, s, t, part, nsplit, Bh, G, c->cfg.num_q_heads,
+               c->cfg.num_kv_heads, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense(sd_ctx* c, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* lengths,
+                        hipStream_t s, Timing t) {
+    AttendParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.lengths = lengths;
+    p.flag = c->flag;
+    p.part = c->part;
+    p.nsplit = c->nsplit_d;
+    p.Bh = c->cfg.batch * c->cfg.num_kv_heads;
+    p.Lmax = c->Lmax;
+    p.Hq = c->cfg.num_q_heads;
+    p.Hkv = c->cfg.num_kv_heads;
+    p.scale_log2 = c->scale_log2;
+    const dim3 grid(c->nsplit_d, c->cfg.num_kv_heads, c->cfg.batch), block(kAttnThreads);
+    switch (c->G) {
+        case 1: launch(sd_dense_decode_kernel<1>, grid, block, 0, s, t, p); break;
+        case 2: launch(sd_dense_decode_kernel<2>, grid, block, 0, s, t, p); break;
+        default: launch(sd_dense_decode_kernel<4>, grid, block, 0, s, t, p); break;
+    }
     return hipGetLastError();
 }
 

@@ -60,6 +60,7 @@ struct sd_ctx {
     int max_blocks;         // attended 8-token blocks per (request, KV head)
     int nsplit;             // flash-decode splits per (request, KV head)
     int nsplit_a;           // of which cover the sink/window blocks (device values only)
+    int nsplit_d;           // splits per (request, KV head) of the dense decode (sd_dense_decode)
     float scale_log2;       // softmax_scale * log2(e)
     sd::StageGeom st[SD_MAX_STAGES];
     size_t select_lds;      // dynamic LDS bytes of the stage kernels
@@ -71,7 +72,8 @@ struct sd_ctx {
     int32_t* qgroup;                  // [B][Hkv][d] group query sums
     uint32_t* blocks;                 // [B][Hkv][max_blocks] (block << 8) | token mask
     int32_t* nblocks;                 // [B][Hkv]
-    float* part;                      // acc [B*Hkv][nsplit][G][d], then (m, l) [B*Hkv][nsplit][G][2]
+    float* part;                      // acc [B*Hkv][n][G][d], then (m, l) [B*Hkv][n][G][2], n = the
+                                      // launch's splits (nsplit, or nsplit_d for the dense decode)
     // fused last stage: the kernel of stage S-2 also scores every child chunk
     // of every stage S-2 candidate for stage S-1 (reading all rows stage S-1
     // samples), and the decode kernel selects stage S-2, gathers the kept
@@ -124,7 +126,12 @@ hipError_t launch_prune_stage(sd_ctx* c, int stage, bool given, bool fused, cons
                               const int32_t* lengths, int32_t* kept, hipStream_t s, Timing t = {});
 hipError_t launch_attend(sd_ctx* c, bool given, bool fused, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const int32_t* lengths, int32_t* kept, uint16_t* out, hipStream_t s, Timing t = {});
-hipError_t launch_combine(sd_ctx* c, uint16_t* out, hipStream_t s, Timing t = {});
+// Merges `nsplit` split partials per (request, KV head) into the bf16 output.
+hipError_t launch_combine(sd_ctx* c, int nsplit, uint16_t* out, hipStream_t s, Timing t = {});
+// Dense decode over every token t < L_b (split partials; launch_combine
+// with c->nsplit_d merges them).
+hipError_t launch_dense(sd_ctx* c, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* lengths,
+                        hipStream_t s, Timing t = {});
 hipError_t launch_value_cache_update(sd_ctx* c, bool given, const int32_t* lengths, int32_t* kept, hipStream_t s,
                                      Timing t = {});
 hipError_t launch_value_cache_reset(sd_ctx* c, hipStream_t s);

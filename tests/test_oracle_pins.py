@@ -348,6 +348,40 @@ def test_full_budgets_equal_dense_attention():
     assert np.max(np.abs(res.psum - 1)) < 1e-12
 
 
+def test_dense_attention_matches_library_sdpa():
+    """The oracle's dense attention against an independent implementation:
+    torch's CPU scaled_dot_product_attention in fp64 (GQA heads expanded
+    by hand), on random bf16-valued inputs with lengths that are not
+    multiples of 8."""
+    import torch
+    rng = np.random.default_rng(31)
+    for L in (1, 7, 333, 2049):
+        q = rng.standard_normal((4, 128))
+        k = rng.standard_normal((L, 128)) * 2.0
+        v = rng.standard_normal((L, 128))
+        lib = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None, :, None, :], torch.from_numpy(k)[None, None].expand(1, 4, L, 128),
+            torch.from_numpy(v)[None, None].expand(1, 4, L, 128), scale=1 / np.sqrt(128))[0, :, 0].numpy()
+        for h in range(4):
+            ours = O.dense_attention(q[h], k, v, 1 / np.sqrt(128))
+            assert np.max(np.abs(ours - lib[h])) < 1e-12
+
+
+def test_dense_attention_closed_forms():
+    """Equal keys give the mean of the values; two tokens give the logistic
+    weight sigma(z0 - z1) on the first."""
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal(128)
+    v = rng.standard_normal((9, 128))
+    k = np.tile(rng.standard_normal(128), (9, 1))
+    assert np.max(np.abs(O.dense_attention(q, k, v, 0.3) - v.mean(axis=0))) < 1e-13
+    k2 = rng.standard_normal((2, 128))
+    z = 0.1 * (k2 @ q)
+    p0 = 1.0 / (1.0 + np.exp(z[1] - z[0]))
+    want = p0 * v[0] + (1 - p0) * v[1]
+    assert np.max(np.abs(O.dense_attention(q, k2, v[:2], 0.1) - want)) < 1e-13
+
+
 def test_length_one_returns_the_value():
     q, k, v = _tiny_inputs(1, seed=3)
     res, _ = _run_oracle(q, k, v, 1, [(256, 8, 16), (32, 2, 32), (8, 1, 64)], 64, 512)
