@@ -103,16 +103,6 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
         na = na < 1 ? 1 : na > c->nsplit - 1 ? c->nsplit - 1 : na;
         c->nsplit_a = na;
     }
-    // Dense decode (sd_dense_decode): about 2048 workgroups in all (eight per
-    // compute unit), at most 512 splits per (request, KV head) (the merge's
-    // limit), and at least 32 blocks of the longest request per split.
-    {
-        const int64_t nbmax = (cfg.max_context + 7) / 8;
-        int64_t nd = (2048 + BH - 1) / BH;
-        nd = std::min<int64_t>(nd, 512);
-        nd = std::min<int64_t>(nd, std::max<int64_t>(1, (nbmax + 31) / 32));
-        c->nsplit_d = int(std::max<int64_t>(nd, 1));
-    }
     // Fuse the last stage Q into the kernel of the stage P before it (unless
     // the environment sets SD_FUSE_LAST_STAGE=0).  Possible when Q's chunks
     // are exactly 8 sampled rows (one load slot), Q's stride divides P's (so
@@ -238,6 +228,25 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
                                                                  sd::stage_dev(c, c->S - 1), c->fuse_rq));
         const int64_t static_bytes = 4 * (4 * (2 + sd::kHeadDim) * c->G + 64);
         if (words * 4 + static_bytes > lds_max) { delete c; return SD_ERR_UNSUPPORTED; }
+        // Dense decode (sd_dense_decode): 8 workgroups per compute unit in
+        // all (about 2.7 times the kernel's resident occupancy of 3, which
+        // measured faster than one resident wave of workgroups at 128K and
+        // 1M; SD_DENSE_WG_PER_CU overrides the 8), at most 512 splits per
+        // (request, KV head) (the merge's limit), at least 32 blocks of the
+        // longest request per split.
+        int cus = 0, occ = 8;
+        e0 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->device);
+        if (e0 != hipSuccess) { delete c; return from_hip(e0, "hipDeviceGetAttribute"); }
+        if (const char* env = std::getenv("SD_DENSE_WG_PER_CU")) {
+            const int o = std::atoi(env);
+            if (o >= 1 && o <= 64) occ = o;
+        }
+        const int64_t BH = int64_t(cfg->batch) * cfg->num_kv_heads;
+        const int64_t nbmax = (cfg->max_context + 7) / 8;
+        int64_t nd = (int64_t(std::max(cus, 1)) * std::max(occ, 1) + BH - 1) / BH;
+        nd = std::min<int64_t>(nd, 512);
+        nd = std::min<int64_t>(nd, std::max<int64_t>(1, (nbmax + 31) / 32));
+        c->nsplit_d = int(std::max<int64_t>(nd, 1));
     }
 
     const size_t B = size_t(cfg->batch), H = size_t(cfg->num_kv_heads), BH = B * H;
