@@ -58,7 +58,8 @@ from sparse_attention_kv_int8_amd.inputs import WORKLOADS, make_inputs, make_que
 
 METRIC = "sparse decode-attention µs/step + achieved HBM GB/s at 128K and 1M ctx (GQA 32/8)"
 HBM_PEAK_GBS = 8000.0
-KIND_NAMES = ["stage0", "stage1", "stage2", "stage3", "value_cache", "attend", "quantize", "combine", "dense"]
+KIND_NAMES = ["stage0", "stage1", "stage2", "stage3", "value_cache", "attend", "quantize", "combine", "dense",
+              "append"]
 
 
 def log(*a):

@@ -135,6 +135,33 @@ const char* sd_last_error(void);
 sd_status sd_quantize_keys(sd_ctx* ctx, const uint16_t* k_bf16, const int32_t* lengths,
                            int8_t* k_int8, float* k_absmax, void* stream);
 
+/* Appends n_new tokens per request to the caches, as a decode loop does
+ * after each step (the pages keep the cache growing by one token per decode
+ * step: page "KV Cache 与长上下文推理", section "KV Cache 回顾"; they say
+ * nothing of how a quantised cache's scale follows that growth).  The key
+ * scale is a running absmax: the new keys of (request b, KV head j) are
+ * coded with a' = max(a_bj, absmax of the new keys), and when a' > a_bj
+ * every earlier row of that (b, j) is recoded with a' on the device.  So
+ * after the call the codes and scales equal what sd_quantize_keys gives for
+ * the grown cache (t < L_b + n_new), bit for bit.  a_bj is the scale this
+ * context holds for the cache: the one sd_quantize_keys (or an earlier
+ * sd_append_kv) on this context computed; the call continues that cache.
+ *  k_new    device [B][Hkv][n_new][d] bf16 new keys.
+ *  v_new    device [B][Hkv][n_new][d] bf16 new values.
+ *  n_new    tokens per request, in [1, Lmax].
+ *  lengths  device [B] int32: the lengths L_b BEFORE the append (not
+ *           modified: the caller passes L_b + n_new to the next call).
+ *  k_bf16, k_int8, v  device caches ([B][Hkv][Lmax][d]); rows
+ *           [L_b, L_b + n_new) are written (all rows t < L_b + n_new of
+ *           k_int8 when the scale grew).
+ *  k_absmax device [B][Hkv] fp32 output a', or NULL.
+ * A request with L_b < 1 or L_b + n_new > Lmax is left untouched and
+ * raises the device flag (see sd_check).  Needs values_on_host = 0 (else
+ * SD_ERR_UNSUPPORTED).  Allocates nothing. */
+sd_status sd_append_kv(sd_ctx* ctx, const uint16_t* k_new, const uint16_t* v_new, int32_t n_new,
+                       const int32_t* lengths, uint16_t* k_bf16, int8_t* k_int8, uint16_t* v,
+                       float* k_absmax, void* stream);
+
 /* One decode step (parts 2 and 3).
  *  q        device [B][Hq][d] bf16 query of the step.
  *  k_bf16   device [B][Hkv][Lmax][d] bf16 keys (exact attention).
@@ -234,7 +261,8 @@ enum {
     SD_PROF_QUANTIZE = 6,       /* the three kernels of sd_quantize_keys, as one interval */
     SD_PROF_COMBINE = 7,        /* log-sum-exp merge of the splits into the bf16 output */
     SD_PROF_DENSE = 8,          /* dense flash decode of sd_dense_decode (partials; its merge is COMBINE) */
-    SD_PROF_KINDS = 9
+    SD_PROF_APPEND = 9,         /* the two kernels of sd_append_kv, as one interval */
+    SD_PROF_KINDS = 10
 };
 
 typedef struct sd_profile {

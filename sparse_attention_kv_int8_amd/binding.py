@@ -40,9 +40,11 @@ class sd_config(C.Structure):
     ]
 
 
-SD_PROF_KINDS = 9
-SD_PROF_STAGE0, SD_PROF_VALUE_CACHE, SD_PROF_ATTEND, SD_PROF_QUANTIZE, SD_PROF_COMBINE, SD_PROF_DENSE = 0, 4, 5, 6, 7, 8
-PROF_NAMES = ["stage0", "stage1", "stage2", "stage3", "value_cache", "attend", "quantize", "combine", "dense"]
+SD_PROF_KINDS = 10
+SD_PROF_STAGE0, SD_PROF_VALUE_CACHE, SD_PROF_ATTEND, SD_PROF_QUANTIZE = 0, 4, 5, 6
+SD_PROF_COMBINE, SD_PROF_DENSE, SD_PROF_APPEND = 7, 8, 9
+PROF_NAMES = ["stage0", "stage1", "stage2", "stage3", "value_cache", "attend", "quantize", "combine", "dense",
+              "append"]
 
 
 class sd_profile(C.Structure):
@@ -73,6 +75,7 @@ _SIGS = {
     "sd_decode_step": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "sd_decode_step_reuse": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, C.c_int32, _p]),
     "sd_dense_decode": (C.c_int, [_p, _p, _p, _p, _p, _p, _p]),
+    "sd_append_kv": (C.c_int, [_p, _p, _p, C.c_int32, _p, _p, _p, _p, _p, _p]),
     "sd_quantize_query": (C.c_int, [_p, _p, _p, _p, _p]),
     "sd_stage_scores": (C.c_int, [_p, C.c_int32, _p, C.c_int64, _p]),
     "sd_stage_candidates": (C.c_int64, [_p, C.c_int32]),
@@ -188,6 +191,10 @@ class SparseDecoder:
     def sd_dense_decode(self, q, k, v, lengths, out, stream=None) -> None:
         check(lib.sd_dense_decode(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(lengths), _ptr(out),
                                   _stream(stream)), "sd_dense_decode")
+
+    def sd_append_kv(self, k_new, v_new, n_new: int, lengths, k, k_int8, v, k_absmax=None, stream=None) -> None:
+        check(lib.sd_append_kv(self.handle, _ptr(k_new), _ptr(v_new), int(n_new), _ptr(lengths), _ptr(k),
+                               _ptr(k_int8), _ptr(v), _ptr(k_absmax), _stream(stream)), "sd_append_kv")
 
     def sd_quantize_query(self, q, q8=None, q_group=None, stream=None) -> None:
         check(lib.sd_quantize_query(self.handle, _ptr(q), _ptr(q8), _ptr(q_group), _stream(stream)),

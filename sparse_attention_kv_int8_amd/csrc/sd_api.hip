@@ -258,6 +258,7 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
     const size_t o_nblocks = cv.take<int32_t>(BH);
     const size_t o_part = cv.take<float>(BH * size_t(std::max(c->nsplit, c->nsplit_d)) * c->G * (2 + sd::kHeadDim));
     const size_t o_abs = cv.take<unsigned>(BH);
+    const size_t o_req = cv.take<int32_t>(BH);
     const size_t o_flag = cv.take<int32_t>(1);
     const size_t o_pre = c->fuse ? cv.take<int32_t>(BH * size_t(c->st[c->S - 2].ncand) * c->fuse_rq) : 0;
     size_t o_vc[10] = {0};
@@ -284,6 +285,7 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
     c->nblocks = reinterpret_cast<int32_t*>(base + o_nblocks);
     c->part = reinterpret_cast<float*>(base + o_part);
     c->absmax_bits = reinterpret_cast<unsigned*>(base + o_abs);
+    c->requant = reinterpret_cast<int32_t*>(base + o_req);
     c->flag = reinterpret_cast<int32_t*>(base + o_flag);
     c->pre = c->fuse ? reinterpret_cast<int32_t*>(base + o_pre) : nullptr;
     if (cfg->values_on_host) {
@@ -325,6 +327,19 @@ sd_status sd_quantize_keys(sd_ctx* c, const uint16_t* k, const int32_t* lengths,
     hipStream_t s = static_cast<hipStream_t>(stream);
     return from_hip(timed(c, SD_PROF_QUANTIZE, s,
                           [&](sd::Timing t) { return sd::launch_quantize_keys(c, k, lengths, k8, absmax, s, t); }));
+}
+
+sd_status sd_append_kv(sd_ctx* c, const uint16_t* k_new, const uint16_t* v_new, int32_t n_new, const int32_t* lengths,
+                       uint16_t* k, int8_t* k8, uint16_t* v, float* absmax, void* stream) {
+    if (!c || !k_new || !v_new || !lengths || !k || !k8 || !v) return SD_ERR_INVALID_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k) || !aligned16(k8) || !aligned16(v))
+        return SD_ERR_INVALID_ARG;
+    if (n_new < 1 || n_new > c->Lmax) return SD_ERR_INVALID_ARG;
+    if (c->cfg.values_on_host) return SD_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return from_hip(timed(c, SD_PROF_APPEND, s, [&](sd::Timing t) {
+        return sd::launch_append(c, k_new, v_new, n_new, lengths, k, k8, v, absmax, s, t);
+    }));
 }
 
 sd_status sd_quantize_query(sd_ctx* c, const uint16_t* q, int8_t* q8, int32_t* qg, void* stream) {

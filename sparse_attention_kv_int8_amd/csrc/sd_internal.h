@@ -82,7 +82,8 @@ struct sd_ctx {
     int fuse_rq;                      // children per stage S-2 chunk
     int fuse_m;                       // stage S-2 stride / stage S-1 stride
     int32_t* pre;                     // [B][Hkv][st[S-2].ncand * fuse_rq] children's stage S-1 scores
-    unsigned* absmax_bits;            // [B][Hkv]
+    unsigned* absmax_bits;            // [B][Hkv] bf16 bits of each key scale (sd_quantize_keys, sd_append_kv)
+    int32_t* requant;                 // [B][Hkv] set by sd_append_kv when the scale grew
     int32_t* flag;                    // device error flag
     sd::ValueCache vc;
     int64_t vc_step;                  // steps applied to the value cache since its reset
@@ -116,6 +117,10 @@ inline void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, 
 
 hipError_t launch_quantize_keys(sd_ctx* c, const uint16_t* k, const int32_t* lengths, int8_t* k8,
                                 float* absmax, hipStream_t s, Timing t = {});
+// Appends n rows per (request, KV head) at lengths[b] and recodes the rows of
+// the (request, KV head)s whose key scale grew.
+hipError_t launch_append(sd_ctx* c, const uint16_t* k_new, const uint16_t* v_new, int n, const int32_t* lengths,
+                         uint16_t* k, int8_t* k8, uint16_t* v, float* absmax, hipStream_t s, Timing t = {});
 hipError_t launch_quantize_query(sd_ctx* c, const uint16_t* q, int8_t* q8, int32_t* qg, hipStream_t s);
 // given: the kept set that the launch would select (stage - 1's for a
 // pruning stage, the last stage's for the decode and value-cache kernels)

@@ -9,6 +9,8 @@
 // Both passes stream the bf16 cache with 16-byte loads, 16 lanes per
 // 256-byte row.  The absmax pass works on bf16 bit patterns (|x| ordering is
 // the ordering of the low 15 bits for finite values).
+#include <algorithm>
+
 #include "sd_device.h"
 #include "sd_internal.h"
 
@@ -79,28 +81,90 @@ __device__ __forceinline__ uint2 codes8(u32x4 w, float a) {
     return r;
 }
 
+// Codes of rows [0, lengths[b] + len_add) with the stored scale; workgroup
+// x takes row tiles x, x + gridDim.x, ...  With `only` set, a (request, KV
+// head) whose only[bj] is 0 is skipped (the append's requantisation).
 __global__ __launch_bounds__(kQuantThreads) void sd_quantize_kernel(
-    const uint16_t* __restrict__ k, const int32_t* __restrict__ lengths, int64_t Lmax, int Hkv,
-    const unsigned* __restrict__ absmax_bits, int8_t* __restrict__ k8, float* __restrict__ absmax_out) {
+    const uint16_t* __restrict__ k, const int32_t* __restrict__ lengths, int len_add, int64_t Lmax, int Hkv,
+    const unsigned* __restrict__ absmax_bits, const int32_t* __restrict__ only, int8_t* __restrict__ k8,
+    float* __restrict__ absmax_out) {
     const int bj = blockIdx.y, b = bj / Hkv;
-    const int64_t L = lengths[b];
+    if (only && only[bj] == 0) return;
+    const int64_t L = int64_t(lengths[b]) + len_add;
     if (L < 1 || L > Lmax) return;
     const float a = bf16_to_f32(uint16_t(absmax_bits[bj]));
     if (absmax_out && blockIdx.x == 0 && threadIdx.x == 0) absmax_out[bj] = a;
-    const int64_t r0 = int64_t(blockIdx.x) * kQuantRowsPerWg;
-    const int64_t r1 = min(r0 + kQuantRowsPerWg, L);
-    if (r0 >= r1) return;
     const u32x4* src = reinterpret_cast<const u32x4*>(k + int64_t(bj) * Lmax * kHeadDim);
     uint2* dst = reinterpret_cast<uint2*>(k8 + int64_t(bj) * Lmax * kHeadDim);
-    const int64_t e0 = r0 * 16, e1 = r1 * 16;
-    int64_t e = e0 + threadIdx.x;
-    for (; e + kQuantThreads < e1; e += 2 * kQuantThreads) {
-        u32x4 w0 = __builtin_nontemporal_load(src + e);
-        u32x4 w1 = __builtin_nontemporal_load(src + e + kQuantThreads);
-        dst[e] = codes8(w0, a);
-        dst[e + kQuantThreads] = codes8(w1, a);
+    for (int64_t r0 = int64_t(blockIdx.x) * kQuantRowsPerWg; r0 < L; r0 += int64_t(gridDim.x) * kQuantRowsPerWg) {
+        const int64_t r1 = min(r0 + kQuantRowsPerWg, L);
+        const int64_t e0 = r0 * 16, e1 = r1 * 16;
+        int64_t e = e0 + threadIdx.x;
+        for (; e + kQuantThreads < e1; e += 2 * kQuantThreads) {
+            u32x4 w0 = __builtin_nontemporal_load(src + e);
+            u32x4 w1 = __builtin_nontemporal_load(src + e + kQuantThreads);
+            dst[e] = codes8(w0, a);
+            dst[e + kQuantThreads] = codes8(w1, a);
+        }
+        for (; e < e1; e += kQuantThreads) dst[e] = codes8(src[e], a);
     }
-    for (; e < e1; e += kQuantThreads) dst[e] = codes8(src[e], a);
+}
+
+// Appends n rows per (request, KV head) at t = L_b .. L_b + n - 1: copies
+// the new bf16 keys and values into the caches and codes the new keys with
+// a' = max(a, absmax of the new keys), a being the scale stored for the
+// cache.  Stores a' and sets requant[bj] when a' > a (the earlier rows are
+// then recoded by sd_quantize_kernel with `only` = requant).  One workgroup
+// per (request, KV head), so the scale is read and written by one
+// workgroup.  A request with L_b < 1 or L_b + n > Lmax is left untouched and
+// raises the flag.
+__global__ __launch_bounds__(kQuantThreads) void sd_append_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, int n,
+    const int32_t* __restrict__ lengths, int64_t Lmax, int Hkv, uint16_t* __restrict__ k, int8_t* __restrict__ k8,
+    uint16_t* __restrict__ v, unsigned* __restrict__ absmax_bits, int32_t* __restrict__ requant,
+    float* __restrict__ absmax_out, int32_t* __restrict__ flag) {
+    const int j = blockIdx.x, b = blockIdx.y, bj = b * Hkv + j;
+    const int64_t L = lengths[b];
+    if (L < 1 || L > Lmax - n) {
+        if (threadIdx.x == 0) {
+            requant[bj] = 0;
+            if (j == 0) atomicOr(flag, 1);
+        }
+        return;
+    }
+    const u32x4* ks = reinterpret_cast<const u32x4*>(k_new + int64_t(bj) * n * kHeadDim);
+    const u32x4* vs = reinterpret_cast<const u32x4*>(v_new + int64_t(bj) * n * kHeadDim);
+    const int64_t ne = int64_t(n) * 16;        // 16 u32x4 per row
+    unsigned m = 0;
+    for (int64_t e = threadIdx.x; e < ne; e += kQuantThreads) {
+        const u32x4 w = ks[e];
+        m = max(m, max(max(abs_bits2(w.x), abs_bits2(w.y)), max(abs_bits2(w.z), abs_bits2(w.w))));
+    }
+    m = wave_max_u(m);
+    __shared__ unsigned red[kQuantThreads / kWave];
+    __shared__ unsigned anew;
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned r = absmax_bits[bj];
+        const unsigned old = r;
+        for (int i = 0; i < kQuantThreads / kWave; ++i) r = max(r, red[i]);
+        absmax_bits[bj] = r;
+        requant[bj] = r > old ? 1 : 0;
+        if (absmax_out) absmax_out[bj] = bf16_to_f32(uint16_t(r));
+        anew = r;
+    }
+    __syncthreads();
+    const float a = bf16_to_f32(uint16_t(anew));
+    u32x4* kd = reinterpret_cast<u32x4*>(k + (int64_t(bj) * Lmax + L) * kHeadDim);
+    u32x4* vd = reinterpret_cast<u32x4*>(v + (int64_t(bj) * Lmax + L) * kHeadDim);
+    uint2* k8d = reinterpret_cast<uint2*>(k8 + (int64_t(bj) * Lmax + L) * kHeadDim);
+    for (int64_t e = threadIdx.x; e < ne; e += kQuantThreads) {
+        const u32x4 w = ks[e];
+        kd[e] = w;
+        k8d[e] = codes8(w, a);
+        vd[e] = vs[e];
+    }
 }
 
 }  // namespace
@@ -127,8 +191,24 @@ hipError_t launch_quantize_keys(sd_ctx* c, const uint16_t* k, const int32_t* len
     dim3 grid(nwg, BH);
     launch(sd_absmax_kernel, grid, dim3(kQuantThreads), 0, s, Timing{}, k, lengths, c->Lmax,
            c->cfg.num_kv_heads, c->absmax_bits, c->flag);
-    launch(sd_quantize_kernel, grid, dim3(kQuantThreads), 0, s, Timing{nullptr, t.stop}, k, lengths, c->Lmax,
-           c->cfg.num_kv_heads, (const unsigned*)c->absmax_bits, k8, absmax);
+    launch(sd_quantize_kernel, grid, dim3(kQuantThreads), 0, s, Timing{nullptr, t.stop}, k, lengths, 0, c->Lmax,
+           c->cfg.num_kv_heads, (const unsigned*)c->absmax_bits, (const int32_t*)nullptr, k8, absmax);
+    return hipGetLastError();
+}
+
+hipError_t launch_append(sd_ctx* c, const uint16_t* k_new, const uint16_t* v_new, int n, const int32_t* lengths,
+                         uint16_t* k, int8_t* k8, uint16_t* v, float* absmax, hipStream_t s, Timing t) {
+    const int BH = c->cfg.batch * c->cfg.num_kv_heads;
+    launch(sd_append_kernel, dim3(c->cfg.num_kv_heads, c->cfg.batch), dim3(kQuantThreads), 0, s,
+           Timing{t.start, nullptr}, k_new, v_new, n, lengths, c->Lmax, c->cfg.num_kv_heads, k, k8, v,
+           c->absmax_bits, c->requant, absmax, c->flag);
+    // recoding of every row of the (request, KV head)s whose scale grew: at
+    // most 64 workgroups per (request, KV head), each looping over row tiles
+    // (the others exit at once)
+    const int ntile = int((c->Lmax + kQuantRowsPerWg - 1) / kQuantRowsPerWg);
+    launch(sd_quantize_kernel, dim3(std::min(ntile, 64), BH), dim3(kQuantThreads), 0, s, Timing{nullptr, t.stop},
+           (const uint16_t*)k, lengths, n, c->Lmax, c->cfg.num_kv_heads, (const unsigned*)c->absmax_bits,
+           (const int32_t*)c->requant, k8, (float*)nullptr);
     return hipGetLastError();
 }
 

@@ -272,6 +272,20 @@ def make_inputs(w: Workload, seed: Optional[int] = None,
     return Inputs(w, q, k, v, L, planted, scales)
 
 
+def make_append_tokens(w: Workload, n: int, seed: int):
+    """New key and value rows for an append of n tokens per request:
+    uint16 bf16 bits [B][Hkv][n][d], i.i.d. N(0, 1) (keys times the
+    workload's channel scales when it has them, drawn afresh from `seed`)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, n])))
+    shape = (w.batch, w.num_kv_heads, n, w.head_dim)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    if w.channel_scale:
+        k *= np.exp(rng.uniform(np.log(0.25), np.log(4.0), size=(w.batch, w.num_kv_heads, 1, w.head_dim))
+                    ).astype(np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    return f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
 def tiny_workload(**kw) -> Workload:
     """A small variant of ``tiny16k`` for quick tests; fields overridable."""
     return WORKLOADS["tiny16k"].replace(**kw)

@@ -1,0 +1,167 @@
+"""GPU parity of the KV append (sd_append_kv) against the oracle.
+
+The append's contract: after it, the int8 codes and the key scale of every
+(request, KV head) equal the oracle's quantisation of the grown cache
+(t < L_b + n), bit for bit, whether or not the new keys raised the scale;
+a decode step on the grown cache then matches the oracle's step on it
+(kept sets bit-exact, outputs within 8e-3).
+"""
+import numpy as np
+import pytest
+
+from oracle import sparse_decode as O
+from sparse_attention_kv_int8_amd.inputs import WORKLOADS, make_append_tokens, make_inputs, tiny_workload
+from tests.gpu_util import GpuRun, compare_step, oracle_keys, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    import sparse_attention_kv_int8_amd.binding  # noqa: F401  (fails loudly when unbuilt)
+    yield
+    torch.cuda.synchronize()
+
+
+def append(g, k_new, v_new, lengths_before, absmax=None):
+    """sd_append_kv through the C ABI; then mirrors the append in the host
+    inputs (rows written, lengths grown) and on the device lengths."""
+    n = k_new.shape[2]
+    g.dec.sd_append_kv(to_dev_bf16(k_new), to_dev_bf16(v_new), n, g.lengths, g.k, g.k8, g.v,
+                       g.absmax if absmax is None else absmax)
+    g.torch.cuda.synchronize()
+    inp = g.inp
+    for b in range(inp.workload.batch):
+        L = int(lengths_before[b])
+        if 1 <= L and L + n <= inp.workload.max_context:
+            inp.k[b, :, L:L + n] = k_new[b]
+            inp.v[b, :, L:L + n] = v_new[b]
+            inp.lengths[b] = L + n
+    g.set_lengths(inp.lengths)
+
+
+def check_codes(g, requests=None):
+    """Device codes and scales against the oracle's quantisation of each
+    request's current cache."""
+    inp = g.inp
+    k8_ref, a_ref = oracle_keys(inp)
+    k8 = g.k8.cpu().numpy()
+    a = g.absmax.cpu().numpy()
+    for b in (range(inp.workload.batch) if requests is None else requests):
+        L = int(inp.lengths[b])
+        assert np.array_equal(k8[b, :, :L], k8_ref[b, :, :L]), f"codes differ (request {b}, L {L})"
+        assert np.array_equal(a[b], a_ref[b]), f"scales differ (request {b})"
+    return k8_ref
+
+
+def test_decode_loop_with_appends():
+    """step, append one token, step, ... on a ragged two-request cache: every
+    step's kept sets and outputs, and every append's codes, match the oracle
+    on the grown cache."""
+    w = tiny_workload(name="append_loop", batch=2, num_q_heads=8, num_kv_heads=2, max_context=4096 + 64)
+    print("case append loop B=2 lengths [4000, 2500]", flush=True)
+    inp = make_inputs(w, lengths=[4000, 2500])
+    g = GpuRun(inp)
+    g.quantize()
+    for t in range(4):
+        k8_ref = check_codes(g)
+        out, kept = g.step(inp.q)
+        compare_step(inp, inp.q, k8_ref, out, kept)
+        k_new, v_new = make_append_tokens(w, 1, seed=100 + t)
+        append(g, k_new, v_new, inp.lengths.copy())
+    check_codes(g)
+    assert g.dec.sd_check() == 0
+
+
+def test_append_that_raises_the_scale_recodes_the_head():
+    """New keys above the stored scale: the scale grows to their absmax and
+    every earlier row of that (request, KV head) is recoded; other heads keep
+    theirs.  Thirteen tokens cross an 8-token block boundary."""
+    w = tiny_workload(name="append_grow", batch=2, num_q_heads=8, num_kv_heads=2, max_context=8192)
+    print("case append growth n=13", flush=True)
+    inp = make_inputs(w, lengths=[5001, 8000])
+    g = GpuRun(inp)
+    g.quantize()
+    a0 = g.absmax.cpu().numpy().copy()
+    k_new, v_new = make_append_tokens(w, 13, seed=7)
+    # one element of request 0, KV head 1 at 8x the head's scale
+    big = np.float32(8.0) * a0[0, 1]
+    k_new[0, 1, 5, 17] = np.frombuffer(np.float32(big).tobytes(), np.uint32)[0] >> 16
+    append(g, k_new, v_new, inp.lengths.copy())
+    a1 = g.absmax.cpu().numpy()
+    assert a1[0, 1] > a0[0, 1]
+    k8_ref = check_codes(g)
+    out, kept = g.step(inp.q)
+    compare_step(inp, inp.q, k8_ref, out, kept)
+    assert g.dec.sd_check() == 0
+
+
+def test_append_past_the_end_flags_and_leaves_the_request():
+    """A request with L_b + n > Lmax (or a bad length) is left untouched and
+    raises the flag; the others are appended."""
+    import torch
+    w = tiny_workload(name="append_bad", batch=3, num_q_heads=4, num_kv_heads=1, max_context=2048)
+    print("case append bad lengths", flush=True)
+    inp = make_inputs(w, lengths=[1000, 2045, 1500])
+    g = GpuRun(inp)
+    g.quantize()
+    k8_before = g.k8.cpu().numpy().copy()
+    k_before = g.k.view(torch.int16).cpu().numpy().copy()
+    k_new, v_new = make_append_tokens(w, 5, seed=3)
+    dev_lengths = np.array([1000, 2045, 0], np.int32)
+    g.set_lengths(dev_lengths)
+    inp.lengths[2] = 0                    # mirrored as untouched by append()
+    append(g, k_new, v_new, dev_lengths)
+    from sparse_attention_kv_int8_amd.binding import SD_ERR_DEVICE_FLAG
+    assert g.dec.sd_check() == SD_ERR_DEVICE_FLAG
+    k8 = g.k8.cpu().numpy()
+    kk = g.k.view(torch.int16).cpu().numpy()
+    assert np.array_equal(k8[1:], k8_before[1:]) and np.array_equal(kk[1:], k_before[1:])
+    inp.lengths[2] = 1500
+    check_codes(g, requests=[0])
+
+
+def test_append_argument_errors():
+    import torch
+    from sparse_attention_kv_int8_amd.binding import (SD_ERR_INVALID_ARG, SD_ERR_UNSUPPORTED, SDError,
+                                                      SparseDecoder)
+    w = tiny_workload(name="append_args", max_context=1024)
+    dec = SparseDecoder.for_workload(w)
+    z = torch.zeros((1, 1, 1024, 128), dtype=torch.bfloat16, device="cuda")
+    z8 = torch.zeros((1, 1, 1024, 128), dtype=torch.int8, device="cuda")
+    lengths = torch.ones(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(SDError) as e:
+        dec.sd_append_kv(z, z, 0, lengths, z, z8, z)
+    assert e.value.status == SD_ERR_INVALID_ARG
+    wh = WORKLOADS["ctx_3m_hostv"].replace(max_context=65536, value_cache_tokens=8192, steps=1)
+    dech = SparseDecoder.for_workload(wh)
+    with pytest.raises(SDError) as e:
+        dech.sd_append_kv(z, z, 1, lengths, z, z8, z)
+    assert e.value.status == SD_ERR_UNSUPPORTED
+
+
+def test_append_llama8b_128k():
+    """The 128K workload with room to grow: one token appended (codes of the
+    new rows and every scale checked), then a token that raises one head's
+    scale (all its rows recoded), then a decode step on the grown cache."""
+    w = WORKLOADS["llama8b_128k"].replace(max_context=131072 + 256)
+    print("case append llama8b_128k", flush=True)
+    inp = make_inputs(w, lengths=[131072])
+    g = GpuRun(inp)
+    g.quantize()
+    k_new, v_new = make_append_tokens(w, 1, seed=11)
+    append(g, k_new, v_new, inp.lengths.copy())
+    check_codes(g)
+    a0 = g.absmax.cpu().numpy().copy()
+    k_new, v_new = make_append_tokens(w, 1, seed=12)
+    big = np.float32(-3.0) * a0[0, 6]
+    k_new[0, 6, 0, 99] = np.frombuffer(np.float32(big).tobytes(), np.uint32)[0] >> 16
+    append(g, k_new, v_new, inp.lengths.copy())
+    assert g.absmax.cpu().numpy()[0, 6] > a0[0, 6]
+    k8_ref = check_codes(g)
+    out, kept = g.step(inp.q)
+    compare_step(inp, inp.q, k8_ref, out, kept)
+    assert g.dec.sd_check() == 0
