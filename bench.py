@@ -32,6 +32,10 @@ stream_ceiling = a plain streaming copy (torch.neg, 1 GiB read + 1 GiB
 dense  = dense decode attention over every cached token (sd_dense_decode),
          timed the same way: us per step, its kernel's bandwidth against
          8 TB/s, and the sparse step's speedup over it.
+append = KV append (sd_append_kv) of one token per call on the same
+         workload grown to hold more tokens: us per append, us for one
+         append that raises a scale (its rows recoded), and us per token of
+         a decode loop (step + append).
 reuse  = steps that reuse the first r pruning stages' kept sets from an
          earlier step (sd_decode_step_reuse): us per step for each r, and,
          over a drifting query sequence, how much of the fully recomputed
@@ -317,6 +321,79 @@ def dense_study(b, steps: int, warmup: int, sparse_us: float) -> dict:
             "note": "sd_dense_decode over every token, same rotating cold copies, HIP graph replay"}
 
 
+def append_study(w, steps: int) -> dict:
+    """KV append (sd_append_kv), one token per call, on the workload's cache
+    grown to hold `steps` more tokens (fresh inputs of the same recipe):
+    - append_us: the append's two kernels per call, timed with HIP events
+      carried by their dispatches, when no new key raises a scale (the
+      usual case);
+    - grow_us: one append whose new key raises one KV head's scale, so that
+      all of that head's rows are recoded;
+    - loop_us_per_token: wall time per iteration of a decode loop (decode
+      step, append of that token, lengths + 1 on the device), eager
+      launches, one cache (warm in the Infinity Cache)."""
+    import torch
+    from sparse_attention_kv_int8_amd import binding as B
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    L0 = w.max_context
+    wa = w.replace(max_context=L0 + 2 * steps + 64)
+    inp = make_inputs(wa, lengths=[L0] * w.batch)
+    dec = B.SparseDecoder.for_workload(wa)
+    k, v = to_dev(inp.k), to_dev(inp.v)
+    k8 = torch.empty(inp.k.shape, dtype=torch.int8, device="cuda")
+    lengths = torch.from_numpy(inp.lengths.astype(np.int32)).cuda()
+    dec.sd_quantize_keys(k, lengths, k8)
+    q = to_dev(inp.q_step0)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    kept = torch.empty((w.batch, w.num_kv_heads, wa.keep_total), dtype=torch.int32, device="cuda")
+    from sparse_attention_kv_int8_amd.inputs import make_append_tokens
+    kn, vn = make_append_tokens(wa, 1, seed=2024)
+    kn, vn = to_dev(kn), to_dev(vn)
+    # every new key of the timed appends stays below the scales: |N(0,1)| keys
+    # are far below the cache's absmax, checked after the loop
+    absmax0 = torch.empty((w.batch, w.num_kv_heads), dtype=torch.float32, device="cuda")
+    absmax1 = torch.empty_like(absmax0)
+    dec.sd_append_kv(kn, vn, 1, lengths, k, k8, v, absmax0)
+    lengths.add_(1)
+    torch.cuda.synchronize()
+    dec.sd_profile_start(1 << B.SD_PROF_APPEND, steps + 8)
+    for _ in range(steps // 2):
+        dec.sd_append_kv(kn, vn, 1, lengths, k, k8, v, absmax1)
+        lengths.add_(1)
+    prof = dec.sd_profile_stop()
+    assert torch.equal(absmax0, absmax1), "a timed append raised a scale"
+    app_us = prof["append"][0] * 1e3 / prof["append"][1]
+    # decode loop: step, append, length + 1
+    for _ in range(5):
+        dec.sd_decode_step(q, k, k8, v, lengths, out, kept)
+        dec.sd_append_kv(kn, vn, 1, lengths, k, k8, v, None)
+        lengths.add_(1)
+    torch.cuda.synchronize()
+    n_loop = steps // 2 - 8
+    t0 = time.perf_counter()
+    for _ in range(n_loop):
+        dec.sd_decode_step(q, k, k8, v, lengths, out, kept)
+        dec.sd_append_kv(kn, vn, 1, lengths, k, k8, v, None)
+        lengths.add_(1)
+    torch.cuda.synchronize()
+    loop_us = (time.perf_counter() - t0) / n_loop * 1e6
+    # one append that raises KV head 0's scale of every request
+    big = kn.clone()
+    big[:, 0, 0, 0] = 4.0 * float(absmax1.max())
+    dec.sd_profile_start(1 << B.SD_PROF_APPEND, 4)
+    dec.sd_append_kv(big, vn, 1, lengths, k, k8, v, absmax1)
+    prof = dec.sd_profile_stop()
+    assert bool((absmax1[:, 0] > absmax0[:, 0]).all()), "the growth append did not raise the scale"
+    grow_us = prof["append"][0] * 1e3
+    assert dec.sd_check() == 0
+    del k, v, k8
+    torch.cuda.empty_cache()
+    return {"append_us": round(app_us, 3), "grow_us": round(grow_us, 3), "loop_us_per_token": round(loop_us, 3),
+            "tokens_appended": steps // 2 + n_loop + 7,
+            "note": "one token per call; grow_us recodes one KV head's rows per request; the loop is eager "
+                    "(decode step + append + lengths + 1) on one warm cache"}
+
+
 def stream_ceiling(mib: int = 1024) -> dict:
     """A plain streaming kernel on the same GPU, for context: torch's
     elementwise negation of a bf16 tensor of `mib` MiB into another (the
@@ -492,6 +569,7 @@ def main() -> int:
     ap.add_argument("--no-reuse", action="store_true", help="skip the stage-reuse study (profiling runs: its "
                     "warm-cache steps would mix into the per-kernel averages)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-decode comparison (sd_dense_decode)")
+    ap.add_argument("--no-append", action="store_true", help="skip the KV-append study (sd_append_kv)")
     ap.add_argument("--secondary", default="ctx_1m", help="second workload reported inside the line ('' = none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain elementwise copy (torch.neg) of MIB MiB three times: the "
@@ -592,6 +670,8 @@ def main() -> int:
     del b
     b_torch = __import__("torch")
     b_torch.cuda.empty_cache()
+    if not args.no_append:
+        line["append"] = append_study(w, args.steps)
     if args.secondary and args.secondary != w.name:
         w2 = WORKLOADS[args.secondary]
         b2, r2 = measure(w2, max(20, args.steps // 2), args.warmup, auto_copies(w2), not args.no_reuse,
