@@ -112,6 +112,27 @@ def quantize_keys(k_bits: np.ndarray, length: int) -> Tuple[np.ndarray, np.float
     return quantize_symmetric(k_bits[:length], a), a
 
 
+def quantize_int4(x_bits: np.ndarray, scale: np.float32) -> np.ndarray:
+    """4-bit code = round_half_even(7 * x / scale) in fp32, code in [-7, 7];
+    scale == 0 gives all-zero codes.  7 * x is exact in fp32, so as for the
+    int8 codes one correctly rounded division and rint give the exact
+    rational rounding (proved in the tests)."""
+    if scale == 0:
+        return np.zeros(np.shape(x_bits), dtype=np.int8)
+    x = np.float32(7.0) * bf16_to_f32(x_bits)
+    return np.rint(x / np.float32(scale)).astype(np.int8)
+
+
+def key_sketch4(k_bits: np.ndarray, length: int, stride: int) -> np.ndarray:
+    """int4 codes (held as int8 values) of the rows t = 0, stride, 2 stride,
+    ... < length of one (request, KV head), with the key scale a of
+    quantize_keys: the rows the first pruning stage samples, scored at 4 bits
+    (the notes page's INT4 cache quantisation, "KV Cache 压缩技术", applied to
+    the scoring keys only)."""
+    a = key_absmax(k_bits, length)
+    return quantize_int4(k_bits[:length:stride], a)
+
+
 # --------------------------------------------------------------------------
 # O3-O5: query quantisation, group sum, token scores
 # [KVN "KV Cache 压缩技术", GQA table: query heads h of one group share KV head j]
@@ -174,8 +195,11 @@ def children(kept: np.ndarray, parent_chunk: int, chunk: int, length: int) -> np
 
 
 def prune(S_of_rows, length: int, stages: Sequence[StageSpec],
-          given: Sequence[np.ndarray] = ()) -> List[np.ndarray]:
+          given: Sequence[np.ndarray] = (), S0_of_rows=None) -> List[np.ndarray]:
     """Runs the stages; returns the kept chunk starts P_1..P_S (ascending).
+
+    ``S0_of_rows``, when given, scores the first stage's samples in place of
+    ``S_of_rows`` (the int4 sketch of the first stage's rows).
 
     ``given`` holds kept sets of the first len(given) stages, reused from an
     earlier step ([HiP] same section: the modular design lets the pruning
@@ -191,7 +215,8 @@ def prune(S_of_rows, length: int, stages: Sequence[StageSpec],
         cand = children(kept_all[r - 1], stages[r - 1].chunk, stages[r].chunk, length)
     for s in range(r, len(stages)):
         st = stages[s]
-        sc = chunk_scores(S_of_rows, cand, st.chunk, st.stride, length)
+        score_fn = S0_of_rows if (s == 0 and S0_of_rows is not None) else S_of_rows
+        sc = chunk_scores(score_fn, cand, st.chunk, st.stride, length)
         kept = select_top(cand, sc, st.keep)
         kept_all.append(kept)
         if s + 1 < len(stages):
@@ -260,14 +285,17 @@ class StepResult:
 
 def decode_step(q_bits: np.ndarray, k_bits: np.ndarray, k8: np.ndarray, v_bits: np.ndarray,
                 lengths: Sequence[int], cfg: StepConfig, reuse: int = 0,
-                kept_prev: Optional[np.ndarray] = None) -> StepResult:
+                kept_prev: Optional[np.ndarray] = None,
+                sketch4: Optional[Sequence[Sequence[np.ndarray]]] = None) -> StepResult:
     """One decode step for a batch.
 
     q_bits [B][Hq][d] bf16 bits; k_bits, v_bits [B][Hkv][Lmax][d] bf16 bits;
     k8 [B][Hkv][Lmax][d] int8 codes (only rows t < L_b are read).  With
     reuse > 0 the first ``reuse`` stages are not run: their kept sets are
     taken from kept_prev [B][Hkv][sum keep] (an earlier step's kept_idx),
-    whose rows for those stages are also returned unchanged."""
+    whose rows for those stages are also returned unchanged.  With
+    ``sketch4`` ([b][j] -> key_sketch4 codes of rows 0, r_1, 2 r_1, ...) the
+    first stage scores S4_t = Q_j . K4_(t / r_1) instead of Q_j . K8_t."""
     if reuse:
         assert kept_prev is not None and 0 < reuse <= len(cfg.stages)
     B, Hq, d = q_bits.shape
@@ -286,9 +314,16 @@ def decode_step(q_bits: np.ndarray, k_bits: np.ndarray, k8: np.ndarray, v_bits: 
             Qj = Qs[b, j]
             k8_bj = k8[b, j]
             S_of_rows = lambda t, k8_bj=k8_bj, Qj=Qj: token_scores(Qj, k8_bj[t.reshape(-1)]).reshape(t.shape)
+            S0 = None
+            if sketch4 is not None:
+                r1 = cfg.stages[0].stride
+                k4_bj = sketch4[b][j]
+                # every first-stage sample is a multiple of r_1 (chunk starts are
+                # multiples of the chunk, which r_1 divides)
+                S0 = lambda t, k4_bj=k4_bj, Qj=Qj, r1=r1: token_scores(Qj, k4_bj[t.reshape(-1) // r1]).reshape(t.shape)
             offs = np.cumsum([0] + [st.keep for st in cfg.stages])
             given = [kept_prev[b, j, offs[s]:offs[s + 1]] for s in range(reuse)]
-            kept = prune(S_of_rows, L, cfg.stages, given)
+            kept = prune(S_of_rows, L, cfg.stages, given, S0)
             for s, (st, P) in enumerate(zip(cfg.stages, kept)):
                 if s < reuse:
                     kept_idx[b, j, offs[s]:offs[s + 1]] = given[s]

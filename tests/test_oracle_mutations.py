@@ -33,6 +33,12 @@ MUTATIONS = {
     "reuse_ignores_given_parents": ("cand = children(kept_all[r - 1], stages[r - 1].chunk, stages[r].chunk, length)",
                                     "cand = np.arange(0, length, stages[r].chunk, dtype=np.int64)"),
     "reuse_keeps_padding": ("kept_all = [g[(g >= 0) & (g < length)] for g in kept_all]", "kept_all = list(kept_all)"),
+    "int4_scale_127": ("x = np.float32(7.0) * bf16_to_f32(x_bits)", "x = np.float32(127.0) * bf16_to_f32(x_bits)"),
+    "sketch_row_index": ("token_scores(Qj, k4_bj[t.reshape(-1) // r1])",
+                         "token_scores(Qj, k4_bj[np.minimum(t.reshape(-1) // r1 + 1, len(k4_bj) - 1)])"),
+    "sketch_every_row": ("return quantize_int4(k_bits[:length:stride], a)", "return quantize_int4(k_bits[:length], a)"),
+    "sketch_unused": ("score_fn = S0_of_rows if (s == 0 and S0_of_rows is not None) else S_of_rows",
+                      "score_fn = S_of_rows"),
 }
 
 

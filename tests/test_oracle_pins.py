@@ -382,6 +382,91 @@ def test_dense_attention_closed_forms():
     assert np.max(np.abs(O.dense_attention(q, k2, v[:2], 0.1) - want)) < 1e-13
 
 
+# ------------------------------------------------------ int4 sketch ----
+def exact_code4(k_bits, a_bits):
+    """Exact rational round-half-even of 7 k / a."""
+    k = Fraction(float(O.bf16_to_f32(np.uint16(k_bits))))
+    a = Fraction(float(O.bf16_to_f32(np.uint16(a_bits))))
+    return round(Fraction(7) * k / a)
+
+
+def test_quantize_int4_random_pairs_and_ties_match_exact_rounding():
+    """quantize_int4 vs exact rational RNE: random bf16 pairs |k| <= a over
+    a wide exponent range, every tie k = (2n+1) a / 14 for a = 7 * 2^e and
+    for every bf16 a in [1, 2) where such a k is a bf16 value."""
+    rng = np.random.default_rng(17)
+    n = 20000
+    a = bf16_from_f32(np.exp(rng.uniform(-20, 20, n)).astype(np.float32))
+    af = O.bf16_to_f32(a)
+    k = bf16_from_f32((af * rng.uniform(-1, 1, n)).astype(np.float32))
+    ok = np.abs(O.bf16_to_f32(k)) <= af
+    a, k = a[ok], k[ok]
+    got = np.array([O.quantize_int4(k[i:i + 1], O.bf16_to_f32(a[i]))[0] for i in range(len(a))])
+    want = np.array([exact_code4(k[i], a[i]) for i in range(len(a))])
+    assert np.array_equal(got, want)
+    ties = 0
+    a_list = [bf16_from_f32(np.float32(7.0 * 2.0 ** e)) for e in (-9, -2, 0, 3)] + \
+             [np.uint16(x) for x in range(0x3F80, 0x4000)]
+    for ab in a_list:
+        af = Fraction(float(O.bf16_to_f32(ab)))
+        for m in range(7):
+            kk = Fraction(2 * m + 1) * af / 14
+            kf = np.float32(float(kk))
+            if Fraction(float(kf)) != kk:
+                continue
+            kb = bf16_from_f32(kf)
+            if Fraction(float(O.bf16_to_f32(kb))) != kk:
+                continue
+            for kbs in (kb, np.uint16(kb | 0x8000)):
+                got = int(O.quantize_int4(np.array([kbs]), O.bf16_to_f32(ab))[0])
+                assert got == exact_code4(kbs, ab)
+                ties += 1
+    assert ties > 100
+
+
+def test_quantize_int4_range_and_sketch_rows():
+    """Codes lie in [-7, 7] with |code| = 7 at the absmax; the sketch holds
+    exactly the rows 0, r, 2r, ... < L, coded with the int8 path's scale."""
+    rng = np.random.default_rng(2)
+    L, r = 1003, 8
+    k = bf16_from_f32(rng.standard_normal((1024, 128)).astype(np.float32) * 3)
+    k[L:] = bf16_from_f32(np.float32(500.0))          # padding must not count
+    a = O.key_absmax(k, L)
+    full = O.quantize_int4(k[:L], a)
+    assert full.min() >= -7 and full.max() <= 7 and np.abs(full).max() == 7
+    sk = O.key_sketch4(k, L, r)
+    assert sk.shape == (len(range(0, L, r)), 128)
+    assert np.array_equal(sk, full[::r])
+    assert O.quantize_keys(k, L)[1] == a
+
+
+def test_sketch_first_stage_equals_brute_force_top_k():
+    """With the sketch, the first stage keeps the brute-force top K of chunks
+    by the max of Q . K4 over its samples t = x, x + r, ... (lexsort on
+    (score desc, start asc)); later stages score int8 rows as before."""
+    rng = np.random.default_rng(44)
+    for L in (700, 1024, 1201):
+        q, k, v = _tiny_inputs(L, Hkv=1, G=4, seed=int(L))
+        k8 = np.zeros(k.shape, np.int8)
+        k8[0, :L] = O.quantize_keys(k[0], L)[0]
+        stages = [O.StageSpec(64, 8, 5), O.StageSpec(16, 2, 9), O.StageSpec(8, 1, 11)]
+        cfg = O.StepConfig(tuple(stages), 16, 32, 1 / np.sqrt(128))
+        sk = O.key_sketch4(k[0], L, 8)
+        res = O.decode_step(q[None], k[None], k8[None], v[None], [L], cfg, sketch4=[[sk]])
+        Q = O.group_query(O.quantize_query(q), 1)[0]
+        S4 = sk.astype(np.int64) @ Q                      # score of sample row i = token 8 i
+        starts = np.arange(0, L, 64)
+        sc = np.array([max(S4[(x + t) // 8] for t in range(0, 64, 8) if x + t < L) for x in starts])
+        order = np.lexsort((starts, -sc))
+        assert np.array_equal(res.kept_idx[0, 0, :5], np.sort(starts[order[:5]]))
+        # the later stages match the plain oracle run on the same first-stage set
+        plain = O.decode_step(q[None], k[None], k8[None], v[None], [L], cfg, reuse=1,
+                              kept_prev=res.kept_idx)
+        assert np.array_equal(plain.kept_idx, res.kept_idx)
+        assert np.max(np.abs(plain.out - res.out)) == 0
+    assert rng is not None
+
+
 def test_length_one_returns_the_value():
     q, k, v = _tiny_inputs(1, seed=3)
     res, _ = _run_oracle(q, k, v, 1, [(256, 8, 16), (32, 2, 32), (8, 1, 64)], 64, 512)
