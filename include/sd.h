@@ -225,6 +225,41 @@ sd_status sd_dense_decode(sd_ctx* ctx, const uint16_t* q, const uint16_t* k_bf16
                           const uint16_t* v, const int32_t* lengths, uint16_t* out,
                           void* stream);
 
+/* int4 scoring keys for the first pruning stage (the notes page "KV Cache 与
+ * 长上下文推理", section "KV Cache 压缩技术", lists INT4 next to INT8 as a
+ * cache quantisation; here it is applied to the first stage's scoring
+ * only, the stage that reads the most key rows).  The sketch holds the rows
+ * the first stage samples, t = i * r_1 (r_1 = stage[0].stride), i <
+ * ceil(L_b / r_1): codes c = rint(7 * k / a_bj) in [-7, 7] (round half to
+ * even, correctly rounded fp32 division) with the key scale a_bj of
+ * sd_quantize_keys, stored as nibbles c + 8; byte m of a row holds channel
+ * 2m in its low and channel 2m + 1 in its high nibble (64 bytes per row).
+ *
+ * Rows per (request, KV head) of the sketch: ceil(Lmax / r_1). */
+int64_t sd_sketch4_rows(const sd_ctx* ctx);
+
+/* Writes the sketch of the cache whose scales the context holds (the last
+ * sd_quantize_keys on this context; sd_append_kv does not update a sketch:
+ * call this again after appends).
+ *  k_bf16     device [B][Hkv][Lmax][d] bf16 keys.
+ *  lengths    device [B] int32 in [1, Lmax] (other requests are skipped).
+ *  k_sketch4  device [B][Hkv][sd_sketch4_rows][64] uint8 output; rows
+ *             i >= ceil(L_b / r_1) are not written. */
+sd_status sd_quantize_sketch4(sd_ctx* ctx, const uint16_t* k_bf16, const int32_t* lengths,
+                              uint8_t* k_sketch4, void* stream);
+
+/* sd_decode_step with the first stage scored from the sketch: its chunk
+ * score is the max over its samples t of S4_t = Q_j . K4_(t / r_1) (exact
+ * integer; Q_j as in sd_decode_step); every later stage, the attended set
+ * and the attention are those of sd_decode_step.  Arguments as in
+ * sd_decode_step, plus k_sketch4 from sd_quantize_sketch4.  Needs the first
+ * stage to run unfused: SD_ERR_UNSUPPORTED for a 2-stage configuration
+ * whose last stage is fused into the first (see sd_create). */
+sd_status sd_decode_step_sketch4(sd_ctx* ctx, const uint16_t* q, const uint16_t* k_bf16,
+                                 const int8_t* k_int8, const uint8_t* k_sketch4, const uint16_t* v,
+                                 const int32_t* lengths, uint16_t* out, int32_t* kept_idx,
+                                 void* stream);
+
 /* The step's query codes, for inspection: q8 device [B][Hq][d] int8 with one
  * absmax scale per query head (same rounding as the keys), and q_group
  * device [B][Hkv][d] int32, the sum of q8 over each KV head's group.  Either

@@ -76,6 +76,9 @@ _SIGS = {
     "sd_decode_step_reuse": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, C.c_int32, _p]),
     "sd_dense_decode": (C.c_int, [_p, _p, _p, _p, _p, _p, _p]),
     "sd_append_kv": (C.c_int, [_p, _p, _p, C.c_int32, _p, _p, _p, _p, _p, _p]),
+    "sd_sketch4_rows": (C.c_int64, [_p]),
+    "sd_quantize_sketch4": (C.c_int, [_p, _p, _p, _p, _p]),
+    "sd_decode_step_sketch4": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "sd_quantize_query": (C.c_int, [_p, _p, _p, _p, _p]),
     "sd_stage_scores": (C.c_int, [_p, C.c_int32, _p, C.c_int64, _p]),
     "sd_stage_candidates": (C.c_int64, [_p, C.c_int32]),
@@ -195,6 +198,18 @@ class SparseDecoder:
     def sd_append_kv(self, k_new, v_new, n_new: int, lengths, k, k_int8, v, k_absmax=None, stream=None) -> None:
         check(lib.sd_append_kv(self.handle, _ptr(k_new), _ptr(v_new), int(n_new), _ptr(lengths), _ptr(k),
                                _ptr(k_int8), _ptr(v), _ptr(k_absmax), _stream(stream)), "sd_append_kv")
+
+    def sd_sketch4_rows(self) -> int:
+        return int(lib.sd_sketch4_rows(self.handle))
+
+    def sd_quantize_sketch4(self, k, lengths, k_sketch4, stream=None) -> None:
+        check(lib.sd_quantize_sketch4(self.handle, _ptr(k), _ptr(lengths), _ptr(k_sketch4), _stream(stream)),
+              "sd_quantize_sketch4")
+
+    def sd_decode_step_sketch4(self, q, k, k_int8, k_sketch4, v, lengths, out, kept_idx, stream=None) -> None:
+        check(lib.sd_decode_step_sketch4(self.handle, _ptr(q), _ptr(k), _ptr(k_int8), _ptr(k_sketch4), _ptr(v),
+                                         _ptr(lengths), _ptr(out), _ptr(kept_idx), _stream(stream)),
+              "sd_decode_step_sketch4")
 
     def sd_quantize_query(self, q, q8=None, q_group=None, stream=None) -> None:
         check(lib.sd_quantize_query(self.handle, _ptr(q), _ptr(q8), _ptr(q_group), _stream(stream)),

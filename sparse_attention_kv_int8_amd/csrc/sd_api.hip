@@ -82,6 +82,7 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
     if (cfg.stage[cfg.num_stages - 1].chunk % 8 != 0) return SD_ERR_UNSUPPORTED;
     if (koff > 65535) return SD_ERR_UNSUPPORTED;
     c->keep_total = koff;
+    c->sketch_rows = (cfg.max_context + cfg.stage[0].stride - 1) / cfg.stage[0].stride;
     const sd_stage& last = cfg.stage[cfg.num_stages - 1];
     const int64_t mb = int64_t(last.keep) * (last.chunk / 8) + (cfg.sink + 7) / 8 + (cfg.window + 7) / 8 + 1;
     if (mb > (int64_t(1) << 20)) return SD_ERR_UNSUPPORTED;
@@ -348,8 +349,12 @@ sd_status sd_quantize_query(sd_ctx* c, const uint16_t* q, int8_t* q8, int32_t* q
     return from_hip(sd::launch_quantize_query(c, q, q8, qg, static_cast<hipStream_t>(stream)));
 }
 
-sd_status sd_decode_step_reuse(sd_ctx* c, const uint16_t* q, const uint16_t* k, const int8_t* k8, const uint16_t* v,
-                               const int32_t* lengths, uint16_t* out, int32_t* kept, int32_t reuse, void* stream) {
+namespace {
+
+// One decode step; k4 (the int4 first-stage sketch) or null.
+sd_status decode_step(sd_ctx* c, const uint16_t* q, const uint16_t* k, const int8_t* k8, const uint8_t* k4,
+                      const uint16_t* v, const int32_t* lengths, uint16_t* out, int32_t* kept, int32_t reuse,
+                      void* stream) {
     if (!c || !q || !k || !k8 || !v || !lengths || !out || !kept) return SD_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(k8) || !aligned16(v) || !aligned16(out))
         return SD_ERR_INVALID_ARG;
@@ -379,7 +384,7 @@ sd_status sd_decode_step_reuse(sd_ctx* c, const uint16_t* q, const uint16_t* k, 
     const int nprune = fused ? c->S - 1 : c->S;
     for (int st = reuse; st < nprune && e == hipSuccess; ++st)
         e = timed(c, SD_PROF_STAGE0 + st, s, [&](sd::Timing t) {
-            return sd::launch_prune_stage(c, st, st == reuse && st > 0, fused, q, k8, lengths, kept, s, t);
+            return sd::launch_prune_stage(c, st, st == reuse && st > 0, fused, q, k8, k4, lengths, kept, s, t);
         });
     const bool last_given = reuse == c->S;
     if (e == hipSuccess && c->cfg.values_on_host)
@@ -409,9 +414,35 @@ sd_status sd_dense_decode(sd_ctx* c, const uint16_t* q, const uint16_t* k, const
     return from_hip(e);
 }
 
+}  // namespace
+
+sd_status sd_decode_step_reuse(sd_ctx* c, const uint16_t* q, const uint16_t* k, const int8_t* k8, const uint16_t* v,
+                               const int32_t* lengths, uint16_t* out, int32_t* kept, int32_t reuse, void* stream) {
+    return decode_step(c, q, k, k8, nullptr, v, lengths, out, kept, reuse, stream);
+}
+
 sd_status sd_decode_step(sd_ctx* c, const uint16_t* q, const uint16_t* k, const int8_t* k8, const uint16_t* v,
                          const int32_t* lengths, uint16_t* out, int32_t* kept, void* stream) {
-    return sd_decode_step_reuse(c, q, k, k8, v, lengths, out, kept, 0, stream);
+    return decode_step(c, q, k, k8, nullptr, v, lengths, out, kept, 0, stream);
+}
+
+int64_t sd_sketch4_rows(const sd_ctx* c) { return c ? c->sketch_rows : -1; }
+
+sd_status sd_quantize_sketch4(sd_ctx* c, const uint16_t* k, const int32_t* lengths, uint8_t* k4, void* stream) {
+    if (!c || !k || !lengths || !k4) return SD_ERR_INVALID_ARG;
+    if (!aligned16(k) || !aligned16(k4)) return SD_ERR_INVALID_ARG;
+    return from_hip(sd::launch_sketch4(c, k, lengths, k4, static_cast<hipStream_t>(stream)));
+}
+
+sd_status sd_decode_step_sketch4(sd_ctx* c, const uint16_t* q, const uint16_t* k, const int8_t* k8,
+                                 const uint8_t* k4, const uint16_t* v, const int32_t* lengths, uint16_t* out,
+                                 int32_t* kept, void* stream) {
+    if (!c || !k4) return SD_ERR_INVALID_ARG;
+    if (!aligned16(k4)) return SD_ERR_INVALID_ARG;
+    // the first stage must run in a kernel of its own (not fused with the
+    // last stage, which reads rows the sketch does not hold)
+    if (c->fuse && c->S == 2) return SD_ERR_UNSUPPORTED;
+    return decode_step(c, q, k, k8, k4, v, lengths, out, kept, 0, stream);
 }
 
 int64_t sd_stage_candidates(const sd_ctx* c, int32_t stage) {

@@ -309,7 +309,7 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
 
     const int sp = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int bj = b * p.Hkv + j;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int sl = lane & 7;
     const int64_t Lraw = p.lengths[b];
     const int L = (Lraw < 1 || Lraw > p.Lmax) ? 0 : int(Lraw);

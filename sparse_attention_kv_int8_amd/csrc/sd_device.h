@@ -8,6 +8,7 @@ namespace sd {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -34,6 +35,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 __device__ __forceinline__ int code_of(float x, float scale) {
     if (scale == 0.0f) return 0;
     return int(__builtin_rintf((127.0f * x) / scale));
+}
+
+// Symmetric 4-bit code of one bf16 value: rint((7 * x) / scale) in
+// [-7, 7] (7 * x is exact in fp32, the division correctly rounded, as
+// above).  scale == 0 gives 0.
+__device__ __forceinline__ int code4_of(float x, float scale) {
+    if (scale == 0.0f) return 0;
+    return int(__builtin_rintf((7.0f * x) / scale));
 }
 
 // ----------------------------------------------------------- DPP moves ----

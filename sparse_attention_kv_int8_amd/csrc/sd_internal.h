@@ -61,6 +61,7 @@ struct sd_ctx {
     int nsplit;             // flash-decode splits per (request, KV head)
     int nsplit_a;           // of which cover the sink/window blocks (device values only)
     int nsplit_d;           // splits per (request, KV head) of the dense decode (sd_dense_decode)
+    int64_t sketch_rows;    // rows per (request, KV head) of the int4 first-stage sketch: ceil(Lmax / r_1)
     float scale_log2;       // softmax_scale * log2(e)
     sd::StageGeom st[SD_MAX_STAGES];
     size_t select_lds;      // dynamic LDS bytes of the stage kernels
@@ -127,8 +128,13 @@ hipError_t launch_quantize_query(sd_ctx* c, const uint16_t* q, int8_t* q8, int32
 // is read from kept_idx instead, where an earlier step left it.
 // fused: this step runs the fused plan (the stage before the last also
 // scores the last stage's candidates, and the decode kernel selects both).
+// k4: the int4 sketch of the first stage's rows (stage 0 scores it in place
+// of k8), or null.
 hipError_t launch_prune_stage(sd_ctx* c, int stage, bool given, bool fused, const uint16_t* q, const int8_t* k8,
-                              const int32_t* lengths, int32_t* kept, hipStream_t s, Timing t = {});
+                              const uint8_t* k4, const int32_t* lengths, int32_t* kept, hipStream_t s,
+                              Timing t = {});
+// int4 sketch rows of the first stage (codes with the stored key scales).
+hipError_t launch_sketch4(sd_ctx* c, const uint16_t* k, const int32_t* lengths, uint8_t* k4, hipStream_t s);
 hipError_t launch_attend(sd_ctx* c, bool given, bool fused, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const int32_t* lengths, int32_t* kept, uint16_t* out, hipStream_t s, Timing t = {});
 // Merges `nsplit` split partials per (request, KV head) into the bf16 output.

@@ -47,6 +47,8 @@ struct PruneParams {
     int nrows, rstride;           // key rows read per candidate, and their token stride
     int fuse_rq, fuse_m;          // fused next stage: children per chunk, stride ratio
     int32_t* pre;                 // fused next stage: [B][Hkv][cur.ncand * fuse_rq] children's scores
+    const uint8_t* k4;            // first stage from the int4 sketch: [B][Hkv][k4_rows][64]
+    int64_t k4_rows;
 };
 
 // Score `cpw` candidates per wave.  NS8 = rows per candidate / 8 (rounded up);
@@ -57,11 +59,19 @@ struct PruneParams {
 // the next stage's samples (rstride = its stride, one 8-row slot per child
 // chunk): this stage's score is the max over rows i % fuse_m == 0 (its own
 // samples), and each slot's max is written as that child's score.
-template <int NS8, bool FUSE>
+//
+// Q4 (first stage only, unfused): the rows are read from the int4 sketch
+// instead, row t at sketch row t / rstride (every first-stage sample is a
+// multiple of its stride), 8 lanes x 8 bytes per 64-byte row.  The nibbles
+// u = code + 8 are unpacked into four words of bytes, channels
+// (0,2,4,6) (1,3,5,7) (8,...,14) (9,...,15) of the lane's 16, which is the
+// channel order split_query4 gives qh and ql; S = Q . u - 8 sum(Q), the
+// constant `corr` = 8 sum(Q) being subtracted from every row's score.
+template <int NS8, bool FUSE, bool Q4>
 __device__ __forceinline__ void score_slice(const PruneParams& p, const int* cstart, int64_t L,
-                                            const int8_t* __restrict__ k8_bj, const u32x4& qh,
-                                            const u32x4& ql, int first, int32_t* __restrict__ out,
-                                            int32_t* __restrict__ pre_bj) {
+                                            const int8_t* __restrict__ k8_bj, const uint8_t* __restrict__ k4_bj,
+                                            const u32x4& qh, const u32x4& ql, int corr, int first,
+                                            int32_t* __restrict__ out, int32_t* __restrict__ pre_bj) {
     const StageDev& st = p.cur;
     constexpr int CB = NS8 >= 8 ? 1 : 8 / NS8;     // candidates per batch
     constexpr int NL = CB * NS8;                   // loads per batch
@@ -81,8 +91,16 @@ __device__ __forceinline__ void score_slice(const PruneParams& p, const int* cst
             const int i = it * 8 + row8;
             const int64_t t = xs[c] + int64_t(i) * p.rstride;
             ok[u] = xs[c] >= 0 && i < p.nrows && t < L;
-            v[u] = ok[u] ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k8_bj + t * kHeadDim) + sl)
-                         : u32x4{0, 0, 0, 0};
+            if constexpr (Q4) {
+                const int64_t row = int64_t(int(xs[c]) / p.rstride) + i;   // = t / rstride
+                const u32x2 w = ok[u] ? __builtin_nontemporal_load(
+                                            reinterpret_cast<const u32x2*>(k4_bj + row * (kHeadDim / 2)) + sl)
+                                      : u32x2{0u, 0u};
+                v[u] = u32x4{w.x & 0x0f0f0f0fu, (w.x >> 4) & 0x0f0f0f0fu, w.y & 0x0f0f0f0fu, (w.y >> 4) & 0x0f0f0f0fu};
+            } else {
+                v[u] = ok[u] ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k8_bj + t * kHeadDim) + sl)
+                             : u32x4{0, 0, 0, 0};
+            }
         }
         int best[CB];
 #pragma unroll
@@ -97,7 +115,7 @@ __device__ __forceinline__ void score_slice(const PruneParams& p, const int* cst
             al = __builtin_amdgcn_sdot4((int)ql.y, (int)v[u].y, al, false);
             al = __builtin_amdgcn_sdot4((int)ql.z, (int)v[u].z, al, false);
             al = __builtin_amdgcn_sdot4((int)ql.w, (int)v[u].w, al, false);
-            const int s = sum8_i(ah * 64 + al);
+            const int s = sum8_i(ah * 64 + al) - (Q4 ? corr : 0);
             if (ok[u] && own[u % NS8]) best[u / NS8] = max(best[u / NS8], s);
             if (FUSE) {
                 const int c = u / NS8, it = u % NS8;
@@ -136,12 +154,36 @@ __device__ __forceinline__ void split_query(const int* Qlds, int sl, u32x4& qh, 
     ql = u32x4{l4[0], l4[1], l4[2], l4[3]};
 }
 
+// split_query for the int4 sketch's channel order: words hold the lane's
+// channels (0,2,4,6), (1,3,5,7), (8,10,12,14), (9,11,13,15).
+__device__ __forceinline__ void split_query4(const int* Qlds, int sl, u32x4& qh, u32x4& ql) {
+    uint32_t h4[4], l4[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t hw = 0, lw = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int ch = (w >> 1) * 8 + 2 * u + (w & 1);
+            const int Q = Qlds[sl * 16 + ch];
+            const int lo = ((Q + 32) & 63) - 32;
+            const int hi = (Q - lo) >> 6;
+            hw |= (uint32_t(hi) & 0xffu) << (8 * u);
+            lw |= (uint32_t(lo) & 0xffu) << (8 * u);
+        }
+        h4[w] = hw;
+        l4[w] = lw;
+    }
+    qh = u32x4{h4[0], h4[1], h4[2], h4[3]};
+    ql = u32x4{l4[0], l4[1], l4[2], l4[3]};
+}
+
 // One instantiation per (rows per candidate / 8, select code of the
 // previous stage (0 = stage 0, kGiven = the previous stage reused), fused
 // next stage): each launch carries only
 // its own path, which keeps code size and scalar-register pressure down.
-template <int NS8, int SEL, bool FUSE>
+template <int NS8, int SEL, bool FUSE, bool Q4 = false>
 __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PruneParams p) {
+    static_assert(!Q4 || (SEL == 0 && !FUSE), "the int4 sketch serves the unfused first stage only");
     extern __shared__ uint32_t dyn[];      // the previous stage's select (kept_lds_words)
     __shared__ int Qlds[kHeadDim];
     __shared__ unsigned tmp[32];
@@ -187,15 +229,24 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
         cstart[threadIdx.x] = int(cand_start(p.cur, SEL == 0, parents, wg_first + threadIdx.x, L));
     const int sl = threadIdx.x & 7;
     u32x4 qh, ql;
-    split_query(Qlds, sl, qh, ql);
+    int corr = 0;
+    if constexpr (Q4) {
+        split_query4(Qlds, sl, qh, ql);
+        int sq = 0;
+        for (int c = 0; c < kHeadDim; ++c) sq += Qlds[c];     // the same in every thread
+        corr = 8 * sq;
+    } else {
+        split_query(Qlds, sl, qh, ql);
+    }
     __syncthreads();
 
     const int8_t* k8_bj = p.k8 + int64_t(bj) * p.Lmax * kHeadDim;
+    const uint8_t* k4_bj = Q4 ? p.k4 + int64_t(bj) * p.k4_rows * (kHeadDim / 2) : nullptr;
     int32_t* scores_bj = p.scores + int64_t(bj) * p.cur.ncand;
     const int wave = threadIdx.x >> 6;
     const int first = wg_first + wave * p.cpw;
-    score_slice<NS8, FUSE>(p, cstart + wave * p.cpw, L, k8_bj, qh, ql, first, scores_bj,
-                           FUSE ? p.pre + int64_t(bj) * p.cur.ncand * p.fuse_rq : nullptr);
+    score_slice<NS8, FUSE, Q4>(p, cstart + wave * p.cpw, L, k8_bj, k4_bj, qh, ql, corr, first, scores_bj,
+                               FUSE ? p.pre + int64_t(bj) * p.cur.ncand * p.fuse_rq : nullptr);
     if constexpr (SEL != 0 && SEL != kGiven) {
         // workgroup 0 publishes the previous stage's kept set (ascending,
         // -1 padded); stored last, so no barrier waits on these stores
@@ -218,10 +269,12 @@ StageDev stage_dev(const sd_ctx* c, int st) {
 }
 
 hipError_t launch_prune_stage(sd_ctx* c, int st, bool given, bool fused, const uint16_t* q, const int8_t* k8,
-                              const int32_t* lengths, int32_t* kept, hipStream_t s, Timing t) {
+                              const uint8_t* k4, const int32_t* lengths, int32_t* kept, hipStream_t s, Timing t) {
     PruneParams p{};
     p.q = q;
     p.k8 = k8;
+    p.k4 = k4;
+    p.k4_rows = c->sketch_rows;
     p.lengths = lengths;
     p.Lmax = c->Lmax;
     p.Hq = c->cfg.num_q_heads;
@@ -265,7 +318,13 @@ hipError_t launch_prune_stage(sd_ctx* c, int st, bool given, bool fused, const u
     } else {                                                    \
         SD_PRUNE_UNFUSED(S);                                    \
     }
-    if (sel == 0) { SD_PRUNE_NS(0); }
+    const bool q4 = k4 != nullptr && st == 0 && !fuse;
+    if (q4) {
+        if (ns8 == 1) launch(sd_prune_stage_kernel<1, 0, false, true>, grid, dim3(kPruneThreads), lds, s, t, p);
+        else if (ns8 == 2) launch(sd_prune_stage_kernel<2, 0, false, true>, grid, dim3(kPruneThreads), lds, s, t, p);
+        else if (ns8 <= 4) launch(sd_prune_stage_kernel<4, 0, false, true>, grid, dim3(kPruneThreads), lds, s, t, p);
+        else launch(sd_prune_stage_kernel<8, 0, false, true>, grid, dim3(kPruneThreads), lds, s, t, p);
+    } else if (sel == 0) { SD_PRUNE_NS(0); }
     else if (sel == kGiven) { SD_PRUNE_NS(kGiven); }
     else if (sel == 4) { SD_PRUNE_NS(4); }
     else if (sel == 16) { SD_PRUNE_NS(16); }

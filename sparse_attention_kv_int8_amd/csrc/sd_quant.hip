@@ -110,6 +110,37 @@ __global__ __launch_bounds__(kQuantThreads) void sd_quantize_kernel(
     }
 }
 
+// int4 sketch of the first pruning stage's rows: for t = i * stride < L,
+// row i of the sketch holds the 4-bit codes of key row t with the stored
+// scale, as nibbles code + 8 (1..15), channel 2m in the low and channel
+// 2m + 1 in the high nibble of byte m (64 bytes per row).  16 threads per
+// row, each codes 8 channels (one 16-byte load) into one 4-byte word.
+__global__ __launch_bounds__(kQuantThreads) void sd_sketch4_kernel(
+    const uint16_t* __restrict__ k, const int32_t* __restrict__ lengths, int64_t Lmax, int Hkv, int stride,
+    int64_t rows, const unsigned* __restrict__ absmax_bits, uint8_t* __restrict__ k4) {
+    const int bj = blockIdx.y, b = bj / Hkv;
+    const int64_t L = lengths[b];
+    if (L < 1 || L > Lmax) return;
+    const float a = bf16_to_f32(uint16_t(absmax_bits[bj]));
+    const int64_t n = (L + stride - 1) / stride;             // sketch rows of this request
+    const u32x4* src = reinterpret_cast<const u32x4*>(k + int64_t(bj) * Lmax * kHeadDim);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(k4 + int64_t(bj) * rows * (kHeadDim / 2));
+    const int sub = threadIdx.x & 15;
+    for (int64_t i = int64_t(blockIdx.x) * kQuantRowsPerWg + (threadIdx.x >> 4);
+         i < min(n, int64_t(blockIdx.x + 1) * kQuantRowsPerWg); i += kQuantThreads / 16) {
+        const u32x4 w = src[i * stride * 16 + sub];
+        const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+        uint32_t word = 0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t lo = uint32_t(code4_of(bf16_lo(x[m]), a) + 8);
+            const uint32_t hi = uint32_t(code4_of(bf16_hi(x[m]), a) + 8);
+            word |= (lo | (hi << 4)) << (8 * m);
+        }
+        dst[i * 16 + sub] = word;
+    }
+}
+
 // Appends n rows per (request, KV head) at t = L_b .. L_b + n - 1: copies
 // the new bf16 keys and values into the caches and codes the new keys with
 // a' = max(a, absmax of the new keys), a being the scale stored for the
@@ -193,6 +224,15 @@ hipError_t launch_quantize_keys(sd_ctx* c, const uint16_t* k, const int32_t* len
            c->cfg.num_kv_heads, c->absmax_bits, c->flag);
     launch(sd_quantize_kernel, grid, dim3(kQuantThreads), 0, s, Timing{nullptr, t.stop}, k, lengths, 0, c->Lmax,
            c->cfg.num_kv_heads, (const unsigned*)c->absmax_bits, (const int32_t*)nullptr, k8, absmax);
+    return hipGetLastError();
+}
+
+hipError_t launch_sketch4(sd_ctx* c, const uint16_t* k, const int32_t* lengths, uint8_t* k4, hipStream_t s) {
+    const int BH = c->cfg.batch * c->cfg.num_kv_heads;
+    const int64_t rows = c->sketch_rows;
+    const int nwg = int((rows + kQuantRowsPerWg - 1) / kQuantRowsPerWg);
+    launch(sd_sketch4_kernel, dim3(nwg, BH), dim3(kQuantThreads), 0, s, Timing{}, k, lengths, c->Lmax,
+           c->cfg.num_kv_heads, c->st[0].stride, rows, (const unsigned*)c->absmax_bits, k4);
     return hipGetLastError();
 }
 

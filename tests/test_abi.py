@@ -15,7 +15,7 @@ B = pytest.importorskip("sparse_attention_kv_int8_amd.binding")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(sd_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(sd_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_every_declared_symbol_is_exported():
