@@ -32,6 +32,9 @@ stream_ceiling = a plain streaming copy (torch.neg, 1 GiB read + 1 GiB
 dense  = dense decode attention over every cached token (sd_dense_decode),
          timed the same way: us per step, its kernel's bandwidth against
          8 TB/s, and the sparse step's speedup over it.
+sketch4 = the first stage scored from the int4 sketch of its rows
+         (sd_decode_step_sketch4), timed the same way, with its selection
+         compared to the int8 step's on the same query.
 append = KV append (sd_append_kv) of one token per call on the same
          workload grown to hold more tokens: us per append, us for one
          append that raises a scale (its rows recoded), and us per token of
@@ -321,6 +324,83 @@ def dense_study(b, steps: int, warmup: int, sparse_us: float) -> dict:
             "note": "sd_dense_decode over every token, same rotating cold copies, HIP graph replay"}
 
 
+def sketch_study(b, steps: int, warmup: int, sparse_us: float) -> dict:
+    """The first stage scored from the int4 sketch (sd_decode_step_sketch4),
+    timed like the main figure (HIP graph replay over the rotating copies,
+    each with its own sketch), with the first-stage kernel timed by HIP
+    events carried by its dispatches.  Selection against the int8 step on
+    the same query: the share of the int8 step's last-stage kept chunks the
+    sketch step also keeps, the share of planted heavy tokens each attends,
+    and the largest output difference."""
+    torch, lib, h, w, B = b.torch, b.B.lib, b.dec.handle, b.w, b.B
+    rows = b.dec.sd_sketch4_rows()
+    sk0 = torch.empty((w.batch, w.num_kv_heads, rows, 64), dtype=torch.uint8, device="cuda")
+    b.dec.sd_quantize_sketch4(b.ks[0], b.lengths, sk0)
+    sks = [sk0] + [sk0.clone() for _ in range(len(b.ks) - 1)]
+    out = torch.empty_like(b.out)
+    kept = torch.empty_like(b.kept)
+    args = [(b.q.data_ptr(), b.ks[i].data_ptr(), b.k8s[i].data_ptr(), sks[i].data_ptr(), b.vs[i].data_ptr(),
+             b.lengths.data_ptr(), out.data_ptr(), kept.data_ptr()) for i in range(len(b.ks))]
+    graphs = []
+    torch.cuda.synchronize()
+    for a in args:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st = lib.sd_decode_step_sketch4(h, *a, torch.cuda.current_stream().cuda_stream)
+            if st:
+                B.check(st, "sd_decode_step_sketch4 (capture)")
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / steps * 1e6
+    del graphs
+    b.dec.sd_profile_start(0xFF, 8 * steps + 8)
+    for i in range(steps):
+        st = lib.sd_decode_step_sketch4(h, *args[i % len(args)], b.stream)
+        if st:
+            B.check(st, "sd_decode_step_sketch4")
+    prof = b.dec.sd_profile_stop()
+    kern = {k: round(v[0] * 1e3 / v[1], 3) for k, v in prof.items()}
+    # selection against the int8 step (same query, same cache)
+    b.run(1)
+    torch.cuda.synchronize()
+    k8set, o8 = b.kept.cpu().numpy(), b.out.float()
+    k4set = kept.cpu().numpy()
+    off = sum(st.keep for st in w.stages[:-1])
+    c_last = w.stages[-1].chunk
+    rec, hit4, hit8, n = [], 0, 0, 0
+    for bb in range(w.batch):
+        L = int(b.inp.lengths[bb])
+        for j in range(w.num_kv_heads):
+            f = set(k8set[bb, j, off:][k8set[bb, j, off:] >= 0].tolist())
+            if f:
+                rec.append(len(f & set(k4set[bb, j, off:].tolist())) / len(f))
+            pos = np.asarray(b.inp.planted[bb][j])
+            for ks_, name in ((k4set, 4), (k8set, 8)):
+                kk = ks_[bb, j, off:]
+                kk = kk[kk >= 0]
+                inside = ((pos[:, None] >= kk[None, :]) & (pos[:, None] < kk[None, :] + c_last)).any(axis=1)
+                inside |= (pos < w.sink) | (pos >= L - w.window)
+                if name == 4:
+                    hit4 += int(inside.sum())
+                else:
+                    hit8 += int(inside.sum())
+            n += len(pos)
+    first_rows = int(sum(-(-int(L) // w.stages[0].stride) for L in b.inp.lengths)) * w.num_kv_heads
+    return {"us_per_step": round(us, 3), "speedup_vs_int8": round(sparse_us / us, 3), "step_kernels_us": kern,
+            "stage0_bytes": 64 * first_rows,
+            "stage0_roofline_frac": round(64 * first_rows / (kern["stage0"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "last_stage_overlap_with_int8": round(statistics.fmean(rec), 4),
+            "planted_recall": {"sketch4": round(hit4 / max(1, n), 4), "int8": round(hit8 / max(1, n), 4)},
+            "max_abs_out_diff_vs_int8": round(float((out.float() - o8).abs().max()), 4),
+            "note": "first stage scored from the int4 sketch (64 B per sampled row, contiguous); later stages int8"}
+
+
 def append_study(w, steps: int) -> dict:
     """KV append (sd_append_kv), one token per call, on the workload's cache
     grown to hold `steps` more tokens (fresh inputs of the same recipe):
@@ -451,7 +531,8 @@ def oracle_baseline(w, inp, kept_gpu_bytes: float) -> dict:
             "s_per_step": round(ts, 4), "quantize_s": round(tq, 3)}
 
 
-def measure(w, steps: int, warmup: int, copies: int, reuse: bool = True, dense: bool = True) -> tuple:
+def measure(w, steps: int, warmup: int, copies: int, reuse: bool = True, dense: bool = True,
+            sketch: bool = True) -> tuple:
     b = Bench(w, copies)
     torch = b.torch
     b.run(warmup)
@@ -495,8 +576,9 @@ def measure(w, steps: int, warmup: int, copies: int, reuse: bool = True, dense: 
     ab = algorithmic_bytes(w, kept, b.inp.lengths)
     reuse = reuse_study(b, steps) if reuse and w.steps == 1 else None
     dense = dense_study(b, steps, warmup, us_per_step) if dense else None
+    sketch = sketch_study(b, steps, warmup, us_per_step) if sketch else None
     return b, dict(us_per_step=us_per_step, us_eager=us_eager, avg_us=avg_us, dominant=dominant, dominant_us=dom_us,
-                   bytes=ab, reuse=reuse, spread=spread, dense=dense)
+                   bytes=ab, reuse=reuse, spread=spread, dense=dense, sketch=sketch)
 
 
 def measure_hostv(w, repeats: int = 3) -> dict:
@@ -505,7 +587,8 @@ def measure_hostv(w, repeats: int = 3) -> dict:
     with a drifting query, from a cold cache, `repeats` times.  Each step is
     timed with HIP events on the launch stream (eager launches: the cache's
     step index is passed per call); the cache statistics are read after each
-    step, outside its timed region."""
+    step, outside its timed region.  The sequence is then run again with
+    the first stage scored from the int4 sketch (`sketch4`)."""
     import torch
     from sparse_attention_kv_int8_amd import binding as B
     t = time.perf_counter()
@@ -525,21 +608,36 @@ def measure_hostv(w, repeats: int = 3) -> dict:
     out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
     kept = torch.empty((w.batch, w.num_kv_heads, w.keep_total), dtype=torch.int32, device="cuda")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(w.steps)]
-    runs = []
-    for rep in range(repeats):
-        dec.sd_reset_value_cache()
-        torch.cuda.synchronize()
-        steps = []
-        for t in range(w.steps):
-            a, b = ev[t]
-            a.record()
-            dec.sd_decode_step(qs[t], k, k8, v, lengths, out, kept)
-            b.record()
+
+    def sequence(step_fn, label):
+        runs = []
+        for rep in range(repeats):
+            dec.sd_reset_value_cache()
             torch.cuda.synchronize()
-            st = dec.sd_get_stats()
-            steps.append((a.elapsed_time(b) * 1e3, st.last_needed, st.last_hits, st.last_misses))
-        runs.append(steps)
-        log(f"[bench] host-value run {rep}: {sum(x[0] for x in steps) / len(steps):.1f} us/step")
+            steps = []
+            for t in range(w.steps):
+                a, b = ev[t]
+                a.record()
+                step_fn(t)
+                b.record()
+                torch.cuda.synchronize()
+                st = dec.sd_get_stats()
+                steps.append((a.elapsed_time(b) * 1e3, st.last_needed, st.last_hits, st.last_misses))
+            runs.append(steps)
+            log(f"[bench] host-value run {rep} ({label}): {sum(x[0] for x in steps) / len(steps):.1f} us/step")
+        return runs
+
+    runs = sequence(lambda t: dec.sd_decode_step(qs[t], k, k8, v, lengths, out, kept), "int8")
+    kept_np = kept.cpu().numpy()
+    # the same sequence with the first stage scored from the int4 sketch
+    sk = torch.empty((w.batch, w.num_kv_heads, dec.sd_sketch4_rows(), 64), dtype=torch.uint8, device="cuda")
+    dec.sd_quantize_sketch4(k, lengths, sk)
+    runs4 = sequence(lambda t: dec.sd_decode_step_sketch4(qs[t], k, k8, sk, v, lengths, out, kept), "sketch4")
+    all4 = [x for r in runs4 for x in r]
+    sketch4 = {"us_per_step": round(statistics.fmean(x[0] for x in all4), 3),
+               "us_per_step_after_first": round(statistics.fmean(x[0] for r in runs4 for x in r[1:]), 3),
+               "hit_rate": round(sum(x[2] for x in all4) / max(1, sum(x[1] for x in all4)), 4),
+               "note": "first stage scored from the int4 sketch; same sequence, cold cache, same runs"}
     allsteps = [x for r in runs for x in r]
     us = [x[0] for x in allsteps]
     warm = [x[0] for r in runs for x in r[1:]]
@@ -547,14 +645,13 @@ def measure_hostv(w, repeats: int = 3) -> dict:
     hits = sum(x[2] for x in allsteps)
     misses = sum(x[3] for x in allsteps)
     h2d = misses * 8 * w.head_dim * 2
-    kept_np = kept.cpu().numpy()
     ab = algorithmic_bytes(w, kept_np, inp.lengths)
     return dict(us_per_step=statistics.fmean(us), us_first_step=statistics.fmean(r[0][0] for r in runs),
                 us_per_step_after_first=statistics.fmean(warm), hit_rate=hits / max(1, needed),
                 h2d_bytes_per_step=h2d / len(allsteps), pcie_GBs=h2d / (sum(us) * 1e-6) / 1e9,
                 quantize_us=quantize_us, bytes=ab, repeats=repeats,
                 per_step_us=[round(x[0], 2) for x in runs[-1]],
-                per_step_hit_rate=[round(x[2] / max(1, x[1]), 4) for x in runs[-1]])
+                per_step_hit_rate=[round(x[2] / max(1, x[1]), 4) for x in runs[-1]], sketch4=sketch4)
 
 
 def main() -> int:
@@ -570,6 +667,7 @@ def main() -> int:
                     "warm-cache steps would mix into the per-kernel averages)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-decode comparison (sd_dense_decode)")
     ap.add_argument("--no-append", action="store_true", help="skip the KV-append study (sd_append_kv)")
+    ap.add_argument("--no-sketch", action="store_true", help="skip the int4 first-stage sketch study")
     ap.add_argument("--secondary", default="ctx_1m", help="second workload reported inside the line ('' = none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain elementwise copy (torch.neg) of MIB MiB three times: the "
@@ -606,6 +704,7 @@ def main() -> int:
             "algorithmic_bytes": total,
             "quantize_keys_us": round(r["quantize_us"], 2),
             "per_step_us": r["per_step_us"], "per_step_hit_rate": r["per_step_hit_rate"],
+            "sketch4": r["sketch4"],
         }), flush=True)
         return 0
 
@@ -626,7 +725,8 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
-    b, r = measure(w, args.steps, args.warmup, auto_copies(w), not args.no_reuse, not args.no_dense)
+    b, r = measure(w, args.steps, args.warmup, auto_copies(w), not args.no_reuse, not args.no_dense,
+                   not args.no_sketch)
     total = r["bytes"]["total"]
     dom_bytes = r["bytes"]["per_kernel"][r["dominant"]]
     achieved = dom_bytes / (r["dominant_us"] * 1e-6) / 1e9
@@ -665,6 +765,7 @@ def main() -> int:
         "quantize_keys_us": round(b.quantize_us, 2),
         "reuse": r["reuse"],
         "dense": r["dense"],
+        "sketch4": r["sketch"],
     }
     inp, kb = b.inp, total
     del b
@@ -675,7 +776,7 @@ def main() -> int:
     if args.secondary and args.secondary != w.name:
         w2 = WORKLOADS[args.secondary]
         b2, r2 = measure(w2, max(20, args.steps // 2), args.warmup, auto_copies(w2), not args.no_reuse,
-                         not args.no_dense)
+                         not args.no_dense, not args.no_sketch)
         t2 = r2["bytes"]["total"]
         line["secondary"] = {"workload": w2.name, "us_per_step": round(r2["us_per_step"], 3),
                              "value_GBs": round(t2 / (r2["us_per_step"] * 1e-6) / 1e9, 2),
@@ -684,7 +785,7 @@ def main() -> int:
                              "dominant_frac": round(r2["bytes"]["per_kernel"][r2["dominant"]] /
                                                     (r2["dominant_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                              "quantize_keys_us": round(b2.quantize_us, 2), "reuse": r2["reuse"],
-                             "dense": r2["dense"]}
+                             "dense": r2["dense"], "sketch4": r2["sketch"]}
         del b2
         b_torch.cuda.empty_cache()
     if not args.copy_calibration:            # its copies would mix with the calibration copies

@@ -26,7 +26,14 @@ namespace sd {
 
 constexpr int kPruneThreads = 256;
 constexpr int kPruneWaves = kPruneThreads / kWave;
-constexpr int kMaxCandPerWave = 8;          // candidates per wave (one batch of 8 row loads)
+constexpr int kMaxCandPerWave = 16;         // candidates per wave (int8: one batch of 8 row loads; int4
+                                            // sketch: one batch of 16, twice the candidates)
+
+// Candidates per load batch: 8 row loads (8 rows each) per batch for int8
+// rows, 16 for the half-size int4 sketch rows (the same bytes in flight).
+__host__ __device__ constexpr int batch_candidates(int ns8, bool q4) {
+    return ns8 >= (q4 ? 16 : 8) ? 1 : (q4 ? 16 : 8) / ns8;
+}
 
 struct PruneParams {
     const uint16_t* q;        // [B][Hq][d]
@@ -67,24 +74,21 @@ struct PruneParams {
 // (0,2,4,6) (1,3,5,7) (8,...,14) (9,...,15) of the lane's 16, which is the
 // channel order split_query4 gives qh and ql; S = Q . u - 8 sum(Q), the
 // constant `corr` = 8 sum(Q) being subtracted from every row's score.
+// One load batch of a wave: CB candidates (starts xs, -1 = none) x NS8
+// slots of 8 rows.  load() issues every row load of the batch; score()
+// consumes them, so the two can be separated by work that does not touch
+// the rows (the first stage issues its loads before it forms the query).
 template <int NS8, bool FUSE, bool Q4>
-__device__ __forceinline__ void score_slice(const PruneParams& p, const int* cstart, int64_t L,
-                                            const int8_t* __restrict__ k8_bj, const uint8_t* __restrict__ k4_bj,
-                                            const u32x4& qh, const u32x4& ql, int corr, int first,
-                                            int32_t* __restrict__ out, int32_t* __restrict__ pre_bj) {
-    const StageDev& st = p.cur;
-    constexpr int CB = NS8 >= 8 ? 1 : 8 / NS8;     // candidates per batch
-    constexpr int NL = CB * NS8;                   // loads per batch
-    const int lane = threadIdx.x & 63, row8 = lane >> 3, sl = lane & 7;
-    bool own[NS8];                                 // row of slot it is one of this stage's samples
-#pragma unroll
-    for (int it = 0; it < NS8; ++it) own[it] = !FUSE || ((it * 8 + row8) % p.fuse_m) == 0;
-    for (int c0 = 0; c0 < p.cpw; c0 += CB) {
-        int64_t xs[CB];
-#pragma unroll
-        for (int c = 0; c < CB; ++c) xs[c] = (c0 + c < p.cpw) ? cstart[c0 + c] : -1;
-        u32x4 v[NL];
-        bool ok[NL];
+struct RowBatch {
+    static constexpr int CB = batch_candidates(NS8, Q4);   // candidates per batch
+    static constexpr int NL = CB * NS8;                    // loads per batch
+    u32x4 v8[Q4 ? 1 : NL];      // int8 rows as loaded
+    u32x2 v4[Q4 ? NL : 1];      // int4 sketch rows as loaded (unpacked at use)
+    bool ok[NL];
+
+    __device__ __forceinline__ void load(const PruneParams& p, const int64_t (&xs)[CB], int64_t L,
+                                         const int8_t* __restrict__ k8_bj, const uint8_t* __restrict__ k4_bj) {
+        const int lane = threadIdx.x & 63, row8 = lane >> 3, sl = lane & 7;
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
             const int c = u / NS8, it = u % NS8;
@@ -93,42 +97,92 @@ __device__ __forceinline__ void score_slice(const PruneParams& p, const int* cst
             ok[u] = xs[c] >= 0 && i < p.nrows && t < L;
             if constexpr (Q4) {
                 const int64_t row = int64_t(int(xs[c]) / p.rstride) + i;   // = t / rstride
-                const u32x2 w = ok[u] ? __builtin_nontemporal_load(
-                                            reinterpret_cast<const u32x2*>(k4_bj + row * (kHeadDim / 2)) + sl)
-                                      : u32x2{0u, 0u};
-                v[u] = u32x4{w.x & 0x0f0f0f0fu, (w.x >> 4) & 0x0f0f0f0fu, w.y & 0x0f0f0f0fu, (w.y >> 4) & 0x0f0f0f0fu};
+                v4[u] = ok[u] ? __builtin_nontemporal_load(
+                                    reinterpret_cast<const u32x2*>(k4_bj + row * (kHeadDim / 2)) + sl)
+                              : u32x2{0u, 0u};
             } else {
-                v[u] = ok[u] ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k8_bj + t * kHeadDim) + sl)
-                             : u32x4{0, 0, 0, 0};
+                v8[u] = ok[u] ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k8_bj + t * kHeadDim) + sl)
+                              : u32x4{0, 0, 0, 0};
             }
         }
+    }
+
+    // Scores candidates first + c (c < CB, first + c < ncand, c < nvalid)
+    // into out (and, with FUSE, every child's score into pre_bj).
+    __device__ __forceinline__ void score(const PruneParams& p, const u32x4& qh, const u32x4& ql, int corr,
+                                          int first, int nvalid, int32_t* __restrict__ out,
+                                          int32_t* __restrict__ pre_bj) const {
+        const StageDev& st = p.cur;
+        const int lane = threadIdx.x & 63, row8 = lane >> 3;
+        bool own[NS8];                             // row of slot it is one of this stage's samples
+#pragma unroll
+        for (int it = 0; it < NS8; ++it) own[it] = !FUSE || ((it * 8 + row8) % p.fuse_m) == 0;
         int best[CB];
 #pragma unroll
         for (int c = 0; c < CB; ++c) best[c] = INT32_MIN;
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
-            int ah = __builtin_amdgcn_sdot4((int)qh.x, (int)v[u].x, 0, false);
-            ah = __builtin_amdgcn_sdot4((int)qh.y, (int)v[u].y, ah, false);
-            ah = __builtin_amdgcn_sdot4((int)qh.z, (int)v[u].z, ah, false);
-            ah = __builtin_amdgcn_sdot4((int)qh.w, (int)v[u].w, ah, false);
-            int al = __builtin_amdgcn_sdot4((int)ql.x, (int)v[u].x, 0, false);
-            al = __builtin_amdgcn_sdot4((int)ql.y, (int)v[u].y, al, false);
-            al = __builtin_amdgcn_sdot4((int)ql.z, (int)v[u].z, al, false);
-            al = __builtin_amdgcn_sdot4((int)ql.w, (int)v[u].w, al, false);
+            u32x4 x;
+            if constexpr (Q4) {
+                const u32x2 w = v4[u];
+                x = u32x4{w.x & 0x0f0f0f0fu, (w.x >> 4) & 0x0f0f0f0fu, w.y & 0x0f0f0f0fu, (w.y >> 4) & 0x0f0f0f0fu};
+            } else {
+                x = v8[u];
+            }
+            int ah = __builtin_amdgcn_sdot4((int)qh.x, (int)x.x, 0, false);
+            ah = __builtin_amdgcn_sdot4((int)qh.y, (int)x.y, ah, false);
+            ah = __builtin_amdgcn_sdot4((int)qh.z, (int)x.z, ah, false);
+            ah = __builtin_amdgcn_sdot4((int)qh.w, (int)x.w, ah, false);
+            int al = __builtin_amdgcn_sdot4((int)ql.x, (int)x.x, 0, false);
+            al = __builtin_amdgcn_sdot4((int)ql.y, (int)x.y, al, false);
+            al = __builtin_amdgcn_sdot4((int)ql.z, (int)x.z, al, false);
+            al = __builtin_amdgcn_sdot4((int)ql.w, (int)x.w, al, false);
             const int s = sum8_i(ah * 64 + al) - (Q4 ? corr : 0);
             if (ok[u] && own[u % NS8]) best[u / NS8] = max(best[u / NS8], s);
             if (FUSE) {
                 const int c = u / NS8, it = u % NS8;
                 const int sub = max_groups_i(ok[u] ? s : INT32_MIN);
-                if (lane == 0 && it < p.fuse_rq && c0 + c < p.cpw && first + c0 + c < st.ncand)
-                    pre_bj[int64_t(first + c0 + c) * p.fuse_rq + it] = sub;
+                if (lane == 0 && it < p.fuse_rq && c < nvalid && first + c < st.ncand)
+                    pre_bj[int64_t(first + c) * p.fuse_rq + it] = sub;
             }
         }
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
             const int m = max_groups_i(best[c]);
-            if (lane == 0 && c0 + c < p.cpw && first + c0 + c < st.ncand) out[first + c0 + c] = m;
+            if (lane == 0 && c < nvalid && first + c < st.ncand) out[first + c] = m;
         }
+    }
+};
+
+// Score `cpw` candidates per wave.  NS8 = rows per candidate / 8 (rounded up);
+// each load slot covers 8 rows (8 lanes x 16 bytes per 128-byte row).
+// cstart: LDS, the starts of this wave's candidates (-1 = none).  Rows
+// t = x + i * rstride, i < nrows, are read (8 lanes per row, 8 rows per load
+// slot).  Without FUSE they are this stage's samples.  With FUSE they are
+// the next stage's samples (rstride = its stride, one 8-row slot per child
+// chunk): this stage's score is the max over rows i % fuse_m == 0 (its own
+// samples), and each slot's max is written as that child's score.
+//
+// Q4 (first stage only, unfused): the rows are read from the int4 sketch
+// instead, row t at sketch row t / rstride (every first-stage sample is a
+// multiple of its stride), 8 lanes x 8 bytes per 64-byte row.  The nibbles
+// u = code + 8 are unpacked into four words of bytes, channels
+// (0,2,4,6) (1,3,5,7) (8,...,14) (9,...,15) of the lane's 16, which is the
+// channel order split_query4 gives qh and ql; S = Q . u - 8 sum(Q), the
+// constant `corr` = 8 sum(Q) being subtracted from every row's score.
+template <int NS8, bool FUSE, bool Q4>
+__device__ __forceinline__ void score_slice(const PruneParams& p, const int* cstart, int64_t L,
+                                            const int8_t* __restrict__ k8_bj, const uint8_t* __restrict__ k4_bj,
+                                            const u32x4& qh, const u32x4& ql, int corr, int first,
+                                            int32_t* __restrict__ out, int32_t* __restrict__ pre_bj) {
+    using RB = RowBatch<NS8, FUSE, Q4>;
+    for (int c0 = 0; c0 < p.cpw; c0 += RB::CB) {
+        int64_t xs[RB::CB];
+#pragma unroll
+        for (int c = 0; c < RB::CB; ++c) xs[c] = (c0 + c < p.cpw) ? cstart[c0 + c] : -1;
+        RB rb;
+        rb.load(p, xs, L, k8_bj, k4_bj);
+        rb.score(p, qh, ql, corr, first + c0, p.cpw - c0, out, pre_bj);
     }
 }
 
@@ -155,9 +209,11 @@ __device__ __forceinline__ void split_query(const int* Qlds, int sl, u32x4& qh, 
 }
 
 // split_query for the int4 sketch's channel order: words hold the lane's
-// channels (0,2,4,6), (1,3,5,7), (8,10,12,14), (9,11,13,15).
-__device__ __forceinline__ void split_query4(const int* Qlds, int sl, u32x4& qh, u32x4& ql) {
+// channels (0,2,4,6), (1,3,5,7), (8,10,12,14), (9,11,13,15).  Returns the
+// sum of Q over all 128 channels (the lane's 16, summed over its 8-lane group).
+__device__ __forceinline__ int split_query4(const int* Qlds, int sl, u32x4& qh, u32x4& ql) {
     uint32_t h4[4], l4[4];
+    int sq = 0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         uint32_t hw = 0, lw = 0;
@@ -165,6 +221,7 @@ __device__ __forceinline__ void split_query4(const int* Qlds, int sl, u32x4& qh,
         for (int u = 0; u < 4; ++u) {
             const int ch = (w >> 1) * 8 + 2 * u + (w & 1);
             const int Q = Qlds[sl * 16 + ch];
+            sq += Q;
             const int lo = ((Q + 32) & 63) - 32;
             const int hi = (Q - lo) >> 6;
             hw |= (uint32_t(hi) & 0xffu) << (8 * u);
@@ -175,6 +232,7 @@ __device__ __forceinline__ void split_query4(const int* Qlds, int sl, u32x4& qh,
     }
     qh = u32x4{h4[0], h4[1], h4[2], h4[3]};
     ql = u32x4{l4[0], l4[1], l4[2], l4[3]};
+    return sum8_i(sq);
 }
 
 // One instantiation per (rows per candidate / 8, select code of the
@@ -195,6 +253,34 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
     const bool bad = Lraw < 1 || Lraw > p.Lmax;
     const int64_t L = bad ? 0 : Lraw;          // an invalid request has no candidates
     int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
+
+    const int8_t* k8_bj = p.k8 + int64_t(bj) * p.Lmax * kHeadDim;
+    const uint8_t* k4_bj = Q4 ? p.k4 + int64_t(bj) * p.k4_rows * (kHeadDim / 2) : nullptr;
+    int32_t* scores_bj = p.scores + int64_t(bj) * p.cur.ncand;
+    const int wave = threadIdx.x >> 6;
+    const int sl = threadIdx.x & 7;
+    if constexpr (SEL == 0 && !FUSE) {
+        // First stage, one load batch per wave (cpw = CB): the candidate
+        // starts follow from the indices, so the rows are loaded first and
+        // the query codes are formed while the loads are in flight.
+        using RB = RowBatch<NS8, false, Q4>;
+        const int first = (blockIdx.x * kPruneWaves + wave) * p.cpw;
+        int64_t xs[RB::CB];
+#pragma unroll
+        for (int c = 0; c < RB::CB; ++c) xs[c] = c < p.cpw ? cand_start(p.cur, true, nullptr, first + c, L) : -1;
+        RB rb;
+        rb.load(p, xs, L, k8_bj, k4_bj);
+        if (bad && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(p.flag, 1);
+        group_query_codes(p.q + int64_t(b) * p.Hq * kHeadDim, j, p.G, Qlds, nullptr);
+        if (blockIdx.x == 0 && threadIdx.x < kHeadDim)
+            p.qgroup[int64_t(bj) * kHeadDim + threadIdx.x] = Qlds[threadIdx.x];
+        u32x4 qh, ql;
+        int corr = 0;
+        if constexpr (Q4) corr = 8 * split_query4(Qlds, sl, qh, ql);
+        else split_query(Qlds, sl, qh, ql);
+        rb.score(p, qh, ql, corr, first, p.cpw, scores_bj, nullptr);
+        return;
+    }
 
     const int32_t* parents = nullptr;
     if constexpr (SEL == 0 || SEL == kGiven) {
@@ -227,25 +313,13 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
     const int wg_first = blockIdx.x * kPruneWaves * p.cpw;
     if (int(threadIdx.x) < kPruneWaves * p.cpw)
         cstart[threadIdx.x] = int(cand_start(p.cur, SEL == 0, parents, wg_first + threadIdx.x, L));
-    const int sl = threadIdx.x & 7;
     u32x4 qh, ql;
-    int corr = 0;
-    if constexpr (Q4) {
-        split_query4(Qlds, sl, qh, ql);
-        int sq = 0;
-        for (int c = 0; c < kHeadDim; ++c) sq += Qlds[c];     // the same in every thread
-        corr = 8 * sq;
-    } else {
-        split_query(Qlds, sl, qh, ql);
-    }
+    split_query(Qlds, sl, qh, ql);
     __syncthreads();
 
-    const int8_t* k8_bj = p.k8 + int64_t(bj) * p.Lmax * kHeadDim;
-    const uint8_t* k4_bj = Q4 ? p.k4 + int64_t(bj) * p.k4_rows * (kHeadDim / 2) : nullptr;
-    int32_t* scores_bj = p.scores + int64_t(bj) * p.cur.ncand;
-    const int wave = threadIdx.x >> 6;
     const int first = wg_first + wave * p.cpw;
-    score_slice<NS8, FUSE, Q4>(p, cstart + wave * p.cpw, L, k8_bj, k4_bj, qh, ql, corr, first, scores_bj,
+    // (the int4 sketch serves only the first stage, which returned above)
+    score_slice<NS8, FUSE, false>(p, cstart + wave * p.cpw, L, k8_bj, nullptr, qh, ql, 0, first, scores_bj,
                                FUSE ? p.pre + int64_t(bj) * p.cur.ncand * p.fuse_rq : nullptr);
     if constexpr (SEL != 0 && SEL != kGiven) {
         // workgroup 0 publishes the previous stage's kept set (ascending,
@@ -320,6 +394,9 @@ hipError_t launch_prune_stage(sd_ctx* c, int st, bool given, bool fused, const u
     }
     const bool q4 = k4 != nullptr && st == 0 && !fuse;
     if (q4) {
+        // one batch of int4 candidates per wave (batch_candidates(ns8, true))
+        p.cpw = batch_candidates(ns8 == 1 ? 1 : ns8 == 2 ? 2 : ns8 <= 4 ? 4 : 8, true);
+        grid.x = (p.cur.ncand + kPruneWaves * p.cpw - 1) / (kPruneWaves * p.cpw);
         if (ns8 == 1) launch(sd_prune_stage_kernel<1, 0, false, true>, grid, dim3(kPruneThreads), lds, s, t, p);
         else if (ns8 == 2) launch(sd_prune_stage_kernel<2, 0, false, true>, grid, dim3(kPruneThreads), lds, s, t, p);
         else if (ns8 <= 4) launch(sd_prune_stage_kernel<4, 0, false, true>, grid, dim3(kPruneThreads), lds, s, t, p);
