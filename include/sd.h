@@ -154,13 +154,18 @@ sd_status sd_quantize_keys(sd_ctx* ctx, const uint16_t* k_bf16, const int32_t* l
  *  k_bf16, k_int8, v  device caches ([B][Hkv][Lmax][d]); rows
  *           [L_b, L_b + n_new) are written (all rows t < L_b + n_new of
  *           k_int8 when the scale grew).
+ *  k_sketch4 device int4 first-stage sketch (see sd_quantize_sketch4) kept
+ *           up to date as well, or NULL: the new rows t that are multiples
+ *           of stage[0].stride are coded into it, and when a scale grew all
+ *           of that (request, KV head)'s sketch rows are recoded, so it
+ *           equals sd_quantize_sketch4 of the grown cache.
  *  k_absmax device [B][Hkv] fp32 output a', or NULL.
  * A request with L_b < 1 or L_b + n_new > Lmax is left untouched and
  * raises the device flag (see sd_check).  Needs values_on_host = 0 (else
  * SD_ERR_UNSUPPORTED).  Allocates nothing. */
 sd_status sd_append_kv(sd_ctx* ctx, const uint16_t* k_new, const uint16_t* v_new, int32_t n_new,
                        const int32_t* lengths, uint16_t* k_bf16, int8_t* k_int8, uint16_t* v,
-                       float* k_absmax, void* stream);
+                       uint8_t* k_sketch4, float* k_absmax, void* stream);
 
 /* One decode step (parts 2 and 3).
  *  q        device [B][Hq][d] bf16 query of the step.
@@ -239,8 +244,8 @@ sd_status sd_dense_decode(sd_ctx* ctx, const uint16_t* q, const uint16_t* k_bf16
 int64_t sd_sketch4_rows(const sd_ctx* ctx);
 
 /* Writes the sketch of the cache whose scales the context holds (the last
- * sd_quantize_keys on this context; sd_append_kv does not update a sketch:
- * call this again after appends).
+ * sd_quantize_keys on this context, and the sd_append_kv calls after it;
+ * an append given the sketch keeps it up to date).
  *  k_bf16     device [B][Hkv][Lmax][d] bf16 keys.
  *  lengths    device [B] int32 in [1, Lmax] (other requests are skipped).
  *  k_sketch4  device [B][Hkv][sd_sketch4_rows][64] uint8 output; rows

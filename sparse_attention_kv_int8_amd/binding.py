@@ -75,7 +75,7 @@ _SIGS = {
     "sd_decode_step": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "sd_decode_step_reuse": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, C.c_int32, _p]),
     "sd_dense_decode": (C.c_int, [_p, _p, _p, _p, _p, _p, _p]),
-    "sd_append_kv": (C.c_int, [_p, _p, _p, C.c_int32, _p, _p, _p, _p, _p, _p]),
+    "sd_append_kv": (C.c_int, [_p, _p, _p, C.c_int32, _p, _p, _p, _p, _p, _p, _p]),
     "sd_sketch4_rows": (C.c_int64, [_p]),
     "sd_quantize_sketch4": (C.c_int, [_p, _p, _p, _p, _p]),
     "sd_decode_step_sketch4": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
@@ -195,9 +195,11 @@ class SparseDecoder:
         check(lib.sd_dense_decode(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(lengths), _ptr(out),
                                   _stream(stream)), "sd_dense_decode")
 
-    def sd_append_kv(self, k_new, v_new, n_new: int, lengths, k, k_int8, v, k_absmax=None, stream=None) -> None:
+    def sd_append_kv(self, k_new, v_new, n_new: int, lengths, k, k_int8, v, k_absmax=None, stream=None,
+                     k_sketch4=None) -> None:
         check(lib.sd_append_kv(self.handle, _ptr(k_new), _ptr(v_new), int(n_new), _ptr(lengths), _ptr(k),
-                               _ptr(k_int8), _ptr(v), _ptr(k_absmax), _stream(stream)), "sd_append_kv")
+                               _ptr(k_int8), _ptr(v), _ptr(k_sketch4), _ptr(k_absmax), _stream(stream)),
+              "sd_append_kv")
 
     def sd_sketch4_rows(self) -> int:
         return int(lib.sd_sketch4_rows(self.handle))

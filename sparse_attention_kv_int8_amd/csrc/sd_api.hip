@@ -331,15 +331,16 @@ sd_status sd_quantize_keys(sd_ctx* c, const uint16_t* k, const int32_t* lengths,
 }
 
 sd_status sd_append_kv(sd_ctx* c, const uint16_t* k_new, const uint16_t* v_new, int32_t n_new, const int32_t* lengths,
-                       uint16_t* k, int8_t* k8, uint16_t* v, float* absmax, void* stream) {
+                       uint16_t* k, int8_t* k8, uint16_t* v, uint8_t* k4, float* absmax, void* stream) {
     if (!c || !k_new || !v_new || !lengths || !k || !k8 || !v) return SD_ERR_INVALID_ARG;
-    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k) || !aligned16(k8) || !aligned16(v))
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k) || !aligned16(k8) || !aligned16(v) ||
+        (k4 && !aligned16(k4)))
         return SD_ERR_INVALID_ARG;
     if (n_new < 1 || n_new > c->Lmax) return SD_ERR_INVALID_ARG;
     if (c->cfg.values_on_host) return SD_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return from_hip(timed(c, SD_PROF_APPEND, s, [&](sd::Timing t) {
-        return sd::launch_append(c, k_new, v_new, n_new, lengths, k, k8, v, absmax, s, t);
+        return sd::launch_append(c, k_new, v_new, n_new, lengths, k, k8, v, k4, absmax, s, t);
     }));
 }
 

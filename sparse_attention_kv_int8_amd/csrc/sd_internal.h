@@ -121,7 +121,8 @@ hipError_t launch_quantize_keys(sd_ctx* c, const uint16_t* k, const int32_t* len
 // Appends n rows per (request, KV head) at lengths[b] and recodes the rows of
 // the (request, KV head)s whose key scale grew.
 hipError_t launch_append(sd_ctx* c, const uint16_t* k_new, const uint16_t* v_new, int n, const int32_t* lengths,
-                         uint16_t* k, int8_t* k8, uint16_t* v, float* absmax, hipStream_t s, Timing t = {});
+                         uint16_t* k, int8_t* k8, uint16_t* v, uint8_t* k4, float* absmax, hipStream_t s,
+                         Timing t = {});
 hipError_t launch_quantize_query(sd_ctx* c, const uint16_t* q, int8_t* q8, int32_t* qg, hipStream_t s);
 // given: the kept set that the launch would select (stage - 1's for a
 // pruning stage, the last stage's for the decode and value-cache kernels)

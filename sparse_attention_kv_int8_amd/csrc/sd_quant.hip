@@ -115,11 +115,27 @@ __global__ __launch_bounds__(kQuantThreads) void sd_quantize_kernel(
 // scale, as nibbles code + 8 (1..15), channel 2m in the low and channel
 // 2m + 1 in the high nibble of byte m (64 bytes per row).  16 threads per
 // row, each codes 8 channels (one 16-byte load) into one 4-byte word.
+__device__ __forceinline__ uint32_t sketch_word(u32x4 w, float a) {
+    const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+    uint32_t word = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t lo = uint32_t(code4_of(bf16_lo(x[m]), a) + 8);
+        const uint32_t hi = uint32_t(code4_of(bf16_hi(x[m]), a) + 8);
+        word |= (lo | (hi << 4)) << (8 * m);
+    }
+    return word;
+}
+
+// Rows of t < lengths[b] + len_add; with `only` set, a (request, KV head)
+// whose only[bj] is 0 is skipped (the append's recoding).
 __global__ __launch_bounds__(kQuantThreads) void sd_sketch4_kernel(
-    const uint16_t* __restrict__ k, const int32_t* __restrict__ lengths, int64_t Lmax, int Hkv, int stride,
-    int64_t rows, const unsigned* __restrict__ absmax_bits, uint8_t* __restrict__ k4) {
+    const uint16_t* __restrict__ k, const int32_t* __restrict__ lengths, int len_add, int64_t Lmax, int Hkv,
+    int stride, int64_t rows, const unsigned* __restrict__ absmax_bits, const int32_t* __restrict__ only,
+    uint8_t* __restrict__ k4) {
     const int bj = blockIdx.y, b = bj / Hkv;
-    const int64_t L = lengths[b];
+    if (only && only[bj] == 0) return;
+    const int64_t L = int64_t(lengths[b]) + len_add;
     if (L < 1 || L > Lmax) return;
     const float a = bf16_to_f32(uint16_t(absmax_bits[bj]));
     const int64_t n = (L + stride - 1) / stride;             // sketch rows of this request
@@ -128,16 +144,7 @@ __global__ __launch_bounds__(kQuantThreads) void sd_sketch4_kernel(
     const int sub = threadIdx.x & 15;
     for (int64_t i = int64_t(blockIdx.x) * kQuantRowsPerWg + (threadIdx.x >> 4);
          i < min(n, int64_t(blockIdx.x + 1) * kQuantRowsPerWg); i += kQuantThreads / 16) {
-        const u32x4 w = src[i * stride * 16 + sub];
-        const uint32_t x[4] = {w.x, w.y, w.z, w.w};
-        uint32_t word = 0;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const uint32_t lo = uint32_t(code4_of(bf16_lo(x[m]), a) + 8);
-            const uint32_t hi = uint32_t(code4_of(bf16_hi(x[m]), a) + 8);
-            word |= (lo | (hi << 4)) << (8 * m);
-        }
-        dst[i * 16 + sub] = word;
+        dst[i * 16 + sub] = sketch_word(src[i * stride * 16 + sub], a);
     }
 }
 
@@ -153,7 +160,8 @@ __global__ __launch_bounds__(kQuantThreads) void sd_append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, int n,
     const int32_t* __restrict__ lengths, int64_t Lmax, int Hkv, uint16_t* __restrict__ k, int8_t* __restrict__ k8,
     uint16_t* __restrict__ v, unsigned* __restrict__ absmax_bits, int32_t* __restrict__ requant,
-    float* __restrict__ absmax_out, int32_t* __restrict__ flag) {
+    float* __restrict__ absmax_out, int32_t* __restrict__ flag, uint8_t* __restrict__ k4, int stride4,
+    int64_t rows4) {
     const int j = blockIdx.x, b = blockIdx.y, bj = b * Hkv + j;
     const int64_t L = lengths[b];
     if (L < 1 || L > Lmax - n) {
@@ -190,11 +198,14 @@ __global__ __launch_bounds__(kQuantThreads) void sd_append_kernel(
     u32x4* kd = reinterpret_cast<u32x4*>(k + (int64_t(bj) * Lmax + L) * kHeadDim);
     u32x4* vd = reinterpret_cast<u32x4*>(v + (int64_t(bj) * Lmax + L) * kHeadDim);
     uint2* k8d = reinterpret_cast<uint2*>(k8 + (int64_t(bj) * Lmax + L) * kHeadDim);
+    uint32_t* k4d = k4 ? reinterpret_cast<uint32_t*>(k4 + int64_t(bj) * rows4 * (kHeadDim / 2)) : nullptr;
     for (int64_t e = threadIdx.x; e < ne; e += kQuantThreads) {
         const u32x4 w = ks[e];
         kd[e] = w;
         k8d[e] = codes8(w, a);
         vd[e] = vs[e];
+        const int64_t t = L + e / 16;             // token of this word
+        if (k4d && t % stride4 == 0) k4d[(t / stride4) * 16 + e % 16] = sketch_word(w, a);
     }
 }
 
@@ -231,24 +242,30 @@ hipError_t launch_sketch4(sd_ctx* c, const uint16_t* k, const int32_t* lengths, 
     const int BH = c->cfg.batch * c->cfg.num_kv_heads;
     const int64_t rows = c->sketch_rows;
     const int nwg = int((rows + kQuantRowsPerWg - 1) / kQuantRowsPerWg);
-    launch(sd_sketch4_kernel, dim3(nwg, BH), dim3(kQuantThreads), 0, s, Timing{}, k, lengths, c->Lmax,
-           c->cfg.num_kv_heads, c->st[0].stride, rows, (const unsigned*)c->absmax_bits, k4);
+    launch(sd_sketch4_kernel, dim3(nwg, BH), dim3(kQuantThreads), 0, s, Timing{}, k, lengths, 0, c->Lmax,
+           c->cfg.num_kv_heads, c->st[0].stride, rows, (const unsigned*)c->absmax_bits, (const int32_t*)nullptr, k4);
     return hipGetLastError();
 }
 
 hipError_t launch_append(sd_ctx* c, const uint16_t* k_new, const uint16_t* v_new, int n, const int32_t* lengths,
-                         uint16_t* k, int8_t* k8, uint16_t* v, float* absmax, hipStream_t s, Timing t) {
+                         uint16_t* k, int8_t* k8, uint16_t* v, uint8_t* k4, float* absmax, hipStream_t s, Timing t) {
     const int BH = c->cfg.batch * c->cfg.num_kv_heads;
     launch(sd_append_kernel, dim3(c->cfg.num_kv_heads, c->cfg.batch), dim3(kQuantThreads), 0, s,
            Timing{t.start, nullptr}, k_new, v_new, n, lengths, c->Lmax, c->cfg.num_kv_heads, k, k8, v,
-           c->absmax_bits, c->requant, absmax, c->flag);
+           c->absmax_bits, c->requant, absmax, c->flag, k4, c->st[0].stride, c->sketch_rows);
     // recoding of every row of the (request, KV head)s whose scale grew: at
     // most 64 workgroups per (request, KV head), each looping over row tiles
-    // (the others exit at once)
+    // (the others exit at once); then their sketch rows
     const int ntile = int((c->Lmax + kQuantRowsPerWg - 1) / kQuantRowsPerWg);
-    launch(sd_quantize_kernel, dim3(std::min(ntile, 64), BH), dim3(kQuantThreads), 0, s, Timing{nullptr, t.stop},
-           (const uint16_t*)k, lengths, n, c->Lmax, c->cfg.num_kv_heads, (const unsigned*)c->absmax_bits,
-           (const int32_t*)c->requant, k8, (float*)nullptr);
+    launch(sd_quantize_kernel, dim3(std::min(ntile, 64), BH), dim3(kQuantThreads), 0, s,
+           Timing{nullptr, k4 ? nullptr : t.stop}, (const uint16_t*)k, lengths, n, c->Lmax, c->cfg.num_kv_heads,
+           (const unsigned*)c->absmax_bits, (const int32_t*)c->requant, k8, (float*)nullptr);
+    if (k4) {
+        const int nwg4 = int((c->sketch_rows + kQuantRowsPerWg - 1) / kQuantRowsPerWg);
+        launch(sd_sketch4_kernel, dim3(nwg4, BH), dim3(kQuantThreads), 0, s, Timing{nullptr, t.stop},
+               (const uint16_t*)k, lengths, n, c->Lmax, c->cfg.num_kv_heads, c->st[0].stride, c->sketch_rows,
+               (const unsigned*)c->absmax_bits, (const int32_t*)c->requant, k4);
+    }
     return hipGetLastError();
 }
 

@@ -165,3 +165,64 @@ def test_append_llama8b_128k():
     out, kept = g.step(inp.q)
     compare_step(inp, inp.q, k8_ref, out, kept)
     assert g.dec.sd_check() == 0
+
+
+def test_append_keeps_the_int4_sketch_current():
+    """Appends given the int4 first-stage sketch keep it equal to the
+    oracle's sketch of the grown cache (new rows at multiples of the first
+    stride, and every row of a head whose scale grew); a sketch step on the
+    grown cache then matches the oracle."""
+    import torch
+    from tests.gpu_util import bf16_dev_to_bits, oracle_config
+    w = tiny_workload(name="append_sketch", batch=2, num_q_heads=8, num_kv_heads=2, max_context=8192)
+    print("case append with sketch", flush=True)
+    inp = make_inputs(w, lengths=[5001, 7000])
+    g = GpuRun(inp)
+    g.quantize()
+    r1 = w.stages[0].stride
+    sk = torch.zeros((w.batch, w.num_kv_heads, g.dec.sd_sketch4_rows(), 64), dtype=torch.uint8, device="cuda")
+    g.dec.sd_quantize_sketch4(g.k, g.lengths, sk)
+
+    def sketch_append(k_new, v_new):
+        n = k_new.shape[2]
+        before = inp.lengths.copy()
+        g.dec.sd_append_kv(to_dev_bf16(k_new), to_dev_bf16(v_new), n, g.lengths, g.k, g.k8, g.v, g.absmax,
+                           k_sketch4=sk)
+        torch.cuda.synchronize()
+        for b in range(w.batch):
+            L = int(before[b])
+            inp.k[b, :, L:L + n] = k_new[b]
+            inp.v[b, :, L:L + n] = v_new[b]
+            inp.lengths[b] = L + n
+        g.set_lengths(inp.lengths)
+
+    def check_sketch():
+        got = sk.cpu().numpy()
+        dec = np.empty(got.shape[:-1] + (128,), np.int8)
+        dec[..., 0::2] = (got & 15).astype(np.int8) - 8
+        dec[..., 1::2] = (got >> 4).astype(np.int8) - 8
+        ref = [[O.key_sketch4(inp.k[b, j], int(inp.lengths[b]), r1) for j in range(w.num_kv_heads)]
+               for b in range(w.batch)]
+        for b in range(w.batch):
+            n = -(-int(inp.lengths[b]) // r1)
+            for j in range(w.num_kv_heads):
+                assert np.array_equal(dec[b, j, :n], ref[b][j]), f"sketch differs (request {b}, head {j})"
+        return ref
+
+    k_new, v_new = make_append_tokens(w, 13, seed=21)
+    sketch_append(k_new, v_new)                 # crosses multiples of the first stride
+    check_sketch()
+    a0 = g.absmax.cpu().numpy().copy()
+    k_new, v_new = make_append_tokens(w, 3, seed=22)
+    big = np.float32(6.0) * a0[1, 0]
+    k_new[1, 0, 2, 64] = np.frombuffer(np.float32(big).tobytes(), np.uint32)[0] >> 16
+    sketch_append(k_new, v_new)                 # raises request 1, head 0's scale
+    assert g.absmax.cpu().numpy()[1, 0] > a0[1, 0]
+    ref_sk = check_sketch()
+    k8_ref = check_codes(g)
+    q = to_dev_bf16(inp.q_step0)
+    g.dec.sd_decode_step_sketch4(q, g.k, g.k8, sk, g.v, g.lengths, g.out, g.kept)
+    torch.cuda.synchronize()
+    res = O.decode_step(inp.q_step0, inp.k, k8_ref, inp.v, inp.lengths, oracle_config(w), sketch4=ref_sk)
+    compare_step(inp, inp.q_step0, k8_ref, bf16_dev_to_bits(g.out), g.kept.cpu().numpy(), ref=res)
+    assert g.dec.sd_check() == 0
