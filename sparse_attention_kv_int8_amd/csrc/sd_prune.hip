@@ -26,14 +26,7 @@ namespace sd {
 
 constexpr int kPruneThreads = 256;
 constexpr int kPruneWaves = kPruneThreads / kWave;
-constexpr int kMaxCandPerWave = 16;         // candidates per wave (int8: one batch of 8 row loads; int4
-                                            // sketch: one batch of 16, twice the candidates)
-
-// Candidates per load batch: 8 row loads (8 rows each) per batch for int8
-// rows, 16 for the half-size int4 sketch rows (the same bytes in flight).
-__host__ __device__ constexpr int batch_candidates(int ns8, bool q4) {
-    return ns8 >= (q4 ? 16 : 8) ? 1 : (q4 ? 16 : 8) / ns8;
-}
+constexpr int kMaxCandPerWave = 8;          // candidates per wave (one batch of 8 row loads)
 
 struct PruneParams {
     const uint16_t* q;        // [B][Hq][d]
@@ -58,36 +51,20 @@ struct PruneParams {
     int64_t k4_rows;
 };
 
-// Score `cpw` candidates per wave.  NS8 = rows per candidate / 8 (rounded up);
-// each load slot covers 8 rows (8 lanes x 16 bytes per 128-byte row).
-// cstart: LDS, the starts of this wave's candidates (-1 = none).  Rows
-// t = x + i * rstride, i < nrows, are read (8 lanes per row, 8 rows per load
-// slot).  Without FUSE they are this stage's samples.  With FUSE they are
-// the next stage's samples (rstride = its stride, one 8-row slot per child
-// chunk): this stage's score is the max over rows i % fuse_m == 0 (its own
-// samples), and each slot's max is written as that child's score.
-//
-// Q4 (first stage only, unfused): the rows are read from the int4 sketch
-// instead, row t at sketch row t / rstride (every first-stage sample is a
-// multiple of its stride), 8 lanes x 8 bytes per 64-byte row.  The nibbles
-// u = code + 8 are unpacked into four words of bytes, channels
-// (0,2,4,6) (1,3,5,7) (8,...,14) (9,...,15) of the lane's 16, which is the
-// channel order split_query4 gives qh and ql; S = Q . u - 8 sum(Q), the
-// constant `corr` = 8 sum(Q) being subtracted from every row's score.
 // One load batch of a wave: CB candidates (starts xs, -1 = none) x NS8
-// slots of 8 rows.  load() issues every row load of the batch; score()
-// consumes them, so the two can be separated by work that does not touch
-// the rows (the first stage issues its loads before it forms the query).
-template <int NS8, bool FUSE, bool Q4>
+// slots of 8 rows (8 lanes x 16 bytes per 128-byte int8 row).  load()
+// issues every row load of the batch; score() consumes them, so the two
+// can be separated by work that does not touch the rows (the first stage
+// issues its loads before it forms the query).
+template <int NS8, bool FUSE>
 struct RowBatch {
-    static constexpr int CB = batch_candidates(NS8, Q4);   // candidates per batch
+    static constexpr int CB = NS8 >= 8 ? 1 : 8 / NS8;     // candidates per batch
     static constexpr int NL = CB * NS8;                    // loads per batch
-    u32x4 v8[Q4 ? 1 : NL];      // int8 rows as loaded
-    u32x2 v4[Q4 ? NL : 1];      // int4 sketch rows as loaded (unpacked at use)
+    u32x4 v[NL];
     bool ok[NL];
 
     __device__ __forceinline__ void load(const PruneParams& p, const int64_t (&xs)[CB], int64_t L,
-                                         const int8_t* __restrict__ k8_bj, const uint8_t* __restrict__ k4_bj) {
+                                         const int8_t* __restrict__ k8_bj) {
         const int lane = threadIdx.x & 63, row8 = lane >> 3, sl = lane & 7;
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
@@ -95,23 +72,15 @@ struct RowBatch {
             const int i = it * 8 + row8;
             const int64_t t = xs[c] + int64_t(i) * p.rstride;
             ok[u] = xs[c] >= 0 && i < p.nrows && t < L;
-            if constexpr (Q4) {
-                const int64_t row = int64_t(int(xs[c]) / p.rstride) + i;   // = t / rstride
-                v4[u] = ok[u] ? __builtin_nontemporal_load(
-                                    reinterpret_cast<const u32x2*>(k4_bj + row * (kHeadDim / 2)) + sl)
-                              : u32x2{0u, 0u};
-            } else {
-                v8[u] = ok[u] ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k8_bj + t * kHeadDim) + sl)
-                              : u32x4{0, 0, 0, 0};
-            }
+            v[u] = ok[u] ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k8_bj + t * kHeadDim) + sl)
+                         : u32x4{0, 0, 0, 0};
         }
     }
 
     // Scores candidates first + c (c < CB, first + c < ncand, c < nvalid)
     // into out (and, with FUSE, every child's score into pre_bj).
-    __device__ __forceinline__ void score(const PruneParams& p, const u32x4& qh, const u32x4& ql, int corr,
-                                          int first, int nvalid, int32_t* __restrict__ out,
-                                          int32_t* __restrict__ pre_bj) const {
+    __device__ __forceinline__ void score(const PruneParams& p, const u32x4& qh, const u32x4& ql, int first,
+                                          int nvalid, int32_t* __restrict__ out, int32_t* __restrict__ pre_bj) const {
         const StageDev& st = p.cur;
         const int lane = threadIdx.x & 63, row8 = lane >> 3;
         bool own[NS8];                             // row of slot it is one of this stage's samples
@@ -122,13 +91,7 @@ struct RowBatch {
         for (int c = 0; c < CB; ++c) best[c] = INT32_MIN;
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
-            u32x4 x;
-            if constexpr (Q4) {
-                const u32x2 w = v4[u];
-                x = u32x4{w.x & 0x0f0f0f0fu, (w.x >> 4) & 0x0f0f0f0fu, w.y & 0x0f0f0f0fu, (w.y >> 4) & 0x0f0f0f0fu};
-            } else {
-                x = v8[u];
-            }
+            const u32x4 x = v[u];
             int ah = __builtin_amdgcn_sdot4((int)qh.x, (int)x.x, 0, false);
             ah = __builtin_amdgcn_sdot4((int)qh.y, (int)x.y, ah, false);
             ah = __builtin_amdgcn_sdot4((int)qh.z, (int)x.z, ah, false);
@@ -137,7 +100,7 @@ struct RowBatch {
             al = __builtin_amdgcn_sdot4((int)ql.y, (int)x.y, al, false);
             al = __builtin_amdgcn_sdot4((int)ql.z, (int)x.z, al, false);
             al = __builtin_amdgcn_sdot4((int)ql.w, (int)x.w, al, false);
-            const int s = sum8_i(ah * 64 + al) - (Q4 ? corr : 0);
+            const int s = sum8_i(ah * 64 + al);
             if (ok[u] && own[u % NS8]) best[u / NS8] = max(best[u / NS8], s);
             if (FUSE) {
                 const int c = u / NS8, it = u % NS8;
@@ -154,6 +117,73 @@ struct RowBatch {
     }
 };
 
+// One load batch of the first stage from the int4 sketch: 4 lanes x 16
+// bytes per 64-byte sketch row (lane = 4 * row + part; part p holds
+// channels [32 p, 32 p + 32)), 16 rows per load slot, NS16 slots per
+// candidate, 8 loads per batch (CB = 8 / NS16 candidates).  Each 4-byte
+// word m of a part holds channels 8m .. 8m + 7 of it as nibbles (even
+// channels low); the low and high nibbles are unpacked into two words of
+// bytes, whose channel order split_query4w gives qh and ql.  The nibbles
+// are u = code + 8, so S = Q . u - 8 sum(Q) (`corr` = 8 sum(Q)); every
+// first-stage sample t is a multiple of the stride, at sketch row t / stride.
+template <int NS16>
+struct SketchBatch {
+    static constexpr int CB = 8 / NS16;
+    static constexpr int NL = CB * NS16;
+    u32x4 v[NL];
+    bool ok[NL];
+
+    __device__ __forceinline__ void load(const PruneParams& p, const int64_t (&xs)[CB], int64_t L,
+                                         const uint8_t* __restrict__ k4_bj) {
+        const int lane = threadIdx.x & 63, r16 = lane >> 2, part = lane & 3;
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const int c = u / NS16, it = u % NS16;
+            const int i = it * 16 + r16;
+            const int64_t t = xs[c] + int64_t(i) * p.rstride;
+            ok[u] = xs[c] >= 0 && i < p.nrows && t < L;
+            const int64_t row = int64_t(int(xs[c]) / p.rstride) + i;   // = t / rstride
+            v[u] = ok[u] ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k4_bj + row * (kHeadDim / 2)) + part)
+                         : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    __device__ __forceinline__ void score(const PruneParams& p, const uint32_t (&qh)[8], const uint32_t (&ql)[8],
+                                          int corr, int first, int nvalid, int32_t* __restrict__ out) const {
+        const int lane = threadIdx.x & 63;
+        int best[CB];
+#pragma unroll
+        for (int c = 0; c < CB; ++c) best[c] = INT32_MIN;
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            int ah = 0, al = 0;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int lo = int(w[m] & 0x0f0f0f0fu), hi = int((w[m] >> 4) & 0x0f0f0f0fu);
+                ah = __builtin_amdgcn_sdot4(int(qh[2 * m]), lo, ah, false);
+                ah = __builtin_amdgcn_sdot4(int(qh[2 * m + 1]), hi, ah, false);
+                al = __builtin_amdgcn_sdot4(int(ql[2 * m]), lo, al, false);
+                al = __builtin_amdgcn_sdot4(int(ql[2 * m + 1]), hi, al, false);
+            }
+            int sv = ah * 64 + al;
+            sv += dpp_i<kDppXor1>(sv);
+            sv += dpp_i<kDppXor2>(sv);                 // the row's score in its 4 lanes
+            if (ok[u]) best[u / NS16] = max(best[u / NS16], sv - corr);
+        }
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+            // max over the 16 row groups: groups of a row of 16 lanes, then the four rows
+            int m = best[c];
+            m = max(m, dpp_i<0x124>(m));               // row_ror:4
+            m = max(m, dpp_i<kDppRor8>(m));
+            m = max(max(__builtin_amdgcn_readlane(m, 0), __builtin_amdgcn_readlane(m, 16)),
+                    max(__builtin_amdgcn_readlane(m, 32), __builtin_amdgcn_readlane(m, 48)));
+            if (lane == 0 && c < nvalid && first + c < p.cur.ncand) out[first + c] = m;
+        }
+    }
+};
+
 // Score `cpw` candidates per wave.  NS8 = rows per candidate / 8 (rounded up);
 // each load slot covers 8 rows (8 lanes x 16 bytes per 128-byte row).
 // cstart: LDS, the starts of this wave's candidates (-1 = none).  Rows
@@ -162,27 +192,18 @@ struct RowBatch {
 // the next stage's samples (rstride = its stride, one 8-row slot per child
 // chunk): this stage's score is the max over rows i % fuse_m == 0 (its own
 // samples), and each slot's max is written as that child's score.
-//
-// Q4 (first stage only, unfused): the rows are read from the int4 sketch
-// instead, row t at sketch row t / rstride (every first-stage sample is a
-// multiple of its stride), 8 lanes x 8 bytes per 64-byte row.  The nibbles
-// u = code + 8 are unpacked into four words of bytes, channels
-// (0,2,4,6) (1,3,5,7) (8,...,14) (9,...,15) of the lane's 16, which is the
-// channel order split_query4 gives qh and ql; S = Q . u - 8 sum(Q), the
-// constant `corr` = 8 sum(Q) being subtracted from every row's score.
-template <int NS8, bool FUSE, bool Q4>
+template <int NS8, bool FUSE>
 __device__ __forceinline__ void score_slice(const PruneParams& p, const int* cstart, int64_t L,
-                                            const int8_t* __restrict__ k8_bj, const uint8_t* __restrict__ k4_bj,
-                                            const u32x4& qh, const u32x4& ql, int corr, int first,
-                                            int32_t* __restrict__ out, int32_t* __restrict__ pre_bj) {
-    using RB = RowBatch<NS8, FUSE, Q4>;
+                                            const int8_t* __restrict__ k8_bj, const u32x4& qh, const u32x4& ql,
+                                            int first, int32_t* __restrict__ out, int32_t* __restrict__ pre_bj) {
+    using RB = RowBatch<NS8, FUSE>;
     for (int c0 = 0; c0 < p.cpw; c0 += RB::CB) {
         int64_t xs[RB::CB];
 #pragma unroll
         for (int c = 0; c < RB::CB; ++c) xs[c] = (c0 + c < p.cpw) ? cstart[c0 + c] : -1;
         RB rb;
-        rb.load(p, xs, L, k8_bj, k4_bj);
-        rb.score(p, qh, ql, corr, first + c0, p.cpw - c0, out, pre_bj);
+        rb.load(p, xs, L, k8_bj);
+        rb.score(p, qh, ql, first + c0, p.cpw - c0, out, pre_bj);
     }
 }
 
@@ -208,31 +229,30 @@ __device__ __forceinline__ void split_query(const int* Qlds, int sl, u32x4& qh, 
     ql = u32x4{l4[0], l4[1], l4[2], l4[3]};
 }
 
-// split_query for the int4 sketch's channel order: words hold the lane's
-// channels (0,2,4,6), (1,3,5,7), (8,10,12,14), (9,11,13,15).  Returns the
-// sum of Q over all 128 channels (the lane's 16, summed over its 8-lane group).
-__device__ __forceinline__ int split_query4(const int* Qlds, int sl, u32x4& qh, u32x4& ql) {
-    uint32_t h4[4], l4[4];
+// Query words for SketchBatch: word 2m + h of part `part` holds channels
+// 32 part + 8m + 2b + h, b = 0..3 (h = 0: low nibbles, 1: high), split
+// Q = 64 hi + lo as in split_query.  Returns the sum of Q over all 128
+// channels (the part's 32, summed over the 4 lanes of a row).
+__device__ __forceinline__ int split_query4w(const int* Qlds, int part, uint32_t (&qh)[8], uint32_t (&ql)[8]) {
     int sq = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int k = 0; k < 8; ++k) {
         uint32_t hw = 0, lw = 0;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int ch = (w >> 1) * 8 + 2 * u + (w & 1);
-            const int Q = Qlds[sl * 16 + ch];
+        for (int bb = 0; bb < 4; ++bb) {
+            const int Q = Qlds[32 * part + 8 * (k >> 1) + 2 * bb + (k & 1)];
             sq += Q;
             const int lo = ((Q + 32) & 63) - 32;
             const int hi = (Q - lo) >> 6;
-            hw |= (uint32_t(hi) & 0xffu) << (8 * u);
-            lw |= (uint32_t(lo) & 0xffu) << (8 * u);
+            hw |= (uint32_t(hi) & 0xffu) << (8 * bb);
+            lw |= (uint32_t(lo) & 0xffu) << (8 * bb);
         }
-        h4[w] = hw;
-        l4[w] = lw;
+        qh[k] = hw;
+        ql[k] = lw;
     }
-    qh = u32x4{h4[0], h4[1], h4[2], h4[3]};
-    ql = u32x4{l4[0], l4[1], l4[2], l4[3]};
-    return sum8_i(sq);
+    sq += dpp_i<kDppXor1>(sq);
+    sq += dpp_i<kDppXor2>(sq);
+    return sq;
 }
 
 // One instantiation per (rows per candidate / 8, select code of the
@@ -259,26 +279,43 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
     int32_t* scores_bj = p.scores + int64_t(bj) * p.cur.ncand;
     const int wave = threadIdx.x >> 6;
     const int sl = threadIdx.x & 7;
-    if constexpr (SEL == 0 && !FUSE) {
+    if constexpr (Q4) {
+        // First stage from the int4 sketch, one load batch per wave (cpw =
+        // CB): rows loaded first, query codes formed while they are in flight.
+        constexpr int NS16 = NS8 >= 2 ? NS8 / 2 : 1;
+        using SB = SketchBatch<NS16>;
+        const int first = (blockIdx.x * kPruneWaves + wave) * p.cpw;
+        int64_t xs[SB::CB];
+#pragma unroll
+        for (int c = 0; c < SB::CB; ++c) xs[c] = c < p.cpw ? cand_start(p.cur, true, nullptr, first + c, L) : -1;
+        SB sb;
+        sb.load(p, xs, L, k4_bj);
+        if (bad && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(p.flag, 1);
+        group_query_codes(p.q + int64_t(b) * p.Hq * kHeadDim, j, p.G, Qlds, nullptr);
+        if (blockIdx.x == 0 && threadIdx.x < kHeadDim)
+            p.qgroup[int64_t(bj) * kHeadDim + threadIdx.x] = Qlds[threadIdx.x];
+        uint32_t qh4[8], ql4[8];
+        const int corr = 8 * split_query4w(Qlds, threadIdx.x & 3, qh4, ql4);
+        sb.score(p, qh4, ql4, corr, first, p.cpw, scores_bj);
+        return;
+    } else if constexpr (SEL == 0 && !FUSE) {
         // First stage, one load batch per wave (cpw = CB): the candidate
         // starts follow from the indices, so the rows are loaded first and
         // the query codes are formed while the loads are in flight.
-        using RB = RowBatch<NS8, false, Q4>;
+        using RB = RowBatch<NS8, false>;
         const int first = (blockIdx.x * kPruneWaves + wave) * p.cpw;
         int64_t xs[RB::CB];
 #pragma unroll
         for (int c = 0; c < RB::CB; ++c) xs[c] = c < p.cpw ? cand_start(p.cur, true, nullptr, first + c, L) : -1;
         RB rb;
-        rb.load(p, xs, L, k8_bj, k4_bj);
+        rb.load(p, xs, L, k8_bj);
         if (bad && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(p.flag, 1);
         group_query_codes(p.q + int64_t(b) * p.Hq * kHeadDim, j, p.G, Qlds, nullptr);
         if (blockIdx.x == 0 && threadIdx.x < kHeadDim)
             p.qgroup[int64_t(bj) * kHeadDim + threadIdx.x] = Qlds[threadIdx.x];
         u32x4 qh, ql;
-        int corr = 0;
-        if constexpr (Q4) corr = 8 * split_query4(Qlds, sl, qh, ql);
-        else split_query(Qlds, sl, qh, ql);
-        rb.score(p, qh, ql, corr, first, p.cpw, scores_bj, nullptr);
+        split_query(Qlds, sl, qh, ql);
+        rb.score(p, qh, ql, first, p.cpw, scores_bj, nullptr);
         return;
     }
 
@@ -318,8 +355,7 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
     __syncthreads();
 
     const int first = wg_first + wave * p.cpw;
-    // (the int4 sketch serves only the first stage, which returned above)
-    score_slice<NS8, FUSE, false>(p, cstart + wave * p.cpw, L, k8_bj, nullptr, qh, ql, 0, first, scores_bj,
+    score_slice<NS8, FUSE>(p, cstart + wave * p.cpw, L, k8_bj, qh, ql, first, scores_bj,
                                FUSE ? p.pre + int64_t(bj) * p.cur.ncand * p.fuse_rq : nullptr);
     if constexpr (SEL != 0 && SEL != kGiven) {
         // workgroup 0 publishes the previous stage's kept set (ascending,
@@ -394,8 +430,9 @@ hipError_t launch_prune_stage(sd_ctx* c, int st, bool given, bool fused, const u
     }
     const bool q4 = k4 != nullptr && st == 0 && !fuse;
     if (q4) {
-        // one batch of int4 candidates per wave (batch_candidates(ns8, true))
-        p.cpw = batch_candidates(ns8 == 1 ? 1 : ns8 == 2 ? 2 : ns8 <= 4 ? 4 : 8, true);
+        // one batch of int4 candidates per wave (SketchBatch: 8 / NS16)
+        const int ns8p = ns8 == 1 ? 1 : ns8 == 2 ? 2 : ns8 <= 4 ? 4 : 8;
+        p.cpw = 8 / (ns8p >= 2 ? ns8p / 2 : 1);
         grid.x = (p.cur.ncand + kPruneWaves * p.cpw - 1) / (kPruneWaves * p.cpw);
         if (ns8 == 1) launch(sd_prune_stage_kernel<1, 0, false, true>, grid, dim3(kPruneThreads), lds, s, t, p);
         else if (ns8 == 2) launch(sd_prune_stage_kernel<2, 0, false, true>, grid, dim3(kPruneThreads), lds, s, t, p);
