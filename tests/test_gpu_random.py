@@ -1,0 +1,70 @@
+"""Randomised GPU parity: seeded random configurations (stage count, chunk /
+stride / keep per stage, group size, KV heads, batch, ragged lengths
+including 1 and Lmax, sink and window, budgets above the candidate count)
+through the C ABI against the oracle, under both the fused and the unfused
+last stage.  Bar as everywhere: int8 codes, every stage's scores and kept
+sets bit-exact; outputs within 8e-3.  Each configuration prints its seed
+and shape before it runs.
+"""
+import numpy as np
+import pytest
+
+from sparse_attention_kv_int8_amd.inputs import Stage, tiny_workload
+from tests.test_gpu_parity import fusion, run_case  # noqa: F401  (fixture)
+
+pytestmark = pytest.mark.gpu
+
+SEEDS = list(range(24))
+
+
+def random_case(seed: int):
+    """A valid configuration (the library's limits: stride divides chunk,
+    chunks nest, the last chunk is a multiple of 8, at most 64 samples per
+    chunk) and request lengths, drawn from `seed`."""
+    rng = np.random.default_rng(10_000 + seed)
+    S = int(rng.integers(1, 5))
+    chunks = [int(rng.choice([8, 16, 32]))]
+    for _ in range(S - 1):
+        chunks.insert(0, chunks[0] * int(rng.choice([2, 4, 8])))
+    Lmax = int(rng.integers(1000, 20001))
+    n = -(-Lmax // chunks[0])
+    stages = []
+    for s, c in enumerate(chunks):
+        strides = [1 << e for e in range(15) if (1 << e) <= c and c % (1 << e) == 0 and c // (1 << e) <= 64]
+        r = int(rng.choice(strides))
+        keep = int(rng.integers(1, min(n, 300) + 3))            # sometimes more than the candidates
+        stages.append(Stage(c, r, keep))
+        if s + 1 < S:
+            n = keep * (c // chunks[s + 1])
+    G = int(rng.choice([1, 2, 4]))
+    Hkv = int(rng.integers(1, 4))
+    B = int(rng.integers(1, 4))
+    sink = int(rng.choice([0, 1, 7, 64]))
+    window = int(rng.choice([0, 5, 100, 512]))
+    lengths = rng.integers(1, Lmax + 1, size=B)
+    if B >= 2 and rng.random() < 0.5:
+        lengths[0] = Lmax
+    if B >= 3 and rng.random() < 0.5:
+        lengths[2] = 1
+    w = tiny_workload(name=f"random{seed}", batch=B, num_q_heads=G * Hkv, num_kv_heads=Hkv, max_context=Lmax,
+                      stages=tuple(stages), sink=sink, window=window, planted=4, seed=20_000 + seed)
+    return w, [int(x) for x in lengths]
+
+
+def test_random_cases_are_valid_configurations():
+    """The generator stays inside the documented limits (checked without a
+    context, so a generator mistake shows here and not as a create error)."""
+    for seed in SEEDS:
+        w, lengths = random_case(seed)
+        st = w.stages
+        assert all(s.chunk % s.stride == 0 and s.chunk // s.stride <= 64 for s in st)
+        assert all(st[i].chunk % st[i + 1].chunk == 0 for i in range(len(st) - 1))
+        assert st[-1].chunk % 8 == 0
+        assert len(lengths) == w.batch and min(lengths) >= 1 and max(lengths) <= w.max_context
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_configuration(seed, fusion):
+    w, lengths = random_case(seed)
+    print(f"seed {seed} lengths {lengths}", flush=True)
+    run_case(w, lengths=lengths, check_scores=True)
