@@ -39,6 +39,9 @@ append = KV append (sd_append_kv) of one token per call on the same
          workload grown to hold more tokens: us per append, us for one
          append that raises a scale (its rows recoded), and us per token of
          a decode loop (step + append).
+batched = the 16-request ragged workload (up to 128K tokens each), timed
+         like the main figure: what the same kernels reach with many
+         requests in flight (context; `value` stays the B = 1 figure).
 reuse  = steps that reuse the first r pruning stages' kept sets from an
          earlier step (sd_decode_step_reuse): us per step for each r, and,
          over a drifting query sequence, how much of the fully recomputed
@@ -668,6 +671,8 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-decode comparison (sd_dense_decode)")
     ap.add_argument("--no-append", action="store_true", help="skip the KV-append study (sd_append_kv)")
     ap.add_argument("--no-sketch", action="store_true", help="skip the int4 first-stage sketch study")
+    ap.add_argument("--batched", default="ragged_b16", help="batched workload reported inside the line for "
+                    "context ('' = none): the same kernels with many requests in flight")
     ap.add_argument("--secondary", default="ctx_1m", help="second workload reported inside the line ('' = none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain elementwise copy (torch.neg) of MIB MiB three times: the "
@@ -787,6 +792,21 @@ def main() -> int:
                              "quantize_keys_us": round(b2.quantize_us, 2), "reuse": r2["reuse"],
                              "dense": r2["dense"], "sketch4": r2["sketch"]}
         del b2
+        b_torch.cuda.empty_cache()
+    if args.batched and args.batched != w.name:
+        w3 = WORKLOADS[args.batched]
+        b3, r3 = measure(w3, max(20, args.steps // 4), args.warmup, auto_copies(w3), False, False, False)
+        t3 = r3["bytes"]["total"]
+        line["batched"] = {"workload": w3.name, "batch": w3.batch, "us_per_step": round(r3["us_per_step"], 3),
+                           "value_GBs": round(t3 / (r3["us_per_step"] * 1e-6) / 1e9, 2),
+                           "frac": round(t3 / (r3["us_per_step"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                           "algorithmic_bytes": t3, "tokens_per_s": round(w3.batch / (r3["us_per_step"] * 1e-6), 1),
+                           "step_kernels_us": {k: round(v, 3) for k, v in r3["avg_us"].items()},
+                           "dominant": r3["dominant"],
+                           "dominant_frac": round(r3["bytes"]["per_kernel"][r3["dominant"]] /
+                                                  (r3["dominant_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                           "note": "context: the same kernels with 16 requests of ragged lengths in flight"}
+        del b3
         b_torch.cuda.empty_cache()
     if not args.copy_calibration:            # its copies would mix with the calibration copies
         line["stream_ceiling"] = stream_ceiling()

@@ -68,3 +68,22 @@ def test_random_configuration(seed, fusion):
     w, lengths = random_case(seed)
     print(f"seed {seed} lengths {lengths}", flush=True)
     run_case(w, lengths=lengths, check_scores=True)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_configuration_sketch_and_dense(seed, monkeypatch):
+    """The same configurations through the int4 first-stage sketch step
+    (sketch codes, first-stage scores, kept sets, outputs) and the dense
+    decode (every head against the oracle's dense attention).  Two-stage
+    configurations run unfused there (a fused first stage reads rows the
+    sketch does not hold)."""
+    from tests.test_gpu_dense import DenseRun, all_pairs, check
+    from tests.test_gpu_sketch4 import run_sketch_case
+    w, lengths = random_case(seed)
+    print(f"seed {seed} lengths {lengths} (sketch, dense)", flush=True)
+    if len(w.stages) == 2:
+        monkeypatch.setenv("SD_FUSE_LAST_STAGE", "0")
+    g, _ = run_sketch_case(w, lengths=lengths, check_scores=True)
+    d = DenseRun(g.inp)
+    check(g.inp, d.run(), all_pairs(w))
+    assert d.dec.sd_check() == 0
