@@ -129,3 +129,42 @@ def test_sketch_fused_two_stages_unsupported():
 @pytest.mark.parametrize("name", ["llama8b_128k", "ragged_b16", "ctx_1m"])
 def test_sketch_full_workload(name):
     run_sketch_case(WORKLOADS[name], check_scores=name == "llama8b_128k")
+
+
+def test_sketch_graph_replays_match_eager():
+    """A sketch step captured into a HIP graph replays to the eager result,
+    with eager steps and synchronisations between the replays; repeated
+    eager steps are bit-identical."""
+    import torch
+    w = WORKLOADS["llama8b_128k"].replace(max_context=32768, planted=16)
+    print("case sketch4 graph capture", flush=True)
+    inp = make_inputs(w)
+    g = GpuRun(inp)
+    g.quantize()
+    sk = torch.zeros((w.batch, w.num_kv_heads, g.dec.sd_sketch4_rows(), 64), dtype=torch.uint8, device="cuda")
+    g.dec.sd_quantize_sketch4(g.k, g.lengths, sk)
+    q = to_dev_bf16(inp.q_step0)
+
+    def eager():
+        g.dec.sd_decode_step_sketch4(q, g.k, g.k8, sk, g.v, g.lengths, g.out, g.kept)
+        torch.cuda.synchronize()
+        return bf16_dev_to_bits(g.out).copy(), g.kept.cpu().numpy().copy()
+
+    out_e, kept_e = eager()
+    out2, kept2 = eager()
+    assert np.array_equal(out_e, out2) and np.array_equal(kept_e, kept2)
+    out_g = torch.empty_like(g.out)
+    kept_g = torch.empty_like(g.kept)
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        g.dec.sd_decode_step_sketch4(q, g.k, g.k8, sk, g.v, g.lengths, out_g, kept_g)
+    for rep in range(3):
+        out_g.zero_()
+        kept_g.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_dev_to_bits(out_g), out_e), rep
+        assert np.array_equal(kept_g.cpu().numpy(), kept_e), rep
+        eager()
