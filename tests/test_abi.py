@@ -89,3 +89,29 @@ def test_single_hip_runtime_in_process():
     maps = open("/proc/self/maps").read()
     hip = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
     assert len(hip) == 1, hip
+
+
+def test_candidate_limit_is_exact():
+    """n_1 + keep_1 = 15872 passes validation (on a machine without a GPU the
+    create then fails in the HIP runtime, not in validation); 15873 is
+    rejected as unsupported."""
+    ok = _cfg(max_context=8 * 15808, stages=[(8, 8, 64)])
+    over = _cfg(max_context=8 * 15809, stages=[(8, 8, 64)])
+    h = C.c_void_p()
+    st = B.lib.sd_create(C.byref(ok), C.byref(h))
+    assert st not in (B.SD_ERR_INVALID_ARG, B.SD_ERR_UNSUPPORTED)
+    if st == B.SD_OK:
+        B.lib.sd_destroy(h)
+    h = C.c_void_p(123)
+    assert B.lib.sd_create(C.byref(over), C.byref(h)) == B.SD_ERR_UNSUPPORTED
+    assert h.value is None
+
+
+def test_null_arguments_of_the_other_entry_points():
+    assert B.lib.sd_dense_decode(None, None, None, None, None, None, None) == B.SD_ERR_INVALID_ARG
+    assert B.lib.sd_append_kv(None, None, None, 1, None, None, None, None, None, None, None) == B.SD_ERR_INVALID_ARG
+    assert B.lib.sd_quantize_sketch4(None, None, None, None, None) == B.SD_ERR_INVALID_ARG
+    assert B.lib.sd_decode_step_sketch4(None, None, None, None, None, None, None, None, None, None) == \
+        B.SD_ERR_INVALID_ARG
+    assert B.lib.sd_decode_step_reuse(None, None, None, None, None, None, None, None, 0, None) == B.SD_ERR_INVALID_ARG
+    assert B.lib.sd_sketch4_rows(None) == -1

@@ -112,6 +112,11 @@ SMALL = {
 }
 
 
+SMALL["candidate_limit"] = tiny_workload(name="limit", batch=1, num_q_heads=4, num_kv_heads=1,
+                                         max_context=8 * 15808, stages=(Stage(8, 8, 64),), sink=16, window=64,
+                                         planted=8)   # n_1 + keep_1 = 15872, the documented maximum
+
+
 @pytest.fixture(params=["unfused", "fused"])
 def fusion(request, monkeypatch):
     """Runs a case with the last stage in its own kernel and, where the
