@@ -168,3 +168,37 @@ def test_sketch_graph_replays_match_eager():
         assert np.array_equal(bf16_dev_to_bits(out_g), out_e), rep
         assert np.array_equal(kept_g.cpu().numpy(), kept_e), rep
         eager()
+
+
+def test_side_stream_matches_default_stream():
+    """The sketch, the sketch step, the dense decode and the KV append
+    enqueued on a non-default stream give the same bits as on the default
+    stream (two contexts, one per stream, on copies of the same cache)."""
+    import torch
+    from sparse_attention_kv_int8_amd.inputs import make_append_tokens
+    w = tiny_workload(name="streams", batch=2, num_q_heads=8, num_kv_heads=2, max_context=8192)
+    print("case side stream (sketch, dense, append)", flush=True)
+    inp = make_inputs(w, lengths=[8000, 3001])
+    k_new, v_new = make_append_tokens(w, 5, seed=9)
+    results = []
+    for side in (False, True):
+        s = torch.cuda.Stream() if side else None
+        g = GpuRun(inp, stream=s)
+        ctx = torch.cuda.stream(s) if side else torch.cuda.stream(torch.cuda.current_stream())
+        with ctx:
+            g.quantize()
+            sk = torch.zeros((w.batch, w.num_kv_heads, g.dec.sd_sketch4_rows(), 64), dtype=torch.uint8,
+                             device="cuda")
+            g.dec.sd_quantize_sketch4(g.k, g.lengths, sk, stream=s)
+            q = to_dev_bf16(inp.q_step0)
+            g.dec.sd_decode_step_sketch4(q, g.k, g.k8, sk, g.v, g.lengths, g.out, g.kept, stream=s)
+            out_dense = torch.empty_like(g.out)
+            g.dec.sd_dense_decode(q, g.k, g.v, g.lengths, out_dense, stream=s)
+            g.dec.sd_append_kv(to_dev_bf16(k_new), to_dev_bf16(v_new), 5, g.lengths, g.k, g.k8, g.v, g.absmax,
+                               stream=s, k_sketch4=sk)
+            (s or torch.cuda.current_stream()).synchronize()
+        results.append([bf16_dev_to_bits(g.out), g.kept.cpu().numpy(), bf16_dev_to_bits(out_dense),
+                        g.k8.cpu().numpy(), sk.cpu().numpy(), g.absmax.cpu().numpy()])
+        assert g.dec.sd_check(stream=s) == 0
+    for a, b in zip(*results):
+        assert np.array_equal(a, b)
