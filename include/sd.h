@@ -237,8 +237,9 @@ sd_status sd_dense_decode(sd_ctx* ctx, const uint16_t* q, const uint16_t* k_bf16
  * the first stage samples, t = i * r_1 (r_1 = stage[0].stride), i <
  * ceil(L_b / r_1): codes c = rint(7 * k / a_bj) in [-7, 7] (round half to
  * even, correctly rounded fp32 division) with the key scale a_bj of
- * sd_quantize_keys, stored as nibbles c + 8; byte m of a row holds channel
- * 2m in its low and channel 2m + 1 in its high nibble (64 bytes per row).
+ * sd_quantize_keys, stored as two's-complement nibbles; byte m of a row
+ * holds channel 2m in its low and channel 2m + 1 in its high nibble (64
+ * bytes per row).
  *
  * Rows per (request, KV head) of the sketch: ceil(Lmax / r_1). */
 int64_t sd_sketch4_rows(const sd_ctx* ctx);

@@ -120,12 +120,12 @@ struct RowBatch {
 // One load batch of the first stage from the int4 sketch: 4 lanes x 16
 // bytes per 64-byte sketch row (lane = 4 * row + part; part p holds
 // channels [32 p, 32 p + 32)), 16 rows per load slot, NS16 slots per
-// candidate, 8 loads per batch (CB = 8 / NS16 candidates).  Each 4-byte
-// word m of a part holds channels 8m .. 8m + 7 of it as nibbles (even
-// channels low); the low and high nibbles are unpacked into two words of
-// bytes, whose channel order split_query4w gives qh and ql.  The nibbles
-// are u = code + 8, so S = Q . u - 8 sum(Q) (`corr` = 8 sum(Q)); every
-// first-stage sample t is a multiple of the stride, at sketch row t / stride.
+// candidate, 8 loads per batch (CB = 8 / NS16 candidates).  Word m of a
+// part holds channels 32 p + 8 m + k as two's-complement nibbles k = 0..7,
+// which v_dot8_i32_i4 multiplies pairwise with the same nibbles of a query
+// digit word (split_query4d); S = d0 . K4 + 16 (d1 . K4) + 256 (d2 . K4),
+// exact in int32.  Every first-stage sample t is a multiple of the stride,
+// at sketch row t / stride.
 template <int NS16>
 struct SketchBatch {
     static constexpr int CB = 8 / NS16;
@@ -148,28 +148,27 @@ struct SketchBatch {
         }
     }
 
-    __device__ __forceinline__ void score(const PruneParams& p, const uint32_t (&qh)[8], const uint32_t (&ql)[8],
-                                          int corr, int first, int nvalid, int32_t* __restrict__ out) const {
+    __device__ __forceinline__ void score(const PruneParams& p, const uint32_t (&d0)[4], const uint32_t (&d1)[4],
+                                          const uint32_t (&d2)[4], int first, int nvalid,
+                                          int32_t* __restrict__ out) const {
         const int lane = threadIdx.x & 63;
         int best[CB];
 #pragma unroll
         for (int c = 0; c < CB; ++c) best[c] = INT32_MIN;
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
-            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-            int ah = 0, al = 0;
+            const int w[4] = {int(v[u].x), int(v[u].y), int(v[u].z), int(v[u].w)};
+            int a0 = 0, a1 = 0, a2 = 0;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const int lo = int(w[m] & 0x0f0f0f0fu), hi = int((w[m] >> 4) & 0x0f0f0f0fu);
-                ah = __builtin_amdgcn_sdot4(int(qh[2 * m]), lo, ah, false);
-                ah = __builtin_amdgcn_sdot4(int(qh[2 * m + 1]), hi, ah, false);
-                al = __builtin_amdgcn_sdot4(int(ql[2 * m]), lo, al, false);
-                al = __builtin_amdgcn_sdot4(int(ql[2 * m + 1]), hi, al, false);
+                a0 = __builtin_amdgcn_sdot8(int(d0[m]), w[m], a0, false);
+                a1 = __builtin_amdgcn_sdot8(int(d1[m]), w[m], a1, false);
+                a2 = __builtin_amdgcn_sdot8(int(d2[m]), w[m], a2, false);
             }
-            int sv = ah * 64 + al;
+            int sv = a0 + 16 * a1 + 256 * a2;
             sv += dpp_i<kDppXor1>(sv);
             sv += dpp_i<kDppXor2>(sv);                 // the row's score in its 4 lanes
-            if (ok[u]) best[u / NS16] = max(best[u / NS16], sv - corr);
+            if (ok[u]) best[u / NS16] = max(best[u / NS16], sv);
         }
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
@@ -229,30 +228,30 @@ __device__ __forceinline__ void split_query(const int* Qlds, int sl, u32x4& qh, 
     ql = u32x4{l4[0], l4[1], l4[2], l4[3]};
 }
 
-// Query words for SketchBatch: word 2m + h of part `part` holds channels
-// 32 part + 8m + 2b + h, b = 0..3 (h = 0: low nibbles, 1: high), split
-// Q = 64 hi + lo as in split_query.  Returns the sum of Q over all 128
-// channels (the part's 32, summed over the 4 lanes of a row).
-__device__ __forceinline__ int split_query4w(const int* Qlds, int part, uint32_t (&qh)[8], uint32_t (&ql)[8]) {
-    int sq = 0;
+// Query digit words for SketchBatch: Q = d0 + 16 d1 + 256 d2 with every
+// digit in [-8, 7] (balanced base 16; |Q| <= 508 < 7 (1 + 16 + 256)), and
+// word m of digit i holds d_i of channels 32 part + 8 m + k as
+// two's-complement nibbles k = 0..7.
+__device__ __forceinline__ void split_query4d(const int* Qlds, int part, uint32_t (&d0)[4], uint32_t (&d1)[4],
+                                              uint32_t (&d2)[4]) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        uint32_t hw = 0, lw = 0;
+    for (int m = 0; m < 4; ++m) {
+        uint32_t w0 = 0, w1 = 0, w2 = 0;
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            const int Q = Qlds[32 * part + 8 * (k >> 1) + 2 * bb + (k & 1)];
-            sq += Q;
-            const int lo = ((Q + 32) & 63) - 32;
-            const int hi = (Q - lo) >> 6;
-            hw |= (uint32_t(hi) & 0xffu) << (8 * bb);
-            lw |= (uint32_t(lo) & 0xffu) << (8 * bb);
+        for (int k = 0; k < 8; ++k) {
+            int Q = Qlds[32 * part + 8 * m + k];
+            const int e0 = ((Q + 8) & 15) - 8;
+            Q = (Q - e0) >> 4;
+            const int e1 = ((Q + 8) & 15) - 8;
+            const int e2 = (Q - e1) >> 4;
+            w0 |= (uint32_t(e0) & 0xfu) << (4 * k);
+            w1 |= (uint32_t(e1) & 0xfu) << (4 * k);
+            w2 |= (uint32_t(e2) & 0xfu) << (4 * k);
         }
-        qh[k] = hw;
-        ql[k] = lw;
+        d0[m] = w0;
+        d1[m] = w1;
+        d2[m] = w2;
     }
-    sq += dpp_i<kDppXor1>(sq);
-    sq += dpp_i<kDppXor2>(sq);
-    return sq;
 }
 
 // One instantiation per (rows per candidate / 8, select code of the
@@ -294,9 +293,9 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
         group_query_codes(p.q + int64_t(b) * p.Hq * kHeadDim, j, p.G, Qlds, nullptr);
         if (blockIdx.x == 0 && threadIdx.x < kHeadDim)
             p.qgroup[int64_t(bj) * kHeadDim + threadIdx.x] = Qlds[threadIdx.x];
-        uint32_t qh4[8], ql4[8];
-        const int corr = 8 * split_query4w(Qlds, threadIdx.x & 3, qh4, ql4);
-        sb.score(p, qh4, ql4, corr, first, p.cpw, scores_bj);
+        uint32_t d0[4], d1[4], d2[4];
+        split_query4d(Qlds, threadIdx.x & 3, d0, d1, d2);
+        sb.score(p, d0, d1, d2, first, p.cpw, scores_bj);
         return;
     } else if constexpr (SEL == 0 && !FUSE) {
         // First stage, one load batch per wave (cpw = CB): the candidate

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kQuantThreads) void sd_quantize_kernel(
 
 // int4 sketch of the first pruning stage's rows: for t = i * stride < L,
 // row i of the sketch holds the 4-bit codes of key row t with the stored
-// scale, as nibbles code + 8 (1..15), channel 2m in the low and channel
+// scale, as two's-complement nibbles, channel 2m in the low and channel
 // 2m + 1 in the high nibble of byte m (64 bytes per row).  16 threads per
 // row, each codes 8 channels (one 16-byte load) into one 4-byte word.
 __device__ __forceinline__ uint32_t sketch_word(u32x4 w, float a) {
@@ -120,8 +120,8 @@ __device__ __forceinline__ uint32_t sketch_word(u32x4 w, float a) {
     uint32_t word = 0;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const uint32_t lo = uint32_t(code4_of(bf16_lo(x[m]), a) + 8);
-        const uint32_t hi = uint32_t(code4_of(bf16_hi(x[m]), a) + 8);
+        const uint32_t lo = uint32_t(code4_of(bf16_lo(x[m]), a)) & 0xfu;
+        const uint32_t hi = uint32_t(code4_of(bf16_hi(x[m]), a)) & 0xfu;
         word |= (lo | (hi << 4)) << (8 * m);
     }
     return word;

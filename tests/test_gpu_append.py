@@ -199,8 +199,8 @@ def test_append_keeps_the_int4_sketch_current():
     def check_sketch():
         got = sk.cpu().numpy()
         dec = np.empty(got.shape[:-1] + (128,), np.int8)
-        dec[..., 0::2] = (got & 15).astype(np.int8) - 8
-        dec[..., 1::2] = (got >> 4).astype(np.int8) - 8
+        dec[..., 0::2] = ((got & 15).astype(np.int8) ^ 8) - 8
+        dec[..., 1::2] = ((got >> 4).astype(np.int8) ^ 8) - 8
         ref = [[O.key_sketch4(inp.k[b, j], int(inp.lengths[b]), r1) for j in range(w.num_kv_heads)]
                for b in range(w.batch)]
         for b in range(w.batch):

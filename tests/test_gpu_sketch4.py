@@ -32,10 +32,10 @@ def sketch_ref(inp):
 
 
 def unpack(sk: np.ndarray) -> np.ndarray:
-    """uint8 [..][64] nibbles (code + 8; channel 2m low, 2m + 1 high) -> int8 codes [..][128]."""
+    """uint8 [..][64] two's-complement nibbles (channel 2m low, 2m + 1 high) -> int8 codes [..][128]."""
     out = np.empty(sk.shape[:-1] + (128,), np.int8)
-    out[..., 0::2] = (sk & 15).astype(np.int8) - 8
-    out[..., 1::2] = (sk >> 4).astype(np.int8) - 8
+    out[..., 0::2] = ((sk & 15).astype(np.int8) ^ 8) - 8
+    out[..., 1::2] = ((sk >> 4).astype(np.int8) ^ 8) - 8
     return out
 
 
