@@ -37,6 +37,12 @@ MUTATIONS = {
     "sketch_row_index": ("token_scores(Qj, k4_bj[t.reshape(-1) // r1])",
                          "token_scores(Qj, k4_bj[np.minimum(t.reshape(-1) // r1 + 1, len(k4_bj) - 1)])"),
     "sketch_every_row": ("return quantize_int4(k_bits[:length:stride], a)", "return quantize_int4(k_bits[:length], a)"),
+    "needed_blocks_shifted": ("return np.unique(np.asarray(tokens, dtype=np.int64) // block)",
+                              "return np.unique((np.asarray(tokens, dtype=np.int64) + 1) // block)"),
+    "needed_blocks_wrong_size": ("def needed_blocks(tokens: np.ndarray, block: int = 8)",
+                                 "def needed_blocks(tokens: np.ndarray, block: int = 16)"),
+    "needed_blocks_one_extra": ("return np.unique(np.asarray(tokens, dtype=np.int64) // block)",
+                                "return np.unique(np.asarray(tokens, dtype=np.int64) // block + 1)"),
     "sketch_unused": ("score_fn = S0_of_rows if (s == 0 and S0_of_rows is not None) else S_of_rows",
                       "score_fn = S_of_rows"),
 }

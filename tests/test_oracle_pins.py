@@ -555,3 +555,32 @@ def test_lru_matches_brute_force_definition():
                 last[x] = t
         assert lru.step(need, t) == (h, len(need) - h)
         assert lru.last == last
+
+
+def test_needed_blocks_hand_worked():
+    """needed_blocks on hand-worked token sets and on hand-worked attended
+    sets (sink and window overlapping kept chunks, L not a multiple of 8,
+    sink and window covering everything) -- tests/golden/needed_blocks_hand.json."""
+    g = json.load(open(os.path.join(GOLDEN, "needed_blocks_hand.json")))
+    for case in g["token_cases"]:
+        got = O.needed_blocks(np.asarray(case["tokens"], dtype=np.int64)).tolist()
+        assert got == case["expected"], case["work"]
+    for case in g["attended_cases"]:
+        T = O.attended_tokens(np.asarray(case["kept"], dtype=np.int64), case["chunk"], case["length"],
+                              case["sink"], case["window"])
+        assert O.needed_blocks(T).tolist() == case["expected"], case["work"]
+
+
+def test_needed_blocks_brute_force_intersection():
+    """needed_blocks(T) equals the blocks b whose token range [8b, 8b + 8)
+    meets T, found by scanning every block of [0, L) (a different
+    formulation: block-major instead of token-major)."""
+    rng = np.random.default_rng(11)
+    for trial in range(200):
+        L = int(rng.integers(1, 400))
+        n = int(rng.integers(0, L + 1))
+        T = rng.choice(L, size=n, replace=bool(rng.integers(0, 2)))
+        inT = np.zeros(L, dtype=bool)
+        inT[T] = True
+        want = [b for b in range((L + 7) // 8) if inT[8 * b:8 * b + 8].any()]
+        assert O.needed_blocks(T).tolist() == want, (L, n)
