@@ -96,16 +96,21 @@ typedef struct sd_config {
 } sd_config;
 
 /* Counters of the host-value path (values_on_host = 1), over all steps
- * since creation or the last sd_reset_value_cache, and for the last step. */
+ * since creation or the last sd_reset_value_cache, and for the last step.
+ * A refill is a hit whose cached block was written when fewer of its rows
+ * were below the length than now (the length grew since): the block is
+ * read from host memory again.  It counts as a hit of the LRU policy. */
 typedef struct sd_stats {
     int64_t steps;
     int64_t blocks_needed;      /* sum over steps and (request, KV head) of |blocks of T| */
     int64_t hits;
     int64_t misses;
-    int64_t h2d_bytes;          /* misses * 8 tokens * d * 2 bytes */
+    int64_t h2d_bytes;          /* (misses + refills) * 8 tokens * d * 2 bytes read from host memory */
     int64_t last_needed;
     int64_t last_hits;
     int64_t last_misses;
+    int64_t refills;
+    int64_t last_refills;
 } sd_stats;
 
 /* Creates a context on the current HIP device, validating `cfg` and

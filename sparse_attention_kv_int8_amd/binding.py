@@ -53,7 +53,7 @@ class sd_profile(C.Structure):
 
 class sd_stats(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("steps", "blocks_needed", "hits", "misses", "h2d_bytes",
-                                         "last_needed", "last_hits", "last_misses")]
+                                         "last_needed", "last_hits", "last_misses", "refills", "last_refills")]
 
 
 if not os.path.exists(LIB_PATH):

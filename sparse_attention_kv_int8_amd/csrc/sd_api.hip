@@ -262,7 +262,7 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
     const size_t o_req = cv.take<int32_t>(BH);
     const size_t o_flag = cv.take<int32_t>(1);
     const size_t o_pre = c->fuse ? cv.take<int32_t>(BH * size_t(c->st[c->S - 2].ncand) * c->fuse_rq) : 0;
-    size_t o_vc[10] = {0};
+    size_t o_vc[11] = {0};
     if (cfg->values_on_host) {
         c->vc.slots = int32_t(cfg->value_cache_tokens / 8);
         c->vc.nblk_max = int32_t((c->Lmax + 7) / 8);
@@ -275,6 +275,8 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
         o_vc[6] = cv.take<int32_t>(BH * size_t(c->max_blocks));
         o_vc[7] = cv.take<int32_t>(BH * size_t(c->max_blocks));
         o_vc[8] = cv.take<int64_t>(sd::kVcCounters);
+        o_vc[9] = cv.take<int32_t>(BH * size_t(c->vc.slots));
+        o_vc[10] = cv.take<int32_t>(BH);
     }
     c->ws_bytes = cv.off;
     hipError_t e = hipMalloc(&c->ws, c->ws_bytes);
@@ -299,6 +301,8 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
         c->vc.evicted = reinterpret_cast<int32_t*>(base + o_vc[6]);
         c->vc.blk_slot = reinterpret_cast<int32_t*>(base + o_vc[7]);
         c->vc.counters = reinterpret_cast<int64_t*>(base + o_vc[8]);
+        c->vc.slot_fill = reinterpret_cast<int32_t*>(base + o_vc[9]);
+        c->vc.stepc = reinterpret_cast<int32_t*>(base + o_vc[10]);
     }
     // Flag and score buffers start defined; this is setup, outside any step.
     e = hipMemset(c->ws, 0, c->ws_bytes);
@@ -488,12 +492,14 @@ sd_status sd_get_stats(sd_ctx* c, sd_stats* out, void* stream) {
     out->blocks_needed = h[1];
     out->hits = h[2];
     out->misses = h[3];
-    out->h2d_bytes = h[3] * 8 * sd::kHeadDim * 2;
+    out->refills = h[12];
+    out->h2d_bytes = (h[3] + h[12]) * 8 * sd::kHeadDim * 2;
     if (h[0] > 0) {
         const int par = int((h[0] - 1) & 1);
         out->last_needed = h[4 + 4 * par];
         out->last_hits = h[5 + 4 * par];
         out->last_misses = h[6 + 4 * par];
+        out->last_refills = h[7 + 4 * par];
     }
     return SD_OK;
 }

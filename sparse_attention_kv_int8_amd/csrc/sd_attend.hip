@@ -135,7 +135,8 @@ struct BlockData {
 // values: every load is issued unconditionally, from rows clamped below L
 // (always inside the cache), and rows outside the mask are zeroed by a
 // select, so the issue is branch-free.  Host values: hits come from the slot
-// pool, misses from host memory (rows t < L), written into their slot.
+// pool, misses and refills from host memory (rows t < L), written into their
+// slot.
 template <bool HOSTV>
 __device__ __forceinline__ void load_block(const AttendParams& p, int r, int t0, uint32_t mask, int bj, int L,
                                            const uint16_t* kbase, const uint16_t* vbase, BlockData& d) {
@@ -146,8 +147,8 @@ __device__ __forceinline__ void load_block(const AttendParams& p, int r, int t0,
     d.k1 = __builtin_nontemporal_load(kp + 1);
     if (HOSTV) {
         const int32_t se = p.blk_slot[int64_t(bj) * p.max_blocks + r];
-        uint32_t* prow = reinterpret_cast<uint32_t*>(p.vpool + (int64_t(bj) * p.vslots + (se & ~kVcMissBit)) * 8 * kHeadDim);
-        if (se & kVcMissBit) {
+        uint32_t* prow = reinterpret_cast<uint32_t*>(p.vpool + (int64_t(bj) * p.vslots + (se & kVcSlotMask)) * 8 * kHeadDim);
+        if (se & (kVcMissBit | kVcRefillBit)) {
             const uint32_t* hrow = reinterpret_cast<const uint32_t*>(vbase + int64_t(t0) * kHeadDim);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {

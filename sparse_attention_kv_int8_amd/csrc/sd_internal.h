@@ -30,7 +30,13 @@ struct StageDev {
 };
 
 constexpr int kVcCounters = 16;
+// Entry of the per-step block -> slot map: the slot in the low 24 bits, a
+// miss (block not resident: read it from host memory into its slot) or a
+// refill (resident, but written when fewer of its rows were below the
+// length than now: read it again) in the flag bits.
 constexpr int32_t kVcMissBit = int32_t(0x40000000);
+constexpr int32_t kVcRefillBit = int32_t(0x20000000);
+constexpr int32_t kVcSlotMask = int32_t(0x00ffffff);
 
 // Device-side state of the host-value path (values_on_host = 1).
 struct ValueCache {
@@ -43,9 +49,12 @@ struct ValueCache {
     int32_t* used;          // [B][Hkv] slots filled so far
     int32_t* order;         // [2][B][Hkv][slots] recency order (oldest first), double buffered
     int32_t* evicted;       // [B][Hkv][max_blocks] slots evicted this step, oldest first
-    int32_t* blk_slot;      // [B][Hkv][max_blocks] slot of each attended block (| kVcMissBit on a miss)
+    int32_t* blk_slot;      // [B][Hkv][max_blocks] slot of each attended block (| kVcMissBit, | kVcRefillBit)
+    int32_t* slot_fill;     // [B][Hkv][slots] rows of its block a slot holds (those below the length when filled)
+    int32_t* stepc;         // [B][Hkv] steps applied since the reset (the LRU's clock, kept on the device)
     int64_t* counters;      // [16]: steps, needed, hits, misses, then per step parity p:
-                            //       [4+4p] needed, [5+4p] hits, [6+4p] misses
+                            //       [4+4p] needed, [5+4p] hits, [6+4p] misses, [7+4p] refills;
+                            //       [12] refills over all steps
 };
 
 }  // namespace sd
@@ -87,7 +96,6 @@ struct sd_ctx {
     int32_t* requant;                 // [B][Hkv] set by sd_append_kv when the scale grew
     int32_t* flag;                    // device error flag
     sd::ValueCache vc;
-    int64_t vc_step;                  // steps applied to the value cache since its reset
     const void* vhost_key;            // last host value pointer seen, and its device alias
     const uint16_t* vhost_dev;
     // profiling (sd_profile_start / sd_profile_stop)

@@ -19,6 +19,14 @@
 // attended block list, which it publishes for the decode kernel); the decode
 // kernel then reads hits from the slot pool and misses straight from host
 // memory, writing each missed block into its slot.
+//
+// The LRU's clock (the step number) lives on the device, one counter per
+// (request, KV head) that this kernel reads and advances, so a step
+// captured in a graph replays with the right clock.  A slot also records
+// how many rows of its block it holds: the rows below the length when it
+// was filled.  When the length has grown since, a hit on a block that ends
+// at or after the old length is served by reading the block from host
+// memory again (a refill); the LRU treats it as the hit it is.
 #include "sd_device.h"
 #include "sd_internal.h"
 #include "sd_select.h"
@@ -35,8 +43,12 @@ __global__ void sd_vcache_reset_kernel(ValueCache vc, int64_t BH) {
     for (int64_t i = t0; i < n_slot; i += stride) {
         vc.slot_block[i] = -1;
         vc.slot_last[i] = -1;
+        vc.slot_fill[i] = 0;
     }
-    for (int64_t i = t0; i < BH; i += stride) vc.used[i] = 0;
+    for (int64_t i = t0; i < BH; i += stride) {
+        vc.used[i] = 0;
+        vc.stepc[i] = 0;
+    }
     if (t0 < kVcCounters) vc.counters[t0] = 0;
 }
 
@@ -58,7 +70,6 @@ struct VcStepParams {
     int32_t* nblocks;             // [B][Hkv]
     int max_blocks;
     int Hkv;
-    int32_t step;
 };
 
 // SEL: select code of the last stage, or kGiven when it is reused (read
@@ -69,8 +80,8 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
     __shared__ unsigned tmp[32];
     const ValueCache& vc = p.vc;
     const int max_blocks = p.max_blocks;
-    const int32_t step = p.step;
     const int j = blockIdx.x, b = blockIdx.y, bj = b * p.Hkv + j;
+    const int32_t step = p.vc.stepc[bj];
     const int64_t BH = int64_t(gridDim.x) * gridDim.y;
     const int tid = threadIdx.x;
     int64_t L = p.lengths[b];
@@ -109,21 +120,35 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
     // (the loops below take kVcBatch entries at a time: their independent
     // loads, then the loads that depend on them, then the updates, so that
     // a batch costs two memory round trips instead of two per entry)
-    unsigned nm = 0;
+    // (a hit whose slot holds fewer rows than are below the length now is
+    // refilled from host memory: only the block holding the old last token
+    // can be one, after the length grew)
+    int32_t* sfill = vc.slot_fill + int64_t(bj) * vc.slots;
+    unsigned nm = 0, nref = 0;
     for (int b0 = r0; b0 < r1; b0 += kVcBatch) {
         uint32_t e[kVcBatch];
-        int32_t sv[kVcBatch];
+        int32_t sv[kVcBatch], fv[kVcBatch];
 #pragma unroll
         for (int u = 0; u < kVcBatch; ++u) e[u] = bl[min(b0 + u, r1 - 1)];    // clamped: no branch
 #pragma unroll
         for (int u = 0; u < kVcBatch; ++u) sv[u] = page[e[u] >> 8];
 #pragma unroll
+        for (int u = 0; u < kVcBatch; ++u) fv[u] = sfill[max(sv[u], 0)];
+#pragma unroll
         for (int u = 0; u < kVcBatch; ++u) {
             const int r = b0 + u;
             if (r >= r1) break;
             if (sv[u] >= 0) {
+                const int64_t blk = int64_t(e[u] >> 8);
+                const int rows = int(min<int64_t>(8, L - 8 * blk));
                 slast[sv[u]] = step;
-                bslot[r] = sv[u];
+                if (fv[u] < rows) {
+                    sfill[sv[u]] = rows;
+                    bslot[r] = sv[u] | kVcRefillBit;
+                    ++nref;
+                } else {
+                    bslot[r] = sv[u];
+                }
             } else {
                 bslot[r] = -1;
                 ++nm;
@@ -184,11 +209,16 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
         page[blk] = s;
         sblk[s] = blk;
         slast[s] = step;
+        sfill[s] = int(min<int64_t>(8, L - 8 * int64_t(blk)));
         bslot[r] = s | kVcMissBit;
     }
     // 4. this step's blocks become the newest entries, ascending by id
-    for (int r = r0; r < r1; ++r) order_new[nsurv + r] = bslot[r] & ~kVcMissBit;
+    for (int r = r0; r < r1; ++r) order_new[nsurv + r] = bslot[r] & kVcSlotMask;
+    // refills of this (request, KV head), summed over the block
+    if (nref) atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 12), (unsigned long long)nref);
+    if (nref) atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 7 + 4 * (step & 1)), (unsigned long long)nref);
     if (tid == 0) {
+        vc.stepc[bj] = step + 1;
         vc.used[bj] = used + (int(nmiss) < nfree ? int(nmiss) : nfree);
         const int par = step & 1;
         atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 1), (unsigned long long)nb);
@@ -203,6 +233,7 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
             vc.counters[4 + 4 * nxt] = 0;
             vc.counters[5 + 4 * nxt] = 0;
             vc.counters[6 + 4 * nxt] = 0;
+            vc.counters[7 + 4 * nxt] = 0;
         }
     }
 }
@@ -210,7 +241,6 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
 hipError_t launch_value_cache_reset(sd_ctx* c, hipStream_t s) {
     const int64_t BH = int64_t(c->cfg.batch) * c->cfg.num_kv_heads;
     sd_vcache_reset_kernel<<<1024, 256, 0, s>>>(c->vc, BH);
-    c->vc_step = 0;
     return hipGetLastError();
 }
 
@@ -234,7 +264,6 @@ hipError_t launch_value_cache_update(sd_ctx* c, bool given, const int32_t* lengt
     p.nblocks = c->nblocks;
     p.max_blocks = c->max_blocks;
     p.Hkv = c->cfg.num_kv_heads;
-    p.step = int32_t(c->vc_step);
     const size_t lds = size_t(kept_lds_words(p.last, p.first_stage != 0)) * 4;
     dim3 grid(c->cfg.num_kv_heads, c->cfg.batch);
     const int sw = select_width(p.last.ncand);
@@ -242,7 +271,6 @@ hipError_t launch_value_cache_update(sd_ctx* c, bool given, const int32_t* lengt
     else if (sw == 4) launch(sd_vcache_step_kernel<4>, grid, dim3(kLruThreads), lds, s, t, p);
     else if (sw == 16) launch(sd_vcache_step_kernel<16>, grid, dim3(kLruThreads), lds, s, t, p);
     else launch(sd_vcache_step_kernel<kSelLds>, grid, dim3(kLruThreads), lds, s, t, p);
-    ++c->vc_step;
     return hipGetLastError();
 }
 

@@ -98,3 +98,87 @@ def test_hostv_reset_starts_cold():
 @pytest.mark.timeout(900)
 def test_hostv_full_3m_workload():
     run_sequence(WORKLOADS["ctx_3m_hostv"], check_every=4)
+
+
+def test_hostv_graph_replay_follows_the_lru():
+    """One host-value step captured in a HIP graph and replayed over the
+    drifting sequence (the step's query copied into the captured buffer
+    before each replay, eager work and a synchronisation between replays):
+    every replay's hits and misses equal the oracle LRU's, and kept sets and
+    outputs match the oracle.  The LRU's clock lives on the device, so each
+    replay advances it."""
+    import torch
+    from tests.gpu_util import bf16_dev_to_bits, to_dev_bf16
+    w = WORKLOADS["ctx_3m_hostv"].replace(name="hostv_graph", max_context=131072, value_cache_tokens=8192,
+                                          planted=64, steps=16)
+    print(f"host-value graph replay {w.name} L={w.max_context} cache={w.value_cache_tokens}", flush=True)
+    inp = make_inputs(w)
+    g = GpuRun(inp)
+    g.quantize()
+    k8_ref, _ = oracle_keys(inp)
+    cfg = oracle_config(w)
+    qbuf = to_dev_bf16(inp.q[0])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.dec.sd_decode_step(qbuf, g.k, g.k8, g.v, g.lengths, g.out, g.kept)
+    st = g.dec.sd_get_stats()
+    assert st.steps == 0, "capturing must not run the step"
+    cap = w.value_cache_tokens // 8
+    lrus = [O.LRU(cap) for _ in range(w.num_kv_heads)]
+    evicting = False
+    for t in range(w.steps):
+        qbuf.copy_(to_dev_bf16(inp.q[t]))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = O.decode_step(inp.q[t], inp.k, k8_ref, inp.v, inp.lengths, cfg)
+        hits = misses = 0
+        for j in range(w.num_kv_heads):
+            evicting |= len(lrus[j].last) + len(O.needed_blocks(ref.attended[0][j])) > cap
+            h, m = lrus[j].step(O.needed_blocks(ref.attended[0][j]), t)
+            hits, misses = hits + h, misses + m
+        st = g.dec.sd_get_stats()
+        assert st.steps == t + 1
+        assert (st.last_hits, st.last_misses) == (hits, misses), f"replay {t}: gpu {(st.last_hits, st.last_misses)} oracle {(hits, misses)}"
+        compare_step(inp, inp.q[t], k8_ref, bf16_dev_to_bits(g.out), g.kept.cpu().numpy(), ref=ref)
+        print(f"  replay {t}: hits {hits} misses {misses}", flush=True)
+    assert evicting, "the sequence should outgrow the cache"
+
+
+def test_hostv_growing_lengths_refill_partial_blocks():
+    """Lengths grow by 1 to 3 tokens between steps, as in a decode loop, so
+    the block holding the old last token is needed again with more valid
+    rows: the cache must serve those rows (refilled from host memory), not
+    the rows the slot held when it was filled.  Outputs, kept sets and the
+    LRU's hits and misses match the oracle at every step, and refills
+    happen."""
+    w = WORKLOADS["ctx_3m_hostv"].replace(name="hostv_grow", max_context=65536, value_cache_tokens=16384,
+                                          planted=32, steps=14)
+    rng = np.random.default_rng(5)
+    L_last = 65531
+    lengths = [L_last]
+    for _ in range(w.steps - 1):
+        lengths.append(lengths[-1] - int(rng.integers(1, 4)))
+    lengths = lengths[::-1]
+    print(f"host-value growing lengths {lengths}", flush=True)
+    inp = make_inputs(w, lengths=[L_last])       # every row below the last length holds data
+    g = GpuRun(inp)
+    g.quantize()
+    k8_ref, _ = oracle_keys(inp)
+    cfg = oracle_config(w)
+    lru = [O.LRU(w.value_cache_tokens // 8) for _ in range(w.num_kv_heads)]
+    for t, L in enumerate(lengths):
+        g.set_lengths([L])
+        out, kept = g.step(inp.q[t])
+        ref = O.decode_step(inp.q[t], inp.k, k8_ref, inp.v, [L], cfg)
+        hits = misses = 0
+        for j in range(w.num_kv_heads):
+            h, m = lru[j].step(O.needed_blocks(ref.attended[0][j]), t)
+            hits, misses = hits + h, misses + m
+        st = g.dec.sd_get_stats()
+        assert (st.last_hits, st.last_misses) == (hits, misses), f"step {t}"
+        _, err, _ = compare_step(inp, inp.q[t], k8_ref, out, kept, ref=ref)
+        print(f"  step {t} L={L}: hits {hits} misses {misses} refills {st.last_refills} err {err:.2e}", flush=True)
+    st = g.dec.sd_get_stats()
+    assert st.refills > 0
+    assert st.h2d_bytes == (st.misses + st.refills) * 8 * 128 * 2
