@@ -189,6 +189,31 @@ sd_status sd_decode_step(sd_ctx* ctx, const uint16_t* q, const uint16_t* k_bf16,
                          const int8_t* k_int8, const uint16_t* v, const int32_t* lengths,
                          uint16_t* out, int32_t* kept_idx, void* stream);
 
+/* sd_decode_step for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes the configuration instead of a context and allocates
+ * nothing (no hipMalloc, hipFree or allocating library call): the step's
+ * workspace (chunk scores, group query sums, split partials and the error
+ * flag) lives in a fixed 16 MiB array of device memory that the library
+ * holds on every GPU it runs on until the process ends; its address on each
+ * GPU is looked up on the first call there.  Arguments and results are
+ * those of sd_decode_step on a context created from *cfg (same kernels,
+ * bit-identical outputs and kept_idx).
+ *  cfg      host pointer, read during the call only; values_on_host must be
+ *           0 (SD_ERR_UNSUPPORTED otherwise: the value cache needs a
+ *           context).  A configuration whose workspace exceeds the 16 MiB
+ *           (many requests at long contexts) gets SD_ERR_UNSUPPORTED with
+ *           the sizes in sd_last_error(); about 1.3 MiB serve one request at
+ *           1M tokens (GQA 32/8), about 3 MiB sixteen requests of 128K.
+ * Every call on a GPU uses that GPU's one array: calls that overlap on one
+ * GPU (other streams, other threads) race and give wrong results; calls in
+ * one stream order are safe.  The error flag is cleared by the call itself;
+ * a length outside [1, Lmax] gives zero output and -1 indices, as in
+ * sd_decode_step, but no sd_check can report it (there is no context). */
+sd_status sd_decode_step_noalloc(const sd_config* cfg, const uint16_t* q, const uint16_t* k_bf16,
+                                 const int8_t* k_int8, const uint16_t* v, const int32_t* lengths,
+                                 uint16_t* out, int32_t* kept_idx, void* stream);
+
 /* sd_decode_step with the first `reuse_stages` pruning stages reused from an
  * earlier step: news article on InfiniteHiP ("韩国通过卸载键值缓存节约英伟达GPU
  * 内存，实现18.95倍解码加速"), section "实现 7.24 倍的端到端解码加速": the modular

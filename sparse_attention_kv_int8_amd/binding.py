@@ -74,6 +74,7 @@ _SIGS = {
     "sd_quantize_keys": (C.c_int, [_p, _p, _p, _p, _p, _p]),
     "sd_decode_step": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "sd_decode_step_reuse": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, C.c_int32, _p]),
+    "sd_decode_step_noalloc": (C.c_int, [C.POINTER(sd_config), _p, _p, _p, _p, _p, _p, _p, _p]),
     "sd_dense_decode": (C.c_int, [_p, _p, _p, _p, _p, _p, _p]),
     "sd_append_kv": (C.c_int, [_p, _p, _p, C.c_int32, _p, _p, _p, _p, _p, _p, _p]),
     "sd_sketch4_rows": (C.c_int64, [_p]),
@@ -135,6 +136,13 @@ def _stream(stream) -> Optional[int]:
         import torch
         return torch.cuda.current_stream().cuda_stream
     return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def decode_step_noalloc(cfg: sd_config, q, k, k_int8, v, lengths, out, kept_idx, stream=None) -> None:
+    """sd_decode_step_noalloc: the step without a context, its workspace in
+    the library's fixed per-GPU scratch array (no allocation)."""
+    check(lib.sd_decode_step_noalloc(C.byref(cfg), _ptr(q), _ptr(k), _ptr(k_int8), _ptr(v), _ptr(lengths),
+                                     _ptr(out), _ptr(kept_idx), _stream(stream)), "sd_decode_step_noalloc")
 
 
 class SparseDecoder:

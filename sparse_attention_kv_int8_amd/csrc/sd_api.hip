@@ -8,11 +8,21 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "sd_device.h"
 #include "sd_internal.h"
 #include "sd_select.h"
+
+// Workspace of sd_decode_step_noalloc, for callers that cannot allocate:
+// a fixed array in device memory, one copy on every GPU the library runs on,
+// held until the process ends.  Host code never passes its name to a
+// kernel (in host code the name is a stand-in, not a device address): the
+// device address of each GPU's copy is looked up once with
+// hipGetSymbolAddress and used from then on.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -186,6 +196,144 @@ struct Carver {
     }
 };
 
+// Device-dependent part of a context's set-up (no allocation): the device,
+// the LDS check of the largest kernel, and the dense decode's split count.
+sd_status device_setup(sd_ctx* c) {
+    hipError_t e0 = hipGetDevice(&c->device);
+    if (e0 != hipSuccess) return from_hip(e0, "hipGetDevice");
+    int lds_max = 0;
+    e0 = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device);
+    if (e0 != hipSuccess) return from_hip(e0, "hipDeviceGetAttribute");
+    // every stage's select runs in some kernel (stage s - 1's in the
+    // pruning kernel of stage s, the last one's in the decode kernel); the
+    // decode kernel's static LDS is the largest: the four waves' softmax
+    // state (m, l and the G x 128 accumulators), the 32-word exchange and
+    // the block tile's starts and masks
+    int64_t words = 0;
+    for (int s = 0; s < c->S; ++s)
+        words = std::max<int64_t>(words, sd::kept_lds_words(sd::stage_dev(c, s), s == 0));
+    if (c->fuse)
+        words = std::max<int64_t>(words, sd::fused_lds_words(sd::stage_dev(c, c->S - 2), c->S == 2,
+                                                             sd::stage_dev(c, c->S - 1), c->fuse_rq));
+    const int64_t static_bytes = 4 * (4 * (2 + sd::kHeadDim) * int64_t(c->G) + 32 + 2 * 256);
+    if (words * 4 + static_bytes > lds_max) {
+        std::snprintf(g_last_error, sizeof(g_last_error), "a select needs %lld bytes of LDS, more than the %d a "
+                      "workgroup has", (long long)(words * 4 + static_bytes), lds_max);
+        return SD_ERR_UNSUPPORTED;
+    }
+    // Dense decode (sd_dense_decode): 8 workgroups per compute unit in
+    // all (about 2.7 times the kernel's resident occupancy of 3, which
+    // measured faster than one resident wave of workgroups at 128K and
+    // 1M; SD_DENSE_WG_PER_CU overrides the 8), at most 512 splits per
+    // (request, KV head) (the merge's limit), at least 32 blocks of the
+    // longest request per split.
+    int cus = 0, occ = 8;
+    e0 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->device);
+    if (e0 != hipSuccess) return from_hip(e0, "hipDeviceGetAttribute");
+    if (const char* env = std::getenv("SD_DENSE_WG_PER_CU")) {
+        const int o = std::atoi(env);
+        if (o >= 1 && o <= 64) occ = o;
+    }
+    const int64_t BH = int64_t(c->cfg.batch) * c->cfg.num_kv_heads;
+    const int64_t nbmax = (c->cfg.max_context + 7) / 8;
+    int64_t nd = (int64_t(std::max(cus, 1)) * std::max(occ, 1) + BH - 1) / BH;
+    nd = std::min<int64_t>(nd, 512);
+    nd = std::min<int64_t>(nd, std::max<int64_t>(1, (nbmax + 31) / 32));
+    c->nsplit_d = int(std::max<int64_t>(nd, 1));
+    return SD_OK;
+}
+
+// Workspace layout of a planned context, every region 256-byte aligned.
+// Returns the bytes it needs; when base is not null, also points the
+// context's workspace members into [base, base + bytes).  dense: room for
+// the dense decode's split partials as well (sd_dense_decode).
+size_t carve_workspace(sd_ctx* c, char* base, bool dense) {
+    const size_t BH = size_t(c->cfg.batch) * size_t(c->cfg.num_kv_heads);
+    Carver cv;
+    size_t o_scores[SD_MAX_STAGES];
+    for (int s = 0; s < c->S; ++s) o_scores[s] = cv.take<int32_t>(BH * c->st[s].ncand);
+    const size_t o_qg = cv.take<int32_t>(BH * sd::kHeadDim);
+    const size_t o_blocks = cv.take<uint32_t>(BH * c->max_blocks);
+    const size_t o_nblocks = cv.take<int32_t>(BH);
+    const size_t nsp = size_t(dense ? std::max(c->nsplit, c->nsplit_d) : c->nsplit);
+    const size_t o_part = cv.take<float>(BH * nsp * c->G * (2 + sd::kHeadDim));
+    const size_t o_abs = cv.take<unsigned>(BH);
+    const size_t o_req = cv.take<int32_t>(BH);
+    const size_t o_flag = cv.take<int32_t>(1);
+    const size_t o_pre = c->fuse ? cv.take<int32_t>(BH * size_t(c->st[c->S - 2].ncand) * c->fuse_rq) : 0;
+    size_t o_vc[11] = {0};
+    if (c->cfg.values_on_host) {
+        c->vc.slots = int32_t(c->cfg.value_cache_tokens / 8);
+        c->vc.nblk_max = int32_t((c->Lmax + 7) / 8);
+        o_vc[0] = cv.take<uint16_t>(BH * size_t(c->vc.slots) * 8 * sd::kHeadDim);
+        o_vc[1] = cv.take<int32_t>(BH * size_t(c->vc.nblk_max));
+        o_vc[2] = cv.take<int32_t>(BH * size_t(c->vc.slots));
+        o_vc[3] = cv.take<int32_t>(BH * size_t(c->vc.slots));
+        o_vc[4] = cv.take<int32_t>(BH);
+        o_vc[5] = cv.take<int32_t>(2 * BH * size_t(c->vc.slots));
+        o_vc[6] = cv.take<int32_t>(BH * size_t(c->max_blocks));
+        o_vc[7] = cv.take<int32_t>(BH * size_t(c->max_blocks));
+        o_vc[8] = cv.take<int64_t>(sd::kVcCounters);
+        o_vc[9] = cv.take<int32_t>(BH * size_t(c->vc.slots));
+        o_vc[10] = cv.take<int32_t>(BH);
+    }
+    if (!base) return cv.off;
+    for (int s = 0; s < c->S; ++s) c->scores[s] = reinterpret_cast<int32_t*>(base + o_scores[s]);
+    c->qgroup = reinterpret_cast<int32_t*>(base + o_qg);
+    c->blocks = reinterpret_cast<uint32_t*>(base + o_blocks);
+    c->nblocks = reinterpret_cast<int32_t*>(base + o_nblocks);
+    c->part = reinterpret_cast<float*>(base + o_part);
+    c->absmax_bits = reinterpret_cast<unsigned*>(base + o_abs);
+    c->requant = reinterpret_cast<int32_t*>(base + o_req);
+    c->flag = reinterpret_cast<int32_t*>(base + o_flag);
+    c->pre = c->fuse ? reinterpret_cast<int32_t*>(base + o_pre) : nullptr;
+    if (c->cfg.values_on_host) {
+        c->vc.pool = reinterpret_cast<uint16_t*>(base + o_vc[0]);
+        c->vc.page = reinterpret_cast<int32_t*>(base + o_vc[1]);
+        c->vc.slot_block = reinterpret_cast<int32_t*>(base + o_vc[2]);
+        c->vc.slot_last = reinterpret_cast<int32_t*>(base + o_vc[3]);
+        c->vc.used = reinterpret_cast<int32_t*>(base + o_vc[4]);
+        c->vc.order = reinterpret_cast<int32_t*>(base + o_vc[5]);
+        c->vc.evicted = reinterpret_cast<int32_t*>(base + o_vc[6]);
+        c->vc.blk_slot = reinterpret_cast<int32_t*>(base + o_vc[7]);
+        c->vc.counters = reinterpret_cast<int64_t*>(base + o_vc[8]);
+        c->vc.slot_fill = reinterpret_cast<int32_t*>(base + o_vc[9]);
+        c->vc.stepc = reinterpret_cast<int32_t*>(base + o_vc[10]);
+    }
+    return cv.off;
+}
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxScratchDevices];     // device address of `scratch` on each GPU, null until looked up
+
+// Address of the scratch array on device `dev` (which must be current),
+// looked up on the first call for that device.
+sd_status scratch_on_device(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxScratchDevices) {
+        std::snprintf(g_last_error, sizeof(g_last_error), "device %d: no scratch slot (at most %d devices)", dev,
+                      kMaxScratchDevices);
+        return SD_ERR_UNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return from_hip(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return from_hip(hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return SD_OK;
+}
+
+// Zeroes n words (a fill kernel rather than a memset, so that a caller may
+// capture the call in a graph).
+__global__ void sd_clear_words_kernel(int32_t* p, int n) {
+    const int i = int(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n) p[i] = 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -211,99 +359,12 @@ sd_status sd_create(const sd_config* cfg, sd_ctx** out) {
     sd_ctx* c = new (std::nothrow) sd_ctx();
     if (!c) return SD_ERR_OUT_OF_MEMORY;
     sd_status st = plan(*cfg, c);
+    if (st == SD_OK) st = device_setup(c);
     if (st != SD_OK) { delete c; return st; }
-    {
-        hipError_t e0 = hipGetDevice(&c->device);
-        if (e0 != hipSuccess) { delete c; return from_hip(e0, "hipGetDevice"); }
-        int lds_max = 0;
-        e0 = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device);
-        if (e0 != hipSuccess) { delete c; return from_hip(e0, "hipDeviceGetAttribute"); }
-        // every stage's select runs in some kernel (stage s - 1's in the
-        // pruning kernel of stage s, the last one's in the decode kernel);
-        // the decode kernel's static LDS (partials of 4 waves) is the largest
-        int64_t words = 0;
-        for (int s = 0; s < c->S; ++s)
-            words = std::max<int64_t>(words, sd::kept_lds_words(sd::stage_dev(c, s), s == 0));
-        if (c->fuse)
-            words = std::max<int64_t>(words, sd::fused_lds_words(sd::stage_dev(c, c->S - 2), c->S == 2,
-                                                                 sd::stage_dev(c, c->S - 1), c->fuse_rq));
-        const int64_t static_bytes = 4 * (4 * (2 + sd::kHeadDim) * c->G + 64);
-        if (words * 4 + static_bytes > lds_max) { delete c; return SD_ERR_UNSUPPORTED; }
-        // Dense decode (sd_dense_decode): 8 workgroups per compute unit in
-        // all (about 2.7 times the kernel's resident occupancy of 3, which
-        // measured faster than one resident wave of workgroups at 128K and
-        // 1M; SD_DENSE_WG_PER_CU overrides the 8), at most 512 splits per
-        // (request, KV head) (the merge's limit), at least 32 blocks of the
-        // longest request per split.
-        int cus = 0, occ = 8;
-        e0 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->device);
-        if (e0 != hipSuccess) { delete c; return from_hip(e0, "hipDeviceGetAttribute"); }
-        if (const char* env = std::getenv("SD_DENSE_WG_PER_CU")) {
-            const int o = std::atoi(env);
-            if (o >= 1 && o <= 64) occ = o;
-        }
-        const int64_t BH = int64_t(cfg->batch) * cfg->num_kv_heads;
-        const int64_t nbmax = (cfg->max_context + 7) / 8;
-        int64_t nd = (int64_t(std::max(cus, 1)) * std::max(occ, 1) + BH - 1) / BH;
-        nd = std::min<int64_t>(nd, 512);
-        nd = std::min<int64_t>(nd, std::max<int64_t>(1, (nbmax + 31) / 32));
-        c->nsplit_d = int(std::max<int64_t>(nd, 1));
-    }
-
-    const size_t B = size_t(cfg->batch), H = size_t(cfg->num_kv_heads), BH = B * H;
-    Carver cv;
-    size_t o_scores[SD_MAX_STAGES];
-    for (int s = 0; s < c->S; ++s) o_scores[s] = cv.take<int32_t>(BH * c->st[s].ncand);
-    const size_t o_qg = cv.take<int32_t>(BH * sd::kHeadDim);
-    const size_t o_blocks = cv.take<uint32_t>(BH * c->max_blocks);
-    const size_t o_nblocks = cv.take<int32_t>(BH);
-    const size_t o_part = cv.take<float>(BH * size_t(std::max(c->nsplit, c->nsplit_d)) * c->G * (2 + sd::kHeadDim));
-    const size_t o_abs = cv.take<unsigned>(BH);
-    const size_t o_req = cv.take<int32_t>(BH);
-    const size_t o_flag = cv.take<int32_t>(1);
-    const size_t o_pre = c->fuse ? cv.take<int32_t>(BH * size_t(c->st[c->S - 2].ncand) * c->fuse_rq) : 0;
-    size_t o_vc[11] = {0};
-    if (cfg->values_on_host) {
-        c->vc.slots = int32_t(cfg->value_cache_tokens / 8);
-        c->vc.nblk_max = int32_t((c->Lmax + 7) / 8);
-        o_vc[0] = cv.take<uint16_t>(BH * size_t(c->vc.slots) * 8 * sd::kHeadDim);
-        o_vc[1] = cv.take<int32_t>(BH * size_t(c->vc.nblk_max));
-        o_vc[2] = cv.take<int32_t>(BH * size_t(c->vc.slots));
-        o_vc[3] = cv.take<int32_t>(BH * size_t(c->vc.slots));
-        o_vc[4] = cv.take<int32_t>(BH);
-        o_vc[5] = cv.take<int32_t>(2 * BH * size_t(c->vc.slots));
-        o_vc[6] = cv.take<int32_t>(BH * size_t(c->max_blocks));
-        o_vc[7] = cv.take<int32_t>(BH * size_t(c->max_blocks));
-        o_vc[8] = cv.take<int64_t>(sd::kVcCounters);
-        o_vc[9] = cv.take<int32_t>(BH * size_t(c->vc.slots));
-        o_vc[10] = cv.take<int32_t>(BH);
-    }
-    c->ws_bytes = cv.off;
+    c->ws_bytes = carve_workspace(c, nullptr, true);
     hipError_t e = hipMalloc(&c->ws, c->ws_bytes);
     if (e != hipSuccess) { (void)hipGetLastError(); delete c; return from_hip(e, "hipMalloc(workspace)"); }
-    char* base = static_cast<char*>(c->ws);
-    for (int s = 0; s < c->S; ++s) c->scores[s] = reinterpret_cast<int32_t*>(base + o_scores[s]);
-    c->qgroup = reinterpret_cast<int32_t*>(base + o_qg);
-    c->blocks = reinterpret_cast<uint32_t*>(base + o_blocks);
-    c->nblocks = reinterpret_cast<int32_t*>(base + o_nblocks);
-    c->part = reinterpret_cast<float*>(base + o_part);
-    c->absmax_bits = reinterpret_cast<unsigned*>(base + o_abs);
-    c->requant = reinterpret_cast<int32_t*>(base + o_req);
-    c->flag = reinterpret_cast<int32_t*>(base + o_flag);
-    c->pre = c->fuse ? reinterpret_cast<int32_t*>(base + o_pre) : nullptr;
-    if (cfg->values_on_host) {
-        c->vc.pool = reinterpret_cast<uint16_t*>(base + o_vc[0]);
-        c->vc.page = reinterpret_cast<int32_t*>(base + o_vc[1]);
-        c->vc.slot_block = reinterpret_cast<int32_t*>(base + o_vc[2]);
-        c->vc.slot_last = reinterpret_cast<int32_t*>(base + o_vc[3]);
-        c->vc.used = reinterpret_cast<int32_t*>(base + o_vc[4]);
-        c->vc.order = reinterpret_cast<int32_t*>(base + o_vc[5]);
-        c->vc.evicted = reinterpret_cast<int32_t*>(base + o_vc[6]);
-        c->vc.blk_slot = reinterpret_cast<int32_t*>(base + o_vc[7]);
-        c->vc.counters = reinterpret_cast<int64_t*>(base + o_vc[8]);
-        c->vc.slot_fill = reinterpret_cast<int32_t*>(base + o_vc[9]);
-        c->vc.stepc = reinterpret_cast<int32_t*>(base + o_vc[10]);
-    }
+    carve_workspace(c, static_cast<char*>(c->ws), true);
     // Flag and score buffers start defined; this is setup, outside any step.
     e = hipMemset(c->ws, 0, c->ws_bytes);
     if (e == hipSuccess && cfg->values_on_host) e = sd::launch_value_cache_reset(c, nullptr);
@@ -429,6 +490,40 @@ sd_status sd_decode_step_reuse(sd_ctx* c, const uint16_t* q, const uint16_t* k, 
 sd_status sd_decode_step(sd_ctx* c, const uint16_t* q, const uint16_t* k, const int8_t* k8, const uint16_t* v,
                          const int32_t* lengths, uint16_t* out, int32_t* kept, void* stream) {
     return decode_step(c, q, k, k8, nullptr, v, lengths, out, kept, 0, stream);
+}
+
+sd_status sd_decode_step_noalloc(const sd_config* cfg, const uint16_t* q, const uint16_t* k, const int8_t* k8,
+                                 const uint16_t* v, const int32_t* lengths, uint16_t* out, int32_t* kept,
+                                 void* stream) {
+    if (!cfg) return SD_ERR_INVALID_ARG;
+    if (cfg->values_on_host) {
+        std::snprintf(g_last_error, sizeof(g_last_error), "sd_decode_step_noalloc: values in host memory need a "
+                      "context (sd_create) for their value cache");
+        return SD_ERR_UNSUPPORTED;
+    }
+    sd_ctx c{};                  // the plan, on the stack; its workspace is the scratch array
+    sd_status st = plan(*cfg, &c);
+    if (st == SD_OK) st = device_setup(&c);
+    if (st != SD_OK) return st;
+    const size_t need = carve_workspace(&c, nullptr, false);
+    if (need > kNoAllocScratchBytes) {
+        std::snprintf(g_last_error, sizeof(g_last_error), "sd_decode_step_noalloc: the step needs %zu bytes of "
+                      "workspace, more than the %zu of the scratch array", need, kNoAllocScratchBytes);
+        return SD_ERR_UNSUPPORTED;
+    }
+    void* base = nullptr;
+    st = scratch_on_device(c.device, &base);
+    if (st != SD_OK) return st;
+    carve_workspace(&c, static_cast<char*>(base), false);
+    c.ws = base;
+    c.ws_bytes = need;
+    // the scratch keeps the last call's contents: the error flag must start
+    // at zero (every other word a step reads, it writes first)
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    sd_clear_words_kernel<<<1, 64, 0, s>>>(c.flag, 1);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return from_hip(e, "sd_clear_words_kernel");
+    return decode_step(&c, q, k, k8, nullptr, v, lengths, out, kept, 0, stream);
 }
 
 int64_t sd_sketch4_rows(const sd_ctx* c) { return c ? c->sketch_rows : -1; }
