@@ -204,21 +204,27 @@ sd_status device_setup(sd_ctx* c) {
     int lds_max = 0;
     e0 = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device);
     if (e0 != hipSuccess) return from_hip(e0, "hipDeviceGetAttribute");
-    // every stage's select runs in some kernel (stage s - 1's in the
-    // pruning kernel of stage s, the last one's in the decode kernel); the
-    // decode kernel's static LDS is the largest: the four waves' softmax
-    // state (m, l and the G x 128 accumulators), the 32-word exchange and
-    // the block tile's starts and masks
-    int64_t words = 0;
-    for (int s = 0; s < c->S; ++s)
-        words = std::max<int64_t>(words, sd::kept_lds_words(sd::stage_dev(c, s), s == 0));
-    if (c->fuse)
-        words = std::max<int64_t>(words, sd::fused_lds_words(sd::stage_dev(c, c->S - 2), c->S == 2,
-                                                             sd::stage_dev(c, c->S - 1), c->fuse_rq));
-    const int64_t static_bytes = 4 * (4 * (2 + sd::kHeadDim) * int64_t(c->G) + 32 + 2 * 256);
-    if (words * 4 + static_bytes > lds_max) {
-        std::snprintf(g_last_error, sizeof(g_last_error), "a select needs %lld bytes of LDS, more than the %d a "
-                      "workgroup has", (long long)(words * 4 + static_bytes), lds_max);
+    // stage s's select runs at the head of stage s + 1's pruning kernel,
+    // the last stage's (fused: the last two stages') at the head of the
+    // decode kernel.  The pruning kernels' static LDS is the query codes,
+    // the exchange words and the candidate starts (4 waves x 8); the decode
+    // kernel's is the four waves' softmax state (m, l and the G x 128
+    // accumulators), the exchange words, the block tile's starts and masks,
+    // the hand-off word and the merge's reduction (one float4 per thread).
+    const int64_t prune_static = 4 * (sd::kHeadDim + 32 + 4 * 8);
+    const int64_t attend_static = 4 * (4 * (2 + sd::kHeadDim) * int64_t(c->G) + 32 + 2 * 256 + 1 + 4 * 256);
+    int64_t need = 0;
+    for (int s = 0; s + 1 < c->S; ++s)
+        need = std::max<int64_t>(need, 4 * int64_t(sd::kept_lds_words(sd::stage_dev(c, s), s == 0)) + prune_static);
+    const int64_t last_words = c->fuse ? sd::fused_lds_words(sd::stage_dev(c, c->S - 2), c->S == 2,
+                                                             sd::stage_dev(c, c->S - 1), c->fuse_rq)
+                                       : sd::kept_lds_words(sd::stage_dev(c, c->S - 1), c->S == 1);
+    need = std::max(need, 4 * last_words + attend_static);
+    // (unfused with the stage before the last reused, the last stage is selected in the decode kernel too)
+    need = std::max(need, 4 * int64_t(sd::kept_lds_words(sd::stage_dev(c, c->S - 1), c->S == 1)) + attend_static);
+    if (need > lds_max) {
+        std::snprintf(g_last_error, sizeof(g_last_error), "a kernel needs %lld bytes of LDS, more than the %d a "
+                      "workgroup has", (long long)need, lds_max);
         return SD_ERR_UNSUPPORTED;
     }
     // Dense decode (sd_dense_decode): 8 workgroups per compute unit in
@@ -250,6 +256,10 @@ sd_status device_setup(sd_ctx* c) {
 size_t carve_workspace(sd_ctx* c, char* base, bool dense) {
     const size_t BH = size_t(c->cfg.batch) * size_t(c->cfg.num_kv_heads);
     Carver cv;
+    // the hand-off counters first, the error flag right after them: one
+    // contiguous run that sd_decode_step_noalloc clears with one fill
+    const size_t o_tick = cv.take<int32_t>(BH * sd::kTickInts);
+    const size_t o_flag = cv.take<int32_t>(1);
     size_t o_scores[SD_MAX_STAGES];
     for (int s = 0; s < c->S; ++s) o_scores[s] = cv.take<int32_t>(BH * c->st[s].ncand);
     const size_t o_qg = cv.take<int32_t>(BH * sd::kHeadDim);
@@ -259,7 +269,6 @@ size_t carve_workspace(sd_ctx* c, char* base, bool dense) {
     const size_t o_part = cv.take<float>(BH * nsp * c->G * (2 + sd::kHeadDim));
     const size_t o_abs = cv.take<unsigned>(BH);
     const size_t o_req = cv.take<int32_t>(BH);
-    const size_t o_flag = cv.take<int32_t>(1);
     const size_t o_pre = c->fuse ? cv.take<int32_t>(BH * size_t(c->st[c->S - 2].ncand) * c->fuse_rq) : 0;
     size_t o_vc[11] = {0};
     if (c->cfg.values_on_host) {
@@ -285,6 +294,7 @@ size_t carve_workspace(sd_ctx* c, char* base, bool dense) {
     c->part = reinterpret_cast<float*>(base + o_part);
     c->absmax_bits = reinterpret_cast<unsigned*>(base + o_abs);
     c->requant = reinterpret_cast<int32_t*>(base + o_req);
+    c->tick = reinterpret_cast<int32_t*>(base + o_tick);
     c->flag = reinterpret_cast<int32_t*>(base + o_flag);
     c->pre = c->fuse ? reinterpret_cast<int32_t*>(base + o_pre) : nullptr;
     if (c->cfg.values_on_host) {
@@ -445,7 +455,8 @@ sd_status decode_step(sd_ctx* c, const uint16_t* q, const uint16_t* k, const int
     // stage run reads its parents from there.  The fused plan (the last
     // stage scored inside the kernel of the one before, both selected by
     // the decode kernel) serves while that stage before the last runs;
-    // when it is reused, the last stage runs in a kernel of its own.
+    // when it is reused, the last stage runs in a kernel of its own.  The
+    // decode kernel's last split per (request, KV head) writes the output.
     const bool fused = c->fuse && reuse <= c->S - 2;
     const int nprune = fused ? c->S - 1 : c->S;
     for (int st = reuse; st < nprune && e == hipSuccess; ++st)
@@ -461,8 +472,6 @@ sd_status decode_step(sd_ctx* c, const uint16_t* q, const uint16_t* k, const int
         e = timed(c, SD_PROF_ATTEND, s, [&](sd::Timing t) {
             return sd::launch_attend(c, last_given, fused, q, k, vk, lengths, kept, out, s, t);
         });
-    if (e == hipSuccess)
-        e = timed(c, SD_PROF_COMBINE, s, [&](sd::Timing t) { return sd::launch_combine(c, c->nsplit, out, s, t); });
     return from_hip(e);
 }
 
@@ -517,10 +526,13 @@ sd_status sd_decode_step_noalloc(const sd_config* cfg, const uint16_t* q, const 
     carve_workspace(&c, static_cast<char*>(base), false);
     c.ws = base;
     c.ws_bytes = need;
-    // the scratch keeps the last call's contents: the error flag must start
-    // at zero (every other word a step reads, it writes first)
+    // the scratch keeps the last call's contents, possibly of another
+    // configuration: the hand-off counters and the error flag (one run at
+    // the start of the workspace) must start at zero; every other word a
+    // step reads, it writes first
     hipStream_t s = static_cast<hipStream_t>(stream);
-    sd_clear_words_kernel<<<1, 64, 0, s>>>(c.flag, 1);
+    const int nclear = int((c.flag - c.tick) + 1);
+    sd_clear_words_kernel<<<(nclear + 255) / 256, 256, 0, s>>>(c.tick, nclear);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return from_hip(e, "sd_clear_words_kernel");
     return decode_step(&c, q, k, k8, nullptr, v, lengths, out, kept, 0, stream);
@@ -569,6 +581,10 @@ sd_status sd_check(sd_ctx* c, void* stream) {
     if (flag) {
         e = hipMemset(c->flag, 0, sizeof(int32_t));
         if (e != hipSuccess) return from_hip(e);
+        std::snprintf(g_last_error, sizeof(g_last_error), "%s%s",
+                      (flag & sd::kFlagBadLength) ? "a length outside [1, max_context]; " : "",
+                      (flag & sd::kFlagPlacement) ? "the workgroups of one (request, KV head) ran on more than one "
+                                                    "XCD: their hand-offs, and the results, are not reliable" : "");
         return SD_ERR_DEVICE_FLAG;
     }
     return SD_OK;

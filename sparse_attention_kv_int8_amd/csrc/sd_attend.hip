@@ -7,17 +7,21 @@
 // memory: each split keeps a running max, a running sum and an fp32
 // accumulator (the tiling idea the InfiniteHiP article credits to
 // FlashAttention, section "从赫赫有名的注意力机制说起"), and the last split
-// of each (request, KV head) merges all splits by log-sum-exp.
+// of each (request, KV head) to finish merges all splits by log-sum-exp.
 //
-// Every workgroup first recomputes the last stage's kept set from its scores
-// and builds the attended block list in LDS (with values in host memory the
-// value-cache kernel has built it already); workgroup 0 publishes the kept
-// set.  Workgroup (split, KV head, request) = 4 waves; waves take the
-// split's blocks round-robin.  For one 8-token block a wave computes the G scores of
-// every token (lane = token * 8 + 16-dim slice; bf16 pair dot products,
-// DPP sum over the 8 slice lanes), takes the block max per head (uniform
-// over the wave), then accumulates P V with lane l owning output dims 2l and
-// 2l+1, reading each value row with one coalesced dword per lane.
+// The last stage's kept set is in kept_idx (the last pruning kernel wrote
+// it, or an earlier step did).  Workgroup (split, request, KV head) = 4
+// waves: the last nsplit_a splits take the sink and window (dispatched
+// last, so that their bulk loads queue behind the other splits' small loads
+// of the kept set); the others take the kept chunks' blocks (with values in
+// host memory, the value-cache kernel's block list instead); waves take the
+// split's blocks round-robin.  For one 8-token
+// block a wave computes the G scores of every token (lane = token * 8 +
+// 16-dim slice; bf16 pair dot products, DPP sum over the 8 slice lanes),
+// takes the block max per head (uniform over the wave), then accumulates
+// P V with lane l owning output dims 2l and 2l+1, reading each value row
+// with one coalesced dword per lane.  All splits of a (request, KV head) run
+// on one XCD (sd_device.h), so the merge reads their partials from its L2.
 #include "sd_device.h"
 #include "sd_internal.h"
 #include "sd_select.h"
@@ -54,12 +58,13 @@ struct AttendParams {
     int fuse_rq;
     int32_t* kept;            // [B][Hkv][keep_total]
     int keep_total;
-    int32_t* flag;            // set when the last stage is given (no pruning kernel ran)
+    int32_t* flag;            // error flags; a bad length is flagged here when the last stage is given
     int sink, window;
     float* part;              // acc [B*Hkv][nsplit][G][d], then (m, l) [B*Hkv][nsplit][G][2]
     int nsplit;               // splits per (request, KV head)
     int nsplit_a;             // of which sink/window splits (device values)
     int Bh;                   // B * Hkv
+    int32_t* tick;            // [B*Hkv][kTickInts] hand-off counters (merge by the last split)
     int64_t Lmax;
     int Hq, Hkv;
     float scale_log2;
@@ -294,22 +299,99 @@ __device__ __forceinline__ void write_partials(float* part, int Bh, int nsplit, 
     }
 }
 
+// Log-sum-exp merge of the nsplit partials of (request, KV head) bj into
+// the bf16 output of its G query heads, by the last split to finish (its
+// partials were written in this launch on the same XCD: read from the L2).
+// Weights exp2(m_s - M) / sum_s l_s exp2(m_s - M) per head (wave h < G,
+// lane = split); thread t sums output quad t % (32 G) over the splits
+// t / (32 G) + k SG (SG = 8 / G split groups, every float4 load issued at
+// once: one memory round trip), and the split groups are added through LDS.
+constexpr int kMergeMaxSplit = 64;
+
+template <int G>
+__device__ __forceinline__ void merge_splits(const AttendParams& p, int bj, int b, int j, float* wgt, float4* red) {
+    constexpr int NQ = G * kHeadDim / 4;         // float4 quads of outputs
+    constexpr int SG = kAttnThreads / NQ;        // split groups
+    constexpr int NB = kMergeMaxSplit / SG;      // splits per thread, at most
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int q = tid % NQ, sg = tid / NQ, h = (4 * q) / kHeadDim;
+    const int ns = p.nsplit;
+    const float* pa = p.part + int64_t(bj) * ns * G * kHeadDim + 4 * q;
+    const float* pml = p.part + int64_t(p.Bh) * G * kHeadDim * ns + int64_t(bj) * ns * G * 2;
+    // every load issued at once (splits beyond ns re-read the last one; their weight is 0)
+    float4 v[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+        v[u] = *reinterpret_cast<const float4*>(pa + int64_t(min(sg + u * SG, ns - 1)) * G * kHeadDim);
+    if (wave < G) {
+        const float2 ml = *reinterpret_cast<const float2*>(pml + min(lane, ns - 1) * G * 2 + wave * 2);
+        const float m = lane < ns ? ml.x : -INFINITY;
+        const float l = lane < ns ? ml.y : 0.f;
+        const float M = wave_max_f(m);
+        const float f = rescale(m, M);
+        const float Lt = wave_sum_f(l * f);
+        wgt[wave * kWave + lane] = (lane < ns && Lt > 0.f) ? f / Lt : 0.f;
+    }
+    __syncthreads();
+    SD_PHASE(3, 7);
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        const int sp = sg + u * SG;
+        const float wv = sp < ns ? wgt[h * kWave + sp] : 0.f;
+        a.x = fmaf(v[u].x, wv, a.x);
+        a.y = fmaf(v[u].y, wv, a.y);
+        a.z = fmaf(v[u].z, wv, a.z);
+        a.w = fmaf(v[u].w, wv, a.w);
+    }
+    red[sg * NQ + q] = a;
+    __syncthreads();
+    if (tid < NQ) {
+        float4 t = red[tid];
+#pragma unroll
+        for (int g = 1; g < SG; ++g) {
+            const float4 u = red[g * NQ + tid];
+            t.x += u.x;
+            t.y += u.y;
+            t.z += u.z;
+            t.w += u.w;
+        }
+        const int hh = (4 * tid) / kHeadDim, dd = (4 * tid) % kHeadDim;
+        uint16_t* o = p.out + (int64_t(b) * p.Hq + j * G + hh) * kHeadDim + dd;
+        const uint32_t lo = uint32_t(f32_to_bf16_rne(t.x)) | (uint32_t(f32_to_bf16_rne(t.y)) << 16);
+        const uint32_t hi = uint32_t(f32_to_bf16_rne(t.z)) | (uint32_t(f32_to_bf16_rne(t.w)) << 16);
+        *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+    }
+}
+
 // One instantiation per (group size, values on host, select code of the
 // last stage (kGiven: reused, read from kept_idx; unused with host values),
-// select code of the stage before
-// it when the last two stages are fused here (0 = not fused)).
+// select code of the stage before it when the last two stages are fused
+// here (0 = not fused)).
+//
+// Workgroup slots follow pipe_slot (all splits of a (request, KV head) on
+// one XCD): the kept-chunk splits come first, the sink/window splits last.
+// Every kept-chunk split selects the last stage's kept set itself (the
+// selection is deterministic, so they agree) and the first of them
+// publishes it to kept_idx; the last split to finish merges all partials.
 template <int G, bool HOSTV, int SEL, int SELP>
 __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendParams p) {
-    extern __shared__ uint32_t dyn[];   // device values: keys [last.ncand], sel [last.keep + 1], select scratch
+    extern __shared__ uint32_t dyn[];   // device values: the select (keys, sel, scratch)
     __shared__ float wm[kAttnWaves][G];
     __shared__ float wl[kAttnWaves][G];
     __shared__ float wacc[kAttnWaves][G][kHeadDim];
     __shared__ unsigned tmp[32];
     __shared__ int tblk[kBlkTile];          // first token of each block of the current tile
     __shared__ uint32_t tmask[kBlkTile];    // its token mask
+    __shared__ int ticket;
+    __shared__ float4 red[kAttnThreads];    // the merge's reduction over split groups
+    static_assert(sizeof(tblk) >= sizeof(float) * 4 * kWave, "the merge's weights fit the block tile");
 
-    const int sp = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-    const int bj = b * p.Hkv + j;
+    SD_PHASE(3, 0);
+    const PipeSlot ps = pipe_slot(p.nsplit, p.Bh);
+    if (ps.bj < 0) return;
+    const int bj = ps.bj, sp = ps.w;
+    const int b = bj / p.Hkv, j = bj - b * p.Hkv;
     const int lane = threadIdx.x & 63;
     const int sl = lane & 7;
     const int64_t Lraw = p.lengths[b];
@@ -324,9 +406,6 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         qv[h][0] = a.x; qv[h][1] = a.y; qv[h][2] = a.z; qv[h][3] = a.w;
         qv[h][4] = c.x; qv[h][5] = c.y; qv[h][6] = c.z; qv[h][7] = c.w;
     }
-
-    const int s_end = min(p.sink, L);
-    const int w0 = p.window > 0 ? max(0, L - p.window) : L;
 
     float m[G], lsum[G], acc0[G], acc1[G];
 #pragma unroll
@@ -343,26 +422,31 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         const int r0 = min(nb, sp * per), r1 = min(nb, r0 + per);
         decode_blocks<G, HOSTV>(p, ListSrc{p.blocks + int64_t(bj) * p.max_blocks}, r0, r1, bj, L, kbase, vbase,
                                 qv, m, lsum, acc0, acc1, tblk, tmask);
-    } else if (sp < p.nsplit_a) {
+    } else if (sp >= p.nsplit - p.nsplit_a) {
         // sink / window blocks: known without any selection
+        const int s_end = min(p.sink, L);
+        const int w0 = p.window > 0 ? max(0, L - p.window) : L;
         const int sb1 = (s_end + 7) >> 3, wb1 = (L + 7) >> 3;
         const int wb0 = p.window > 0 ? (w0 >> 3) : wb1;
         const bool merged = wb0 <= sb1;
         const int nr1 = merged ? wb1 : sb1;
         const int nb = nr1 + (merged ? 0 : wb1 - wb0);
         const int per = (nb + p.nsplit_a - 1) / p.nsplit_a;
-        const int r0 = min(nb, sp * per), r1 = min(nb, r0 + per);
+        const int spa = sp - (p.nsplit - p.nsplit_a);
+        const int r0 = min(nb, spa * per), r1 = min(nb, r0 + per);
         decode_blocks<G, HOSTV>(p, RangeSrc{nr1, wb0, s_end, w0, L}, r0, r1, bj, L, kbase, vbase, qv, m, lsum,
                                 acc0, acc1, tblk, tmask);
     } else {
-        // kept chunks of the last stage, recomputed from its scores (fused:
-        // from the previous stage's scores and every child's precomputed score)
+        // the kept chunks of the last stage, recomputed from its scores
+        // (fused: from the previous stage's scores and every child's
+        // precomputed score)
         int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
         int nk;
         const int* kstarts;
         if constexpr (SEL == kGiven) {
             // the last stage is reused: its kept set is read from kept_idx
-            if (L == 0 && sp == p.nsplit_a && threadIdx.x == 0) atomicOr(p.flag, 1);
+            // (and no pruning kernel ran this step to flag a bad length)
+            if (L == 0 && sp == 0 && threadIdx.x == 0) atomicOr(p.flag, kFlagBadLength);
             int* sel = reinterpret_cast<int*>(dyn + p.last.ncand);
             nk = given_kept<kAttnThreads>(p.last, kept_bj + p.last.koff, L, sel, tmp);
             kstarts = sel;
@@ -378,21 +462,24 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
                                                   p.first_stage ? nullptr : kept_bj + p.pp_koff, L, dyn, tmp);
             kstarts = reinterpret_cast<const int*>(dyn + p.last.ncand);
         }
-        const int spb = sp - p.nsplit_a, nsb = p.nsplit - p.nsplit_a;
-        kept_n = spb == 0 && SEL != kGiven ? nk : -1;   // the first of these workgroups publishes the kept set
+        SD_PHASE(3, 2);
+        kept_n = sp == 0 && SEL != kGiven ? nk : -1;   // the first of these workgroups publishes the kept set
+        const int s_end = min(p.sink, L);
+        const int w0 = p.window > 0 ? max(0, L - p.window) : L;
+        const int nsb = p.nsplit - p.nsplit_a;
         const int bpc = p.last.chunk >> 3;
         const int nb = nk * bpc;
         const int per = (nb + nsb - 1) / nsb;
-        const int r0 = min(nb, spb * per), r1 = min(nb, r0 + per);
+        const int r0 = min(nb, sp * per), r1 = min(nb, r0 + per);
         decode_blocks<G, HOSTV>(p, KeptSrc{kstarts, bpc, s_end, w0, L}, r0, r1, bj, L, kbase, vbase, qv, m, lsum,
                                 acc0, acc1, tblk, tmask);
     }
 
+    SD_PHASE(3, 3);
     write_partials<G>(p.part, p.Bh, p.nsplit, bj, sp, m, lsum, acc0, acc1, wm, wl, wacc);
     if (!HOSTV && kept_n >= 0) {
-        // the last stage's kept set (ascending, -1 padded), stored last so
-        // that no barrier waits on these stores; fused: also the previous
-        // stage's kept set and the last stage's candidate scores
+        // the last stage's kept set (ascending, -1 padded); fused: also the
+        // previous stage's kept set and the last stage's candidate scores
         int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
         const int* sel = SELP != 0 ? fused.q_starts : reinterpret_cast<const int*>(dyn + p.last.ncand);
         for (int i = threadIdx.x; i < p.last.keep; i += kAttnThreads) kept_bj[p.last.koff + i] = i < kept_n ? sel[i] : -1;
@@ -405,6 +492,13 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
             }
         }
     }
+    SD_PHASE(3, 4);
+    // the last split of this (request, KV head) to finish merges them all
+    const bool last = handoff_last(p.tick + int64_t(bj) * kTickInts, p.nsplit, &ticket, p.flag);
+    SD_PHASE(3, 5);
+    if (!last) return;
+    merge_splits<G>(p, bj, b, j, reinterpret_cast<float*>(tblk), red);
+    SD_PHASE(3, 6);
 }
 
 // Dense decode over every token t < L, the comparison path of
@@ -602,6 +696,7 @@ hipError_t launch_attend(sd_ctx* c, bool given, bool fused, const uint16_t* q, c
     p.nsplit = c->nsplit;
     p.nsplit_a = c->nsplit_a;
     p.Bh = c->cfg.batch * c->cfg.num_kv_heads;
+    p.tick = c->tick;
     const int S = c->S;
     p.last = stage_dev(c, S - 1);
     p.first_stage = S == 1;
@@ -628,7 +723,7 @@ hipError_t launch_attend(sd_ctx* c, bool given, bool fused, const uint16_t* q, c
     p.Hkv = c->cfg.num_kv_heads;
     p.scale_log2 = c->scale_log2;
     p.out = out;
-    dim3 grid(c->nsplit, c->cfg.num_kv_heads, c->cfg.batch);
+    const dim3 grid(unsigned(pipe_grid(c->nsplit, p.Bh)));
     const bool hostv = c->cfg.values_on_host != 0;
     switch (c->G) {
         case 1: launch_g<1>(p, grid, hostv, fuse, given, lds, s, t); break;
@@ -683,3 +778,5 @@ hipError_t launch_dense(sd_ctx* c, const uint16_t* q, const uint16_t* k, const u
 }
 
 }  // namespace sd
+
+SD_PHASE_SETUP(attend)

@@ -6,8 +6,32 @@
 
 namespace sd {
 
+// Phase timestamps for latency studies, compiled in only with
+// -DSD_PHASE_STAMPS: thread 0 of each workgroup records the 100 MHz
+// s_memrealtime counter at the marked points of a kernel, into
+// buf[slot][linear workgroup][phase], with buf set per source file by its
+// sd_phase_setup_* function.
+#ifdef SD_PHASE_STAMPS
+static __device__ unsigned long long* g_phase_buf;
+static __device__ int g_phase_maxwg;
+__device__ __forceinline__ void phase_stamp(int slot, int phase) {
+    unsigned long long* buf = g_phase_buf;
+    const int g = int(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+    if (buf && threadIdx.x == 0 && g < g_phase_maxwg)
+        buf[(int64_t(slot) * g_phase_maxwg + g) * 16 + phase] = __builtin_amdgcn_s_memrealtime();
+}
+#define SD_PHASE(slot, phase) ::sd::phase_stamp((slot), (phase))
+#define SD_PHASE_SETUP(name)                                                                            \
+    extern "C" int sd_phase_setup_##name(unsigned long long* buf, int maxwg) {                          \
+        if (hipMemcpyToSymbol(HIP_SYMBOL(::sd::g_phase_buf), &buf, sizeof(buf)) != hipSuccess) return 1; \
+        return hipMemcpyToSymbol(HIP_SYMBOL(::sd::g_phase_maxwg), &maxwg, sizeof(int)) != hipSuccess;   \
+    }
+#else
+#define SD_PHASE(slot, phase) ((void)0)
+#define SD_PHASE_SETUP(name)
+#endif
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
@@ -164,6 +188,89 @@ __device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* tmp, u
     *total = all;
     __syncthreads();
     return before + incl - v;
+}
+
+// ------------------------------------------------------- pipelines ----
+// The work of one (request, KV head) -- a "pipeline" -- runs on one XCD.
+// The dispatcher hands workgroups to the eight XCDs round robin, so the
+// workgroups whose linear index agrees modulo 8 share an XCD and its L2:
+// workgroup g serves pipeline (g % 8) + 8 m with m = (g / 8) / W, as its
+// workgroup w = (g / 8) % W, where W is the launch's workgroups per
+// pipeline.  Their hand-offs (the last-arriver tails below) meet in that
+// L2, with no write-back of the cache to memory.  Every workgroup also
+// records its XCD, so the last one can check that the pipeline stayed on
+// one XCD (kFlagPlacement in the error flag otherwise).
+constexpr int kXcds = 8;
+constexpr int kTickInts = 128;        // per pipeline: one 8-byte ticket word, pipelines 512 bytes apart
+constexpr int kMaxHandoffWgs = 4096;  // workgroups of one pipeline that the ticket word can count
+constexpr int32_t kFlagBadLength = 1;
+constexpr int32_t kFlagPlacement = 2;
+
+// Workgroups of a launch with W workgroups per pipeline for BH pipelines.
+__host__ __device__ constexpr int64_t pipe_grid(int W, int BH) {
+    return int64_t(kXcds) * ((BH + kXcds - 1) / kXcds) * W;
+}
+
+struct PipeSlot {
+    int bj;     // pipeline (request * Hkv + KV head), or -1: no work for this workgroup
+    int w;      // workgroup index inside the pipeline
+};
+__device__ __forceinline__ PipeSlot pipe_slot(int W, int BH) {
+    const int g = int(blockIdx.x);
+    const int x = g % kXcds, k = g / kXcds;
+    const int m = k / W, w = k - m * W;
+    const int bj = x + kXcds * m;
+    return PipeSlot{bj < BH ? bj : -1, w};
+}
+
+__device__ __forceinline__ int xcc_id() {
+    int x;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+    return x & 0xf;
+}
+
+// Waits until this wave's vector stores (and atomics) have been acknowledged
+// by the L2.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Invalidates this compute unit's vector L1: a line it cached earlier in the
+// launch (a neighbour of data it read) may be stale where another
+// workgroup wrote since; after this, plain loads fetch from the XCD's L2.
+__device__ __forceinline__ void inv_l1() { asm volatile("buffer_inv sc0" ::: "memory"); }
+
+// Last-arriver hand-off of one pipeline's workgroups: each waits for its
+// own stores, then takes a ticket; the workgroup with the last ticket gets
+// true (in every thread) and continues with the pipeline's tail, after
+// invalidating its L1 (so plain loads see what the others stored) and
+// resetting the ticket word for the next launch.  No workgroup waits for
+// another.  `word`: one int of LDS.
+//
+// The hand-off relies on one L2 for the whole pipeline, so the ticket also
+// records where the workgroups ran: each adds 1 + (x << 16) + (x^2 << 32)
+// to one 64-bit word, x its XCD.  With n tickets, count n, S1 = sum x and
+// S2 = sum x^2, all x are equal exactly when n S2 = S1^2 (the variance is
+// zero); otherwise the last workgroup sets kFlagPlacement.  Fields: count
+// 16 bits, S1 16 bits (n <= kMaxHandoffWgs, x < 16), S2 32 bits.
+__device__ __forceinline__ bool handoff_last(int32_t* tick, int nwg, int* word, int32_t* flag) {
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint64_t x = uint64_t(xcc_id());
+        const uint64_t mine = 1ull | (x << 16) | ((x * x) << 32);
+        uint64_t* t = reinterpret_cast<uint64_t*>(tick);
+        const uint64_t all = __hip_atomic_fetch_add(t, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + mine;
+        const bool last = int(all & 0xffffu) == nwg;
+        *word = last;
+        if (last) {
+            __hip_atomic_store(t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t s1 = (all >> 16) & 0xffffu, s2 = all >> 32;
+            if (uint64_t(nwg) * s2 != s1 * s1) atomicOr(flag, kFlagPlacement);
+        }
+    }
+    __syncthreads();
+    const bool last = *word != 0;
+    if (last) inv_l1();
+    return last;
 }
 
 // |x| of the two bf16 values of a dword, as bit patterns; max of the two.

@@ -94,7 +94,8 @@ struct sd_ctx {
     int32_t* pre;                     // [B][Hkv][st[S-2].ncand * fuse_rq] children's stage S-1 scores
     unsigned* absmax_bits;            // [B][Hkv] bf16 bits of each key scale (sd_quantize_keys, sd_append_kv)
     int32_t* requant;                 // [B][Hkv] set by sd_append_kv when the scale grew
-    int32_t* flag;                    // device error flag
+    int32_t* tick;                    // [B*Hkv][kTickInts] last-arriver counters (zero between launches)
+    int32_t* flag;                    // device error flag (kFlagBadLength | kFlagPlacement), right after tick
     sd::ValueCache vc;
     const void* vhost_key;            // last host value pointer seen, and its device alias
     const uint16_t* vhost_dev;
@@ -144,9 +145,13 @@ hipError_t launch_prune_stage(sd_ctx* c, int stage, bool given, bool fused, cons
                               Timing t = {});
 // int4 sketch rows of the first stage (codes with the stored key scales).
 hipError_t launch_sketch4(sd_ctx* c, const uint16_t* k, const int32_t* lengths, uint8_t* k4, hipStream_t s);
+// Attention over the attended set (the last stage's kept set, sink and
+// window), the splits merged into `out` by the last split of each (request,
+// KV head) to finish.
 hipError_t launch_attend(sd_ctx* c, bool given, bool fused, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const int32_t* lengths, int32_t* kept, uint16_t* out, hipStream_t s, Timing t = {});
-// Merges `nsplit` split partials per (request, KV head) into the bf16 output.
+// Merges `nsplit` split partials per (request, KV head) into the bf16 output
+// (the dense decode's merge).
 hipError_t launch_combine(sd_ctx* c, int nsplit, uint16_t* out, hipStream_t s, Timing t = {});
 // Dense decode over every token t < L_b (split partials; launch_combine
 // with c->nsplit_d merges them).

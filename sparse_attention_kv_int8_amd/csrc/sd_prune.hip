@@ -15,9 +15,10 @@
 // workgroup 0 publishes it in kept_idx.  When stage s-1 is reused from an
 // earlier step (the same article, same section: the modular design gives
 // fine-grained control over caching the pruning stages), that kept set is
-// read from kept_idx instead.  Then each workgroup scores its
-// slice of stage s's candidates (the children of that kept set).  The kept
-// set of the last stage is selected by the attention kernel.
+// read from kept_idx instead.  Then each workgroup scores its slice of stage
+// s's candidates (the children of that kept set).  The kept set of the last
+// stage (fused: of the last two) is selected by the attention kernel.
+
 #include "sd_device.h"
 #include "sd_internal.h"
 #include "sd_select.h"
@@ -33,7 +34,8 @@ struct PruneParams {
     const int8_t* k8;         // [B][Hkv][Lmax][d]
     const int32_t* lengths;   // [B]
     int64_t Lmax;
-    int Hq, Hkv, G;
+    int Hq, Hkv, G, BH;
+    int W;                    // workgroups per (request, KV head)
     int32_t* qgroup;          // [B][Hkv][d]
     int32_t* kept;            // [B][Hkv][keep_total]
     int keep_total;
@@ -254,77 +256,22 @@ __device__ __forceinline__ void split_query4d(const int* Qlds, int part, uint32_
     }
 }
 
-// One instantiation per (rows per candidate / 8, select code of the
-// previous stage (0 = stage 0, kGiven = the previous stage reused), fused
-// next stage): each launch carries only
-// its own path, which keeps code size and scalar-register pressure down.
-template <int NS8, int SEL, bool FUSE, bool Q4 = false>
-__global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PruneParams p) {
-    static_assert(!Q4 || (SEL == 0 && !FUSE), "the int4 sketch serves the unfused first stage only");
-    extern __shared__ uint32_t dyn[];      // the previous stage's select (kept_lds_words)
-    __shared__ int Qlds[kHeadDim];
-    __shared__ unsigned tmp[32];
-    __shared__ int cstart[kPruneWaves * kMaxCandPerWave];
-
-    const int j = blockIdx.y, b = blockIdx.z;
-    const int bj = b * p.Hkv + j;
-    const int64_t Lraw = p.lengths[b];
-    const bool bad = Lraw < 1 || Lraw > p.Lmax;
-    const int64_t L = bad ? 0 : Lraw;          // an invalid request has no candidates
-    int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
-
-    const int8_t* k8_bj = p.k8 + int64_t(bj) * p.Lmax * kHeadDim;
-    const uint8_t* k4_bj = Q4 ? p.k4 + int64_t(bj) * p.k4_rows * (kHeadDim / 2) : nullptr;
-    int32_t* scores_bj = p.scores + int64_t(bj) * p.cur.ncand;
+// Stages other than the first unfused one: the previous stage's kept set
+// (selected here, or given), then this workgroup's slice of the candidates.
+template <int NS8, int SEL, bool FUSE>
+__device__ __forceinline__ void score_later(const PruneParams& p, int bj, int wgi, int b, int j, bool bad,
+                                            int64_t L, int32_t* kept_bj, const int8_t* __restrict__ k8_bj,
+                                            int32_t* scores_bj, uint32_t* dyn, int* Qlds, unsigned* tmp,
+                                            int* cstart) {
     const int wave = threadIdx.x >> 6;
     const int sl = threadIdx.x & 7;
-    if constexpr (Q4) {
-        // First stage from the int4 sketch, one load batch per wave (cpw =
-        // CB): rows loaded first, query codes formed while they are in flight.
-        constexpr int NS16 = NS8 >= 2 ? NS8 / 2 : 1;
-        using SB = SketchBatch<NS16>;
-        const int first = (blockIdx.x * kPruneWaves + wave) * p.cpw;
-        int64_t xs[SB::CB];
-#pragma unroll
-        for (int c = 0; c < SB::CB; ++c) xs[c] = c < p.cpw ? cand_start(p.cur, true, nullptr, first + c, L) : -1;
-        SB sb;
-        sb.load(p, xs, L, k4_bj);
-        if (bad && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(p.flag, 1);
-        group_query_codes(p.q + int64_t(b) * p.Hq * kHeadDim, j, p.G, Qlds, nullptr);
-        if (blockIdx.x == 0 && threadIdx.x < kHeadDim)
-            p.qgroup[int64_t(bj) * kHeadDim + threadIdx.x] = Qlds[threadIdx.x];
-        uint32_t d0[4], d1[4], d2[4];
-        split_query4d(Qlds, threadIdx.x & 3, d0, d1, d2);
-        sb.score(p, d0, d1, d2, first, p.cpw, scores_bj);
-        return;
-    } else if constexpr (SEL == 0 && !FUSE) {
-        // First stage, one load batch per wave (cpw = CB): the candidate
-        // starts follow from the indices, so the rows are loaded first and
-        // the query codes are formed while the loads are in flight.
-        using RB = RowBatch<NS8, false>;
-        const int first = (blockIdx.x * kPruneWaves + wave) * p.cpw;
-        int64_t xs[RB::CB];
-#pragma unroll
-        for (int c = 0; c < RB::CB; ++c) xs[c] = c < p.cpw ? cand_start(p.cur, true, nullptr, first + c, L) : -1;
-        RB rb;
-        rb.load(p, xs, L, k8_bj);
-        if (bad && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(p.flag, 1);
-        group_query_codes(p.q + int64_t(b) * p.Hq * kHeadDim, j, p.G, Qlds, nullptr);
-        if (blockIdx.x == 0 && threadIdx.x < kHeadDim)
-            p.qgroup[int64_t(bj) * kHeadDim + threadIdx.x] = Qlds[threadIdx.x];
-        u32x4 qh, ql;
-        split_query(Qlds, sl, qh, ql);
-        rb.score(p, qh, ql, first, p.cpw, scores_bj, nullptr);
-        return;
-    }
-
     const int32_t* parents = nullptr;
     if constexpr (SEL == 0 || SEL == kGiven) {
         // the first stage this step runs: flags a bad length and forms the
         // group query codes, which the later stages read
-        if (bad && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(p.flag, 1);
+        if (bad && wgi == 0 && threadIdx.x == 0) atomicOr(p.flag, 1);
         group_query_codes(p.q + int64_t(b) * p.Hq * kHeadDim, j, p.G, Qlds, nullptr);
-        if (blockIdx.x == 0 && threadIdx.x < kHeadDim)
+        if (wgi == 0 && threadIdx.x < kHeadDim)
             p.qgroup[int64_t(bj) * kHeadDim + threadIdx.x] = Qlds[threadIdx.x];
     }
     if constexpr (SEL == kGiven) {
@@ -345,8 +292,9 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
         __syncthreads();
         parents = sel;
     }
+    SD_PHASE(p.stage, 1);
     // the starts of this workgroup's candidates, one thread each
-    const int wg_first = blockIdx.x * kPruneWaves * p.cpw;
+    const int wg_first = wgi * kPruneWaves * p.cpw;
     if (int(threadIdx.x) < kPruneWaves * p.cpw)
         cstart[threadIdx.x] = int(cand_start(p.cur, SEL == 0, parents, wg_first + threadIdx.x, L));
     u32x4 qh, ql;
@@ -359,9 +307,80 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
     if constexpr (SEL != 0 && SEL != kGiven) {
         // workgroup 0 publishes the previous stage's kept set (ascending,
         // -1 padded); stored last, so no barrier waits on these stores
-        if (blockIdx.x == 0)
+        if (wgi == 0)
             for (int i = threadIdx.x; i < p.prev.keep; i += kPruneThreads) kept_bj[p.prev.koff + i] = parents[i];
     }
+}
+
+// One instantiation per (rows per candidate / 8, select code of the
+// previous stage (0 = stage 0, kGiven = the previous stage reused), fused
+// next stage, int4 sketch): each launch carries only its own path, which
+// keeps code size and scalar-register pressure down.
+template <int NS8, int SEL, bool FUSE, bool Q4 = false>
+__global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PruneParams p) {
+    static_assert(!Q4 || (SEL == 0 && !FUSE), "the int4 sketch serves the unfused first stage only");
+    extern __shared__ uint32_t dyn[];      // the previous stage's select (kept_lds_words)
+    __shared__ int Qlds[kHeadDim];
+    __shared__ unsigned tmp[32];
+    __shared__ int cstart[kPruneWaves * kMaxCandPerWave];
+
+    SD_PHASE(p.stage, 0);
+    // all workgroups of a (request, KV head) on one XCD (sd_device.h): the
+    // scores they write stay in that XCD's L2 for the kernel after
+    const PipeSlot ps = pipe_slot(p.W, p.BH);
+    if (ps.bj < 0) return;
+    const int bj = ps.bj, wgi = ps.w;
+    const int b = bj / p.Hkv, j = bj - b * p.Hkv;
+    const int64_t Lraw = p.lengths[b];
+    const bool bad = Lraw < 1 || Lraw > p.Lmax;
+    const int64_t L = bad ? 0 : Lraw;          // an invalid request has no candidates
+    int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
+
+    const int8_t* k8_bj = p.k8 + int64_t(bj) * p.Lmax * kHeadDim;
+    const uint8_t* k4_bj = Q4 ? p.k4 + int64_t(bj) * p.k4_rows * (kHeadDim / 2) : nullptr;
+    int32_t* scores_bj = p.scores + int64_t(bj) * p.cur.ncand;
+    const int wave = threadIdx.x >> 6;
+    const int sl = threadIdx.x & 7;
+    if constexpr (Q4) {
+        // First stage from the int4 sketch, one load batch per wave (cpw =
+        // CB): rows loaded first, query codes formed while they are in flight.
+        constexpr int NS16 = NS8 >= 2 ? NS8 / 2 : 1;
+        using SB = SketchBatch<NS16>;
+        const int first = (wgi * kPruneWaves + wave) * p.cpw;
+        int64_t xs[SB::CB];
+#pragma unroll
+        for (int c = 0; c < SB::CB; ++c) xs[c] = c < p.cpw ? cand_start(p.cur, true, nullptr, first + c, L) : -1;
+        SB sb;
+        sb.load(p, xs, L, k4_bj);
+        if (bad && wgi == 0 && threadIdx.x == 0) atomicOr(p.flag, 1);
+        group_query_codes(p.q + int64_t(b) * p.Hq * kHeadDim, j, p.G, Qlds, nullptr);
+        if (wgi == 0 && threadIdx.x < kHeadDim)
+            p.qgroup[int64_t(bj) * kHeadDim + threadIdx.x] = Qlds[threadIdx.x];
+        uint32_t d0[4], d1[4], d2[4];
+        split_query4d(Qlds, threadIdx.x & 3, d0, d1, d2);
+        sb.score(p, d0, d1, d2, first, p.cpw, scores_bj);
+    } else if constexpr (SEL == 0 && !FUSE) {
+        // First stage, one load batch per wave (cpw = CB): the candidate
+        // starts follow from the indices, so the rows are loaded first and
+        // the query codes are formed while the loads are in flight.
+        using RB = RowBatch<NS8, false>;
+        const int first = (wgi * kPruneWaves + wave) * p.cpw;
+        int64_t xs[RB::CB];
+#pragma unroll
+        for (int c = 0; c < RB::CB; ++c) xs[c] = c < p.cpw ? cand_start(p.cur, true, nullptr, first + c, L) : -1;
+        RB rb;
+        rb.load(p, xs, L, k8_bj);
+        if (bad && wgi == 0 && threadIdx.x == 0) atomicOr(p.flag, 1);
+        group_query_codes(p.q + int64_t(b) * p.Hq * kHeadDim, j, p.G, Qlds, nullptr);
+        if (wgi == 0 && threadIdx.x < kHeadDim)
+            p.qgroup[int64_t(bj) * kHeadDim + threadIdx.x] = Qlds[threadIdx.x];
+        u32x4 qh, ql;
+        split_query(Qlds, sl, qh, ql);
+        rb.score(p, qh, ql, first, p.cpw, scores_bj, nullptr);
+    } else {
+        score_later<NS8, SEL, FUSE>(p, bj, wgi, b, j, bad, L, kept_bj, k8_bj, scores_bj, dyn, Qlds, tmp, cstart);
+    }
+    SD_PHASE(p.stage, 2);
 }
 
 StageDev stage_dev(const sd_ctx* c, int st) {
@@ -389,6 +408,8 @@ hipError_t launch_prune_stage(sd_ctx* c, int st, bool given, bool fused, const u
     p.Hq = c->cfg.num_q_heads;
     p.Hkv = c->cfg.num_kv_heads;
     p.G = c->G;
+    p.BH = c->cfg.batch * c->cfg.num_kv_heads;
+    p.W = c->st[st].nwg;
     p.qgroup = c->qgroup;
     p.kept = kept;
     p.keep_total = c->keep_total;
@@ -403,49 +424,52 @@ hipError_t launch_prune_stage(sd_ctx* c, int st, bool given, bool fused, const u
     p.fuse_rq = fuse ? c->fuse_rq : 0;
     p.fuse_m = fuse ? c->fuse_m : 1;
     p.pre = fuse ? c->pre : nullptr;
-    size_t lds = 0;
+    size_t words = 0;
     if (st > 0) {
         p.prev = stage_dev(c, st - 1);
         p.prev_scores = c->scores[st - 1];
         p.pp_koff = st >= 2 ? c->st[st - 2].koff : 0;
-        lds = size_t(kept_lds_words(p.prev, st == 1)) * 4;
+        if (!given) words = size_t(kept_lds_words(p.prev, st == 1));
+        else words = size_t(p.prev.ncand + p.prev.keep + 1);
     }
-    dim3 grid(c->st[st].nwg, c->cfg.num_kv_heads, c->cfg.batch);
+    const size_t lds = words * 4;
     const int ns8 = (p.nrows + 7) >> 3;
     const int sel = st == 0 ? 0 : given ? kGiven : select_width(p.prev.ncand);
-#define SD_PRUNE(N, S, F) launch(sd_prune_stage_kernel<N, S, F>, grid, dim3(kPruneThreads), lds, s, t, p)
-#define SD_PRUNE_UNFUSED(S)                                     \
-    if (ns8 == 1) SD_PRUNE(1, S, false);                        \
-    else if (ns8 == 2) SD_PRUNE(2, S, false);                   \
-    else if (ns8 <= 4) SD_PRUNE(4, S, false);                   \
-    else SD_PRUNE(8, S, false)
-#define SD_PRUNE_NS(S)                                          \
-    if (fuse) {                                                 \
-        if (ns8 <= 2) SD_PRUNE(2, S, true);                     \
-        else if (ns8 <= 4) SD_PRUNE(4, S, true);                \
-        else SD_PRUNE(8, S, true);                              \
-    } else {                                                    \
-        SD_PRUNE_UNFUSED(S);                                    \
-    }
     const bool q4 = k4 != nullptr && st == 0 && !fuse;
     if (q4) {
         // one batch of int4 candidates per wave (SketchBatch: 8 / NS16)
         const int ns8p = ns8 == 1 ? 1 : ns8 == 2 ? 2 : ns8 <= 4 ? 4 : 8;
         p.cpw = 8 / (ns8p >= 2 ? ns8p / 2 : 1);
-        grid.x = (p.cur.ncand + kPruneWaves * p.cpw - 1) / (kPruneWaves * p.cpw);
-        if (ns8 == 1) launch(sd_prune_stage_kernel<1, 0, false, true>, grid, dim3(kPruneThreads), lds, s, t, p);
-        else if (ns8 == 2) launch(sd_prune_stage_kernel<2, 0, false, true>, grid, dim3(kPruneThreads), lds, s, t, p);
-        else if (ns8 <= 4) launch(sd_prune_stage_kernel<4, 0, false, true>, grid, dim3(kPruneThreads), lds, s, t, p);
-        else launch(sd_prune_stage_kernel<8, 0, false, true>, grid, dim3(kPruneThreads), lds, s, t, p);
-    } else if (sel == 0) { SD_PRUNE_NS(0); }
-    else if (sel == kGiven) { SD_PRUNE_NS(kGiven); }
-    else if (sel == 4) { SD_PRUNE_NS(4); }
-    else if (sel == 16) { SD_PRUNE_NS(16); }
-    else { SD_PRUNE_NS(kSelLds); }
-#undef SD_PRUNE_NS
-#undef SD_PRUNE_UNFUSED
-#undef SD_PRUNE
+        p.W = (p.cur.ncand + kPruneWaves * p.cpw - 1) / (kPruneWaves * p.cpw);
+    }
+    const dim3 grid(unsigned(pipe_grid(p.W, p.BH))), block(kPruneThreads);
+#define SD_K(N, S, F, Q) launch(sd_prune_stage_kernel<N, S, F, Q>, grid, block, lds, s, t, p)
+#define SD_NS(S)                                               \
+    if (fuse) {                                                \
+        if (ns8 <= 2) SD_K(2, S, true, false);                 \
+        else if (ns8 <= 4) SD_K(4, S, true, false);            \
+        else SD_K(8, S, true, false);                          \
+    } else {                                                   \
+        if (ns8 == 1) SD_K(1, S, false, false);                \
+        else if (ns8 == 2) SD_K(2, S, false, false);           \
+        else if (ns8 <= 4) SD_K(4, S, false, false);           \
+        else SD_K(8, S, false, false);                         \
+    }
+    if (q4) {
+        if (ns8 == 1) SD_K(1, 0, false, true);
+        else if (ns8 == 2) SD_K(2, 0, false, true);
+        else if (ns8 <= 4) SD_K(4, 0, false, true);
+        else SD_K(8, 0, false, true);
+    } else if (sel == 0) { SD_NS(0); }
+    else if (sel == kGiven) { SD_NS(kGiven); }
+    else if (sel == 4) { SD_NS(4); }
+    else if (sel == 16) { SD_NS(16); }
+    else { SD_NS(kSelLds); }
+#undef SD_NS
+#undef SD_K
     return hipGetLastError();
 }
 
 }  // namespace sd
+
+SD_PHASE_SETUP(prune)

@@ -1,11 +1,10 @@
 // Exact per-(request, KV head) top-K select and the attended block list.
 //
-// Every workgroup that needs a stage's kept set recomputes it from that
-// stage's candidate scores (a few KiB, cache resident): the selection is
-// deterministic, so all workgroups of a (request, KV head) agree, and no
-// cross-workgroup counter or fence is needed (device-scope atomics on one
-// address serialise at roughly 0.1 us each on this chip, which made a
-// "last workgroup" hand-off far slower than recomputing).
+// A stage's kept set is selected by every workgroup of the next kernel that
+// needs it (the next pruning kernel, or the decode kernel's kept-chunk
+// splits for the last stage), redundantly, from the stage's scores (a few
+// KiB): the selection is deterministic, so all workgroups of a (request, KV
+// head) agree, and no workgroup waits for another.
 //
 // Selection order: score descending, then candidate index (= chunk start)
 // ascending, following the top-K chunk rule of the news article on
@@ -119,7 +118,8 @@ __device__ __forceinline__ KeyStats block_key_stats(unsigned nv, uint32_t kmin, 
 
 // Loads n chunk scores into LDS as select keys, clears the histogram of the
 // select scratch `cand` (kRadixWords words), and returns the KeyStats; also
-// stages npar ints `parents` into `par` (LDS).  The parents' loads and the
+// stages npar ints `parents` (the previous stage's kept starts) into `par`
+// (LDS).  Both are read from the L2.  The parents' loads and the
 // first kLoadBatch scores of every thread are issued before any of them is
 // waited for, so up to 2048 candidates cost one memory round trip (the loads of a
 // wave complete in issue order: a load-wait-store loop would pay one round
@@ -455,21 +455,32 @@ __device__ FusedOut kept_two_stages(const StageDev& P, bool p_first, const int32
     int* candQ = selQ + Q.keep + 1;
     int* startsP = candQ + select_cand_words(Q.ncand, Q.keep);
 
-    // the children's Q scores are issued first (in batches, no wait between
-    // the loads of a batch), then P's parents and scores
-    for (int i0 = threadIdx.x; i0 < P.ncand * rq; i0 += kLoadBatch * NT) {
+    // the first batch of the children's Q scores is issued, then P's parents
+    // and scores (load_keys): one memory round trip for all of them up to
+    // kLoadBatch * NT children (the loads of a wave complete in issue order)
+    const int npre = P.ncand * rq;
+    int32_t v0[kLoadBatch];
+#pragma unroll
+    for (int u = 0; u < kLoadBatch; ++u) {
+        const int i = threadIdx.x + u * NT;
+        v0[u] = i < npre ? pre_bj[i] : 0;
+    }
+    const KeyStats ksP = load_keys<NT>(scoresP_bj, P.ncand, keysP, reinterpret_cast<uint32_t*>(candP), tmp, parentsP,
+                                       p_first ? 0 : P.ncand / P.ratio, parP);
+#pragma unroll
+    for (int u = 0; u < kLoadBatch; ++u)
+        if (threadIdx.x + u * NT < npre) preL[threadIdx.x + u * NT] = v0[u];
+    for (int i0 = threadIdx.x + kLoadBatch * NT; i0 < npre; i0 += kLoadBatch * NT) {
         int32_t v[kLoadBatch];
 #pragma unroll
         for (int u = 0; u < kLoadBatch; ++u) {
             const int i = i0 + u * NT;
-            v[u] = i < P.ncand * rq ? pre_bj[i] : 0;
+            v[u] = i < npre ? pre_bj[i] : 0;
         }
 #pragma unroll
         for (int u = 0; u < kLoadBatch; ++u)
-            if (i0 + u * NT < P.ncand * rq) preL[i0 + u * NT] = v[u];
+            if (i0 + u * NT < npre) preL[i0 + u * NT] = v[u];
     }
-    const KeyStats ksP = load_keys<NT>(scoresP_bj, P.ncand, keysP, reinterpret_cast<uint32_t*>(candP), tmp, parentsP,
-                                       p_first ? 0 : P.ncand / P.ratio, parP);
     const int np = select_top<NT, EP>(keysP, P.ncand, P.keep, selP, candP, tmp, ksP);
     // P starts; Q candidate i is child i % rq of kept P chunk i / rq
     for (int i = threadIdx.x; i < P.keep; i += NT)

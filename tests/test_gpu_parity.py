@@ -162,13 +162,14 @@ def test_many_candidate_groups_with_ties():
     run_case(w, modify=dup, check_scores=True)
 
 
-@pytest.mark.parametrize("max_context", [65536, 131072 - 40, 300000 - 8])
+@pytest.mark.parametrize("max_context", [32768, 20000 - 8, 65536, 131072 - 40, 300000 - 8])
 def test_all_scores_equal_in_full_groups(max_context):
     """Every key row identical, so every chunk score of a stage is equal: the
-    lowest starts must win.  The sizes give 1,024 stage-0 candidates (four
-    keys per lane of the cooperative select, all slots full), 2,048 with a
-    ragged last chunk (sixteen per lane), and 4,688 (read from LDS in every
-    pass, last block partial)."""
+    lowest starts must win.  The sizes give 512 stage-0 candidates (four
+    keys per lane of the cooperative select, half the slots empty), 313 with
+    a ragged last chunk, 1,024 (all slots full), 2,048 with a ragged last
+    chunk (sixteen per lane), and 4,688 (read from LDS in every pass, last
+    block partial)."""
     w = tiny_workload(name="equal", batch=1, num_q_heads=4, num_kv_heads=1, max_context=max_context,
                       stages=(Stage(64, 8, 40), Stage(8, 1, 64)), sink=0, window=0, planted=0)
 
