@@ -111,6 +111,7 @@ typedef struct sd_stats {
     int64_t last_misses;
     int64_t refills;
     int64_t last_refills;
+    int64_t last_copies;        /* SD_VALUE_FETCH_COPY: hipMemcpyAsync calls of the last step (else 0) */
 } sd_stats;
 
 /* Creates a context on the current HIP device, validating `cfg` and
@@ -303,6 +304,27 @@ sd_status sd_decode_step_sketch4(sd_ctx* ctx, const uint16_t* q, const uint16_t*
 sd_status sd_quantize_query(sd_ctx* ctx, const uint16_t* q, int8_t* q8, int32_t* q_group,
                             void* stream);
 
+/* Records the attended set as the decode kernel walks it, for inspection:
+ * from the next sd_decode_step / sd_decode_step_reuse / sd_decode_step_sketch4
+ * of this context on, until called with dst = NULL, each 8-token block the
+ * kernel's block loop attends is stored as one word, block << 8 | mask
+ * (block = first token / 8; bit i of the 8-bit mask set when token
+ * 8 block + i is attended), into device memory dst laid out
+ * [B][Hkv][max_blocks], max_blocks = keep_last * chunk_last / 8 +
+ * ceil(sink / 8) + ceil(window / 8) + 1.  Device values: words
+ * [0, keep_last * chunk_last / 8) of a (request, KV head) are the blocks of
+ * the last stage's kept chunks (in kept order, sink and window tokens
+ * masked out), words from keep_last * chunk_last / 8 on are the sink and
+ * window blocks; host values: the attended block list.  So the union of the
+ * masks is the attended set (kept last-stage chunks, sink and window:
+ * "KV Cache 与长上下文推理", section "KV Cache 压缩技术"), each token once.
+ * Words the step does not write keep their value: clear dst before a step.
+ * The caller keeps dst alive while recording is on; the words are stored by
+ * the same block loop that loads the keys and values.
+ *  SD_ERR_INVALID_ARG  dst_len < B * Hkv * max_blocks.
+ *  SD_ERR_UNSUPPORTED  max_context > 2^27 (block ids must fit 24 bits). */
+sd_status sd_record_attended(sd_ctx* ctx, uint32_t* dst, int64_t dst_len);
+
 /* Copies the chunk scores stage `stage` (0-based) computed by the last
  * sd_decode_step into device memory `dst`, laid out [B][Hkv][n_stage] int32
  * (n_0 = ceil(Lmax / chunk_0), n_s = keep_{s-1} * chunk_{s-1} / chunk_s);
@@ -323,6 +345,28 @@ sd_status sd_get_stats(sd_ctx* ctx, sd_stats* stats, void* stream);
 
 /* Empties the value cache and zeroes the counters (enqueued on `stream`). */
 sd_status sd_reset_value_cache(sd_ctx* ctx, void* stream);
+
+/* How missed value blocks reach the device (values_on_host = 1).
+ *  SD_VALUE_FETCH_MAPPED (default): the decode kernel reads each missed
+ *    block from pinned host memory through its device alias and writes it
+ *    into the block's slot, in the same pass that attends it; the step
+ *    stays asynchronous and graph-capturable.
+ *  SD_VALUE_FETCH_COPY: the gathered-copy design (HCAttention, section 引言:
+ *    values kept in CPU memory and fetched late, for the final weighted
+ *    sum; news article on InfiniteHiP, section "解决长上下文推理问题，能通过键值
+ *    缓存卸载节约 GPU 内存": offloaded KV blocks fetched on demand): after
+ *    the value-cache kernel, the host waits for the step's block list,
+ *    enqueues one hipMemcpyAsync per run of missed blocks (consecutive in
+ *    host memory and in the slot pool) on a side stream of the context,
+ *    and the decode kernel, ordered after those copies by an event, reads
+ *    every block from the slot pool.  Same LRU, same results; the step
+ *    synchronises the host once and cannot be captured in a graph
+ *    (SD_ERR_UNSUPPORTED while `stream` is capturing).
+ * SD_ERR_UNSUPPORTED if values_on_host = 0; SD_ERR_INVALID_ARG for another
+ * mode.  Takes effect from the next step. */
+#define SD_VALUE_FETCH_MAPPED 0
+#define SD_VALUE_FETCH_COPY 1
+sd_status sd_set_value_fetch(sd_ctx* ctx, int32_t mode);
 
 /* Kernel kinds timed by the profiler. */
 enum {

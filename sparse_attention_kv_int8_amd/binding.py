@@ -43,6 +43,7 @@ class sd_config(C.Structure):
 SD_PROF_KINDS = 10
 SD_PROF_STAGE0, SD_PROF_VALUE_CACHE, SD_PROF_ATTEND, SD_PROF_QUANTIZE = 0, 4, 5, 6
 SD_PROF_COMBINE, SD_PROF_DENSE, SD_PROF_APPEND = 7, 8, 9
+SD_VALUE_FETCH_MAPPED, SD_VALUE_FETCH_COPY = 0, 1
 PROF_NAMES = ["stage0", "stage1", "stage2", "stage3", "value_cache", "attend", "quantize", "combine", "dense",
               "append"]
 
@@ -53,7 +54,8 @@ class sd_profile(C.Structure):
 
 class sd_stats(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("steps", "blocks_needed", "hits", "misses", "h2d_bytes",
-                                         "last_needed", "last_hits", "last_misses", "refills", "last_refills")]
+                                         "last_needed", "last_hits", "last_misses", "refills", "last_refills",
+                                         "last_copies")]
 
 
 if not os.path.exists(LIB_PATH):
@@ -82,6 +84,8 @@ _SIGS = {
     "sd_decode_step_sketch4": (C.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "sd_quantize_query": (C.c_int, [_p, _p, _p, _p, _p]),
     "sd_stage_scores": (C.c_int, [_p, C.c_int32, _p, C.c_int64, _p]),
+    "sd_record_attended": (C.c_int, [_p, _p, C.c_int64]),
+    "sd_set_value_fetch": (C.c_int, [_p, C.c_int32]),
     "sd_stage_candidates": (C.c_int64, [_p, C.c_int32]),
     "sd_check": (C.c_int, [_p, _p]),
     "sd_get_stats": (C.c_int, [_p, C.POINTER(sd_stats), _p]),
@@ -231,6 +235,16 @@ class SparseDecoder:
     def sd_stage_scores(self, stage: int, dst, stream=None) -> None:
         check(lib.sd_stage_scores(self.handle, stage, _ptr(dst), dst.numel(), _stream(stream)),
               "sd_stage_scores")
+
+    def sd_set_value_fetch(self, mode: int) -> None:
+        check(lib.sd_set_value_fetch(self.handle, mode), "sd_set_value_fetch")
+
+    def sd_record_attended(self, dst) -> None:
+        """dst: a device uint32/int32 tensor of B * Hkv * max_blocks words, or None to stop."""
+        if dst is None:
+            check(lib.sd_record_attended(self.handle, None, 0), "sd_record_attended")
+        else:
+            check(lib.sd_record_attended(self.handle, _ptr(dst), dst.numel()), "sd_record_attended")
 
     def sd_check(self, stream=None) -> int:
         return int(lib.sd_check(self.handle, _stream(stream)))

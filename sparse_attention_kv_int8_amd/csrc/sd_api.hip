@@ -391,6 +391,9 @@ void sd_destroy(sd_ctx* c) {
     if (cur != c->device) (void)hipSetDevice(c->device);
     (void)hipDeviceSynchronize();
     free_profiler(c);
+    if (c->vside) (void)hipStreamDestroy(c->vside);
+    if (c->vside_done) (void)hipEventDestroy(c->vside_done);
+    if (c->vstage) (void)hipHostFree(c->vstage);
     (void)hipFree(c->ws);
     if (cur != c->device && cur >= 0) (void)hipSetDevice(cur);
     delete c;
@@ -427,6 +430,67 @@ sd_status sd_quantize_query(sd_ctx* c, const uint16_t* q, int8_t* q8, int32_t* q
 
 namespace {
 
+// SD_VALUE_FETCH_COPY, after the value-cache kernel of a step on stream s:
+// waits for the step's attended block list, then copies every missed (or
+// refilled) block's rows t < L from host memory v into its slot, one
+// hipMemcpyAsync per run of blocks consecutive both in host memory and in
+// the slot pool, on the side stream; s waits for them before the decode
+// kernel.
+hipError_t copy_missed_blocks(sd_ctx* c, const uint16_t* v, const int32_t* lengths, hipStream_t s) {
+    const int B = c->cfg.batch, Hkv = c->cfg.num_kv_heads, BH = B * Hkv, MB = c->max_blocks;
+    int32_t* h_nb = c->vstage;
+    int32_t* h_len = h_nb + BH;
+    int32_t* h_blocks = h_len + B;
+    int32_t* h_slot = h_blocks + int64_t(BH) * MB;
+    hipError_t e = hipMemcpyAsync(h_nb, c->nblocks, sizeof(int32_t) * BH, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(h_len, lengths, sizeof(int32_t) * B, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(h_blocks, c->blocks, sizeof(int32_t) * BH * MB, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(h_slot, c->vc.blk_slot, sizeof(int32_t) * BH * MB, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return e;
+    constexpr int64_t kBlockElems = 8 * sd::kHeadDim;
+    const int64_t slots = c->vc.slots;
+    int64_t runs = 0;
+    for (int bj = 0; bj < BH && e == hipSuccess; ++bj) {
+        const int64_t L = h_len[bj / Hkv];
+        if (L < 1 || L > c->Lmax) continue;          // no blocks (flagged by the pruning kernels)
+        const int nb = std::min(h_nb[bj], MB);
+        int64_t run_blk = -1, run_slot = -1, run_rows = 0;
+        auto flush = [&]() -> hipError_t {
+            if (run_rows == 0) return hipSuccess;
+            ++runs;
+            return hipMemcpyAsync(c->vc.pool + (int64_t(bj) * slots + run_slot) * kBlockElems,
+                                  v + (int64_t(bj) * c->Lmax + run_blk * 8) * sd::kHeadDim,
+                                  size_t(run_rows) * sd::kHeadDim * sizeof(uint16_t), hipMemcpyHostToDevice,
+                                  c->vside);
+        };
+        for (int r = 0; r < nb && e == hipSuccess; ++r) {
+            const int32_t se = h_slot[int64_t(bj) * MB + r];
+            if (!(se & (sd::kVcMissBit | sd::kVcRefillBit))) continue;
+            const int64_t blk = int64_t(uint32_t(h_blocks[int64_t(bj) * MB + r]) >> 8);
+            const int64_t slot = se & sd::kVcSlotMask;
+            const int64_t rows = std::min<int64_t>(8, L - 8 * blk);
+            if (rows <= 0 || slot >= slots) continue;
+            // extends the run when both sides continue it (the run's rows so far are whole blocks)
+            if (run_rows > 0 && run_rows % 8 == 0 && blk == run_blk + run_rows / 8 && slot == run_slot + run_rows / 8) {
+                run_rows += rows;
+                continue;
+            }
+            e = flush();
+            run_blk = blk;
+            run_slot = slot;
+            run_rows = rows;
+        }
+        if (e == hipSuccess) e = flush();
+    }
+    c->vcopies = runs;
+    if (e == hipSuccess) e = hipEventRecord(c->vside_done, c->vside);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, c->vside_done, 0);
+    return e;
+}
+
 // One decode step; k4 (the int4 first-stage sketch) or null.
 sd_status decode_step(sd_ctx* c, const uint16_t* q, const uint16_t* k, const int8_t* k8, const uint8_t* k4,
                       const uint16_t* v, const int32_t* lengths, uint16_t* out, int32_t* kept, int32_t reuse,
@@ -436,6 +500,13 @@ sd_status decode_step(sd_ctx* c, const uint16_t* q, const uint16_t* k, const int
         return SD_ERR_INVALID_ARG;
     if (reuse < 0 || reuse > c->S) return SD_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool vcopy = c->cfg.values_on_host && c->vfetch == SD_VALUE_FETCH_COPY;
+    if (vcopy) {
+        // the copies wait for the host, which a captured graph cannot do
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) != hipSuccess) return from_hip(hipGetLastError());
+        if (cs != hipStreamCaptureStatusNone) return SD_ERR_UNSUPPORTED;
+    }
     const uint16_t* vk = v;
     if (c->cfg.values_on_host) {
         // v is pinned host memory: the kernels read it through its device alias
@@ -468,6 +539,7 @@ sd_status decode_step(sd_ctx* c, const uint16_t* q, const uint16_t* k, const int
         e = timed(c, SD_PROF_VALUE_CACHE, s, [&](sd::Timing t) {
             return sd::launch_value_cache_update(c, last_given, lengths, kept, s, t);
         });
+    if (e == hipSuccess && vcopy) e = copy_missed_blocks(c, v, lengths, s);
     if (e == hipSuccess)
         e = timed(c, SD_PROF_ATTEND, s, [&](sd::Timing t) {
             return sd::launch_attend(c, last_given, fused, q, k, vk, lengths, kept, out, s, t);
@@ -562,6 +634,46 @@ int64_t sd_stage_candidates(const sd_ctx* c, int32_t stage) {
     return c->st[stage].ncand;
 }
 
+sd_status sd_set_value_fetch(sd_ctx* c, int32_t mode) {
+    if (!c) return SD_ERR_INVALID_ARG;
+    if (mode != SD_VALUE_FETCH_MAPPED && mode != SD_VALUE_FETCH_COPY) return SD_ERR_INVALID_ARG;
+    if (!c->cfg.values_on_host) return SD_ERR_UNSUPPORTED;
+    if (mode == SD_VALUE_FETCH_COPY && !c->vstage) {
+        int cur = -1;
+        (void)hipGetDevice(&cur);
+        if (cur != c->device) (void)hipSetDevice(c->device);
+        const int64_t BH = int64_t(c->cfg.batch) * c->cfg.num_kv_heads;
+        const size_t bytes = sizeof(int32_t) * size_t(BH + c->cfg.batch + 2 * BH * c->max_blocks);
+        hipError_t e = hipStreamCreateWithFlags(&c->vside, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&c->vside_done, hipEventDisableTiming);
+        void* h = nullptr;
+        if (e == hipSuccess) e = hipHostMalloc(&h, bytes, hipHostMallocDefault);
+        if (cur != c->device && cur >= 0) (void)hipSetDevice(cur);
+        if (e != hipSuccess) {
+            if (c->vside) (void)hipStreamDestroy(c->vside);
+            if (c->vside_done) (void)hipEventDestroy(c->vside_done);
+            c->vside = nullptr;
+            c->vside_done = nullptr;
+            return from_hip(e, "sd_set_value_fetch");
+        }
+        c->vstage = static_cast<int32_t*>(h);
+    }
+    c->vfetch = mode;
+    return SD_OK;
+}
+
+sd_status sd_record_attended(sd_ctx* c, uint32_t* dst, int64_t dst_len) {
+    if (!c) return SD_ERR_INVALID_ARG;
+    if (!dst) {
+        c->rec = nullptr;
+        return SD_OK;
+    }
+    if (dst_len < int64_t(c->cfg.batch) * c->cfg.num_kv_heads * c->max_blocks) return SD_ERR_INVALID_ARG;
+    if (c->Lmax > (int64_t(1) << 27)) return SD_ERR_UNSUPPORTED;    // block ids must fit 24 bits
+    c->rec = dst;
+    return SD_OK;
+}
+
 sd_status sd_stage_scores(sd_ctx* c, int32_t stage, int32_t* dst, int64_t dst_len, void* stream) {
     if (!c || !dst || stage < 0 || stage >= c->S) return SD_ERR_INVALID_ARG;
     const int64_t n = int64_t(c->cfg.batch) * c->cfg.num_kv_heads * c->st[stage].ncand;
@@ -612,6 +724,7 @@ sd_status sd_get_stats(sd_ctx* c, sd_stats* out, void* stream) {
         out->last_misses = h[6 + 4 * par];
         out->last_refills = h[7 + 4 * par];
     }
+    out->last_copies = c->vfetch == SD_VALUE_FETCH_COPY ? c->vcopies : 0;
     return SD_OK;
 }
 

@@ -40,6 +40,7 @@ struct AttendParams {
     uint16_t* vpool;          // [B][Hkv][slots][8][d] (host-value path)
     const int32_t* blk_slot;  // [B][Hkv][max_blocks]   (host-value path)
     int vslots;
+    int vcopied;              // host values: this step's missed blocks were copied into their slots already
     const int32_t* lengths;
     const uint32_t* blocks;   // [B][Hkv][max_blocks] (host-value path: built by the value-cache kernel)
     const int32_t* nblocks;   // [B][Hkv]           (host-value path)
@@ -69,6 +70,7 @@ struct AttendParams {
     int Hq, Hkv;
     float scale_log2;
     uint16_t* out;            // [B][Hq][d]
+    uint32_t* rec;            // null, or [B][Hkv][max_blocks]: the (block << 8 | mask) words attended
 };
 
 __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
@@ -153,7 +155,7 @@ __device__ __forceinline__ void load_block(const AttendParams& p, int r, int t0,
     if (HOSTV) {
         const int32_t se = p.blk_slot[int64_t(bj) * p.max_blocks + r];
         uint32_t* prow = reinterpret_cast<uint32_t*>(p.vpool + (int64_t(bj) * p.vslots + (se & kVcSlotMask)) * 8 * kHeadDim);
-        if (se & (kVcMissBit | kVcRefillBit)) {
+        if (!p.vcopied && (se & (kVcMissBit | kVcRefillBit))) {
             const uint32_t* hrow = reinterpret_cast<const uint32_t*>(vbase + int64_t(t0) * kHeadDim);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -224,15 +226,17 @@ __device__ __forceinline__ void attend_block(const BlockData& d, const uint32_t 
 
 // The block loop of one workgroup over blocks [r0, r1) of its source.  The
 // (block, mask) entries are computed once per tile of kBlkTile blocks, one
-// per thread, into LDS; each wave then takes every kAttnWaves-th block of
-// the tile, two blocks in flight.
+// per thread, into LDS (and, when rec is not null, stored as rec[r] =
+// block << 8 | mask for inspection); each wave then takes every
+// kAttnWaves-th block of the tile, two blocks in flight.
 constexpr int kBlkTile = kAttnThreads;
 
 template <int G, bool HOSTV, class Src>
 __device__ __forceinline__ void decode_blocks(const AttendParams& p, const Src& src, int r0, int r1, int bj, int L,
                                               const uint16_t* kbase, const uint16_t* vbase,
                                               const uint32_t (&qv)[G][8], float (&m)[G], float (&lsum)[G],
-                                              float (&acc0)[G], float (&acc1)[G], int* tblk, uint32_t* tmask) {
+                                              float (&acc0)[G], float (&acc1)[G], int* tblk, uint32_t* tmask,
+                                              uint32_t* rec) {
     const int wave = threadIdx.x >> 6;
     if (L <= 0) return;                    // no blocks (and no row to clamp to)
     for (int tb = r0; tb < r1; tb += kBlkTile) {
@@ -243,6 +247,7 @@ __device__ __forceinline__ void decode_blocks(const AttendParams& p, const Src& 
             src.at(tb + threadIdx.x, blk, mask);
             tblk[threadIdx.x] = blk * 8;
             tmask[threadIdx.x] = mask;
+            if (rec) rec[tb + threadIdx.x] = (uint32_t(blk) << 8) | mask;
         }
         __syncthreads();
         for (int i = wave; i < n; i += 2 * kAttnWaves) {
@@ -414,6 +419,12 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
     const uint16_t* kbase = p.k + int64_t(bj) * p.Lmax * kHeadDim;
     const uint16_t* vbase = p.v + int64_t(bj) * p.Lmax * kHeadDim;
 
+    // inspection record of this pipeline's attended words: host values, the
+    // block list; device values, the kept blocks, then (from kept_words on)
+    // the sink / window blocks
+    uint32_t* rec = p.rec ? p.rec + int64_t(bj) * p.max_blocks : nullptr;
+    const int kept_words = p.last.keep * (p.last.chunk >> 3);
+
     int kept_n = -1;
     FusedOut fused{};
     if (HOSTV) {
@@ -421,7 +432,7 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         const int per = (nb + p.nsplit - 1) / p.nsplit;
         const int r0 = min(nb, sp * per), r1 = min(nb, r0 + per);
         decode_blocks<G, HOSTV>(p, ListSrc{p.blocks + int64_t(bj) * p.max_blocks}, r0, r1, bj, L, kbase, vbase,
-                                qv, m, lsum, acc0, acc1, tblk, tmask);
+                                qv, m, lsum, acc0, acc1, tblk, tmask, rec);
     } else if (sp >= p.nsplit - p.nsplit_a) {
         // sink / window blocks: known without any selection
         const int s_end = min(p.sink, L);
@@ -435,7 +446,7 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         const int spa = sp - (p.nsplit - p.nsplit_a);
         const int r0 = min(nb, spa * per), r1 = min(nb, r0 + per);
         decode_blocks<G, HOSTV>(p, RangeSrc{nr1, wb0, s_end, w0, L}, r0, r1, bj, L, kbase, vbase, qv, m, lsum,
-                                acc0, acc1, tblk, tmask);
+                                acc0, acc1, tblk, tmask, rec ? rec + kept_words : nullptr);
     } else {
         // the kept chunks of the last stage, recomputed from its scores
         // (fused: from the previous stage's scores and every child's
@@ -472,7 +483,7 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         const int per = (nb + nsb - 1) / nsb;
         const int r0 = min(nb, sp * per), r1 = min(nb, r0 + per);
         decode_blocks<G, HOSTV>(p, KeptSrc{kstarts, bpc, s_end, w0, L}, r0, r1, bj, L, kbase, vbase, qv, m, lsum,
-                                acc0, acc1, tblk, tmask);
+                                acc0, acc1, tblk, tmask, rec);
     }
 
     SD_PHASE(3, 3);
@@ -688,6 +699,7 @@ hipError_t launch_attend(sd_ctx* c, bool given, bool fused, const uint16_t* q, c
     p.vpool = c->vc.pool;
     p.blk_slot = c->vc.blk_slot;
     p.vslots = c->vc.slots;
+    p.vcopied = c->vfetch == SD_VALUE_FETCH_COPY;
     p.lengths = lengths;
     p.blocks = c->blocks;
     p.nblocks = c->nblocks;
@@ -723,6 +735,7 @@ hipError_t launch_attend(sd_ctx* c, bool given, bool fused, const uint16_t* q, c
     p.Hkv = c->cfg.num_kv_heads;
     p.scale_log2 = c->scale_log2;
     p.out = out;
+    p.rec = c->rec;
     const dim3 grid(unsigned(pipe_grid(c->nsplit, p.Bh)));
     const bool hostv = c->cfg.values_on_host != 0;
     switch (c->G) {

@@ -96,6 +96,13 @@ struct sd_ctx {
     int32_t* requant;                 // [B][Hkv] set by sd_append_kv when the scale grew
     int32_t* tick;                    // [B*Hkv][kTickInts] last-arriver counters (zero between launches)
     int32_t* flag;                    // device error flag (kFlagBadLength | kFlagPlacement), right after tick
+    uint32_t* rec;                    // caller's attended-word record (sd_record_attended), or null
+    // gathered-copy value fetch (SD_VALUE_FETCH_COPY)
+    int vfetch;                       // SD_VALUE_FETCH_*
+    hipStream_t vside;                // side stream of the copies (default priority)
+    hipEvent_t vside_done;            // recorded after a step's copies
+    int32_t* vstage;                  // pinned host staging: nblocks [BH], lengths [B], blocks and blk_slot [BH][max_blocks]
+    int64_t vcopies;                  // copies (runs) enqueued by the last step
     sd::ValueCache vc;
     const void* vhost_key;            // last host value pointer seen, and its device alias
     const uint16_t* vhost_dev;

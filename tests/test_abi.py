@@ -33,7 +33,7 @@ def test_struct_layout_matches_header():
     assert B.sd_config.stage.offset == 28
     assert B.sd_config.value_cache_tokens.offset == 96
     assert C.sizeof(B.sd_config) == 104
-    assert C.sizeof(B.sd_stats) == 80
+    assert C.sizeof(B.sd_stats) == 88
 
 
 def test_status_strings():

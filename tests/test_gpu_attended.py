@@ -1,0 +1,159 @@
+"""The attended set as the decode kernel walks it, token for token.
+
+sd_record_attended makes the decode kernel's own block loop store every
+8-token block it attends as block << 8 | token mask.  The union of those
+masks must be exactly the oracle's attended set (the last stage's kept
+chunks, the sink and the recent window: "KV Cache 与长上下文推理", section
+"KV Cache 压缩技术"), and no token may be attended twice.  The output
+tolerance cannot see one dropped or doubled token among ~3,000 (it moves
+the output by ~1/|T|), so this is the exact check of the set on both the
+device-value path (kept-chunk and sink/window splits) and the host-value
+path (the value-cache kernel's block list).
+"""
+import numpy as np
+import pytest
+
+from oracle import sparse_decode as O
+from sparse_attention_kv_int8_amd.binding import SDError
+from sparse_attention_kv_int8_amd.inputs import WORKLOADS, Stage, make_inputs, tiny_workload
+from tests.gpu_util import GpuRun, compare_step, oracle_config, oracle_keys
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(params=["unfused", "fused"])
+def fusion(request, monkeypatch):
+    monkeypatch.setenv("SD_FUSE_LAST_STAGE", "1" if request.param == "fused" else "0")
+    return request.param
+
+
+def max_blocks(w) -> int:
+    last = w.stages[-1]
+    return last.keep * last.chunk // 8 + (w.sink + 7) // 8 + (w.window + 7) // 8 + 1
+
+
+def recorded_tokens(words: np.ndarray) -> np.ndarray:
+    """Token positions of the (block << 8 | mask) words, repeats kept."""
+    words = words[words != 0].astype(np.int64)
+    blk, mask = words >> 8, words & 0xFF
+    bits = (mask[:, None] >> np.arange(8)[None, :]) & 1
+    return (blk[:, None] * 8 + np.arange(8)[None, :])[bits == 1]
+
+
+def check_recorded(w, rec: np.ndarray, ref, lengths):
+    for b in range(w.batch):
+        for j in range(w.num_kv_heads):
+            t = recorded_tokens(rec[b, j])
+            u, cnt = np.unique(t, return_counts=True)
+            assert (cnt == 1).all(), f"(b={b}, j={j}): tokens attended twice: {u[cnt > 1][:8].tolist()}"
+            exp = ref.attended[b][j]
+            if not np.array_equal(u, exp):
+                extra = np.setdiff1d(u, exp)[:8].tolist()
+                missing = np.setdiff1d(exp, u)[:8].tolist()
+                raise AssertionError(f"(b={b}, j={j}, L={int(lengths[b])}): {len(u)} tokens vs {len(exp)}; "
+                                     f"extra {extra}, missing {missing}")
+
+
+def record_step(g, w, step):
+    torch = g.torch
+    rec = torch.zeros((w.batch, w.num_kv_heads, max_blocks(w)), dtype=torch.int32, device="cuda")
+    g.dec.sd_record_attended(rec)
+    try:
+        out, kept = step()
+    finally:
+        g.dec.sd_record_attended(None)
+    return out, kept, rec.cpu().numpy().view(np.uint32)
+
+
+def run_recorded(w, lengths=None):
+    print(f"attended case {w.name} B={w.batch} Lmax={w.max_context} "
+          f"stages={[(s.chunk, s.stride, s.keep) for s in w.stages]} sink={w.sink} window={w.window}", flush=True)
+    inp = make_inputs(w, lengths=lengths)
+    g = GpuRun(inp)
+    g.quantize()
+    k8_ref, _ = oracle_keys(inp)
+    q = inp.q_step0
+    out, kept, rec = record_step(g, w, lambda: g.step(q))
+    ref, err, _ = compare_step(inp, q, k8_ref, out, kept)
+    check_recorded(w, rec, ref, inp.lengths)
+    # recording off again: a step stores nothing more
+    g.torch.cuda.synchronize()
+    print(f"  ok: {sum(len(ref.attended[b][j]) for b in range(w.batch) for j in range(w.num_kv_heads))} "
+          f"tokens, max|err|={err:.2e}", flush=True)
+    return g, inp, ref, k8_ref
+
+
+SMALL = {
+    # sink and window overlap kept chunks; ragged lengths
+    "ragged": dict(name="att_ragged", batch=3, num_q_heads=8, num_kv_heads=2, max_context=5000,
+                   stages=(Stage(256, 8, 5), Stage(32, 2, 9), Stage(8, 1, 17)), sink=13, window=100, planted=4),
+    # no sink, no window: only kept chunks
+    "kept_only": dict(name="att_kept_only", batch=1, num_q_heads=2, num_kv_heads=2, max_context=3000,
+                      stages=(Stage(128, 4, 6), Stage(16, 2, 10), Stage(8, 1, 12)), sink=0, window=0, planted=4),
+    # chunks of 16 tokens (two blocks each), unaligned sink and window
+    "two_block_chunks": dict(name="att_16", batch=2, num_q_heads=4, num_kv_heads=2, max_context=4096,
+                             stages=(Stage(64, 8, 10), Stage(16, 4, 12)), sink=5, window=61, planted=4),
+    # a budget larger than short contexts: sink + window cover everything
+    "covering": dict(name="att_cover", batch=2, num_q_heads=4, num_kv_heads=1, max_context=2000,
+                     stages=(Stage(64, 8, 40), Stage(8, 1, 64)), sink=64, window=1024, planted=2),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_attended_small(name, fusion):
+    run_recorded(tiny_workload(**SMALL[name]))
+
+
+def test_attended_short_and_odd_lengths(fusion):
+    """Lengths 1, 7, 9, 65 and 1,031: a window or sink that ends inside a
+    block, a context shorter than one chunk."""
+    w = tiny_workload(name="att_short", batch=5, num_q_heads=4, num_kv_heads=1, max_context=2048,
+                      stages=(Stage(64, 8, 6), Stage(8, 1, 20)), sink=5, window=37, planted=0)
+    run_recorded(w, lengths=np.array([1, 7, 9, 65, 1031]))
+
+
+def test_attended_tiny16k(fusion):
+    run_recorded(WORKLOADS["tiny16k"])
+
+
+@pytest.mark.parametrize("name", ["llama8b_128k", "ragged_b16", "ctx_1m"])
+def test_attended_full_size(name):
+    run_recorded(WORKLOADS[name])
+
+
+def test_attended_with_reused_stages(fusion):
+    """Every stage reused (the decode kernel reads the last kept set from
+    kept_idx) and one stage reused (the last stages run again)."""
+    w = WORKLOADS["llama8b_128k"].replace(name="att_reuse", max_context=32768, planted=16, steps=2)
+    g, inp, ref0, k8_ref = run_recorded(w)
+    cfg = oracle_config(w)
+    for r in (len(w.stages), 1):
+        q = inp.q[1]
+        out, kept, rec = record_step(g, w, lambda: g.step_reuse(q, r, kept_prev=ref0.kept_idx))
+        ref = O.decode_step(q, inp.k, k8_ref, inp.v, inp.lengths, cfg, reuse=r, kept_prev=ref0.kept_idx)
+        compare_step(inp, q, k8_ref, out, kept, ref=ref)
+        check_recorded(w, rec, ref, inp.lengths)
+        print(f"  reuse {r}: ok", flush=True)
+
+
+def test_attended_host_values():
+    """Host values: the words are the value-cache kernel's block list."""
+    w = WORKLOADS["ctx_3m_hostv"].replace(name="att_hostv", max_context=65536, value_cache_tokens=16384,
+                                          planted=16, steps=2)
+    g, inp, ref, k8_ref = run_recorded(w)
+    cfg = oracle_config(w)
+    q = inp.q[1]
+    out, kept, rec = record_step(g, w, lambda: g.step(q))
+    ref = O.decode_step(q, inp.k, k8_ref, inp.v, inp.lengths, cfg)
+    compare_step(inp, q, k8_ref, out, kept, ref=ref)
+    check_recorded(w, rec, ref, inp.lengths)
+
+
+def test_record_argument_errors():
+    w = tiny_workload(name="att_args", max_context=4096)
+    inp = make_inputs(w)
+    g = GpuRun(inp)
+    small = g.torch.zeros(max_blocks(w) * w.batch * w.num_kv_heads - 1, dtype=g.torch.int32, device="cuda")
+    with pytest.raises(SDError):
+        g.dec.sd_record_attended(small)
+    g.dec.sd_record_attended(None)

@@ -182,3 +182,62 @@ def test_hostv_growing_lengths_refill_partial_blocks():
     st = g.dec.sd_get_stats()
     assert st.refills > 0
     assert st.h2d_bytes == (st.misses + st.refills) * 8 * 128 * 2
+
+
+def test_hostv_side_stream_copies_match_mapped_reads():
+    """SD_VALUE_FETCH_COPY (missed blocks gathered into their slots by
+    hipMemcpyAsync on a side stream, the decode kernel reading only the
+    slot pool) against the default mapped reads, over the same drifting
+    sequence with growing lengths (so refills happen too): outputs and kept
+    sets bit-identical at every step, the same hits, misses and refills, at
+    least one copy per step with misses, and outputs within the oracle bar."""
+    from sparse_attention_kv_int8_amd.binding import SD_VALUE_FETCH_COPY, SD_VALUE_FETCH_MAPPED
+    w = WORKLOADS["ctx_3m_hostv"].replace(name="hostv_copy", max_context=65536, value_cache_tokens=4096,
+                                          planted=32, steps=10)
+    L_last = 65533
+    lengths = [L_last - 2 * (w.steps - 1 - t) for t in range(w.steps)]
+    print(f"host-value copy vs mapped, lengths {lengths}", flush=True)
+    inp = make_inputs(w, lengths=[L_last])
+    runs = {}
+    for mode in (SD_VALUE_FETCH_MAPPED, SD_VALUE_FETCH_COPY):
+        g = GpuRun(inp)
+        g.quantize()
+        g.dec.sd_set_value_fetch(mode)
+        seq = []
+        for t, L in enumerate(lengths):
+            g.set_lengths([L])
+            out, kept = g.step(inp.q[t])
+            st = g.dec.sd_get_stats()
+            seq.append((out, kept, st.last_hits, st.last_misses, st.last_refills, st.last_copies))
+        runs[mode] = seq
+        g.dec.close()
+    k8_ref, _ = oracle_keys(inp)
+    cfg = oracle_config(w)
+    evictions = 0
+    for t, L in enumerate(lengths):
+        a, b = runs[SD_VALUE_FETCH_MAPPED][t], runs[SD_VALUE_FETCH_COPY][t]
+        assert np.array_equal(a[0], b[0]), f"step {t}: outputs differ"
+        assert np.array_equal(a[1], b[1]), f"step {t}: kept sets differ"
+        assert a[2:5] == b[2:5], f"step {t}: cache statistics differ {a[2:5]} vs {b[2:5]}"
+        assert a[5] == 0
+        if b[3] + b[4] > 0:
+            assert 1 <= b[5] <= b[3] + b[4], f"step {t}: {b[5]} copies for {b[3] + b[4]} blocks"
+        evictions += b[3]
+        print(f"  step {t} L={L}: hits {b[2]} misses {b[3]} refills {b[4]} copies {b[5]}", flush=True)
+        if t in (0, w.steps - 1):
+            ref = O.decode_step(inp.q[t], inp.k, k8_ref, inp.v, [L], cfg)
+            compare_step(inp, inp.q[t], k8_ref, b[0], b[1], ref=ref)
+    assert evictions > w.value_cache_tokens // 8 * w.num_kv_heads, "the sequence should outgrow the cache"
+
+
+def test_value_fetch_argument_errors():
+    from sparse_attention_kv_int8_amd.binding import SD_ERR_INVALID_ARG, SD_ERR_UNSUPPORTED, SDError
+    w = WORKLOADS["ctx_3m_hostv"].replace(name="hostv_args", max_context=16384, value_cache_tokens=8192, steps=1)
+    g = GpuRun(make_inputs(w))
+    with pytest.raises(SDError) as e:
+        g.dec.sd_set_value_fetch(7)
+    assert e.value.status == SD_ERR_INVALID_ARG
+    dev = GpuRun(make_inputs(WORKLOADS["tiny16k"]))
+    with pytest.raises(SDError) as e:
+        dev.dec.sd_set_value_fetch(1)
+    assert e.value.status == SD_ERR_UNSUPPORTED
