@@ -22,8 +22,9 @@ roofline = the dominant kernel's algorithmic bytes per launch / its average
          bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE counters
          (scaled by a plain copy of known size; see profiles/), or null when
          no record exists or the kernel sources changed since it was taken.
-cpu_baseline = the CPU oracle (numpy, one core) on full steps of the same
-         workload, repeated for about 10 s of CPU work (median step).
+cpu_baseline = the CPU oracle (numpy, one of the process's cores) on full
+         steps of the same workload, repeated for about 10 s of CPU work
+         (median step), with the CPU model.
 us_per_step_spread = p10 / p50 / p90 of single replayed steps, each
          between HIP events (outside the timed region).
 stream_ceiling = a plain streaming copy (torch.neg, 1 GiB read + 1 GiB
@@ -42,6 +43,16 @@ append = KV append (sd_append_kv) of one token per call on the same
 batched = the 16-request ragged workload (up to 128K tokens each), timed
          like the main figure: what the same kernels reach with many
          requests in flight (context; `value` stays the B = 1 figure).
+per_kernel_frac = each step kernel's algorithmic bytes (a stage scored
+         inside the kernel of the stage before it counts with that kernel) /
+         its average duration, against 8 TB/s, and the pruning and decode
+         kernels together; `target` compares the latter at 128K and 1M with
+         60% of 8 TB/s.
+hostv  = the 3M-token host-resident-value workload (32 steps, drifting
+         query, cold cache): graph-replayed us per step with and without
+         the cold first step, hit rate, the PCIe rate (missed bytes / the
+         time of the decode kernel that reads them), and the same sequence
+         with the gathered hipMemcpyAsync side-stream fetch for comparison.
 reuse  = steps that reuse the first r pruning stages' kept sets from an
          earlier step (sd_decode_step_reuse): us per step for each r, and,
          over a drifting query sequence, how much of the fully recomputed
@@ -116,6 +127,28 @@ def algorithmic_bytes(w, kept: np.ndarray, lengths: np.ndarray) -> dict:
     per["stage0"] += qbytes
     per["attend"] += 2 * qbytes            # query in, output out
     return dict(per_kernel=per, total=sum(per.values()), int8_rows=rows_total, attended_tokens=tokens_total)
+
+
+def kernel_bytes(per: dict, avg_us: dict) -> dict:
+    """Algorithmic bytes per kernel that ran: a stage scored inside the
+    kernel of the stage before it (the fused plan launches no kernel of its
+    own for it) counts with that kernel."""
+    out = dict(per)
+    n = sum(1 for k in per if k.startswith("stage"))
+    for s in range(n - 1, 0, -1):
+        if f"stage{s}" not in avg_us and f"stage{s - 1}" in avg_us:
+            out[f"stage{s - 1}"] += out.pop(f"stage{s}")
+    return out
+
+
+def kernel_fracs(kb: dict, avg_us: dict) -> dict:
+    """Each step kernel's algorithmic bytes / its average duration, as a
+    fraction of 8 TB/s; and the pruning + decode kernels together."""
+    fr = {k: round(kb[k] / (avg_us[k] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) for k in kb if k in avg_us}
+    ks = [k for k in kb if k in avg_us]
+    fr["prune_and_decode"] = round(sum(kb[k] for k in ks) / (sum(avg_us[k] for k in ks) * 1e-6) / 1e9 /
+                                   HBM_PEAK_GBS, 4)
+    return fr
 
 
 # ---------------------------------------------------------------- GPU -----
@@ -501,6 +534,26 @@ def stream_ceiling(mib: int = 1024) -> dict:
             "bytes": 2 * mib * (1 << 20)}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        r = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10)
+        for ln in r.stdout.splitlines():
+            if ln.startswith("Model name:"):
+                return ln.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def oracle_baseline(w, inp, kept_gpu_bytes: float, budget_s: float = 10.0) -> dict:
     """The CPU oracle on full steps of the same inputs (one core): the key
     quantisation once, then the step repeated for about `budget_s` seconds
@@ -530,7 +583,13 @@ def oracle_baseline(w, inp, kept_gpu_bytes: float, budget_s: float = 10.0) -> di
             O.decode_step(inp.q_step0, inp.k, k8, inp.v, inp.lengths, cfg)
             times.append(time.perf_counter() - t)
     ts = statistics.median(times)
-    return {"value": round(kept_gpu_bytes / ts / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):      # pragma: no cover
+        avail = os.cpu_count() or 1
+    return {"value": round(kept_gpu_bytes / ts / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "cores_note": f"1 of {avail} cores available to the process (BLAS and numpy threads pinned to 1)",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"full decode steps of {w.name}, repeated for {sum(times) + tq:.1f} s of CPU work "
                       f"({len(times)} steps, median {ts * 1e3:.1f} ms/step) after the key quantisation "
                       f"({tq:.2f} s, once)",
@@ -580,6 +639,7 @@ def measure(w, steps: int, warmup: int, copies: int, reuse: bool = True, dense: 
     dom_us = live[dominant][0] * 1e3 / live[dominant][1]
     kept = b.kept.cpu().numpy()
     ab = algorithmic_bytes(w, kept, b.inp.lengths)
+    ab["per_launch"] = kernel_bytes(ab["per_kernel"], avg_us)
     reuse = reuse_study(b, steps) if reuse and w.steps == 1 else None
     dense = dense_study(b, steps, warmup, us_per_step) if dense else None
     sketch = sketch_study(b, steps, warmup, us_per_step) if sketch else None
@@ -587,14 +647,24 @@ def measure(w, steps: int, warmup: int, copies: int, reuse: bool = True, dense: 
                    bytes=ab, reuse=reuse, spread=spread, dense=dense, sketch=sketch)
 
 
-def measure_hostv(w, repeats: int = 3) -> dict:
+def measure_hostv(w, repeats: int = 3, sketch: bool = True) -> dict:
     """The host-resident-value workload: values in pinned host memory behind
     the device LRU of 8-token blocks, over the workload's sequence of steps
-    with a drifting query, from a cold cache, `repeats` times.  Each step is
-    timed with HIP events on the launch stream (eager launches: the cache's
-    step index is passed per call); the cache statistics are read after each
-    step, outside its timed region.  The sequence is then run again with
-    the first stage scored from the int4 sketch (`sketch4`)."""
+    with a drifting query, each run from a cold cache.
+
+    graph: one step captured in a HIP graph and replayed over the sequence
+      (the step's query copied into the captured buffer before each replay,
+      outside its timed span; the LRU's clock lives on the device), each
+      replay timed with HIP events: the headline figures.
+    eager: the same sequence launched eagerly, with the decode kernel (the
+      one that reads the missed blocks from host memory) timed by HIP events
+      on its launch stream: the PCIe rate is the missed bytes / that
+      kernel's time, i.e. over the time in which the host reads happen.
+    copy: the same sequence with SD_VALUE_FETCH_COPY (missed blocks gathered
+      by hipMemcpyAsync on a side stream after a host wait; eager: it cannot
+      be captured), for comparison.
+    sketch4: the eager sequence with the first stage scored from the int4
+      sketch."""
     import torch
     from sparse_attention_kv_int8_amd import binding as B
     t = time.perf_counter()
@@ -611,53 +681,109 @@ def measure_hostv(w, repeats: int = 3) -> dict:
     dec.sd_quantize_keys(k, lengths, k8)
     quantize_us = dec.sd_profile_stop()["quantize"][0] * 1e3
     qs = [to_dev(inp.q[t]) for t in range(w.steps)]
+    qbuf = qs[0].clone()
     out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
     kept = torch.empty((w.batch, w.num_kv_heads, w.keep_total), dtype=torch.int32, device="cuda")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(w.steps)]
 
-    def sequence(step_fn, label):
-        runs = []
-        for rep in range(repeats):
+    def sequence(step_fn, label, before=None, reps=repeats, prof_mask=0):
+        runs, prof = [], {}
+        for rep in range(reps):
             dec.sd_reset_value_cache()
             torch.cuda.synchronize()
+            if prof_mask:
+                dec.sd_profile_start(prof_mask, 8 * w.steps + 8)
             steps = []
             for t in range(w.steps):
+                if before:
+                    before(t)
                 a, b = ev[t]
                 a.record()
                 step_fn(t)
                 b.record()
                 torch.cuda.synchronize()
                 st = dec.sd_get_stats()
-                steps.append((a.elapsed_time(b) * 1e3, st.last_needed, st.last_hits, st.last_misses))
+                steps.append((a.elapsed_time(b) * 1e3, st.last_needed, st.last_hits, st.last_misses,
+                              st.last_refills, st.last_copies))
+            if prof_mask:
+                for kname, (ms, n) in dec.sd_profile_stop().items():
+                    pm, pn = prof.get(kname, (0.0, 0))
+                    prof[kname] = (pm + ms, pn + n)
             runs.append(steps)
             log(f"[bench] host-value run {rep} ({label}): {sum(x[0] for x in steps) / len(steps):.1f} us/step")
-        return runs
+        return runs, prof
 
-    runs = sequence(lambda t: dec.sd_decode_step(qs[t], k, k8, v, lengths, out, kept), "int8")
+    def summary(runs):
+        flat = [x for r in runs for x in r]
+        needed = sum(x[1] for x in flat)
+        return {"us_per_step": round(statistics.fmean(x[0] for x in flat), 3),
+                "us_first_step": round(statistics.fmean(r[0][0] for r in runs), 3),
+                "us_per_step_after_first": round(statistics.fmean(x[0] for r in runs for x in r[1:]), 3),
+                "hit_rate": round(sum(x[2] for x in flat) / max(1, needed), 4)}
+
+    step = lambda t: dec.sd_decode_step(qs[t], k, k8, v, lengths, out, kept)
+    # eager, with the decode kernel timed: the PCIe rate
+    eruns, eprof = sequence(step, "eager", prof_mask=1 << B.SD_PROF_ATTEND)
     kept_np = kept.cpu().numpy()
-    # the same sequence with the first stage scored from the int4 sketch
-    sk = torch.empty((w.batch, w.num_kv_heads, dec.sd_sketch4_rows(), 64), dtype=torch.uint8, device="cuda")
-    dec.sd_quantize_sketch4(k, lengths, sk)
-    runs4 = sequence(lambda t: dec.sd_decode_step_sketch4(qs[t], k, k8, sk, v, lengths, out, kept), "sketch4")
-    all4 = [x for r in runs4 for x in r]
-    sketch4 = {"us_per_step": round(statistics.fmean(x[0] for x in all4), 3),
-               "us_per_step_after_first": round(statistics.fmean(x[0] for r in runs4 for x in r[1:]), 3),
-               "hit_rate": round(sum(x[2] for x in all4) / max(1, sum(x[1] for x in all4)), 4),
-               "note": "first stage scored from the int4 sketch; same sequence, cold cache, same runs"}
-    allsteps = [x for r in runs for x in r]
-    us = [x[0] for x in allsteps]
-    warm = [x[0] for r in runs for x in r[1:]]
-    needed = sum(x[1] for x in allsteps)
-    hits = sum(x[2] for x in allsteps)
-    misses = sum(x[3] for x in allsteps)
-    h2d = misses * 8 * w.head_dim * 2
+    eflat = [x for r in eruns for x in r]
+    missed = sum(x[3] + x[4] for x in eflat) * 8 * w.head_dim * 2      # misses and refills, bytes
+    attend_ms = eprof["attend"][0]
+    # graph replay: the headline
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dec.sd_decode_step(qbuf, k, k8, v, lengths, out, kept)
+    granal = sequence(lambda t: graph.replay(), "graph", before=lambda t: qbuf.copy_(qs[t]))[0]
+    del graph
+    # hit/miss sequences must agree between the eager and the replayed runs
+    same = [(x[1], x[2], x[3]) for x in eruns[0]] == [(x[1], x[2], x[3]) for x in granal[0]]
+    # the gathered-copy variant (eager)
+    dec.sd_set_value_fetch(B.SD_VALUE_FETCH_COPY)
+    cruns = sequence(step, "side-stream copies", reps=1)[0]
+    dec.sd_set_value_fetch(B.SD_VALUE_FETCH_MAPPED)
+    copy = summary(cruns)
+    copy["copies_per_step"] = round(statistics.fmean(x[5] for x in cruns[0]), 1)
+    copy["note"] = ("SD_VALUE_FETCH_COPY: host waits for the block list, one hipMemcpyAsync per run of missed "
+                    "blocks on a side stream, decode kernel after them; eager launches")
+    sketch4 = None
+    if sketch:
+        sk = torch.empty((w.batch, w.num_kv_heads, dec.sd_sketch4_rows(), 64), dtype=torch.uint8, device="cuda")
+        dec.sd_quantize_sketch4(k, lengths, sk)
+        runs4 = sequence(lambda t: dec.sd_decode_step_sketch4(qs[t], k, k8, sk, v, lengths, out, kept), "sketch4",
+                         reps=1)[0]
+        sketch4 = summary(runs4)
+        sketch4["note"] = "first stage scored from the int4 sketch; same sequence, cold cache, eager"
+        del sk
+    g = summary(granal)
+    e = summary(eruns)
     ab = algorithmic_bytes(w, kept_np, inp.lengths)
-    return dict(us_per_step=statistics.fmean(us), us_first_step=statistics.fmean(r[0][0] for r in runs),
-                us_per_step_after_first=statistics.fmean(warm), hit_rate=hits / max(1, needed),
-                h2d_bytes_per_step=h2d / len(allsteps), pcie_GBs=h2d / (sum(us) * 1e-6) / 1e9,
-                quantize_us=quantize_us, bytes=ab, repeats=repeats,
-                per_step_us=[round(x[0], 2) for x in runs[-1]],
-                per_step_hit_rate=[round(x[2] / max(1, x[1]), 4) for x in runs[-1]], sketch4=sketch4)
+    res = dict(graph=g, eager=e, copy=copy, sketch4=sketch4, replay_matches_eager=same,
+               h2d_bytes_per_step=round(missed / len(eflat)),
+               pcie_GBs=round(missed / (attend_ms * 1e-3) / 1e9, 2),
+               attend_us_per_step=round(attend_ms * 1e3 / len(eflat), 3),
+               quantize_us=quantize_us, bytes=ab, repeats=repeats,
+               per_step_us=[round(x[0], 2) for x in granal[-1]],
+               per_step_hit_rate=[round(x[2] / max(1, x[1]), 4) for x in granal[-1]])
+    del k, v, k8, qs, dec
+    torch.cuda.empty_cache()
+    return res
+
+
+def hostv_summary(w, r) -> dict:
+    """The host-value figures as reported inside the line."""
+    return {"workload": w.name, "context": w.max_context, "value_cache_tokens": w.value_cache_tokens,
+            "sequence": f"{w.steps} steps, drifting query, cold cache, {r['repeats']} runs",
+            "us_per_step": r["graph"]["us_per_step"], "us_first_step": r["graph"]["us_first_step"],
+            "us_per_step_after_first": r["graph"]["us_per_step_after_first"],
+            "launch": "HIP graph replay (one captured step; query copied in before each replay)",
+            "hit_rate": r["graph"]["hit_rate"], "replay_matches_eager": r["replay_matches_eager"],
+            "eager_us_per_step": r["eager"]["us_per_step"],
+            "h2d_bytes_per_step": r["h2d_bytes_per_step"], "pcie_GBs": r["pcie_GBs"],
+            "pcie_note": "bytes of missed and refilled blocks read from pinned host memory / the time of the "
+                         "decode kernel that reads them (eager run, HIP events on its launch stream)",
+            "attend_us_per_step": r["attend_us_per_step"],
+            "value_GBs": round(r["bytes"]["total"] / (r["graph"]["us_per_step"] * 1e-6) / 1e9, 2),
+            "side_stream_copy": r["copy"], "sketch4": r["sketch4"]}
 
 
 def main() -> int:
@@ -677,6 +803,8 @@ def main() -> int:
     ap.add_argument("--batched", default="ragged_b16", help="batched workload reported inside the line for "
                     "context ('' = none): the same kernels with many requests in flight")
     ap.add_argument("--secondary", default="ctx_1m", help="second workload reported inside the line ('' = none)")
+    ap.add_argument("--hostv", default="ctx_3m_hostv", help="host-resident-value workload reported inside the "
+                    "line ('' = none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain elementwise copy (torch.neg) of MIB MiB three times: the "
                          "reference that scales hardware byte counters")
@@ -690,29 +818,23 @@ def main() -> int:
     if w.values_on_host:
         r = measure_hostv(w)
         total = r["bytes"]["total"]
+        h = hostv_summary(w, r)
+        us = h["us_per_step"]
         print(json.dumps({
             "metric": METRIC + " [host-resident values]",
-            "value": round(total / (r["us_per_step"] * 1e-6) / 1e9, 2),
+            "value": round(total / (us * 1e-6) / 1e9, 2),
             "unit": "GB/s", "n_gpus": 1, "steps": w.steps * r["repeats"], "warmup": 0,
-            "ms_per_step": round(r["us_per_step"] / 1e3, 6), "higher_is_better": True, "scaling": "weak",
+            "ms_per_step": round(us / 1e3, 6), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "int8+fp32", "data": "synthetic (seeded; shapes and distributions of the workload)",
             "config": {"workload": w.name, "batch": w.batch, "context": w.max_context,
                        "gqa": f"{w.num_q_heads}/{w.num_kv_heads}", "stages": [[s.chunk, s.stride, s.keep] for s in w.stages],
                        "sink": w.sink, "window": w.window, "value_cache_tokens": w.value_cache_tokens,
-                       "sequence": f"{w.steps} steps, drifting query, cold cache, {r['repeats']} runs",
-                       "launch": "eager, one step per call"},
-            "us_per_step": round(r["us_per_step"], 3),
-            "us_first_step": round(r["us_first_step"], 3),
-            "us_per_step_after_first": round(r["us_per_step_after_first"], 3),
-            "tokens_per_s": round(w.batch / (r["us_per_step"] * 1e-6), 1),
-            "hit_rate": round(r["hit_rate"], 4),
-            "h2d_bytes_per_step": round(r["h2d_bytes_per_step"]),
-            "pcie_GBs": round(r["pcie_GBs"], 2),
-            "pcie_note": "bytes read from pinned host memory by the decode kernel / total step time",
+                       "sequence": h["sequence"], "launch": h["launch"]},
+            "tokens_per_s": round(w.batch / (us * 1e-6), 1),
             "algorithmic_bytes": total,
             "quantize_keys_us": round(r["quantize_us"], 2),
+            "hostv": h,
             "per_step_us": r["per_step_us"], "per_step_hit_rate": r["per_step_hit_rate"],
-            "sketch4": r["sketch4"],
         }), flush=True)
         return 0
 
@@ -736,7 +858,7 @@ def main() -> int:
     b, r = measure(w, args.steps, args.warmup, auto_copies(w), not args.no_reuse, not args.no_dense,
                    not args.no_sketch)
     total = r["bytes"]["total"]
-    dom_bytes = r["bytes"]["per_kernel"][r["dominant"]]
+    dom_bytes = r["bytes"]["per_launch"][r["dominant"]]
     achieved = dom_bytes / (r["dominant_us"] * 1e-6) / 1e9
     sum_kernel_us = sum(v for k, v in r["avg_us"].items() if k != "quantize")
     from sparse_attention_kv_int8_amd.profiling import load_traffic
@@ -767,6 +889,7 @@ def main() -> int:
                      "traffic": tr["traffic_bytes"] if tr else None, "bytes_per_launch": dom_bytes,
                      "avg_launch_us": round(r["dominant_us"], 3)},
         "step_kernels_us": {k: round(v, 3) for k, v in r["avg_us"].items()},
+        "per_kernel_frac": kernel_fracs(r["bytes"]["per_launch"], r["avg_us"]),
         "step_roofline": {"achieved": round(total / (sum_kernel_us * 1e-6) / 1e9, 2), "unit": "GB/s",
                           "frac": round(total / (sum_kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                           "note": "all per-step bytes / sum of per-step kernel durations"},
@@ -790,8 +913,9 @@ def main() -> int:
                              "value_GBs": round(t2 / (r2["us_per_step"] * 1e-6) / 1e9, 2),
                              "algorithmic_bytes": t2, "step_kernels_us": {k: round(v, 3) for k, v in r2["avg_us"].items()},
                              "dominant": r2["dominant"],
-                             "dominant_frac": round(r2["bytes"]["per_kernel"][r2["dominant"]] /
+                             "dominant_frac": round(r2["bytes"]["per_launch"][r2["dominant"]] /
                                                     (r2["dominant_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                             "per_kernel_frac": kernel_fracs(r2["bytes"]["per_launch"], r2["avg_us"]),
                              "quantize_keys_us": round(b2.quantize_us, 2), "reuse": r2["reuse"],
                              "dense": r2["dense"], "sketch4": r2["sketch"]}
         del b2
@@ -806,11 +930,23 @@ def main() -> int:
                            "algorithmic_bytes": t3, "tokens_per_s": round(w3.batch / (r3["us_per_step"] * 1e-6), 1),
                            "step_kernels_us": {k: round(v, 3) for k, v in r3["avg_us"].items()},
                            "dominant": r3["dominant"],
-                           "dominant_frac": round(r3["bytes"]["per_kernel"][r3["dominant"]] /
+                           "dominant_frac": round(r3["bytes"]["per_launch"][r3["dominant"]] /
                                                   (r3["dominant_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                           "per_kernel_frac": kernel_fracs(r3["bytes"]["per_launch"], r3["avg_us"]),
                            "note": "context: the same kernels with 16 requests of ragged lengths in flight"}
         del b3
         b_torch.cuda.empty_cache()
+    # the pruning and decode kernels against 60% of 8 TB/s, at 128K (this
+    # line) and 1M (the secondary workload) context
+    if w.name == "llama8b_128k" and "secondary" in line and line["secondary"]["workload"] == "ctx_1m":
+        f128 = line["per_kernel_frac"]["prune_and_decode"]
+        f1m = line["secondary"]["per_kernel_frac"]["prune_and_decode"]
+        line["target"] = {"bound": 0.6, "frac_128k": f128, "frac_1m": f1m, "met": f128 >= 0.6 and f1m >= 0.6,
+                          "note": "algorithmic bytes of the pruning and decode kernels / the sum of their "
+                                  "average durations, as a fraction of 8 TB/s"}
+    if args.hostv and args.hostv != w.name:
+        w4 = WORKLOADS[args.hostv]
+        line["hostv"] = hostv_summary(w4, measure_hostv(w4, repeats=2, sketch=not args.no_sketch))
     if not args.copy_calibration:            # its copies would mix with the calibration copies
         line["stream_ceiling"] = stream_ceiling()
     if not args.no_cpu_baseline:
