@@ -286,7 +286,7 @@ __device__ __forceinline__ void score_later(const PruneParams& p, int bj, int wg
         int* sel = reinterpret_cast<int*>(dyn + p.prev.ncand);
         const int32_t* pp = p.stage >= 2 ? kept_bj + p.pp_koff : nullptr;
         const int nk = kept_of_stage<kPruneThreads, SEL>(p.prev, p.stage == 1, p.prev_scores + int64_t(bj) * p.prev.ncand,
-                                                         pp, L, dyn, tmp);
+                                                         pp, L, dyn, tmp, p.stage);
         for (int i = nk + threadIdx.x; i < p.prev.keep; i += kPruneThreads) sel[i] = -1;
         if (threadIdx.x < kHeadDim) Qlds[threadIdx.x] = qval;
         __syncthreads();

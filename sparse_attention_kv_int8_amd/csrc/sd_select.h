@@ -410,14 +410,17 @@ __host__ __device__ inline int kept_lds_words(const StageDev& st, bool first_sta
 // after the select.  lds: kept_lds_words(st, first_stage) words.
 template <int NT, int E>
 __device__ int kept_of_stage(const StageDev& st, bool first_stage, const int32_t* scores_bj,
-                             const int32_t* parents, int64_t L, uint32_t* lds, unsigned* tmp) {
+                             const int32_t* parents, int64_t L, uint32_t* lds, unsigned* tmp, int pslot = -1) {
+    (void)pslot;                 // phase-stamp slot (latency studies only)
     uint32_t* keys = lds;
     int* sel = reinterpret_cast<int*>(lds + st.ncand);
     int* cand = sel + st.keep + 1;
     int* par = cand + select_cand_words(st.ncand, st.keep);
     const KeyStats ks = load_keys<NT>(scores_bj, st.ncand, keys, reinterpret_cast<uint32_t*>(cand), tmp, parents,
                                       first_stage ? 0 : st.ncand / st.ratio, par);
+    if (pslot >= 0) SD_PHASE(pslot, 6);
     const int nk = select_top<NT, E>(keys, st.ncand, st.keep, sel, cand, tmp, ks);
+    if (pslot >= 0) SD_PHASE(pslot, 7);
     for (int i = threadIdx.x; i < nk; i += NT) sel[i] = int(cand_start(st, first_stage, par, sel[i], L));
     __syncthreads();
     return nk;
@@ -481,10 +484,13 @@ __device__ FusedOut kept_two_stages(const StageDev& P, bool p_first, const int32
         for (int u = 0; u < kLoadBatch; ++u)
             if (i0 + u * NT < npre) preL[i0 + u * NT] = v[u];
     }
+    SD_PHASE(3, 8);
     const int np = select_top<NT, EP>(keysP, P.ncand, P.keep, selP, candP, tmp, ksP);
+    SD_PHASE(3, 9);
     // P starts; Q candidate i is child i % rq of kept P chunk i / rq
     for (int i = threadIdx.x; i < P.keep; i += NT)
         startsP[i] = i < np ? int(cand_start(P, p_first, parP, selP[i], L)) : -1;
+    SD_PHASE(3, 12);
     if (threadIdx.x < 256) candQ[threadIdx.x] = 0;
     unsigned nv = 0, kmin = 0xffffffffu, kmax = 0;
     for (int i = threadIdx.x; i < Q.ncand; i += NT) {
@@ -495,8 +501,11 @@ __device__ FusedOut kept_two_stages(const StageDev& P, bool p_first, const int32
         kmin = min(kmin, k ? k : 0xffffffffu);
         kmax = max(kmax, k);
     }
+    SD_PHASE(3, 13);
     const KeyStats ksQ = block_key_stats<NT>(nv, kmin, kmax, tmp);
+    SD_PHASE(3, 10);
     const int nq = select_top<NT, EQ>(keysQ, Q.ncand, Q.keep, selQ, candQ, tmp, ksQ);
+    SD_PHASE(3, 11);
     for (int i = threadIdx.x; i < nq; i += NT) {
         const int c = selQ[i], q = c / rq;
         selQ[i] = startsP[q] + (c - q * rq) * Q.chunk;
