@@ -291,7 +291,11 @@ sd_status sd_quantize_sketch4(sd_ctx* ctx, const uint16_t* k_bf16, const int32_t
  * and the attention are those of sd_decode_step.  Arguments as in
  * sd_decode_step, plus k_sketch4 from sd_quantize_sketch4.  Needs the first
  * stage to run unfused: SD_ERR_UNSUPPORTED for a 2-stage configuration
- * whose last stage is fused into the first (see sd_create). */
+ * whose last stage the context fuses into the first (sd_create fuses the
+ * last stage into the one before it, where the geometry allows, when the
+ * extra key rows that costs over all (request, KV head) pairs stay within
+ * 8 MiB; the environment variable SD_FUSE_LAST_STAGE=0 turns fusion off,
+ * =1 fuses wherever the geometry allows). */
 sd_status sd_decode_step_sketch4(sd_ctx* ctx, const uint16_t* q, const uint16_t* k_bf16,
                                  const int8_t* k_int8, const uint8_t* k_sketch4, const uint16_t* v,
                                  const int32_t* lengths, uint16_t* out, int32_t* kept_idx,

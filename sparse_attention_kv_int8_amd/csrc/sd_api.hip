@@ -114,26 +114,37 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
         na = na < 1 ? 1 : na > c->nsplit - 1 ? c->nsplit - 1 : na;
         c->nsplit_a = na;
     }
-    // Fuse the last stage Q into the kernel of the stage P before it (unless
-    // the environment sets SD_FUSE_LAST_STAGE=0).  Possible when Q's chunks
-    // are exactly 8 sampled rows (one load slot), Q's stride divides P's (so
-    // P's samples are among the rows read), P reads at most 4x its own
-    // samples, all children's scores fit in LDS, and Q's select keeps its
-    // keys in registers (at most 512 candidates); not with host values
-    // (their value-cache kernel selects the last stage by itself).  It
-    // trades one kernel boundary and one scoring pass for a second select
-    // in the decode kernel and more rows read by P: about 1.5 us less per
-    // step at 128K and at 1M.
+    // Fuse the last stage Q into the kernel of the stage P before it.
+    // Possible when Q's chunks are exactly 8 sampled rows (one load slot),
+    // Q's stride divides P's (so P's samples are among the rows read), P
+    // reads at most 4x its own samples, all children's scores fit in LDS,
+    // and Q's select keeps its keys in registers (at most 512 candidates);
+    // not with host values (their value-cache kernel selects the last stage
+    // by itself).  It trades one kernel boundary and one scoring pass for a
+    // second select in the decode kernel and more rows read by P: P reads
+    // every row at Q's stride of each of its candidates instead of its own
+    // samples, while an unfused Q kernel reads Q.ncand x 8 rows.  Fused when
+    // those extra bytes over all (request, KV head) pipelines stay within
+    // kFuseExtraBytes, about 1.6 us of streaming: then the saved boundary
+    // and scoring pass (about 2 us, measured) win; with many requests in
+    // flight the step is bandwidth-bound and the extra rows cost more (16
+    // requests of up to 128K: 139 us unfused against 148 us fused; 1 request:
+    // 36.5 against 38.5 us at 128K, 55.7 against 58.1 us at 1M).
+    // SD_FUSE_LAST_STAGE=0 never fuses, =1 fuses whenever possible.
+    constexpr int64_t kFuseExtraBytes = int64_t(8) << 20;
     c->fuse = 0;
     c->fuse_rq = 0;
     c->fuse_m = 0;
     const char* fenv = std::getenv("SD_FUSE_LAST_STAGE");
-    const bool want_fuse = !(fenv && fenv[0] == '0');
-    if (want_fuse && cfg.num_stages >= 2 && !cfg.values_on_host) {
+    const int fuse_mode = !fenv ? -1 : fenv[0] == '0' ? 0 : 1;     // -1: by the extra bytes
+    if (fuse_mode != 0 && cfg.num_stages >= 2 && !cfg.values_on_host) {
         sd::StageGeom& P = c->st[cfg.num_stages - 2];
         const sd::StageGeom& Q = c->st[cfg.num_stages - 1];
         const int rq = P.chunk / Q.chunk;
-        if (Q.chunk / Q.stride == 8 && P.stride % Q.stride == 0 && P.stride / Q.stride <= 4 &&
+        const int64_t extra_rows = int64_t(P.ncand) * (P.chunk / Q.stride - P.chunk / P.stride) -
+                                   int64_t(Q.ncand) * (Q.chunk / Q.stride);
+        const bool worth = fuse_mode == 1 || int64_t(BH) * extra_rows * sd::kHeadDim <= kFuseExtraBytes;
+        if (worth && Q.chunk / Q.stride == 8 && P.stride % Q.stride == 0 && P.stride / Q.stride <= 4 &&
             P.chunk / Q.stride <= kMaxSamples && int64_t(P.ncand) * rq <= 8192 && Q.ncand <= 512) {
             c->fuse = 1;
             c->fuse_rq = rq;
