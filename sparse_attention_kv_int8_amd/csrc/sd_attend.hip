@@ -399,8 +399,10 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
     const int b = bj / p.Hkv, j = bj - b * p.Hkv;
     const int lane = threadIdx.x & 63;
     const int sl = lane & 7;
-    const int64_t Lraw = p.lengths[b];
-    const int L = (Lraw < 1 || Lraw > p.Lmax) ? 0 : int(Lraw);
+    // the length, sanitised where each path first needs it (the kept-chunk
+    // splits' select loads do not wait for it)
+    const int32_t Lraw = load_length(p.lengths, b);
+    auto length = [&]() -> int { return int(length_here(Lraw, p.Lmax)); };
 
     // this lane's 16 query dims of every head of the group (bf16 pairs)
     uint32_t qv[G][8];
@@ -428,6 +430,7 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
     int kept_n = -1;
     FusedOut fused{};
     if (HOSTV) {
+        const int L = length();
         const int nb = p.nblocks[bj];
         const int per = (nb + p.nsplit - 1) / p.nsplit;
         const int r0 = min(nb, sp * per), r1 = min(nb, r0 + per);
@@ -435,6 +438,7 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
                                 qv, m, lsum, acc0, acc1, tblk, tmask, rec);
     } else if (sp >= p.nsplit - p.nsplit_a) {
         // sink / window blocks: known without any selection
+        const int L = length();
         const int s_end = min(p.sink, L);
         const int w0 = p.window > 0 ? max(0, L - p.window) : L;
         const int sb1 = (s_end + 7) >> 3, wb1 = (L + 7) >> 3;
@@ -454,25 +458,29 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
         int nk;
         const int* kstarts;
+        // (the selects take Lmax as the length bound: a selected candidate
+        // has a score, so it starts below the length anyway)
         if constexpr (SEL == kGiven) {
             // the last stage is reused: its kept set is read from kept_idx
             // (and no pruning kernel ran this step to flag a bad length)
-            if (L == 0 && sp == 0 && threadIdx.x == 0) atomicOr(p.flag, kFlagBadLength);
+            const int Lg = length();
+            if (Lg == 0 && sp == 0 && threadIdx.x == 0) atomicOr(p.flag, kFlagBadLength);
             int* sel = reinterpret_cast<int*>(dyn + p.last.ncand);
-            nk = given_kept<kAttnThreads>(p.last, kept_bj + p.last.koff, L, sel, tmp);
+            nk = given_kept<kAttnThreads>(p.last, kept_bj + p.last.koff, Lg, sel, tmp);
             kstarts = sel;
         } else if constexpr (SELP != 0) {
             const FusedOut fo = kept_two_stages<kAttnThreads, SELP, SEL>(
                 p.P, p.p_first != 0, p.p_scores + int64_t(bj) * p.P.ncand, p.p_first ? nullptr : kept_bj + p.pp_koff_p,
-                p.pre + int64_t(bj) * p.P.ncand * p.fuse_rq, p.fuse_rq, p.last, L, dyn, tmp);
+                p.pre + int64_t(bj) * p.P.ncand * p.fuse_rq, p.fuse_rq, p.last, p.Lmax, dyn, tmp);
             nk = fo.nq;
             kstarts = fo.q_starts;
             fused = fo;
         } else {
             nk = kept_of_stage<kAttnThreads, SEL>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
-                                                  p.first_stage ? nullptr : kept_bj + p.pp_koff, L, dyn, tmp);
+                                                  p.first_stage ? nullptr : kept_bj + p.pp_koff, p.Lmax, dyn, tmp);
             kstarts = reinterpret_cast<const int*>(dyn + p.last.ncand);
         }
+        const int L = length();
         SD_PHASE(3, 2);
         kept_n = sp == 0 && SEL != kGiven ? nk : -1;   // the first of these workgroups publishes the kept set
         const int s_end = min(p.sink, L);
@@ -530,7 +538,7 @@ __global__ __launch_bounds__(kAttnThreads) void sd_dense_decode_kernel(AttendPar
     const int bj = b * p.Hkv + j;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sl = lane & 7;
-    const int64_t Lraw = p.lengths[b];
+    const int32_t Lraw = load_length(p.lengths, b);
     const bool bad = Lraw < 1 || Lraw > p.Lmax;
     const int L = bad ? 0 : int(Lraw);
     if (bad && sp == 0 && j == 0 && threadIdx.x == 0) atomicOr(p.flag, 1);

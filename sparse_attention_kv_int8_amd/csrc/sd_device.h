@@ -229,6 +229,25 @@ __device__ __forceinline__ int xcc_id() {
     return x & 0xf;
 }
 
+// A request's length, read with a vector load: a plain load of this
+// uniform address compiles to a scalar load, and the wait for it, shared
+// with the kernel-argument loads, then sits in front of every load issued
+// after it, adding one dependent memory round trip to the head of the
+// kernel.  Here the wait falls where the length is first used.
+__device__ __forceinline__ int32_t load_length(const int32_t* lengths, int b) {
+    return __hip_atomic_load(lengths + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// The length from load_length, checked against [1, lmax] (0 when outside)
+// at the point of this call: the compiler would otherwise move the first
+// use of a uniform load, and the wait for it, up to the load itself; adding
+// an opaque per-lane zero ties the use to this point.
+__device__ __forceinline__ int64_t length_here(int32_t raw, int64_t lmax) {
+    int32_t z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    const int64_t x = int64_t(raw + z);
+    return (x < 1 || x > lmax) ? 0 : x;
+}
+
 // Waits until this wave's vector stores (and atomics) have been acknowledged
 // by the L2.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -285,14 +304,20 @@ __device__ __forceinline__ unsigned abs_bits2(uint32_t w) {
 // Wave w < G handles query head j*G + w; lane l handles dims 2l and 2l+1.
 // Qlds must hold 128 ints; the caller's block has at least G waves.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void group_query_codes(const uint16_t* __restrict__ q_b, int j, int G, int* Qlds,
-                                  int8_t* __restrict__ q8_b) {
+// This thread's bf16 pair of the query (wave w < G: head j*G + w, dims 2l
+// and 2l + 1), loaded early so that the codes can be formed while other
+// loads are in flight.
+__device__ __forceinline__ uint32_t query_pair(const uint16_t* __restrict__ q_b, int j, int G) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    return w < G ? reinterpret_cast<const uint32_t*>(q_b + (j * G + w) * kHeadDim)[lane] : 0u;
+}
+
+__device__ __forceinline__ void group_query_codes(uint32_t pr, int j, int G, int* Qlds, int8_t* __restrict__ q8_b) {
     if (threadIdx.x < kHeadDim) Qlds[threadIdx.x] = 0;
     __syncthreads();
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if (w < G) {
         const int h = j * G + w;
-        const uint32_t pr = reinterpret_cast<const uint32_t*>(q_b + h * kHeadDim)[lane];
         const unsigned ab = wave_max_u(abs_bits2(pr));
         const float amax = bf16_to_f32(uint16_t(ab));
         const int c0 = code_of(bf16_lo(pr), amax), c1 = code_of(bf16_hi(pr), amax);
@@ -304,6 +329,10 @@ __device__ __forceinline__ void group_query_codes(const uint16_t* __restrict__ q
         }
     }
     __syncthreads();
+}
+__device__ __forceinline__ void group_query_codes(const uint16_t* __restrict__ q_b, int j, int G, int* Qlds,
+                                                  int8_t* __restrict__ q8_b) {
+    group_query_codes(query_pair(q_b, j, G), j, G, Qlds, q8_b);
 }
 
 }  // namespace sd

@@ -74,8 +74,10 @@ struct RowBatch {
             const int i = it * 8 + row8;
             const int64_t t = xs[c] + int64_t(i) * p.rstride;
             ok[u] = xs[c] >= 0 && i < p.nrows && t < L;
-            v[u] = ok[u] ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k8_bj + t * kHeadDim) + sl)
-                         : u32x4{0, 0, 0, 0};
+            // every load issued, rows that do not count read as row 0 (in bounds) and masked by ok in
+            // score(): a load under a branch makes the compiler wait for it before the next one
+            const int64_t tc = ok[u] ? t : 0;
+            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k8_bj + tc * kHeadDim) + sl);
         }
     }
 
@@ -144,9 +146,8 @@ struct SketchBatch {
             const int i = it * 16 + r16;
             const int64_t t = xs[c] + int64_t(i) * p.rstride;
             ok[u] = xs[c] >= 0 && i < p.nrows && t < L;
-            const int64_t row = int64_t(int(xs[c]) / p.rstride) + i;   // = t / rstride
-            v[u] = ok[u] ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k4_bj + row * (kHeadDim / 2)) + part)
-                         : u32x4{0u, 0u, 0u, 0u};
+            const int64_t row = ok[u] ? int64_t(int(xs[c]) / p.rstride) + i : 0;   // = t / rstride (row 0: masked)
+            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k4_bj + row * (kHeadDim / 2)) + part);
         }
     }
 
@@ -258,15 +259,20 @@ __device__ __forceinline__ void split_query4d(const int* Qlds, int part, uint32_
 
 // Stages other than the first unfused one: the previous stage's kept set
 // (selected here, or given), then this workgroup's slice of the candidates.
+// Lraw: the request's length as loaded (sanitised here, where first needed,
+// so that the head select's loads do not wait for it).
 template <int NS8, int SEL, bool FUSE>
-__device__ __forceinline__ void score_later(const PruneParams& p, int bj, int wgi, int b, int j, bool bad,
-                                            int64_t L, int32_t* kept_bj, const int8_t* __restrict__ k8_bj,
+__device__ __forceinline__ void score_later(const PruneParams& p, int bj, int wgi, int b, int j, int32_t Lraw,
+                                            int32_t* kept_bj, const int8_t* __restrict__ k8_bj,
                                             int32_t* scores_bj, uint32_t* dyn, int* Qlds, unsigned* tmp,
                                             int* cstart) {
     const int wave = threadIdx.x >> 6;
     const int sl = threadIdx.x & 7;
     const int32_t* parents = nullptr;
+    int64_t L = 0;
     if constexpr (SEL == 0 || SEL == kGiven) {
+        const bool bad = Lraw < 1 || Lraw > p.Lmax;
+        L = bad ? 0 : Lraw;
         // the first stage this step runs: flags a bad length and forms the
         // group query codes, which the later stages read
         if (bad && wgi == 0 && threadIdx.x == 0) atomicOr(p.flag, 1);
@@ -282,11 +288,14 @@ __device__ __forceinline__ void score_later(const PruneParams& p, int bj, int wg
     } else if constexpr (SEL != 0) {
         // the group query load is issued together with the previous scores' loads
         const int qval = threadIdx.x < kHeadDim ? p.qgroup[int64_t(bj) * kHeadDim + threadIdx.x] : 0;
-        // kept set of the previous stage (its own parents are in kept_idx already)
+        // kept set of the previous stage (its own parents are in kept_idx
+        // already).  The length bound is Lmax here: a selected candidate has
+        // a score, so it starts below the length anyway.
         int* sel = reinterpret_cast<int*>(dyn + p.prev.ncand);
         const int32_t* pp = p.stage >= 2 ? kept_bj + p.pp_koff : nullptr;
         const int nk = kept_of_stage<kPruneThreads, SEL>(p.prev, p.stage == 1, p.prev_scores + int64_t(bj) * p.prev.ncand,
-                                                         pp, L, dyn, tmp, p.stage);
+                                                         pp, p.Lmax, dyn, tmp, p.stage);
+        L = length_here(Lraw, p.Lmax);
         for (int i = nk + threadIdx.x; i < p.prev.keep; i += kPruneThreads) sel[i] = -1;
         if (threadIdx.x < kHeadDim) Qlds[threadIdx.x] = qval;
         __syncthreads();
@@ -331,9 +340,11 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
     if (ps.bj < 0) return;
     const int bj = ps.bj, wgi = ps.w;
     const int b = bj / p.Hkv, j = bj - b * p.Hkv;
-    const int64_t Lraw = p.lengths[b];
-    const bool bad = Lraw < 1 || Lraw > p.Lmax;
-    const int64_t L = bad ? 0 : Lraw;          // an invalid request has no candidates
+    // the length is sanitised where each path first needs it (an invalid
+    // request has no candidates)
+    const int32_t Lraw = load_length(p.lengths, b);
+    // the first stage's query pair, loaded together with the length
+    const uint32_t qpr = (Q4 || (SEL == 0 && !FUSE)) ? query_pair(p.q + int64_t(b) * p.Hq * kHeadDim, j, p.G) : 0u;
     int32_t* kept_bj = p.kept + int64_t(bj) * p.keep_total;
 
     const int8_t* k8_bj = p.k8 + int64_t(bj) * p.Lmax * kHeadDim;
@@ -346,6 +357,8 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
         // CB): rows loaded first, query codes formed while they are in flight.
         constexpr int NS16 = NS8 >= 2 ? NS8 / 2 : 1;
         using SB = SketchBatch<NS16>;
+        const bool bad = Lraw < 1 || Lraw > p.Lmax;
+        const int64_t L = bad ? 0 : Lraw;
         const int first = (wgi * kPruneWaves + wave) * p.cpw;
         int64_t xs[SB::CB];
 #pragma unroll
@@ -353,7 +366,7 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
         SB sb;
         sb.load(p, xs, L, k4_bj);
         if (bad && wgi == 0 && threadIdx.x == 0) atomicOr(p.flag, 1);
-        group_query_codes(p.q + int64_t(b) * p.Hq * kHeadDim, j, p.G, Qlds, nullptr);
+        group_query_codes(qpr, j, p.G, Qlds, nullptr);
         if (wgi == 0 && threadIdx.x < kHeadDim)
             p.qgroup[int64_t(bj) * kHeadDim + threadIdx.x] = Qlds[threadIdx.x];
         uint32_t d0[4], d1[4], d2[4];
@@ -364,6 +377,8 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
         // starts follow from the indices, so the rows are loaded first and
         // the query codes are formed while the loads are in flight.
         using RB = RowBatch<NS8, false>;
+        const bool bad = Lraw < 1 || Lraw > p.Lmax;
+        const int64_t L = bad ? 0 : Lraw;
         const int first = (wgi * kPruneWaves + wave) * p.cpw;
         int64_t xs[RB::CB];
 #pragma unroll
@@ -371,14 +386,14 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
         RB rb;
         rb.load(p, xs, L, k8_bj);
         if (bad && wgi == 0 && threadIdx.x == 0) atomicOr(p.flag, 1);
-        group_query_codes(p.q + int64_t(b) * p.Hq * kHeadDim, j, p.G, Qlds, nullptr);
+        group_query_codes(qpr, j, p.G, Qlds, nullptr);
         if (wgi == 0 && threadIdx.x < kHeadDim)
             p.qgroup[int64_t(bj) * kHeadDim + threadIdx.x] = Qlds[threadIdx.x];
         u32x4 qh, ql;
         split_query(Qlds, sl, qh, ql);
         rb.score(p, qh, ql, first, p.cpw, scores_bj, nullptr);
     } else {
-        score_later<NS8, SEL, FUSE>(p, bj, wgi, b, j, bad, L, kept_bj, k8_bj, scores_bj, dyn, Qlds, tmp, cstart);
+        score_later<NS8, SEL, FUSE>(p, bj, wgi, b, j, Lraw, kept_bj, k8_bj, scores_bj, dyn, Qlds, tmp, cstart);
     }
     SD_PHASE(p.stage, 2);
 }
