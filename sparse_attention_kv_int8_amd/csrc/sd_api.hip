@@ -98,19 +98,30 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
     if (mb > (int64_t(1) << 20)) return SD_ERR_UNSUPPORTED;
     c->max_blocks = int(mb);
     const int BH = cfg.batch * cfg.num_kv_heads;
+    // Decode splits per (request, KV head): about 512 workgroups in all, at
+    // most 48 per (request, KV head) with device values (the merge reads
+    // every split's partial: at B = 1, 48 splits measured about 1 us faster
+    // per step than 64 at 128K and at 1M; 32 and 40 were no faster than
+    // 64) and 64 with host values (whose decode waits on host reads: 48
+    // measured 6 us slower per step on the 3M sequence), at most one per 4
+    // attended blocks.
     int ns = (512 + BH - 1) / BH;
-    ns = ns < 1 ? 1 : ns > 64 ? 64 : ns;      // at most 64 splits (one per lane in the merge)
+    const int ns_max = cfg.values_on_host ? 64 : 48;      // (the merge takes up to 64: one per lane)
+    ns = ns < 1 ? 1 : ns > ns_max ? ns_max : ns;
     const int cap = (c->max_blocks + 3) / 4;
     c->nsplit = ns > cap ? cap : ns;
-    // device values: split the splits between sink/window blocks and kept blocks
-    // in proportion to their largest sizes
+    // device values: split the splits between sink/window blocks and kept
+    // blocks, a sink/window split taking about 1.25 times the blocks of a
+    // kept-block split, which starts only after its selects (14 of 48 at
+    // these shapes; 10 and 12 measured slower)
     const int64_t ra = (cfg.sink > 0 || cfg.window > 0) ? (cfg.sink + 7) / 8 + (cfg.window + 7) / 8 + 1 : 0;
     const int64_t rk = int64_t(last.keep) * (last.chunk / 8);
     if (cfg.values_on_host || ra == 0) {
         c->nsplit_a = 0;
     } else {
         if (c->nsplit < 2) c->nsplit = 2;
-        int na = int((int64_t(c->nsplit) * ra + (ra + rk) / 2) / (ra + rk));
+        const int64_t den = 4 * ra + 5 * rk;
+        int na = int((int64_t(c->nsplit) * 4 * ra + den / 2) / den);
         na = na < 1 ? 1 : na > c->nsplit - 1 ? c->nsplit - 1 : na;
         c->nsplit_a = na;
     }
