@@ -915,6 +915,7 @@ def main() -> int:
                              "dominant": r2["dominant"],
                              "dominant_frac": round(r2["bytes"]["per_launch"][r2["dominant"]] /
                                                     (r2["dominant_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                             "dominant_traffic": (load_traffic(w2.name, r2["dominant"]) or {}).get("traffic_bytes"),
                              "per_kernel_frac": kernel_fracs(r2["bytes"]["per_launch"], r2["avg_us"]),
                              "quantize_keys_us": round(b2.quantize_us, 2), "reuse": r2["reuse"],
                              "dense": r2["dense"], "sketch4": r2["sketch"]}
