@@ -334,11 +334,104 @@ __device__ int radix_select(const uint32_t* keys, int n, int K, int* sel, uint32
 constexpr int kSelLds = 32;
 __host__ __device__ constexpr int select_width(int n) { return n <= 1024 ? 4 : n <= 4096 ? 16 : kSelLds; }
 
+// Large selects (keys in LDS) first try a threshold from a sample: the
+// top r of kSampleKeys regularly spaced keys, r chosen so that about 4 K
+// keys lie at or above the r-th (T0).  All keys >= T0 are counted; when
+// there are at least K and at most kGatherMax of them, they hold the top K
+// (the K-th largest key is >= T0), and an exact select over just those,
+// gathered in index order, gives the result.  Otherwise (a skewed sample,
+// heavy ties) the full radix select runs.  Either way the result is exact;
+// the sample only decides how much work the exact part does.
+constexpr int kSampleKeys = 512;
+constexpr int kGatherMax = 1024;
+constexpr int kSampledWords = kSampleKeys + 2 * kGatherMax + kSampleKeys + 1;
+
 // LDS words a select needs besides keys [n] and sel [K + 1].
 __host__ __device__ inline int select_cand_words(int n, int K) {
-    (void)n;
     (void)K;
-    return kRadixWords;
+    return kRadixWords + (n > 4096 ? kSampledWords : 0);
+}
+
+template <int NT, int E>
+__device__ int select_top(const uint32_t* keys, int n, int K, int* sel, int* cand, unsigned* tmp,
+                          const KeyStats& ks);
+
+// The sampled path above, for n > 4096 keys in LDS with more than K valid.
+// Returns the kept count, or -1 (uniformly) when the full select must run;
+// leaves the histogram cleared either way.  cand: select_cand_words() words.
+template <int NT>
+__device__ int sampled_select(const uint32_t* keys, int n, int K, int* sel, int* cand, unsigned* tmp) {
+    uint32_t* smp = reinterpret_cast<uint32_t*>(cand) + kRadixWords;    // [kSampleKeys]
+    uint32_t* gk = smp + kSampleKeys;                                    // [kGatherMax] gathered keys
+    int* gi = reinterpret_cast<int*>(gk + kGatherMax);                  // [kGatherMax] their indices
+    int* ssel = gi + kGatherMax;                                         // [kSampleKeys + 1]
+    const int tid = threadIdx.x;
+    // odd strides keep the lanes' LDS reads on distinct banks
+    const int stride = ((n / kSampleKeys) - 1) | 1;
+    unsigned nv = 0, kmin = 0xffffffffu, kmax = 0;
+    for (int i = tid; i < kSampleKeys; i += NT) {
+        const uint32_t k = keys[i * stride];
+        smp[i] = k;
+        nv += k != 0u;
+        kmin = min(kmin, k ? k : 0xffffffffu);
+        kmax = max(kmax, k);
+    }
+    const KeyStats ss = block_key_stats<NT>(nv, kmin, kmax, tmp);
+    const int r = max(1, (4 * K + stride - 1) / stride);
+    if (r >= kSampleKeys || ss.nvalid <= r) return -1;
+    const int nr = select_top<NT, 4>(smp, kSampleKeys, r, ssel, cand, tmp, ss);
+    unsigned mn = 0xffffffffu;
+    for (int i = tid; i < nr; i += NT) mn = min(mn, smp[ssel[i]]);
+    const uint32_t T0 = block_key_stats<NT>(0u, mn, 0u, tmp).kmin;      // the r-th largest sample
+    // keys >= T0 over contiguous ranges of at most 63 keys per thread (for
+    // the ordered gather; an odd range length keeps the lanes' reads on
+    // distinct LDS banks), read eight at a time from clamped indices (no
+    // read under a branch); the thread's passing keys are recorded in a bit
+    // mask, so the gather visits only those (a few per thread)
+    const int per = ((n + NT - 1) / NT) | 1;          // <= 63 for n <= 15872
+    if (per > 63) return -1;
+    const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
+    constexpr int kU = 8;
+    uint64_t pass = 0;
+    for (int i = i0; i < i1; i += kU) {
+        uint32_t k8[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) k8[u] = keys[min(i + u, n - 1)];
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            pass |= uint64_t((i + u < i1) && k8[u] >= T0) << (i + u - i0);
+    }
+    const unsigned c = unsigned(__builtin_popcountll(pass));
+    unsigned total;
+    unsigned pos = block_excl_scan<NT>(c, tmp + 16, &total);
+    if (total < unsigned(K) || total > unsigned(kGatherMax)) return -1;
+    unsigned gmin = 0xffffffffu, gmax = 0;
+    while (pass) {
+        const int j = __builtin_ctzll(pass);
+        pass &= pass - 1;
+        const uint32_t k = keys[i0 + j];
+        gk[pos] = k;
+        gi[pos] = i0 + j;
+        ++pos;
+        gmin = min(gmin, k);
+        gmax = max(gmax, k);
+    }
+    const KeyStats gs = block_key_stats<NT>(c, gmin, gmax, tmp);       // (its barrier orders the gather)
+    const int nk = select_top<NT, 4>(gk, int(total), K, sel, cand, tmp, gs);
+    int idx[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + u * NT;
+        idx[u] = i < nk ? gi[sel[i]] : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + u * NT;
+        if (i < nk) sel[i] = idx[u];
+    }
+    __syncthreads();
+    return nk;
 }
 
 // Workgroup-level: top-K of n keys in LDS (loaded by load_keys, which gave
@@ -362,9 +455,17 @@ __device__ int select_top(const uint32_t* keys, int n, int K, int* sel, int* can
         __syncthreads();
         return int(total);
     }
-    if constexpr (E == 4) return radix_select<NT, 4>(keys, n, K, sel, hist, tmp, ks);
-    else if constexpr (E == 16) return radix_select<NT, 16>(keys, n, K, sel, hist, tmp, ks);
-    else return radix_select<NT, 0>(keys, n, K, sel, hist, tmp, ks);
+    if constexpr (E == 4) {
+        return radix_select<NT, 4>(keys, n, K, sel, hist, tmp, ks);
+    } else if constexpr (E == 16) {
+        return radix_select<NT, 16>(keys, n, K, sel, hist, tmp, ks);
+    } else {
+        if (ks.nvalid > K && K <= 2 * NT) {
+            const int nk = sampled_select<NT>(keys, n, K, sel, cand, tmp);
+            if (nk >= 0) return nk;
+        }
+        return radix_select<NT, 0>(keys, n, K, sel, hist, tmp, ks);
+    }
 }
 
 
