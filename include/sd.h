@@ -376,9 +376,9 @@ sd_status sd_set_value_fetch(sd_ctx* ctx, int32_t mode);
 enum {
     SD_PROF_STAGE0 = 0,         /* pruning stage s is SD_PROF_STAGE0 + s */
     SD_PROF_VALUE_CACHE = 4,    /* LRU update of the host-value path */
-    SD_PROF_ATTEND = 5,         /* last select + attended set + sparse flash decode (partials) */
+    SD_PROF_ATTEND = 5,         /* last select + attended set + sparse flash decode + merge of its splits */
     SD_PROF_QUANTIZE = 6,       /* the three kernels of sd_quantize_keys, as one interval */
-    SD_PROF_COMBINE = 7,        /* log-sum-exp merge of the splits into the bf16 output */
+    SD_PROF_COMBINE = 7,        /* log-sum-exp merge of the dense decode's splits into the bf16 output */
     SD_PROF_DENSE = 8,          /* dense flash decode of sd_dense_decode (partials; its merge is COMBINE) */
     SD_PROF_APPEND = 9,         /* the two kernels of sd_append_kv, as one interval */
     SD_PROF_KINDS = 10

@@ -9,13 +9,13 @@
 // FlashAttention, section "从赫赫有名的注意力机制说起"), and the last split
 // of each (request, KV head) to finish merges all splits by log-sum-exp.
 //
-// The last stage's kept set is in kept_idx (the last pruning kernel wrote
-// it, or an earlier step did).  Workgroup (split, request, KV head) = 4
-// waves: the last nsplit_a splits take the sink and window (dispatched
-// last, so that their bulk loads queue behind the other splits' small loads
-// of the kept set); the others take the kept chunks' blocks (with values in
-// host memory, the value-cache kernel's block list instead); waves take the
-// split's blocks round-robin.  For one 8-token
+// Workgroup (split, request, KV head) = 4 waves: the last nsplit_a splits
+// take the sink and window (dispatched last, so that their bulk loads queue
+// behind the other splits' small loads of the select inputs); the others
+// select the last stage's kept set themselves (fused plan: the last two
+// stages), or read it from kept_idx when the stage is reused, and take the
+// kept chunks' blocks (with values in host memory, the value-cache kernel's
+// block list instead); waves take the split's blocks round-robin.  For one 8-token
 // block a wave computes the G scores of every token (lane = token * 8 +
 // 16-dim slice; bf16 pair dot products, DPP sum over the 8 slice lanes),
 // takes the block max per head (uniform over the wave), then accumulates
