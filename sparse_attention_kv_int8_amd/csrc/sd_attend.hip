@@ -224,6 +224,66 @@ __device__ __forceinline__ void attend_block(const BlockData& d, const uint32_t 
     }
 }
 
+// The same update with two blocks at once (16 tokens): the running max,
+// the rescale of the state and its exp2 are taken once for the pair.
+// ORDERED (blocks whose loads were just issued): the first block's scores,
+// then the second's, and the first block's values before the second's, with
+// scheduling barriers between them, so that the wave starts on the first
+// block as soon as its rows arrive (its loads were issued first).  Not
+// ORDERED (rows loaded long before): the two blocks' chains interleave.
+template <int G, bool ORDERED>
+__device__ __forceinline__ void attend_pair(const BlockData& d0, const BlockData& d1, const uint32_t (&qv)[G][8],
+                                            float scale_log2, float (&m)[G], float (&lsum)[G], float (&acc0)[G],
+                                            float (&acc1)[G]) {
+    const int lane = threadIdx.x & 63, tok = lane >> 3;
+    const bool in0 = (d0.mask >> tok) & 1u, in1 = (d1.mask >> tok) & 1u;
+    auto score = [&](const BlockData& d, int h) {
+        float s = dot2bf(qv[h][0], d.k0.x, 0.f);
+        s = dot2bf(qv[h][1], d.k0.y, s);
+        s = dot2bf(qv[h][2], d.k0.z, s);
+        s = dot2bf(qv[h][3], d.k0.w, s);
+        s = dot2bf(qv[h][4], d.k1.x, s);
+        s = dot2bf(qv[h][5], d.k1.y, s);
+        s = dot2bf(qv[h][6], d.k1.z, s);
+        s = dot2bf(qv[h][7], d.k1.w, s);
+        return sum8_f(s);
+    };
+    float z0[G], z1[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) z0[h] = in0 ? score(d0, h) * scale_log2 : -INFINITY;
+    if constexpr (ORDERED) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int h = 0; h < G; ++h) z1[h] = in1 ? score(d1, h) * scale_log2 : -INFINITY;
+    float pw0[G], pw1[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float bm = max_groups_f(fmaxf(z0[h], z1[h]));
+        const float mn = fmaxf(m[h], bm);
+        const float alpha = rescale(m[h], mn);
+        pw0[h] = in0 ? fast_exp2(z0[h] - mn) : 0.f;
+        pw1[h] = in1 ? fast_exp2(z1[h] - mn) : 0.f;
+        lsum[h] = lsum[h] * alpha + (pw0[h] + pw1[h]);
+        acc0[h] *= alpha;
+        acc1[h] *= alpha;
+        m[h] = mn;
+    }
+    auto pv = [&](const BlockData& d, const float (&pw)[G]) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float v0 = bf16_lo(d.vv[u]), v1 = bf16_hi(d.vv[u]);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float pu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw[h]), u * 8));
+                acc0[h] = fmaf(pu, v0, acc0[h]);
+                acc1[h] = fmaf(pu, v1, acc1[h]);
+            }
+        }
+    };
+    pv(d0, pw0);
+    if constexpr (ORDERED) __builtin_amdgcn_sched_barrier(0);
+    pv(d1, pw1);
+}
+
 // The block loop of one workgroup over blocks [r0, r1) of its source.  The
 // (block, mask) entries are computed once per tile of kBlkTile blocks, one
 // per thread, into LDS (and, when rec is not null, stored as rec[r] =
@@ -256,8 +316,15 @@ __device__ __forceinline__ void decode_blocks(const AttendParams& p, const Src& 
             load_block<HOSTV>(p, tb + i, tblk[i], tmask[i], bj, L, kbase, vbase, d0);
             if (two) load_block<HOSTV>(p, tb + i + kAttnWaves, tblk[i + kAttnWaves], tmask[i + kAttnWaves], bj, L, kbase,
                                        vbase, d1);
-            attend_block<G>(d0, qv, p.scale_log2, m, lsum, acc0, acc1);
-            if (two) attend_block<G>(d1, qv, p.scale_log2, m, lsum, acc0, acc1);
+            if (two && n > 2 * kAttnWaves) {
+                // more than one pair per wave: one softmax update per pair
+                attend_pair<G, true>(d0, d1, qv, p.scale_log2, m, lsum, acc0, acc1);
+            } else {
+                // at most a pair per wave (a latency-bound split): each
+                // block as soon as its rows arrive
+                attend_block<G>(d0, qv, p.scale_log2, m, lsum, acc0, acc1);
+                if (two) attend_block<G>(d1, qv, p.scale_log2, m, lsum, acc0, acc1);
+            }
         }
         __syncthreads();
     }
@@ -576,16 +643,16 @@ __global__ __launch_bounds__(kAttnThreads) void sd_dense_decode_kernel(AttendPar
         if (rb + kAttnWaves < r1)
             load_block<false>(p, rb + kAttnWaves, (rb + kAttnWaves) * 8, valid_mask8(rb + kAttnWaves, L), bj, L,
                               kbase, vbase, b1);
-        attend_block<G>(a0, qv, p.scale_log2, m, lsum, acc0, acc1);
-        if (r + kAttnWaves < r1) attend_block<G>(a1, qv, p.scale_log2, m, lsum, acc0, acc1);
+        if (r + kAttnWaves < r1) attend_pair<G, false>(a0, a1, qv, p.scale_log2, m, lsum, acc0, acc1);
+        else attend_block<G>(a0, qv, p.scale_log2, m, lsum, acc0, acc1);
         if (rb >= r1) break;
         const int ra = rb + kGrp;
         if (ra < r1) load_block<false>(p, ra, ra * 8, valid_mask8(ra, L), bj, L, kbase, vbase, a0);
         if (ra + kAttnWaves < r1)
             load_block<false>(p, ra + kAttnWaves, (ra + kAttnWaves) * 8, valid_mask8(ra + kAttnWaves, L), bj, L,
                               kbase, vbase, a1);
-        attend_block<G>(b0, qv, p.scale_log2, m, lsum, acc0, acc1);
-        if (rb + kAttnWaves < r1) attend_block<G>(b1, qv, p.scale_log2, m, lsum, acc0, acc1);
+        if (rb + kAttnWaves < r1) attend_pair<G, false>(b0, b1, qv, p.scale_log2, m, lsum, acc0, acc1);
+        else attend_block<G>(b0, qv, p.scale_log2, m, lsum, acc0, acc1);
     }
     write_partials<G>(p.part, p.Bh, p.nsplit, bj, sp, m, lsum, acc0, acc1, wm, wl, wacc);
 }
