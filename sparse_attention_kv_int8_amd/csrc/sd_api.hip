@@ -176,6 +176,11 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
         if (cfg.value_cache_tokens / 8 < c->max_blocks) return SD_ERR_INVALID_ARG;
         if (cfg.value_cache_tokens / 8 > (int64_t(1) << 24)) return SD_ERR_UNSUPPORTED;
     }
+    // the LRU step on chip for small caches; SD_VCACHE_ONCHIP=0 takes the
+    // device-memory path for every size
+    const char* venv = std::getenv("SD_VCACHE_ONCHIP");
+    c->vc_onchip = cfg.values_on_host && cfg.value_cache_tokens / 8 <= sd::kVcOnchipSlots &&
+                   c->max_blocks <= sd::kVcOnchipBlocks && !(venv && venv[0] == '0');
     return SD_OK;
 }
 

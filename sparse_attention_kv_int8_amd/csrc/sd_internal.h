@@ -30,6 +30,11 @@ struct StageDev {
 };
 
 constexpr int kVcCounters = 16;
+// Value caches of at most kVcOnchipSlots slots and kVcOnchipBlocks attended
+// blocks per (request, KV head) take the LRU step with its working state on
+// chip (sd_vcache.hip).
+constexpr int kVcOnchipSlots = 8192;
+constexpr int kVcOnchipBlocks = 1024;
 // Entry of the per-step block -> slot map: the slot in the low 24 bits, a
 // miss (block not resident: read it from host memory into its slot) or a
 // refill (resident, but written when fewer of its rows were below the
@@ -104,6 +109,7 @@ struct sd_ctx {
     int32_t* vstage;                  // pinned host staging: nblocks [BH], lengths [B], blocks and blk_slot [BH][max_blocks]
     int64_t vcopies;                  // copies (runs) enqueued by the last step
     sd::ValueCache vc;
+    int vc_onchip;                    // the LRU step keeps its working state on chip (small caches)
     const void* vhost_key;            // last host value pointer seen, and its device alias
     const uint16_t* vhost_dev;
     // profiling (sd_profile_start / sd_profile_stop)

@@ -72,18 +72,65 @@ struct VcStepParams {
     int Hkv;
 };
 
+// Step counters of one (request, KV head) after its LRU step: the clock,
+// the used slots, and the hit / miss / refill statistics (sd_get_stats).
+__device__ __forceinline__ void vcache_step_stats(const ValueCache& vc, int bj, int32_t step, int used, int nb,
+                                                  int nmiss, int nfree, unsigned nref) {
+    // refills of this (request, KV head), summed over the block
+    if (nref) atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 12), (unsigned long long)nref);
+    if (nref) atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 7 + 4 * (step & 1)), (unsigned long long)nref);
+    if (threadIdx.x == 0) {
+        vc.stepc[bj] = step + 1;
+        vc.used[bj] = used + (nmiss < nfree ? nmiss : nfree);
+        const int par = step & 1;
+        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 1), (unsigned long long)nb);
+        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 2), (unsigned long long)(nb - nmiss));
+        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 3), (unsigned long long)nmiss);
+        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 4 + 4 * par), (unsigned long long)nb);
+        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 5 + 4 * par), (unsigned long long)(nb - nmiss));
+        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 6 + 4 * par), (unsigned long long)nmiss);
+        if (bj == 0) {
+            vc.counters[0] = step + 1;
+            const int nxt = (step + 1) & 1;
+            vc.counters[4 + 4 * nxt] = 0;
+            vc.counters[5 + 4 * nxt] = 0;
+            vc.counters[6 + 4 * nxt] = 0;
+            vc.counters[7 + 4 * nxt] = 0;
+        }
+    }
+}
+
+// Small caches (FAST: at most kVcOnchipSlots slots and kVcOnchipBlocks
+// attended blocks per (request, KV head), unless SD_VCACHE_ONCHIP=0) keep the step's working state on chip: the
+// block list and the evicted slots in LDS, each thread's 32 entries of the
+// recency order in registers (loaded while the block list is built), the
+// slots of this step's blocks in registers, and "touched this step" as an
+// LDS bit map of the slots the hits took.  After the select, the only memory
+// round trips left are the hits' page-table and fill lookups and, when
+// slots are evicted, the blocks those held.  Larger caches take the same
+// steps through device memory (slot_last marks the touched slots).
+constexpr int kVcFastSlots = kVcOnchipSlots;
+constexpr int kVcFastOrd = kVcFastSlots / kLruThreads;     // order entries per thread
+constexpr int kVcFastBlocks = kVcOnchipBlocks;
+constexpr int kVcFastPer = kVcFastBlocks / kLruThreads;    // attended blocks per thread
+
 // SEL: select code of the last stage, or kGiven when it is reused (read
 // from kept_idx).
-template <int SEL>
+template <int SEL, bool FAST>
 __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParams p) {
     extern __shared__ uint32_t dyn[];    // the last stage's select (kept_lds_words)
     __shared__ unsigned tmp[32];
+    __shared__ uint32_t touchedL[FAST ? kVcFastSlots / 32 : 1];
+    __shared__ uint32_t blocksL[FAST ? kVcFastBlocks : 1];
+    __shared__ int32_t evictedL[FAST ? kVcFastBlocks : 1];
+    __shared__ int32_t ordL[FAST ? kVcFastSlots + kVcFastSlots / 32 : 1];   // entry i at i + i / 32
     const ValueCache& vc = p.vc;
     const int max_blocks = p.max_blocks;
     const int j = blockIdx.x, b = blockIdx.y, bj = b * p.Hkv + j;
     const int32_t step = p.vc.stepc[bj];
     const int64_t BH = int64_t(gridDim.x) * gridDim.y;
     const int tid = threadIdx.x;
+    SD_PHASE(4, 0);
     int64_t L = p.lengths[b];
     if (L < 1 || L > p.Lmax) L = 0;
 
@@ -101,10 +148,7 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
                                              p.first_stage ? nullptr : kept_bj + p.pp_koff, L, dyn, tmp);
         for (int i = tid; i < p.last.keep; i += kLruThreads) kept_bj[p.last.koff + i] = i < nk ? sel[i] : -1;
     }
-    uint32_t* blocks_bj = p.blocks + int64_t(bj) * max_blocks;
-    const int nb = build_attended<kLruThreads>(sel, nk, p.last.chunk, L, p.sink, p.window, blocks_bj, tmp);
-    if (tid == 0) p.nblocks[bj] = nb;
-    const uint32_t* bl = blocks_bj;
+    SD_PHASE(4, 1);
     int32_t* page = vc.page + int64_t(bj) * vc.nblk_max;
     int32_t* sblk = vc.slot_block + int64_t(bj) * vc.slots;
     int32_t* slast = vc.slot_last + int64_t(bj) * vc.slots;
@@ -112,7 +156,132 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
     int32_t* evicted = vc.evicted + int64_t(bj) * max_blocks;
     const int32_t* order_old = vc.order + (int64_t(step & 1) * BH + bj) * vc.slots;
     int32_t* order_new = vc.order + (int64_t((step + 1) & 1) * BH + bj) * vc.slots;
+    int32_t* sfill = vc.slot_fill + int64_t(bj) * vc.slots;
     const int used = vc.used[bj];
+    uint32_t* blocks_bj = p.blocks + int64_t(bj) * max_blocks;
+    if constexpr (FAST) {
+        // the recency order, loaded while the block list is built
+        // (coalesced: entry tid + 256 k, from clamped in-bounds indices, no
+        // load under a branch; entries at or past `used` are never read),
+        // staged in LDS after the hits' lookups.  The touched map is cleared
+        // before build_attended's closing barrier.
+        int32_t ov[kVcFastOrd];
+#pragma unroll
+        for (int k = 0; k < kVcFastOrd; ++k) ov[k] = order_old[min(tid + kLruThreads * k, vc.slots - 1)];
+        for (int i = tid; i < kVcFastSlots / 32; i += kLruThreads) touchedL[i] = 0u;
+        const int nb = build_attended<kLruThreads>(sel, nk, p.last.chunk, L, p.sink, p.window, blocksL, tmp);
+        for (int i = tid; i < nb; i += kLruThreads) blocks_bj[i] = blocksL[i];
+        if (tid == 0) p.nblocks[bj] = nb;
+        SD_PHASE(4, 2);
+
+        // 1. hits touch their slot (bit map); misses are counted
+        const int per = (nb + kLruThreads - 1) / kLruThreads;     // <= kVcFastPer
+        const int r0 = min(nb, tid * per), r1 = min(nb, r0 + per);
+        uint32_t e[kVcFastPer];
+        int32_t bs[kVcFastPer], fv[kVcFastPer];
+#pragma unroll
+        for (int u = 0; u < kVcFastPer; ++u) e[u] = r0 + u < r1 ? blocksL[r0 + u] : 0u;
+#pragma unroll
+        for (int u = 0; u < kVcFastPer; ++u) bs[u] = page[e[u] >> 8];
+#pragma unroll
+        for (int u = 0; u < kVcFastPer; ++u) fv[u] = sfill[max(bs[u], 0)];
+        unsigned nm = 0, nref = 0;
+#pragma unroll
+        for (int u = 0; u < kVcFastPer; ++u) {
+            if (r0 + u >= r1) continue;
+            const int32_t sv = bs[u];
+            if (sv >= 0) {
+                atomicOr(&touchedL[sv >> 5], 1u << (sv & 31));
+                const int rows = int(min<int64_t>(8, L - 8 * int64_t(e[u] >> 8)));
+                if (fv[u] < rows) {
+                    sfill[sv] = rows;
+                    bs[u] = sv | kVcRefillBit;
+                    ++nref;
+                }
+            } else {
+                ++nm;
+            }
+        }
+        // entry i at ordL[i + i / 32]: thread t's entries [32 t, 32 t + 32)
+        // then sit 33 words apart, on distinct banks
+#pragma unroll
+        for (int k = 0; k < kVcFastOrd; ++k) {
+            const int i = tid + kLruThreads * k;
+            ordL[i + (i >> 5)] = ov[k];
+        }
+        SD_PHASE(4, 3);
+        unsigned nmiss;
+        unsigned mrank = block_excl_scan<kLruThreads>(nm, tmp, &nmiss);   // (its barrier completes the map and ordL)
+        SD_PHASE(4, 4);
+        const int nfree = vc.slots - used;
+        const int nevict = int(nmiss) > nfree ? int(nmiss) - nfree : 0;
+
+        // 2. untouched entries keep their order; the oldest `nevict` of them
+        //    leave.  Thread t takes entries [32 t, 32 t + 32).
+        const int o0 = tid * kVcFastOrd;
+        uint32_t umask = 0;
+#pragma unroll
+        for (int k = 0; k < kVcFastOrd; ++k) {
+            ov[k] = ordL[o0 + (tid) + k];             // entry o0 + k at (o0 + k) + (o0 + k) / 32 = 33 t + k
+            const int32_t sv = ov[k];
+            if (o0 + k < used && !((touchedL[sv >> 5] >> (sv & 31)) & 1u)) umask |= 1u << k;
+        }
+        unsigned nuntouched;
+        unsigned krank = block_excl_scan<kLruThreads>(unsigned(__builtin_popcount(umask)), tmp, &nuntouched);
+        SD_PHASE(4, 5);
+        if (nevict > 0) {
+            int32_t bv[kVcFastOrd];
+#pragma unroll
+            for (int k = 0; k < kVcFastOrd; ++k) bv[k] = sblk[((umask >> k) & 1u) ? ov[k] : 0];
+#pragma unroll
+            for (int k = 0; k < kVcFastOrd; ++k) {
+                if (!((umask >> k) & 1u)) continue;
+                if (int(krank) < nevict) {
+                    page[bv[k]] = -1;
+                    evictedL[krank] = ov[k];
+                } else {
+                    order_new[krank - nevict] = ov[k];
+                }
+                ++krank;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kVcFastOrd; ++k)
+                if ((umask >> k) & 1u) order_new[krank++] = ov[k];
+        }
+        __syncthreads();
+        SD_PHASE(4, 6);
+        const int nsurv = int(nuntouched) - nevict;
+
+        // 3. misses take free slots first (ascending), then the evicted slots
+        //    (oldest first); the decode kernel fills them from host memory
+#pragma unroll
+        for (int u = 0; u < kVcFastPer; ++u) {
+            if (r0 + u >= r1 || bs[u] >= 0) continue;
+            const int32_t blk = int32_t(e[u] >> 8);
+            const int m = int(mrank++);
+            const int32_t sl = m < nfree ? used + m : evictedL[m - nfree];
+            page[blk] = sl;
+            sblk[sl] = blk;
+            sfill[sl] = int(min<int64_t>(8, L - 8 * int64_t(blk)));
+            bs[u] = sl | kVcMissBit;
+        }
+        SD_PHASE(4, 7);
+        // 4. this step's blocks become the newest entries, ascending by id
+#pragma unroll
+        for (int u = 0; u < kVcFastPer; ++u) {
+            if (r0 + u >= r1) continue;
+            bslot[r0 + u] = bs[u];
+            order_new[nsurv + r0 + u] = bs[u] & kVcSlotMask;
+        }
+        SD_PHASE(4, 8);
+        vcache_step_stats(vc, bj, step, used, nb, int(nmiss), nfree, nref);
+        return;
+    }
+    const int nb = build_attended<kLruThreads>(sel, nk, p.last.chunk, L, p.sink, p.window, blocks_bj, tmp);
+    if (tid == 0) p.nblocks[bj] = nb;
+    SD_PHASE(4, 2);
+    const uint32_t* bl = blocks_bj;
 
     // 1. hits touch their slot; misses are ranked in block order (ascending id)
     const int per = (nb + kLruThreads - 1) / kLruThreads;
@@ -123,7 +292,6 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
     // (a hit whose slot holds fewer rows than are below the length now is
     // refilled from host memory: only the block holding the old last token
     // can be one, after the length grew)
-    int32_t* sfill = vc.slot_fill + int64_t(bj) * vc.slots;
     unsigned nm = 0, nref = 0;
     for (int b0 = r0; b0 < r1; b0 += kVcBatch) {
         uint32_t e[kVcBatch];
@@ -155,8 +323,10 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
             }
         }
     }
+    SD_PHASE(4, 3);
     unsigned nmiss;
     unsigned mrank = block_excl_scan<kLruThreads>(nm, tmp, &nmiss);   // barriers inside
+    SD_PHASE(4, 4);
     const int nfree = vc.slots - used;
     const int nevict = int(nmiss) > nfree ? int(nmiss) - nfree : 0;
 
@@ -175,6 +345,7 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
     }
     unsigned nuntouched;
     unsigned krank = block_excl_scan<kLruThreads>(nu, tmp, &nuntouched);
+    SD_PHASE(4, 5);
     for (int b0 = i0; b0 < i1; b0 += kVcBatch) {
         int32_t sv[kVcBatch], lv[kVcBatch], bv[kVcBatch];
 #pragma unroll
@@ -197,6 +368,7 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
         }
     }
     __syncthreads();
+    SD_PHASE(4, 6);
     const int nsurv = int(nuntouched) - nevict;
 
     // 3. misses take free slots first (ascending), then the evicted slots
@@ -212,31 +384,14 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
         sfill[s] = int(min<int64_t>(8, L - 8 * int64_t(blk)));
         bslot[r] = s | kVcMissBit;
     }
+    SD_PHASE(4, 7);
     // 4. this step's blocks become the newest entries, ascending by id
     for (int r = r0; r < r1; ++r) order_new[nsurv + r] = bslot[r] & kVcSlotMask;
-    // refills of this (request, KV head), summed over the block
-    if (nref) atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 12), (unsigned long long)nref);
-    if (nref) atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 7 + 4 * (step & 1)), (unsigned long long)nref);
-    if (tid == 0) {
-        vc.stepc[bj] = step + 1;
-        vc.used[bj] = used + (int(nmiss) < nfree ? int(nmiss) : nfree);
-        const int par = step & 1;
-        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 1), (unsigned long long)nb);
-        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 2), (unsigned long long)(nb - int(nmiss)));
-        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 3), (unsigned long long)nmiss);
-        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 4 + 4 * par), (unsigned long long)nb);
-        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 5 + 4 * par), (unsigned long long)(nb - int(nmiss)));
-        atomicAdd(reinterpret_cast<unsigned long long*>(vc.counters + 6 + 4 * par), (unsigned long long)nmiss);
-        if (bj == 0) {
-            vc.counters[0] = step + 1;
-            const int nxt = (step + 1) & 1;
-            vc.counters[4 + 4 * nxt] = 0;
-            vc.counters[5 + 4 * nxt] = 0;
-            vc.counters[6 + 4 * nxt] = 0;
-            vc.counters[7 + 4 * nxt] = 0;
-        }
-    }
+    SD_PHASE(4, 8);
+    vcache_step_stats(vc, bj, step, used, nb, int(nmiss), nfree, nref);
 }
+
+SD_PHASE_SETUP(vcache)
 
 hipError_t launch_value_cache_reset(sd_ctx* c, hipStream_t s) {
     const int64_t BH = int64_t(c->cfg.batch) * c->cfg.num_kv_heads;
@@ -267,10 +422,17 @@ hipError_t launch_value_cache_update(sd_ctx* c, bool given, const int32_t* lengt
     const size_t lds = size_t(kept_lds_words(p.last, p.first_stage != 0)) * 4;
     dim3 grid(c->cfg.num_kv_heads, c->cfg.batch);
     const int sw = select_width(p.last.ncand);
-    if (given) launch(sd_vcache_step_kernel<kGiven>, grid, dim3(kLruThreads), lds, s, t, p);
-    else if (sw == 4) launch(sd_vcache_step_kernel<4>, grid, dim3(kLruThreads), lds, s, t, p);
-    else if (sw == 16) launch(sd_vcache_step_kernel<16>, grid, dim3(kLruThreads), lds, s, t, p);
-    else launch(sd_vcache_step_kernel<kSelLds>, grid, dim3(kLruThreads), lds, s, t, p);
+    if (c->vc_onchip) {
+        if (given) launch(sd_vcache_step_kernel<kGiven, true>, grid, dim3(kLruThreads), lds, s, t, p);
+        else if (sw == 4) launch(sd_vcache_step_kernel<4, true>, grid, dim3(kLruThreads), lds, s, t, p);
+        else if (sw == 16) launch(sd_vcache_step_kernel<16, true>, grid, dim3(kLruThreads), lds, s, t, p);
+        else launch(sd_vcache_step_kernel<kSelLds, true>, grid, dim3(kLruThreads), lds, s, t, p);
+    } else {
+        if (given) launch(sd_vcache_step_kernel<kGiven, false>, grid, dim3(kLruThreads), lds, s, t, p);
+        else if (sw == 4) launch(sd_vcache_step_kernel<4, false>, grid, dim3(kLruThreads), lds, s, t, p);
+        else if (sw == 16) launch(sd_vcache_step_kernel<16, false>, grid, dim3(kLruThreads), lds, s, t, p);
+        else launch(sd_vcache_step_kernel<kSelLds, false>, grid, dim3(kLruThreads), lds, s, t, p);
+    }
     return hipGetLastError();
 }
 

@@ -17,6 +17,16 @@ from tests.gpu_util import GpuRun, compare_step, oracle_config, oracle_keys
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(params=["onchip", "device"])
+def lru_path(request, monkeypatch):
+    """Both paths of the value-cache kernel's LRU step: the working state on
+    chip (the default for caches of at most 8,192 slots) and in device
+    memory (larger caches; forced here by SD_VCACHE_ONCHIP=0)."""
+    if request.param == "device":
+        monkeypatch.setenv("SD_VCACHE_ONCHIP", "0")
+    return request.param
+
+
 def run_sequence(w, check_every=1, reuse_at=None):
     """reuse_at(t): how many pruning stages step t reuses from step t - 1
     (default none)."""
@@ -61,7 +71,7 @@ def run_sequence(w, check_every=1, reuse_at=None):
     return tot_h, tot_m
 
 
-def test_hostv_small_with_evictions():
+def test_hostv_small_with_evictions(lru_path):
     """128K tokens, a 2,048-block cache per KV head: the drifting query makes
     the attended blocks outgrow the cache, so evictions happen."""
     w = WORKLOADS["ctx_3m_hostv"].replace(name="hostv_small", max_context=131072, value_cache_tokens=16384,
@@ -71,7 +81,7 @@ def test_hostv_small_with_evictions():
     assert h > 0
 
 
-def test_hostv_with_reused_stages():
+def test_hostv_with_reused_stages(lru_path):
     """Host values with pruning stages reused between refreshes: every
     fourth step runs all stages, the others reuse one, two or all three."""
     w = WORKLOADS["ctx_3m_hostv"].replace(name="hostv_reuse", max_context=65536, value_cache_tokens=16384,
@@ -79,7 +89,7 @@ def test_hostv_with_reused_stages():
     run_sequence(w, reuse_at=lambda t: t % 4)
 
 
-def test_hostv_reset_starts_cold():
+def test_hostv_reset_starts_cold(lru_path):
     w = WORKLOADS["ctx_3m_hostv"].replace(name="hostv_reset", max_context=32768, value_cache_tokens=8192,
                                           planted=16, steps=3)
     inp = make_inputs(w)
@@ -100,7 +110,7 @@ def test_hostv_full_3m_workload():
     run_sequence(WORKLOADS["ctx_3m_hostv"], check_every=4)
 
 
-def test_hostv_graph_replay_follows_the_lru():
+def test_hostv_graph_replay_follows_the_lru(lru_path):
     """One host-value step captured in a HIP graph and replayed over the
     drifting sequence (the step's query copied into the captured buffer
     before each replay, eager work and a synchronisation between replays):
@@ -145,7 +155,7 @@ def test_hostv_graph_replay_follows_the_lru():
     assert evicting, "the sequence should outgrow the cache"
 
 
-def test_hostv_growing_lengths_refill_partial_blocks():
+def test_hostv_growing_lengths_refill_partial_blocks(lru_path):
     """Lengths grow by 1 to 3 tokens between steps, as in a decode loop, so
     the block holding the old last token is needed again with more valid
     rows: the cache must serve those rows (refilled from host memory), not
