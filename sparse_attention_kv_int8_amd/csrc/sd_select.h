@@ -642,17 +642,26 @@ __device__ int build_attended(const int32_t* kept_s, int nk, int chunk, int64_t 
     const int bpc = chunk >> 3;
     const int nq = nk * bpc;
     auto blk_at = [&](int q) -> int64_t { return (int64_t(kept_s[q / bpc]) >> 3) + (q % bpc); };
-    auto lower = [&](int64_t v) -> int {     // first q with blk_at(q) >= v
-        int lo = 0, hi = nq;
+    auto first_block = [&](int c) -> int64_t { return int64_t(kept_s[c]) >> 3; };
+    // first kept chunk whose last block is >= v (nk if none): a search over
+    // the chunks, with no division in its loop
+    auto chunk_lower = [&](int64_t v) -> int {
+        int lo = 0, hi = nk;
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
-            if (blk_at(mid) < v) lo = mid + 1; else hi = mid;
+            if (first_block(mid) + bpc - 1 < v) lo = mid + 1; else hi = mid;
         }
         return lo;
     };
+    auto lower = [&](int64_t v) -> int {     // first q with blk_at(q) >= v
+        const int c = chunk_lower(v);
+        if (c >= nk) return nq;
+        const int64_t off = v - first_block(c);
+        return c * bpc + int(off > 0 ? off : 0);
+    };
     auto kept_block = [&](int64_t blk) -> bool {
-        const int q = lower(blk);
-        return q < nq && blk_at(q) == blk;
+        const int c = chunk_lower(blk);
+        return c < nk && first_block(c) <= blk;
     };
     auto valid_mask = [&](int64_t blk) -> uint32_t {
         const int64_t over = blk * 8 + 8 - L;

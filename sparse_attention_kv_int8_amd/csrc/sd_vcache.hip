@@ -229,6 +229,9 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
         unsigned nuntouched;
         unsigned krank = block_excl_scan<kLruThreads>(unsigned(__builtin_popcount(umask)), tmp, &nuntouched);
         SD_PHASE(4, 5);
+        // the new order is assembled in ordL (every thread has read its old
+        // entries: the scan's barriers) and stored coalesced at the end
+        auto pad = [](int i) { return i + (i >> 5); };
         if (nevict > 0) {
             int32_t bv[kVcFastOrd];
 #pragma unroll
@@ -240,14 +243,14 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
                     page[bv[k]] = -1;
                     evictedL[krank] = ov[k];
                 } else {
-                    order_new[krank - nevict] = ov[k];
+                    ordL[pad(int(krank) - nevict)] = ov[k];
                 }
                 ++krank;
             }
         } else {
 #pragma unroll
             for (int k = 0; k < kVcFastOrd; ++k)
-                if ((umask >> k) & 1u) order_new[krank++] = ov[k];
+                if ((umask >> k) & 1u) ordL[pad(int(krank++))] = ov[k];
         }
         __syncthreads();
         SD_PHASE(4, 6);
@@ -272,8 +275,10 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
         for (int u = 0; u < kVcFastPer; ++u) {
             if (r0 + u >= r1) continue;
             bslot[r0 + u] = bs[u];
-            order_new[nsurv + r0 + u] = bs[u] & kVcSlotMask;
+            ordL[pad(nsurv + r0 + u)] = bs[u] & kVcSlotMask;
         }
+        __syncthreads();
+        for (int i = tid; i < nsurv + nb; i += kLruThreads) order_new[i] = ordL[pad(i)];
         SD_PHASE(4, 8);
         vcache_step_stats(vc, bj, step, used, nb, int(nmiss), nfree, nref);
         return;
