@@ -20,8 +20,10 @@
 // 16-dim slice; bf16 pair dot products, DPP sum over the 8 slice lanes),
 // takes the block max per head (uniform over the wave), then accumulates
 // P V with lane l owning output dims 2l and 2l+1, reading each value row
-// with one coalesced dword per lane.  All splits of a (request, KV head) run
-// on one XCD (sd_device.h), so the merge reads their partials from its L2.
+// with one coalesced dword per lane; where a wave takes more than one pair
+// of blocks, the running max and the rescale are taken once per pair.  All
+// splits of a (request, KV head) run on one XCD (sd_device.h), so the merge
+// reads their partials from its L2.
 #include "sd_device.h"
 #include "sd_internal.h"
 #include "sd_select.h"
