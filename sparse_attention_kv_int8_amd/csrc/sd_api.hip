@@ -105,8 +105,16 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
     // 64) and 64 with host values (whose decode waits on host reads: 48
     // measured 6 us slower per step on the 3M sequence), at most one per 4
     // attended blocks.
-    int ns = (512 + BH - 1) / BH;
-    const int ns_max = cfg.values_on_host ? 64 : 48;      // (the merge takes up to 64: one per lane)
+    // With at least kDecodeWideMinPipes pipelines (device values), about
+    // kDecodeWideWgs workgroups and the wide kernel instead: its merge sizes
+    // its loads for at most kDecodeWideSplits splits, which leaves room for
+    // three workgroups per CU.  16 requests of up to 128K: 6 splits per
+    // (request, KV head), the decode kernel 60 -> 48 us.  (At B = 1 the
+    // wide kernel measured 1.2 us slower per step: the compiler schedules
+    // its other code for the higher occupancy.)
+    c->decode_wide = !cfg.values_on_host && BH >= sd::kDecodeWideMinPipes;
+    int ns = ((c->decode_wide ? sd::kDecodeWideWgs : 512) + BH - 1) / BH;
+    const int ns_max = cfg.values_on_host ? sd::kDecodeMaxSplits : sd::kDecodeWideSplits;
     ns = ns < 1 ? 1 : ns > ns_max ? ns_max : ns;
     const int cap = (c->max_blocks + 3) / 4;
     c->nsplit = ns > cap ? cap : ns;

@@ -380,13 +380,15 @@ __device__ __forceinline__ void write_partials(float* part, int Bh, int nsplit, 
 // lane = split); thread t sums output quad t % (32 G) over the splits
 // t / (32 G) + k SG (SG = 8 / G split groups, every float4 load issued at
 // once: one memory round trip), and the split groups are added through LDS.
-constexpr int kMergeMaxSplit = 64;
-
-template <int G>
+// MAXS: the most splits the launch can have (kDecodeMaxSplits, or
+// kDecodeWideSplits for the wide kernel); it sizes the per-thread loads,
+// the kernel's largest register set.
+template <int G, int MAXS>
 __device__ __forceinline__ void merge_splits(const AttendParams& p, int bj, int b, int j, float* wgt, float4* red) {
+    static_assert(MAXS <= kDecodeMaxSplits, "one split per lane in the weight pass");
     constexpr int NQ = G * kHeadDim / 4;         // float4 quads of outputs
     constexpr int SG = kAttnThreads / NQ;        // split groups
-    constexpr int NB = kMergeMaxSplit / SG;      // splits per thread, at most
+    constexpr int NB = (MAXS + SG - 1) / SG;     // splits per thread, at most
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int q = tid % NQ, sg = tid / NQ, h = (4 * q) / kHeadDim;
     const int ns = p.nsplit;
@@ -448,7 +450,7 @@ __device__ __forceinline__ void merge_splits(const AttendParams& p, int bj, int 
 // Every kept-chunk split selects the last stage's kept set itself (the
 // selection is deterministic, so they agree) and the first of them
 // publishes it to kept_idx; the last split to finish merges all partials.
-template <int G, bool HOSTV, int SEL, int SELP>
+template <int G, bool HOSTV, int SEL, int SELP, int MAXS = kDecodeMaxSplits>
 __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendParams p) {
     extern __shared__ uint32_t dyn[];   // device values: the select (keys, sel, scratch)
     __shared__ float wm[kAttnWaves][G];
@@ -585,7 +587,7 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
     const bool last = handoff_last(p.tick + int64_t(bj) * kTickInts, p.nsplit, &ticket, p.flag);
     SD_PHASE(3, 5);
     if (!last) return;
-    merge_splits<G>(p, bj, b, j, reinterpret_cast<float*>(tblk), red);
+    merge_splits<G, MAXS>(p, bj, b, j, reinterpret_cast<float*>(tblk), red);
     SD_PHASE(3, 6);
 }
 
@@ -752,11 +754,20 @@ __global__ __launch_bounds__(kAttnThreads) void sd_combine_kernel(const float* _
 }
 
 template <int G>
-static void launch_g(const AttendParams& p, dim3 grid, bool hostv, bool fuse, bool given, size_t lds, hipStream_t s,
-                     Timing t) {
+static void launch_g(const AttendParams& p, dim3 grid, bool hostv, bool fuse, bool given, bool wide, size_t lds,
+                     hipStream_t s, Timing t) {
     const dim3 block(kAttnThreads);
     // a fused Q select is the 4-wide one (Q.ncand <= 512 when fused)
     const int sq = select_width(p.last.ncand), sp = fuse ? select_width(p.P.ncand) : 0;
+    constexpr int W = kDecodeWideSplits;
+    if (wide && !hostv && !fuse) {
+        // many pipelines (the unfused plan, or reused stages)
+        if (given) launch(sd_flash_decode_kernel<G, false, kGiven, 0, W>, grid, block, lds, s, t, p);
+        else if (sq == 4) launch(sd_flash_decode_kernel<G, false, 4, 0, W>, grid, block, lds, s, t, p);
+        else if (sq == 16) launch(sd_flash_decode_kernel<G, false, 16, 0, W>, grid, block, lds, s, t, p);
+        else launch(sd_flash_decode_kernel<G, false, kSelLds, 0, W>, grid, block, lds, s, t, p);
+        return;
+    }
     if (hostv) launch(sd_flash_decode_kernel<G, true, 4, 0>, grid, block, 0, s, t, p);
     else if (given) launch(sd_flash_decode_kernel<G, false, kGiven, 0>, grid, block, lds, s, t, p);
     else if (fuse && sp == 4) launch(sd_flash_decode_kernel<G, false, 4, 4>, grid, block, lds, s, t, p);
@@ -816,9 +827,9 @@ hipError_t launch_attend(sd_ctx* c, bool given, bool fused, const uint16_t* q, c
     const dim3 grid(unsigned(pipe_grid(c->nsplit, p.Bh)));
     const bool hostv = c->cfg.values_on_host != 0;
     switch (c->G) {
-        case 1: launch_g<1>(p, grid, hostv, fuse, given, lds, s, t); break;
-        case 2: launch_g<2>(p, grid, hostv, fuse, given, lds, s, t); break;
-        default: launch_g<4>(p, grid, hostv, fuse, given, lds, s, t); break;
+        case 1: launch_g<1>(p, grid, hostv, fuse, given, c->decode_wide != 0, lds, s, t); break;
+        case 2: launch_g<2>(p, grid, hostv, fuse, given, c->decode_wide != 0, lds, s, t); break;
+        default: launch_g<4>(p, grid, hostv, fuse, given, c->decode_wide != 0, lds, s, t); break;
     }
     return hipGetLastError();
 }

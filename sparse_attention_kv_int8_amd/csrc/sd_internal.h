@@ -30,6 +30,15 @@ struct StageDev {
 };
 
 constexpr int kVcCounters = 16;
+// Decode splits per (request, KV head): at most 64 (one per lane of the
+// merge's weight pass).  With many (request, KV head) pipelines the decode
+// runs "wide": at most kDecodeWideSplits splits, about kDecodeWideWgs
+// workgroups in all, and a kernel whose merge sizes its loads for that many
+// splits (fewer registers, three workgroups per CU instead of two).
+constexpr int kDecodeMaxSplits = 64;
+constexpr int kDecodeWideSplits = 48;
+constexpr int kDecodeWideWgs = 768;
+constexpr int kDecodeWideMinPipes = 32;
 // Value caches of at most kVcOnchipSlots slots and kVcOnchipBlocks attended
 // blocks per (request, KV head) take the LRU step with its working state on
 // chip (sd_vcache.hip).
@@ -74,6 +83,7 @@ struct sd_ctx {
     int max_blocks;         // attended 8-token blocks per (request, KV head)
     int nsplit;             // flash-decode splits per (request, KV head)
     int nsplit_a;           // of which cover the sink/window blocks (device values only)
+    int decode_wide;        // many pipelines: at most kDecodeWideSplits splits, the wide decode kernel
     int nsplit_d;           // splits per (request, KV head) of the dense decode (sd_dense_decode)
     int64_t sketch_rows;    // rows per (request, KV head) of the int4 first-stage sketch: ceil(Lmax / r_1)
     float scale_log2;       // softmax_scale * log2(e)
