@@ -176,6 +176,19 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
             P.nwg = (P.ncand + P.per_wg - 1) / P.per_wg;
         }
     }
+    // With many pipelines the unfused stages after the first score two load
+    // batches per wave: half the workgroups, so half the redundant selects
+    // at their heads (16 requests of up to 128K: stage 1 26.3 -> 24.7 us).
+    if (BH >= sd::kDecodeWideMinPipes) {
+        for (int s = 1; s < cfg.num_stages; ++s) {
+            sd::StageGeom& g = c->st[s];
+            if (c->fuse && s == cfg.num_stages - 2) continue;
+            const int cpw = 2 * (g.per_wg / 4);
+            if (cpw > sd::kMaxCandPerWave) continue;
+            g.per_wg = 4 * cpw;
+            g.nwg = (g.ncand + g.per_wg - 1) / g.per_wg;
+        }
+    }
     const float scale = cfg.softmax_scale > 0.0f ? cfg.softmax_scale : 1.0f / std::sqrt(float(cfg.head_dim));
     c->scale_log2 = scale * 1.4426950408889634f;
 
@@ -242,11 +255,11 @@ sd_status device_setup(sd_ctx* c) {
     // stage s's select runs at the head of stage s + 1's pruning kernel,
     // the last stage's (fused: the last two stages') at the head of the
     // decode kernel.  The pruning kernels' static LDS is the query codes,
-    // the exchange words and the candidate starts (4 waves x 8); the decode
+    // the exchange words and the candidate starts (4 waves x kMaxCandPerWave); the decode
     // kernel's is the four waves' softmax state (m, l and the G x 128
     // accumulators), the exchange words, the block tile's starts and masks,
     // the hand-off word and the merge's reduction (one float4 per thread).
-    const int64_t prune_static = 4 * (sd::kHeadDim + 32 + 4 * 8);
+    const int64_t prune_static = 4 * (sd::kHeadDim + 32 + 4 * sd::kMaxCandPerWave);
     const int64_t attend_static = 4 * (4 * (2 + sd::kHeadDim) * int64_t(c->G) + 32 + 2 * 256 + 1 + 4 * 256);
     int64_t need = 0;
     for (int s = 0; s + 1 < c->S; ++s)

@@ -39,6 +39,9 @@ constexpr int kDecodeMaxSplits = 64;
 constexpr int kDecodeWideSplits = 48;
 constexpr int kDecodeWideWgs = 768;
 constexpr int kDecodeWideMinPipes = 32;
+// Candidates per wave of a pruning kernel, at most: one batch of 8 row
+// loads, or two for the stages after the first with many pipelines.
+constexpr int kMaxCandPerWave = 16;
 // Value caches of at most kVcOnchipSlots slots and kVcOnchipBlocks attended
 // blocks per (request, KV head) take the LRU step with its working state on
 // chip (sd_vcache.hip).

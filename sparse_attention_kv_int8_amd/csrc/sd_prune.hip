@@ -27,7 +27,7 @@ namespace sd {
 
 constexpr int kPruneThreads = 256;
 constexpr int kPruneWaves = kPruneThreads / kWave;
-constexpr int kMaxCandPerWave = 8;          // candidates per wave (one batch of 8 row loads)
+// (kMaxCandPerWave, candidates per wave at most: sd_internal.h)
 
 struct PruneParams {
     const uint16_t* q;        // [B][Hq][d]
