@@ -109,6 +109,11 @@ SMALL = {
     "twelve_samples": tiny_workload(name="twelve", batch=2, num_q_heads=4, num_kv_heads=1, max_context=3000,
                                     stages=(Stage(96, 8, 6), Stage(24, 3, 10), Stage(8, 1, 12)), sink=5,
                                     window=40, planted=4),
+    # 32 (request, KV head) pipelines: the stages after the first score two
+    # load batches per wave and, unfused, the decode runs wide; ragged lengths
+    "many_pipelines": tiny_workload(name="many", batch=4, num_q_heads=32, num_kv_heads=8, max_context=6000,
+                                    stages=(Stage(256, 8, 6), Stage(32, 2, 11), Stage(8, 1, 19)), sink=9,
+                                    window=77, planted=4),
 }
 
 
@@ -133,6 +138,8 @@ def test_small_shapes(name, fusion):
         lengths = [1, 777, 5000]
     elif name == "g2_strided_last":
         lengths = [4096, 1001]
+    elif name == "many_pipelines":
+        lengths = [6000, 2049, 313, 4500]
     elif name == "twelve_samples":
         lengths = [2999, 95]
     run_case(w, lengths=lengths, check_scores=True)
