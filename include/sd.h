@@ -116,7 +116,19 @@ typedef struct sd_stats {
 
 /* Creates a context on the current HIP device, validating `cfg` and
  * allocating all device workspace (no later call allocates).  On success
- * *out receives the context; on failure *out is set to NULL. */
+ * *out receives the context; on failure *out is set to NULL.
+ * The context's launch plan (which changes no result) is fixed here and
+ * read from these environment variables, when set:
+ *  SD_FUSE_LAST_STAGE=0 / =1  never / always (where the stage geometry
+ *                             allows) score the last stage inside the
+ *                             kernel of the stage before it; default: when
+ *                             the extra key rows stay within 8 MiB.
+ *  SD_VCACHE_ONCHIP=0         host values: the LRU step through device
+ *                             memory at every cache size; default: on chip
+ *                             for at most 8,192 slots and 1,024 attended
+ *                             blocks per (request, KV head).
+ *  SD_DENSE_WG_PER_CU=n       sd_dense_decode's workgroups per CU
+ *                             (default 8). */
 sd_status sd_create(const sd_config* cfg, sd_ctx** out);
 
 /* Releases the context and its workspace after the device is idle.
