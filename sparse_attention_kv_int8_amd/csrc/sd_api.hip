@@ -137,10 +137,10 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
     // Possible when Q's chunks are exactly 8 sampled rows (one load slot),
     // Q's stride divides P's (so P's samples are among the rows read), P
     // reads at most 4x its own samples, all children's scores fit in LDS,
-    // and Q's select keeps its keys in registers (at most 512 candidates);
-    // not with host values (their value-cache kernel selects the last stage
-    // by itself).  It trades one kernel boundary and one scoring pass for a
-    // second select in the decode kernel and more rows read by P: P reads
+    // and Q's select keeps its keys in registers (at most 512 candidates).
+    // (With host values the value-cache kernel takes the two selects.)  It
+    // trades one kernel boundary and one scoring pass for a second select
+    // in the decode kernel and more rows read by P: P reads
     // every row at Q's stride of each of its candidates instead of its own
     // samples, while an unfused Q kernel reads Q.ncand x 8 rows.  Fused when
     // those extra bytes over all (request, KV head) pipelines stay within
@@ -156,7 +156,7 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
     c->fuse_m = 0;
     const char* fenv = std::getenv("SD_FUSE_LAST_STAGE");
     const int fuse_mode = !fenv ? -1 : fenv[0] == '0' ? 0 : 1;     // -1: by the extra bytes
-    if (fuse_mode != 0 && cfg.num_stages >= 2 && !cfg.values_on_host) {
+    if (fuse_mode != 0 && cfg.num_stages >= 2) {
         sd::StageGeom& P = c->st[cfg.num_stages - 2];
         const sd::StageGeom& Q = c->st[cfg.num_stages - 1];
         const int rq = P.chunk / Q.chunk;
@@ -270,6 +270,17 @@ sd_status device_setup(sd_ctx* c) {
     need = std::max(need, 4 * last_words + attend_static);
     // (unfused with the stage before the last reused, the last stage is selected in the decode kernel too)
     need = std::max(need, 4 * int64_t(sd::kept_lds_words(sd::stage_dev(c, c->S - 1), c->S == 1)) + attend_static);
+    if (c->cfg.values_on_host) {
+        // the value-cache kernel takes the selects instead, next to its LRU
+        // state (on chip: the touched map, the block list, the evicted
+        // slots and the padded recency order)
+        const int64_t vcache_static =
+            4 * (32 + (c->vc_onchip ? int64_t(sd::kVcOnchipSlots / 32 + 2 * sd::kVcOnchipBlocks + sd::kVcOnchipSlots +
+                                              sd::kVcOnchipSlots / 32)
+                                    : 3));
+        need = std::max(need, 4 * last_words + vcache_static);
+        need = std::max(need, 4 * int64_t(sd::kept_lds_words(sd::stage_dev(c, c->S - 1), c->S == 1)) + vcache_static);
+    }
     if (need > lds_max) {
         std::snprintf(g_last_error, sizeof(g_last_error), "a kernel needs %lld bytes of LDS, more than the %d a "
                       "workgroup has", (long long)need, lds_max);
@@ -585,7 +596,7 @@ sd_status decode_step(sd_ctx* c, const uint16_t* q, const uint16_t* k, const int
     const bool last_given = reuse == c->S;
     if (e == hipSuccess && c->cfg.values_on_host)
         e = timed(c, SD_PROF_VALUE_CACHE, s, [&](sd::Timing t) {
-            return sd::launch_value_cache_update(c, last_given, lengths, kept, s, t);
+            return sd::launch_value_cache_update(c, last_given, fused, lengths, kept, s, t);
         });
     if (e == hipSuccess && vcopy) e = copy_missed_blocks(c, v, lengths, s);
     if (e == hipSuccess)

@@ -183,8 +183,8 @@ hipError_t launch_combine(sd_ctx* c, int nsplit, uint16_t* out, hipStream_t s, T
 // with c->nsplit_d merges them).
 hipError_t launch_dense(sd_ctx* c, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* lengths,
                         hipStream_t s, Timing t = {});
-hipError_t launch_value_cache_update(sd_ctx* c, bool given, const int32_t* lengths, int32_t* kept, hipStream_t s,
-                                     Timing t = {});
+hipError_t launch_value_cache_update(sd_ctx* c, bool given, bool fused, const int32_t* lengths, int32_t* kept,
+                                     hipStream_t s, Timing t = {});
 hipError_t launch_value_cache_reset(sd_ctx* c, hipStream_t s);
 StageDev stage_dev(const sd_ctx* c, int st);
 

@@ -70,6 +70,15 @@ struct VcStepParams {
     int32_t* nblocks;             // [B][Hkv]
     int max_blocks;
     int Hkv;
+    // fused last two stages (SELP != 0): P = the stage before the last,
+    // scored with every child's last-stage score by its pruning kernel
+    StageDev P;
+    int p_first;                  // P is the first stage
+    int pp_koff_p;                // kept_idx offset of the stage before P
+    const int32_t* p_scores;      // [B][Hkv][P.ncand]
+    const int32_t* pre;           // [B][Hkv][P.ncand * fuse_rq]
+    int fuse_rq;
+    int32_t* last_scores_out;     // [B][Hkv][last.ncand]: the last stage's candidate scores (inspection)
 };
 
 // Step counters of one (request, KV head) after its LRU step: the clock,
@@ -115,10 +124,12 @@ constexpr int kVcFastBlocks = kVcOnchipBlocks;
 constexpr int kVcFastPer = kVcFastBlocks / kLruThreads;    // attended blocks per thread
 
 // SEL: select code of the last stage, or kGiven when it is reused (read
-// from kept_idx).
-template <int SEL, bool FAST>
+// from kept_idx).  SELP: select code of the stage before the last when the
+// two are fused (that stage's pruning kernel scored the last stage's
+// candidates too; both are selected here), else 0.
+template <int SEL, bool FAST, int SELP>
 __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParams p) {
-    extern __shared__ uint32_t dyn[];    // the last stage's select (kept_lds_words)
+    extern __shared__ uint32_t dyn[];    // the select(s) (kept_lds_words, or fused_lds_words)
     __shared__ unsigned tmp[32];
     __shared__ uint32_t touchedL[FAST ? kVcFastSlots / 32 : 1];
     __shared__ uint32_t blocksL[FAST ? kVcFastBlocks : 1];
@@ -143,6 +154,22 @@ __global__ __launch_bounds__(kLruThreads) void sd_vcache_step_kernel(VcStepParam
         // no pruning kernel ran this step to flag a bad length)
         if (L == 0 && tid == 0) atomicOr(p.flag, 1);
         nk = given_kept<kLruThreads>(p.last, kept_bj + p.last.koff, L, sel, tmp);
+    } else if constexpr (SELP != 0) {
+        // fused: select the stage before the last, gather its kept chunks'
+        // children's scores, select the last stage; publish both kept sets
+        // and the last stage's candidate scores
+        const FusedOut fo = kept_two_stages<kLruThreads, SELP, SEL>(
+            p.P, p.p_first != 0, p.p_scores + int64_t(bj) * p.P.ncand, p.p_first ? nullptr : kept_bj + p.pp_koff_p,
+            p.pre + int64_t(bj) * p.P.ncand * p.fuse_rq, p.fuse_rq, p.last, L, dyn, tmp);
+        nk = fo.nq;
+        sel = fo.q_starts;
+        for (int i = tid; i < p.last.keep; i += kLruThreads) kept_bj[p.last.koff + i] = i < nk ? sel[i] : -1;
+        for (int i = tid; i < p.P.keep; i += kLruThreads) kept_bj[p.P.koff + i] = fo.p_starts[i];
+        int32_t* sc = p.last_scores_out + int64_t(bj) * p.last.ncand;
+        for (int i = tid; i < p.last.ncand; i += kLruThreads) {
+            const uint32_t key = fo.q_keys[i];
+            sc[i] = key ? int32_t(key) - (1 << 23) : INT32_MIN;
+        }
     } else {
         nk = kept_of_stage<kLruThreads, SEL>(p.last, p.first_stage != 0, p.last_scores + int64_t(bj) * p.last.ncand,
                                              p.first_stage ? nullptr : kept_bj + p.pp_koff, L, dyn, tmp);
@@ -404,8 +431,8 @@ hipError_t launch_value_cache_reset(sd_ctx* c, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_value_cache_update(sd_ctx* c, bool given, const int32_t* lengths, int32_t* kept, hipStream_t s,
-                                     Timing t) {
+hipError_t launch_value_cache_update(sd_ctx* c, bool given, bool fused, const int32_t* lengths, int32_t* kept,
+                                     hipStream_t s, Timing t) {
     VcStepParams p{};
     p.vc = c->vc;
     const int S = c->S;
@@ -424,20 +451,35 @@ hipError_t launch_value_cache_update(sd_ctx* c, bool given, const int32_t* lengt
     p.nblocks = c->nblocks;
     p.max_blocks = c->max_blocks;
     p.Hkv = c->cfg.num_kv_heads;
-    const size_t lds = size_t(kept_lds_words(p.last, p.first_stage != 0)) * 4;
-    dim3 grid(c->cfg.num_kv_heads, c->cfg.batch);
-    const int sw = select_width(p.last.ncand);
-    if (c->vc_onchip) {
-        if (given) launch(sd_vcache_step_kernel<kGiven, true>, grid, dim3(kLruThreads), lds, s, t, p);
-        else if (sw == 4) launch(sd_vcache_step_kernel<4, true>, grid, dim3(kLruThreads), lds, s, t, p);
-        else if (sw == 16) launch(sd_vcache_step_kernel<16, true>, grid, dim3(kLruThreads), lds, s, t, p);
-        else launch(sd_vcache_step_kernel<kSelLds, true>, grid, dim3(kLruThreads), lds, s, t, p);
-    } else {
-        if (given) launch(sd_vcache_step_kernel<kGiven, false>, grid, dim3(kLruThreads), lds, s, t, p);
-        else if (sw == 4) launch(sd_vcache_step_kernel<4, false>, grid, dim3(kLruThreads), lds, s, t, p);
-        else if (sw == 16) launch(sd_vcache_step_kernel<16, false>, grid, dim3(kLruThreads), lds, s, t, p);
-        else launch(sd_vcache_step_kernel<kSelLds, false>, grid, dim3(kLruThreads), lds, s, t, p);
+    const bool fuse = fused && !given;
+    if (fuse) {
+        p.P = stage_dev(c, S - 2);
+        p.p_first = S == 2;
+        p.pp_koff_p = S >= 3 ? c->st[S - 3].koff : 0;
+        p.p_scores = c->scores[S - 2];
+        p.pre = c->pre;
+        p.fuse_rq = c->fuse_rq;
+        p.last_scores_out = c->scores[S - 1];
     }
+    const size_t lds = size_t(fuse ? fused_lds_words(p.P, p.p_first != 0, p.last, p.fuse_rq)
+                                   : kept_lds_words(p.last, p.first_stage != 0)) * 4;
+    dim3 grid(c->cfg.num_kv_heads, c->cfg.batch);
+    const int sw = select_width(p.last.ncand), sp = fuse ? select_width(p.P.ncand) : 0;
+    const dim3 block(kLruThreads);
+#define SD_VC(F)                                                                                 \
+    if (given) launch(sd_vcache_step_kernel<kGiven, F, 0>, grid, block, lds, s, t, p);           \
+    else if (fuse && sp == 4) launch(sd_vcache_step_kernel<4, F, 4>, grid, block, lds, s, t, p);  \
+    else if (fuse && sp == 16) launch(sd_vcache_step_kernel<4, F, 16>, grid, block, lds, s, t, p); \
+    else if (fuse) launch(sd_vcache_step_kernel<4, F, kSelLds>, grid, block, lds, s, t, p);       \
+    else if (sw == 4) launch(sd_vcache_step_kernel<4, F, 0>, grid, block, lds, s, t, p);          \
+    else if (sw == 16) launch(sd_vcache_step_kernel<16, F, 0>, grid, block, lds, s, t, p);        \
+    else launch(sd_vcache_step_kernel<kSelLds, F, 0>, grid, block, lds, s, t, p);
+    if (c->vc_onchip) {
+        SD_VC(true)
+    } else {
+        SD_VC(false)
+    }
+#undef SD_VC
     return hipGetLastError();
 }
 

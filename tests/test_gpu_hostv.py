@@ -17,6 +17,15 @@ from tests.gpu_util import GpuRun, compare_step, oracle_config, oracle_keys
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(params=["fused", "unfused"])
+def fusion(request, monkeypatch):
+    """The last stage scored inside the kernel of the stage before it, both
+    selected by the value-cache kernel (the default plan at these sizes),
+    or in its own kernel."""
+    monkeypatch.setenv("SD_FUSE_LAST_STAGE", "1" if request.param == "fused" else "0")
+    return request.param
+
+
 @pytest.fixture(params=["onchip", "device"])
 def lru_path(request, monkeypatch):
     """Both paths of the value-cache kernel's LRU step: the working state on
@@ -71,7 +80,7 @@ def run_sequence(w, check_every=1, reuse_at=None):
     return tot_h, tot_m
 
 
-def test_hostv_small_with_evictions(lru_path):
+def test_hostv_small_with_evictions(lru_path, fusion):
     """128K tokens, a 2,048-block cache per KV head: the drifting query makes
     the attended blocks outgrow the cache, so evictions happen."""
     w = WORKLOADS["ctx_3m_hostv"].replace(name="hostv_small", max_context=131072, value_cache_tokens=16384,
@@ -81,7 +90,7 @@ def test_hostv_small_with_evictions(lru_path):
     assert h > 0
 
 
-def test_hostv_with_reused_stages(lru_path):
+def test_hostv_with_reused_stages(lru_path, fusion):
     """Host values with pruning stages reused between refreshes: every
     fourth step runs all stages, the others reuse one, two or all three."""
     w = WORKLOADS["ctx_3m_hostv"].replace(name="hostv_reuse", max_context=65536, value_cache_tokens=16384,
@@ -110,7 +119,7 @@ def test_hostv_full_3m_workload():
     run_sequence(WORKLOADS["ctx_3m_hostv"], check_every=4)
 
 
-def test_hostv_graph_replay_follows_the_lru(lru_path):
+def test_hostv_graph_replay_follows_the_lru(lru_path, fusion):
     """One host-value step captured in a HIP graph and replayed over the
     drifting sequence (the step's query copied into the captured buffer
     before each replay, eager work and a synchronisation between replays):
@@ -155,7 +164,7 @@ def test_hostv_graph_replay_follows_the_lru(lru_path):
     assert evicting, "the sequence should outgrow the cache"
 
 
-def test_hostv_growing_lengths_refill_partial_blocks(lru_path):
+def test_hostv_growing_lengths_refill_partial_blocks(lru_path, fusion):
     """Lengths grow by 1 to 3 tokens between steps, as in a decode loop, so
     the block holding the old last token is needed again with more valid
     rows: the cache must serve those rows (refilled from host memory), not
