@@ -297,6 +297,15 @@ def test_reused_stages_small(fusion):
     reuse_sequence(w, L1=[19000, 2900], L2=[20000, 3011], reuses=[0, 1, 2, 3])
 
 
+def test_reused_stages_many_pipelines(fusion):
+    """Four requests x 8 KV heads (32 pipelines: the later stages score two
+    load batches per wave, the decode runs wide when unfused), grown since
+    the reused step, every reuse level."""
+    w = tiny_workload(name="reuse_many", batch=4, num_q_heads=32, num_kv_heads=8, max_context=6000, steps=2,
+                      stages=(Stage(256, 8, 6), Stage(32, 2, 11), Stage(8, 1, 19)), sink=9, window=77)
+    reuse_sequence(w, L1=[5900, 2000, 313, 4400], L2=[6000, 2049, 313, 4500], reuses=[0, 1, 2, 3])
+
+
 def test_reused_stages_llama8b_128k(fusion):
     """The benchmark's 128K shape (launch configuration included), one
     decode step later (length + 1, next drifting query)."""
