@@ -810,9 +810,9 @@ def main() -> int:
                          "reference that scales hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
-        log("bench.py: one GPU only (the per-(request, KV head) path shards trivially, but no "
-            "multi-GPU run is part of this build)")
+        print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1"}))
+        log("bench.py: one GPU only (the (request, KV head) pipelines are independent and shard across "
+            "GPUs without communication, but only the one-GPU step is measured)")
         return 2
     w = WORKLOADS[args.workload]
     if w.values_on_host:
