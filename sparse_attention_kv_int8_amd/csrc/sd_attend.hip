@@ -145,15 +145,17 @@ struct BlockData {
 // (always inside the cache), and rows outside the mask are zeroed by a
 // select, so the issue is branch-free.  Host values: hits come from the slot
 // pool, misses and refills from host memory (rows t < L), written into their
-// slot.
-template <bool HOSTV>
+// slot.  KROWS = false: the values only (the keys come by load_pair_k).
+template <bool HOSTV, bool KROWS = true>
 __device__ __forceinline__ void load_block(const AttendParams& p, int r, int t0, uint32_t mask, int bj, int L,
                                            const uint16_t* kbase, const uint16_t* vbase, BlockData& d) {
     const int lane = threadIdx.x & 63, tok = lane >> 3, sl = lane & 7;
     d.mask = mask;
-    const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + int64_t(min(t0 + tok, L - 1)) * kHeadDim + sl * 16);
-    d.k0 = __builtin_nontemporal_load(kp);
-    d.k1 = __builtin_nontemporal_load(kp + 1);
+    if constexpr (KROWS) {
+        const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + int64_t(min(t0 + tok, L - 1)) * kHeadDim + sl * 16);
+        d.k0 = __builtin_nontemporal_load(kp);
+        d.k1 = __builtin_nontemporal_load(kp + 1);
+    }
     if (HOSTV) {
         const int32_t se = p.blk_slot[int64_t(bj) * p.max_blocks + r];
         uint32_t* prow = reinterpret_cast<uint32_t*>(p.vpool + (int64_t(bj) * p.vslots + (se & kVcSlotMask)) * 8 * kHeadDim);
@@ -178,6 +180,109 @@ __device__ __forceinline__ void load_block(const AttendParams& p, int r, int t0,
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) d.vv[u] = ((mask >> u) & 1u) ? d.vv[u] : 0u;
+    }
+}
+
+// G = 4 on the matrix cores.  The scores of a pair of blocks (16 tokens)
+// for the group's 4 query heads are one 16 x 16 x 128 product, four
+// v_mfma_f32_16x16x32_bf16 (bf16 products, fp32 sums): A = the 16 key rows
+// (lane l: token row l % 16 of the pair, block (l % 16) / 8), B = the query
+// (lane l: head l % 16 of the group, clamped to the group's last for
+// l % 16 >= 4, whose columns are never read).  Instruction i takes dims
+// 32 i + 8 c + e, e < 8, from lane group c = l / 16, for A and B alike, so
+// the four cover each dim once and one instruction's key loads stay inside
+// one 64-byte piece of each row (one cache line per row).  The result leaves lane l holding tokens
+// 4 c + r, r < 4, of head l % 16: each lane keeps the running max and its
+// share of the sum for its head, and the heads' softmax runs side by side.
+// P V stays on the vector ALU (lane l owns dims 2l, 2l+1, as in
+// attend_block).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Max or sum of lane l's value and lane (l ^ 16)'s (or (l ^ 32)'s), by the
+// row-swap permutes (no LDS round trip): swapping a register with itself
+// leaves lane l's own value in one result and its partner's in the other,
+// so a symmetric operation on the two gives the pair's.
+__device__ __forceinline__ float max_xor16_f(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32_f(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16_f(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32_f(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+struct PairK {
+    u32x4 k[4];
+};
+
+// The A operand of a pair's keys: blocks at t0a and t0b (t0b = t0a when
+// the pair has one block; its tokens are masked), rows clamped below L.
+__device__ __forceinline__ void load_pair_k(int t0a, int t0b, int L, const uint16_t* kbase, PairK& pk) {
+    const int lane = threadIdx.x & 63, m = lane & 15, c = lane >> 4;
+    const int t = min((m < 8 ? t0a : t0b) + (m & 7), L - 1);
+    const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + int64_t(t) * kHeadDim + 8 * c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pk.k[i] = __builtin_nontemporal_load(kp + 4 * i);
+}
+
+// Running max of head lane % 16 (the same in its four lanes) and this
+// lane's share of that head's sum (its tokens 4 (lane / 16) + r).
+struct MState {
+    float m, l;
+};
+
+// Online-softmax update with a pair of blocks on the matrix cores; d1's
+// values are read only when `two` (else its tokens count for nothing).
+__device__ __forceinline__ void attend_pair_mfma(const PairK& pk, const BlockData& d0, const BlockData& d1, bool two,
+                                                 const u32x4 (&qb)[4], float scale_log2, MState& st,
+                                                 float (&acc0)[4], float (&acc1)[4]) {
+    const int lane = threadIdx.x & 63;
+    f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pk.k[i]),
+                                                    __builtin_bit_cast(bf16x8_t, qb[i]), d, 0, 0, 0);
+    const int t0 = 4 * (lane >> 4);                     // this lane's first token of the 16
+    const uint32_t mask1 = two ? d1.mask : 0u;
+    const uint32_t msk = t0 < 8 ? (d0.mask >> t0) : (mask1 >> (t0 - 8));
+    float z[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[r] = ((msk >> r) & 1u) ? d[r] * scale_log2 : -INFINITY;
+    float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    bm = max_xor32_f(max_xor16_f(bm));                  // the head's other token groups
+    const float mn = fmaxf(st.m, bm);
+    const float alpha = rescale(st.m, mn);
+    float pw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pw[r] = ((msk >> r) & 1u) ? fast_exp2(z[r] - mn) : 0.f;
+    st.l = st.l * alpha + ((pw[0] + pw[1]) + (pw[2] + pw[3]));
+    st.m = mn;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
+        acc0[h] *= a;
+        acc1[h] *= a;
+    }
+    // tokens outside the masks have p = 0 and zeroed values: no branch
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        const uint32_t w = t < 8 ? d0.vv[t] : (two ? d1.vv[t - 8] : 0u);
+        const float v0 = bf16_lo(w), v1 = bf16_hi(w);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const float pu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw[t & 3]), h + 16 * (t >> 2)));
+            acc0[h] = fmaf(pu, v0, acc0[h]);
+            acc1[h] = fmaf(pu, v1, acc1[h]);
+        }
     }
 }
 
@@ -293,14 +398,66 @@ __device__ __forceinline__ void attend_pair(const BlockData& d0, const BlockData
 // kAttnWaves-th block of the tile, two blocks in flight.
 constexpr int kBlkTile = kAttnThreads;
 
-template <int G, bool HOSTV, class Src>
+template <int G, bool HOSTV, bool MF, class Src>
 __device__ __forceinline__ void decode_blocks(const AttendParams& p, const Src& src, int r0, int r1, int bj, int L,
                                               const uint16_t* kbase, const uint16_t* vbase,
-                                              const uint32_t (&qv)[G][8], float (&m)[G], float (&lsum)[G],
-                                              float (&acc0)[G], float (&acc1)[G], int* tblk, uint32_t* tmask,
-                                              uint32_t* rec) {
+                                              const uint32_t (&qv)[G][8], const uint16_t* qg, float (&m)[G],
+                                              float (&lsum)[G], float (&acc0)[G], float (&acc1)[G], int* tblk,
+                                              uint32_t* tmask, uint32_t* rec) {
     const int wave = threadIdx.x >> 6;
     if (L <= 0) return;                    // no blocks (and no row to clamp to)
+    // MF (the wide decode, G = 4) and more than one pair per wave: pairs of
+    // blocks on the matrix cores (a last single block as a pair whose second
+    // half is masked).  The one-request plans' splits are latency-bound (a
+    // wave waits for a pair's rows, then has little left to compute); they
+    // take the vector path below, which starts on each block as its rows
+    // arrive and measured faster there.
+    if constexpr (MF && G == 4) if (r1 - r0 > 2 * kAttnWaves) {
+        // the query as the B operand: lane l gives head l % 16 (clamped to
+        // the group's last head; those columns are never read)
+        u32x4 qb[4];
+        {
+            const int lane = threadIdx.x & 63;
+            const u32x4* qp = reinterpret_cast<const u32x4*>(qg + min(lane & 15, G - 1) * kHeadDim + 8 * (lane >> 4));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qb[i] = qp[4 * i];
+        }
+        MState st{-INFINITY, 0.f};
+        for (int tb = r0; tb < r1; tb += kBlkTile) {
+            const int n = min(kBlkTile, r1 - tb);
+            if (int(threadIdx.x) < n) {
+                int blk;
+                uint32_t mask;
+                src.at(tb + threadIdx.x, blk, mask);
+                tblk[threadIdx.x] = blk * 8;
+                tmask[threadIdx.x] = mask;
+                if (rec) rec[tb + threadIdx.x] = (uint32_t(blk) << 8) | mask;
+            }
+            __syncthreads();
+            for (int i = wave; i < n; i += 2 * kAttnWaves) {
+                BlockData d0, d1;
+                PairK pk;
+                const bool two = i + kAttnWaves < n;
+                const int i1 = two ? i + kAttnWaves : i;
+                load_pair_k(tblk[i], tblk[i1], L, kbase, pk);
+                load_block<HOSTV, false>(p, tb + i, tblk[i], tmask[i], bj, L, kbase, vbase, d0);
+                if (two) load_block<HOSTV, false>(p, tb + i1, tblk[i1], tmask[i1], bj, L, kbase, vbase, d1);
+                attend_pair_mfma(pk, d0, d1, two, qb, p.scale_log2, st, acc0, acc1);
+            }
+            __syncthreads();
+        }
+        // to the per-head state of the vector path: the max, and the sum in
+        // lane 0 only (write_partials adds one lane per 8-lane token group)
+        const float x = sum_xor32_f(sum_xor16_f(st.l));
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            m[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(st.m), h));
+            const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), h));
+            lsum[h] = lane == 0 ? tot : 0.f;
+        }
+        return;
+    }
     for (int tb = r0; tb < r1; tb += kBlkTile) {
         const int n = min(kBlkTile, r1 - tb);
         if (int(threadIdx.x) < n) {
@@ -485,6 +642,9 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         qv[h][4] = c.x; qv[h][5] = c.y; qv[h][6] = c.z; qv[h][7] = c.w;
     }
 
+    // the group's query rows (the matrix-core path loads its own operand)
+    const uint16_t* qg = p.q + (int64_t(b) * p.Hq + j * G) * kHeadDim;
+
     float m[G], lsum[G], acc0[G], acc1[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) { m[h] = -INFINITY; lsum[h] = 0.f; acc0[h] = 0.f; acc1[h] = 0.f; }
@@ -505,8 +665,8 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         const int nb = p.nblocks[bj];
         const int per = (nb + p.nsplit - 1) / p.nsplit;
         const int r0 = min(nb, sp * per), r1 = min(nb, r0 + per);
-        decode_blocks<G, HOSTV>(p, ListSrc{p.blocks + int64_t(bj) * p.max_blocks}, r0, r1, bj, L, kbase, vbase,
-                                qv, m, lsum, acc0, acc1, tblk, tmask, rec);
+        decode_blocks<G, HOSTV, !HOSTV && MAXS == kDecodeWideSplits>(p, ListSrc{p.blocks + int64_t(bj) * p.max_blocks}, r0, r1, bj, L, kbase, vbase,
+                                qv, qg, m, lsum, acc0, acc1, tblk, tmask, rec);
     } else if (sp >= p.nsplit - p.nsplit_a) {
         // sink / window blocks: known without any selection
         const int L = length();
@@ -520,7 +680,7 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         const int per = (nb + p.nsplit_a - 1) / p.nsplit_a;
         const int spa = sp - (p.nsplit - p.nsplit_a);
         const int r0 = min(nb, spa * per), r1 = min(nb, r0 + per);
-        decode_blocks<G, HOSTV>(p, RangeSrc{nr1, wb0, s_end, w0, L}, r0, r1, bj, L, kbase, vbase, qv, m, lsum,
+        decode_blocks<G, HOSTV, !HOSTV && MAXS == kDecodeWideSplits>(p, RangeSrc{nr1, wb0, s_end, w0, L}, r0, r1, bj, L, kbase, vbase, qv, qg, m, lsum,
                                 acc0, acc1, tblk, tmask, rec ? rec + kept_words : nullptr);
     } else {
         // the kept chunks of the last stage, recomputed from its scores
@@ -561,7 +721,7 @@ __global__ __launch_bounds__(kAttnThreads) void sd_flash_decode_kernel(AttendPar
         const int nb = nk * bpc;
         const int per = (nb + nsb - 1) / nsb;
         const int r0 = min(nb, sp * per), r1 = min(nb, r0 + per);
-        decode_blocks<G, HOSTV>(p, KeptSrc{kstarts, bpc, s_end, w0, L}, r0, r1, bj, L, kbase, vbase, qv, m, lsum,
+        decode_blocks<G, HOSTV, !HOSTV && MAXS == kDecodeWideSplits>(p, KeptSrc{kstarts, bpc, s_end, w0, L}, r0, r1, bj, L, kbase, vbase, qv, qg, m, lsum,
                                 acc0, acc1, tblk, tmask, rec);
     }
 

@@ -96,6 +96,11 @@ SMALL = {
     # a budget larger than short contexts: sink + window cover everything
     "covering": dict(name="att_cover", batch=2, num_q_heads=4, num_kv_heads=1, max_context=2000,
                      stages=(Stage(64, 8, 40), Stage(8, 1, 64)), sink=64, window=1024, planted=2),
+    # the wide decode with more than one pair of blocks per wave in its
+    # kept-chunk splits: the matrix-core scores (G = 4), ragged tiles and
+    # single-block pairs
+    "wide_many_blocks": dict(name="att_wide_many", batch=4, num_q_heads=32, num_kv_heads=8, max_context=16384,
+                             stages=(Stage(256, 8, 24), Stage(64, 1, 67)), sink=16, window=200, planted=4),
     # 32 (request, KV head) pipelines: the wide decode kernel (unfused plan)
     "wide": dict(name="att_wide", batch=4, num_q_heads=32, num_kv_heads=8, max_context=4096,
                  stages=(Stage(256, 8, 4), Stage(32, 2, 8), Stage(8, 1, 16)), sink=16, window=100, planted=4),
