@@ -61,12 +61,59 @@ def test_random_cases_are_valid_configurations():
         assert all(st[i].chunk % st[i + 1].chunk == 0 for i in range(len(st) - 1))
         assert st[-1].chunk % 8 == 0
         assert len(lengths) == w.batch and min(lengths) >= 1 and max(lengths) <= w.max_context
+    for seed in WIDE_SEEDS:
+        w, lengths = random_wide_case(seed)
+        st = w.stages
+        assert w.batch * w.num_kv_heads >= 32 and w.num_q_heads == 4 * w.num_kv_heads
+        assert all(s.chunk % s.stride == 0 and s.chunk // s.stride <= 64 for s in st)
+        assert all(st[i].chunk % st[i + 1].chunk == 0 for i in range(len(st) - 1))
+        assert len(lengths) == w.batch and min(lengths) >= 1 and max(lengths) <= w.max_context
 
 
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_configuration(seed, fusion):
     w, lengths = random_case(seed)
     print(f"seed {seed} lengths {lengths}", flush=True)
+    run_case(w, lengths=lengths, check_scores=True)
+
+
+WIDE_SEEDS = list(range(6))
+
+
+def random_wide_case(seed: int):
+    """32 or 64 (request, KV head) pipelines at G = 4: the plan for many
+    pipelines (two load batches in the later stages, the wide decode, whose
+    kept-chunk splits score pairs of blocks on the matrix cores when a wave
+    takes more than one pair), with random strides, budgets that put from a
+    few to a few dozen blocks in a split, ragged lengths, sink and window."""
+    rng = np.random.default_rng(30_000 + seed)
+    BH = int(rng.choice([32, 64]))
+    B = int(rng.choice([2, 4, 8]))
+    Hkv = BH // B
+    Lmax = int(rng.integers(3000, 9001))
+    n0 = -(-Lmax // 256)
+    k0 = int(rng.integers(4, n0 + 3))
+    k1 = int(rng.integers(k0, 8 * k0 + 1))
+    c2 = int(rng.choice([8, 16]))
+    k2 = int(rng.integers(max(1, k1 // 2), k1 * (32 // c2) + 3))
+    stages = (Stage(256, int(rng.choice([4, 8, 16])), k0), Stage(32, int(rng.choice([1, 2, 4])), k1),
+              Stage(c2, int(rng.choice([1, 2])), k2))
+    sink = int(rng.choice([0, 3, 64]))
+    window = int(rng.choice([0, 37, 256]))
+    lengths = rng.integers(1, Lmax + 1, size=B)
+    lengths[0] = Lmax
+    if B >= 4:
+        lengths[-1] = int(rng.integers(1, 65))
+    w = tiny_workload(name=f"random_wide{seed}", batch=B, num_q_heads=4 * Hkv, num_kv_heads=Hkv, max_context=Lmax,
+                      stages=stages, sink=sink, window=window, planted=4, seed=40_000 + seed)
+    return w, [int(x) for x in lengths]
+
+
+@pytest.mark.parametrize("seed", WIDE_SEEDS)
+def test_random_wide_configuration(seed, fusion):
+    w, lengths = random_wide_case(seed)
+    print(f"wide seed {seed} B={w.batch} Hkv={w.num_kv_heads} Lmax={w.max_context} "
+          f"stages={[(s.chunk, s.stride, s.keep) for s in w.stages]} lengths {lengths}", flush=True)
     run_case(w, lengths=lengths, check_scores=True)
 
 
