@@ -123,6 +123,11 @@ typedef struct sd_stats {
  *                             allows) score the last stage inside the
  *                             kernel of the stage before it; default: when
  *                             the extra key rows stay within 8 MiB.
+ *  SD_HALF_ROWS=0             unfused, with the stage before the last
+ *                             sampling every other row of the last stage's
+ *                             8-row chunks: the last stage reads all eight
+ *                             rows; default: only the four that stage did
+ *                             not read, the other four's maximum stored by it.
  *  SD_VCACHE_ONCHIP=0         host values: the LRU step through device
  *                             memory at every cache size; default: on chip
  *                             for at most 8,192 slots and 1,024 attended

@@ -176,6 +176,26 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
             P.nwg = (P.ncand + P.per_wg - 1) / P.per_wg;
         }
     }
+    // Unfused, with stage S-2's stride twice stage S-1's and 8 rows per
+    // stage S-1 chunk: stage S-2 also stores each child's maximum over the
+    // 4 of its 8 rows it reads anyway, and stage S-1 reads only the other 4
+    // (half its bytes; the score is the larger maximum, exactly).
+    // SD_HALF_ROWS=0 reads every row in stage S-1.
+    c->half = 0;
+    c->half_rq = 0;
+    const char* henv = std::getenv("SD_HALF_ROWS");
+    if (!c->fuse && cfg.num_stages >= 2 && !(henv && henv[0] == '0')) {
+        const sd::StageGeom& P = c->st[cfg.num_stages - 2];
+        const sd::StageGeom& Q = c->st[cfg.num_stages - 1];
+        const int rq = P.chunk / Q.chunk;
+        // (rq a power of two from 2 to 16: stage S-2 reads 4 rq rows, whole
+        // 8-row load slots of 2 children each, in an instantiated slot count)
+        if (Q.chunk / Q.stride == 8 && P.stride == 2 * Q.stride && P.chunk % Q.chunk == 0 && rq >= 2 &&
+            (rq & (rq - 1)) == 0 && rq <= 16) {
+            c->half = 1;
+            c->half_rq = P.chunk / Q.chunk;
+        }
+    }
     // With many pipelines the unfused stages after the first score two load
     // batches per wave: half the workgroups, so half the redundant selects
     // at their heads (16 requests of up to 128K: stage 1 26.3 -> 24.7 us).
@@ -268,6 +288,17 @@ sd_status device_setup(sd_ctx* c) {
                                                              sd::stage_dev(c, c->S - 1), c->fuse_rq)
                                        : sd::kept_lds_words(sd::stage_dev(c, c->S - 1), c->S == 1);
     need = std::max(need, 4 * last_words + attend_static);
+    // half: stage S-1's kernel keeps stage S-2's kept indices too, and the
+    // stored-maximum index of each of its candidates
+    // and stage S-2's kernel stages its row scores (4 waves x 256 words)
+    if (c->half) {
+        need = std::max<int64_t>(need, 4 * int64_t(sd::kept_lds_words(sd::stage_dev(c, c->S - 2), c->S == 2) +
+                                                    c->st[c->S - 2].keep) +
+                                           prune_static + 4 * 4 * 16);
+        need = std::max<int64_t>(
+            need, (c->S >= 3 ? 4 * int64_t(sd::kept_lds_words(sd::stage_dev(c, c->S - 3), c->S == 3)) : 0) +
+                      prune_static + 4 * 4 * 256);
+    }
     // (unfused with the stage before the last reused, the last stage is selected in the decode kernel too)
     need = std::max(need, 4 * int64_t(sd::kept_lds_words(sd::stage_dev(c, c->S - 1), c->S == 1)) + attend_static);
     if (c->cfg.values_on_host) {
@@ -328,7 +359,9 @@ size_t carve_workspace(sd_ctx* c, char* base, bool dense) {
     const size_t o_part = cv.take<float>(BH * nsp * c->G * (2 + sd::kHeadDim));
     const size_t o_abs = cv.take<unsigned>(BH);
     const size_t o_req = cv.take<int32_t>(BH);
-    const size_t o_pre = c->fuse ? cv.take<int32_t>(BH * size_t(c->st[c->S - 2].ncand) * c->fuse_rq) : 0;
+    const size_t o_pre = c->fuse   ? cv.take<int32_t>(BH * size_t(c->st[c->S - 2].ncand) * c->fuse_rq)
+                         : c->half ? cv.take<int32_t>(BH * size_t(c->st[c->S - 2].ncand) * c->half_rq)
+                                   : 0;
     size_t o_vc[11] = {0};
     if (c->cfg.values_on_host) {
         c->vc.slots = int32_t(c->cfg.value_cache_tokens / 8);
@@ -355,7 +388,7 @@ size_t carve_workspace(sd_ctx* c, char* base, bool dense) {
     c->requant = reinterpret_cast<int32_t*>(base + o_req);
     c->tick = reinterpret_cast<int32_t*>(base + o_tick);
     c->flag = reinterpret_cast<int32_t*>(base + o_flag);
-    c->pre = c->fuse ? reinterpret_cast<int32_t*>(base + o_pre) : nullptr;
+    c->pre = c->fuse || c->half ? reinterpret_cast<int32_t*>(base + o_pre) : nullptr;
     if (c->cfg.values_on_host) {
         c->vc.pool = reinterpret_cast<uint16_t*>(base + o_vc[0]);
         c->vc.page = reinterpret_cast<int32_t*>(base + o_vc[1]);

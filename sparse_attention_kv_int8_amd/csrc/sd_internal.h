@@ -110,6 +110,10 @@ struct sd_ctx {
     int fuse_rq;                      // children per stage S-2 chunk
     int fuse_m;                       // stage S-2 stride / stage S-1 stride
     int32_t* pre;                     // [B][Hkv][st[S-2].ncand * fuse_rq] children's stage S-1 scores
+                                      // (half: [st[S-2].ncand * half_rq] maxima over the rows stage S-2 read)
+    int half;                         // unfused, stage S-2's stride twice stage S-1's (8 rows per chunk):
+                                      // stage S-1 reads only the rows stage S-2 did not
+    int half_rq;                      // children per stage S-2 chunk (half)
     unsigned* absmax_bits;            // [B][Hkv] bf16 bits of each key scale (sd_quantize_keys, sd_append_kv)
     int32_t* requant;                 // [B][Hkv] set by sd_append_kv when the scale grew
     int32_t* tick;                    // [B*Hkv][kTickInts] last-arriver counters (zero between launches)

@@ -27,6 +27,10 @@ namespace sd {
 
 constexpr int kPruneThreads = 256;
 constexpr int kPruneWaves = kPruneThreads / kWave;
+// PARTS staging: a wave's row scores, cpw x nrows <= 8 load slots x 8 rows
+// per batch, times the batches (at most 2 with kMaxCandPerWave = 16: the
+// geometry keeps cpw x nrows <= 128 for the sizes the plan admits)
+constexpr int kStageRowsPerWave = 256;
 // (kMaxCandPerWave, candidates per wave at most: sd_internal.h)
 
 struct PruneParams {
@@ -51,6 +55,14 @@ struct PruneParams {
     int32_t* pre;                 // fused next stage: [B][Hkv][cur.ncand * fuse_rq] children's scores
     const uint8_t* k4;            // first stage from the int4 sketch: [B][Hkv][k4_rows][64]
     int64_t k4_rows;
+    // rows shared with the stage before the last (unfused plan, that stage's
+    // stride twice the last's): children per chunk of the stage before, the
+    // children's maxima over the rows that stage read ([B][Hkv][its ncand *
+    // half_rq]), and, in the last stage's launch, the token offset of the
+    // first row it reads itself (its stride)
+    int half_rq;
+    int32_t* parts;
+    int odd_off;
 };
 
 // One load batch of a wave: CB candidates (starts xs, -1 = none) x NS8
@@ -58,7 +70,7 @@ struct PruneParams {
 // issues every row load of the batch; score() consumes them, so the two
 // can be separated by work that does not touch the rows (the first stage
 // issues its loads before it forms the query).
-template <int NS8, bool FUSE>
+template <int NS8, bool FUSE, bool PARTS = false>
 struct RowBatch {
     static constexpr int CB = NS8 >= 8 ? 1 : 8 / NS8;     // candidates per batch
     static constexpr int NL = CB * NS8;                    // loads per batch
@@ -82,7 +94,8 @@ struct RowBatch {
     }
 
     // Scores candidates first + c (c < CB, first + c < ncand, c < nvalid)
-    // into out (and, with FUSE, every child's score into pre_bj).
+    // into out (and, with FUSE, every child's score into pre_bj; with PARTS,
+    // every row's score into pre_bj, the batch's LDS staging rows).
     __device__ __forceinline__ void score(const PruneParams& p, const u32x4& qh, const u32x4& ql, int first,
                                           int nvalid, int32_t* __restrict__ out, int32_t* __restrict__ pre_bj) const {
         const StageDev& st = p.cur;
@@ -93,6 +106,7 @@ struct RowBatch {
         int best[CB];
 #pragma unroll
         for (int c = 0; c < CB; ++c) best[c] = INT32_MIN;
+        int rs[PARTS ? NL : 1];
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
             const u32x4 x = v[u];
@@ -112,11 +126,96 @@ struct RowBatch {
                 if (lane == 0 && it < p.fuse_rq && c < nvalid && first + c < st.ncand)
                     pre_bj[int64_t(first + c) * p.fuse_rq + it] = sub;
             }
+            if (PARTS) rs[u] = ok[u] ? s : INT32_MIN;
         }
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
             const int m = max_groups_i(best[c]);
             if (lane == 0 && c < nvalid && first + c < st.ncand) out[first + c] = m;
+        }
+        if (PARTS) {
+            // every row's score (INT32_MIN for rows that do not count), one
+            // lane per row, into this batch's [candidate][row] rows of the
+            // wave's LDS staging (pre_bj here); store_child_max reduces them
+#pragma unroll
+            for (int u = 0; u < NL; ++u) {
+                const int c = u / NS8, it = u % NS8;
+                if ((lane & 7) == 0) pre_bj[c * p.nrows + it * 8 + row8] = rs[u];
+            }
+        }
+    }
+};
+
+// PARTS: the wave's staged row scores ([cpw][nrows] in LDS, 4 rows per
+// child of the next stage) reduced to each child's maximum and stored
+// [candidate][child] from candidate `first` on: one store for the wave,
+// whole cache lines when cpw * half_rq is a multiple of 32.
+__device__ __forceinline__ void store_child_max(const PruneParams& p, const int* rows, int first, int cpw,
+                                                int32_t* __restrict__ parts_bj) {
+    const int lane = threadIdx.x & 63;
+    const int rq = p.half_rq;
+    for (int l = lane; l < cpw * rq; l += kWave) {
+        const int c = l / rq, k = l - c * rq;
+        const i32x4 r = *reinterpret_cast<const i32x4*>(rows + c * p.nrows + 4 * k);
+        if (first + c < p.cur.ncand) parts_bj[int64_t(first) * rq + l] = max(max(r.x, r.y), max(r.z, r.w));
+    }
+}
+
+// One load batch of the last stage's own rows when the stage before it
+// read every other one (its stride twice the last's; 8 rows per last-stage
+// chunk): rows x + odd_off + r rstride, r < 4, of 16 candidates, two per
+// load slot (lanes [0, 32): candidate 2 u, lanes [32, 64): 2 u + 1; 8 lanes
+// per 128-byte row).  A candidate's score is the larger of the maximum over
+// these rows and the maximum over the other four (parts, stored by the
+// stage before, which read them): the maximum over all eight, exactly, with
+// half the rows read.
+struct OddBatch {
+    static constexpr int CB = 16;
+    u32x4 v[8];
+    bool ok[8];
+    int part;          // lane c < CB: candidate c's stored maximum
+
+    __device__ __forceinline__ void load(const PruneParams& p, const int* xs, const int* pidx, int64_t L,
+                                         const int8_t* __restrict__ k8_bj, const int32_t* __restrict__ parts_bj) {
+        const int lane = threadIdx.x & 63, r4 = (lane >> 3) & 3, hf = lane >> 5, sl = lane & 7;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int x = xs[2 * u + hf];
+            const int64_t t = int64_t(x) + p.odd_off + int64_t(r4) * p.rstride;
+            ok[u] = x >= 0 && t < L;
+            const int64_t tc = ok[u] ? t : 0;      // issued for every lane (masked in score)
+            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k8_bj + tc * kHeadDim) + sl);
+        }
+        const int pi = lane < CB ? pidx[lane] : -1;
+        part = pi >= 0 ? parts_bj[pi] : INT32_MIN;
+    }
+
+    __device__ __forceinline__ void score(const PruneParams& p, const u32x4& qh, const u32x4& ql, int first,
+                                          int nvalid, int32_t* __restrict__ out) const {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const u32x4 x = v[u];
+            int ah = __builtin_amdgcn_sdot4((int)qh.x, (int)x.x, 0, false);
+            ah = __builtin_amdgcn_sdot4((int)qh.y, (int)x.y, ah, false);
+            ah = __builtin_amdgcn_sdot4((int)qh.z, (int)x.z, ah, false);
+            ah = __builtin_amdgcn_sdot4((int)qh.w, (int)x.w, ah, false);
+            int al = __builtin_amdgcn_sdot4((int)ql.x, (int)x.x, 0, false);
+            al = __builtin_amdgcn_sdot4((int)ql.y, (int)x.y, al, false);
+            al = __builtin_amdgcn_sdot4((int)ql.z, (int)x.z, al, false);
+            al = __builtin_amdgcn_sdot4((int)ql.w, (int)x.w, al, false);
+            int h = sum8_i(ah * 64 + al);
+            h = ok[u] ? h : INT32_MIN;
+            h = max(h, dpp_i<kDppRor8>(h));
+            const int c0 = 2 * u, c1 = 2 * u + 1;
+            const int m0 = max(max(__builtin_amdgcn_readlane(h, 0), __builtin_amdgcn_readlane(h, 16)),
+                               __builtin_amdgcn_readlane(part, c0));
+            const int m1 = max(max(__builtin_amdgcn_readlane(h, 32), __builtin_amdgcn_readlane(h, 48)),
+                               __builtin_amdgcn_readlane(part, c1));
+            if (lane == 0) {
+                if (c0 < nvalid && first + c0 < p.cur.ncand) out[first + c0] = m0;
+                if (c1 < nvalid && first + c1 < p.cur.ncand) out[first + c1] = m1;
+            }
         }
     }
 };
@@ -194,19 +293,21 @@ struct SketchBatch {
 // the next stage's samples (rstride = its stride, one 8-row slot per child
 // chunk): this stage's score is the max over rows i % fuse_m == 0 (its own
 // samples), and each slot's max is written as that child's score.
-template <int NS8, bool FUSE>
+template <int NS8, bool FUSE, bool PARTS = false>
 __device__ __forceinline__ void score_slice(const PruneParams& p, const int* cstart, int64_t L,
                                             const int8_t* __restrict__ k8_bj, const u32x4& qh, const u32x4& ql,
-                                            int first, int32_t* __restrict__ out, int32_t* __restrict__ pre_bj) {
-    using RB = RowBatch<NS8, FUSE>;
+                                            int first, int32_t* __restrict__ out, int32_t* __restrict__ pre_bj,
+                                            int* stage_rows = nullptr) {
+    using RB = RowBatch<NS8, FUSE, PARTS>;
     for (int c0 = 0; c0 < p.cpw; c0 += RB::CB) {
         int64_t xs[RB::CB];
 #pragma unroll
         for (int c = 0; c < RB::CB; ++c) xs[c] = (c0 + c < p.cpw) ? cstart[c0 + c] : -1;
         RB rb;
         rb.load(p, xs, L, k8_bj);
-        rb.score(p, qh, ql, first + c0, p.cpw - c0, out, pre_bj);
+        rb.score(p, qh, ql, first + c0, p.cpw - c0, out, PARTS ? stage_rows + c0 * p.nrows : pre_bj);
     }
+    if (PARTS) store_child_max(p, stage_rows, first, p.cpw, pre_bj);
 }
 
 // hi/lo int8 split of the 16 query dims [16 sl, 16 sl + 16): Q = 64 hi + lo,
@@ -261,11 +362,16 @@ __device__ __forceinline__ void split_query4d(const int* Qlds, int part, uint32_
 // (selected here, or given), then this workgroup's slice of the candidates.
 // Lraw: the request's length as loaded (sanitised here, where first needed,
 // so that the head select's loads do not wait for it).
-template <int NS8, int SEL, bool FUSE>
+// HR (rows shared with the stage before the last): 1, this stage is the
+// one before the last and also stores its children's maxima (parts); 2,
+// this is the last stage and reads only its rows that the stage before did
+// not (OddBatch; 16 candidates per wave).
+template <int NS8, int SEL, bool FUSE, int HR>
 __device__ __forceinline__ void score_later(const PruneParams& p, int bj, int wgi, int b, int j, int32_t Lraw,
                                             int32_t* kept_bj, const int8_t* __restrict__ k8_bj,
                                             int32_t* scores_bj, uint32_t* dyn, int* Qlds, unsigned* tmp,
-                                            int* cstart) {
+                                            int* cstart, int* cpre, int* stage_rows) {
+    static_assert(HR != 2 || (SEL != 0 && SEL != kGiven && !FUSE), "odd rows: the stage before ran this step");
     const int wave = threadIdx.x >> 6;
     const int sl = threadIdx.x & 7;
     const int32_t* parents = nullptr;
@@ -293,8 +399,12 @@ __device__ __forceinline__ void score_later(const PruneParams& p, int bj, int wg
         // a score, so it starts below the length anyway.
         int* sel = reinterpret_cast<int*>(dyn + p.prev.ncand);
         const int32_t* pp = p.stage >= 2 ? kept_bj + p.pp_koff : nullptr;
+        // HR = 2: the kept chunks' indices too (after the select's words)
+        int* pidx = HR == 2 ? reinterpret_cast<int*>(dyn + kept_lds_words(p.prev, p.stage == 1)) : nullptr;
         const int nk = kept_of_stage<kPruneThreads, SEL>(p.prev, p.stage == 1, p.prev_scores + int64_t(bj) * p.prev.ncand,
-                                                         pp, p.Lmax, dyn, tmp, p.stage);
+                                                         pp, p.Lmax, dyn, tmp, p.stage, pidx);
+        if (HR == 2)
+            for (int i = nk + threadIdx.x; i < p.prev.keep; i += kPruneThreads) pidx[i] = -1;
         L = length_here(Lraw, p.Lmax);
         for (int i = nk + threadIdx.x; i < p.prev.keep; i += kPruneThreads) sel[i] = -1;
         if (threadIdx.x < kHeadDim) Qlds[threadIdx.x] = qval;
@@ -304,15 +414,34 @@ __device__ __forceinline__ void score_later(const PruneParams& p, int bj, int wg
     SD_PHASE(p.stage, 1);
     // the starts of this workgroup's candidates, one thread each
     const int wg_first = wgi * kPruneWaves * p.cpw;
-    if (int(threadIdx.x) < kPruneWaves * p.cpw)
-        cstart[threadIdx.x] = int(cand_start(p.cur, SEL == 0, parents, wg_first + threadIdx.x, L));
+    if (int(threadIdx.x) < kPruneWaves * p.cpw) {
+        const int ci = wg_first + threadIdx.x;
+        const int x = int(cand_start(p.cur, SEL == 0, parents, ci, L));
+        cstart[threadIdx.x] = x;
+        if constexpr (HR == 2) {
+            // this candidate's stored maximum: it is child ci % rq of kept
+            // chunk ci / rq of the stage before (index pidx there)
+            const int* pidx = reinterpret_cast<const int*>(dyn + kept_lds_words(p.prev, p.stage == 1));
+            cpre[threadIdx.x] = x >= 0 ? pidx[ci / p.half_rq] * p.half_rq + ci % p.half_rq : -1;
+        }
+    }
     u32x4 qh, ql;
     split_query(Qlds, sl, qh, ql);
     __syncthreads();
 
     const int first = wg_first + wave * p.cpw;
-    score_slice<NS8, FUSE>(p, cstart + wave * p.cpw, L, k8_bj, qh, ql, first, scores_bj,
-                               FUSE ? p.pre + int64_t(bj) * p.cur.ncand * p.fuse_rq : nullptr);
+    if constexpr (HR == 2) {
+        OddBatch ob;
+        ob.load(p, cstart + wave * p.cpw, cpre + wave * p.cpw, L, k8_bj,
+                p.parts + int64_t(bj) * p.prev.ncand * p.half_rq);
+        ob.score(p, qh, ql, first, p.cpw, scores_bj);
+    } else {
+        score_slice<NS8, FUSE, HR == 1>(p, cstart + wave * p.cpw, L, k8_bj, qh, ql, first, scores_bj,
+                                        FUSE     ? p.pre + int64_t(bj) * p.cur.ncand * p.fuse_rq
+                                        : HR == 1 ? p.parts + int64_t(bj) * p.cur.ncand * p.half_rq
+                                                  : nullptr,
+                                        HR == 1 ? stage_rows + wave * kStageRowsPerWave : nullptr);
+    }
     if constexpr (SEL != 0 && SEL != kGiven) {
         // workgroup 0 publishes the previous stage's kept set (ascending,
         // -1 padded); stored last, so no barrier waits on these stores
@@ -325,13 +454,16 @@ __device__ __forceinline__ void score_later(const PruneParams& p, int bj, int wg
 // previous stage (0 = stage 0, kGiven = the previous stage reused), fused
 // next stage, int4 sketch): each launch carries only its own path, which
 // keeps code size and scalar-register pressure down.
-template <int NS8, int SEL, bool FUSE, bool Q4 = false>
+template <int NS8, int SEL, bool FUSE, bool Q4 = false, int HR = 0>
 __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PruneParams p) {
-    static_assert(!Q4 || (SEL == 0 && !FUSE), "the int4 sketch serves the unfused first stage only");
+    static_assert(!Q4 || (SEL == 0 && !FUSE && HR == 0), "the int4 sketch serves the unfused first stage only");
+    static_assert(HR == 0 || !FUSE, "rows shared with the stage before: unfused plan");
     extern __shared__ uint32_t dyn[];      // the previous stage's select (kept_lds_words)
     __shared__ int Qlds[kHeadDim];
     __shared__ unsigned tmp[32];
     __shared__ int cstart[kPruneWaves * kMaxCandPerWave];
+    __shared__ int cpre[HR == 2 ? kPruneWaves * OddBatch::CB : 1];   // HR = 2: stored-maximum indices
+    __shared__ __align__(16) int stage_rows[HR == 1 ? kPruneWaves * kStageRowsPerWave : 1];   // HR = 1: row scores
 
     SD_PHASE(p.stage, 0);
     // all workgroups of a (request, KV head) on one XCD (sd_device.h): the
@@ -376,7 +508,7 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
         // First stage, one load batch per wave (cpw = CB): the candidate
         // starts follow from the indices, so the rows are loaded first and
         // the query codes are formed while the loads are in flight.
-        using RB = RowBatch<NS8, false>;
+        using RB = RowBatch<NS8, false, HR == 1>;
         const bool bad = Lraw < 1 || Lraw > p.Lmax;
         const int64_t L = bad ? 0 : Lraw;
         const int first = (wgi * kPruneWaves + wave) * p.cpw;
@@ -391,9 +523,12 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
             p.qgroup[int64_t(bj) * kHeadDim + threadIdx.x] = Qlds[threadIdx.x];
         u32x4 qh, ql;
         split_query(Qlds, sl, qh, ql);
-        rb.score(p, qh, ql, first, p.cpw, scores_bj, nullptr);
+        int* rows_w = stage_rows + wave * kStageRowsPerWave;
+        rb.score(p, qh, ql, first, p.cpw, scores_bj, HR == 1 ? rows_w : nullptr);
+        if (HR == 1) store_child_max(p, rows_w, first, p.cpw, p.parts + int64_t(bj) * p.cur.ncand * p.half_rq);
     } else {
-        score_later<NS8, SEL, FUSE>(p, bj, wgi, b, j, Lraw, kept_bj, k8_bj, scores_bj, dyn, Qlds, tmp, cstart);
+        score_later<NS8, SEL, FUSE, HR>(p, bj, wgi, b, j, Lraw, kept_bj, k8_bj, scores_bj, dyn, Qlds, tmp, cstart,
+                                        cpre, stage_rows);
     }
     SD_PHASE(p.stage, 2);
 }
@@ -439,18 +574,36 @@ hipError_t launch_prune_stage(sd_ctx* c, int st, bool given, bool fused, const u
     p.fuse_rq = fuse ? c->fuse_rq : 0;
     p.fuse_m = fuse ? c->fuse_m : 1;
     p.pre = fuse ? c->pre : nullptr;
+    const bool q4 = k4 != nullptr && st == 0 && !fuse;
+    // rows shared between the last two stages (unfused plan): stage S-2
+    // stores its children's maxima, unless scored from the int4 sketch;
+    // stage S-1 then reads only its other rows, when stage S-2 ran in this
+    // step (not reused: `given`) and stored them
+    const int hr = !c->half || fused                                         ? 0
+                   : st == c->S - 2                                          ? (q4 ? 0 : 1)
+                   : st == c->S - 1 && !given && !(st == 1 && k4 != nullptr) ? 2
+                                                                             : 0;
+    p.half_rq = hr ? c->half_rq : 0;
+    p.parts = hr ? c->pre : nullptr;
+    p.odd_off = 0;
+    if (hr == 2) {
+        p.nrows = 4;
+        p.rstride = c->st[st - 1].stride;
+        p.odd_off = c->st[st].stride;
+        p.cpw = OddBatch::CB;
+        p.W = (p.cur.ncand + kPruneWaves * p.cpw - 1) / (kPruneWaves * p.cpw);
+    }
     size_t words = 0;
     if (st > 0) {
         p.prev = stage_dev(c, st - 1);
         p.prev_scores = c->scores[st - 1];
         p.pp_koff = st >= 2 ? c->st[st - 2].koff : 0;
-        if (!given) words = size_t(kept_lds_words(p.prev, st == 1));
+        if (!given) words = size_t(kept_lds_words(p.prev, st == 1)) + (hr == 2 ? size_t(p.prev.keep) : 0);
         else words = size_t(p.prev.ncand + p.prev.keep + 1);
     }
     const size_t lds = words * 4;
     const int ns8 = (p.nrows + 7) >> 3;
     const int sel = st == 0 ? 0 : given ? kGiven : select_width(p.prev.ncand);
-    const bool q4 = k4 != nullptr && st == 0 && !fuse;
     if (q4) {
         // one batch of int4 candidates per wave (SketchBatch: 8 / NS16)
         const int ns8p = ns8 == 1 ? 1 : ns8 == 2 ? 2 : ns8 <= 4 ? 4 : 8;
@@ -459,18 +612,29 @@ hipError_t launch_prune_stage(sd_ctx* c, int st, bool given, bool fused, const u
     }
     const dim3 grid(unsigned(pipe_grid(p.W, p.BH))), block(kPruneThreads);
 #define SD_K(N, S, F, Q) launch(sd_prune_stage_kernel<N, S, F, Q>, grid, block, lds, s, t, p)
+#define SD_KH(N, S, H) launch(sd_prune_stage_kernel<N, S, false, false, H>, grid, block, lds, s, t, p)
 #define SD_NS(S)                                               \
     if (fuse) {                                                \
         if (ns8 <= 2) SD_K(2, S, true, false);                 \
         else if (ns8 <= 4) SD_K(4, S, true, false);            \
         else SD_K(8, S, true, false);                          \
+    } else if (hr == 1) {                                      \
+        if (ns8 == 1) SD_KH(1, S, 1);                          \
+        else if (ns8 == 2) SD_KH(2, S, 1);                     \
+        else if (ns8 <= 4) SD_KH(4, S, 1);                     \
+        else SD_KH(8, S, 1);                                   \
     } else {                                                   \
         if (ns8 == 1) SD_K(1, S, false, false);                \
         else if (ns8 == 2) SD_K(2, S, false, false);           \
         else if (ns8 <= 4) SD_K(4, S, false, false);           \
         else SD_K(8, S, false, false);                         \
     }
-    if (q4) {
+    if (hr == 2) {
+        // the stage before ran and was selected here: never kGiven
+        if (sel == 4) SD_KH(1, 4, 2);
+        else if (sel == 16) SD_KH(1, 16, 2);
+        else SD_KH(1, kSelLds, 2);
+    } else if (q4) {
         if (ns8 == 1) SD_K(1, 0, false, true);
         else if (ns8 == 2) SD_K(2, 0, false, true);
         else if (ns8 <= 4) SD_K(4, 0, false, true);
@@ -481,6 +645,7 @@ hipError_t launch_prune_stage(sd_ctx* c, int st, bool given, bool fused, const u
     else if (sel == 16) { SD_NS(16); }
     else { SD_NS(kSelLds); }
 #undef SD_NS
+#undef SD_KH
 #undef SD_K
     return hipGetLastError();
 }

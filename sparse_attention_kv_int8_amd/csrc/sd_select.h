@@ -509,9 +509,11 @@ __host__ __device__ inline int kept_lds_words(const StageDev& st, bool first_sta
 // unused for the first stage): they are staged in LDS together with the
 // scores, so turning selected indices into starts costs no memory latency
 // after the select.  lds: kept_lds_words(st, first_stage) words.
+// idx_out (optional, nk words): the kept candidates' indices, ascending.
 template <int NT, int E>
 __device__ int kept_of_stage(const StageDev& st, bool first_stage, const int32_t* scores_bj,
-                             const int32_t* parents, int64_t L, uint32_t* lds, unsigned* tmp, int pslot = -1) {
+                             const int32_t* parents, int64_t L, uint32_t* lds, unsigned* tmp, int pslot = -1,
+                             int* idx_out = nullptr) {
     (void)pslot;                 // phase-stamp slot (latency studies only)
     uint32_t* keys = lds;
     int* sel = reinterpret_cast<int*>(lds + st.ncand);
@@ -522,7 +524,11 @@ __device__ int kept_of_stage(const StageDev& st, bool first_stage, const int32_t
     if (pslot >= 0) SD_PHASE(pslot, 6);
     const int nk = select_top<NT, E>(keys, st.ncand, st.keep, sel, cand, tmp, ks);
     if (pslot >= 0) SD_PHASE(pslot, 7);
-    for (int i = threadIdx.x; i < nk; i += NT) sel[i] = int(cand_start(st, first_stage, par, sel[i], L));
+    for (int i = threadIdx.x; i < nk; i += NT) {
+        const int ci = sel[i];
+        if (idx_out) idx_out[i] = ci;
+        sel[i] = int(cand_start(st, first_stage, par, ci, L));
+    }
     __syncthreads();
     return nk;
 }

@@ -130,19 +130,26 @@ def fusion(request, monkeypatch):
     return request.param
 
 
+SMALL_LENGTHS = {"ragged_g4": [1, 777, 5000], "g2_strided_last": [4096, 1001],
+                 "many_pipelines": [6000, 2049, 313, 4500], "twelve_samples": [2999, 95]}
+
+
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_small_shapes(name, fusion):
-    w = SMALL[name]
-    lengths = None
-    if name == "ragged_g4":
-        lengths = [1, 777, 5000]
-    elif name == "g2_strided_last":
-        lengths = [4096, 1001]
-    elif name == "many_pipelines":
-        lengths = [6000, 2049, 313, 4500]
-    elif name == "twelve_samples":
-        lengths = [2999, 95]
-    run_case(w, lengths=lengths, check_scores=True)
+    run_case(SMALL[name], lengths=SMALL_LENGTHS.get(name), check_scores=True)
+
+
+@pytest.mark.parametrize("name", ["ragged_g4", "g1_no_sink_window", "many_pipelines"])
+def test_small_shapes_last_stage_reads_every_row(name, monkeypatch):
+    """Unfused shapes whose stage before the last samples every other row
+    of the last stage's chunks: by default the last stage reads only the
+    rows that stage did not and takes the larger of the two maxima; here
+    (SD_HALF_ROWS=0) it reads all eight.  Every stage's scores bit-exact
+    either way (the default is covered by the unfused runs of the other
+    tests)."""
+    monkeypatch.setenv("SD_FUSE_LAST_STAGE", "0")
+    monkeypatch.setenv("SD_HALF_ROWS", "0")
+    run_case(SMALL[name], lengths=SMALL_LENGTHS.get(name), check_scores=True)
 
 
 def test_full_budgets_equal_dense(fusion):
