@@ -209,6 +209,9 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
             g.nwg = (g.ncand + g.per_wg - 1) / g.per_wg;
         }
     }
+    // (stage S-2's row scores are staged per wave in LDS: 256 words, 128
+    // with every geometry above; checked, not assumed)
+    if (c->half && (c->st[cfg.num_stages - 2].per_wg / 4) * c->st[cfg.num_stages - 2].nrows > 256) c->half = 0;
     const float scale = cfg.softmax_scale > 0.0f ? cfg.softmax_scale : 1.0f / std::sqrt(float(cfg.head_dim));
     c->scale_log2 = scale * 1.4426950408889634f;
 
@@ -290,14 +293,14 @@ sd_status device_setup(sd_ctx* c) {
     need = std::max(need, 4 * last_words + attend_static);
     // half: stage S-1's kernel keeps stage S-2's kept indices too, and the
     // stored-maximum index of each of its candidates
-    // and stage S-2's kernel stages its row scores (4 waves x 256 words)
+    // and stage S-2's kernel stages its row scores (4 waves x 320 words)
     if (c->half) {
         need = std::max<int64_t>(need, 4 * int64_t(sd::kept_lds_words(sd::stage_dev(c, c->S - 2), c->S == 2) +
                                                     c->st[c->S - 2].keep) +
                                            prune_static + 4 * 4 * 16);
         need = std::max<int64_t>(
             need, (c->S >= 3 ? 4 * int64_t(sd::kept_lds_words(sd::stage_dev(c, c->S - 3), c->S == 3)) : 0) +
-                      prune_static + 4 * 4 * 256);
+                      prune_static + 4 * 4 * (256 + 64));
     }
     // (unfused with the stage before the last reused, the last stage is selected in the decode kernel too)
     need = std::max(need, 4 * int64_t(sd::kept_lds_words(sd::stage_dev(c, c->S - 1), c->S == 1)) + attend_static);

@@ -27,10 +27,11 @@ namespace sd {
 
 constexpr int kPruneThreads = 256;
 constexpr int kPruneWaves = kPruneThreads / kWave;
-// PARTS staging: a wave's row scores, cpw x nrows <= 8 load slots x 8 rows
-// per batch, times the batches (at most 2 with kMaxCandPerWave = 16: the
-// geometry keeps cpw x nrows <= 128 for the sizes the plan admits)
-constexpr int kStageRowsPerWave = 256;
+// PARTS staging: a wave's row scores, cpw x nrows <= kStageRows words (128
+// for every geometry the plan admits: cpw x nrows = 8 per load slot x 8
+// slots per batch x at most 2 batches), then one spare word per lane
+constexpr int kStageRows = 256;
+constexpr int kStageRowsPerWave = kStageRows + kWave;
 // (kMaxCandPerWave, candidates per wave at most: sd_internal.h)
 
 struct PruneParams {
@@ -95,9 +96,11 @@ struct RowBatch {
 
     // Scores candidates first + c (c < CB, first + c < ncand, c < nvalid)
     // into out (and, with FUSE, every child's score into pre_bj; with PARTS,
-    // every row's score into pre_bj, the batch's LDS staging rows).
+    // every row's score into pre_bj, the batch's LDS staging rows, the other
+    // lanes' stores going to spare[lane], the wave's 64 spare words).
     __device__ __forceinline__ void score(const PruneParams& p, const u32x4& qh, const u32x4& ql, int first,
-                                          int nvalid, int32_t* __restrict__ out, int32_t* __restrict__ pre_bj) const {
+                                          int nvalid, int32_t* __restrict__ out, int32_t* __restrict__ pre_bj,
+                                          int* spare = nullptr) const {
         const StageDev& st = p.cur;
         const int lane = threadIdx.x & 63, row8 = lane >> 3;
         bool own[NS8];                             // row of slot it is one of this stage's samples
@@ -106,7 +109,6 @@ struct RowBatch {
         int best[CB];
 #pragma unroll
         for (int c = 0; c < CB; ++c) best[c] = INT32_MIN;
-        int rs[PARTS ? NL : 1];
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
             const u32x4 x = v[u];
@@ -126,22 +128,24 @@ struct RowBatch {
                 if (lane == 0 && it < p.fuse_rq && c < nvalid && first + c < st.ncand)
                     pre_bj[int64_t(first + c) * p.fuse_rq + it] = sub;
             }
-            if (PARTS) rs[u] = ok[u] ? s : INT32_MIN;
+            if (PARTS) {
+                // every row's score (INT32_MIN for rows that do not count),
+                // one lane per row, into this batch's [candidate][row] rows
+                // of the wave's LDS staging (pre_bj here; LDS writes leave
+                // the load counter alone); store_child_max reduces them
+                // (every lane stores, without a branch: the group's first
+                // lane to its row, the others to a spare word of their own
+                // past the rows; a branch here made the compiler wait for all
+                // of the batch's loads at once)
+                const int c = u / NS8, it = u % NS8;
+                int* at = (lane & 7) == 0 ? pre_bj + c * p.nrows + it * 8 + row8 : spare + lane;
+                *at = ok[u] ? s : INT32_MIN;
+            }
         }
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
             const int m = max_groups_i(best[c]);
             if (lane == 0 && c < nvalid && first + c < st.ncand) out[first + c] = m;
-        }
-        if (PARTS) {
-            // every row's score (INT32_MIN for rows that do not count), one
-            // lane per row, into this batch's [candidate][row] rows of the
-            // wave's LDS staging (pre_bj here); store_child_max reduces them
-#pragma unroll
-            for (int u = 0; u < NL; ++u) {
-                const int c = u / NS8, it = u % NS8;
-                if ((lane & 7) == 0) pre_bj[c * p.nrows + it * 8 + row8] = rs[u];
-            }
         }
     }
 };
@@ -305,7 +309,8 @@ __device__ __forceinline__ void score_slice(const PruneParams& p, const int* cst
         for (int c = 0; c < RB::CB; ++c) xs[c] = (c0 + c < p.cpw) ? cstart[c0 + c] : -1;
         RB rb;
         rb.load(p, xs, L, k8_bj);
-        rb.score(p, qh, ql, first + c0, p.cpw - c0, out, PARTS ? stage_rows + c0 * p.nrows : pre_bj);
+        rb.score(p, qh, ql, first + c0, p.cpw - c0, out, PARTS ? stage_rows + c0 * p.nrows : pre_bj,
+                 PARTS ? stage_rows + kStageRows : nullptr);
     }
     if (PARTS) store_child_max(p, stage_rows, first, p.cpw, pre_bj);
 }
@@ -524,7 +529,7 @@ __global__ __launch_bounds__(kPruneThreads) void sd_prune_stage_kernel(PrunePara
         u32x4 qh, ql;
         split_query(Qlds, sl, qh, ql);
         int* rows_w = stage_rows + wave * kStageRowsPerWave;
-        rb.score(p, qh, ql, first, p.cpw, scores_bj, HR == 1 ? rows_w : nullptr);
+        rb.score(p, qh, ql, first, p.cpw, scores_bj, HR == 1 ? rows_w : nullptr, HR == 1 ? rows_w + kStageRows : nullptr);
         if (HR == 1) store_child_max(p, rows_w, first, p.cpw, p.parts + int64_t(bj) * p.cur.ncand * p.half_rq);
     } else {
         score_later<NS8, SEL, FUSE, HR>(p, bj, wgi, b, j, Lraw, kept_bj, k8_bj, scores_bj, dyn, Qlds, tmp, cstart,
