@@ -126,7 +126,8 @@ typedef struct sd_stats {
  *  SD_HALF_ROWS=0             unfused, with the stage before the last
  *                             sampling every other row of the last stage's
  *                             8-row chunks: the last stage reads all eight
- *                             rows; default: only the four that stage did
+ *                             rows; default with 32 or more (request, KV
+ *                             head) pipelines: only the four that stage did
  *                             not read, the other four's maximum stored by it.
  *  SD_VCACHE_ONCHIP=0         host values: the LRU step through device
  *                             memory at every cache size; default: on chip

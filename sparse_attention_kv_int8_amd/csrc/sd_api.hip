@@ -177,14 +177,18 @@ sd_status plan(const sd_config& cfg, sd_ctx* c) {
         }
     }
     // Unfused, with stage S-2's stride twice stage S-1's and 8 rows per
-    // stage S-1 chunk: stage S-2 also stores each child's maximum over the
-    // 4 of its 8 rows it reads anyway, and stage S-1 reads only the other 4
-    // (half its bytes; the score is the larger maximum, exactly).
+    // stage S-1 chunk, and many pipelines: stage S-2 also stores each
+    // child's maximum over the 4 of its 8 rows it reads anyway, and stage
+    // S-1 reads only the other 4 (half its bytes; the score is the larger
+    // maximum, exactly).  16 requests of up to 128K: stage 2 16.3 -> 12.0 us,
+    // the step 125.8 -> 122.3 us.  With few pipelines the stages are
+    // latency, not bytes, and stage S-1's 16 candidates per wave halve its
+    // workgroups: one request unfused, 35.7 -> 36.5 us at 128K.
     // SD_HALF_ROWS=0 reads every row in stage S-1.
     c->half = 0;
     c->half_rq = 0;
     const char* henv = std::getenv("SD_HALF_ROWS");
-    if (!c->fuse && cfg.num_stages >= 2 && !(henv && henv[0] == '0')) {
+    if (!c->fuse && cfg.num_stages >= 2 && BH >= sd::kDecodeWideMinPipes && !(henv && henv[0] == '0')) {
         const sd::StageGeom& P = c->st[cfg.num_stages - 2];
         const sd::StageGeom& Q = c->st[cfg.num_stages - 1];
         const int rq = P.chunk / Q.chunk;

@@ -142,11 +142,12 @@ def test_small_shapes(name, fusion):
 @pytest.mark.parametrize("name", ["ragged_g4", "g1_no_sink_window", "many_pipelines"])
 def test_small_shapes_last_stage_reads_every_row(name, monkeypatch):
     """Unfused shapes whose stage before the last samples every other row
-    of the last stage's chunks: by default the last stage reads only the
-    rows that stage did not and takes the larger of the two maxima; here
-    (SD_HALF_ROWS=0) it reads all eight.  Every stage's scores bit-exact
-    either way (the default is covered by the unfused runs of the other
-    tests)."""
+    of the last stage's chunks: with 32 or more pipelines (many_pipelines)
+    the last stage by default reads only the rows that stage did not and
+    takes the larger of the two maxima; here (SD_HALF_ROWS=0) it reads all
+    eight, as it does by default with fewer pipelines.  Every stage's
+    scores bit-exact either way (the default is covered by the unfused runs
+    of the other tests)."""
     monkeypatch.setenv("SD_FUSE_LAST_STAGE", "0")
     monkeypatch.setenv("SD_HALF_ROWS", "0")
     run_case(SMALL[name], lengths=SMALL_LENGTHS.get(name), check_scores=True)
